@@ -1,0 +1,28 @@
+"""CPU oracle for exact scaled-dot-product attention — TEST INFRASTRUCTURE ONLY.
+
+Only the test suite, the package smoke check and the benchmark's CPU-baseline
+leg may import this package. The GPU library never calls it and shares no
+code with it; if the HIP library is missing the product path fails instead of
+falling back here.
+
+What it computes is the plain definition of attention (FlashAttention guide,
+cxbdf.cn, part 1: Attention(Q, K, V) = softmax(QKᵀ/√d_k)·V, softmax per row),
+with the N×N score matrix materialised in float64. The fused method reaches
+this same result up to summation order (the pages call it exact, not an
+approximation: Flash Attention 是什麼, adersaytech.com, section "exact, 不是
+近似"), so the definition itself is the oracle.
+
+Modules:
+  attention   NumPy float64 forward and backward, whole tensors or sampled rows
+  bruteforce  pure-Python loops (math.exp / math.fsum) for tiny shapes
+
+Pins: every function here is checked in tests/test_oracle_*.py against hand-
+derived worked values (tests/golden/), closed forms, invariants, finite
+differences and torch's CPU float64 SDPA. No function is "parity unpinned".
+"""
+from .attention import (attention_fwd, attention_bwd, attention_probs,
+                        attention_fwd_rows, attention_bwd_sampled)
+from . import bruteforce
+
+__all__ = ["attention_fwd", "attention_bwd", "attention_probs", "attention_fwd_rows",
+           "attention_bwd_sampled", "bruteforce"]

@@ -1,0 +1,212 @@
+"""NumPy float64 oracle: attention by its definition, with S materialised.
+
+Test infrastructure only (see the package docstring).
+
+Forward, per sequence s, query head h and its KV head g = ⌊h / (Hq/Hkv)⌋,
+positions local to the sequence (FlashAttention guide, cxbdf.cn, part 1,
+"計算注意力分數" / "應用 Softmax" / "與 V 聚合"):
+
+    S_ij  = scale · Σ_c Q[i,c]·K[j,c]           for j visible from i
+    LSE_i = ln Σ_j exp(S_ij)                     (computed as m_i + ln Σ exp(S_ij − m_i))
+    P_ij  = exp(S_ij − LSE_i)                    (softmax along the row)
+    O_i   = Σ_j P_ij · V_j
+
+Visibility: every key of the same sequence, or keys j ≤ i when causal (the
+causal flag of ``flash_attn_func``, Llama-Factory page, first code sample).
+Sequences never see each other (padding-free packing; the mlqm.cn page,
+section 四, lists padding masks among what the method supports).
+The row logsumexp is the ``softmax_lse`` the forward kernel writes out
+(FlashAttention-2 全解析, blog.gitcode.com, core tiling sketch), in natural
+log of the scaled logits.
+
+Backward, given dO (chain rule; the pages only say the backward recomputes
+S from Q, K, V blocks instead of storing it: cxbdf.cn guide, part 2, item 3):
+
+    dV_j  = Σ_i P_ij · dO_i
+    dP_ij = dO_i · V_j
+    D_i   = Σ_j P_ij · dP_ij
+    dS_ij = P_ij · (dP_ij − D_i)
+    dQ_i  = scale · Σ_j dS_ij · K_j
+    dK_j  = scale · Σ_i dS_ij · Q_i
+
+dK and dV of a KV head are summed over the query heads that share it.
+
+Large sequences are processed in blocks of whole rows, so a block holds
+complete rows of S and nothing is reordered within a row.
+"""
+from __future__ import annotations
+
+from typing import Dict, Iterable, List, Optional, Sequence, Tuple
+
+import numpy as np
+
+_BLOCK_ELEMS = 1 << 25   # at most 32 Mi score entries (256 MiB) per row block
+
+
+def _segments(T: int, cu_seqlens) -> List[Tuple[int, int]]:
+    if cu_seqlens is None:
+        return [(0, T)]
+    cu = [int(x) for x in np.asarray(cu_seqlens)]
+    return [(cu[i], cu[i + 1]) for i in range(len(cu) - 1)]
+
+
+def _f64(x) -> np.ndarray:
+    if hasattr(x, "detach"):          # a torch tensor: exact upcast of fp16/bf16
+        x = x.detach().cpu().double().numpy()
+    return np.asarray(x, dtype=np.float64)
+
+
+def _group(Hq: int, Hkv: int) -> int:
+    if Hkv <= 0 or Hq % Hkv:
+        raise ValueError(f"Hq={Hq} must be a positive multiple of Hkv={Hkv}")
+    return Hq // Hkv
+
+
+def _scores(Qr: np.ndarray, rows: np.ndarray, Ks: np.ndarray, scale: float,
+            causal: bool) -> np.ndarray:
+    """S for the query rows ``rows`` (positions in the sequence) against all keys."""
+    S = scale * (Qr @ Ks.T)
+    if causal:
+        keys = np.arange(Ks.shape[0])[None, :]
+        S = np.where(keys <= rows[:, None], S, -np.inf)
+    return S
+
+
+def _lse(S: np.ndarray) -> np.ndarray:
+    m = S.max(axis=1)
+    return m + np.log(np.exp(S - m[:, None]).sum(axis=1))
+
+
+def _row_blocks(rows: np.ndarray, L: int):
+    step = max(1, _BLOCK_ELEMS // max(L, 1))
+    for a in range(0, len(rows), step):
+        yield rows[a:a + step]
+
+
+def head_fwd(Qs, Ks, Vs, scale: float, causal: bool, rows=None):
+    """One (sequence, query head): O [R, d] and LSE [R] for ``rows`` (default all)."""
+    Qs, Ks, Vs = _f64(Qs), _f64(Ks), _f64(Vs)
+    L = Ks.shape[0]
+    rows = np.arange(Qs.shape[0]) if rows is None else np.asarray(rows, dtype=np.int64)
+    O = np.empty((len(rows), Vs.shape[1]))
+    lse = np.empty(len(rows))
+    pos = 0
+    for blk in _row_blocks(rows, L):
+        S = _scores(Qs[blk], blk, Ks, scale, causal)
+        l = _lse(S)
+        P = np.exp(S - l[:, None])
+        O[pos:pos + len(blk)] = P @ Vs
+        lse[pos:pos + len(blk)] = l
+        pos += len(blk)
+    return O, lse
+
+
+def head_bwd(Qs, Ks, Vs, dOs, scale: float, causal: bool):
+    """One (sequence, query head): dQ, dK, dV [L, d] by the chain rule above."""
+    Qs, Ks, Vs, dOs = _f64(Qs), _f64(Ks), _f64(Vs), _f64(dOs)
+    L = Qs.shape[0]
+    dQ = np.empty_like(Qs)
+    dK = np.zeros_like(Ks)
+    dV = np.zeros_like(Vs)
+    for blk in _row_blocks(np.arange(L), L):
+        S = _scores(Qs[blk], blk, Ks, scale, causal)
+        P = np.exp(S - _lse(S)[:, None])
+        dO = dOs[blk]
+        dV += P.T @ dO
+        dP = dO @ Vs.T
+        D = (P * dP).sum(axis=1)
+        dS = P * (dP - D[:, None])
+        dQ[blk] = scale * (dS @ Ks)
+        dK += scale * (dS.T @ Qs[blk])
+    return dQ, dK, dV
+
+
+def attention_probs(Qs, Ks, scale: float, causal: bool) -> np.ndarray:
+    """The full softmax matrix P [L, L] of one (sequence, head)."""
+    Qs, Ks = _f64(Qs), _f64(Ks)
+    S = _scores(Qs, np.arange(Qs.shape[0]), Ks, scale, causal)
+    return np.exp(S - _lse(S)[:, None])
+
+
+def attention_fwd(q, k, v, scale: float, causal: bool = False, cu_seqlens=None):
+    """Whole-tensor forward.
+
+    q [T, Hq, d], k/v [T, Hkv, d] (any float type; upcast exactly to float64);
+    cu_seqlens: B+1 prefix sums of sequence lengths, or None for one sequence.
+    Returns o [T, Hq, d] and lse [Hq, T], float64.
+    """
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    T, Hq, d = q.shape
+    g = _group(Hq, k.shape[1])
+    o = np.zeros((T, Hq, v.shape[2]))
+    lse = np.zeros((Hq, T))
+    for a, b in _segments(T, cu_seqlens):
+        if b <= a:
+            continue
+        for h in range(Hq):
+            O, l = head_fwd(q[a:b, h], k[a:b, h // g], v[a:b, h // g], scale, causal)
+            o[a:b, h] = O
+            lse[h, a:b] = l
+    return o, lse
+
+
+def attention_fwd_rows(q, k, v, scale: float, causal: bool, cu_seqlens, seq: int,
+                       head: int, rows: Sequence[int]):
+    """O and LSE of selected query rows (positions inside sequence ``seq``) of one head."""
+    q, k, v = _seq_head_views(q, k, v, cu_seqlens, seq, head)
+    return head_fwd(q, k, v, scale, causal, rows=np.asarray(rows))
+
+
+def _seq_head_views(q, k, v, cu_seqlens, seq, head):
+    T, Hq = q.shape[0], q.shape[1]
+    g = _group(Hq, k.shape[1])
+    a, b = _segments(T, cu_seqlens)[seq]
+    return q[a:b, head], k[a:b, head // g], v[a:b, head // g]
+
+
+def attention_bwd(q, k, v, do, scale: float, causal: bool = False, cu_seqlens=None):
+    """Whole-tensor backward: dq [T, Hq, d], dk/dv [T, Hkv, d] in float64."""
+    q, k, v, do = _f64(q), _f64(k), _f64(v), _f64(do)
+    T, Hq, d = q.shape
+    g = _group(Hq, k.shape[1])
+    dq = np.zeros_like(q)
+    dk = np.zeros_like(k)
+    dv = np.zeros_like(v)
+    for a, b in _segments(T, cu_seqlens):
+        if b <= a:
+            continue
+        for h in range(Hq):
+            dQ, dK, dV = head_bwd(q[a:b, h], k[a:b, h // g], v[a:b, h // g], do[a:b, h],
+                                  scale, causal)
+            dq[a:b, h] = dQ
+            dk[a:b, h // g] += dK
+            dv[a:b, h // g] += dV
+    return dq, dk, dv
+
+
+def attention_bwd_sampled(q, k, v, do, scale: float, causal: bool, cu_seqlens,
+                          units: Iterable[Tuple[int, int]]) -> Dict[Tuple[int, int], tuple]:
+    """Backward of selected (sequence, KV head) units only.
+
+    Returns {(seq, kv_head): (dq [L, g, d], dk [L, d], dv [L, d])}, where the
+    g query heads are those sharing the KV head. Inputs may be torch tensors;
+    only the selected slices are upcast.
+    """
+    T, Hq = q.shape[0], q.shape[1]
+    g = _group(Hq, k.shape[1])
+    segs = _segments(T, cu_seqlens)
+    res = {}
+    for s, kvh in units:
+        a, b = segs[s]
+        Ks, Vs = _f64(k[a:b, kvh]), _f64(v[a:b, kvh])
+        dq = np.zeros((b - a, g, Ks.shape[1]))
+        dk = np.zeros_like(Ks)
+        dv = np.zeros_like(Vs)
+        for r in range(g):
+            h = kvh * g + r
+            dQ, dK, dV = head_bwd(q[a:b, h], Ks, Vs, do[a:b, h], scale, causal)
+            dq[:, r] = dQ
+            dk += dK
+            dv += dV
+        res[(s, kvh)] = (dq, dk, dv)
+    return res

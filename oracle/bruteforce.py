@@ -1,0 +1,83 @@
+"""Pure-Python attention for tiny shapes: explicit loops, math.exp, math.fsum.
+
+Test infrastructure only. Written independently of the NumPy oracle (no
+NumPy, no shared helpers) so that the two can pin each other on tiny cases.
+Inputs are nested lists q[t][h][c], k[t][g][c], v[t][g][c] (t = packed token,
+h/g = head, c = feature); ``seqs`` lists (start, end) token ranges.
+
+Definition followed: the attention formula of the FlashAttention guide
+(cxbdf.cn, part 1), softmax along each query row, with the causal and
+padding-free visibility rules; the backward is the chain rule of that formula.
+"""
+from __future__ import annotations
+
+import math
+
+
+def _dot(a, b):
+    return math.fsum(x * y for x, y in zip(a, b))
+
+
+def _visible(i, L, causal):
+    return range(0, i + 1) if causal else range(0, L)
+
+
+def forward(q, k, v, scale, causal, seqs):
+    Hq, Hkv = len(q[0]), len(k[0])
+    grp = Hq // Hkv
+    o = [[None] * Hq for _ in q]
+    lse = [[None] * len(q) for _ in range(Hq)]
+    for (a, b) in seqs:
+        L = b - a
+        for h in range(Hq):
+            g = h // grp
+            for i in range(L):
+                js = list(_visible(i, L, causal))
+                s = [scale * _dot(q[a + i][h], k[a + j][g]) for j in js]
+                m = max(s)
+                lsum = math.log(math.fsum(math.exp(x - m) for x in s)) + m
+                p = [math.exp(x - lsum) for x in s]
+                dv = len(v[0][0])
+                o[a + i][h] = [math.fsum(p[n] * v[a + j][g][c] for n, j in enumerate(js))
+                               for c in range(dv)]
+                lse[h][a + i] = lsum
+    return o, lse
+
+
+def backward(q, k, v, do, scale, causal, seqs):
+    Hq, Hkv = len(q[0]), len(k[0])
+    grp = Hq // Hkv
+    d = len(q[0][0])
+    dv_ = len(v[0][0])
+    dq = [[[0.0] * d for _ in range(Hq)] for _ in q]
+    dk = [[[0.0] * d for _ in range(Hkv)] for _ in k]
+    dvv = [[[0.0] * dv_ for _ in range(Hkv)] for _ in v]
+    for (a, b) in seqs:
+        L = b - a
+        for h in range(Hq):
+            g = h // grp
+            # P and dP for the whole (sequence, head), then the sums term by term
+            P = [[0.0] * L for _ in range(L)]
+            dP = [[0.0] * L for _ in range(L)]
+            for i in range(L):
+                js = list(_visible(i, L, causal))
+                s = [scale * _dot(q[a + i][h], k[a + j][g]) for j in js]
+                m = max(s)
+                lsum = math.log(math.fsum(math.exp(x - m) for x in s)) + m
+                for n, j in enumerate(js):
+                    P[i][j] = math.exp(s[n] - lsum)
+                    dP[i][j] = _dot(do[a + i][h], v[a + j][g])
+            D = [math.fsum(P[i][j] * dP[i][j] for j in range(L)) for i in range(L)]
+            dS = [[P[i][j] * (dP[i][j] - D[i]) for j in range(L)] for i in range(L)]
+            for i in range(L):
+                for c in range(d):
+                    dq[a + i][h][c] = scale * math.fsum(dS[i][j] * k[a + j][g][c]
+                                                        for j in range(L))
+            for j in range(L):
+                for c in range(d):
+                    dk[a + j][g][c] += scale * math.fsum(dS[i][j] * q[a + i][h][c]
+                                                         for i in range(L))
+                for c in range(dv_):
+                    dvv[a + j][g][c] += math.fsum(P[i][j] * do[a + i][h][c]
+                                                  for i in range(L))
+    return dq, dk, dvv

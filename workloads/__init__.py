@@ -1,0 +1,169 @@
+"""Seeded synthetic inputs for the attention workloads.
+
+This module is shared by the oracle tests, the GPU parity tests and the
+benchmark. It only draws random numbers and describes shapes; it holds none
+of the attention arithmetic, so neither side of a parity check can borrow a
+computation from the other through it.
+
+The workloads are the ones the pages time: random normal fp16/bf16 Q, K, V
+tensors in the (batch, seq, heads, head_dim) order of the ``flash_attn_func``
+example (Llama-Factory page, first code sample) and the N sweep
+{512 … 8192} at batch 4, 32 heads, head_dim 128 of the A/B harness
+(mlqm.cn evaluation page, section 三). Two further workloads use the
+Llama-3-8B head shape (32 query heads sharing 8 KV heads) over a padding-free
+packed batch, and a 16k-token causal training step.
+
+Recipe (one generator per workload, NumPy PCG64):
+  1. ``rng = numpy.random.default_rng(seed)``
+  2. varlen only: ``lens = rng.integers(1024, 8192, size=8, endpoint=True)``
+  3. Q, K, V, then dO, each ``rng.standard_normal(shape, dtype=float32)``
+     with shapes [T, Hq, d] / [T, Hkv, d] / [T, Hkv, d] / [T, Hq, d]
+  4. the caller rounds to fp16 / bf16 (round to nearest even).
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+from typing import Dict, List, Optional
+
+import numpy as np
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    name: str
+    B: int
+    Hq: int
+    Hkv: int
+    N: int            # fixed length, or the longest sequence for varlen
+    d: int
+    dtype: str        # "fp16" | "bf16"
+    causal: bool
+    seed: int
+    varlen: bool = False
+    backward: bool = False
+    lens: Optional[tuple] = None   # varlen sequence lengths
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / math.sqrt(self.d)
+
+    @property
+    def seq_lens(self) -> List[int]:
+        if self.varlen:
+            return list(self.lens)
+        return [self.N] * self.B
+
+    @property
+    def T(self) -> int:
+        return int(sum(self.seq_lens))
+
+    def cu_seqlens(self) -> np.ndarray:
+        return np.concatenate([[0], np.cumsum(self.seq_lens)]).astype(np.int32)
+
+    def fwd_flop(self) -> float:
+        """4·Hq·L²·d per sequence, halved when causal (the metric's convention)."""
+        f = sum(4.0 * self.Hq * L * L * self.d for L in self.seq_lens)
+        return f / 2 if self.causal else f
+
+    def bwd_flop(self) -> float:
+        return 2.5 * self.fwd_flop()
+
+    def fwd_bytes(self) -> int:
+        """Compulsory HBM bytes of the forward: read Q, K, V once, write O and LSE."""
+        e = 2
+        T = self.T
+        return (2 * T * self.Hq * self.d * e          # Q in, O out
+                + 2 * T * self.Hkv * self.d * e       # K, V in
+                + 4 * T * self.Hq)                    # LSE out
+
+    def bwd_bytes(self) -> int:
+        """Read Q, K, V, O, dO, LSE; write dQ, dK, dV (plus the fp32 D row)."""
+        e = 2
+        T = self.T
+        return (4 * T * self.Hq * self.d * e          # Q, O, dO in, dQ out
+                + 4 * T * self.Hkv * self.d * e       # K, V in, dK, dV out
+                + 4 * T * self.Hq * 2)                # LSE in, D out
+
+
+def varlen_lengths(seed: int, count: int = 8, lo: int = 1024, hi: int = 8192) -> List[int]:
+    rng = np.random.default_rng(seed)
+    return [int(x) for x in rng.integers(lo, hi, size=count, endpoint=True)]
+
+
+def _sweep(N: int, causal: bool) -> Workload:
+    return Workload(f"sweep_N{N}_{'causal' if causal else 'full'}", B=4, Hq=32, Hkv=32,
+                    N=N, d=128, dtype="fp16", causal=causal, seed=3)
+
+
+def _build() -> Dict[str, Workload]:
+    w = {
+        "tiny": Workload("tiny", B=1, Hq=2, Hkv=2, N=128, d=64, dtype="fp16",
+                         causal=False, seed=1),
+        "causal_d64": Workload("causal_d64", B=1, Hq=16, Hkv=16, N=2048, d=64,
+                               dtype="fp16", causal=True, seed=2),
+    }
+    for N in (512, 1024, 2048, 4096, 8192):
+        for c in (False, True):
+            s = _sweep(N, c)
+            w[s.name] = s
+    lens = tuple(varlen_lengths(4))
+    w["gqa_varlen"] = Workload("gqa_varlen", B=len(lens), Hq=32, Hkv=8, N=max(lens), d=128,
+                               dtype="bf16", causal=True, seed=4, varlen=True, lens=lens)
+    w["train_16k"] = Workload("train_16k", B=2, Hq=16, Hkv=16, N=16384, d=128, dtype="bf16",
+                              causal=True, seed=5, backward=True)
+    return w
+
+
+WORKLOADS: Dict[str, Workload] = _build()
+
+
+def custom(B, Hq, Hkv, N, d, dtype="fp16", causal=False, seed=0, lens=None,
+           backward=False) -> Workload:
+    """A workload of any shape (used for small parity cases and edge cases)."""
+    if lens is not None:
+        lens = tuple(int(x) for x in lens)
+        return Workload(f"custom_varlen", B=len(lens), Hq=Hq, Hkv=Hkv,
+                        N=max(lens) if lens else 0, d=d, dtype=dtype, causal=causal,
+                        seed=seed, varlen=True, lens=lens, backward=backward)
+    return Workload("custom", B=B, Hq=Hq, Hkv=Hkv, N=N, d=d, dtype=dtype, causal=causal,
+                    seed=seed, backward=backward)
+
+
+def generate(w: Workload, with_grad: Optional[bool] = None):
+    """Draw float32 Q, K, V (and dO) for a workload, in the recipe's order.
+
+    Returns a dict of NumPy float32 arrays with token-major shapes
+    q [T, Hq, d], k/v [T, Hkv, d], do [T, Hq, d] and cu_seqlens int32 [B+1].
+    A varlen workload whose lengths are drawn (``lens`` from
+    :func:`varlen_lengths`) consumes the same generator stream first.
+    """
+    if with_grad is None:
+        with_grad = w.backward
+    rng = np.random.default_rng(w.seed)
+    if w.varlen and w.name == "gqa_varlen":
+        drawn = rng.integers(1024, 8192, size=8, endpoint=True)
+        assert tuple(int(x) for x in drawn) == tuple(w.lens)
+    T = w.T
+    out = {
+        "q": rng.standard_normal((T, w.Hq, w.d), dtype=np.float32),
+        "k": rng.standard_normal((T, w.Hkv, w.d), dtype=np.float32),
+        "v": rng.standard_normal((T, w.Hkv, w.d), dtype=np.float32),
+    }
+    if with_grad:
+        out["do"] = rng.standard_normal((T, w.Hq, w.d), dtype=np.float32)
+    out["cu_seqlens"] = w.cu_seqlens()
+    return out
+
+
+def to_torch(arrays, dtype: str, device="cpu"):
+    """Round float32 arrays to fp16/bf16 (nearest even) as torch tensors."""
+    import torch
+    td = {"fp16": torch.float16, "bf16": torch.bfloat16}[dtype]
+    res = {}
+    for name, a in arrays.items():
+        if name == "cu_seqlens":
+            res[name] = torch.from_numpy(a).to(device)
+        else:
+            res[name] = torch.from_numpy(a).to(td).to(device)
+    return res
