@@ -1,0 +1,176 @@
+"""Python binding of libfa.so: exact fused attention on MI355X (gfx950).
+
+Argument marshalling only. Every step of the computation runs in the HIP
+kernels of libfa.so; torch supplies device memory and the current stream.
+If the library has not been built, importing the binding raises: there is no
+fallback implementation.
+
+Raw entry points with the C names and arguments (pointers as ints):
+    fa_fwd, fa_bwd, fa_bwd_workspace_size, fa_status_string
+Tensor-level helpers:
+    flash_attn_func(q, k, v, causal=False, softmax_scale=None,
+                    cu_seqlens=None, max_seqlen=None, dropout_p=0.0) -> (o, lse)
+    flash_attn_backward(dout, q, k, v, o, lse, causal=False, softmax_scale=None,
+                        cu_seqlens=None, max_seqlen=None) -> (dq, dk, dv)
+The call shape follows flash_attn_func in the pages' examples (Llama-Factory
+page, first code sample: q, k, v as (batch, seq, heads, head_dim), causal flag;
+FlashAttention-2 全解析, blog.gitcode.com: dropout_p and softmax_scale).
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+__all__ = ["FA_OK", "FA_ERR_INVALID_ARG", "FA_ERR_UNSUPPORTED", "FA_ERR_HIP", "FA_ERR_WORKSPACE",
+           "FA_FP16", "FA_BF16", "FaError", "lib", "lib_path", "fa_fwd", "fa_bwd",
+           "fa_bwd_workspace_size", "fa_status_string", "flash_attn_func",
+           "flash_attn_backward"]
+
+FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_HIP, FA_ERR_WORKSPACE = 0, -1, -2, -3, -4
+FA_FP16, FA_BF16 = 0, 1
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+
+
+def lib_path() -> str:
+    return os.path.join(_HERE, "libfa.so")
+
+
+class FaError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {fa_status_string(status)} ({status})")
+
+
+def _load():
+    path = lib_path()
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is missing: build it with `python -m exact_io_aware_12_amd.build` "
+                          "(there is no non-HIP fallback)")
+    L = ctypes.CDLL(path)
+    vp, i, f, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    L.fa_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp, i, vp]
+    L.fa_fwd.restype = i
+    L.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp, i, vp, sz, vp]
+    L.fa_bwd.restype = i
+    L.fa_bwd_workspace_size.argtypes = [i, i, i, i, i]
+    L.fa_bwd_workspace_size.restype = sz
+    L.fa_status_string.argtypes = [i]
+    L.fa_status_string.restype = ctypes.c_char_p
+    return L
+
+
+lib = _load()
+
+
+# ---- raw C entry points ------------------------------------------------------
+def fa_fwd(q, k, v, o, lse, B, Hq, Hkv, N, d, scale, causal, cu_seqlens, dtype, stream) -> int:
+    return lib.fa_fwd(q, k, v, o, lse, B, Hq, Hkv, N, d, scale, causal, cu_seqlens, dtype, stream)
+
+
+def fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, B, Hq, Hkv, N, d, scale, causal, cu_seqlens, dtype,
+           workspace, workspace_bytes, stream) -> int:
+    return lib.fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, B, Hq, Hkv, N, d, scale, causal,
+                      cu_seqlens, dtype, workspace, workspace_bytes, stream)
+
+
+def fa_bwd_workspace_size(B, Hq, Hkv, N, d) -> int:
+    return lib.fa_bwd_workspace_size(B, Hq, Hkv, N, d)
+
+
+def fa_status_string(status: int) -> str:
+    return lib.fa_status_string(status).decode()
+
+
+# ---- tensor helpers ----------------------------------------------------------
+def _dtype_code(t):
+    import torch
+    if t.dtype == torch.float16:
+        return FA_FP16
+    if t.dtype == torch.bfloat16:
+        return FA_BF16
+    raise TypeError(f"fa supports float16 and bfloat16 tensors, got {t.dtype}")
+
+
+def _shape(q, k, cu_seqlens, max_seqlen):
+    """(B, N, T, Hq, Hkv, d) from (B, N, H, d) tensors or packed [T, H, d] + cu_seqlens."""
+    if cu_seqlens is None:
+        if q.dim() != 4 or k.dim() != 4:
+            raise ValueError("fixed-length inputs are (batch, seq, heads, head_dim)")
+        B, N, Hq, d = q.shape
+        if k.shape[0] != B or k.shape[1] != N or k.shape[3] != d:
+            raise ValueError(f"q {tuple(q.shape)} and k {tuple(k.shape)} do not match")
+        return B, N, B * N, Hq, k.shape[2], d
+    if q.dim() != 3 or k.dim() != 3:
+        raise ValueError("varlen inputs are packed (total_tokens, heads, head_dim)")
+    if max_seqlen is None:
+        raise ValueError("varlen needs max_seqlen (the longest sequence)")
+    T, Hq, d = q.shape
+    if k.shape[0] != T or k.shape[2] != d:
+        raise ValueError(f"q {tuple(q.shape)} and k {tuple(k.shape)} do not match")
+    return cu_seqlens.numel() - 1, int(max_seqlen), T, Hq, k.shape[1], d
+
+
+def _check_dev(*ts):
+    for t in ts:
+        if not t.is_cuda:
+            raise ValueError("fa tensors must be on the GPU")
+        if not t.is_contiguous():
+            raise ValueError("fa tensors must be contiguous")
+
+
+def _stream():
+    import torch
+    return torch.cuda.current_stream().cuda_stream
+
+
+def flash_attn_func(q, k, v, causal=False, softmax_scale=None, cu_seqlens=None, max_seqlen=None,
+                    dropout_p=0.0):
+    """Forward. Returns (o, lse); lse is float32 [Hq, T] (natural log)."""
+    import torch
+    if dropout_p != 0.0:
+        raise NotImplementedError("dropout is not implemented (dropout_p must be 0.0)")
+    B, N, T, Hq, Hkv, d = _shape(q, k, cu_seqlens, max_seqlen)
+    if v.shape != k.shape:
+        raise ValueError("k and v must have the same shape")
+    if not (q.dtype == k.dtype == v.dtype):
+        raise TypeError("q, k, v must share one dtype")
+    _check_dev(q, k, v)
+    if cu_seqlens is not None:
+        _check_dev(cu_seqlens)
+        if cu_seqlens.dtype != torch.int32:
+            raise TypeError("cu_seqlens must be int32")
+    scale = softmax_scale if softmax_scale is not None else 1.0 / math.sqrt(d)
+    o = torch.empty_like(q)
+    lse = torch.empty((Hq, T), dtype=torch.float32, device=q.device)
+    st = lib.fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                    B, Hq, Hkv, N, d, float(scale), int(bool(causal)),
+                    cu_seqlens.data_ptr() if cu_seqlens is not None else None,
+                    _dtype_code(q), _stream())
+    if st != FA_OK:
+        raise FaError(st, "fa_fwd")
+    return o, lse
+
+
+def flash_attn_backward(dout, q, k, v, o, lse, causal=False, softmax_scale=None, cu_seqlens=None,
+                        max_seqlen=None, workspace=None):
+    """Backward. Returns (dq, dk, dv) shaped like q, k, v."""
+    import torch
+    B, N, T, Hq, Hkv, d = _shape(q, k, cu_seqlens, max_seqlen)
+    _check_dev(dout, q, k, v, o, lse)
+    if cu_seqlens is not None:
+        _check_dev(cu_seqlens)
+    scale = softmax_scale if softmax_scale is not None else 1.0 / math.sqrt(d)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    need = fa_bwd_workspace_size(B, Hq, Hkv, N, d)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    st = lib.fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(),
+                    lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
+                    B, Hq, Hkv, N, d, float(scale), int(bool(causal)),
+                    cu_seqlens.data_ptr() if cu_seqlens is not None else None,
+                    _dtype_code(q), workspace.data_ptr(), workspace.numel(), _stream())
+    if st != FA_OK:
+        raise FaError(st, "fa_bwd")
+    return dq, dk, dv

@@ -1,0 +1,122 @@
+// C ABI of libfa.so (declared in include/fa.h): argument checks, then the
+// kernel launches. Nothing here allocates memory or keeps state.
+#include <cmath>
+#include <cstdint>
+
+#include "../../include/fa.h"
+#include "fa_kernels.h"
+
+namespace {
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+// Checks shared by fa_fwd and fa_bwd that need no pointer. Returns FA_OK or
+// the status to report; *noop is set when there is nothing to compute.
+int check_sizes(int B, int Hq, int Hkv, int N, int d, float scale, int causal, int dtype,
+                bool* noop) {
+  *noop = false;
+  if (dtype != FA_FP16 && dtype != FA_BF16) return FA_ERR_INVALID_ARG;
+  if (B < 0 || N < 0 || Hq <= 0 || Hkv <= 0 || d <= 0) return FA_ERR_INVALID_ARG;
+  if (Hq % Hkv != 0) return FA_ERR_INVALID_ARG;
+  if (causal != 0 && causal != 1) return FA_ERR_INVALID_ARG;
+  if (!std::isfinite(scale) || !(scale > 0.f)) return FA_ERR_INVALID_ARG;
+  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+  // token and grid indices are 32-bit inside the kernels
+  const int64_t T = (int64_t)B * N;
+  if (T >= (int64_t)1 << 31 || T * Hq >= (int64_t)1 << 31) return FA_ERR_UNSUPPORTED;
+  if (B == 0 || N == 0) *noop = true;
+  return FA_OK;
+}
+
+// The kernels move 16-byte vectors; device pointers must be 16-byte aligned.
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+}  // namespace
+
+extern "C" {
+
+int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq,
+           int Hkv, int N, int d, float scale, int causal, const int32_t* cu_seqlens, int dtype,
+           hipStream_t stream) {
+  bool noop;
+  int st = check_sizes(B, Hq, Hkv, N, d, scale, causal, dtype, &noop);
+  if (st != FA_OK || noop) return st;
+  if (!q || !k || !v || !o || !lse) return FA_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse))
+    return FA_ERR_INVALID_ARG;
+  fa::FwdArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.lse = lse;
+  a.cu_seqlens = cu_seqlens;
+  a.B = B;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.N = N;
+  a.group = Hq / Hkv;
+  const int br = fa::fwd_query_tile();
+  a.n_qtiles = (N + br - 1) / br;
+  a.scale_log2 = scale * kLog2e;
+  if ((int64_t)a.n_qtiles * Hq * B >= (int64_t)1 << 31) return FA_ERR_UNSUPPORTED;
+  hipError_t e = fa::launch_fwd(a, dtype == FA_BF16, d, causal != 0, cu_seqlens != nullptr, stream);
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+size_t fa_bwd_workspace_size(int B, int Hq, int Hkv, int N, int d) {
+  bool noop;
+  if (check_sizes(B, Hq, Hkv, N, d, 1.f, 0, FA_FP16, &noop) != FA_OK) return 0;
+  // D = rowsum(dO∘O): float32 [Hq, T], T <= B·N; 256-byte granule
+  const size_t bytes = (size_t)B * N * Hq * sizeof(float);
+  return (bytes + 255) / 256 * 256;
+}
+
+int fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+           const float* lse, void* dq, void* dk, void* dv, int B, int Hq, int Hkv, int N, int d,
+           float scale, int causal, const int32_t* cu_seqlens, int dtype, void* workspace,
+           size_t workspace_bytes, hipStream_t stream) {
+  bool noop;
+  int st = check_sizes(B, Hq, Hkv, N, d, scale, causal, dtype, &noop);
+  if (st != FA_OK || noop) return st;
+  if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv) return FA_ERR_INVALID_ARG;
+  const void* ptrs[] = {q, k, v, o, dout, lse, dq, dk, dv, workspace};
+  for (const void* p : ptrs)
+    if (p && !aligned16(p)) return FA_ERR_INVALID_ARG;
+  if (!workspace || workspace_bytes < fa_bwd_workspace_size(B, Hq, Hkv, N, d))
+    return FA_ERR_WORKSPACE;
+  fa::BwdArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.dout = dout;
+  a.lse = lse;
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  a.delta = static_cast<float*>(workspace);
+  a.cu_seqlens = cu_seqlens;
+  a.B = B;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.N = N;
+  a.group = Hq / Hkv;
+  a.scale = scale;
+  a.scale_log2 = scale * kLog2e;
+  hipError_t e = fa::launch_bwd(a, dtype == FA_BF16, d, causal != 0, cu_seqlens != nullptr, stream);
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+const char* fa_status_string(int status) {
+  switch (status) {
+    case FA_OK: return "FA_OK: success";
+    case FA_ERR_INVALID_ARG: return "FA_ERR_INVALID_ARG: invalid argument";
+    case FA_ERR_UNSUPPORTED: return "FA_ERR_UNSUPPORTED: outside the supported envelope";
+    case FA_ERR_HIP: return "FA_ERR_HIP: the HIP runtime refused the launch";
+    case FA_ERR_WORKSPACE: return "FA_ERR_WORKSPACE: workspace missing or too small";
+    default: return "unknown fa status";
+  }
+}
+
+}  // extern "C"

@@ -1,0 +1,378 @@
+// Fused attention backward for gfx950.
+//
+// The probabilities are never stored: each kernel recomputes S from Q and K
+// tiles and P = exp(S·scale − LSE) from the forward's row log-sum-exp
+// (recomputation in the backward pass, FlashAttention guide, cxbdf.cn,
+// part 2, item 3). With dP = dO·Vᵀ and D_i = rowsum(dO∘O) (equal to
+// Σ_j P_ij·dP_ij because O_i = Σ_j P_ij·V_j):
+//   dS = P∘(dP − D),  dV = Pᵀ·dO,  dK = scale·dSᵀ·Q,  dQ = scale·dS·K.
+//
+// Three kernels on one stream, all deterministic (fixed summation order):
+//   delta_kernel  D = rowsum(dO∘O) in float32                       (HBM bound)
+//   dkdv_kernel   one workgroup per 128-key tile of one KV head; loops over
+//                 the query heads of its group and the visible 64-query
+//                 tiles; dKᵀ and dVᵀ accumulate in registers
+//   dq_kernel     one workgroup per 128-query tile of one query head; loops
+//                 over the visible 64-key tiles; dQᵀ accumulates in registers
+#include "fa_device.h"
+#include "fa_kernels.h"
+
+namespace fa {
+
+namespace {
+
+constexpr int kThreads = 256;
+
+struct SeqInfo {
+  int seq0, L, T;
+};
+
+template <bool VARLEN>
+__device__ __forceinline__ SeqInfo seq_info(const BwdArgs& a, int b) {
+  if constexpr (VARLEN) {
+    const int s0 = a.cu_seqlens[b];
+    return {s0, a.cu_seqlens[b + 1] - s0, a.cu_seqlens[a.B]};
+  } else {
+    return {b * a.N, a.N, a.B * a.N};
+  }
+}
+
+template <typename T>
+__device__ __forceinline__ float lo_f(uint32_t w) {
+  if constexpr (__is_same(T, bf16)) return __uint_as_float(w << 16);
+  else return (float)__builtin_bit_cast(f16, (uint16_t)(w & 0xffffu));
+}
+template <typename T>
+__device__ __forceinline__ float hi_f(uint32_t w) {
+  if constexpr (__is_same(T, bf16)) return __uint_as_float(w & 0xffff0000u);
+  else return (float)__builtin_bit_cast(f16, (uint16_t)(w >> 16));
+}
+
+// ---------------------------------------------------------------------------
+// D_i = Σ_c dO[i,c]·O[i,c]; D/8 consecutive threads share one (token, head) row.
+template <typename T, int D, bool VARLEN>
+__global__ __launch_bounds__(kThreads) void delta_kernel(BwdArgs a) {
+  constexpr int TPR = D / 8;
+  const int T_total = VARLEN ? a.cu_seqlens[a.B] : a.B * a.N;
+  const int64_t rows = (int64_t)T_total * a.Hq;
+  const int64_t row = (int64_t)blockIdx.x * (kThreads / TPR) + threadIdx.x / TPR;
+  const int part = threadIdx.x % TPR;
+  float acc = 0.f;
+  if (row < rows) {
+    const u32x4 x = ldg16(static_cast<const T*>(a.dout) + row * D + part * 8);
+    const u32x4 y = ldg16(static_cast<const T*>(a.o) + row * D + part * 8);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      acc = fmaf(lo_f<T>(x[i]), lo_f<T>(y[i]), acc);
+      acc = fmaf(hi_f<T>(x[i]), hi_f<T>(y[i]), acc);
+    }
+  }
+#pragma unroll
+  for (int off = TPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
+  if (row < rows && part == 0) {
+    const int t = (int)(row / a.Hq), h = (int)(row % a.Hq);
+    a.delta[(int64_t)h * T_total + t] = acc;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// dK, dV. Orientation S = Q·Kᵀ with the wave's 32 keys as MFMA columns, so the
+// accumulators of P and dS have one key per lane and 16 queries in registers,
+// which is exactly the B-operand layout dVᵀ = dOᵀ·P and dKᵀ = Qᵀ·dS need.
+constexpr int kDkvKeys = 128;   // keys per workgroup (32 per wave)
+constexpr int kDkvQ = 64;       // queries per inner tile
+
+template <typename T, int D, bool CAUSAL, bool VARLEN>
+__global__ __launch_bounds__(kThreads, 1) void dkdv_kernel(BwdArgs a, int n_ktiles) {
+  constexpr int RS = D + 8;        // row-major tile stride (elements)
+  constexpr int TS = kDkvQ + 8;    // transposed tile stride (elements)
+  constexpr int NKB = D / 16;
+  constexpr int NCB = D / 32;
+  __shared__ __attribute__((aligned(16))) T q_lds[kDkvQ * RS];
+  __shared__ __attribute__((aligned(16))) T do_lds[kDkvQ * RS];
+  __shared__ __attribute__((aligned(16))) T qt_lds[D * TS];
+  __shared__ __attribute__((aligned(16))) T dot_lds[D * TS];
+  __shared__ __attribute__((aligned(16))) float lse_lds[kDkvQ];   // LSE·log2 e
+  __shared__ __attribute__((aligned(16))) float dl_lds[kDkvQ];    // D
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int col = lane & 31, half = lane >> 5;
+
+  const int G = gridDim.x;
+  const int logical = xcd_remap(blockIdx.x, G);
+  const int kt = logical % n_ktiles;           // ascending = heaviest first when causal
+  const int gb = logical / n_ktiles;
+  const int g = gb % a.Hkv, b = gb / a.Hkv;
+  const SeqInfo si = seq_info<VARLEN>(a, b);
+  const int k0 = kt * kDkvKeys;
+  if (k0 >= si.L) return;
+  const int L = si.L;
+
+  const int64_t qs = (int64_t)a.Hq * D, kvs = (int64_t)a.Hkv * D;
+  const int key = k0 + wave * 32 + col;
+  // K and V fragments of this wave's 32 keys (B operands), kept in registers
+  u32x4 kf[NKB], vf[NKB];
+  {
+    const T* kp = static_cast<const T*>(a.k) + (int64_t)(si.seq0 + key) * kvs + (int64_t)g * D;
+    const T* vp = static_cast<const T*>(a.v) + (int64_t)(si.seq0 + key) * kvs + (int64_t)g * D;
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) {
+      kf[kb] = key < L ? ldg16(kp + kb * 16 + half * 8) : u32x4{0, 0, 0, 0};
+      vf[kb] = key < L ? ldg16(vp + kb * 16 + half * 8) : u32x4{0, 0, 0, 0};
+    }
+  }
+  f32x16 dkt[NCB], dvt[NCB];
+#pragma unroll
+  for (int cb = 0; cb < NCB; ++cb) {
+    dkt[cb] = f32x16{};
+    dvt[cb] = f32x16{};
+  }
+  const float c = a.scale_log2;
+  const int wk_first = k0 + wave * 32, wk_last = wk_first + 31;
+  const int qt_begin = CAUSAL ? k0 / kDkvQ : 0;
+  const int nqt = (L + kDkvQ - 1) / kDkvQ;
+
+  for (int r = 0; r < a.group; ++r) {
+    const int h = g * a.group + r;
+    const T* qp = static_cast<const T*>(a.q) + (int64_t)si.seq0 * qs + (int64_t)h * D;
+    const T* dop = static_cast<const T*>(a.dout) + (int64_t)si.seq0 * qs + (int64_t)h * D;
+    const float* lsep = a.lse + (int64_t)h * si.T + si.seq0;
+    const float* dlp = a.delta + (int64_t)h * si.T + si.seq0;
+
+    for (int qt = qt_begin; qt < nqt; ++qt) {
+      const int q0 = qt * kDkvQ;
+      __syncthreads();
+      tile_to_lds_t<T, kDkvQ, D, TS, kThreads, true, RS>(qt_lds, q_lds, qp, qs, q0, L, tid);
+      tile_to_lds_t<T, kDkvQ, D, TS, kThreads, true, RS>(dot_lds, do_lds, dop, qs, q0, L, tid);
+      if (tid < kDkvQ) {
+        const int qi = q0 + tid;
+        lse_lds[tid] = qi < L ? lsep[qi] * kLog2e : INFINITY;   // P = 0 past the end
+        dl_lds[tid] = qi < L ? dlp[qi] : 0.f;
+      }
+      __syncthreads();
+      if (CAUSAL && q0 + kDkvQ - 1 < wk_first) continue;   // all queries before this wave's keys
+
+      // S = Q·Kᵀ and dP = dO·Vᵀ: 2 blocks of 32 queries each
+      f32x16 s[2] = {f32x16{}, f32x16{}}, dp[2] = {f32x16{}, f32x16{}};
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) {
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) {
+          const u32x4 qa = lds16(q_lds + (qb * 32 + col) * RS + kb * 16 + half * 8);
+          s[qb] = mfma32<T>(qa, kf[kb], s[qb]);
+          const u32x4 da = lds16(do_lds + (qb * 32 + col) * RS + kb * 16 + half * 8);
+          dp[qb] = mfma32<T>(da, vf[kb], dp[qb]);
+        }
+      }
+      // P = exp2(S·c − LSE·log2 e), dS = P∘(dP − D); causal: key > query → 0
+      const bool edge = CAUSAL && q0 < wk_last;
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+          const int qoff = qb * 32 + 8 * rr + 4 * half;
+          const float4 lv = *reinterpret_cast<const float4*>(lse_lds + qoff);
+          const float4 dv4 = *reinterpret_cast<const float4*>(dl_lds + qoff);
+          const float lsev[4] = {lv.x, lv.y, lv.z, lv.w};
+          const float dlv[4] = {dv4.x, dv4.y, dv4.z, dv4.w};
+#pragma unroll
+          for (int t = 0; t < 4; ++t) {
+            const int i = 4 * rr + t;
+            float p = fast_exp2(fmaf(s[qb][i], c, -lsev[t]));
+            if (edge && key > q0 + qoff + t) p = 0.f;
+            s[qb][i] = p;
+            dp[qb][i] = p * (dp[qb][i] - dlv[t]);
+          }
+        }
+      // dVᵀ += dOᵀ·P and dKᵀ += Qᵀ·dS over the tile's 64 queries
+#pragma unroll
+      for (int kk = 0; kk < kDkvQ / 16; ++kk) {
+        const u32x4 pb = acc_operand<T>(s[kk >> 1], (kk & 1) * 2);
+        const u32x4 sb = acc_operand<T>(dp[kk >> 1], (kk & 1) * 2);
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb) {
+          const u32x4 doa = lds16(dot_lds + (cb * 32 + col) * TS + kk * 16 + half * 8);
+          dvt[cb] = mfma32<T>(doa, pb, dvt[cb]);
+          const u32x4 qa = lds16(qt_lds + (cb * 32 + col) * TS + kk * 16 + half * 8);
+          dkt[cb] = mfma32<T>(qa, sb, dkt[cb]);
+        }
+      }
+    }
+  }
+
+  if (key < L) {
+    const int64_t off = (int64_t)(si.seq0 + key) * kvs + (int64_t)g * D;
+    T* dkp = static_cast<T*>(a.dk) + off;
+    T* dvp = static_cast<T*>(a.dv) + off;
+    const float sc = a.scale;
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        const int d0 = cb * 32 + 8 * rr + 4 * half;
+        u32x2 w;
+        w[0] = pack2<T>(dkt[cb][4 * rr + 0] * sc, dkt[cb][4 * rr + 1] * sc);
+        w[1] = pack2<T>(dkt[cb][4 * rr + 2] * sc, dkt[cb][4 * rr + 3] * sc);
+        *reinterpret_cast<u32x2*>(dkp + d0) = w;
+        w[0] = pack2<T>(dvt[cb][4 * rr + 0], dvt[cb][4 * rr + 1]);
+        w[1] = pack2<T>(dvt[cb][4 * rr + 2], dvt[cb][4 * rr + 3]);
+        *reinterpret_cast<u32x2*>(dvp + d0) = w;
+      }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// dQ. Orientation Sᵀ = K·Qᵀ as in the forward: one query per lane, so LSE and
+// D are per-lane scalars and the dSᵀ accumulator is the B operand of
+// dQᵀ = Kᵀ·dSᵀ (K stored transposed in LDS with the perm16 key order).
+constexpr int kDqQ = 128;   // queries per workgroup (32 per wave)
+constexpr int kDqK = 64;    // keys per tile
+
+template <typename T, int D, bool CAUSAL, bool VARLEN>
+__global__ __launch_bounds__(kThreads, 2) void dq_kernel(BwdArgs a, int n_qtiles) {
+  constexpr int RS = D + 8;
+  constexpr int TS = kDqK + 8;
+  constexpr int NKB = D / 16;
+  constexpr int NCB = D / 32;
+  __shared__ __attribute__((aligned(16))) T k_lds[kDqK * RS];
+  __shared__ __attribute__((aligned(16))) T v_lds[kDqK * RS];
+  __shared__ __attribute__((aligned(16))) T kt_lds[D * TS];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int col = lane & 31, half = lane >> 5;
+
+  const int G = gridDim.x;
+  const int logical = xcd_remap(blockIdx.x, G);
+  const int qt_ord = logical % n_qtiles;
+  const int hb = logical / n_qtiles;
+  const int h = hb % a.Hq, b = hb / a.Hq;
+  const int qt = CAUSAL ? n_qtiles - 1 - qt_ord : qt_ord;
+  const SeqInfo si = seq_info<VARLEN>(a, b);
+  const int q0 = qt * kDqQ;
+  if (q0 >= si.L) return;
+  const int L = si.L;
+  const int g = h / a.group;
+
+  const int64_t qs = (int64_t)a.Hq * D, kvs = (int64_t)a.Hkv * D;
+  const T* kp = static_cast<const T*>(a.k) + (int64_t)si.seq0 * kvs + (int64_t)g * D;
+  const T* vp = static_cast<const T*>(a.v) + (int64_t)si.seq0 * kvs + (int64_t)g * D;
+
+  const int qrow = q0 + wave * 32 + col;
+  u32x4 qf[NKB], df[NKB];
+  float lse2 = INFINITY, dl = 0.f;
+  {
+    const int64_t off = (int64_t)(si.seq0 + qrow) * qs + (int64_t)h * D;
+    const T* qp = static_cast<const T*>(a.q) + off;
+    const T* dop = static_cast<const T*>(a.dout) + off;
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) {
+      qf[kb] = qrow < L ? ldg16(qp + kb * 16 + half * 8) : u32x4{0, 0, 0, 0};
+      df[kb] = qrow < L ? ldg16(dop + kb * 16 + half * 8) : u32x4{0, 0, 0, 0};
+    }
+    if (qrow < L) {
+      lse2 = a.lse[(int64_t)h * si.T + si.seq0 + qrow] * kLog2e;
+      dl = a.delta[(int64_t)h * si.T + si.seq0 + qrow];
+    }
+  }
+  f32x16 dqt[NCB];
+#pragma unroll
+  for (int cb = 0; cb < NCB; ++cb) dqt[cb] = f32x16{};
+  const float c = a.scale_log2;
+  const int kv_end = CAUSAL ? min(L, q0 + kDqQ) : L;
+  const int ntiles = (kv_end + kDqK - 1) / kDqK;
+  const int wq_first = q0 + wave * 32, wq_last = wq_first + 31;
+
+  for (int j = 0; j < ntiles; ++j) {
+    const int kv0 = j * kDqK;
+    __syncthreads();
+    tile_to_lds_t<T, kDqK, D, TS, kThreads, true, RS>(kt_lds, k_lds, kp, kvs, kv0, L, tid);
+    tile_to_lds<T, kDqK, D, RS, kThreads>(v_lds, vp, kvs, kv0, L, tid);
+    __syncthreads();
+    if (CAUSAL && kv0 > wq_last) continue;
+
+    f32x16 s[2] = {f32x16{}, f32x16{}}, dp[2] = {f32x16{}, f32x16{}};
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) {
+#pragma unroll
+      for (int jb = 0; jb < 2; ++jb) {
+        const u32x4 ka = lds16(k_lds + (jb * 32 + col) * RS + kb * 16 + half * 8);
+        s[jb] = mfma32<T>(ka, qf[kb], s[jb]);
+        const u32x4 va = lds16(v_lds + (jb * 32 + col) * RS + kb * 16 + half * 8);
+        dp[jb] = mfma32<T>(va, df[kb], dp[jb]);
+      }
+    }
+    const bool edge = (kv0 + kDqK > L) || (CAUSAL && kv0 + kDqK - 1 > wq_first);
+#pragma unroll
+    for (int jb = 0; jb < 2; ++jb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        float p = fast_exp2(fmaf(s[jb][i], c, -lse2));
+        if (edge) {
+          const int kj = kv0 + jb * 32 + 8 * (i >> 2) + 4 * half + (i & 3);
+          if (kj >= L || (CAUSAL && kj > qrow)) p = 0.f;
+        }
+        dp[jb][i] = p * (dp[jb][i] - dl);
+      }
+#pragma unroll
+    for (int kk = 0; kk < kDqK / 16; ++kk) {
+      const u32x4 sb = acc_operand<T>(dp[kk >> 1], (kk & 1) * 2);
+#pragma unroll
+      for (int cb = 0; cb < NCB; ++cb) {
+        const u32x4 ka = lds16(kt_lds + (cb * 32 + col) * TS + kk * 16 + half * 8);
+        dqt[cb] = mfma32<T>(ka, sb, dqt[cb]);
+      }
+    }
+  }
+
+  if (qrow < L) {
+    T* dqp = static_cast<T*>(a.dq) + (int64_t)(si.seq0 + qrow) * qs + (int64_t)h * D;
+    const float sc = a.scale;
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        u32x2 w;
+        w[0] = pack2<T>(dqt[cb][4 * rr + 0] * sc, dqt[cb][4 * rr + 1] * sc);
+        w[1] = pack2<T>(dqt[cb][4 * rr + 2] * sc, dqt[cb][4 * rr + 3] * sc);
+        *reinterpret_cast<u32x2*>(dqp + cb * 32 + 8 * rr + 4 * half) = w;
+      }
+  }
+}
+
+template <typename T, int D, bool CAUSAL, bool VARLEN>
+hipError_t launch(const BwdArgs& a, hipStream_t s) {
+  const int64_t rows = (int64_t)a.B * a.N * a.Hq;   // upper bound on T·Hq
+  const int rows_per_block = kThreads / (D / 8);
+  const int g0 = (int)((rows + rows_per_block - 1) / rows_per_block);
+  hipLaunchKernelGGL((delta_kernel<T, D, VARLEN>), dim3(g0), dim3(kThreads), 0, s, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int nkt = (a.N + kDkvKeys - 1) / kDkvKeys;
+  hipLaunchKernelGGL((dkdv_kernel<T, D, CAUSAL, VARLEN>), dim3(nkt * a.Hkv * a.B), dim3(kThreads),
+                     0, s, a, nkt);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int nqt = (a.N + kDqQ - 1) / kDqQ;
+  hipLaunchKernelGGL((dq_kernel<T, D, CAUSAL, VARLEN>), dim3(nqt * a.Hq * a.B), dim3(kThreads), 0,
+                     s, a, nqt);
+  return hipGetLastError();
+}
+
+template <typename T, int D>
+hipError_t dispatch_mask(const BwdArgs& a, bool causal, bool varlen, hipStream_t s) {
+  if (causal) return varlen ? launch<T, D, true, true>(a, s) : launch<T, D, true, false>(a, s);
+  return varlen ? launch<T, D, false, true>(a, s) : launch<T, D, false, false>(a, s);
+}
+
+}  // namespace
+
+hipError_t launch_bwd(const BwdArgs& a, bool bf16_in, int d, bool causal, bool varlen,
+                      hipStream_t s) {
+  if (bf16_in)
+    return d == 64 ? dispatch_mask<bf16, 64>(a, causal, varlen, s)
+                   : dispatch_mask<bf16, 128>(a, causal, varlen, s);
+  return d == 64 ? dispatch_mask<f16, 64>(a, causal, varlen, s)
+                 : dispatch_mask<f16, 128>(a, causal, varlen, s);
+}
+
+}  // namespace fa

@@ -1,0 +1,171 @@
+// Device helpers shared by the forward and backward kernels (gfx950 only).
+//
+// MFMA 32x32x16 (bf16 / fp16 in, fp32 accumulate), one wavefront of 64 lanes:
+//   A operand: lane l holds row  l%32, k-slots 8·(l/32) + e, e = 0..7
+//   B operand: lane l holds col  l%32, k-slots 8·(l/32) + e
+//   C/D      : lane l holds col  l%32, rows 8·r + 4·(l/32) + t in element 4·r + t
+// The contraction pairs A's slot (l/32, e) with B's slot (l/32, e), so any
+// consistent assignment of the k index to slots is a valid product. The
+// kernels use that freedom to feed an accumulator straight back in as an
+// operand: an accumulator column holds, in lane half h, the k values
+// {4h..4h+3, 8+4h..8+4h+3} of each 16-wide k step, and the matching operand
+// from LDS is stored with the same permutation (see perm16()).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fa {
+
+typedef __bf16 bf16;
+typedef _Float16 f16;
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef f16 f16x8 __attribute__((ext_vector_type(8)));
+typedef bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef f16 f16x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+template <typename T>
+__device__ __forceinline__ f32x16 mfma32(u32x4 a, u32x4 b, f32x16 c) {
+  if constexpr (__is_same(T, bf16)) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+  } else {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
+                                                  __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+  }
+}
+
+// Two floats -> two 16-bit values of T packed in one dword, round to nearest even.
+template <typename T>
+__device__ __forceinline__ uint32_t pack2(float lo, float hi) {
+  f32x2 x = {lo, hi};
+  if constexpr (__is_same(T, bf16)) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(x, bf16x2));
+  } else {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(x, f16x2));
+  }
+}
+
+// Elements 4·r .. 4·r+7 of an accumulator (rows 8r+4h+t and 8(r+1)+4h+t for
+// even r) as one 8-element operand, i.e. the 16-wide k step r/2 of the
+// accumulator's row dimension in the permuted slot order.
+template <typename T>
+__device__ __forceinline__ u32x4 acc_operand(const f32x16& a, int r) {
+  u32x4 p;
+  p[0] = pack2<T>(a[4 * r + 0], a[4 * r + 1]);
+  p[1] = pack2<T>(a[4 * r + 2], a[4 * r + 3]);
+  p[2] = pack2<T>(a[4 * r + 4], a[4 * r + 5]);
+  p[3] = pack2<T>(a[4 * r + 6], a[4 * r + 7]);
+  return p;
+}
+
+// Position, inside a 16-wide k step, where operand data for index x (0..15)
+// is stored so that lane half h reads slots e = 0..7 contiguously as the
+// indices {4h..4h+3, 8+4h..8+4h+3}: the middle two groups of 4 swap places.
+__device__ __forceinline__ constexpr int perm16(int x) {
+  return (x & ~15) | (((x >> 2) & 1) << 3) | (((x >> 3) & 1) << 2) | (x & 3);
+}
+
+// 4 rows x 8 columns of 16-bit values (one 16-byte chunk per row) ->
+// column w as 4 values (rows 0..3) in two dwords.
+__device__ __forceinline__ u32x2 transpose_col(const u32x4 (&in)[4], int w) {
+  const int dw = w >> 1;
+  u32x2 r;
+  if (w & 1) {
+    r[0] = (in[0][dw] >> 16) | (in[1][dw] & 0xffff0000u);
+    r[1] = (in[2][dw] >> 16) | (in[3][dw] & 0xffff0000u);
+  } else {
+    r[0] = (in[0][dw] & 0xffffu) | (in[1][dw] << 16);
+    r[1] = (in[2][dw] & 0xffffu) | (in[3][dw] << 16);
+  }
+  return r;
+}
+
+__device__ __forceinline__ float wave_max_halves(float x) {
+  // lanes l and l^32 hold the two halves of one column
+  return fmaxf(x, __shfl_xor(x, 32));
+}
+
+__device__ __forceinline__ float wave_sum_halves(float x) {
+  return x + __shfl_xor(x, 32);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Hardware places workgroup w on XCD w % 8 (8 XCDs, each with its own L2).
+// Return a logical id so that each XCD receives one contiguous range of
+// logical ids; consecutive logical ids then share K/V tiles within one L2.
+__device__ __forceinline__ int xcd_remap(int w, int G) {
+  const int per = G >> 3, rem = G & 7, x = w & 7;
+  return x * per + (x < rem ? x : rem) + (w >> 3);
+}
+
+template <typename T>
+__device__ __forceinline__ u32x4 ldg16(const T* p) {
+  return *reinterpret_cast<const u32x4*>(p);
+}
+
+template <typename T>
+__device__ __forceinline__ u32x4 lds16(const T* p) {
+  return *reinterpret_cast<const u32x4*>(p);
+}
+
+// Row-major tile: rows r0 .. r0+R-1 of a sequence with L rows, D columns,
+// into lds[r·LS + c]; rows at or past L are zero. Consecutive threads read
+// consecutive 16-byte chunks of a row.
+template <typename T, int R, int D, int LS, int NT>
+__device__ __forceinline__ void tile_to_lds(T* lds, const T* src, int64_t rstride, int r0, int L,
+                                            int tid) {
+  constexpr int CH = R * D / 8;
+#pragma unroll
+  for (int u = 0; u < (CH + NT - 1) / NT; ++u) {
+    const int ci = tid + NT * u;
+    if (CH % NT == 0 || ci < CH) {
+      const int r = ci / (D / 8), dc = ci % (D / 8);
+      u32x4 val = u32x4{0, 0, 0, 0};
+      if (r0 + r < L) val = ldg16(src + (int64_t)(r0 + r) * rstride + dc * 8);
+      *reinterpret_cast<u32x4*>(lds + r * LS + dc * 8) = val;
+    }
+  }
+}
+
+// Transposed tile: lds_t[c·LS_T + perm16(r)] = src[r0 + r][c], rows at or past
+// L are zero. A thread reads a 4-row x 8-column block and writes 8 rows of
+// the transpose (4 values each). When ROWS_TOO is set the same block is also
+// stored row-major into lds[r·LS + c].
+template <typename T, int R, int D, int LS_T, int NT, bool ROWS_TOO = false, int LS = D + 8>
+__device__ __forceinline__ void tile_to_lds_t(T* lds_t, T* lds, const T* src, int64_t rstride,
+                                              int r0, int L, int tid) {
+  constexpr int BL = (R / 4) * (D / 8);
+#pragma unroll
+  for (int u = 0; u < (BL + NT - 1) / NT; ++u) {
+    const int bi = tid + NT * u;
+    if (BL % NT == 0 || bi < BL) {
+      const int rq = bi % (R / 4), dc = bi / (R / 4);
+      u32x4 in[4];
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        const int row = r0 + 4 * rq + rr;
+        in[rr] = row < L ? ldg16(src + (int64_t)row * rstride + dc * 8) : u32x4{0, 0, 0, 0};
+      }
+      const int pos = perm16(4 * rq);
+#pragma unroll
+      for (int w = 0; w < 8; ++w)
+        *reinterpret_cast<u32x2*>(lds_t + (dc * 8 + w) * LS_T + pos) = transpose_col(in, w);
+      if constexpr (ROWS_TOO) {
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr)
+          *reinterpret_cast<u32x4*>(lds + (4 * rq + rr) * LS + dc * 8) = in[rr];
+      }
+    }
+  }
+}
+
+}  // namespace fa

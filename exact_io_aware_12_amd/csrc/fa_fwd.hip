@@ -1,0 +1,203 @@
+// Fused attention forward for gfx950.
+//
+// One workgroup = 4 wavefronts = a tile of 128 query rows of one (sequence,
+// query head); each wavefront owns 32 rows. The workgroup streams the visible
+// 64-key tiles of K and V through LDS (tiling and fusion as in the
+// FlashAttention guide, cxbdf.cn, part 2; the K/V-tiles-in-fast-memory, loop
+// over Q blocks description in Flash Attention 是什麼, adersaytech.com,
+// section 分塊計算), so S and P live only in registers.
+//
+// Per 64-key tile and wavefront:
+//   Sᵀ = K·Qᵀ        32 MFMA columns = the wave's 32 queries, so every lane
+//                    owns one query row and the row statistics are lane-local
+//                    (plus one exchange between the two lane halves)
+//   online softmax   running row max m and row sum l in registers, base-2
+//                    exponentials with the scale folded in (c = scale·log2 e)
+//   Oᵀ += Vᵀ·Pᵀ      P is fed from the Sᵀ accumulator registers directly; V is
+//                    stored transposed in LDS in the matching key order
+// Epilogue: O = Oᵀ/l rounded to the input type, LSE = (m·c + log2 l)·ln 2.
+#include "fa_device.h"
+#include "fa_kernels.h"
+
+namespace fa {
+
+namespace {
+
+constexpr int kBR = 128;  // query rows per workgroup
+constexpr int kBC = 64;   // keys per tile
+constexpr int kThreads = 256;
+
+template <typename T, int D, bool CAUSAL, bool VARLEN>
+__global__ __launch_bounds__(kThreads, 2) void fwd_kernel(FwdArgs a) {
+  constexpr int KS = D + 8;      // K tile row stride in LDS (elements), 16 B pad
+  constexpr int VS = kBC + 8;    // Vᵀ tile row stride in LDS (elements), 16 B pad
+  constexpr int NKB = D / 16;    // k steps of Q·Kᵀ
+  constexpr int NCB = D / 32;    // 32-row blocks of Oᵀ
+  __shared__ __attribute__((aligned(16))) T k_lds[kBC * KS];
+  __shared__ __attribute__((aligned(16))) T vt_lds[D * VS];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int col = lane & 31, half = lane >> 5;
+
+  // ---- work decomposition: (q tile, head, sequence), heavy tiles first -----
+  const int G = gridDim.x;
+  const int logical = xcd_remap(blockIdx.x, G);
+  const int qt_ord = logical % a.n_qtiles;
+  const int hb = logical / a.n_qtiles;
+  const int h = hb % a.Hq, b = hb / a.Hq;
+  const int qt = CAUSAL ? a.n_qtiles - 1 - qt_ord : qt_ord;
+
+  int seq0, L, T_total;
+  if constexpr (VARLEN) {
+    seq0 = a.cu_seqlens[b];
+    L = a.cu_seqlens[b + 1] - seq0;
+    T_total = a.cu_seqlens[a.B];
+  } else {
+    seq0 = b * a.N;
+    L = a.N;
+    T_total = a.B * a.N;
+  }
+  const int q0 = qt * kBR;
+  if (q0 >= L) return;
+  const int g = h / a.group;
+
+  const int64_t qs = (int64_t)a.Hq * D, kvs = (int64_t)a.Hkv * D;
+  const T* qp = static_cast<const T*>(a.q) + (int64_t)seq0 * qs + (int64_t)h * D;
+  const T* kp = static_cast<const T*>(a.k) + (int64_t)seq0 * kvs + (int64_t)g * D;
+  const T* vp = static_cast<const T*>(a.v) + (int64_t)seq0 * kvs + (int64_t)g * D;
+
+  // ---- Q fragments (B operand of Sᵀ = K·Qᵀ), kept in registers -------------
+  const int qrow = q0 + wave * 32 + col;
+  u32x4 qf[NKB];
+  if (qrow < L) {
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) qf[kb] = ldg16(qp + qrow * qs + kb * 16 + half * 8);
+  } else {
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) qf[kb] = u32x4{0, 0, 0, 0};
+  }
+
+  f32x16 o[NCB];
+#pragma unroll
+  for (int cb = 0; cb < NCB; ++cb) o[cb] = f32x16{};
+  float m = -INFINITY;   // running max of the raw scores S (scale not applied)
+  float l = 0.f;         // running sum of exp2(S·c − m·c), this lane half's keys
+  const float c = a.scale_log2;
+
+  const int kv_end = CAUSAL ? min(L, q0 + kBR) : L;
+  const int ntiles = (kv_end + kBC - 1) / kBC;
+  const int wq_first = q0 + wave * 32, wq_last = wq_first + 31;
+
+  for (int j = 0; j < ntiles; ++j) {
+    const int kv0 = j * kBC;
+    __syncthreads();  // the previous tile's LDS reads are done
+    // K tile row-major; V tile transposed with the key order of perm16()
+    tile_to_lds<T, kBC, D, KS, kThreads>(k_lds, kp, kvs, kv0, L, tid);
+    tile_to_lds_t<T, kBC, D, VS, kThreads>(vt_lds, nullptr, vp, kvs, kv0, L, tid);
+    __syncthreads();
+    if (CAUSAL && kv0 > wq_last) continue;  // every key of the tile is after this wave's rows
+
+    // ---- Sᵀ = K·Qᵀ ----------------------------------------------------------
+    f32x16 s[2] = {f32x16{}, f32x16{}};
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) {
+#pragma unroll
+      for (int jb = 0; jb < 2; ++jb) {
+        const u32x4 kf = lds16(k_lds + (jb * 32 + col) * KS + kb * 16 + half * 8);
+        s[jb] = mfma32<T>(kf, qf[kb], s[jb]);
+      }
+    }
+
+    // ---- mask: keys past the sequence end, keys after the query (causal) ---
+    const bool edge = (kv0 + kBC > L) || (CAUSAL && kv0 + kBC - 1 > wq_first);
+    if (edge) {
+#pragma unroll
+      for (int jb = 0; jb < 2; ++jb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int key = kv0 + jb * 32 + 8 * (i >> 2) + 4 * half + (i & 3);
+          if (key >= L || (CAUSAL && key > qrow)) s[jb][i] = -INFINITY;
+        }
+    }
+
+    // ---- online softmax ----------------------------------------------------
+    float mx = s[0][0];
+#pragma unroll
+    for (int i = 1; i < 16; ++i) mx = fmaxf(mx, s[0][i]);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[1][i]);
+    mx = wave_max_halves(mx);
+    const float m_new = fmaxf(m, mx);        // finite: key 0 is seen in tile 0
+    const float alpha = fast_exp2((m - m_new) * c);
+    const float mc = m_new * c;
+    float rs = 0.f;
+#pragma unroll
+    for (int jb = 0; jb < 2; ++jb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const float p = fast_exp2(fmaf(s[jb][i], c, -mc));
+        s[jb][i] = p;
+        rs += p;
+      }
+    l = fmaf(l, alpha, rs);
+    m = m_new;
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb) o[cb] *= alpha;
+
+    // ---- Oᵀ += Vᵀ·Pᵀ ---------------------------------------------------------
+#pragma unroll
+    for (int kk = 0; kk < kBC / 16; ++kk) {
+      const u32x4 pf = acc_operand<T>(s[kk >> 1], (kk & 1) * 2);
+#pragma unroll
+      for (int cb = 0; cb < NCB; ++cb) {
+        const u32x4 vf = lds16(vt_lds + (cb * 32 + col) * VS + kk * 16 + half * 8);
+        o[cb] = mfma32<T>(vf, pf, o[cb]);
+      }
+    }
+  }
+
+  // ---- epilogue -------------------------------------------------------------
+  const float l_tot = wave_sum_halves(l);
+  if (qrow < L) {
+    const float inv = 1.f / l_tot;
+    T* op = static_cast<T*>(a.o) + (int64_t)seq0 * qs + (int64_t)h * D + qrow * qs;
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        u32x2 w;
+        w[0] = pack2<T>(o[cb][4 * r + 0] * inv, o[cb][4 * r + 1] * inv);
+        w[1] = pack2<T>(o[cb][4 * r + 2] * inv, o[cb][4 * r + 3] * inv);
+        *reinterpret_cast<u32x2*>(op + cb * 32 + 8 * r + 4 * half) = w;
+      }
+    if (half == 0) a.lse[(int64_t)h * T_total + seq0 + qrow] = (m * c + log2f(l_tot)) * kLn2;
+  }
+}
+
+template <typename T, int D, bool CAUSAL, bool VARLEN>
+hipError_t launch(const FwdArgs& a, hipStream_t stream) {
+  const int grid = a.n_qtiles * a.Hq * a.B;
+  hipLaunchKernelGGL((fwd_kernel<T, D, CAUSAL, VARLEN>), dim3(grid), dim3(kThreads), 0, stream, a);
+  return hipGetLastError();
+}
+
+template <typename T, int D>
+hipError_t dispatch_mask(const FwdArgs& a, bool causal, bool varlen, hipStream_t s) {
+  if (causal) return varlen ? launch<T, D, true, true>(a, s) : launch<T, D, true, false>(a, s);
+  return varlen ? launch<T, D, false, true>(a, s) : launch<T, D, false, false>(a, s);
+}
+
+}  // namespace
+
+int fwd_query_tile() { return kBR; }
+
+hipError_t launch_fwd(const FwdArgs& a, bool bf16_in, int d, bool causal, bool varlen,
+                      hipStream_t s) {
+  if (bf16_in)
+    return d == 64 ? dispatch_mask<bf16, 64>(a, causal, varlen, s)
+                   : dispatch_mask<bf16, 128>(a, causal, varlen, s);
+  return d == 64 ? dispatch_mask<f16, 64>(a, causal, varlen, s)
+                 : dispatch_mask<f16, 128>(a, causal, varlen, s);
+}
+
+}  // namespace fa

@@ -1,0 +1,46 @@
+// Launch interface between the C-ABI layer (fa_api.hip) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fa {
+
+struct FwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;
+  const int32_t* cu_seqlens;  // null for fixed length
+  int B, Hq, Hkv, N;
+  int group;                  // Hq / Hkv
+  int n_qtiles;               // ceil(N / query tile)
+  float scale_log2;           // scale · log2(e)
+};
+
+struct BwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o;
+  const void* dout;
+  const float* lse;
+  void* dq;
+  void* dk;
+  void* dv;
+  float* delta;               // workspace: rowsum(dO∘O), [Hq, T] float32
+  const int32_t* cu_seqlens;
+  int B, Hq, Hkv, N;
+  int group;
+  float scale;
+  float scale_log2;
+};
+
+int fwd_query_tile();
+hipError_t launch_fwd(const FwdArgs& a, bool bf16_in, int d, bool causal, bool varlen,
+                      hipStream_t s);
+hipError_t launch_bwd(const BwdArgs& a, bool bf16_in, int d, bool causal, bool varlen,
+                      hipStream_t s);
+
+}  // namespace fa

@@ -1,0 +1,108 @@
+/*
+ * fa.h — C ABI of libfa.so: exact, fused scaled-dot-product attention for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The operation is attention as the FlashAttention guide (cxbdf.cn, part 1)
+ * defines it, O = softmax(Q·Kᵀ·scale)·V with the softmax taken along each
+ * query row, optionally causal (the causal flag of flash_attn_func in the
+ * Llama-Factory page's first code sample), computed tile by tile so that the
+ * N×N score matrix never reaches device memory (cxbdf.cn guide, part 2:
+ * tiling and kernel fusion). The forward also returns the per-row
+ * log-sum-exp, the float "softmax_lse" output of the forward kernel in the
+ * FlashAttention-2 全解析 page (blog.gitcode.com, core tiling sketch), which
+ * the backward uses to recompute the probabilities instead of storing them
+ * (cxbdf.cn guide, part 2, item 3: recomputation in the backward pass).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Layout: all tensors are dense, token-major and contiguous.
+ *   q, o, dout, dq : [T, Hq,  d]   element type `dtype`
+ *   k, v, dk, dv   : [T, Hkv, d]   element type `dtype`
+ *   lse            : [Hq, T]       float32, natural log of the scaled logits
+ * Fixed length (cu_seqlens == NULL): T = B·N, tokens ordered (batch, position),
+ *   i.e. the (B, N, H, d) layout of flash_attn_func.
+ * Variable length (cu_seqlens != NULL): B sequences packed without padding;
+ *   cu_seqlens is int32 device memory with B+1 non-decreasing entries,
+ *   cu_seqlens[0] = 0, sequence s = tokens [cu_seqlens[s], cu_seqlens[s+1]),
+ *   T = cu_seqlens[B], and N must be ≥ the longest sequence (it sizes the
+ *   grid). The caller guarantees this; it is not checked on the device.
+ *   No token attends across a sequence boundary.
+ * Heads: query head h reads KV head h / (Hq/Hkv) (grouped-query attention;
+ *   Hq must be a multiple of Hkv).
+ * Causal: key j is visible from query i iff j <= i, positions counted from
+ *   the start of the sequence.
+ * Supported: dtype FA_FP16 or FA_BF16; d = 64 or 128; scale finite and > 0.
+ *
+ * Alignment: every tensor pointer must be 16-byte aligned (FA_ERR_INVALID_ARG
+ *   otherwise); rows are moved as 16-byte vectors.
+ * Ownership: every pointer is device memory owned by the caller. The library
+ * allocates nothing, keeps no pointer after returning, and holds no mutable
+ * global state; calls on different streams may run concurrently. Outputs must
+ * not alias inputs.
+ *
+ * Errors: arguments are checked on the host before anything is enqueued; on
+ * a negative status nothing was enqueued. FA_ERR_UNSUPPORTED marks a valid
+ * request outside the supported envelope, so the caller can fall back to
+ * another attention implementation. FA_OK means the work was enqueued on
+ * `stream` (NULL = the default stream); device faults surface at the caller's
+ * next synchronisation. B = 0 or N = 0 is a no-op returning FA_OK.
+ *
+ * Determinism: results are bitwise identical from run to run.
+ */
+#ifndef FA_H_
+#define FA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  FA_OK = 0,
+  FA_ERR_INVALID_ARG = -1,  /* null or misaligned pointer, negative size, bad enum,
+                               Hq % Hkv != 0, bad scale */
+  FA_ERR_UNSUPPORTED = -2,  /* head dim other than 64 / 128 */
+  FA_ERR_HIP = -3,          /* the HIP runtime refused a launch (e.g. no device) */
+  FA_ERR_WORKSPACE = -4     /* workspace missing or smaller than fa_bwd_workspace_size() */
+} fa_status;
+
+typedef enum { FA_FP16 = 0, FA_BF16 = 1 } fa_dtype;
+
+/*
+ * Forward: o = softmax(q·kᵀ·scale [causal])·v and lse = ln Σ_j exp(scale·q·k_j)
+ * per (query head, token). o is rounded to `dtype` (nearest even), lse is
+ * float32. B = batch size (number of sequences), N = sequence length (maximum
+ * length for varlen), d = head dim.
+ */
+int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+           int B, int Hq, int Hkv, int N, int d, float scale, int causal,
+           const int32_t* cu_seqlens, int dtype, hipStream_t stream);
+
+/*
+ * Backward of fa_fwd for the upstream gradient `dout`, given the forward's
+ * o and lse (the probabilities are recomputed from lse, never stored).
+ * Writes dq [T, Hq, d], dk and dv [T, Hkv, d] in `dtype` (nearest even);
+ * dk and dv of a KV head are summed over the query heads that share it.
+ * `workspace` is caller-owned device memory of at least
+ * fa_bwd_workspace_size(B, Hq, Hkv, N, d) bytes (float32 rowsum(dout∘o)).
+ */
+int fa_bwd(const void* q, const void* k, const void* v, const void* o,
+           const void* dout, const float* lse, void* dq, void* dk, void* dv,
+           int B, int Hq, int Hkv, int N, int d, float scale, int causal,
+           const int32_t* cu_seqlens, int dtype,
+           void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Workspace bytes fa_bwd needs; an upper bound that uses T <= B·N. 0 on bad sizes. */
+size_t fa_bwd_workspace_size(int B, int Hq, int Hkv, int N, int d);
+
+/* Static, NUL-terminated text for a status code. */
+const char* fa_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_H_ */

@@ -1,0 +1,114 @@
+"""The C ABI without a GPU: the library loads, exports what include/fa.h
+declares, and rejects bad arguments on the host before any HIP call."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fa.h")
+
+fa = pytest.importorskip("exact_io_aware_12_amd")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[A-Za-z_][\w\s\*]*?\b(fa_\w+)\s*\(", text,
+                                 flags=re.M)))
+
+
+def test_header_declares_the_boundary():
+    assert declared_functions() == ["fa_bwd", "fa_bwd_workspace_size", "fa_fwd",
+                                    "fa_status_string"]
+
+
+def test_every_declared_symbol_is_exported():
+    lib = ctypes.CDLL(fa.lib_path())
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_status_strings():
+    for code in (0, -1, -2, -3, -4):
+        assert fa.fa_status_string(code).startswith(
+            {0: "FA_OK", -1: "FA_ERR_INVALID_ARG", -2: "FA_ERR_UNSUPPORTED", -3: "FA_ERR_HIP",
+             -4: "FA_ERR_WORKSPACE"}[code])
+    assert fa.fa_status_string(7) == "unknown fa status"
+
+
+# Fake, never-dereferenced device addresses: every call below must be refused
+# by the host-side checks before anything is enqueued.
+P = 0x1000
+
+
+def fwd(**kw):
+    a = dict(q=P, k=P, v=P, o=P, lse=P, B=1, Hq=2, Hkv=2, N=16, d=64, scale=0.125, causal=0,
+             cu=None, dtype=fa.FA_FP16, stream=None)
+    a.update(kw)
+    return fa.fa_fwd(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["Hq"], a["Hkv"], a["N"],
+                     a["d"], a["scale"], a["causal"], a["cu"], a["dtype"], a["stream"])
+
+
+def bwd(**kw):
+    a = dict(B=1, Hq=2, Hkv=2, N=16, d=64, scale=0.125, causal=0, dtype=fa.FA_BF16, ws=P,
+             wsb=1 << 20)
+    a.update(kw)
+    ptrs = [kw.get(n, P) for n in ("q", "k", "v", "o", "do", "lse", "dq", "dk", "dv")]
+    return fa.fa_bwd(*ptrs, a["B"], a["Hq"], a["Hkv"], a["N"], a["d"], a["scale"], a["causal"],
+                     None, a["dtype"], a["ws"], a["wsb"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dtype=2), fa.FA_ERR_INVALID_ARG),
+    (dict(dtype=-1), fa.FA_ERR_INVALID_ARG),
+    (dict(B=-1), fa.FA_ERR_INVALID_ARG),
+    (dict(N=-5), fa.FA_ERR_INVALID_ARG),
+    (dict(Hq=0), fa.FA_ERR_INVALID_ARG),
+    (dict(Hq=3, Hkv=2), fa.FA_ERR_INVALID_ARG),
+    (dict(causal=2), fa.FA_ERR_INVALID_ARG),
+    (dict(scale=float("nan")), fa.FA_ERR_INVALID_ARG),
+    (dict(scale=float("inf")), fa.FA_ERR_INVALID_ARG),
+    (dict(scale=0.0), fa.FA_ERR_INVALID_ARG),
+    (dict(scale=-0.1), fa.FA_ERR_INVALID_ARG),
+    (dict(q=None), fa.FA_ERR_INVALID_ARG),
+    (dict(lse=None), fa.FA_ERR_INVALID_ARG),
+    (dict(k=P + 8), fa.FA_ERR_INVALID_ARG),      # not 16-byte aligned
+    (dict(d=96), fa.FA_ERR_UNSUPPORTED),
+    (dict(d=256), fa.FA_ERR_UNSUPPORTED),
+    (dict(B=1 << 16, N=1 << 16), fa.FA_ERR_UNSUPPORTED),
+    (dict(B=0), fa.FA_OK),                       # empty batch: no-op
+    (dict(N=0, q=None, k=None), fa.FA_OK),       # empty sequence: no-op, pointers unused
+])
+def test_fwd_host_checks(kw, status):
+    assert fwd(**kw) == status
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dtype=5), fa.FA_ERR_INVALID_ARG),
+    (dict(Hq=4, Hkv=3), fa.FA_ERR_INVALID_ARG),
+    (dict(dv=None), fa.FA_ERR_INVALID_ARG),
+    (dict(do=P + 2), fa.FA_ERR_INVALID_ARG),
+    (dict(d=32), fa.FA_ERR_UNSUPPORTED),
+    (dict(ws=None), fa.FA_ERR_WORKSPACE),
+    (dict(wsb=64), fa.FA_ERR_WORKSPACE),
+    (dict(B=0), fa.FA_OK),
+])
+def test_bwd_host_checks(kw, status):
+    assert bwd(**kw) == status
+
+
+def test_workspace_size():
+    assert fa.fa_bwd_workspace_size(2, 16, 16, 16384, 128) == 2 * 16384 * 16 * 4
+    assert fa.fa_bwd_workspace_size(1, 2, 2, 3, 64) == 256          # 256-byte granule
+    assert fa.fa_bwd_workspace_size(1, 3, 2, 16, 64) == 0            # Hq % Hkv != 0
+    assert fa.fa_bwd_workspace_size(1, 2, 2, 16, 80) == 0            # unsupported d
+
+
+def test_no_device_reports_hip_error():
+    """A valid request with no GPU present fails at the launch, not in the checks."""
+    torch = pytest.importorskip("torch")
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    assert fwd() == fa.FA_ERR_HIP

@@ -1,0 +1,108 @@
+"""GPU parity of fa_bwd against the float64 oracle (through the C ABI).
+
+The GPU backward consumes the GPU forward's O and LSE, exactly as a training
+step does; the oracle recomputes everything from Q, K, V, dO by definition.
+"""
+import numpy as np
+import pytest
+
+import workloads as W
+from oracle import attention_bwd, attention_bwd_sampled
+from parity_util import bits_equal, check_grad, host64, say, to_device
+
+pytestmark = pytest.mark.gpu
+
+
+def run_fwd_bwd(w: W.Workload, arrays=None):
+    import torch
+    import exact_io_aware_12_amd as fa
+    arrays = W.generate(w, with_grad=True) if arrays is None else arrays
+    t = to_device(arrays, w.dtype)
+    say(f"[fa_fwd+fa_bwd] {w.name} B={w.B} Hq={w.Hq} Hkv={w.Hkv} N={w.N} d={w.d} {w.dtype} "
+        f"causal={w.causal} varlen={w.varlen} T={w.T}")
+    kw = dict(causal=w.causal, softmax_scale=w.scale)
+    if w.varlen:
+        kw.update(cu_seqlens=t["cu_seqlens"], max_seqlen=w.N)
+        q, k, v, do = t["q"], t["k"], t["v"], t["do"]
+    else:
+        shp = (w.B, w.N)
+        q, k, v = (t[n].view(*shp, -1, w.d) for n in ("q", "k", "v"))
+        do = t["do"].view(*shp, w.Hq, w.d)
+    o, lse = fa.flash_attn_func(q, k, v, **kw)
+    dq, dk, dv = fa.flash_attn_backward(do, q, k, v, o, lse, **kw)
+    torch.cuda.synchronize()
+    T = w.T
+    return (dq.view(T, w.Hq, w.d), dk.view(T, w.Hkv, w.d), dv.view(T, w.Hkv, w.d)), t
+
+
+def compare_whole(w, arrays=None):
+    (dq, dk, dv), t = run_fwd_bwd(w, arrays)
+    cu = t["cu_seqlens"].cpu().numpy()
+    ref = attention_bwd(host64(t["q"]), host64(t["k"]), host64(t["v"]), host64(t["do"]), w.scale,
+                        w.causal, cu)
+    res = [check_grad(host64(g), r, n) for g, r, n in zip((dq, dk, dv), ref, ("dQ", "dK", "dV"))]
+    say("   " + " ".join(f"{n}: rel {a:.2e} frob {b:.2e}" for n, (a, b) in
+                         zip(("dQ", "dK", "dV"), res)))
+    return (dq, dk, dv), t
+
+
+def test_tiny_backward():
+    w = W.WORKLOADS["tiny"]
+    compare_whole(W.custom(B=w.B, Hq=w.Hq, Hkv=w.Hkv, N=w.N, d=w.d, dtype=w.dtype,
+                           causal=w.causal, seed=w.seed, backward=True))
+
+
+@pytest.mark.parametrize("dtype", ["fp16", "bf16"])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("N", [1, 33, 64, 129, 300])
+def test_ragged_lengths(dtype, d, causal, N):
+    compare_whole(W.custom(B=2, Hq=2, Hkv=2, N=N, d=d, dtype=dtype, causal=causal,
+                           seed=200 + N, backward=True))
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_gqa_varlen(causal):
+    w = W.custom(B=0, Hq=8, Hkv=2, N=0, d=128, dtype="bf16", causal=causal, seed=21,
+                 lens=[0, 1, 77, 128, 200, 64], backward=True)
+    compare_whole(w)
+
+
+def test_causal_d64_shape_backward():
+    compare_whole(W.custom(B=1, Hq=16, Hkv=16, N=2048, d=64, dtype="fp16", causal=True, seed=2,
+                           backward=True))
+
+
+def test_identities_on_gpu():
+    """Σ_j dV_j = Σ_i dO_i and Σ_j dK_j = 0 per (sequence, head), up to rounding."""
+    w = W.custom(B=2, Hq=4, Hkv=4, N=500, d=128, dtype="fp16", causal=True, seed=22, backward=True)
+    (dq, dk, dv), t = run_fwd_bwd(w)
+    dk64, dv64, do64 = host64(dk), host64(dv), host64(t["do"])
+    for b in range(2):
+        sl = slice(b * 500, (b + 1) * 500)
+        np.testing.assert_allclose(dv64[sl].sum(0), do64[sl].sum(0), rtol=1e-2, atol=0.05)
+        bound = 2e-3 * np.abs(dk64[sl]).sum(0) + 1e-3
+        assert (np.abs(dk64[sl].sum(0)) <= bound).all()
+
+
+def test_deterministic():
+    w = W.custom(B=1, Hq=4, Hkv=2, N=700, d=128, dtype="bf16", causal=True, seed=23, backward=True)
+    a = W.generate(w)
+    (g1, _), (g2, _) = run_fwd_bwd(w, a), run_fwd_bwd(w, a)
+    for x, y in zip(g1, g2):
+        assert bits_equal(x, y)
+
+
+def test_train_16k_backward_sampled():
+    """The training-step workload at full size; two (sequence, head) units by the oracle."""
+    w = W.WORKLOADS["train_16k"]
+    (dq, dk, dv), t = run_fwd_bwd(w)
+    cu = w.cu_seqlens()
+    units = [(0, 3), (1, 12)]
+    ref = attention_bwd_sampled(t["q"], t["k"], t["v"], t["do"], w.scale, w.causal, cu, units)
+    for (s, g), (rq, rk, rv) in ref.items():
+        sl = slice(int(cu[s]), int(cu[s + 1]))
+        check_grad(host64(dq[sl, g:g + 1]), rq, f"dQ seq {s} head {g}")
+        check_grad(host64(dk[sl, g]), rk, f"dK seq {s} head {g}")
+        r = check_grad(host64(dv[sl, g]), rv, f"dV seq {s} head {g}")
+        say(f"   unit ({s},{g}) ok; dV rel {r[0]:.2e}")

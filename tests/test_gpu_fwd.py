@@ -1,0 +1,205 @@
+"""GPU parity of fa_fwd against the float64 oracle (through the C ABI).
+
+Small shapes compare every element (several tiles plus a ragged tail); the
+full-size workloads compare sampled rows, which the oracle computes one by
+one, in the launch configuration the benchmark times.
+"""
+import numpy as np
+import pytest
+
+import workloads as W
+from oracle import attention_fwd, attention_fwd_rows
+from parity_util import bits_equal, check_lse, check_o, host64, say, to_device
+
+pytestmark = pytest.mark.gpu
+
+
+def _fa():
+    import exact_io_aware_12_amd as fa   # raises if libfa.so is missing: no fallback
+    return fa
+
+
+def run_fwd(w: W.Workload, arrays=None):
+    """Run fa_fwd on the workload's seeded inputs; returns (o [T,Hq,d], lse [Hq,T], inputs)."""
+    import torch
+    fa = _fa()
+    arrays = W.generate(w, with_grad=False) if arrays is None else arrays
+    t = to_device(arrays, w.dtype)
+    say(f"[fa_fwd] {w.name} B={w.B} Hq={w.Hq} Hkv={w.Hkv} N={w.N} d={w.d} {w.dtype} "
+        f"causal={w.causal} varlen={w.varlen} T={w.T}")
+    if w.varlen:
+        o, lse = fa.flash_attn_func(t["q"], t["k"], t["v"], causal=w.causal, softmax_scale=w.scale,
+                                    cu_seqlens=t["cu_seqlens"], max_seqlen=w.N)
+    else:
+        shp = (w.B, w.N)
+        o, lse = fa.flash_attn_func(t["q"].view(*shp, w.Hq, w.d), t["k"].view(*shp, w.Hkv, w.d),
+                                    t["v"].view(*shp, w.Hkv, w.d), causal=w.causal,
+                                    softmax_scale=w.scale)
+        o = o.view(w.T, w.Hq, w.d)
+    torch.cuda.synchronize()
+    return o, lse, t
+
+
+def compare_whole(w, arrays=None):
+    o, lse, t = run_fwd(w, arrays)
+    cu = t["cu_seqlens"].cpu().numpy()
+    o_ref, lse_ref = attention_fwd(host64(t["q"]), host64(t["k"]), host64(t["v"]), w.scale,
+                                   w.causal, cu)
+    e, floor, exc = check_o(host64(o), o_ref, w.dtype)
+    el = check_lse(host64(lse), lse_ref)
+    say(f"   max|dO|={e:.2e} floor={floor:.2e} exceptions={exc} max|dLSE|={el:.2e}")
+    return o, lse
+
+
+# ---- whole-tensor parity on small shapes -------------------------------------
+def test_tiny_workload():
+    compare_whole(W.WORKLOADS["tiny"])
+
+
+def test_causal_d64_workload():
+    compare_whole(W.WORKLOADS["causal_d64"])
+
+
+@pytest.mark.parametrize("dtype", ["fp16", "bf16"])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("N", [1, 7, 64, 65, 130, 257])
+def test_ragged_lengths(dtype, d, causal, N):
+    compare_whole(W.custom(B=2, Hq=2, Hkv=2, N=N, d=d, dtype=dtype, causal=causal,
+                           seed=100 + N))
+
+
+@pytest.mark.parametrize("dtype", ["fp16", "bf16"])
+@pytest.mark.parametrize("causal", [False, True])
+def test_gqa(dtype, causal):
+    compare_whole(W.custom(B=1, Hq=8, Hkv=2, N=200, d=128, dtype=dtype, causal=causal, seed=7))
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_varlen_with_empty_and_short(d, causal):
+    w = W.custom(B=0, Hq=4, Hkv=2, N=0, d=d, dtype="bf16", causal=causal, seed=8,
+                 lens=[0, 1, 5, 128, 129, 300, 64, 0])
+    compare_whole(w)
+
+
+@pytest.mark.parametrize("kind", ["peaked", "offset", "monotone_max"])
+def test_stress_inputs(kind):
+    """Large logits, shifted keys and a running max that grows every tile."""
+    w = W.custom(B=1, Hq=2, Hkv=2, N=700, d=128, dtype="fp16", causal=True, seed=9)
+    a = W.generate(w)
+    if kind == "peaked":
+        a["q"] = a["q"] * 4.0
+    elif kind == "offset":
+        u = np.random.default_rng(90).standard_normal(w.d).astype(np.float32)
+        a["k"] = a["k"] + 8.0 * u
+        a["q"] = a["q"] + 0.5 * u     # positive correlation with u: large positive logits
+    else:
+        a["k"][:, :, 0] = np.linspace(0, 30, w.T, dtype=np.float32)[:, None]
+        a["q"][:, :, 0] = 1.0
+    compare_whole(w, a)
+
+
+# ---- invariants that hold exactly for this kernel ----------------------------
+def test_deterministic():
+    w = W.custom(B=1, Hq=4, Hkv=4, N=1000, d=128, dtype="bf16", causal=True, seed=10)
+    a = W.generate(w)
+    o1, l1, _ = run_fwd(w, a)
+    o2, l2, _ = run_fwd(w, a)
+    assert bits_equal(o1, o2) and bits_equal(l1, l2)
+
+
+def test_varlen_equals_separate_runs():
+    lens = [300, 129, 1, 64]
+    w = W.custom(B=0, Hq=4, Hkv=1, N=0, d=128, dtype="fp16", causal=True, seed=11, lens=lens)
+    a = W.generate(w)
+    o, lse, _ = run_fwd(w, a)
+    cu = w.cu_seqlens()
+    for s, L in enumerate(lens):
+        ws = W.custom(B=1, Hq=4, Hkv=1, N=L, d=128, dtype="fp16", causal=True, seed=11)
+        sub = {n: a[n][cu[s]:cu[s + 1]] for n in ("q", "k", "v")}
+        sub["cu_seqlens"] = ws.cu_seqlens()
+        os_, ls, _ = run_fwd(ws, sub)
+        assert bits_equal(o[cu[s]:cu[s + 1]], os_), f"sequence {s}"
+        assert bits_equal(lse[:, cu[s]:cu[s + 1]], ls), f"sequence {s}"
+
+
+def test_gqa_equals_repeated_mha():
+    w = W.custom(B=2, Hq=8, Hkv=2, N=333, d=64, dtype="bf16", causal=False, seed=12)
+    a = W.generate(w)
+    o, lse, _ = run_fwd(w, a)
+    wm = W.custom(B=2, Hq=8, Hkv=8, N=333, d=64, dtype="bf16", causal=False, seed=12)
+    am = dict(a, k=np.repeat(a["k"], 4, axis=1), v=np.repeat(a["v"], 4, axis=1))
+    o2, lse2, _ = run_fwd(wm, am)
+    assert bits_equal(o, o2) and bits_equal(lse, lse2)
+
+
+def test_causal_prefix():
+    w = W.custom(B=1, Hq=2, Hkv=2, N=777, d=128, dtype="fp16", causal=True, seed=13)
+    a = W.generate(w)
+    o, lse, _ = run_fwd(w, a)
+    M = 300
+    wp = W.custom(B=1, Hq=2, Hkv=2, N=M, d=128, dtype="fp16", causal=True, seed=13)
+    ap = {n: a[n][:M] for n in ("q", "k", "v")}
+    ap["cu_seqlens"] = wp.cu_seqlens()
+    op, lp, _ = run_fwd(wp, ap)
+    assert bits_equal(o[:M], op) and bits_equal(lse[:, :M], lp)
+
+
+def test_constant_values_exact():
+    """V constant across keys: every output row equals that row (rounded once)."""
+    w = W.custom(B=1, Hq=2, Hkv=2, N=500, d=64, dtype="bf16", causal=True, seed=14)
+    a = W.generate(w)
+    a["v"][:] = a["v"][:1]
+    o, _, t = run_fwd(w, a)
+    want = np.broadcast_to(host64(t["v"][:1]), o.shape)
+    check_o(host64(o), want, w.dtype, "O with constant V")
+
+
+# ---- sampled parity at the full workload sizes --------------------------------
+def _sample_rows(rng, L, n=12):
+    fixed = [0, 1, 63, 64, 127, 128, L // 2, L - 129, L - 65, L - 1]
+    rows = set(r for r in fixed if 0 <= r < L)
+    rows.update(int(x) for x in rng.integers(0, L, size=n))
+    return sorted(rows)
+
+
+def compare_sampled(w, o, lse, t, units, seed=0):
+    import torch
+    rng = np.random.default_rng(seed)
+    cu = w.cu_seqlens()
+    worst_o = worst_l = 0.0
+    for s, h in units:
+        L = int(cu[s + 1] - cu[s])
+        rows = _sample_rows(rng, L)
+        o_ref, l_ref = attention_fwd_rows(t["q"], t["k"], t["v"], w.scale, w.causal, cu, s, h,
+                                          rows)
+        gi = torch.as_tensor(cu[s] + np.array(rows), device=o.device)
+        e, _, _ = check_o(host64(o[gi, h]), o_ref, w.dtype, f"O seq {s} head {h}")
+        el = check_lse(host64(lse[h, gi]), l_ref, f"LSE seq {s} head {h}")
+        worst_o, worst_l = max(worst_o, e), max(worst_l, el)
+    say(f"   sampled {len(units)} (seq, head) units: max|dO|={worst_o:.2e} max|dLSE|={worst_l:.2e}")
+
+
+@pytest.mark.parametrize("N", [512, 1024, 2048, 4096, 8192])
+def test_sweep_sampled(N):
+    base = W.WORKLOADS[f"sweep_N{N}_full"]
+    a = W.generate(base)
+    for causal in (False, True):
+        w = W.WORKLOADS[f"sweep_N{N}_{'causal' if causal else 'full'}"]
+        o, lse, t = run_fwd(w, a)
+        compare_sampled(w, o, lse, t, [(0, 0), (3, 31), (1, 17)], seed=N)
+        del o, lse, t
+
+
+def test_gqa_varlen_sampled():
+    w = W.WORKLOADS["gqa_varlen"]
+    o, lse, t = run_fwd(w)
+    units = [(s, h) for s, h in zip(range(8), (0, 5, 9, 14, 18, 23, 27, 31))]
+    compare_sampled(w, o, lse, t, units, seed=4)
+
+
+def test_train_16k_forward_sampled():
+    w = W.WORKLOADS["train_16k"]
+    o, lse, t = run_fwd(w)
+    compare_sampled(w, o, lse, t, [(0, 0), (1, 15), (1, 6)], seed=5)
