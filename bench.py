@@ -1,0 +1,244 @@
+#!/usr/bin/env python3
+"""Benchmark of the fused exact-attention hot path on one MI355X.
+
+Default run (one JSON line on stdout): the training-step workload — B=2,
+H=16, N=16384, d=128, bf16, causal, Q/K/V/dO ~ N(0,1) from seed 5 — where a
+step is fa_fwd followed by fa_bwd (every stage of the path). Throughput is
+attention TFLOP/s by the usual convention: forward 4·B·H·N²·d, halved for
+causal; backward 2.5× the forward.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+    python bench.py --sweep     # forward TFLOP/s for every forward workload, one line each
+
+Inputs are resident in device memory before the timed region starts; the
+timed region is exactly K steps bracketed by device synchronisation, timed
+with HIP events on the stream the kernels are launched on.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16/fp16 MFMA: 256 CU x 4096 flop/clk x 2.4 GHz
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+
+
+def parse():
+    p = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--workload", default="train_16k")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--sweep", action="store_true",
+                   help="time fa_fwd on every forward workload (10 warmup, 100 timed calls)")
+    return p.parse_args()
+
+
+class Bound:
+    """Device buffers and raw C-ABI calls for one workload (nothing allocated per call)."""
+
+    def __init__(self, w, with_bwd: bool):
+        import torch
+        import exact_io_aware_12_amd as fa
+        import workloads as W
+        self.fa, self.w, self.torch = fa, w, torch
+        td = {"fp16": torch.float16, "bf16": torch.bfloat16}[w.dtype]
+        a = W.generate(w, with_grad=with_bwd)
+        dev = "cuda"
+        self.t = {n: torch.from_numpy(a[n]).to(td).to(dev) for n in a if n != "cu_seqlens"}
+        self.cu = torch.from_numpy(a["cu_seqlens"]).to(dev) if w.varlen else None
+        del a
+        T = w.T
+        self.o = torch.empty_like(self.t["q"])
+        self.lse = torch.empty((w.Hq, T), dtype=torch.float32, device=dev)
+        if with_bwd:
+            self.dq = torch.empty_like(self.t["q"])
+            self.dk = torch.empty_like(self.t["k"])
+            self.dv = torch.empty_like(self.t["v"])
+            nws = fa.fa_bwd_workspace_size(w.B, w.Hq, w.Hkv, w.N, w.d)
+            self.ws = torch.empty(max(nws, 1), dtype=torch.uint8, device=dev)
+        self.code = fa.FA_BF16 if w.dtype == "bf16" else fa.FA_FP16
+        self.cu_ptr = self.cu.data_ptr() if self.cu is not None else None
+        self.stream = torch.cuda.current_stream().cuda_stream
+
+    def fwd(self):
+        w, t = self.w, self.t
+        st = self.fa.fa_fwd(t["q"].data_ptr(), t["k"].data_ptr(), t["v"].data_ptr(),
+                            self.o.data_ptr(), self.lse.data_ptr(), w.B, w.Hq, w.Hkv, w.N, w.d,
+                            w.scale, int(w.causal), self.cu_ptr, self.code, self.stream)
+        if st != self.fa.FA_OK:
+            raise self.fa.FaError(st, "fa_fwd")
+
+    def _bwd_args(self):
+        w, t = self.w, self.t
+        return (t["q"].data_ptr(), t["k"].data_ptr(), t["v"].data_ptr(), self.o.data_ptr(),
+                t["do"].data_ptr(), self.lse.data_ptr(), self.dq.data_ptr(), self.dk.data_ptr(),
+                self.dv.data_ptr(), w.B, w.Hq, w.Hkv, w.N, w.d, w.scale, int(w.causal),
+                self.cu_ptr, self.code, self.ws.data_ptr(), self.ws.numel(), self.stream)
+
+    def bwd(self):
+        st = self.fa.fa_bwd(*self._bwd_args())
+        if st != self.fa.FA_OK:
+            raise self.fa.FaError(st, "fa_bwd")
+
+    def bwd_stage(self, stage):
+        st = self.fa.fa_bwd_stage(stage, *self._bwd_args())
+        if st != self.fa.FA_OK:
+            raise self.fa.FaError(st, "fa_bwd_stage")
+
+    def step(self):
+        self.fwd()
+        self.bwd()
+
+
+def time_calls(torch, fn, iters, warmup):
+    """Average ms per call with HIP events on the current stream."""
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(iters):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / iters
+
+
+def cpu_baseline(w):
+    """The float64 oracle, untouched, on one (sequence, head) unit of the workload."""
+    import numpy as np
+    import oracle.attention as O
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max((d.get("num_threads", 1) for d in threadpool_info()), default=1)
+    except Exception:  # pragma: no cover
+        cores = 1
+    rng = np.random.default_rng(w.seed)
+    L = w.seq_lens[0]
+    q, k, v, do = (rng.standard_normal((L, w.d), dtype=np.float32) for _ in range(4))
+    t0 = time.perf_counter()
+    O.head_fwd(q, k, v, w.scale, w.causal)
+    O.head_bwd(q, k, v, do, w.scale, w.causal)
+    dt = time.perf_counter() - t0
+    units = w.B * w.Hq if not w.varlen else None
+    flop_unit = (w.fwd_flop() + (w.bwd_flop() if w.backward else 0)) / units
+    return {"value": round(flop_unit / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(cores),
+            "kind": "oracle",
+            "sample": f"1 of {units} (sequence, head) units, N={L}, forward + backward, "
+                      f"{dt:.1f} s wall; algorithmic FLOP of that unit / wall time"}
+
+
+def run_step_bench(args):
+    import torch
+    import workloads as W
+    w = W.WORKLOADS[args.workload]
+    if not w.backward:
+        raise SystemExit(f"{w.name} has no backward; the step bench needs the training workload")
+    b = Bound(w, with_bwd=True)
+    flop = w.fwd_flop() + w.bwd_flop()
+
+    for _ in range(args.warmup):
+        b.step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record()
+    for _ in range(args.steps):
+        b.step()
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = e0.elapsed_time(e1) / args.steps
+
+    # per-kernel launch durations (same stream, same buffers)
+    it = max(3, min(args.steps, 20))
+    kern = {"fwd_kernel": time_calls(torch, b.fwd, it, 2)}
+    names = ["delta_kernel", "dkdv_kernel", "dq_kernel"]
+    for s, n in enumerate(names):
+        kern[n] = time_calls(torch, lambda s=s: b.bwd_stage(s), it, 2)
+    bwd_ms = sum(kern[n] for n in names)
+    alg = {  # algorithmic work per launch
+        "fwd_kernel": ("mfma", w.fwd_flop()),
+        "dkdv_kernel": ("mfma", 0.8 * w.bwd_flop()),    # S, dP, dV, dK: 4 of the 5 counted GEMMs
+        "dq_kernel": ("mfma", 0.2 * w.bwd_flop()),      # dQ: the 5th counted GEMM
+        "delta_kernel": ("hbm", 2 * w.T * w.Hq * w.d * 2 + 4 * w.T * w.Hq),
+    }
+    dom = max(kern, key=kern.get)
+    bound, work = alg[dom]
+    if bound == "mfma":
+        ach = work / (kern[dom] * 1e-3) / 1e12
+        roof = {"kernel": dom, "bound": "mfma", "achieved": round(ach, 2),
+                "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4),
+                "traffic": None, "avg_launch_ms": round(kern[dom], 4)}
+    else:
+        ach = work / (kern[dom] * 1e-3) / 1e9
+        roof = {"kernel": dom, "bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS,
+                "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": None,
+                "avg_launch_ms": round(kern[dom], 4)}
+
+    value = flop / (ms * 1e-3) / 1e12
+    out = {
+        "metric": "attention TFLOP/s (fwd+bwd training step) and % of MFMA bf16 dense peak",
+        "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",
+        "config": {"workload": f"{w.name}: fa_fwd + fa_bwd", "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv,
+                   "N": w.N, "d": w.d, "causal": w.causal, "seed": w.seed},
+        "pct_of_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
+        "fwd_tflops": round(w.fwd_flop() / (kern["fwd_kernel"] * 1e-3) / 1e12, 2),
+        "bwd_tflops": round(w.bwd_flop() / (bwd_ms * 1e-3) / 1e12, 2),
+        "kernel_ms": {k: round(v, 4) for k, v in kern.items()},
+        "wall_s_timed": round(wall, 3),
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w)
+    print(json.dumps(out), flush=True)
+
+
+def run_sweep(args):
+    import torch
+    import workloads as W
+    names = ["tiny", "causal_d64"] + [f"sweep_N{N}_{c}" for N in (512, 1024, 2048, 4096, 8192)
+                                      for c in ("full", "causal")] + ["gqa_varlen", "train_16k"]
+    for n in names:
+        w = W.WORKLOADS[n]
+        b = Bound(w, with_bwd=False)
+        ms = time_calls(torch, b.fwd, 100, 10)
+        tf = w.fwd_flop() / (ms * 1e-3) / 1e12
+        print(json.dumps({"workload": n, "N": w.N, "d": w.d, "dtype": w.dtype, "causal": w.causal,
+                          "fwd_ms": round(ms, 4), "fwd_tflops": round(tf, 2),
+                          "pct_of_peak": round(100 * tf / PEAK_BF16_TFLOPS, 2)}), flush=True)
+        del b
+        torch.cuda.empty_cache()
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(the (sequence, head) units are independent; see the sharding notes). "
+              "Run with --gpus 1.", file=sys.stderr, flush=True)
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    if args.sweep:
+        run_sweep(args)
+    else:
+        run_step_bench(args)
+
+
+if __name__ == "__main__":
+    main()

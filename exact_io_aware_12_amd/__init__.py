@@ -6,7 +6,8 @@ If the library has not been built, importing the binding raises: there is no
 fallback implementation.
 
 Raw entry points with the C names and arguments (pointers as ints):
-    fa_fwd, fa_bwd, fa_bwd_workspace_size, fa_status_string
+    fa_fwd, fa_bwd, fa_bwd_stage, fa_bwd_num_stages, fa_bwd_workspace_size,
+    fa_status_string
 Tensor-level helpers:
     flash_attn_func(q, k, v, causal=False, softmax_scale=None,
                     cu_seqlens=None, max_seqlen=None, dropout_p=0.0) -> (o, lse)
@@ -25,7 +26,7 @@ import os
 __all__ = ["FA_OK", "FA_ERR_INVALID_ARG", "FA_ERR_UNSUPPORTED", "FA_ERR_HIP", "FA_ERR_WORKSPACE",
            "FA_FP16", "FA_BF16", "FaError", "lib", "lib_path", "fa_fwd", "fa_bwd",
            "fa_bwd_workspace_size", "fa_status_string", "flash_attn_func",
-           "flash_attn_backward"]
+           "flash_attn_backward", "fa_bwd_stage", "fa_bwd_num_stages"]
 
 FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_HIP, FA_ERR_WORKSPACE = 0, -1, -2, -3, -4
 FA_FP16, FA_BF16 = 0, 1
@@ -46,14 +47,23 @@ class FaError(RuntimeError):
 def _load():
     path = lib_path()
     if not os.path.exists(path):
-        raise ImportError(f"{path} is missing: build it with `python -m exact_io_aware_12_amd.build` "
+        raise ImportError(f"{path} is missing: build it with `python exact_io_aware_12_amd/build.py` "
                           "(there is no non-HIP fallback)")
+    # torch bundles its own HIP runtime under the same soname (libamdhip64.so.7).
+    # Loading torch first makes libfa.so bind to that runtime, so the tensors torch
+    # allocates and the kernels libfa.so launches live in one runtime; loading
+    # libfa.so first would pull in a second runtime that cannot see torch's memory.
+    import torch  # noqa: F401
     L = ctypes.CDLL(path)
     vp, i, f, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
     L.fa_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp, i, vp]
     L.fa_fwd.restype = i
     L.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp, i, vp, sz, vp]
     L.fa_bwd.restype = i
+    L.fa_bwd_stage.argtypes = [i] + L.fa_bwd.argtypes
+    L.fa_bwd_stage.restype = i
+    L.fa_bwd_num_stages.argtypes = []
+    L.fa_bwd_num_stages.restype = i
     L.fa_bwd_workspace_size.argtypes = [i, i, i, i, i]
     L.fa_bwd_workspace_size.restype = sz
     L.fa_status_string.argtypes = [i]
@@ -73,6 +83,16 @@ def fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, B, Hq, Hkv, N, d, scale, causal, c
            workspace, workspace_bytes, stream) -> int:
     return lib.fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, B, Hq, Hkv, N, d, scale, causal,
                       cu_seqlens, dtype, workspace, workspace_bytes, stream)
+
+
+def fa_bwd_stage(stage, q, k, v, o, dout, lse, dq, dk, dv, B, Hq, Hkv, N, d, scale, causal,
+                 cu_seqlens, dtype, workspace, workspace_bytes, stream) -> int:
+    return lib.fa_bwd_stage(stage, q, k, v, o, dout, lse, dq, dk, dv, B, Hq, Hkv, N, d, scale,
+                            causal, cu_seqlens, dtype, workspace, workspace_bytes, stream)
+
+
+def fa_bwd_num_stages() -> int:
+    return lib.fa_bwd_num_stages()
 
 
 def fa_bwd_workspace_size(B, Hq, Hkv, N, d) -> int:

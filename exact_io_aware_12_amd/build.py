@@ -1,6 +1,8 @@
 """Build libfa.so in-tree with hipcc for gfx950.
 
-    python -m exact_io_aware_12_amd.build [--resource-usage]
+    python exact_io_aware_12_amd/build.py [--resource-usage] [-v]
+
+(run as a script: importing the package itself loads the library).
 
 Compiles every HIP source under csrc/ into exact_io_aware_12_amd/libfa.so.
 Packed fp32 VALU instructions are disabled for all device code.

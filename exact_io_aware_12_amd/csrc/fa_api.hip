@@ -72,10 +72,12 @@ size_t fa_bwd_workspace_size(int B, int Hq, int Hkv, int N, int d) {
   return (bytes + 255) / 256 * 256;
 }
 
-int fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
-           const float* lse, void* dq, void* dk, void* dv, int B, int Hq, int Hkv, int N, int d,
-           float scale, int causal, const int32_t* cu_seqlens, int dtype, void* workspace,
-           size_t workspace_bytes, hipStream_t stream) {
+namespace {
+
+int bwd_common(int stage, const void* q, const void* k, const void* v, const void* o,
+               const void* dout, const float* lse, void* dq, void* dk, void* dv, int B, int Hq,
+               int Hkv, int N, int d, float scale, int causal, const int32_t* cu_seqlens, int dtype,
+               void* workspace, size_t workspace_bytes, hipStream_t stream) {
   bool noop;
   int st = check_sizes(B, Hq, Hkv, N, d, scale, causal, dtype, &noop);
   if (st != FA_OK || noop) return st;
@@ -104,8 +106,30 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const voi
   a.group = Hq / Hkv;
   a.scale = scale;
   a.scale_log2 = scale * kLog2e;
-  hipError_t e = fa::launch_bwd(a, dtype == FA_BF16, d, causal != 0, cu_seqlens != nullptr, stream);
+  hipError_t e = fa::launch_bwd(a, dtype == FA_BF16, d, causal != 0, cu_seqlens != nullptr, stage,
+                                stream);
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+}  // namespace
+
+int fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+           const float* lse, void* dq, void* dk, void* dv, int B, int Hq, int Hkv, int N, int d,
+           float scale, int causal, const int32_t* cu_seqlens, int dtype, void* workspace,
+           size_t workspace_bytes, hipStream_t stream) {
+  return bwd_common(-1, q, k, v, o, dout, lse, dq, dk, dv, B, Hq, Hkv, N, d, scale, causal,
+                    cu_seqlens, dtype, workspace, workspace_bytes, stream);
+}
+
+int fa_bwd_num_stages(void) { return fa::bwd_num_stages(); }
+
+int fa_bwd_stage(int stage, const void* q, const void* k, const void* v, const void* o,
+                 const void* dout, const float* lse, void* dq, void* dk, void* dv, int B, int Hq,
+                 int Hkv, int N, int d, float scale, int causal, const int32_t* cu_seqlens,
+                 int dtype, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (stage < 0 || stage >= fa::bwd_num_stages()) return FA_ERR_INVALID_ARG;
+  return bwd_common(stage, q, k, v, o, dout, lse, dq, dk, dv, B, Hq, Hkv, N, d, scale, causal,
+                    cu_seqlens, dtype, workspace, workspace_bytes, stream);
 }
 
 const char* fa_status_string(int status) {

@@ -7,7 +7,8 @@
 // Σ_j P_ij·dP_ij because O_i = Σ_j P_ij·V_j):
 //   dS = P∘(dP − D),  dV = Pᵀ·dO,  dK = scale·dSᵀ·Q,  dQ = scale·dS·K.
 //
-// Three kernels on one stream, all deterministic (fixed summation order):
+// Three kernels (stages 0, 1, 2) on one stream, all deterministic (fixed
+// summation order); stages 1 and 2 both depend on stage 0 only:
 //   delta_kernel  D = rowsum(dO∘O) in float32                       (HBM bound)
 //   dkdv_kernel   one workgroup per 128-key tile of one KV head; loops over
 //                 the query heads of its group and the visible 64-query
@@ -340,39 +341,51 @@ __global__ __launch_bounds__(kThreads, 2) void dq_kernel(BwdArgs a, int n_qtiles
 }
 
 template <typename T, int D, bool CAUSAL, bool VARLEN>
-hipError_t launch(const BwdArgs& a, hipStream_t s) {
-  const int64_t rows = (int64_t)a.B * a.N * a.Hq;   // upper bound on T·Hq
-  const int rows_per_block = kThreads / (D / 8);
-  const int g0 = (int)((rows + rows_per_block - 1) / rows_per_block);
-  hipLaunchKernelGGL((delta_kernel<T, D, VARLEN>), dim3(g0), dim3(kThreads), 0, s, a);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  const int nkt = (a.N + kDkvKeys - 1) / kDkvKeys;
-  hipLaunchKernelGGL((dkdv_kernel<T, D, CAUSAL, VARLEN>), dim3(nkt * a.Hkv * a.B), dim3(kThreads),
-                     0, s, a, nkt);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  const int nqt = (a.N + kDqQ - 1) / kDqQ;
-  hipLaunchKernelGGL((dq_kernel<T, D, CAUSAL, VARLEN>), dim3(nqt * a.Hq * a.B), dim3(kThreads), 0,
-                     s, a, nqt);
-  return hipGetLastError();
+hipError_t launch(const BwdArgs& a, int stage, hipStream_t s) {
+  (void)hipGetLastError();  // drop an error left pending by earlier, unrelated HIP calls
+  if (stage < 0 || stage == 0) {
+    const int64_t rows = (int64_t)a.B * a.N * a.Hq;   // upper bound on T·Hq
+    const int rows_per_block = kThreads / (D / 8);
+    const int g0 = (int)((rows + rows_per_block - 1) / rows_per_block);
+    hipLaunchKernelGGL((delta_kernel<T, D, VARLEN>), dim3(g0), dim3(kThreads), 0, s, a);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (stage < 0 || stage == 1) {
+    const int nkt = (a.N + kDkvKeys - 1) / kDkvKeys;
+    hipLaunchKernelGGL((dkdv_kernel<T, D, CAUSAL, VARLEN>), dim3(nkt * a.Hkv * a.B),
+                       dim3(kThreads), 0, s, a, nkt);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (stage < 0 || stage == 2) {
+    const int nqt = (a.N + kDqQ - 1) / kDqQ;
+    hipLaunchKernelGGL((dq_kernel<T, D, CAUSAL, VARLEN>), dim3(nqt * a.Hq * a.B), dim3(kThreads),
+                       0, s, a, nqt);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 template <typename T, int D>
-hipError_t dispatch_mask(const BwdArgs& a, bool causal, bool varlen, hipStream_t s) {
-  if (causal) return varlen ? launch<T, D, true, true>(a, s) : launch<T, D, true, false>(a, s);
-  return varlen ? launch<T, D, false, true>(a, s) : launch<T, D, false, false>(a, s);
+hipError_t dispatch_mask(const BwdArgs& a, bool causal, bool varlen, int stage, hipStream_t s) {
+  if (causal)
+    return varlen ? launch<T, D, true, true>(a, stage, s) : launch<T, D, true, false>(a, stage, s);
+  return varlen ? launch<T, D, false, true>(a, stage, s) : launch<T, D, false, false>(a, stage, s);
 }
 
 }  // namespace
 
-hipError_t launch_bwd(const BwdArgs& a, bool bf16_in, int d, bool causal, bool varlen,
+int bwd_num_stages() { return 3; }
+
+hipError_t launch_bwd(const BwdArgs& a, bool bf16_in, int d, bool causal, bool varlen, int stage,
                       hipStream_t s) {
   if (bf16_in)
-    return d == 64 ? dispatch_mask<bf16, 64>(a, causal, varlen, s)
-                   : dispatch_mask<bf16, 128>(a, causal, varlen, s);
-  return d == 64 ? dispatch_mask<f16, 64>(a, causal, varlen, s)
-                 : dispatch_mask<f16, 128>(a, causal, varlen, s);
+    return d == 64 ? dispatch_mask<bf16, 64>(a, causal, varlen, stage, s)
+                   : dispatch_mask<bf16, 128>(a, causal, varlen, stage, s);
+  return d == 64 ? dispatch_mask<f16, 64>(a, causal, varlen, stage, s)
+                 : dispatch_mask<f16, 128>(a, causal, varlen, stage, s);
 }
 
 }  // namespace fa

@@ -177,6 +177,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_kernel(FwdArgs a) {
 template <typename T, int D, bool CAUSAL, bool VARLEN>
 hipError_t launch(const FwdArgs& a, hipStream_t stream) {
   const int grid = a.n_qtiles * a.Hq * a.B;
+  (void)hipGetLastError();  // drop an error left pending by earlier, unrelated HIP calls
   hipLaunchKernelGGL((fwd_kernel<T, D, CAUSAL, VARLEN>), dim3(grid), dim3(kThreads), 0, stream, a);
   return hipGetLastError();
 }

@@ -40,7 +40,10 @@ struct BwdArgs {
 int fwd_query_tile();
 hipError_t launch_fwd(const FwdArgs& a, bool bf16_in, int d, bool causal, bool varlen,
                       hipStream_t s);
-hipError_t launch_bwd(const BwdArgs& a, bool bf16_in, int d, bool causal, bool varlen,
+// stage < 0: every stage in order; otherwise only stage 0 (D = rowsum(dO∘O)),
+// 1 (dK, dV) or 2 (dQ).
+int bwd_num_stages();
+hipError_t launch_bwd(const BwdArgs& a, bool bf16_in, int d, bool causal, bool varlen, int stage,
                       hipStream_t s);
 
 }  // namespace fa

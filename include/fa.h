@@ -46,6 +46,8 @@
  * another attention implementation. FA_OK means the work was enqueued on
  * `stream` (NULL = the default stream); device faults surface at the caller's
  * next synchronisation. B = 0 or N = 0 is a no-op returning FA_OK.
+ * A launching call clears the calling thread's pending HIP error
+ * (hipGetLastError) first, so that FA_ERR_HIP reports its own launches only.
  *
  * Determinism: results are bitwise identical from run to run.
  */
@@ -94,6 +96,23 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o,
            int B, int Hq, int Hkv, int N, int d, float scale, int causal,
            const int32_t* cu_seqlens, int dtype,
            void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * fa_bwd is a fixed sequence of stages enqueued on one stream:
+ *   0  D = rowsum(dout∘o) into the workspace
+ *   1  dk, dv            (reads D)
+ *   2  dq                (reads D; independent of stage 1)
+ * fa_bwd_stage enqueues one stage with fa_bwd's arguments and checks, so a
+ * caller can time the stages separately or run stages 1 and 2 on two streams
+ * once stage 0 has completed. Running every stage in order equals fa_bwd.
+ * A stage index outside [0, fa_bwd_num_stages()) is FA_ERR_INVALID_ARG.
+ */
+int fa_bwd_num_stages(void);
+int fa_bwd_stage(int stage, const void* q, const void* k, const void* v, const void* o,
+                 const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                 int B, int Hq, int Hkv, int N, int d, float scale, int causal,
+                 const int32_t* cu_seqlens, int dtype,
+                 void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* Workspace bytes fa_bwd needs; an upper bound that uses T <= B·N. 0 on bad sizes. */
 size_t fa_bwd_workspace_size(int B, int Hq, int Hkv, int N, int d);

@@ -20,8 +20,8 @@ def declared_functions():
 
 
 def test_header_declares_the_boundary():
-    assert declared_functions() == ["fa_bwd", "fa_bwd_workspace_size", "fa_fwd",
-                                    "fa_status_string"]
+    assert declared_functions() == ["fa_bwd", "fa_bwd_num_stages", "fa_bwd_stage",
+                                    "fa_bwd_workspace_size", "fa_fwd", "fa_status_string"]
 
 
 def test_every_declared_symbol_is_exported():
@@ -97,6 +97,17 @@ def test_fwd_host_checks(kw, status):
 ])
 def test_bwd_host_checks(kw, status):
     assert bwd(**kw) == status
+
+
+def test_bwd_stage_index_checked():
+    assert fa.fa_bwd_num_stages() == 3
+    ptrs = [P] * 9
+    for bad in (-1, 3, 100):
+        assert fa.fa_bwd_stage(bad, *ptrs, 1, 2, 2, 16, 64, 0.125, 0, None, 0, P, 1 << 20,
+                               None) == fa.FA_ERR_INVALID_ARG
+    # a valid stage goes through fa_bwd's own checks
+    assert fa.fa_bwd_stage(1, *ptrs, 1, 2, 2, 16, 64, 0.125, 0, None, 0, None, 0,
+                           None) == fa.FA_ERR_WORKSPACE
 
 
 def test_workspace_size():
