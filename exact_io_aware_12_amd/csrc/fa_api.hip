@@ -3,7 +3,7 @@
 #include <cmath>
 #include <cstdint>
 
-#include "../../include/fa.h"
+#include "fa.h"
 #include "fa_kernels.h"
 
 namespace {

@@ -168,4 +168,100 @@ __device__ __forceinline__ void tile_to_lds_t(T* lds_t, T* lds, const T* src, in
   }
 }
 
+// ---------------------------------------------------------------------------
+// Direct global -> LDS staging (gfx950 global_load_lds, 16 bytes per lane).
+// A wave instruction writes 1 KiB of LDS: lane l's 16 bytes land in slot l.
+// Rows of a tile are D·2 bytes; the 16-byte chunks of row r are stored in the
+// order chunk ^ Swz(r), chosen per lane on the global side, so that the read
+// patterns below hit distinct LDS banks.
+
+// Rows read as MFMA operands, 16 contiguous bytes per lane (K in the forward).
+template <int D>
+__device__ __forceinline__ constexpr int swz_rows(int r) {
+  return D == 128 ? (r & 15) : ((r >> 1) & 7);
+}
+// Rows read with ds_read_b64_tr_b16 (4 rows x 32 bytes per 16-lane group).
+template <int D>
+__device__ __forceinline__ constexpr int swz_tr(int r) {
+  return D == 128 ? 4 * (r & 3) : 4 * ((r >> 1) & 1);
+}
+
+// Stage rows r0 .. r0+R-1 (row stride `rstride` elements) of a D-column tile.
+// Rows at or past L are replaced by row L-1 (L >= 1): callers mask those keys.
+// The tile is split evenly over the NW waves of the workgroup. TR selects the
+// swz_tr layout (rows read transposed), otherwise swz_rows.
+template <typename T, int R, int D, int NW, bool TR>
+__device__ __forceinline__ void tile_dma(T* lds, const T* src, int64_t rstride, int r0, int L,
+                                         int wave, int lane) {
+  constexpr int CPR = D / 8;                  // 16-byte chunks per row
+  constexpr int RPI = 64 / CPR;               // rows per wave instruction
+  constexpr int INSTS = R / RPI;
+  static_assert(INSTS % NW == 0, "tile rows must split evenly over the waves");
+#pragma unroll
+  for (int u = 0; u < INSTS / NW; ++u) {
+    const int inst = wave * (INSTS / NW) + u;
+    const int row = inst * RPI + lane / CPR;
+    const int c = (lane % CPR) ^ (TR ? swz_tr<D>(row) : swz_rows<D>(row));
+    const int srow = min(r0 + row, L - 1);
+    const T* g = src + (int64_t)srow * rstride + c * 8;
+#if defined(__HIP_DEVICE_COMPILE__)  // the host pass cannot type-check this device builtin
+    __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)(lds + inst * 512),
+                                     16, 0, 0);
+#else
+    (void)g;
+#endif
+  }
+}
+
+// 16-byte operand read from a swz_rows tile: row r, logical chunk c.
+template <typename T, int D>
+__device__ __forceinline__ u32x4 lds_row16(const T* lds, int r, int c) {
+  return *reinterpret_cast<const u32x4*>(lds + r * D + 8 * (c ^ swz_rows<D>(r)));
+}
+
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+
+// Transposed operand from a row-major swz_tr tile (rows = k, columns = n):
+// lane l receives, for MFMA slots 0..7, tile[k][n] with n = n0 + l%32 and
+// k = k0 + {0..3} (slots 0-3) and k1 + {0..3} (slots 4-7). With lane j of a
+// 16-lane group reading row k+(j>>2), columns n+4(j&3)..+3, the transposing
+// read hands lane i of the group the 4 rows of column n+i.
+template <typename T, int D>
+__device__ __forceinline__ u32x4 lds_tr8(const T* lds, int k0, int k1, int n0, int lane) {
+  const int j = lane & 15;
+  const int n = n0 + 16 * ((lane >> 4) & 1) + 4 * (j & 3);
+  const int c = n >> 3, off = n & 7;
+  const int ka = k0 + (j >> 2), kb = k1 + (j >> 2);
+  typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+  const i16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (lds_i16x4*)(lds + ka * D + 8 * (c ^ swz_tr<D>(ka)) + off));
+  const i16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (lds_i16x4*)(lds + kb * D + 8 * (c ^ swz_tr<D>(kb)) + off));
+  const u32x2 ua = __builtin_bit_cast(u32x2, a), ub = __builtin_bit_cast(u32x2, b);
+  return u32x4{ua[0], ua[1], ub[0], ub[1]};
+}
+
+// Sum of the 8 values of a packed operand (4 dwords of 2 x T), fp32 accumulate.
+template <typename T>
+__device__ __forceinline__ float dot2_sum(u32x4 p, float acc) {
+  if constexpr (__is_same(T, bf16)) {
+    const bf16x2 one = __builtin_bit_cast(bf16x2, 0x3f803f80u);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t w = p[i];  // bit_cast straight from p[i] would ignore the index
+      acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w), one, acc, false);
+    }
+  } else {
+    const f16x2 one = __builtin_bit_cast(f16x2, 0x3c003c00u);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t w = p[i];
+      acc = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, w), one, acc, false);
+    }
+  }
+  return acc;
+}
+
+__device__ __forceinline__ void wait_vmem_all() { __builtin_amdgcn_s_waitcnt(0x0f70); }
+
 }  // namespace fa

@@ -3,18 +3,22 @@
 // One workgroup = 4 wavefronts = a tile of 128 query rows of one (sequence,
 // query head); each wavefront owns 32 rows. The workgroup streams the visible
 // 64-key tiles of K and V through LDS (tiling and fusion as in the
-// FlashAttention guide, cxbdf.cn, part 2; the K/V-tiles-in-fast-memory, loop
-// over Q blocks description in Flash Attention 是什麼, adersaytech.com,
-// section 分塊計算), so S and P live only in registers.
+// FlashAttention guide, cxbdf.cn, part 2; K/V blocks in fast on-chip memory
+// with a loop over Q blocks, Flash Attention 是什麼, adersaytech.com, section
+// 分塊計算), so S and P live only in registers.
 //
 // Per 64-key tile and wavefront:
 //   Sᵀ = K·Qᵀ        32 MFMA columns = the wave's 32 queries, so every lane
 //                    owns one query row and the row statistics are lane-local
 //                    (plus one exchange between the two lane halves)
-//   online softmax   running row max m and row sum l in registers, base-2
-//                    exponentials with the scale folded in (c = scale·log2 e)
-//   Oᵀ += Vᵀ·Pᵀ      P is fed from the Sᵀ accumulator registers directly; V is
-//                    stored transposed in LDS in the matching key order
+//   online softmax   base-2 exponentials with the scale folded in
+//                    (c = scale·log2 e); the reference max is raised only when
+//                    a row's max exceeds it by more than 2^8, so P ≤ 256 and O
+//                    is rarely rescaled
+//   Oᵀ += Vᵀ·Pᵀ      P comes from the Sᵀ accumulator registers; the Vᵀ operand
+//                    is read transposed from the row-major V tile
+// K and V tiles are copied global -> LDS directly and double-buffered: the
+// next tile is in flight while the current one is computed.
 // Epilogue: O = Oᵀ/l rounded to the input type, LSE = (m·c + log2 l)·ln 2.
 #include "fa_device.h"
 #include "fa_kernels.h"
@@ -25,16 +29,16 @@ namespace {
 
 constexpr int kBR = 128;  // query rows per workgroup
 constexpr int kBC = 64;   // keys per tile
-constexpr int kThreads = 256;
+constexpr int kWaves = 4;
+constexpr int kThreads = 64 * kWaves;
+constexpr float kRescaleHeadroom = 8.f;  // log2 of the largest P before the max is raised
 
 template <typename T, int D, bool CAUSAL, bool VARLEN>
 __global__ __launch_bounds__(kThreads, 2) void fwd_kernel(FwdArgs a) {
-  constexpr int KS = D + 8;      // K tile row stride in LDS (elements), 16 B pad
-  constexpr int VS = kBC + 8;    // Vᵀ tile row stride in LDS (elements), 16 B pad
-  constexpr int NKB = D / 16;    // k steps of Q·Kᵀ
+  constexpr int NKB = D / 16;    // k steps of K·Qᵀ
   constexpr int NCB = D / 32;    // 32-row blocks of Oᵀ
-  __shared__ __attribute__((aligned(16))) T k_lds[kBC * KS];
-  __shared__ __attribute__((aligned(16))) T vt_lds[D * VS];
+  constexpr int TILE = kBC * D;  // elements per K or V tile
+  __shared__ __attribute__((aligned(1024))) T lds[2][2][TILE];   // [buffer][K, V]
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int col = lane & 31, half = lane >> 5;
@@ -66,6 +70,13 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_kernel(FwdArgs a) {
   const T* kp = static_cast<const T*>(a.k) + (int64_t)seq0 * kvs + (int64_t)g * D;
   const T* vp = static_cast<const T*>(a.v) + (int64_t)seq0 * kvs + (int64_t)g * D;
 
+  const int kv_end = CAUSAL ? min(L, q0 + kBR) : L;
+  const int ntiles = (kv_end + kBC - 1) / kBC;
+
+  // first tile in flight before anything else
+  tile_dma<T, kBC, D, kWaves, false>(lds[0][0], kp, kvs, 0, L, wave, lane);
+  tile_dma<T, kBC, D, kWaves, true>(lds[0][1], vp, kvs, 0, L, wave, lane);
+
   // ---- Q fragments (B operand of Sᵀ = K·Qᵀ), kept in registers -------------
   const int qrow = q0 + wave * 32 + col;
   u32x4 qf[NKB];
@@ -80,21 +91,21 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_kernel(FwdArgs a) {
   f32x16 o[NCB];
 #pragma unroll
   for (int cb = 0; cb < NCB; ++cb) o[cb] = f32x16{};
-  float m = -INFINITY;   // running max of the raw scores S (scale not applied)
-  float l = 0.f;         // running sum of exp2(S·c − m·c), this lane half's keys
   const float c = a.scale_log2;
-
-  const int kv_end = CAUSAL ? min(L, q0 + kBR) : L;
-  const int ntiles = (kv_end + kBC - 1) / kBC;
+  float mc = -INFINITY;   // reference max of S·c for this row
+  float l = 0.f;          // Σ P over this lane half's keys (fp32)
   const int wq_first = q0 + wave * 32, wq_last = wq_first + 31;
 
   for (int j = 0; j < ntiles; ++j) {
     const int kv0 = j * kBC;
-    __syncthreads();  // the previous tile's LDS reads are done
-    // K tile row-major; V tile transposed with the key order of perm16()
-    tile_to_lds<T, kBC, D, KS, kThreads>(k_lds, kp, kvs, kv0, L, tid);
-    tile_to_lds_t<T, kBC, D, VS, kThreads>(vt_lds, nullptr, vp, kvs, kv0, L, tid);
-    __syncthreads();
+    const T* kt = lds[j & 1][0];
+    const T* vt = lds[j & 1][1];
+    wait_vmem_all();   // this thread's copies of tile j have landed
+    __syncthreads();   // everyone's have, and tile j-1 is no longer read
+    if (j + 1 < ntiles) {
+      tile_dma<T, kBC, D, kWaves, false>(lds[(j + 1) & 1][0], kp, kvs, kv0 + kBC, L, wave, lane);
+      tile_dma<T, kBC, D, kWaves, true>(lds[(j + 1) & 1][1], vp, kvs, kv0 + kBC, L, wave, lane);
+    }
     if (CAUSAL && kv0 > wq_last) continue;  // every key of the tile is after this wave's rows
 
     // ---- Sᵀ = K·Qᵀ ----------------------------------------------------------
@@ -102,10 +113,8 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_kernel(FwdArgs a) {
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) {
 #pragma unroll
-      for (int jb = 0; jb < 2; ++jb) {
-        const u32x4 kf = lds16(k_lds + (jb * 32 + col) * KS + kb * 16 + half * 8);
-        s[jb] = mfma32<T>(kf, qf[kb], s[jb]);
-      }
+      for (int jb = 0; jb < 2; ++jb)
+        s[jb] = mfma32<T>(lds_row16<T, D>(kt, jb * 32 + col, 2 * kb + half), qf[kb], s[jb]);
     }
 
     // ---- mask: keys past the sequence end, keys after the query (causal) ---
@@ -120,39 +129,40 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_kernel(FwdArgs a) {
         }
     }
 
-    // ---- online softmax ----------------------------------------------------
+    // ---- online softmax with a lazily raised reference max -----------------
     float mx = s[0][0];
 #pragma unroll
     for (int i = 1; i < 16; ++i) mx = fmaxf(mx, s[0][i]);
 #pragma unroll
     for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[1][i]);
-    mx = wave_max_halves(mx);
-    const float m_new = fmaxf(m, mx);        // finite: key 0 is seen in tile 0
-    const float alpha = fast_exp2((m - m_new) * c);
-    const float mc = m_new * c;
-    float rs = 0.f;
+    const float mxc = wave_max_halves(mx) * c;
+    if (__builtin_amdgcn_ballot_w64(mxc > mc + kRescaleHeadroom) != 0) {   // wave-uniform
+      const float mc_new = fmaxf(mc, mxc);     // finite: key 0 is seen in tile 0
+      const float alpha = fast_exp2(mc - mc_new);
+      l *= alpha;
+#pragma unroll
+      for (int cb = 0; cb < NCB; ++cb) o[cb] *= alpha;
+      mc = mc_new;
+    }
+    // row sum in fp32 from the unrounded P: LSE carries no rounding of P
+    float ls[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int jb = 0; jb < 2; ++jb)
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        const float p = fast_exp2(fmaf(s[jb][i], c, -mc));
-        s[jb][i] = p;
-        rs += p;
+        s[jb][i] = fast_exp2(fmaf(s[jb][i], c, -mc));
+        ls[i & 3] += s[jb][i];
       }
-    l = fmaf(l, alpha, rs);
-    m = m_new;
-#pragma unroll
-    for (int cb = 0; cb < NCB; ++cb) o[cb] *= alpha;
+    l += (ls[0] + ls[1]) + (ls[2] + ls[3]);
 
     // ---- Oᵀ += Vᵀ·Pᵀ ---------------------------------------------------------
 #pragma unroll
     for (int kk = 0; kk < kBC / 16; ++kk) {
       const u32x4 pf = acc_operand<T>(s[kk >> 1], (kk & 1) * 2);
+      const int k0 = kk * 16 + 4 * half;
 #pragma unroll
-      for (int cb = 0; cb < NCB; ++cb) {
-        const u32x4 vf = lds16(vt_lds + (cb * 32 + col) * VS + kk * 16 + half * 8);
-        o[cb] = mfma32<T>(vf, pf, o[cb]);
-      }
+      for (int cb = 0; cb < NCB; ++cb)
+        o[cb] = mfma32<T>(lds_tr8<T, D>(vt, k0, k0 + 8, cb * 32, lane), pf, o[cb]);
     }
   }
 
@@ -170,7 +180,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_kernel(FwdArgs a) {
         w[1] = pack2<T>(o[cb][4 * r + 2] * inv, o[cb][4 * r + 3] * inv);
         *reinterpret_cast<u32x2*>(op + cb * 32 + 8 * r + 4 * half) = w;
       }
-    if (half == 0) a.lse[(int64_t)h * T_total + seq0 + qrow] = (m * c + log2f(l_tot)) * kLn2;
+    if (half == 0) a.lse[(int64_t)h * T_total + seq0 + qrow] = (mc + log2f(l_tot)) * kLn2;
   }
 }
 
