@@ -67,8 +67,9 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int
 size_t fa_bwd_workspace_size(int B, int Hq, int Hkv, int N, int d) {
   bool noop;
   if (check_sizes(B, Hq, Hkv, N, d, 1.f, 0, FA_FP16, &noop) != FA_OK) return 0;
-  // D = rowsum(dO∘O): float32 [Hq, T], T <= B·N; 256-byte granule
-  const size_t bytes = (size_t)B * N * Hq * sizeof(float);
+  // D = rowsum(dO∘O) and LSE·log2(e): two float32 [Hq][B·N + 64] arrays
+  // (tiles may read up to 63 rows past a sequence end); 256-byte granule
+  const size_t bytes = 2 * (size_t)Hq * ((size_t)B * N + 64) * sizeof(float);
   return (bytes + 255) / 256 * 256;
 }
 
@@ -97,7 +98,9 @@ int bwd_common(int stage, const void* q, const void* k, const void* v, const voi
   a.dq = dq;
   a.dk = dk;
   a.dv = dv;
+  a.ws_stride = B * N + 64;
   a.delta = static_cast<float*>(workspace);
+  a.lse2 = a.delta + (size_t)Hq * a.ws_stride;
   a.cu_seqlens = cu_seqlens;
   a.B = B;
   a.Hq = Hq;

@@ -9,12 +9,15 @@
 //
 // Three kernels (stages 0, 1, 2) on one stream, all deterministic (fixed
 // summation order); stages 1 and 2 both depend on stage 0 only:
-//   delta_kernel  D = rowsum(dO∘O) in float32                       (HBM bound)
+//   delta_kernel  D = rowsum(dO∘O) and LSE·log2 e, float32      (HBM bound)
 //   dkdv_kernel   one workgroup per 128-key tile of one KV head; loops over
 //                 the query heads of its group and the visible 64-query
 //                 tiles; dKᵀ and dVᵀ accumulate in registers
 //   dq_kernel     one workgroup per 128-query tile of one query head; loops
 //                 over the visible 64-key tiles; dQᵀ accumulates in registers
+// Q/dO (stage 1) and K/V (stage 2) tiles are copied global -> LDS directly,
+// double-buffered, one barrier per tile. The transposed operands (Qᵀ, dOᵀ,
+// Kᵀ) are read from the same row-major tiles with the transposing LDS read.
 #include "fa_device.h"
 #include "fa_kernels.h"
 
@@ -23,6 +26,7 @@ namespace fa {
 namespace {
 
 constexpr int kThreads = 256;
+constexpr int kWaves = 4;
 
 struct SeqInfo {
   int seq0, L, T;
@@ -50,7 +54,8 @@ __device__ __forceinline__ float hi_f(uint32_t w) {
 }
 
 // ---------------------------------------------------------------------------
-// D_i = Σ_c dO[i,c]·O[i,c]; D/8 consecutive threads share one (token, head) row.
+// D_i = Σ_c dO[i,c]·O[i,c] and LSE_i·log2 e; D/8 consecutive threads share one
+// (token, head) row.
 template <typename T, int D, bool VARLEN>
 __global__ __launch_bounds__(kThreads) void delta_kernel(BwdArgs a) {
   constexpr int TPR = D / 8;
@@ -72,7 +77,27 @@ __global__ __launch_bounds__(kThreads) void delta_kernel(BwdArgs a) {
   for (int off = TPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
   if (row < rows && part == 0) {
     const int t = (int)(row / a.Hq), h = (int)(row % a.Hq);
-    a.delta[(int64_t)h * T_total + t] = acc;
+    a.delta[(int64_t)h * a.ws_stride + t] = acc;
+    a.lse2[(int64_t)h * a.ws_stride + t] = a.lse[(int64_t)h * T_total + t] * kLog2e;
+  }
+}
+
+// Copy R floats of LSE·log2 e and of D (rows q0 .. q0+R-1 of one head) into
+// lds[0..R-1] and lds[R..2R-1]: one instruction, lanes 0 .. R/2-1 of one wave.
+// Rows past the sequence end read neighbouring workspace entries; the callers
+// mask those rows.
+template <int R>
+__device__ __forceinline__ void rows_dma(float* lds, const float* lse2, const float* delta,
+                                         int lane) {
+  constexpr int LN = R / 4;   // lanes per array
+  if (lane < 2 * LN) {
+    const float* g = lane < LN ? lse2 + 4 * lane : delta + 4 * (lane - LN);
+#if defined(__HIP_DEVICE_COMPILE__)
+    __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)lds, 16, 0, 0);
+#else
+    (void)g;
+    (void)lds;
+#endif
   }
 }
 
@@ -82,19 +107,16 @@ __global__ __launch_bounds__(kThreads) void delta_kernel(BwdArgs a) {
 // which is exactly the B-operand layout dVᵀ = dOᵀ·P and dKᵀ = Qᵀ·dS need.
 constexpr int kDkvKeys = 128;   // keys per workgroup (32 per wave)
 constexpr int kDkvQ = 64;       // queries per inner tile
+constexpr int kDkvQB = kDkvQ / 32;   // 32-query MFMA blocks per inner tile
 
 template <typename T, int D, bool CAUSAL, bool VARLEN>
 __global__ __launch_bounds__(kThreads, 1) void dkdv_kernel(BwdArgs a, int n_ktiles) {
-  constexpr int RS = D + 8;        // row-major tile stride (elements)
-  constexpr int TS = kDkvQ + 8;    // transposed tile stride (elements)
   constexpr int NKB = D / 16;
   constexpr int NCB = D / 32;
-  __shared__ __attribute__((aligned(16))) T q_lds[kDkvQ * RS];
-  __shared__ __attribute__((aligned(16))) T do_lds[kDkvQ * RS];
-  __shared__ __attribute__((aligned(16))) T qt_lds[D * TS];
-  __shared__ __attribute__((aligned(16))) T dot_lds[D * TS];
-  __shared__ __attribute__((aligned(16))) float lse_lds[kDkvQ];   // LSE·log2 e
-  __shared__ __attribute__((aligned(16))) float dl_lds[kDkvQ];    // D
+  constexpr int TILE = kDkvQ * D;
+  __shared__ __attribute__((aligned(1024))) T q_lds[2][TILE];
+  __shared__ __attribute__((aligned(1024))) T do_lds[2][TILE];
+  __shared__ __attribute__((aligned(16))) float ld_lds[2][2 * kDkvQ];   // LSE·log2 e, D
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int col = lane & 31, half = lane >> 5;
@@ -111,6 +133,31 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_kernel(BwdArgs a, int n_ktil
 
   const int64_t qs = (int64_t)a.Hq * D, kvs = (int64_t)a.Hkv * D;
   const int key = k0 + wave * 32 + col;
+  const int qt_begin = CAUSAL ? k0 / kDkvQ : 0;
+  const int nqt = (L + kDkvQ - 1) / kDkvQ - qt_begin;   // visible query tiles per head
+  const int ntile = a.group * nqt;                      // (head, query tile) pairs
+
+  // source pointers of tile i = (head r, query tile qt)
+  auto tile_src = [&](int i, const T*& qp, const T*& dop, const float*& lp, const float*& dp,
+                      int& q0) {
+    const int r = i / nqt, h = g * a.group + r;
+    q0 = (qt_begin + i % nqt) * kDkvQ;
+    qp = static_cast<const T*>(a.q) + (int64_t)si.seq0 * qs + (int64_t)h * D;
+    dop = static_cast<const T*>(a.dout) + (int64_t)si.seq0 * qs + (int64_t)h * D;
+    lp = a.lse2 + (int64_t)h * a.ws_stride + si.seq0 + q0;
+    dp = a.delta + (int64_t)h * a.ws_stride + si.seq0 + q0;
+  };
+  auto issue = [&](int i, int buf) {
+    const T *qp, *dop;
+    const float *lp, *dp;
+    int q0;
+    tile_src(i, qp, dop, lp, dp, q0);
+    tile_dma<T, kDkvQ, D, kWaves>(q_lds[buf], qp, qs, q0, L, wave, lane);
+    tile_dma<T, kDkvQ, D, kWaves>(do_lds[buf], dop, qs, q0, L, wave, lane);
+    if (wave == 0) rows_dma<kDkvQ>(ld_lds[buf], lp, dp, lane);
+  };
+  if (ntile > 0) issue(0, 0);
+
   // K and V fragments of this wave's 32 keys (B operands), kept in registers
   u32x4 kf[NKB], vf[NKB];
   {
@@ -130,73 +177,65 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_kernel(BwdArgs a, int n_ktil
   }
   const float c = a.scale_log2;
   const int wk_first = k0 + wave * 32, wk_last = wk_first + 31;
-  const int qt_begin = CAUSAL ? k0 / kDkvQ : 0;
-  const int nqt = (L + kDkvQ - 1) / kDkvQ;
 
-  for (int r = 0; r < a.group; ++r) {
-    const int h = g * a.group + r;
-    const T* qp = static_cast<const T*>(a.q) + (int64_t)si.seq0 * qs + (int64_t)h * D;
-    const T* dop = static_cast<const T*>(a.dout) + (int64_t)si.seq0 * qs + (int64_t)h * D;
-    const float* lsep = a.lse + (int64_t)h * si.T + si.seq0;
-    const float* dlp = a.delta + (int64_t)h * si.T + si.seq0;
+  for (int i = 0; i < ntile; ++i) {
+    const int buf = i & 1;
+    wait_vmem_all();   // this thread's copies of tile i have landed
+    __syncthreads();   // everyone's have; tile i-1 is no longer read
+    if (i + 1 < ntile) issue(i + 1, buf ^ 1);
+    const int q0 = (qt_begin + i % nqt) * kDkvQ;
+    if (CAUSAL && q0 + kDkvQ - 1 < wk_first) continue;   // all queries before this wave's keys
+    const T* qt_ = q_lds[buf];
+    const T* dot_ = do_lds[buf];
+    const float* ld = ld_lds[buf];
 
-    for (int qt = qt_begin; qt < nqt; ++qt) {
-      const int q0 = qt * kDkvQ;
-      __syncthreads();
-      tile_to_lds_t<T, kDkvQ, D, TS, kThreads, true, RS>(qt_lds, q_lds, qp, qs, q0, L, tid);
-      tile_to_lds_t<T, kDkvQ, D, TS, kThreads, true, RS>(dot_lds, do_lds, dop, qs, q0, L, tid);
-      if (tid < kDkvQ) {
-        const int qi = q0 + tid;
-        lse_lds[tid] = qi < L ? lsep[qi] * kLog2e : INFINITY;   // P = 0 past the end
-        dl_lds[tid] = qi < L ? dlp[qi] : 0.f;
+    // S = Q·Kᵀ and dP = dO·Vᵀ, in blocks of 32 queries
+    f32x16 s[kDkvQB], dp[kDkvQB];
+#pragma unroll
+    for (int qb = 0; qb < kDkvQB; ++qb) s[qb] = dp[qb] = f32x16{};
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) {
+#pragma unroll
+      for (int qb = 0; qb < kDkvQB; ++qb) {
+        s[qb] = mfma32<T>(lds_row16<T, D>(qt_, qb * 32 + col, 2 * kb + half), kf[kb], s[qb]);
+        dp[qb] = mfma32<T>(lds_row16<T, D>(dot_, qb * 32 + col, 2 * kb + half), vf[kb], dp[qb]);
       }
-      __syncthreads();
-      if (CAUSAL && q0 + kDkvQ - 1 < wk_first) continue;   // all queries before this wave's keys
-
-      // S = Q·Kᵀ and dP = dO·Vᵀ: 2 blocks of 32 queries each
-      f32x16 s[2] = {f32x16{}, f32x16{}}, dp[2] = {f32x16{}, f32x16{}};
+    }
+    // P = exp2(S·c − LSE·log2 e), dS = P∘(dP − D); 0 for queries past the end
+    // and, causally, for keys after the query
+    const bool edge = (q0 + kDkvQ > L) || (CAUSAL && q0 < wk_last);
 #pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) {
+    for (int qb = 0; qb < kDkvQB; ++qb)
 #pragma unroll
-        for (int qb = 0; qb < 2; ++qb) {
-          const u32x4 qa = lds16(q_lds + (qb * 32 + col) * RS + kb * 16 + half * 8);
-          s[qb] = mfma32<T>(qa, kf[kb], s[qb]);
-          const u32x4 da = lds16(do_lds + (qb * 32 + col) * RS + kb * 16 + half * 8);
-          dp[qb] = mfma32<T>(da, vf[kb], dp[qb]);
-        }
-      }
-      // P = exp2(S·c − LSE·log2 e), dS = P∘(dP − D); causal: key > query → 0
-      const bool edge = CAUSAL && q0 < wk_last;
+      for (int rr = 0; rr < 4; ++rr) {
+        const int qoff = qb * 32 + 8 * rr + 4 * half;
+        const float4 lv = *reinterpret_cast<const float4*>(ld + qoff);
+        const float4 dv4 = *reinterpret_cast<const float4*>(ld + kDkvQ + qoff);
+        const float lsev[4] = {lv.x, lv.y, lv.z, lv.w};
+        const float dlv[4] = {dv4.x, dv4.y, dv4.z, dv4.w};
 #pragma unroll
-      for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr) {
-          const int qoff = qb * 32 + 8 * rr + 4 * half;
-          const float4 lv = *reinterpret_cast<const float4*>(lse_lds + qoff);
-          const float4 dv4 = *reinterpret_cast<const float4*>(dl_lds + qoff);
-          const float lsev[4] = {lv.x, lv.y, lv.z, lv.w};
-          const float dlv[4] = {dv4.x, dv4.y, dv4.z, dv4.w};
-#pragma unroll
-          for (int t = 0; t < 4; ++t) {
-            const int i = 4 * rr + t;
-            float p = fast_exp2(fmaf(s[qb][i], c, -lsev[t]));
-            if (edge && key > q0 + qoff + t) p = 0.f;
-            s[qb][i] = p;
-            dp[qb][i] = p * (dp[qb][i] - dlv[t]);
+        for (int t = 0; t < 4; ++t) {
+          const int i4 = 4 * rr + t;
+          float p = fast_exp2(fmaf(s[qb][i4], c, -lsev[t]));
+          float ds = p * (dp[qb][i4] - dlv[t]);
+          if (edge) {   // rows past the end hold workspace padding: zero P and dS outright
+            const int q = q0 + qoff + t;
+            if (q >= L || (CAUSAL && key > q)) p = ds = 0.f;
           }
+          s[qb][i4] = p;
+          dp[qb][i4] = ds;
         }
-      // dVᵀ += dOᵀ·P and dKᵀ += Qᵀ·dS over the tile's 64 queries
+      }
+    // dVᵀ += dOᵀ·P and dKᵀ += Qᵀ·dS over the tile's 64 queries
 #pragma unroll
-      for (int kk = 0; kk < kDkvQ / 16; ++kk) {
-        const u32x4 pb = acc_operand<T>(s[kk >> 1], (kk & 1) * 2);
-        const u32x4 sb = acc_operand<T>(dp[kk >> 1], (kk & 1) * 2);
+    for (int kk = 0; kk < kDkvQ / 16; ++kk) {
+      const u32x4 pb = acc_operand<T>(s[kk >> 1], (kk & 1) * 2);
+      const u32x4 sb = acc_operand<T>(dp[kk >> 1], (kk & 1) * 2);
+      const int kq = kk * 16 + 4 * half;
 #pragma unroll
-        for (int cb = 0; cb < NCB; ++cb) {
-          const u32x4 doa = lds16(dot_lds + (cb * 32 + col) * TS + kk * 16 + half * 8);
-          dvt[cb] = mfma32<T>(doa, pb, dvt[cb]);
-          const u32x4 qa = lds16(qt_lds + (cb * 32 + col) * TS + kk * 16 + half * 8);
-          dkt[cb] = mfma32<T>(qa, sb, dkt[cb]);
-        }
+      for (int cb = 0; cb < NCB; ++cb) {
+        dvt[cb] = mfma32<T>(lds_tr8<T, D>(dot_, kq, kq + 8, cb * 32, lane), pb, dvt[cb]);
+        dkt[cb] = mfma32<T>(lds_tr8<T, D>(qt_, kq, kq + 8, cb * 32, lane), sb, dkt[cb]);
       }
     }
   }
@@ -225,19 +264,16 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_kernel(BwdArgs a, int n_ktil
 // ---------------------------------------------------------------------------
 // dQ. Orientation Sᵀ = K·Qᵀ as in the forward: one query per lane, so LSE and
 // D are per-lane scalars and the dSᵀ accumulator is the B operand of
-// dQᵀ = Kᵀ·dSᵀ (K stored transposed in LDS with the perm16 key order).
+// dQᵀ = Kᵀ·dSᵀ (Kᵀ read transposed from the row-major K tile).
 constexpr int kDqQ = 128;   // queries per workgroup (32 per wave)
 constexpr int kDqK = 64;    // keys per tile
 
 template <typename T, int D, bool CAUSAL, bool VARLEN>
 __global__ __launch_bounds__(kThreads, 2) void dq_kernel(BwdArgs a, int n_qtiles) {
-  constexpr int RS = D + 8;
-  constexpr int TS = kDqK + 8;
   constexpr int NKB = D / 16;
   constexpr int NCB = D / 32;
-  __shared__ __attribute__((aligned(16))) T k_lds[kDqK * RS];
-  __shared__ __attribute__((aligned(16))) T v_lds[kDqK * RS];
-  __shared__ __attribute__((aligned(16))) T kt_lds[D * TS];
+  constexpr int TILE = kDqK * D;
+  __shared__ __attribute__((aligned(1024))) T lds[2][2][TILE];   // [buffer][K, V]
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int col = lane & 31, half = lane >> 5;
@@ -257,10 +293,14 @@ __global__ __launch_bounds__(kThreads, 2) void dq_kernel(BwdArgs a, int n_qtiles
   const int64_t qs = (int64_t)a.Hq * D, kvs = (int64_t)a.Hkv * D;
   const T* kp = static_cast<const T*>(a.k) + (int64_t)si.seq0 * kvs + (int64_t)g * D;
   const T* vp = static_cast<const T*>(a.v) + (int64_t)si.seq0 * kvs + (int64_t)g * D;
+  const int kv_end = CAUSAL ? min(L, q0 + kDqQ) : L;
+  const int ntiles = (kv_end + kDqK - 1) / kDqK;
+  tile_dma<T, kDqK, D, kWaves>(lds[0][0], kp, kvs, 0, L, wave, lane);
+  tile_dma<T, kDqK, D, kWaves>(lds[0][1], vp, kvs, 0, L, wave, lane);
 
   const int qrow = q0 + wave * 32 + col;
   u32x4 qf[NKB], df[NKB];
-  float lse2 = INFINITY, dl = 0.f;
+  float lse2 = 0.f, dl = 0.f;
   {
     const int64_t off = (int64_t)(si.seq0 + qrow) * qs + (int64_t)h * D;
     const T* qp = static_cast<const T*>(a.q) + off;
@@ -271,24 +311,26 @@ __global__ __launch_bounds__(kThreads, 2) void dq_kernel(BwdArgs a, int n_qtiles
       df[kb] = qrow < L ? ldg16(dop + kb * 16 + half * 8) : u32x4{0, 0, 0, 0};
     }
     if (qrow < L) {
-      lse2 = a.lse[(int64_t)h * si.T + si.seq0 + qrow] * kLog2e;
-      dl = a.delta[(int64_t)h * si.T + si.seq0 + qrow];
+      lse2 = a.lse2[(int64_t)h * a.ws_stride + si.seq0 + qrow];
+      dl = a.delta[(int64_t)h * a.ws_stride + si.seq0 + qrow];
     }
   }
   f32x16 dqt[NCB];
 #pragma unroll
   for (int cb = 0; cb < NCB; ++cb) dqt[cb] = f32x16{};
   const float c = a.scale_log2;
-  const int kv_end = CAUSAL ? min(L, q0 + kDqQ) : L;
-  const int ntiles = (kv_end + kDqK - 1) / kDqK;
   const int wq_first = q0 + wave * 32, wq_last = wq_first + 31;
 
   for (int j = 0; j < ntiles; ++j) {
     const int kv0 = j * kDqK;
+    const T* kt = lds[j & 1][0];
+    const T* vt = lds[j & 1][1];
+    wait_vmem_all();
     __syncthreads();
-    tile_to_lds_t<T, kDqK, D, TS, kThreads, true, RS>(kt_lds, k_lds, kp, kvs, kv0, L, tid);
-    tile_to_lds<T, kDqK, D, RS, kThreads>(v_lds, vp, kvs, kv0, L, tid);
-    __syncthreads();
+    if (j + 1 < ntiles) {
+      tile_dma<T, kDqK, D, kWaves>(lds[(j + 1) & 1][0], kp, kvs, kv0 + kDqK, L, wave, lane);
+      tile_dma<T, kDqK, D, kWaves>(lds[(j + 1) & 1][1], vp, kvs, kv0 + kDqK, L, wave, lane);
+    }
     if (CAUSAL && kv0 > wq_last) continue;
 
     f32x16 s[2] = {f32x16{}, f32x16{}}, dp[2] = {f32x16{}, f32x16{}};
@@ -296,10 +338,8 @@ __global__ __launch_bounds__(kThreads, 2) void dq_kernel(BwdArgs a, int n_qtiles
     for (int kb = 0; kb < NKB; ++kb) {
 #pragma unroll
       for (int jb = 0; jb < 2; ++jb) {
-        const u32x4 ka = lds16(k_lds + (jb * 32 + col) * RS + kb * 16 + half * 8);
-        s[jb] = mfma32<T>(ka, qf[kb], s[jb]);
-        const u32x4 va = lds16(v_lds + (jb * 32 + col) * RS + kb * 16 + half * 8);
-        dp[jb] = mfma32<T>(va, df[kb], dp[jb]);
+        s[jb] = mfma32<T>(lds_row16<T, D>(kt, jb * 32 + col, 2 * kb + half), qf[kb], s[jb]);
+        dp[jb] = mfma32<T>(lds_row16<T, D>(vt, jb * 32 + col, 2 * kb + half), df[kb], dp[jb]);
       }
     }
     const bool edge = (kv0 + kDqK > L) || (CAUSAL && kv0 + kDqK - 1 > wq_first);
@@ -317,11 +357,10 @@ __global__ __launch_bounds__(kThreads, 2) void dq_kernel(BwdArgs a, int n_qtiles
 #pragma unroll
     for (int kk = 0; kk < kDqK / 16; ++kk) {
       const u32x4 sb = acc_operand<T>(dp[kk >> 1], (kk & 1) * 2);
+      const int kq = kk * 16 + 4 * half;
 #pragma unroll
-      for (int cb = 0; cb < NCB; ++cb) {
-        const u32x4 ka = lds16(kt_lds + (cb * 32 + col) * TS + kk * 16 + half * 8);
-        dqt[cb] = mfma32<T>(ka, sb, dqt[cb]);
-      }
+      for (int cb = 0; cb < NCB; ++cb)
+        dqt[cb] = mfma32<T>(lds_tr8<T, D>(kt, kq, kq + 8, cb * 32, lane), sb, dqt[cb]);
     }
   }
 

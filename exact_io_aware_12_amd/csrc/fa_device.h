@@ -171,26 +171,20 @@ __device__ __forceinline__ void tile_to_lds_t(T* lds_t, T* lds, const T* src, in
 // ---------------------------------------------------------------------------
 // Direct global -> LDS staging (gfx950 global_load_lds, 16 bytes per lane).
 // A wave instruction writes 1 KiB of LDS: lane l's 16 bytes land in slot l.
-// Rows of a tile are D·2 bytes; the 16-byte chunks of row r are stored in the
-// order chunk ^ Swz(r), chosen per lane on the global side, so that the read
-// patterns below hit distinct LDS banks.
-
-// Rows read as MFMA operands, 16 contiguous bytes per lane (K in the forward).
+// Tiles are row-major with D·2-byte rows; the 16-byte chunks of row r are
+// stored in the order chunk ^ swz(r), chosen per lane on the global side.
+// The permutation makes both read patterns below bank-conflict free (64
+// banks x 4 bytes): 16 lanes reading one chunk of 16 consecutive rows, and
+// 32 lanes reading 4 consecutive rows x 32 columns with the transposing read.
 template <int D>
-__device__ __forceinline__ constexpr int swz_rows(int r) {
-  return D == 128 ? (r & 15) : ((r >> 1) & 7);
-}
-// Rows read with ds_read_b64_tr_b16 (4 rows x 32 bytes per 16-lane group).
-template <int D>
-__device__ __forceinline__ constexpr int swz_tr(int r) {
-  return D == 128 ? 4 * (r & 3) : 4 * ((r >> 1) & 1);
+__device__ __forceinline__ constexpr int swz(int r) {
+  return D == 128 ? (((r & 3) << 2) | ((r >> 2) & 3)) : ((((r >> 1) & 1) << 2) | ((r >> 2) & 3));
 }
 
 // Stage rows r0 .. r0+R-1 (row stride `rstride` elements) of a D-column tile.
-// Rows at or past L are replaced by row L-1 (L >= 1): callers mask those keys.
-// The tile is split evenly over the NW waves of the workgroup. TR selects the
-// swz_tr layout (rows read transposed), otherwise swz_rows.
-template <typename T, int R, int D, int NW, bool TR>
+// Rows at or past L are replaced by row L-1 (L >= 1): callers mask them.
+// The tile is split evenly over the NW waves of the workgroup.
+template <typename T, int R, int D, int NW>
 __device__ __forceinline__ void tile_dma(T* lds, const T* src, int64_t rstride, int r0, int L,
                                          int wave, int lane) {
   constexpr int CPR = D / 8;                  // 16-byte chunks per row
@@ -201,7 +195,7 @@ __device__ __forceinline__ void tile_dma(T* lds, const T* src, int64_t rstride, 
   for (int u = 0; u < INSTS / NW; ++u) {
     const int inst = wave * (INSTS / NW) + u;
     const int row = inst * RPI + lane / CPR;
-    const int c = (lane % CPR) ^ (TR ? swz_tr<D>(row) : swz_rows<D>(row));
+    const int c = (lane % CPR) ^ swz<D>(row);
     const int srow = min(r0 + row, L - 1);
     const T* g = src + (int64_t)srow * rstride + c * 8;
 #if defined(__HIP_DEVICE_COMPILE__)  // the host pass cannot type-check this device builtin
@@ -213,16 +207,16 @@ __device__ __forceinline__ void tile_dma(T* lds, const T* src, int64_t rstride, 
   }
 }
 
-// 16-byte operand read from a swz_rows tile: row r, logical chunk c.
+// 16-byte operand read: row r, logical chunk c (8 elements from column 8c).
 template <typename T, int D>
 __device__ __forceinline__ u32x4 lds_row16(const T* lds, int r, int c) {
-  return *reinterpret_cast<const u32x4*>(lds + r * D + 8 * (c ^ swz_rows<D>(r)));
+  return *reinterpret_cast<const u32x4*>(lds + r * D + 8 * (c ^ swz<D>(r)));
 }
 
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 
-// Transposed operand from a row-major swz_tr tile (rows = k, columns = n):
-// lane l receives, for MFMA slots 0..7, tile[k][n] with n = n0 + l%32 and
+// Transposed operand from a row-major tile (rows = k, columns = n): lane l
+// receives, for MFMA slots 0..7, tile[k][n] with n = n0 + l%32 and
 // k = k0 + {0..3} (slots 0-3) and k1 + {0..3} (slots 4-7). With lane j of a
 // 16-lane group reading row k+(j>>2), columns n+4(j&3)..+3, the transposing
 // read hands lane i of the group the 4 rows of column n+i.
@@ -234,9 +228,9 @@ __device__ __forceinline__ u32x4 lds_tr8(const T* lds, int k0, int k1, int n0, i
   const int ka = k0 + (j >> 2), kb = k1 + (j >> 2);
   typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
   const i16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (lds_i16x4*)(lds + ka * D + 8 * (c ^ swz_tr<D>(ka)) + off));
+      (lds_i16x4*)(lds + ka * D + 8 * (c ^ swz<D>(ka)) + off));
   const i16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (lds_i16x4*)(lds + kb * D + 8 * (c ^ swz_tr<D>(kb)) + off));
+      (lds_i16x4*)(lds + kb * D + 8 * (c ^ swz<D>(kb)) + off));
   const u32x2 ua = __builtin_bit_cast(u32x2, a), ub = __builtin_bit_cast(u32x2, b);
   return u32x4{ua[0], ua[1], ub[0], ub[1]};
 }

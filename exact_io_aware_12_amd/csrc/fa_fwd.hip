@@ -74,8 +74,8 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_kernel(FwdArgs a) {
   const int ntiles = (kv_end + kBC - 1) / kBC;
 
   // first tile in flight before anything else
-  tile_dma<T, kBC, D, kWaves, false>(lds[0][0], kp, kvs, 0, L, wave, lane);
-  tile_dma<T, kBC, D, kWaves, true>(lds[0][1], vp, kvs, 0, L, wave, lane);
+  tile_dma<T, kBC, D, kWaves>(lds[0][0], kp, kvs, 0, L, wave, lane);
+  tile_dma<T, kBC, D, kWaves>(lds[0][1], vp, kvs, 0, L, wave, lane);
 
   // ---- Q fragments (B operand of Sᵀ = K·Qᵀ), kept in registers -------------
   const int qrow = q0 + wave * 32 + col;
@@ -103,8 +103,8 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_kernel(FwdArgs a) {
     wait_vmem_all();   // this thread's copies of tile j have landed
     __syncthreads();   // everyone's have, and tile j-1 is no longer read
     if (j + 1 < ntiles) {
-      tile_dma<T, kBC, D, kWaves, false>(lds[(j + 1) & 1][0], kp, kvs, kv0 + kBC, L, wave, lane);
-      tile_dma<T, kBC, D, kWaves, true>(lds[(j + 1) & 1][1], vp, kvs, kv0 + kBC, L, wave, lane);
+      tile_dma<T, kBC, D, kWaves>(lds[(j + 1) & 1][0], kp, kvs, kv0 + kBC, L, wave, lane);
+      tile_dma<T, kBC, D, kWaves>(lds[(j + 1) & 1][1], vp, kvs, kv0 + kBC, L, wave, lane);
     }
     if (CAUSAL && kv0 > wq_last) continue;  // every key of the tile is after this wave's rows
 

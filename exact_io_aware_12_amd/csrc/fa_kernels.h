@@ -29,7 +29,9 @@ struct BwdArgs {
   void* dq;
   void* dk;
   void* dv;
-  float* delta;               // workspace: rowsum(dO∘O), [Hq, T] float32
+  float* delta;               // workspace: rowsum(dO∘O), [Hq][ws_stride] float32
+  float* lse2;                // workspace: LSE·log2(e), [Hq][ws_stride] float32
+  int ws_stride;              // B·N + 64: rows may be read up to 63 past a sequence end
   const int32_t* cu_seqlens;
   int B, Hq, Hkv, N;
   int group;

@@ -89,7 +89,8 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
  * Writes dq [T, Hq, d], dk and dv [T, Hkv, d] in `dtype` (nearest even);
  * dk and dv of a KV head are summed over the query heads that share it.
  * `workspace` is caller-owned device memory of at least
- * fa_bwd_workspace_size(B, Hq, Hkv, N, d) bytes (float32 rowsum(dout∘o)).
+ * fa_bwd_workspace_size(B, Hq, Hkv, N, d) bytes (float32 rowsum(dout∘o) and
+ * the rescaled lse, 8·Hq·(B·N + 64) bytes rounded up to 256).
  */
 int fa_bwd(const void* q, const void* k, const void* v, const void* o,
            const void* dout, const float* lse, void* dq, void* dk, void* dv,
@@ -99,7 +100,7 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o,
 
 /*
  * fa_bwd is a fixed sequence of stages enqueued on one stream:
- *   0  D = rowsum(dout∘o) into the workspace
+ *   0  D = rowsum(dout∘o) and lse·log2(e) into the workspace
  *   1  dk, dv            (reads D)
  *   2  dq                (reads D; independent of stage 1)
  * fa_bwd_stage enqueues one stage with fa_bwd's arguments and checks, so a

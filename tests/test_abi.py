@@ -111,8 +111,8 @@ def test_bwd_stage_index_checked():
 
 
 def test_workspace_size():
-    assert fa.fa_bwd_workspace_size(2, 16, 16, 16384, 128) == 2 * 16384 * 16 * 4
-    assert fa.fa_bwd_workspace_size(1, 2, 2, 3, 64) == 256          # 256-byte granule
+    assert fa.fa_bwd_workspace_size(2, 16, 16, 16384, 128) == 2 * 16 * (2 * 16384 + 64) * 4
+    assert fa.fa_bwd_workspace_size(1, 2, 2, 3, 64) == 1280         # 2·2·67·4 = 1072 -> 256 granule
     assert fa.fa_bwd_workspace_size(1, 3, 2, 16, 64) == 0            # Hq % Hkv != 0
     assert fa.fa_bwd_workspace_size(1, 2, 2, 16, 80) == 0            # unsupported d
 
