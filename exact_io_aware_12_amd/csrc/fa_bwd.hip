@@ -18,6 +18,8 @@
 // Q/dO (stage 1) and K/V (stage 2) tiles are copied global -> LDS directly,
 // double-buffered, one barrier per tile. The transposed operands (Qᵀ, dOᵀ,
 // Kᵀ) are read from the same row-major tiles with the transposing LDS read.
+#include <type_traits>
+
 #include "fa_device.h"
 #include "fa_kernels.h"
 
@@ -109,6 +111,63 @@ constexpr int kDkvKeys = 128;   // keys per workgroup (32 per wave)
 constexpr int kDkvQ = 64;       // queries per inner tile
 constexpr int kDkvQB = kDkvQ / 32;   // 32-query MFMA blocks per inner tile
 
+// One 64-query tile for one wave's 32 keys, in two 32-query blocks: S and
+// dP for the block, then P = exp2(S·c − LSE·log2 e) and dS = P∘(dP − D) in
+// registers, then dVᵀ += dOᵀ·P and dKᵀ += Qᵀ·dS over the block's queries.
+// EDGE tiles zero P and dS for queries past the end and, causally, for keys
+// after the query (rows past the end hold workspace padding).
+template <typename T, int D, bool CAUSAL, bool EDGE>
+__device__ __forceinline__ void dkdv_tile(const T* qt_, const T* dot_, const float* ld,
+                                          const u32x4 (&kf)[D / 16], const u32x4 (&vf)[D / 16],
+                                          f32x16 (&dkt)[D / 32], f32x16 (&dvt)[D / 32], float c,
+                                          int q0, int L, int key, int lane) {
+  constexpr int NKB = D / 16;
+  constexpr int NCB = D / 32;
+  const int col = lane & 31, half = lane >> 5;
+#pragma unroll
+  for (int qb = 0; qb < kDkvQB; ++qb) {
+    f32x16 s = f32x16{}, dp = f32x16{};
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) {
+      s = mfma32<T>(lds_row16<T, D>(qt_, qb * 32 + col, 2 * kb + half), kf[kb], s);
+      dp = mfma32<T>(lds_row16<T, D>(dot_, qb * 32 + col, 2 * kb + half), vf[kb], dp);
+    }
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) {
+      const int qoff = qb * 32 + 8 * rr + 4 * half;
+      const float4 lv = *reinterpret_cast<const float4*>(ld + qoff);
+      const float4 dv4 = *reinterpret_cast<const float4*>(ld + kDkvQ + qoff);
+      const float lsev[4] = {lv.x, lv.y, lv.z, lv.w};
+      const float dlv[4] = {dv4.x, dv4.y, dv4.z, dv4.w};
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const int i4 = 4 * rr + t;
+        float p = fast_exp2(fmaf(s[i4], c, -lsev[t]));
+        float ds = p * (dp[i4] - dlv[t]);
+        if constexpr (EDGE) {
+          const int q = q0 + qoff + t;
+          const bool keep = q < L && !(CAUSAL && key > q);
+          p = keep ? p : 0.f;
+          ds = keep ? ds : 0.f;
+        }
+        s[i4] = p;
+        dp[i4] = ds;
+      }
+    }
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2) {
+      const u32x4 pb = acc_operand<T>(s, h2 * 2);
+      const u32x4 sb = acc_operand<T>(dp, h2 * 2);
+      const int kq = qb * 32 + h2 * 16 + 4 * half;
+#pragma unroll
+      for (int cb = 0; cb < NCB; ++cb) {
+        dvt[cb] = mfma32<T>(lds_tr8<T, D>(dot_, kq, kq + 8, cb * 32, lane), pb, dvt[cb]);
+        dkt[cb] = mfma32<T>(lds_tr8<T, D>(qt_, kq, kq + 8, cb * 32, lane), sb, dkt[cb]);
+      }
+    }
+  }
+}
+
 template <typename T, int D, bool CAUSAL, bool VARLEN>
 __global__ __launch_bounds__(kThreads, 1) void dkdv_kernel(BwdArgs a, int n_ktiles) {
   constexpr int NKB = D / 16;
@@ -133,15 +192,34 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_kernel(BwdArgs a, int n_ktil
 
   const int64_t qs = (int64_t)a.Hq * D, kvs = (int64_t)a.Hkv * D;
   const int key = k0 + wave * 32 + col;
+  // Query tiles of one head: [qt_begin, qt_end). Edge tiles need masking: the
+  // causal diagonal (queries below k0 + kDkvKeys) and a ragged last tile. The
+  // loop visits the edge tiles of every head of the group first, then the
+  // interior tiles, so the interior loop body has no masking at all.
   const int qt_begin = CAUSAL ? k0 / kDkvQ : 0;
-  const int nqt = (L + kDkvQ - 1) / kDkvQ - qt_begin;   // visible query tiles per head
-  const int ntile = a.group * nqt;                      // (head, query tile) pairs
+  const int qt_end = (L + kDkvQ - 1) / kDkvQ;
+  const int nq = qt_end - qt_begin;
+  const int nd = CAUSAL ? min(kDkvKeys / kDkvQ, nq) : 0;
+  const int ne = nd + ((L % kDkvQ != 0 && nq > nd) ? 1 : 0);
+  const int ni = nq - ne;
+  const int n_edge = a.group * ne, ntile = a.group * nq;
+  auto tile_of = [&](int i, int& r) -> int {   // tile i -> (head r, query tile)
+    if (i < n_edge) {
+      r = i / ne;
+      const int e = i - r * ne;
+      return e < nd ? qt_begin + e : qt_end - 1;
+    }
+    const int j = i - n_edge;
+    r = j / ni;
+    return qt_begin + nd + (j - r * ni);
+  };
 
-  // source pointers of tile i = (head r, query tile qt)
+  // source pointers of tile i
   auto tile_src = [&](int i, const T*& qp, const T*& dop, const float*& lp, const float*& dp,
                       int& q0) {
-    const int r = i / nqt, h = g * a.group + r;
-    q0 = (qt_begin + i % nqt) * kDkvQ;
+    int r;
+    q0 = tile_of(i, r) * kDkvQ;
+    const int h = g * a.group + r;
     qp = static_cast<const T*>(a.q) + (int64_t)si.seq0 * qs + (int64_t)h * D;
     dop = static_cast<const T*>(a.dout) + (int64_t)si.seq0 * qs + (int64_t)h * D;
     lp = a.lse2 + (int64_t)h * a.ws_stride + si.seq0 + q0;
@@ -176,69 +254,23 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_kernel(BwdArgs a, int n_ktil
     dvt[cb] = f32x16{};
   }
   const float c = a.scale_log2;
-  const int wk_first = k0 + wave * 32, wk_last = wk_first + 31;
+  const int wk_first = k0 + wave * 32;
 
-  for (int i = 0; i < ntile; ++i) {
+  auto step = [&](auto edge_tag, int i) {
+    constexpr bool EDGE = decltype(edge_tag)::value;
     const int buf = i & 1;
     wait_vmem_all();   // this thread's copies of tile i have landed
     __syncthreads();   // everyone's have; tile i-1 is no longer read
     if (i + 1 < ntile) issue(i + 1, buf ^ 1);
-    const int q0 = (qt_begin + i % nqt) * kDkvQ;
-    if (CAUSAL && q0 + kDkvQ - 1 < wk_first) continue;   // all queries before this wave's keys
-    const T* qt_ = q_lds[buf];
-    const T* dot_ = do_lds[buf];
-    const float* ld = ld_lds[buf];
-
-    // S = Q·Kᵀ and dP = dO·Vᵀ, in blocks of 32 queries
-    f32x16 s[kDkvQB], dp[kDkvQB];
-#pragma unroll
-    for (int qb = 0; qb < kDkvQB; ++qb) s[qb] = dp[qb] = f32x16{};
-#pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) {
-#pragma unroll
-      for (int qb = 0; qb < kDkvQB; ++qb) {
-        s[qb] = mfma32<T>(lds_row16<T, D>(qt_, qb * 32 + col, 2 * kb + half), kf[kb], s[qb]);
-        dp[qb] = mfma32<T>(lds_row16<T, D>(dot_, qb * 32 + col, 2 * kb + half), vf[kb], dp[qb]);
-      }
-    }
-    // P = exp2(S·c − LSE·log2 e), dS = P∘(dP − D); 0 for queries past the end
-    // and, causally, for keys after the query
-    const bool edge = (q0 + kDkvQ > L) || (CAUSAL && q0 < wk_last);
-#pragma unroll
-    for (int qb = 0; qb < kDkvQB; ++qb)
-#pragma unroll
-      for (int rr = 0; rr < 4; ++rr) {
-        const int qoff = qb * 32 + 8 * rr + 4 * half;
-        const float4 lv = *reinterpret_cast<const float4*>(ld + qoff);
-        const float4 dv4 = *reinterpret_cast<const float4*>(ld + kDkvQ + qoff);
-        const float lsev[4] = {lv.x, lv.y, lv.z, lv.w};
-        const float dlv[4] = {dv4.x, dv4.y, dv4.z, dv4.w};
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          const int i4 = 4 * rr + t;
-          float p = fast_exp2(fmaf(s[qb][i4], c, -lsev[t]));
-          float ds = p * (dp[qb][i4] - dlv[t]);
-          if (edge) {   // rows past the end hold workspace padding: zero P and dS outright
-            const int q = q0 + qoff + t;
-            if (q >= L || (CAUSAL && key > q)) p = ds = 0.f;
-          }
-          s[qb][i4] = p;
-          dp[qb][i4] = ds;
-        }
-      }
-    // dVᵀ += dOᵀ·P and dKᵀ += Qᵀ·dS over the tile's 64 queries
-#pragma unroll
-    for (int kk = 0; kk < kDkvQ / 16; ++kk) {
-      const u32x4 pb = acc_operand<T>(s[kk >> 1], (kk & 1) * 2);
-      const u32x4 sb = acc_operand<T>(dp[kk >> 1], (kk & 1) * 2);
-      const int kq = kk * 16 + 4 * half;
-#pragma unroll
-      for (int cb = 0; cb < NCB; ++cb) {
-        dvt[cb] = mfma32<T>(lds_tr8<T, D>(dot_, kq, kq + 8, cb * 32, lane), pb, dvt[cb]);
-        dkt[cb] = mfma32<T>(lds_tr8<T, D>(qt_, kq, kq + 8, cb * 32, lane), sb, dkt[cb]);
-      }
-    }
-  }
+    int r;
+    const int q0 = tile_of(i, r) * kDkvQ;
+    // a diagonal tile can lie entirely before this wave's keys
+    if (EDGE && CAUSAL && q0 + kDkvQ - 1 < wk_first) return;
+    dkdv_tile<T, D, CAUSAL, EDGE>(q_lds[buf], do_lds[buf], ld_lds[buf], kf, vf, dkt, dvt, c, q0,
+                                  L, key, lane);
+  };
+  for (int i = 0; i < n_edge; ++i) step(std::true_type{}, i);
+  for (int i = n_edge; i < ntile; ++i) step(std::false_type{}, i);
 
   if (key < L) {
     const int64_t off = (int64_t)(si.seq0 + key) * kvs + (int64_t)g * D;
