@@ -104,28 +104,47 @@ __device__ __forceinline__ void rows_dma(float* lds, const float* lse2, const fl
 }
 
 // ---------------------------------------------------------------------------
-// dK, dV. Orientation S = Q·Kᵀ with the wave's 32 keys as MFMA columns, so the
-// accumulators of P and dS have one key per lane and 16 queries in registers,
-// which is exactly the B-operand layout dVᵀ = dOᵀ·P and dKᵀ = Qᵀ·dS need.
-constexpr int kDkvKeys = 128;   // keys per workgroup (32 per wave)
-constexpr int kDkvQ = 64;       // queries per inner tile
-constexpr int kDkvQB = kDkvQ / 32;   // 32-query MFMA blocks per inner tile
+// dK, dV. Orientation S = Q·Kᵀ with 32 keys as MFMA columns, so the
+// accumulators of P and dS hold one key per lane and 16 queries in
+// registers, which is exactly the B-operand layout dVᵀ = dOᵀ·P and
+// dKᵀ = Qᵀ·dS need.
+//
+// A workgroup owns 128 keys of one KV head and runs 8 waves, two per SIMD:
+// waves w and w+4 share keys k0+32w .. k0+32w+31. Wave w (producer) keeps K
+// and V of those keys in registers and turns a 64-query tile into P and dS
+// (S and dP by MFMA, then the softmax gradient on the VALU); wave w+4
+// (consumer) keeps dKᵀ and dVᵀ in registers and runs the dVᵀ += dOᵀ·P and
+// dKᵀ += Qᵀ·dS products. P and dS pass through LDS in operand layout. The
+// consumer works one tile behind the producer, so one wave's VALU work
+// overlaps the other's MFMAs on the same SIMD.
+//
+// Per iteration j (j = -1 .. ntile-1), between two workgroup barriers:
+//   A: tile j+1 (Q, dO, LSE, D) has landed; the copy of tile j+2 starts
+//      into the stage that tile j-1 used;
+//      consumer: P, dS of tile j from LDS into registers;
+//      producer: S, dP of tile j+1;
+//   B: consumer: dK/dV products of tile j; producer: P, dS of tile j+1 into
+//      LDS.
+// Q/dO tiles take 3 stages: j (consumer), j+1 (producer), j+2 (in flight).
+constexpr int kDkvKeys = 128;     // keys per workgroup (32 per wave pair)
+constexpr int kDkvQ = 64;         // queries per tile
+constexpr int kDkvWaves = 8;      // 4 producers, 4 consumers
+constexpr int kDkvThreads = 64 * kDkvWaves;
+constexpr int kDkvStages = 3;
+constexpr int kDkvKK = kDkvQ / 16;   // 16-query MFMA k-steps per tile
 
-// One 64-query tile for one wave's 32 keys, in two 32-query blocks: S and
-// dP for the block, then P = exp2(S·c − LSE·log2 e) and dS = P∘(dP − D) in
-// registers, then dVᵀ += dOᵀ·P and dKᵀ += Qᵀ·dS over the block's queries.
-// EDGE tiles zero P and dS for queries past the end and, causally, for keys
-// after the query (rows past the end hold workspace padding).
+// Producer: P and dS of one 64-query tile for 32 keys, written to `xp`
+// (P) and `xs` (dS) as MFMA B operands, [k-step][lane]. EDGE tiles zero P
+// and dS for queries past the end and, causally, for keys after the query.
 template <typename T, int D, bool CAUSAL, bool EDGE>
-__device__ __forceinline__ void dkdv_tile(const T* qt_, const T* dot_, const float* ld,
-                                          const u32x4 (&kf)[D / 16], const u32x4 (&vf)[D / 16],
-                                          f32x16 (&dkt)[D / 32], f32x16 (&dvt)[D / 32], float c,
-                                          int q0, int L, int key, int lane) {
+__device__ __forceinline__ void dkdv_produce(const T* qt_, const T* dot_, const float* ld,
+                                             const u32x4 (&kf)[D / 16],
+                                             const u32x4 (&vf)[D / 16], u32x4* xp, u32x4* xs,
+                                             float c, int q0, int L, int key, int lane) {
   constexpr int NKB = D / 16;
-  constexpr int NCB = D / 32;
   const int col = lane & 31, half = lane >> 5;
 #pragma unroll
-  for (int qb = 0; qb < kDkvQB; ++qb) {
+  for (int qb = 0; qb < kDkvQ / 32; ++qb) {
     f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) {
@@ -156,28 +175,24 @@ __device__ __forceinline__ void dkdv_tile(const T* qt_, const T* dot_, const flo
     }
 #pragma unroll
     for (int h2 = 0; h2 < 2; ++h2) {
-      const u32x4 pb = acc_operand<T>(s, h2 * 2);
-      const u32x4 sb = acc_operand<T>(dp, h2 * 2);
-      const int kq = qb * 32 + h2 * 16 + 4 * half;
-#pragma unroll
-      for (int cb = 0; cb < NCB; ++cb) {
-        dvt[cb] = mfma32<T>(lds_tr8<T, D>(dot_, kq, kq + 8, cb * 32, lane), pb, dvt[cb]);
-        dkt[cb] = mfma32<T>(lds_tr8<T, D>(qt_, kq, kq + 8, cb * 32, lane), sb, dkt[cb]);
-      }
+      xp[(2 * qb + h2) * 64 + lane] = acc_operand<T>(s, h2 * 2);
+      xs[(2 * qb + h2) * 64 + lane] = acc_operand<T>(dp, h2 * 2);
     }
   }
 }
 
 template <typename T, int D, bool CAUSAL, bool VARLEN>
-__global__ __launch_bounds__(kThreads, 1) void dkdv_kernel(BwdArgs a, int n_ktiles) {
+__global__ __launch_bounds__(kDkvThreads, 1) void dkdv_kernel(BwdArgs a, int n_ktiles) {
   constexpr int NKB = D / 16;
   constexpr int NCB = D / 32;
   constexpr int TILE = kDkvQ * D;
-  __shared__ __attribute__((aligned(1024))) T q_lds[2][TILE];
-  __shared__ __attribute__((aligned(1024))) T do_lds[2][TILE];
-  __shared__ __attribute__((aligned(16))) float ld_lds[2][2 * kDkvQ];   // LSE·log2 e, D
+  __shared__ __attribute__((aligned(1024))) T qd_lds[kDkvStages][2][TILE];   // [stage][Q, dO]
+  __shared__ __attribute__((aligned(16))) float ld_lds[kDkvStages][2 * kDkvQ];  // LSE·log2 e, D
+  __shared__ __attribute__((aligned(16))) u32x4 xch[4][2][kDkvKK * 64];   // [pair][P, dS]
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int pair = wave & 3;
+  const bool producer = wave < 4;
   const int col = lane & 31, half = lane >> 5;
 
   const int G = gridDim.x;
@@ -191,11 +206,12 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_kernel(BwdArgs a, int n_ktil
   const int L = si.L;
 
   const int64_t qs = (int64_t)a.Hq * D, kvs = (int64_t)a.Hkv * D;
-  const int key = k0 + wave * 32 + col;
+  const int key = k0 + pair * 32 + col;
+  const int pk_first = k0 + pair * 32;   // first key of this wave pair
+
   // Query tiles of one head: [qt_begin, qt_end). Edge tiles need masking: the
   // causal diagonal (queries below k0 + kDkvKeys) and a ragged last tile. The
-  // loop visits the edge tiles of every head of the group first, then the
-  // interior tiles, so the interior loop body has no masking at all.
+  // edge tiles of every head of the group come first, then the interior ones.
   const int qt_begin = CAUSAL ? k0 / kDkvQ : 0;
   const int qt_end = (L + kDkvQ - 1) / kDkvQ;
   const int nq = qt_end - qt_begin;
@@ -213,32 +229,36 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_kernel(BwdArgs a, int n_ktil
     r = j / ni;
     return qt_begin + nd + (j - r * ni);
   };
-
-  // source pointers of tile i
-  auto tile_src = [&](int i, const T*& qp, const T*& dop, const float*& lp, const float*& dp,
-                      int& q0) {
+  const DmaPlan<T, kDkvQ, D, kDkvWaves> plan(qs, wave, lane);
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  auto issue = [&](int i) {   // start copying tile i into stage i % 3
     int r;
-    q0 = tile_of(i, r) * kDkvQ;
-    const int h = g * a.group + r;
-    qp = static_cast<const T*>(a.q) + (int64_t)si.seq0 * qs + (int64_t)h * D;
-    dop = static_cast<const T*>(a.dout) + (int64_t)si.seq0 * qs + (int64_t)h * D;
-    lp = a.lse2 + (int64_t)h * a.ws_stride + si.seq0 + q0;
-    dp = a.delta + (int64_t)h * a.ws_stride + si.seq0 + q0;
+    const int q0 = tile_of(i, r) * kDkvQ;
+    const int h = g * a.group + r, st = i % kDkvStages;
+    const T* qp = static_cast<const T*>(a.q) + (int64_t)si.seq0 * qs + (int64_t)h * D;
+    const T* dop = static_cast<const T*>(a.dout) + (int64_t)si.seq0 * qs + (int64_t)h * D;
+    if (q0 + kDkvQ <= L) {
+      tile_dma_in<T, kDkvQ, D, kDkvWaves>(qd_lds[st][0], qp + (int64_t)q0 * qs, plan, wave_u);
+      tile_dma_in<T, kDkvQ, D, kDkvWaves>(qd_lds[st][1], dop + (int64_t)q0 * qs, plan, wave_u);
+    } else {
+      tile_dma<T, kDkvQ, D, kDkvWaves>(qd_lds[st][0], qp, qs, q0, L, wave, lane);
+      tile_dma<T, kDkvQ, D, kDkvWaves>(qd_lds[st][1], dop, qs, q0, L, wave, lane);
+    }
+    if (wave == 0) {
+      const int64_t w0 = (int64_t)h * a.ws_stride + si.seq0 + q0;
+      rows_dma<kDkvQ>(ld_lds[st], a.lse2 + w0, a.delta + w0, lane);
+    }
   };
-  auto issue = [&](int i, int buf) {
-    const T *qp, *dop;
-    const float *lp, *dp;
-    int q0;
-    tile_src(i, qp, dop, lp, dp, q0);
-    tile_dma<T, kDkvQ, D, kWaves>(q_lds[buf], qp, qs, q0, L, wave, lane);
-    tile_dma<T, kDkvQ, D, kWaves>(do_lds[buf], dop, qs, q0, L, wave, lane);
-    if (wave == 0) rows_dma<kDkvQ>(ld_lds[buf], lp, dp, lane);
-  };
-  if (ntile > 0) issue(0, 0);
+  if (ntile > 0) issue(0);
+  if (ntile > 1) issue(1);
 
-  // K and V fragments of this wave's 32 keys (B operands), kept in registers
-  u32x4 kf[NKB], vf[NKB];
-  {
+  u32x4* xp = xch[pair][0];
+  u32x4* xs = xch[pair][1];
+  const float c = a.scale_log2;
+
+  if (producer) {
+    // K and V fragments of this pair's 32 keys (B operands), kept in registers
+    u32x4 kf[NKB], vf[NKB];
     const T* kp = static_cast<const T*>(a.k) + (int64_t)(si.seq0 + key) * kvs + (int64_t)g * D;
     const T* vp = static_cast<const T*>(a.v) + (int64_t)(si.seq0 + key) * kvs + (int64_t)g * D;
 #pragma unroll
@@ -246,50 +266,97 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_kernel(BwdArgs a, int n_ktil
       kf[kb] = key < L ? ldg16(kp + kb * 16 + half * 8) : u32x4{0, 0, 0, 0};
       vf[kb] = key < L ? ldg16(vp + kb * 16 + half * 8) : u32x4{0, 0, 0, 0};
     }
-  }
-  f32x16 dkt[NCB], dvt[NCB];
-#pragma unroll
-  for (int cb = 0; cb < NCB; ++cb) {
-    dkt[cb] = f32x16{};
-    dvt[cb] = f32x16{};
-  }
-  const float c = a.scale_log2;
-  const int wk_first = k0 + wave * 32;
-
-  auto step = [&](auto edge_tag, int i) {
-    constexpr bool EDGE = decltype(edge_tag)::value;
-    const int buf = i & 1;
-    wait_vmem_all();   // this thread's copies of tile i have landed
-    __syncthreads();   // everyone's have; tile i-1 is no longer read
-    if (i + 1 < ntile) issue(i + 1, buf ^ 1);
-    int r;
-    const int q0 = tile_of(i, r) * kDkvQ;
-    // a diagonal tile can lie entirely before this wave's keys
-    if (EDGE && CAUSAL && q0 + kDkvQ - 1 < wk_first) return;
-    dkdv_tile<T, D, CAUSAL, EDGE>(q_lds[buf], do_lds[buf], ld_lds[buf], kf, vf, dkt, dvt, c, q0,
-                                  L, key, lane);
-  };
-  for (int i = 0; i < n_edge; ++i) step(std::true_type{}, i);
-  for (int i = n_edge; i < ntile; ++i) step(std::false_type{}, i);
-
-  if (key < L) {
-    const int64_t off = (int64_t)(si.seq0 + key) * kvs + (int64_t)g * D;
-    T* dkp = static_cast<T*>(a.dk) + off;
-    T* dvp = static_cast<T*>(a.dv) + off;
-    const float sc = a.scale;
-#pragma unroll
-    for (int cb = 0; cb < NCB; ++cb)
-#pragma unroll
-      for (int rr = 0; rr < 4; ++rr) {
-        const int d0 = cb * 32 + 8 * rr + 4 * half;
-        u32x2 w;
-        w[0] = pack2<T>(dkt[cb][4 * rr + 0] * sc, dkt[cb][4 * rr + 1] * sc);
-        w[1] = pack2<T>(dkt[cb][4 * rr + 2] * sc, dkt[cb][4 * rr + 3] * sc);
-        *reinterpret_cast<u32x2*>(dkp + d0) = w;
-        w[0] = pack2<T>(dvt[cb][4 * rr + 0], dvt[cb][4 * rr + 1]);
-        w[1] = pack2<T>(dvt[cb][4 * rr + 2], dvt[cb][4 * rr + 3]);
-        *reinterpret_cast<u32x2*>(dvp + d0) = w;
+    for (int j = -1; j < ntile; ++j) {
+      wait_vmem_all();   // this wave's copies of tile j+1 (and K, V) have landed
+      __syncthreads();   // A
+      if (j + 2 < ntile) issue(j + 2);
+      __syncthreads();   // B: the consumers hold tile j's P and dS in registers
+      const int t = j + 1;
+      if (t < ntile) {
+        int r;
+        const int q0 = tile_of(t, r) * kDkvQ;
+        const int st = t % kDkvStages;
+        if (!(CAUSAL && q0 + kDkvQ - 1 < pk_first)) {   // else: before this pair's keys
+          if (t < n_edge)
+            dkdv_produce<T, D, CAUSAL, true>(qd_lds[st][0], qd_lds[st][1], ld_lds[st], kf, vf,
+                                             xp, xs, c, q0, L, key, lane);
+          else
+            dkdv_produce<T, D, CAUSAL, false>(qd_lds[st][0], qd_lds[st][1], ld_lds[st], kf, vf,
+                                              xp, xs, c, q0, L, key, lane);
+        }
       }
+    }
+  } else {
+    f32x16 dkt[NCB], dvt[NCB];
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb) {
+      dkt[cb] = f32x16{};
+      dvt[cb] = f32x16{};
+    }
+    for (int j = -1; j < ntile; ++j) {
+      wait_vmem_all();
+      __syncthreads();   // A: tile j's P and dS are in LDS
+      if (j + 2 < ntile) issue(j + 2);
+      bool active = false;
+      u32x4 pb[kDkvKK], sb[kDkvKK];
+      int st = 0;
+      if (j >= 0) {
+        int r;
+        const int q0 = tile_of(j, r) * kDkvQ;
+        st = j % kDkvStages;
+        active = !(CAUSAL && q0 + kDkvQ - 1 < pk_first);
+        if (active) {
+#pragma unroll
+          for (int kk = 0; kk < kDkvKK; ++kk) {
+            pb[kk] = xp[kk * 64 + lane];
+            sb[kk] = xs[kk * 64 + lane];
+          }
+        }
+      }
+      __syncthreads();   // B (waits for the P, dS reads above)
+      if (active) {
+        const T* qt_ = qd_lds[st][0];
+        const T* dot_ = qd_lds[st][1];
+#pragma unroll
+        for (int kk = 0; kk < kDkvKK; ++kk) {
+          const int kq = kk * 16 + 4 * half;
+#pragma unroll
+          for (int cb = 0; cb < NCB; ++cb) {
+            dvt[cb] = mfma32<T>(lds_tr8<T, D>(dot_, kq, kq + 8, cb * 32, lane), pb[kk], dvt[cb]);
+            dkt[cb] = mfma32<T>(lds_tr8<T, D>(qt_, kq, kq + 8, cb * 32, lane), sb[kk], dkt[cb]);
+          }
+        }
+        // operand reads run one k-step (2·NCB products) ahead of the products
+        constexpr int kSgMFMA = 0x008, kSgDSRead = 0x100;
+        constexpr int kPer = 2 * NCB;   // products per k-step, 2 reads each
+        __builtin_amdgcn_sched_group_barrier(kSgDSRead, 2 * kPer, 0);
+#pragma unroll
+        for (int i = 0; i < (kDkvKK - 1) * kPer; ++i) {
+          __builtin_amdgcn_sched_group_barrier(kSgMFMA, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(kSgDSRead, 2, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(kSgMFMA, kPer, 0);
+      }
+    }
+    if (key < L) {
+      const int64_t off = (int64_t)(si.seq0 + key) * kvs + (int64_t)g * D;
+      T* dkp = static_cast<T*>(a.dk) + off;
+      T* dvp = static_cast<T*>(a.dv) + off;
+      const float sc = a.scale;
+#pragma unroll
+      for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+          const int d0 = cb * 32 + 8 * rr + 4 * half;
+          u32x2 w;
+          w[0] = pack2<T>(dkt[cb][4 * rr + 0] * sc, dkt[cb][4 * rr + 1] * sc);
+          w[1] = pack2<T>(dkt[cb][4 * rr + 2] * sc, dkt[cb][4 * rr + 3] * sc);
+          *reinterpret_cast<u32x2*>(dkp + d0) = w;
+          w[0] = pack2<T>(dvt[cb][4 * rr + 0], dvt[cb][4 * rr + 1]);
+          w[1] = pack2<T>(dvt[cb][4 * rr + 2], dvt[cb][4 * rr + 3]);
+          *reinterpret_cast<u32x2*>(dvp + d0) = w;
+        }
+    }
   }
 }
 
@@ -299,6 +366,45 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_kernel(BwdArgs a, int n_ktil
 // dQᵀ = Kᵀ·dSᵀ (Kᵀ read transposed from the row-major K tile).
 constexpr int kDqQ = 128;   // queries per workgroup (32 per wave)
 constexpr int kDqK = 64;    // keys per tile
+
+// One 64-key tile for one wave's 32 queries: Sᵀ and dPᵀ, then
+// dSᵀ = P∘(dP − D) with P = exp2(S·c − LSE·log2 e), then dQᵀ += Kᵀ·dSᵀ.
+// EDGE tiles zero P for keys past the end and, causally, for keys after the
+// query.
+template <typename T, int D, bool CAUSAL, bool EDGE>
+__device__ __forceinline__ void dq_tile(const T* kt, const T* vt, const u32x4 (&qf)[D / 16],
+                                        const u32x4 (&df)[D / 16], f32x16 (&dqt)[D / 32], float c,
+                                        float lse2, float dl, int kv0, int L, int qrow, int lane) {
+  constexpr int NKB = D / 16;
+  constexpr int NCB = D / 32;
+  const int col = lane & 31, half = lane >> 5;
+#pragma unroll
+  for (int jb = 0; jb < kDqK / 32; ++jb) {   // 32-key blocks
+    f32x16 s = f32x16{}, dp = f32x16{};
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) {
+      s = mfma32<T>(lds_row16<T, D>(kt, jb * 32 + col, 2 * kb + half), qf[kb], s);
+      dp = mfma32<T>(lds_row16<T, D>(vt, jb * 32 + col, 2 * kb + half), df[kb], dp);
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      float p = fast_exp2(fmaf(s[i], c, -lse2));
+      if constexpr (EDGE) {
+        const int kj = kv0 + jb * 32 + 8 * (i >> 2) + 4 * half + (i & 3);
+        p = (kj < L && !(CAUSAL && kj > qrow)) ? p : 0.f;
+      }
+      dp[i] = p * (dp[i] - dl);
+    }
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2) {
+      const u32x4 sb = acc_operand<T>(dp, h2 * 2);
+      const int kq = jb * 32 + h2 * 16 + 4 * half;
+#pragma unroll
+      for (int cb = 0; cb < NCB; ++cb)
+        dqt[cb] = mfma32<T>(lds_tr8<T, D>(kt, kq, kq + 8, cb * 32, lane), sb, dqt[cb]);
+    }
+  }
+}
 
 template <typename T, int D, bool CAUSAL, bool VARLEN>
 __global__ __launch_bounds__(kThreads, 2) void dq_kernel(BwdArgs a, int n_qtiles) {
@@ -351,50 +457,37 @@ __global__ __launch_bounds__(kThreads, 2) void dq_kernel(BwdArgs a, int n_qtiles
 #pragma unroll
   for (int cb = 0; cb < NCB; ++cb) dqt[cb] = f32x16{};
   const float c = a.scale_log2;
-  const int wq_first = q0 + wave * 32, wq_last = wq_first + 31;
+  const int wq_last = q0 + wave * 32 + 31;
 
-  for (int j = 0; j < ntiles; ++j) {
+  // Key tiles [0, j_int) need no masking: all their keys precede every query of
+  // the workgroup (causal) and lie inside the sequence. The rest (the causal
+  // diagonal, a ragged last tile) run in a second loop with masking.
+  const int j_int = CAUSAL ? min((q0 + 1) / kDqK, L / kDqK) : L / kDqK;
+  const DmaPlan<T, kDqK, D, kWaves> plan(kvs, wave, lane);
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  auto step = [&](auto edge_tag, int j) {
+    constexpr bool EDGE = decltype(edge_tag)::value;
     const int kv0 = j * kDqK;
     const T* kt = lds[j & 1][0];
     const T* vt = lds[j & 1][1];
     wait_vmem_all();
     __syncthreads();
     if (j + 1 < ntiles) {
-      tile_dma<T, kDqK, D, kWaves>(lds[(j + 1) & 1][0], kp, kvs, kv0 + kDqK, L, wave, lane);
-      tile_dma<T, kDqK, D, kWaves>(lds[(j + 1) & 1][1], vp, kvs, kv0 + kDqK, L, wave, lane);
-    }
-    if (CAUSAL && kv0 > wq_last) continue;
-
-    f32x16 s[2] = {f32x16{}, f32x16{}}, dp[2] = {f32x16{}, f32x16{}};
-#pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) {
-#pragma unroll
-      for (int jb = 0; jb < 2; ++jb) {
-        s[jb] = mfma32<T>(lds_row16<T, D>(kt, jb * 32 + col, 2 * kb + half), qf[kb], s[jb]);
-        dp[jb] = mfma32<T>(lds_row16<T, D>(vt, jb * 32 + col, 2 * kb + half), df[kb], dp[jb]);
+      const int n0 = kv0 + kDqK;
+      if (n0 + kDqK <= L) {
+        tile_dma_in<T, kDqK, D, kWaves>(lds[(j + 1) & 1][0], kp + (int64_t)n0 * kvs, plan, wave_u);
+        tile_dma_in<T, kDqK, D, kWaves>(lds[(j + 1) & 1][1], vp + (int64_t)n0 * kvs, plan, wave_u);
+      } else {
+        tile_dma<T, kDqK, D, kWaves>(lds[(j + 1) & 1][0], kp, kvs, n0, L, wave, lane);
+        tile_dma<T, kDqK, D, kWaves>(lds[(j + 1) & 1][1], vp, kvs, n0, L, wave, lane);
       }
     }
-    const bool edge = (kv0 + kDqK > L) || (CAUSAL && kv0 + kDqK - 1 > wq_first);
-#pragma unroll
-    for (int jb = 0; jb < 2; ++jb)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        float p = fast_exp2(fmaf(s[jb][i], c, -lse2));
-        if (edge) {
-          const int kj = kv0 + jb * 32 + 8 * (i >> 2) + 4 * half + (i & 3);
-          if (kj >= L || (CAUSAL && kj > qrow)) p = 0.f;
-        }
-        dp[jb][i] = p * (dp[jb][i] - dl);
-      }
-#pragma unroll
-    for (int kk = 0; kk < kDqK / 16; ++kk) {
-      const u32x4 sb = acc_operand<T>(dp[kk >> 1], (kk & 1) * 2);
-      const int kq = kk * 16 + 4 * half;
-#pragma unroll
-      for (int cb = 0; cb < NCB; ++cb)
-        dqt[cb] = mfma32<T>(lds_tr8<T, D>(kt, kq, kq + 8, cb * 32, lane), sb, dqt[cb]);
-    }
-  }
+    if (EDGE && CAUSAL && kv0 > wq_last) return;   // every key after this wave's queries
+    dq_tile<T, D, CAUSAL, EDGE>(kt, vt, qf, df, dqt, c, lse2, dl, kv0, L, qrow, lane);
+  };
+  const int j_mid = min(j_int, ntiles);
+  for (int j = 0; j < j_mid; ++j) step(std::false_type{}, j);
+  for (int j = j_mid; j < ntiles; ++j) step(std::true_type{}, j);
 
   if (qrow < L) {
     T* dqp = static_cast<T*>(a.dq) + (int64_t)(si.seq0 + qrow) * qs + (int64_t)h * D;
@@ -425,7 +518,7 @@ hipError_t launch(const BwdArgs& a, int stage, hipStream_t s) {
   if (stage < 0 || stage == 1) {
     const int nkt = (a.N + kDkvKeys - 1) / kDkvKeys;
     hipLaunchKernelGGL((dkdv_kernel<T, D, CAUSAL, VARLEN>), dim3(nkt * a.Hkv * a.B),
-                       dim3(kThreads), 0, s, a, nkt);
+                       dim3(kDkvThreads), 0, s, a, nkt);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

@@ -207,6 +207,56 @@ __device__ __forceinline__ void tile_dma(T* lds, const T* src, int64_t rstride, 
   }
 }
 
+// Fourth dword of a raw buffer resource on gfx9-family parts: 32-bit data
+// format, no swizzle; with stride 0 the range check is on byte offsets.
+constexpr int kBufferDword3 = 0x00020000;
+
+// Per-lane byte offsets, relative to the tile's first row, of the pieces a
+// wave copies in tile_dma. They are the same for every tile of a matrix, so
+// a tile that lies wholly inside the sequence is copied from a uniform base
+// pointer plus these offsets, with no per-tile vector address arithmetic.
+template <typename T, int R, int D, int NW>
+struct DmaPlan {
+  static constexpr int CPR = D / 8;
+  static constexpr int RPI = 64 / CPR;
+  static constexpr int PER = R / RPI / NW;   // copy instructions per wave
+  static_assert((R / RPI) % NW == 0, "tile rows must split evenly over the waves");
+  uint32_t off[PER];
+  __device__ __forceinline__ DmaPlan(int64_t rstride, int wave, int lane) {
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int row = (wave * PER + u) * RPI + lane / CPR;
+      const int c = (lane % CPR) ^ swz<D>(row);
+      off[u] = (uint32_t)((row * rstride + c * 8) * (int64_t)sizeof(T));
+    }
+  }
+};
+
+// tile_dma for a tile whose R rows all lie inside the sequence; `src_r0`
+// points at the tile's first row and `wave` is the same on all lanes. A
+// buffer load with a 32-bit per-lane offset keeps the base in scalar
+// registers; the resource covers 2 GiB from the tile's first row and the
+// offsets stay far below that.
+template <typename T, int R, int D, int NW>
+__device__ __forceinline__ void tile_dma_in(T* lds, const T* src_r0, const DmaPlan<T, R, D, NW>& p,
+                                            int wave) {
+#if defined(__HIP_DEVICE_COMPILE__)  // the host pass cannot type-check these device builtins
+  const __amdgpu_buffer_rsrc_t rsrc =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<T*>(src_r0), 0, 0x7fffffff, kBufferDword3);
+#pragma unroll
+  for (int u = 0; u < DmaPlan<T, R, D, NW>::PER; ++u)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        rsrc,
+        (__attribute__((address_space(3))) void*)(lds + (wave * DmaPlan<T, R, D, NW>::PER + u) * 512),
+        16, p.off[u], 0, 0, 0);
+#else
+  (void)lds;
+  (void)src_r0;
+  (void)p;
+  (void)wave;
+#endif
+}
+
 // 16-byte operand read: row r, logical chunk c (8 elements from column 8c).
 template <typename T, int D>
 __device__ __forceinline__ u32x4 lds_row16(const T* lds, int r, int c) {

@@ -20,6 +20,8 @@
 // K and V tiles are copied global -> LDS directly and double-buffered: the
 // next tile is in flight while the current one is computed.
 // Epilogue: O = Oᵀ/l rounded to the input type, LSE = (m·c + log2 l)·ln 2.
+#include <type_traits>
+
 #include "fa_device.h"
 #include "fa_kernels.h"
 
@@ -32,6 +34,73 @@ constexpr int kBC = 64;   // keys per tile
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 constexpr float kRescaleHeadroom = 8.f;  // log2 of the largest P before the max is raised
+
+// One 64-key tile for one wave's 32 query rows: Sᵀ = K·Qᵀ, online softmax
+// with a lazily raised reference max, Oᵀ += Vᵀ·Pᵀ. EDGE tiles mask keys past
+// the sequence end and, causally, keys after the query.
+template <typename T, int D, bool CAUSAL, bool EDGE>
+__device__ __forceinline__ void fwd_tile(const T* kt, const T* vt, const u32x4 (&qf)[D / 16],
+                                         f32x16 (&o)[D / 32], float& mc, float& l, float c,
+                                         int kv0, int L, int qrow, int lane) {
+  constexpr int NKB = D / 16;
+  constexpr int NCB = D / 32;
+  const int col = lane & 31, half = lane >> 5;
+  // ---- Sᵀ = K·Qᵀ ----------------------------------------------------------
+  f32x16 s[2] = {f32x16{}, f32x16{}};
+#pragma unroll
+  for (int kb = 0; kb < NKB; ++kb) {
+#pragma unroll
+    for (int jb = 0; jb < 2; ++jb)
+      s[jb] = mfma32<T>(lds_row16<T, D>(kt, jb * 32 + col, 2 * kb + half), qf[kb], s[jb]);
+  }
+
+  // ---- mask: keys past the sequence end, keys after the query (causal) ---
+  if constexpr (EDGE) {
+#pragma unroll
+    for (int jb = 0; jb < 2; ++jb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int key = kv0 + jb * 32 + 8 * (i >> 2) + 4 * half + (i & 3);
+        s[jb][i] = (key < L && !(CAUSAL && key > qrow)) ? s[jb][i] : -INFINITY;
+      }
+  }
+
+  // ---- online softmax with a lazily raised reference max -----------------
+  float mx = s[0][0];
+#pragma unroll
+  for (int i = 1; i < 16; ++i) mx = fmaxf(mx, s[0][i]);
+#pragma unroll
+  for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[1][i]);
+  const float mxc = wave_max_halves(mx) * c;
+  if (__builtin_amdgcn_ballot_w64(mxc > mc + kRescaleHeadroom) != 0) {   // wave-uniform
+    const float mc_new = fmaxf(mc, mxc);     // finite: key 0 is seen in tile 0
+    const float alpha = fast_exp2(mc - mc_new);
+    l *= alpha;
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb) o[cb] *= alpha;
+    mc = mc_new;
+  }
+  // row sum in fp32 from the unrounded P: LSE carries no rounding of P
+  float ls[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int jb = 0; jb < 2; ++jb)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      s[jb][i] = fast_exp2(fmaf(s[jb][i], c, -mc));
+      ls[i & 3] += s[jb][i];
+    }
+  l += (ls[0] + ls[1]) + (ls[2] + ls[3]);
+
+  // ---- Oᵀ += Vᵀ·Pᵀ ---------------------------------------------------------
+#pragma unroll
+  for (int kk = 0; kk < kBC / 16; ++kk) {
+    const u32x4 pf = acc_operand<T>(s[kk >> 1], (kk & 1) * 2);
+    const int k0 = kk * 16 + 4 * half;
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb)
+      o[cb] = mfma32<T>(lds_tr8<T, D>(vt, k0, k0 + 8, cb * 32, lane), pf, o[cb]);
+  }
+}
 
 template <typename T, int D, bool CAUSAL, bool VARLEN>
 __global__ __launch_bounds__(kThreads, 2) void fwd_kernel(FwdArgs a) {
@@ -94,77 +163,37 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_kernel(FwdArgs a) {
   const float c = a.scale_log2;
   float mc = -INFINITY;   // reference max of S·c for this row
   float l = 0.f;          // Σ P over this lane half's keys (fp32)
-  const int wq_first = q0 + wave * 32, wq_last = wq_first + 31;
+  const int wq_last = q0 + wave * 32 + 31;
 
-  for (int j = 0; j < ntiles; ++j) {
+  // Key tiles [0, j_int) need no masking: all their keys precede every row of
+  // the workgroup (causal) and lie inside the sequence. The others (causal
+  // diagonal, ragged last tile) run in a second loop with masking.
+  const int j_int = min(CAUSAL ? min((q0 + 1) / kBC, L / kBC) : L / kBC, ntiles);
+  const DmaPlan<T, kBC, D, kWaves> plan(kvs, wave, lane);
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  // BUF is the LDS buffer of tile j (j & 1), a compile-time constant so that
+  // every LDS address is a fixed per-lane offset plus an immediate
+  auto step = [&](auto edge_tag, int j) {
+    constexpr bool EDGE = decltype(edge_tag)::value;
+    const int BUF = j & 1;
     const int kv0 = j * kBC;
-    const T* kt = lds[j & 1][0];
-    const T* vt = lds[j & 1][1];
     wait_vmem_all();   // this thread's copies of tile j have landed
     __syncthreads();   // everyone's have, and tile j-1 is no longer read
     if (j + 1 < ntiles) {
-      tile_dma<T, kBC, D, kWaves>(lds[(j + 1) & 1][0], kp, kvs, kv0 + kBC, L, wave, lane);
-      tile_dma<T, kBC, D, kWaves>(lds[(j + 1) & 1][1], vp, kvs, kv0 + kBC, L, wave, lane);
-    }
-    if (CAUSAL && kv0 > wq_last) continue;  // every key of the tile is after this wave's rows
-
-    // ---- Sᵀ = K·Qᵀ ----------------------------------------------------------
-    f32x16 s[2] = {f32x16{}, f32x16{}};
-#pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) {
-#pragma unroll
-      for (int jb = 0; jb < 2; ++jb)
-        s[jb] = mfma32<T>(lds_row16<T, D>(kt, jb * 32 + col, 2 * kb + half), qf[kb], s[jb]);
-    }
-
-    // ---- mask: keys past the sequence end, keys after the query (causal) ---
-    const bool edge = (kv0 + kBC > L) || (CAUSAL && kv0 + kBC - 1 > wq_first);
-    if (edge) {
-#pragma unroll
-      for (int jb = 0; jb < 2; ++jb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int key = kv0 + jb * 32 + 8 * (i >> 2) + 4 * half + (i & 3);
-          if (key >= L || (CAUSAL && key > qrow)) s[jb][i] = -INFINITY;
-        }
-    }
-
-    // ---- online softmax with a lazily raised reference max -----------------
-    float mx = s[0][0];
-#pragma unroll
-    for (int i = 1; i < 16; ++i) mx = fmaxf(mx, s[0][i]);
-#pragma unroll
-    for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[1][i]);
-    const float mxc = wave_max_halves(mx) * c;
-    if (__builtin_amdgcn_ballot_w64(mxc > mc + kRescaleHeadroom) != 0) {   // wave-uniform
-      const float mc_new = fmaxf(mc, mxc);     // finite: key 0 is seen in tile 0
-      const float alpha = fast_exp2(mc - mc_new);
-      l *= alpha;
-#pragma unroll
-      for (int cb = 0; cb < NCB; ++cb) o[cb] *= alpha;
-      mc = mc_new;
-    }
-    // row sum in fp32 from the unrounded P: LSE carries no rounding of P
-    float ls[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int jb = 0; jb < 2; ++jb)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        s[jb][i] = fast_exp2(fmaf(s[jb][i], c, -mc));
-        ls[i & 3] += s[jb][i];
+      const int n0 = kv0 + kBC;
+      if (n0 + kBC <= L) {
+        tile_dma_in<T, kBC, D, kWaves>(lds[BUF ^ 1][0], kp + (int64_t)n0 * kvs, plan, wave_u);
+        tile_dma_in<T, kBC, D, kWaves>(lds[BUF ^ 1][1], vp + (int64_t)n0 * kvs, plan, wave_u);
+      } else {
+        tile_dma<T, kBC, D, kWaves>(lds[BUF ^ 1][0], kp, kvs, n0, L, wave, lane);
+        tile_dma<T, kBC, D, kWaves>(lds[BUF ^ 1][1], vp, kvs, n0, L, wave, lane);
       }
-    l += (ls[0] + ls[1]) + (ls[2] + ls[3]);
-
-    // ---- Oᵀ += Vᵀ·Pᵀ ---------------------------------------------------------
-#pragma unroll
-    for (int kk = 0; kk < kBC / 16; ++kk) {
-      const u32x4 pf = acc_operand<T>(s[kk >> 1], (kk & 1) * 2);
-      const int k0 = kk * 16 + 4 * half;
-#pragma unroll
-      for (int cb = 0; cb < NCB; ++cb)
-        o[cb] = mfma32<T>(lds_tr8<T, D>(vt, k0, k0 + 8, cb * 32, lane), pf, o[cb]);
     }
-  }
+    if (EDGE && CAUSAL && kv0 > wq_last) return;  // every key of the tile is after this wave's rows
+    fwd_tile<T, D, CAUSAL, EDGE>(lds[BUF][0], lds[BUF][1], qf, o, mc, l, c, kv0, L, qrow, lane);
+  };
+  for (int j = 0; j < j_int; ++j) step(std::false_type{}, j);
+  for (int j = j_int; j < ntiles; ++j) step(std::true_type{}, j);
 
   // ---- epilogue -------------------------------------------------------------
   const float l_tot = wave_sum_halves(l);
