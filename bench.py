@@ -9,6 +9,15 @@ causal; backward 2.5× the forward.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
     python bench.py --sweep     # forward TFLOP/s for every forward workload, one line each
+    python bench.py --pmc-step  # one calibration copy + one step, for rocprofv3 --pmc runs
+    python bench.py --pmc-summary FETCH_DIR WRITE_DIR   # counters -> profiles/traffic_<workload>.json
+
+HBM traffic (roofline.traffic) comes from two rocprofv3 --pmc runs of
+--pmc-step, one collecting FETCH_SIZE and one WRITE_SIZE. Both counters are
+scaled by what they read for a plain copy of known size in the same process
+(torch.neg over a 256 MiB bf16 tensor: 256 MiB read, 256 MiB written).
+--pmc-summary stores the result with a hash of the kernel sources; the step
+bench reports it only while the sources still hash the same, else null.
 
 Inputs are resident in device memory before the timed region starts; the
 timed region is exactly K steps bracketed by device synchronisation, timed
@@ -39,7 +48,46 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--sweep", action="store_true",
                    help="time fa_fwd on every forward workload (10 warmup, 100 timed calls)")
+    p.add_argument("--pmc-step", action="store_true",
+                   help="one calibration copy and one fa_fwd + fa_bwd step (for counter runs)")
+    p.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                   help="turn FETCH_SIZE / WRITE_SIZE counter runs into profiles/traffic_<workload>.json")
     return p.parse_args()
+
+
+CALIB_BYTES = 256 << 20   # bytes read (and written) by the calibration copy
+KERNELS = ("fwd_kernel", "delta_kernel", "dkdv_kernel", "dq_kernel")
+
+
+def source_hash() -> str:
+    """sha256 over the HIP sources and the public header (what the counters describe)."""
+    import glob
+    import hashlib
+    files = sorted(glob.glob(os.path.join(ROOT, "exact_io_aware_12_amd", "csrc", "*")))
+    files.append(os.path.join(ROOT, "include", "fa.h"))
+    h = hashlib.sha256()
+    for f in files:
+        h.update(os.path.basename(f).encode())
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def traffic_path(workload: str) -> str:
+    return os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+
+
+def load_traffic(workload: str, kernel: str):
+    """Calibrated HBM bytes per launch of `kernel`, or None if absent or stale."""
+    try:
+        with open(traffic_path(workload)) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("source_sha256") != source_hash() or kernel not in t.get("kernels", {}):
+        return None
+    k = t["kernels"][kernel]
+    return k["fetch_bytes"] + k["write_bytes"]
 
 
 class Bound:
@@ -113,8 +161,12 @@ def time_calls(torch, fn, iters, warmup):
     return e0.elapsed_time(e1) / iters
 
 
-def cpu_baseline(w):
-    """The float64 oracle, untouched, on one (sequence, head) unit of the workload."""
+def cpu_baseline(w, min_seconds=10.0, max_units=4):
+    """The float64 oracle, untouched, on (sequence, head) units of the workload.
+
+    Units are run one after another until at least `min_seconds` of wall time
+    (at most `max_units`); throughput = their algorithmic FLOP / wall time.
+    """
     import numpy as np
     import oracle.attention as O
     try:
@@ -124,17 +176,90 @@ def cpu_baseline(w):
         cores = 1
     rng = np.random.default_rng(w.seed)
     L = w.seq_lens[0]
-    q, k, v, do = (rng.standard_normal((L, w.d), dtype=np.float32) for _ in range(4))
-    t0 = time.perf_counter()
-    O.head_fwd(q, k, v, w.scale, w.causal)
-    O.head_bwd(q, k, v, do, w.scale, w.causal)
-    dt = time.perf_counter() - t0
     units = w.B * w.Hq if not w.varlen else None
     flop_unit = (w.fwd_flop() + (w.bwd_flop() if w.backward else 0)) / units
-    return {"value": round(flop_unit / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(cores),
+    done, dt = 0, 0.0
+    while done < max_units and (done == 0 or dt < min_seconds):
+        q, k, v, do = (rng.standard_normal((L, w.d), dtype=np.float32) for _ in range(4))
+        t0 = time.perf_counter()
+        O.head_fwd(q, k, v, w.scale, w.causal)
+        if w.backward:
+            O.head_bwd(q, k, v, do, w.scale, w.causal)
+        dt += time.perf_counter() - t0
+        done += 1
+    return {"value": round(done * flop_unit / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(cores),
             "kind": "oracle",
-            "sample": f"1 of {units} (sequence, head) units, N={L}, forward + backward, "
-                      f"{dt:.1f} s wall; algorithmic FLOP of that unit / wall time"}
+            "sample": f"{done} of {units} (sequence, head) units, N={L}, forward + backward, "
+                      f"{dt:.1f} s wall; algorithmic FLOP of those units / wall time"}
+
+
+def run_pmc_step(args):
+    """Calibration copy of known size, then one fa_fwd + fa_bwd step (no timing)."""
+    import torch
+    import workloads as W
+    w = W.WORKLOADS[args.workload]
+    n = CALIB_BYTES // 2
+    src = torch.ones(n, dtype=torch.bfloat16, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    torch.neg(src, out=dst)            # reads CALIB_BYTES, writes CALIB_BYTES
+    torch.cuda.synchronize()
+    del src, dst
+    b = Bound(w, with_bwd=w.backward)
+    b.fwd()
+    if w.backward:
+        b.bwd()
+    torch.cuda.synchronize()
+    print("pmc step done", flush=True)
+
+
+def _counter_means(d, counter):
+    """Mean per-dispatch value of `counter` per kernel (short name) in a rocprofv3 csv run."""
+    import csv
+    import glob
+    vals = {}
+    for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+        with open(f) as fh:
+            for r in csv.DictReader(fh):
+                if r.get("Counter_Name") != counter:
+                    continue
+                name = r["Kernel_Name"]
+                short = next((k for k in KERNELS if k in name), None)
+                if short is None and "neg" in name.lower():
+                    short = "calibration_copy"
+                if short is not None:
+                    vals.setdefault(short, []).append(float(r["Counter_Value"]))
+    return {k: sum(v) / len(v) for k, v in vals.items()}
+
+
+def run_pmc_summary(args):
+    fetch = _counter_means(args.pmc_summary[0], "FETCH_SIZE")
+    write = _counter_means(args.pmc_summary[1], "WRITE_SIZE")
+    if "calibration_copy" not in fetch or "calibration_copy" not in write:
+        raise SystemExit("no calibration copy dispatch found in the counter runs")
+    f_scale = fetch["calibration_copy"] * 1024 / CALIB_BYTES   # counter bytes per real byte
+    w_scale = write["calibration_copy"] * 1024 / CALIB_BYTES
+    out = {"workload": args.workload, "source_sha256": source_hash(),
+           "calibration": {"bytes_each_way": CALIB_BYTES,
+                           "fetch_size_kib": fetch["calibration_copy"],
+                           "write_size_kib": write["calibration_copy"],
+                           "fetch_scale": f_scale, "write_scale": w_scale},
+           "kernels": {}}
+    for k in KERNELS:
+        if k in fetch and k in write:
+            out["kernels"][k] = {"fetch_size_kib": fetch[k], "write_size_kib": write[k],
+                                 "fetch_bytes": fetch[k] * 1024 / f_scale,
+                                 "write_bytes": write[k] * 1024 / w_scale}
+    os.makedirs(os.path.dirname(traffic_path(args.workload)), exist_ok=True)
+    with open(traffic_path(args.workload), "w") as f:
+        json.dump(out, f, indent=1)
+    print(f"| kernel | FETCH_SIZE KiB | WRITE_SIZE KiB | HBM read MB | HBM write MB |")
+    print(f"|---|---|---|---|---|")
+    print(f"| calibration copy ({CALIB_BYTES >> 20} MiB each way) | {fetch['calibration_copy']:.0f} | "
+          f"{write['calibration_copy']:.0f} | {CALIB_BYTES / 1e6:.1f} | {CALIB_BYTES / 1e6:.1f} |")
+    for k, v in out["kernels"].items():
+        print(f"| {k} | {v['fetch_size_kib']:.0f} | {v['write_size_kib']:.0f} | "
+              f"{v['fetch_bytes'] / 1e6:.1f} | {v['write_bytes'] / 1e6:.1f} |")
 
 
 def run_step_bench(args):
@@ -145,27 +270,44 @@ def run_step_bench(args):
         raise SystemExit(f"{w.name} has no backward; the step bench needs the training workload")
     b = Bound(w, with_bwd=True)
     flop = w.fwd_flop() + w.bwd_flop()
+    nst = b.fa.fa_bwd_num_stages()
+    names = ["fwd_kernel", "delta_kernel", "dkdv_kernel", "dq_kernel"][: 1 + nst]
+
+    def step_staged():   # fa_fwd, then fa_bwd's stages one call each (the same launches)
+        b.fwd()
+        for st in range(nst):
+            b.bwd_stage(st)
 
     for _ in range(args.warmup):
         b.step()
+    # timed region: K steps; an event after every launch gives each kernel's
+    # duration inside the steps, on the stream the kernels run on
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)]
+          for _ in range(args.steps)]
     torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
+    for k in range(args.steps):
+        ev[k][0].record()
+        b.fwd()
+        ev[k][1].record()
+        for st in range(nst):
+            b.bwd_stage(st)
+            ev[k][2 + st].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = ev[0][0].elapsed_time(ev[-1][-1]) / args.steps
+    kern = {n: sum(ev[k][i].elapsed_time(ev[k][i + 1]) for k in range(args.steps)) / args.steps
+            for i, n in enumerate(names)}
+    # the same steps through the single fa_bwd entry point, for comparison
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
     e0.record()
     for _ in range(args.steps):
         b.step()
     e1.record()
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms = e0.elapsed_time(e1) / args.steps
-
-    # per-kernel launch durations (same stream, same buffers)
-    it = max(3, min(args.steps, 20))
-    kern = {"fwd_kernel": time_calls(torch, b.fwd, it, 2)}
-    names = ["delta_kernel", "dkdv_kernel", "dq_kernel"]
-    for s, n in enumerate(names):
-        kern[n] = time_calls(torch, lambda s=s: b.bwd_stage(s), it, 2)
-    bwd_ms = sum(kern[n] for n in names)
+    ms_entry = e0.elapsed_time(e1) / args.steps
+    bwd_ms = sum(kern[n] for n in names[1:])
     alg = {  # algorithmic work per launch
         "fwd_kernel": ("mfma", w.fwd_flop()),
         "dkdv_kernel": ("mfma", 0.8 * w.bwd_flop()),    # S, dP, dV, dK: 4 of the 5 counted GEMMs
@@ -178,12 +320,12 @@ def run_step_bench(args):
         ach = work / (kern[dom] * 1e-3) / 1e12
         roof = {"kernel": dom, "bound": "mfma", "achieved": round(ach, 2),
                 "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4),
-                "traffic": None, "avg_launch_ms": round(kern[dom], 4)}
+                "traffic": load_traffic(w.name, dom), "avg_launch_ms": round(kern[dom], 4)}
     else:
         ach = work / (kern[dom] * 1e-3) / 1e9
         roof = {"kernel": dom, "bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS,
-                "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": None,
-                "avg_launch_ms": round(kern[dom], 4)}
+                "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBS, 4),
+                "traffic": load_traffic(w.name, dom), "avg_launch_ms": round(kern[dom], 4)}
 
     value = flop / (ms * 1e-3) / 1e12
     out = {
@@ -197,6 +339,7 @@ def run_step_bench(args):
         "fwd_tflops": round(w.fwd_flop() / (kern["fwd_kernel"] * 1e-3) / 1e12, 2),
         "bwd_tflops": round(w.bwd_flop() / (bwd_ms * 1e-3) / 1e12, 2),
         "kernel_ms": {k: round(v, 4) for k, v in kern.items()},
+        "ms_per_step_fa_bwd_entry": round(ms_entry, 4),
         "wall_s_timed": round(wall, 3),
         "roofline": roof,
     }
@@ -224,6 +367,9 @@ def run_sweep(args):
 
 def main():
     args = parse()
+    if args.pmc_summary:   # host-only: reads counter files
+        run_pmc_summary(args)
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -236,6 +382,8 @@ def main():
         sys.exit(1)
     if args.sweep:
         run_sweep(args)
+    elif args.pmc_step:
+        run_pmc_step(args)
     else:
         run_step_bench(args)
 

@@ -57,7 +57,7 @@ __device__ __forceinline__ float hi_f(uint32_t w) {
 
 // ---------------------------------------------------------------------------
 // D_i = Σ_c dO[i,c]·O[i,c] and LSE_i·log2 e; D/8 consecutive threads share one
-// (token, head) row.
+// (head, token) row.
 template <typename T, int D, bool VARLEN>
 __global__ __launch_bounds__(kThreads) void delta_kernel(BwdArgs a) {
   constexpr int TPR = D / 8;
@@ -66,9 +66,13 @@ __global__ __launch_bounds__(kThreads) void delta_kernel(BwdArgs a) {
   const int64_t row = (int64_t)blockIdx.x * (kThreads / TPR) + threadIdx.x / TPR;
   const int part = threadIdx.x % TPR;
   float acc = 0.f;
+  // rows are ordered head-major (row = h·T + t) so that consecutive groups
+  // write consecutive entries of the [head][token] workspace
+  const int h = (int)(row / T_total), t = (int)(row - (int64_t)h * T_total);
+  const int64_t src = ((int64_t)t * a.Hq + h) * D + part * 8;
   if (row < rows) {
-    const u32x4 x = ldg16(static_cast<const T*>(a.dout) + row * D + part * 8);
-    const u32x4 y = ldg16(static_cast<const T*>(a.o) + row * D + part * 8);
+    const u32x4 x = ldg16(static_cast<const T*>(a.dout) + src);
+    const u32x4 y = ldg16(static_cast<const T*>(a.o) + src);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       acc = fmaf(lo_f<T>(x[i]), lo_f<T>(y[i]), acc);
@@ -78,7 +82,6 @@ __global__ __launch_bounds__(kThreads) void delta_kernel(BwdArgs a) {
 #pragma unroll
   for (int off = TPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
   if (row < rows && part == 0) {
-    const int t = (int)(row / a.Hq), h = (int)(row % a.Hq);
     a.delta[(int64_t)h * a.ws_stride + t] = acc;
     a.lse2[(int64_t)h * a.ws_stride + t] = a.lse[(int64_t)h * T_total + t] * kLog2e;
   }
