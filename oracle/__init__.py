@@ -14,6 +14,7 @@ approximation: Flash Attention ÊòØ‰ªÄÈ∫º, adersaytech.com, section "exact, ‰∏çÊò
 
 Modules:
   attention   NumPy float64 forward and backward, whole tensors or sampled rows
+  decode      NumPy float64 attention of new queries over a key/value cache
   bruteforce  pure-Python loops (math.exp / math.fsum) for tiny shapes
 
 Pins: every function here is checked in tests/test_oracle_*.py against hand-
@@ -22,7 +23,8 @@ differences and torch's CPU float64 SDPA. No function is "parity unpinned".
 """
 from .attention import (attention_fwd, attention_bwd, attention_probs,
                         attention_fwd_rows, attention_bwd_sampled)
+from .decode import kvcache_fwd, kvcache_fwd_units
 from . import bruteforce
 
 __all__ = ["attention_fwd", "attention_bwd", "attention_probs", "attention_fwd_rows",
-           "attention_bwd_sampled", "bruteforce"]
+           "attention_bwd_sampled", "kvcache_fwd", "kvcache_fwd_units", "bruteforce"]

@@ -81,3 +81,42 @@ def backward(q, k, v, do, scale, causal, seqs):
                     dvv[a + j][g][c] += math.fsum(P[i][j] * do[a + i][h][c]
                                                   for i in range(L))
     return dq, dk, dvv
+
+
+def forward_kvcache(q, k, v, lens, scale, causal):
+    """Decode attention over a cache, loop by loop.
+
+    q[b][i][h][c] (Nq new queries per entry), k[b][j][g][c], v[b][j][g][c]
+    (cache positions), lens[b] valid positions. Query i of entry b sits at
+    position lens[b] − Nq + i; causal keys are those at or before it.
+    Returns o[b][i][h] (list of floats) and lse[b][i][h] (−inf for no key).
+    """
+    o, lse = [], []
+    for b in range(len(q)):
+        Nq, Hq, Hkv = len(q[b]), len(q[b][0]), len(k[b][0])
+        grp = Hq // Hkv
+        L = lens[b]
+        dv = len(v[b][0][0])
+        ob, lb = [], []
+        for i in range(Nq):
+            p = L - Nq + i
+            oi, li = [], []
+            for h in range(Hq):
+                g = h // grp
+                js = [j for j in range(L) if (not causal or j <= p)]
+                if not js:
+                    oi.append([0.0] * dv)
+                    li.append(-math.inf)
+                    continue
+                s = [scale * _dot(q[b][i][h], k[b][j][g]) for j in js]
+                m = max(s)
+                lsum = math.log(math.fsum(math.exp(x - m) for x in s)) + m
+                w = [math.exp(x - lsum) for x in s]
+                oi.append([math.fsum(w[n] * v[b][j][g][c] for n, j in enumerate(js))
+                           for c in range(dv)])
+                li.append(lsum)
+            ob.append(oi)
+            lb.append(li)
+        o.append(ob)
+        lse.append(lb)
+    return o, lse
