@@ -7,12 +7,15 @@ fallback implementation.
 
 Raw entry points with the C names and arguments (pointers as ints):
     fa_fwd, fa_bwd, fa_bwd_stage, fa_bwd_num_stages, fa_bwd_workspace_size,
+    fa_fwd_kvcache, fa_kvcache_num_splits, fa_fwd_kvcache_workspace_size,
     fa_status_string
 Tensor-level helpers:
     flash_attn_func(q, k, v, causal=False, softmax_scale=None,
                     cu_seqlens=None, max_seqlen=None, dropout_p=0.0) -> (o, lse)
     flash_attn_backward(dout, q, k, v, o, lse, causal=False, softmax_scale=None,
                         cu_seqlens=None, max_seqlen=None) -> (dq, dk, dv)
+    flash_attn_with_kvcache(q, k_cache, v_cache, cache_seqlens, causal=False,
+                            softmax_scale=None, num_splits=0) -> (o, lse)
 The call shape follows flash_attn_func in the pages' examples (Llama-Factory
 page, first code sample: q, k, v as (batch, seq, heads, head_dim), causal flag;
 FlashAttention-2 全解析, blog.gitcode.com: dropout_p and softmax_scale).
@@ -26,7 +29,8 @@ import os
 __all__ = ["FA_OK", "FA_ERR_INVALID_ARG", "FA_ERR_UNSUPPORTED", "FA_ERR_HIP", "FA_ERR_WORKSPACE",
            "FA_FP16", "FA_BF16", "FaError", "lib", "lib_path", "fa_fwd", "fa_bwd",
            "fa_bwd_workspace_size", "fa_status_string", "flash_attn_func",
-           "flash_attn_backward", "fa_bwd_stage", "fa_bwd_num_stages"]
+           "flash_attn_backward", "fa_bwd_stage", "fa_bwd_num_stages", "fa_fwd_kvcache",
+           "fa_kvcache_num_splits", "fa_fwd_kvcache_workspace_size", "flash_attn_with_kvcache"]
 
 FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_HIP, FA_ERR_WORKSPACE = 0, -1, -2, -3, -4
 FA_FP16, FA_BF16 = 0, 1
@@ -66,6 +70,12 @@ def _load():
     L.fa_bwd_num_stages.restype = i
     L.fa_bwd_workspace_size.argtypes = [i, i, i, i, i]
     L.fa_bwd_workspace_size.restype = sz
+    L.fa_fwd_kvcache.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, i, i, vp, sz, vp]
+    L.fa_fwd_kvcache.restype = i
+    L.fa_kvcache_num_splits.argtypes = [i, i, i, i, i, i]
+    L.fa_kvcache_num_splits.restype = i
+    L.fa_fwd_kvcache_workspace_size.argtypes = [i, i, i, i, i, i, i]
+    L.fa_fwd_kvcache_workspace_size.restype = sz
     L.fa_status_string.argtypes = [i]
     L.fa_status_string.restype = ctypes.c_char_p
     return L
@@ -97,6 +107,20 @@ def fa_bwd_num_stages() -> int:
 
 def fa_bwd_workspace_size(B, Hq, Hkv, N, d) -> int:
     return lib.fa_bwd_workspace_size(B, Hq, Hkv, N, d)
+
+
+def fa_fwd_kvcache(q, k_cache, v_cache, cache_seqlens, o, lse, B, Hq, Hkv, Nq, Nk, d, scale, causal,
+                   num_splits, dtype, workspace, workspace_bytes, stream) -> int:
+    return lib.fa_fwd_kvcache(q, k_cache, v_cache, cache_seqlens, o, lse, B, Hq, Hkv, Nq, Nk, d,
+                              scale, causal, num_splits, dtype, workspace, workspace_bytes, stream)
+
+
+def fa_kvcache_num_splits(B, Hq, Hkv, Nq, Nk, d) -> int:
+    return lib.fa_kvcache_num_splits(B, Hq, Hkv, Nq, Nk, d)
+
+
+def fa_fwd_kvcache_workspace_size(B, Hq, Hkv, Nq, Nk, d, num_splits) -> int:
+    return lib.fa_fwd_kvcache_workspace_size(B, Hq, Hkv, Nq, Nk, d, num_splits)
 
 
 def fa_status_string(status: int) -> str:
@@ -194,3 +218,38 @@ def flash_attn_backward(dout, q, k, v, o, lse, causal=False, softmax_scale=None,
     if st != FA_OK:
         raise FaError(st, "fa_bwd")
     return dq, dk, dv
+
+
+def flash_attn_with_kvcache(q, k_cache, v_cache, cache_seqlens, causal=False, softmax_scale=None,
+                            num_splits=0, workspace=None):
+    """Decode over a key/value cache. Returns (o, lse); lse is float32 [Hq, B·Nq].
+
+    q [B, Nq, Hq, d]; k_cache, v_cache [B, Nk, Hkv, d]; cache_seqlens int32 [B]
+    (valid positions per entry). The queries are the newest Nq positions of
+    each sequence (see fa_fwd_kvcache in include/fa.h).
+    """
+    import torch
+    if q.dim() != 4 or k_cache.dim() != 4 or v_cache.shape != k_cache.shape:
+        raise ValueError("q is (B, Nq, Hq, d); k_cache and v_cache are (B, Nk, Hkv, d)")
+    B, Nq, Hq, d = q.shape
+    if k_cache.shape[0] != B or k_cache.shape[3] != d:
+        raise ValueError(f"q {tuple(q.shape)} and k_cache {tuple(k_cache.shape)} do not match")
+    Nk, Hkv = k_cache.shape[1], k_cache.shape[2]
+    if not (q.dtype == k_cache.dtype == v_cache.dtype):
+        raise TypeError("q, k_cache, v_cache must share one dtype")
+    _check_dev(q, k_cache, v_cache, cache_seqlens)
+    if cache_seqlens.dtype != torch.int32 or cache_seqlens.numel() != B:
+        raise TypeError("cache_seqlens must be int32 with one entry per batch entry")
+    scale = softmax_scale if softmax_scale is not None else 1.0 / math.sqrt(d)
+    o = torch.empty_like(q)
+    lse = torch.empty((Hq, B * Nq), dtype=torch.float32, device=q.device)
+    need = fa_fwd_kvcache_workspace_size(B, Hq, Hkv, Nq, Nk, d, num_splits)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    st = lib.fa_fwd_kvcache(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+                            cache_seqlens.data_ptr(), o.data_ptr(), lse.data_ptr(), B, Hq, Hkv, Nq,
+                            Nk, d, float(scale), int(bool(causal)), int(num_splits), _dtype_code(q),
+                            workspace.data_ptr(), workspace.numel(), _stream())
+    if st != FA_OK:
+        raise FaError(st, "fa_fwd_kvcache")
+    return o, lse

@@ -1,5 +1,6 @@
 // C ABI of libfa.so (declared in include/fa.h): argument checks, then the
 // kernel launches. Nothing here allocates memory or keeps state.
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 
@@ -133,6 +134,97 @@ int fa_bwd_stage(int stage, const void* q, const void* k, const void* v, const v
   if (stage < 0 || stage >= fa::bwd_num_stages()) return FA_ERR_INVALID_ARG;
   return bwd_common(stage, q, k, v, o, dout, lse, dq, dk, dv, B, Hq, Hkv, N, d, scale, causal,
                     cu_seqlens, dtype, workspace, workspace_bytes, stream);
+}
+
+namespace {
+
+// Sizes of fa_fwd_kvcache; *noop when there is nothing to compute.
+int check_kvcache(int B, int Hq, int Hkv, int Nq, int Nk, int d, float scale, int causal,
+                  int num_splits, int dtype, bool* noop) {
+  *noop = false;
+  if (dtype != FA_FP16 && dtype != FA_BF16) return FA_ERR_INVALID_ARG;
+  if (B < 0 || Nq < 0 || Nk < 0 || Hq <= 0 || Hkv <= 0 || d <= 0 || num_splits < 0)
+    return FA_ERR_INVALID_ARG;
+  if (Hq % Hkv != 0) return FA_ERR_INVALID_ARG;
+  if (causal != 0 && causal != 1) return FA_ERR_INVALID_ARG;
+  if (!std::isfinite(scale) || !(scale > 0.f)) return FA_ERR_INVALID_ARG;
+  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+  // cache and row indices are formed in 64 bits, grid and query counts in 32
+  if ((int64_t)B * Nq * Hq >= (int64_t)1 << 31 || (int64_t)Nk * Hkv * d >= (int64_t)1 << 31)
+    return FA_ERR_UNSUPPORTED;
+  if (B == 0 || Nq == 0) *noop = true;
+  return FA_OK;
+}
+
+int kv_splits(int B, int Hq, int Hkv, int Nq, int Nk) {
+  // about 8 one-wave workgroups per CU over the 256 CUs, each range at least
+  // two key tiles, at most one range per tile
+  const int tk = fa::decode_tile_keys();
+  const int64_t rows = (int64_t)(Hq / Hkv) * Nq;
+  const int64_t base = (int64_t)B * Hkv * ((rows + 31) / 32);
+  const int64_t want = (2048 + base - 1) / (base > 0 ? base : 1);
+  const int64_t most = std::max<int64_t>(1, (Nk + 2 * tk - 1) / (2 * tk));
+  return (int)std::max<int64_t>(1, std::min<int64_t>(want, std::min<int64_t>(most, 256)));
+}
+
+}  // namespace
+
+int fa_kvcache_num_splits(int B, int Hq, int Hkv, int Nq, int Nk, int d) {
+  bool noop;
+  if (check_kvcache(B, Hq, Hkv, Nq, Nk, d, 1.f, 0, 0, FA_FP16, &noop) != FA_OK) return 0;
+  return kv_splits(B, Hq, Hkv, Nq, Nk);
+}
+
+size_t fa_fwd_kvcache_workspace_size(int B, int Hq, int Hkv, int Nq, int Nk, int d,
+                                     int num_splits) {
+  bool noop;
+  if (check_kvcache(B, Hq, Hkv, Nq, Nk, d, 1.f, 0, num_splits, FA_FP16, &noop) != FA_OK) return 0;
+  const int sp = num_splits > 0 ? num_splits : kv_splits(B, Hq, Hkv, Nq, Nk);
+  const size_t bytes = (size_t)sp * B * Hq * Nq * (size_t)(d + 1) * sizeof(float);
+  return (bytes + 255) / 256 * 256;
+}
+
+int fa_fwd_kvcache(const void* q, const void* k_cache, const void* v_cache,
+                   const int32_t* cache_seqlens, void* o, float* lse, int B, int Hq, int Hkv,
+                   int Nq, int Nk, int d, float scale, int causal, int num_splits, int dtype,
+                   void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  bool noop;
+  int st = check_kvcache(B, Hq, Hkv, Nq, Nk, d, scale, causal, num_splits, dtype, &noop);
+  if (st != FA_OK || noop) return st;
+  if (!q || !k_cache || !v_cache || !cache_seqlens || !o || !lse) return FA_ERR_INVALID_ARG;
+  const void* ptrs[] = {q, k_cache, v_cache, o, lse, workspace};
+  for (const void* p : ptrs)
+    if (p && !aligned16(p)) return FA_ERR_INVALID_ARG;
+  if ((reinterpret_cast<uintptr_t>(cache_seqlens) & 3u) != 0) return FA_ERR_INVALID_ARG;
+  const int sp = num_splits > 0 ? num_splits : kv_splits(B, Hq, Hkv, Nq, Nk);
+  if (!workspace || workspace_bytes < fa_fwd_kvcache_workspace_size(B, Hq, Hkv, Nq, Nk, d, sp))
+    return FA_ERR_WORKSPACE;
+  fa::DecodeArgs a;
+  a.q = q;
+  a.k = k_cache;
+  a.v = v_cache;
+  a.seqlens = cache_seqlens;
+  a.o = o;
+  a.lse = lse;
+  const size_t units = (size_t)B * Hq * Nq;
+  a.part_o = static_cast<float*>(workspace);
+  a.part_lse = a.part_o + (size_t)sp * units * d;
+  a.B = B;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.Nq = Nq;
+  a.Nk = Nk;
+  a.group = Hq / Hkv;
+  a.rows = a.group * Nq;
+  a.n_rb = (a.rows + 31) / 32;
+  a.splits = sp;
+  const int tk = fa::decode_tile_keys();
+  const int per = (Nk + sp - 1) / sp;
+  a.chunk = std::max(tk, (per + tk - 1) / tk * tk);
+  a.scale_log2 = scale * kLog2e;
+  if ((int64_t)a.n_rb * sp * Hkv * B >= (int64_t)1 << 31) return FA_ERR_UNSUPPORTED;
+  hipError_t e = fa::launch_decode(a, dtype == FA_BF16, d, causal != 0, stream);
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
 const char* fa_status_string(int status) {

@@ -1,0 +1,234 @@
+// Attention of a few new queries over a key/value cache (decode), gfx950.
+//
+// Per batch entry b the cache holds L_b valid positions; the Nq new queries
+// are its newest Nq positions (query i at L_b − Nq + i) and, when causal, see
+// the keys at or before their position. The cache is split along the keys
+// into `splits` ranges; one wavefront per (32-row block, split, KV head,
+// entry) streams its range of K and V through LDS once and computes, for the
+// rows of that block, a partial O over its keys and the matching log-sum-exp.
+// The rows are the Hq/Hkv query heads of the KV head times the Nq queries,
+// so the cache is read once per KV head, not once per query head. A second
+// kernel merges the partials exactly by their log-sum-exp (one exchange step:
+// LSE = ln Σ_s e^{LSE_s}, O = Σ_s e^{LSE_s − LSE}·O_s), the identity that also
+// merges results computed on different GPUs.
+//
+// Inside a wave the tile step is the forward's: Sᵀ = K·Qᵀ on MFMA (a lane per
+// row), masking, online softmax with a lazily raised reference max, Oᵀ += Vᵀ·Pᵀ
+// with Vᵀ read transposed from the row-major LDS tile. The work per byte is
+// small (d FLOP per loaded K or V element per row), so the kernel is bound by
+// HBM: K/V tiles of 32 keys are copied global -> LDS three stages deep.
+#include "fa_device.h"
+#include "fa_kernels.h"
+
+namespace fa {
+
+namespace {
+
+constexpr int kTK = 32;       // keys per tile
+constexpr int kStages = 3;    // K/V tiles in flight or in use
+constexpr float kRescaleHeadroom = 8.f;
+
+// s_waitcnt with vmcnt = N (0..63), other counters not waited for
+template <int N>
+__device__ __forceinline__ void wait_vmem_le() {
+  static_assert(N >= 0 && N < 64, "vmcnt holds 0..63");
+  __builtin_amdgcn_s_waitcnt(0x0f70 | (N & 15) | ((N >> 4) << 14));
+}
+
+template <typename T, int D, bool CAUSAL>
+__global__ __launch_bounds__(64) void decode_kernel(DecodeArgs a) {
+  constexpr int NKB = D / 16;
+  constexpr int NCB = D / 32;
+  constexpr int TILE = kTK * D;
+  constexpr int PER = kTK / (64 / (D / 8));   // copy instructions per K or V tile
+  __shared__ __attribute__((aligned(1024))) T k_lds[kStages][TILE];
+  __shared__ __attribute__((aligned(1024))) T v_lds[kStages][TILE];
+
+  const int lane = threadIdx.x, col = lane & 31, half = lane >> 5;
+  int idx = blockIdx.x;
+  const int rb = idx % a.n_rb;
+  idx /= a.n_rb;
+  const int sp = idx % a.splits;
+  idx /= a.splits;
+  const int g = idx % a.Hkv, b = idx / a.Hkv;
+
+  const int L = min(max(a.seqlens[b], 0), a.Nk);   // valid cache positions
+  const int k_begin = sp * a.chunk;
+  const int k_end = min(L, k_begin + a.chunk);
+
+  // this lane's row: query head g·group + hg, query i
+  const int r = rb * 32 + col;
+  const bool row_ok = r < a.rows;
+  const int hg = row_ok ? r / a.Nq : 0, qi = row_ok ? r % a.Nq : 0;
+  const int h = g * a.group + hg;
+  const int qpos = L - a.Nq + qi;                     // the query's position in the sequence
+  const int64_t unit = ((int64_t)b * a.Hq + h) * a.Nq + qi;
+  const int64_t units = (int64_t)a.B * a.Hq * a.Nq;
+  float* po = a.part_o + ((int64_t)sp * units + unit) * D;
+  float* pl = a.part_lse + (int64_t)sp * units + unit;
+
+  f32x16 o[NCB];
+#pragma unroll
+  for (int cb = 0; cb < NCB; ++cb) o[cb] = f32x16{};
+  float mc = -INFINITY, l = 0.f;
+
+  if (k_begin < k_end) {
+    const int64_t kvs = (int64_t)a.Hkv * D;
+    const T* kp = static_cast<const T*>(a.k) + (int64_t)b * a.Nk * kvs + (int64_t)g * D;
+    const T* vp = static_cast<const T*>(a.v) + (int64_t)b * a.Nk * kvs + (int64_t)g * D;
+    const int ntiles = (k_end - k_begin + kTK - 1) / kTK;
+    auto issue = [&](int t) {   // rows past k_end repeat row k_end-1 (masked below)
+      tile_dma<T, kTK, D, 1>(k_lds[t % kStages], kp, kvs, k_begin + t * kTK, k_end, 0, lane);
+      tile_dma<T, kTK, D, 1>(v_lds[t % kStages], vp, kvs, k_begin + t * kTK, k_end, 0, lane);
+    };
+    issue(0);
+    if (ntiles > 1) issue(1);
+
+    u32x4 qf[NKB];
+    {
+      const T* qp = static_cast<const T*>(a.q) + (((int64_t)b * a.Nq + qi) * a.Hq + h) * D;
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+        qf[kb] = row_ok ? ldg16(qp + kb * 16 + half * 8) : u32x4{0, 0, 0, 0};
+    }
+    const float c = a.scale_log2;
+
+    for (int t = 0; t < ntiles; ++t) {
+      // tile t has landed once only the newer tile's copies are outstanding
+      if (t + 1 < ntiles)
+        wait_vmem_le<2 * PER>();
+      else
+        wait_vmem_le<0>();
+      if (t + 2 < ntiles) issue(t + 2);   // into the stage tile t-1 used (this wave is done with it)
+      const T* kt = k_lds[t % kStages];
+      const T* vt = v_lds[t % kStages];
+      const int kbase = k_begin + t * kTK;
+
+      f32x16 s = f32x16{};
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+        s = mfma32<T>(lds_row16<T, D>(kt, col, 2 * kb + half), qf[kb], s);
+
+      // mask keys past the range and, causally, keys after the query
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int kj = kbase + 8 * (i >> 2) + 4 * half + (i & 3);
+        s[i] = (kj < k_end && !(CAUSAL && kj > qpos)) ? s[i] : -INFINITY;
+      }
+      float mx = s[0];
+#pragma unroll
+      for (int i = 1; i < 16; ++i) mx = fmaxf(mx, s[i]);
+      const float mxc = wave_max_halves(mx) * c;
+      if (__builtin_amdgcn_ballot_w64(mxc > mc + kRescaleHeadroom) != 0) {
+        const float mc_new = fmaxf(mc, mxc);
+        // a row that has seen no key yet keeps mc = −inf and nothing to scale
+        const float alpha = mc_new == -INFINITY ? 1.f : fast_exp2(mc - mc_new);
+        l *= alpha;
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb) o[cb] *= alpha;
+        mc = mc_new;
+      }
+      const float mcs = mc == -INFINITY ? 0.f : mc;   // all of such a row's scores are −inf
+      float ls[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        s[i] = fast_exp2(fmaf(s[i], c, -mcs));
+        ls[i & 3] += s[i];
+      }
+      l += (ls[0] + ls[1]) + (ls[2] + ls[3]);
+#pragma unroll
+      for (int kk = 0; kk < kTK / 16; ++kk) {
+        const u32x4 pf = acc_operand<T>(s, kk * 2);
+        const int k0 = kk * 16 + 4 * half;
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb)
+          o[cb] = mfma32<T>(lds_tr8<T, D>(vt, k0, k0 + 8, cb * 32, lane), pf, o[cb]);
+      }
+    }
+  }
+
+  // partial result of this split: normalised O and its LSE (−inf, O = 0 if no key)
+  const float l_tot = wave_sum_halves(l);
+  if (row_ok) {
+    const bool any = l_tot > 0.f;
+    const float inv = any ? 1.f / l_tot : 0.f;
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        float4 w;
+        w.x = o[cb][4 * rr + 0] * inv;
+        w.y = o[cb][4 * rr + 1] * inv;
+        w.z = o[cb][4 * rr + 2] * inv;
+        w.w = o[cb][4 * rr + 3] * inv;
+        *reinterpret_cast<float4*>(po + cb * 32 + 8 * rr + 4 * half) = w;
+      }
+    if (half == 0) *pl = any ? (mc + log2f(l_tot)) * kLn2 : -INFINITY;
+  }
+}
+
+// Merge of the splits for one (entry, query head, query) row per wave:
+// LSE = m + ln Σ_s e^{LSE_s − m}, O = Σ_s e^{LSE_s − LSE}·O_s (m = max_s LSE_s).
+template <typename T, int D>
+__global__ __launch_bounds__(256) void decode_combine_kernel(DecodeArgs a) {
+  constexpr int PER_LANE = D / 64;
+  const int64_t units = (int64_t)a.B * a.Hq * a.Nq;
+  const int64_t unit = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (unit >= units) return;
+  float m = -INFINITY;
+  for (int sp = 0; sp < a.splits; ++sp) m = fmaxf(m, a.part_lse[sp * units + unit]);
+  float acc[PER_LANE] = {};
+  float wsum = 0.f;
+  if (m != -INFINITY) {
+    for (int sp = 0; sp < a.splits; ++sp) {
+      const float ls = a.part_lse[sp * units + unit];
+      if (ls == -INFINITY) continue;           // this split saw no key of the row
+      const float w = expf(ls - m);
+      wsum += w;
+      const float* po = a.part_o + (sp * units + unit) * D;
+#pragma unroll
+      for (int e = 0; e < PER_LANE; ++e) acc[e] = fmaf(w, po[PER_LANE * lane + e], acc[e]);
+    }
+  }
+  const int qi = (int)(unit % a.Nq);
+  const int64_t bh = unit / a.Nq;
+  const int h = (int)(bh % a.Hq), b = (int)(bh / a.Hq);
+  T* op = static_cast<T*>(a.o) + (((int64_t)b * a.Nq + qi) * a.Hq + h) * D;
+  const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
+  if constexpr (PER_LANE == 2)
+    *reinterpret_cast<uint32_t*>(op + 2 * lane) = pack2<T>(acc[0] * inv, acc[1] * inv);
+  else
+    op[lane] = static_cast<T>(acc[0] * inv);
+  if (lane == 0)
+    a.lse[(int64_t)h * a.B * a.Nq + (int64_t)b * a.Nq + qi] =
+        wsum > 0.f ? m + logf(wsum) : -INFINITY;
+}
+
+template <typename T, int D, bool CAUSAL>
+hipError_t launch(const DecodeArgs& a, hipStream_t s) {
+  (void)hipGetLastError();  // drop an error left pending by earlier, unrelated HIP calls
+  const int64_t g1 = (int64_t)a.n_rb * a.splits * a.Hkv * a.B;
+  hipLaunchKernelGGL((decode_kernel<T, D, CAUSAL>), dim3((unsigned)g1), dim3(64), 0, s, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int64_t units = (int64_t)a.B * a.Hq * a.Nq;
+  hipLaunchKernelGGL((decode_combine_kernel<T, D>), dim3((unsigned)((units + 3) / 4)), dim3(256),
+                     0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+int decode_tile_keys() { return kTK; }
+
+hipError_t launch_decode(const DecodeArgs& a, bool bf16_in, int d, bool causal, hipStream_t s) {
+  if (bf16_in) {
+    if (d == 64) return causal ? launch<bf16, 64, true>(a, s) : launch<bf16, 64, false>(a, s);
+    return causal ? launch<bf16, 128, true>(a, s) : launch<bf16, 128, false>(a, s);
+  }
+  if (d == 64) return causal ? launch<f16, 64, true>(a, s) : launch<f16, 64, false>(a, s);
+  return causal ? launch<f16, 128, true>(a, s) : launch<f16, 128, false>(a, s);
+}
+
+}  // namespace fa

@@ -39,6 +39,24 @@ struct BwdArgs {
   float scale_log2;
 };
 
+struct DecodeArgs {
+  const void* q;              // [B, Nq, Hq, d]
+  const void* k;              // [B, Nk, Hkv, d]
+  const void* v;
+  const int32_t* seqlens;     // [B] valid cache positions (device)
+  void* o;                    // [B, Nq, Hq, d]
+  float* lse;                 // [Hq, B·Nq]
+  float* part_o;              // workspace [splits][B·Hq·Nq][d] float32
+  float* part_lse;            // workspace [splits][B·Hq·Nq] float32
+  int B, Hq, Hkv, Nq, Nk;
+  int group;                  // Hq / Hkv
+  int rows;                   // group · Nq rows per (entry, KV head)
+  int n_rb;                   // ceil(rows / 32)
+  int splits;                 // key ranges per (entry, KV head)
+  int chunk;                  // keys per range, a multiple of the key tile
+  float scale_log2;
+};
+
 int fwd_query_tile();
 hipError_t launch_fwd(const FwdArgs& a, bool bf16_in, int d, bool causal, bool varlen,
                       hipStream_t s);
@@ -47,5 +65,7 @@ hipError_t launch_fwd(const FwdArgs& a, bool bf16_in, int d, bool causal, bool v
 int bwd_num_stages();
 hipError_t launch_bwd(const BwdArgs& a, bool bf16_in, int d, bool causal, bool varlen, int stage,
                       hipStream_t s);
+int decode_tile_keys();
+hipError_t launch_decode(const DecodeArgs& a, bool bf16_in, int d, bool causal, hipStream_t s);
 
 }  // namespace fa

@@ -68,7 +68,7 @@ typedef enum {
                                Hq % Hkv != 0, bad scale */
   FA_ERR_UNSUPPORTED = -2,  /* head dim other than 64 / 128 */
   FA_ERR_HIP = -3,          /* the HIP runtime refused a launch (e.g. no device) */
-  FA_ERR_WORKSPACE = -4     /* workspace missing or smaller than fa_bwd_workspace_size() */
+  FA_ERR_WORKSPACE = -4     /* workspace missing or smaller than the size function returns */
 } fa_status;
 
 typedef enum { FA_FP16 = 0, FA_BF16 = 1 } fa_dtype;
@@ -117,6 +117,43 @@ int fa_bwd_stage(int stage, const void* q, const void* k, const void* v, const v
 
 /* Workspace bytes fa_bwd needs; an upper bound that uses T <= B·N. 0 on bad sizes. */
 size_t fa_bwd_workspace_size(int B, int Hq, int Hkv, int N, int d);
+
+/*
+ * Decode: attention of Nq new queries per batch entry over a key/value cache
+ * (the inference use of the method, Flash Attention 是什麼, adersaytech.com,
+ * "適用場景": long contexts at inference time).
+ *   q       : [B, Nq, Hq, d]   the new queries, `dtype`
+ *   k_cache : [B, Nk, Hkv, d]  cache capacity Nk per entry, `dtype`
+ *   v_cache : [B, Nk, Hkv, d]
+ *   cache_seqlens : int32 device [B], valid positions L_b of entry b
+ *                   (0 <= L_b <= Nk; values outside are clamped into range)
+ *   o       : [B, Nq, Hq, d]   `dtype` (nearest even)
+ *   lse     : [Hq, B·Nq]       float32, column b·Nq + i for query i of entry b
+ * The queries are the newest Nq positions of each sequence: query i of entry
+ * b sits at position L_b − Nq + i and, when causal, sees the cached keys at
+ * or before that position; otherwise it sees all L_b keys. A query that sees
+ * no key gets o = 0 and lse = −inf.
+ * The cache is split along the keys into `num_splits` ranges per (entry, KV
+ * head) processed in parallel and merged exactly by their log-sum-exp;
+ * num_splits = 0 picks fa_kvcache_num_splits(...). `workspace` holds the
+ * per-split partial results: at least fa_fwd_kvcache_workspace_size(...)
+ * bytes for the same sizes and num_splits.
+ * Conventions (alignment, ownership, errors, determinism) as above; B = 0 or
+ * Nq = 0 is a no-op.
+ */
+int fa_fwd_kvcache(const void* q, const void* k_cache, const void* v_cache,
+                   const int32_t* cache_seqlens, void* o, float* lse,
+                   int B, int Hq, int Hkv, int Nq, int Nk, int d, float scale, int causal,
+                   int num_splits, int dtype, void* workspace, size_t workspace_bytes,
+                   hipStream_t stream);
+
+/* The key-range count fa_fwd_kvcache uses for num_splits = 0 (>= 1); 0 on bad sizes. */
+int fa_kvcache_num_splits(int B, int Hq, int Hkv, int Nq, int Nk, int d);
+
+/* Workspace bytes for fa_fwd_kvcache: (d + 1)·4 bytes per (split, entry, query head,
+ * query), rounded up to 256; num_splits = 0 means the automatic count. 0 on bad sizes. */
+size_t fa_fwd_kvcache_workspace_size(int B, int Hq, int Hkv, int Nq, int Nk, int d,
+                                     int num_splits);
 
 /* Static, NUL-terminated text for a status code. */
 const char* fa_status_string(int status);

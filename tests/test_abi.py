@@ -21,7 +21,9 @@ def declared_functions():
 
 def test_header_declares_the_boundary():
     assert declared_functions() == ["fa_bwd", "fa_bwd_num_stages", "fa_bwd_stage",
-                                    "fa_bwd_workspace_size", "fa_fwd", "fa_status_string"]
+                                    "fa_bwd_workspace_size", "fa_fwd", "fa_fwd_kvcache",
+                                    "fa_fwd_kvcache_workspace_size", "fa_kvcache_num_splits",
+                                    "fa_status_string"]
 
 
 def test_every_declared_symbol_is_exported():
@@ -123,3 +125,45 @@ def test_no_device_reports_hip_error():
     if torch.cuda.is_available():
         pytest.skip("a GPU is present")
     assert fwd() == fa.FA_ERR_HIP
+
+
+def kvc(**kw):
+    a = dict(q=P, k=P, v=P, lens=P, o=P, lse=P, B=2, Hq=4, Hkv=2, Nq=1, Nk=64, d=128,
+             scale=0.125, causal=1, splits=2, dtype=fa.FA_BF16, ws=P, wsb=1 << 20)
+    a.update(kw)
+    return fa.fa_fwd_kvcache(a["q"], a["k"], a["v"], a["lens"], a["o"], a["lse"], a["B"], a["Hq"],
+                             a["Hkv"], a["Nq"], a["Nk"], a["d"], a["scale"], a["causal"],
+                             a["splits"], a["dtype"], a["ws"], a["wsb"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dtype=5), fa.FA_ERR_INVALID_ARG),
+    (dict(Hq=3), fa.FA_ERR_INVALID_ARG),
+    (dict(Nq=-1), fa.FA_ERR_INVALID_ARG),
+    (dict(Nk=-1), fa.FA_ERR_INVALID_ARG),
+    (dict(splits=-1), fa.FA_ERR_INVALID_ARG),
+    (dict(causal=2), fa.FA_ERR_INVALID_ARG),
+    (dict(scale=0.0), fa.FA_ERR_INVALID_ARG),
+    (dict(d=96), fa.FA_ERR_UNSUPPORTED),
+    (dict(lens=None), fa.FA_ERR_INVALID_ARG),
+    (dict(q=P + 8), fa.FA_ERR_INVALID_ARG),
+    (dict(lens=P + 2), fa.FA_ERR_INVALID_ARG),
+    (dict(ws=None), fa.FA_ERR_WORKSPACE),
+    (dict(wsb=16), fa.FA_ERR_WORKSPACE),
+    (dict(B=0), fa.FA_OK),
+    (dict(Nq=0), fa.FA_OK),
+])
+def test_kvcache_host_checks(kw, status):
+    assert kvc(**kw) == status
+
+
+def test_kvcache_splits_and_workspace():
+    # rows per (entry, KV head) = (Hq/Hkv)·Nq = 4 -> one 32-row block; 16·8 blocks want 16 ranges
+    assert fa.fa_kvcache_num_splits(16, 32, 8, 1, 8192, 128) == 16
+    # at most one range per two 32-key tiles
+    assert fa.fa_kvcache_num_splits(1, 2, 2, 1, 100, 64) == 2
+    assert fa.fa_kvcache_num_splits(1, 2, 2, 1, 0, 64) == 1
+    assert fa.fa_kvcache_num_splits(1, 3, 2, 1, 64, 64) == 0
+    assert fa.fa_fwd_kvcache_workspace_size(2, 4, 2, 3, 64, 128, 5) == (5 * 2 * 4 * 3 * 129 * 4 + 255) // 256 * 256
+    assert fa.fa_fwd_kvcache_workspace_size(16, 32, 8, 1, 8192, 128, 0) == 16 * 16 * 32 * 129 * 4
+    assert fa.fa_fwd_kvcache_workspace_size(1, 2, 2, 1, 64, 80, 1) == 0

@@ -167,3 +167,92 @@ def to_torch(arrays, dtype: str, device="cpu"):
         else:
             res[name] = torch.from_numpy(a).to(td).to(device)
     return res
+
+
+# ---------------------------------------------------------------------------
+# Decode over a key/value cache: Nq new queries per batch entry against a
+# cache of capacity Nk with L_b valid positions per entry.
+#
+# Recipe (one generator per workload, NumPy PCG64):
+#   1. rng = numpy.random.default_rng(seed)
+#   2. lengths: the given list, else all Nk ("full"), else
+#      rng.integers(lo, Nk, size=B, endpoint=True) for lens="draw:lo"
+#   3. q [B, Nq, Hq, d], then k, v [B, Nk, Hkv, d], each
+#      rng.standard_normal(shape, dtype=float32); cache slots past L_b hold
+#      random values too (they must never be read into the result)
+#   4. the caller rounds to fp16 / bf16 (round to nearest even)
+@dataclasses.dataclass(frozen=True)
+class DecodeWorkload:
+    name: str
+    B: int
+    Hq: int
+    Hkv: int
+    Nq: int
+    Nk: int
+    d: int
+    dtype: str = "bf16"
+    causal: bool = True
+    seed: int = 0
+    lens: object = "full"        # "full", "draw:<lo>", or a tuple of B lengths
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / math.sqrt(self.d)
+
+    def cache_lens(self) -> List[int]:
+        if isinstance(self.lens, (tuple, list)):
+            return [int(x) for x in self.lens]
+        if self.lens == "full":
+            return [self.Nk] * self.B
+        lo = int(str(self.lens).split(":")[1])
+        return [int(x) for x in np.random.default_rng(self.seed).integers(
+            lo, self.Nk, size=self.B, endpoint=True)]
+
+    def kv_bytes(self) -> int:
+        """K and V bytes of the valid cache positions (what one call must read)."""
+        return 2 * sum(self.cache_lens()) * self.Hkv * self.d * 2
+
+    def io_bytes(self) -> int:
+        """Compulsory HBM bytes of one call: valid K/V, q and o, lse."""
+        qo = 2 * self.B * self.Nq * self.Hq * self.d * 2
+        return self.kv_bytes() + qo + 4 * self.Hq * self.B * self.Nq + 4 * self.B
+
+    def flop(self) -> float:
+        """4·d FLOP per (query, visible key) pair (the forward convention)."""
+        tot = 0
+        for L in self.cache_lens():
+            for i in range(self.Nq):
+                vis = min(L, max(0, L - self.Nq + i + 1)) if self.causal else L
+                tot += vis
+        return 4.0 * self.d * self.Hq * tot
+
+
+DECODE_WORKLOADS: Dict[str, DecodeWorkload] = {
+    # Llama-3-8B heads decoding one token per sequence over 8k-token caches
+    "decode_llama": DecodeWorkload("decode_llama", B=16, Hq=32, Hkv=8, Nq=1, Nk=8192, d=128,
+                                   dtype="bf16", causal=True, seed=6),
+    # four new tokens per sequence (draft verification), ragged cache lengths
+    "decode_multi": DecodeWorkload("decode_multi", B=4, Hq=32, Hkv=8, Nq=4, Nk=4096, d=128,
+                                   dtype="bf16", causal=True, seed=7, lens="draw:1024"),
+}
+
+
+def decode_custom(B, Hq, Hkv, Nq, Nk, d, dtype="bf16", causal=True, seed=0, lens="full"):
+    if isinstance(lens, list):
+        lens = tuple(lens)
+    return DecodeWorkload("decode_custom", B=B, Hq=Hq, Hkv=Hkv, Nq=Nq, Nk=Nk, d=d, dtype=dtype,
+                          causal=causal, seed=seed, lens=lens)
+
+
+def generate_decode(w: DecodeWorkload):
+    """float32 q [B, Nq, Hq, d], k/v [B, Nk, Hkv, d] and int32 cache_seqlens [B]."""
+    lens = w.cache_lens()
+    rng = np.random.default_rng(w.seed)
+    if isinstance(w.lens, str) and w.lens.startswith("draw:"):
+        rng.integers(int(w.lens.split(":")[1]), w.Nk, size=w.B, endpoint=True)
+    return {
+        "q": rng.standard_normal((w.B, w.Nq, w.Hq, w.d), dtype=np.float32),
+        "k": rng.standard_normal((w.B, w.Nk, w.Hkv, w.d), dtype=np.float32),
+        "v": rng.standard_normal((w.B, w.Nk, w.Hkv, w.d), dtype=np.float32),
+        "cache_seqlens": np.asarray(lens, dtype=np.int32),
+    }
