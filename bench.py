@@ -9,6 +9,7 @@ causal; backward 2.5× the forward.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
     python bench.py --sweep     # forward TFLOP/s for every forward workload, one line each
+    python bench.py --workload decode_llama   # decode over a KV cache: HBM GB/s, one line
     python bench.py --pmc-step  # one calibration copy + one step, for rocprofv3 --pmc runs
     python bench.py --pmc-summary FETCH_DIR WRITE_DIR   # counters -> profiles/traffic_<workload>.json
 
@@ -19,9 +20,12 @@ scaled by what they read for a plain copy of known size in the same process
 --pmc-summary stores the result with a hash of the kernel sources; the step
 bench reports it only while the sources still hash the same, else null.
 
-Inputs are resident in device memory before the timed region starts; the
-timed region is exactly K steps bracketed by device synchronisation, timed
-with HIP events on the stream the kernels are launched on.
+Inputs are resident in device memory before the timed region starts. The
+timed region is exactly K steps through the entry points (fa_fwd + fa_bwd, or
+fa_fwd_kvcache) bracketed by device synchronisation, timed with HIP events on
+the stream the kernels are launched on; `value` and `ms_per_step` come from
+it. A second pass of K steps calls the stages one by one with an event after
+every launch, for each kernel's average duration (`kernel_ms`, the roofline).
 """
 from __future__ import annotations
 
@@ -56,7 +60,8 @@ def parse():
 
 
 CALIB_BYTES = 256 << 20   # bytes read (and written) by the calibration copy
-KERNELS = ("fwd_kernel", "delta_kernel", "dkdv_kernel", "dq_kernel")
+KERNELS = ("fwd_kernel", "delta_kernel", "dkdv_kernel", "dq_kernel", "decode_combine_kernel",
+           "decode_kernel")
 
 
 def source_hash() -> str:
@@ -193,11 +198,133 @@ def cpu_baseline(w, min_seconds=10.0, max_units=4):
                       f"{dt:.1f} s wall; algorithmic FLOP of those units / wall time"}
 
 
+class DecodeBound:
+    """Device buffers and raw C-ABI calls of one decode workload."""
+
+    def __init__(self, w):
+        import torch
+        import exact_io_aware_12_amd as fa
+        import workloads as W
+        self.fa, self.w, self.torch = fa, w, torch
+        td = {"fp16": torch.float16, "bf16": torch.bfloat16}[w.dtype]
+        a = W.generate_decode(w)
+        self.q = torch.from_numpy(a["q"]).to(td).cuda()
+        self.k = torch.from_numpy(a["k"]).to(td).cuda()
+        self.v = torch.from_numpy(a["v"]).to(td).cuda()
+        self.lens = torch.from_numpy(a["cache_seqlens"]).cuda()
+        del a
+        self.o = torch.empty_like(self.q)
+        self.lse = torch.empty((w.Hq, w.B * w.Nq), dtype=torch.float32, device="cuda")
+        self.splits = fa.fa_kvcache_num_splits(w.B, w.Hq, w.Hkv, w.Nq, w.Nk, w.d)
+        nws = fa.fa_fwd_kvcache_workspace_size(w.B, w.Hq, w.Hkv, w.Nq, w.Nk, w.d, self.splits)
+        self.ws = torch.empty(nws, dtype=torch.uint8, device="cuda")
+        self.code = fa.FA_BF16 if w.dtype == "bf16" else fa.FA_FP16
+        self.stream = torch.cuda.current_stream().cuda_stream
+
+    def _args(self):
+        w = self.w
+        return (self.q.data_ptr(), self.k.data_ptr(), self.v.data_ptr(), self.lens.data_ptr(),
+                self.o.data_ptr(), self.lse.data_ptr(), w.B, w.Hq, w.Hkv, w.Nq, w.Nk, w.d, w.scale,
+                int(w.causal), self.splits, self.code, self.ws.data_ptr(), self.ws.numel(),
+                self.stream)
+
+    def call(self):
+        st = self.fa.fa_fwd_kvcache(*self._args())
+        if st != self.fa.FA_OK:
+            raise self.fa.FaError(st, "fa_fwd_kvcache")
+
+    def stage(self, i):
+        st = self.fa.fa_fwd_kvcache_stage(i, *self._args())
+        if st != self.fa.FA_OK:
+            raise self.fa.FaError(st, "fa_fwd_kvcache_stage")
+
+
+def cpu_baseline_decode(w, min_seconds=10.0, max_rounds=50):
+    """The float64 decode oracle, untouched, over the whole workload, repeated to >= 10 s."""
+    import numpy as np
+    import oracle.decode as OD
+    import workloads as W
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max((d.get("num_threads", 1) for d in threadpool_info()), default=1)
+    except Exception:  # pragma: no cover
+        cores = 1
+    a = W.generate_decode(w)
+    rounds, dt = 0, 0.0
+    while rounds < max_rounds and (rounds == 0 or dt < min_seconds):
+        t0 = time.perf_counter()
+        OD.kvcache_fwd(a["q"], a["k"], a["v"], a["cache_seqlens"], w.scale, w.causal)
+        dt += time.perf_counter() - t0
+        rounds += 1
+    return {"value": round(rounds * w.io_bytes() / dt / 1e9, 4), "unit": "GB/s",
+            "cores": int(cores), "kind": "oracle",
+            "sample": f"the whole workload {rounds} times, {dt:.1f} s wall; compulsory bytes of "
+                      f"one call (valid K/V, q, o, lse) x calls / wall time"}
+
+
+def run_decode_bench(args):
+    import torch
+    import workloads as W
+    w = W.DECODE_WORKLOADS[args.workload]
+    b = DecodeBound(w)
+    nst = b.fa.fa_fwd_kvcache_num_stages()
+    names = ["decode_kernel", "decode_combine_kernel"][:nst]
+    for _ in range(args.warmup):
+        b.call()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(nst + 1)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        ev[k][0].record()
+        for st in range(nst):
+            b.stage(st)
+            ev[k][st + 1].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = ev[0][0].elapsed_time(ev[-1][-1]) / args.steps
+    kern = {n: sum(ev[k][i].elapsed_time(ev[k][i + 1]) for k in range(args.steps)) / args.steps
+            for i, n in enumerate(names)}
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(args.steps):
+        b.call()
+    e1.record()
+    torch.cuda.synchronize()
+    ms_entry = e0.elapsed_time(e1) / args.steps
+    value = w.io_bytes() / (ms_entry * 1e-3) / 1e9
+    # dominant kernel: the range pass; its algorithmic bytes are the valid K/V and q it must read
+    dom = max(kern, key=kern.get)
+    alg = {"decode_kernel": w.kv_bytes() + 2 * w.B * w.Nq * w.Hq * w.d,
+           "decode_combine_kernel": 2 * w.B * w.Nq * w.Hq * w.d + 4 * w.B * w.Nq * w.Hq}[dom]
+    ach = alg / (kern[dom] * 1e-3) / 1e9
+    out = {
+        "metric": "decode attention over a KV cache: HBM GB/s (compulsory bytes / time)",
+        "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_entry, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",
+        "config": {"workload": f"{w.name}: fa_fwd_kvcache", "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv,
+                   "Nq": w.Nq, "Nk": w.Nk, "d": w.d, "causal": w.causal, "seed": w.seed,
+                   "splits": b.splits, "cache_lens": w.cache_lens()},
+        "pct_of_hbm_peak": round(100 * value / PEAK_HBM_GBS, 2),
+        "attention_tflops": round(w.flop() / (ms_entry * 1e-3) / 1e12, 3),
+        "kernel_ms": {k: round(v, 5) for k, v in kern.items()},
+        "ms_per_step_staged": round(ms, 5),
+        "wall_s_timed": round(wall, 3),
+        "roofline": {"kernel": dom, "bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS,
+                     "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBS, 4),
+                     "traffic": load_traffic(w.name, dom), "avg_launch_ms": round(kern[dom], 5)},
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline_decode(w)
+    print(json.dumps(out), flush=True)
+
+
 def run_pmc_step(args):
     """Calibration copy of known size, then one fa_fwd + fa_bwd step (no timing)."""
     import torch
     import workloads as W
-    w = W.WORKLOADS[args.workload]
+    w = W.WORKLOADS.get(args.workload)
     n = CALIB_BYTES // 2
     src = torch.ones(n, dtype=torch.bfloat16, device="cuda")
     dst = torch.empty_like(src)
@@ -205,10 +332,13 @@ def run_pmc_step(args):
     torch.neg(src, out=dst)            # reads CALIB_BYTES, writes CALIB_BYTES
     torch.cuda.synchronize()
     del src, dst
-    b = Bound(w, with_bwd=w.backward)
-    b.fwd()
-    if w.backward:
-        b.bwd()
+    if args.workload in W.DECODE_WORKLOADS:
+        DecodeBound(W.DECODE_WORKLOADS[args.workload]).call()
+    else:
+        b = Bound(w, with_bwd=w.backward)
+        b.fwd()
+        if w.backward:
+            b.bwd()
     torch.cuda.synchronize()
     print("pmc step done", flush=True)
 
@@ -280,8 +410,8 @@ def run_step_bench(args):
 
     for _ in range(args.warmup):
         b.step()
-    # timed region: K steps; an event after every launch gives each kernel's
-    # duration inside the steps, on the stream the kernels run on
+    # K steps with fa_bwd's stages called one by one and an event after every
+    # launch: each kernel's duration inside the steps, on the launch stream
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)]
           for _ in range(args.steps)]
     torch.cuda.synchronize()
@@ -298,7 +428,7 @@ def run_step_bench(args):
     ms = ev[0][0].elapsed_time(ev[-1][-1]) / args.steps
     kern = {n: sum(ev[k][i].elapsed_time(ev[k][i + 1]) for k in range(args.steps)) / args.steps
             for i, n in enumerate(names)}
-    # the same steps through the single fa_bwd entry point, for comparison
+    # the steps through the entry points: fa_fwd, fa_bwd (what `value` reports)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     e0.record()
@@ -327,11 +457,11 @@ def run_step_bench(args):
                 "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBS, 4),
                 "traffic": load_traffic(w.name, dom), "avg_launch_ms": round(kern[dom], 4)}
 
-    value = flop / (ms * 1e-3) / 1e12
+    value = flop / (ms_entry * 1e-3) / 1e12
     out = {
         "metric": "attention TFLOP/s (fwd+bwd training step) and % of MFMA bf16 dense peak",
         "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True,
+        "warmup": args.warmup, "ms_per_step": round(ms_entry, 4), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",
         "config": {"workload": f"{w.name}: fa_fwd + fa_bwd", "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv,
                    "N": w.N, "d": w.d, "causal": w.causal, "seed": w.seed},
@@ -339,7 +469,7 @@ def run_step_bench(args):
         "fwd_tflops": round(w.fwd_flop() / (kern["fwd_kernel"] * 1e-3) / 1e12, 2),
         "bwd_tflops": round(w.bwd_flop() / (bwd_ms * 1e-3) / 1e12, 2),
         "kernel_ms": {k: round(v, 4) for k, v in kern.items()},
-        "ms_per_step_fa_bwd_entry": round(ms_entry, 4),
+        "ms_per_step_staged": round(ms, 4),
         "wall_s_timed": round(wall, 3),
         "roofline": roof,
     }
@@ -384,6 +514,8 @@ def main():
         run_sweep(args)
     elif args.pmc_step:
         run_pmc_step(args)
+    elif args.workload in __import__("workloads").DECODE_WORKLOADS:
+        run_decode_bench(args)
     else:
         run_step_bench(args)
 

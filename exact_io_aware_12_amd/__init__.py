@@ -7,7 +7,8 @@ fallback implementation.
 
 Raw entry points with the C names and arguments (pointers as ints):
     fa_fwd, fa_bwd, fa_bwd_stage, fa_bwd_num_stages, fa_bwd_workspace_size,
-    fa_fwd_kvcache, fa_kvcache_num_splits, fa_fwd_kvcache_workspace_size,
+    fa_fwd_kvcache, fa_fwd_kvcache_stage, fa_fwd_kvcache_num_stages,
+    fa_kvcache_num_splits, fa_fwd_kvcache_workspace_size,
     fa_status_string
 Tensor-level helpers:
     flash_attn_func(q, k, v, causal=False, softmax_scale=None,
@@ -30,7 +31,8 @@ __all__ = ["FA_OK", "FA_ERR_INVALID_ARG", "FA_ERR_UNSUPPORTED", "FA_ERR_HIP", "F
            "FA_FP16", "FA_BF16", "FaError", "lib", "lib_path", "fa_fwd", "fa_bwd",
            "fa_bwd_workspace_size", "fa_status_string", "flash_attn_func",
            "flash_attn_backward", "fa_bwd_stage", "fa_bwd_num_stages", "fa_fwd_kvcache",
-           "fa_kvcache_num_splits", "fa_fwd_kvcache_workspace_size", "flash_attn_with_kvcache"]
+           "fa_kvcache_num_splits", "fa_fwd_kvcache_workspace_size", "flash_attn_with_kvcache",
+           "fa_fwd_kvcache_stage", "fa_fwd_kvcache_num_stages"]
 
 FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_HIP, FA_ERR_WORKSPACE = 0, -1, -2, -3, -4
 FA_FP16, FA_BF16 = 0, 1
@@ -72,6 +74,10 @@ def _load():
     L.fa_bwd_workspace_size.restype = sz
     L.fa_fwd_kvcache.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, i, i, vp, sz, vp]
     L.fa_fwd_kvcache.restype = i
+    L.fa_fwd_kvcache_stage.argtypes = [i] + L.fa_fwd_kvcache.argtypes
+    L.fa_fwd_kvcache_stage.restype = i
+    L.fa_fwd_kvcache_num_stages.argtypes = []
+    L.fa_fwd_kvcache_num_stages.restype = i
     L.fa_kvcache_num_splits.argtypes = [i, i, i, i, i, i]
     L.fa_kvcache_num_splits.restype = i
     L.fa_fwd_kvcache_workspace_size.argtypes = [i, i, i, i, i, i, i]
@@ -113,6 +119,18 @@ def fa_fwd_kvcache(q, k_cache, v_cache, cache_seqlens, o, lse, B, Hq, Hkv, Nq, N
                    num_splits, dtype, workspace, workspace_bytes, stream) -> int:
     return lib.fa_fwd_kvcache(q, k_cache, v_cache, cache_seqlens, o, lse, B, Hq, Hkv, Nq, Nk, d,
                               scale, causal, num_splits, dtype, workspace, workspace_bytes, stream)
+
+
+def fa_fwd_kvcache_stage(stage, q, k_cache, v_cache, cache_seqlens, o, lse, B, Hq, Hkv, Nq, Nk, d,
+                         scale, causal, num_splits, dtype, workspace, workspace_bytes,
+                         stream) -> int:
+    return lib.fa_fwd_kvcache_stage(stage, q, k_cache, v_cache, cache_seqlens, o, lse, B, Hq, Hkv,
+                                    Nq, Nk, d, scale, causal, num_splits, dtype, workspace,
+                                    workspace_bytes, stream)
+
+
+def fa_fwd_kvcache_num_stages() -> int:
+    return lib.fa_fwd_kvcache_num_stages()
 
 
 def fa_kvcache_num_splits(B, Hq, Hkv, Nq, Nk, d) -> int:

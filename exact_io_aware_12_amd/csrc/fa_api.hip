@@ -184,7 +184,9 @@ size_t fa_fwd_kvcache_workspace_size(int B, int Hq, int Hkv, int Nq, int Nk, int
   return (bytes + 255) / 256 * 256;
 }
 
-int fa_fwd_kvcache(const void* q, const void* k_cache, const void* v_cache,
+namespace {
+
+int kvcache_common(int stage, const void* q, const void* k_cache, const void* v_cache,
                    const int32_t* cache_seqlens, void* o, float* lse, int B, int Hq, int Hkv,
                    int Nq, int Nk, int d, float scale, int causal, int num_splits, int dtype,
                    void* workspace, size_t workspace_bytes, hipStream_t stream) {
@@ -223,8 +225,29 @@ int fa_fwd_kvcache(const void* q, const void* k_cache, const void* v_cache,
   a.chunk = std::max(tk, (per + tk - 1) / tk * tk);
   a.scale_log2 = scale * kLog2e;
   if ((int64_t)a.n_rb * sp * Hkv * B >= (int64_t)1 << 31) return FA_ERR_UNSUPPORTED;
-  hipError_t e = fa::launch_decode(a, dtype == FA_BF16, d, causal != 0, stream);
+  hipError_t e = fa::launch_decode(a, dtype == FA_BF16, d, causal != 0, stage, stream);
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+}  // namespace
+
+int fa_fwd_kvcache(const void* q, const void* k_cache, const void* v_cache,
+                   const int32_t* cache_seqlens, void* o, float* lse, int B, int Hq, int Hkv,
+                   int Nq, int Nk, int d, float scale, int causal, int num_splits, int dtype,
+                   void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  return kvcache_common(-1, q, k_cache, v_cache, cache_seqlens, o, lse, B, Hq, Hkv, Nq, Nk, d,
+                        scale, causal, num_splits, dtype, workspace, workspace_bytes, stream);
+}
+
+int fa_fwd_kvcache_num_stages(void) { return fa::decode_num_stages(); }
+
+int fa_fwd_kvcache_stage(int stage, const void* q, const void* k_cache, const void* v_cache,
+                         const int32_t* cache_seqlens, void* o, float* lse, int B, int Hq,
+                         int Hkv, int Nq, int Nk, int d, float scale, int causal, int num_splits,
+                         int dtype, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (stage < 0 || stage >= fa::decode_num_stages()) return FA_ERR_INVALID_ARG;
+  return kvcache_common(stage, q, k_cache, v_cache, cache_seqlens, o, lse, B, Hq, Hkv, Nq, Nk, d,
+                        scale, causal, num_splits, dtype, workspace, workspace_bytes, stream);
 }
 
 const char* fa_status_string(int status) {

@@ -35,6 +35,19 @@ __device__ __forceinline__ void wait_vmem_le() {
   __builtin_amdgcn_s_waitcnt(0x0f70 | (N & 15) | ((N >> 4) << 14));
 }
 
+// Wait until at most min(newer, MAXN) tiles of PER_TILE copies each are outstanding.
+template <int PER_TILE, int MAXN>
+__device__ __forceinline__ void wait_tiles(int newer) {
+  if constexpr (MAXN <= 0) {
+    wait_vmem_le<0>();
+  } else {
+    if (newer >= MAXN)
+      wait_vmem_le<MAXN * PER_TILE>();
+    else
+      wait_tiles<PER_TILE, MAXN - 1>(newer);
+  }
+}
+
 template <typename T, int D, bool CAUSAL>
 __global__ __launch_bounds__(64) void decode_kernel(DecodeArgs a) {
   constexpr int NKB = D / 16;
@@ -81,8 +94,10 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeArgs a) {
       tile_dma<T, kTK, D, 1>(k_lds[t % kStages], kp, kvs, k_begin + t * kTK, k_end, 0, lane);
       tile_dma<T, kTK, D, 1>(v_lds[t % kStages], vp, kvs, k_begin + t * kTK, k_end, 0, lane);
     };
-    issue(0);
-    if (ntiles > 1) issue(1);
+    // tiles 0 .. kStages-2 in flight; tile t+kStages-1 starts once tile t has landed
+#pragma unroll
+    for (int p = 0; p < kStages - 1; ++p)
+      if (p < ntiles) issue(p);
 
     u32x4 qf[NKB];
     {
@@ -94,12 +109,10 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeArgs a) {
     const float c = a.scale_log2;
 
     for (int t = 0; t < ntiles; ++t) {
-      // tile t has landed once only the newer tile's copies are outstanding
-      if (t + 1 < ntiles)
-        wait_vmem_le<2 * PER>();
-      else
-        wait_vmem_le<0>();
-      if (t + 2 < ntiles) issue(t + 2);   // into the stage tile t-1 used (this wave is done with it)
+      // tile t has landed once only the copies of the newer tiles in flight
+      // (at most kStages-2 of them) are outstanding
+      wait_tiles<2 * PER, kStages - 2>(ntiles - 1 - t);
+      if (t + kStages - 1 < ntiles) issue(t + kStages - 1);   // into the stage of tile t-1
       const T* kt = k_lds[t % kStages];
       const T* vt = v_lds[t % kStages];
       const int kbase = k_begin + t * kTK;
@@ -169,26 +182,36 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeArgs a) {
 
 // Merge of the splits for one (entry, query head, query) row per wave:
 // LSE = m + ln Σ_s e^{LSE_s − m}, O = Σ_s e^{LSE_s − LSE}·O_s (m = max_s LSE_s).
+// The lanes load the splits' LSEs in parallel (64 at a time); each split's
+// weight is then broadcast and its partial O rows accumulated, so the loads
+// of different splits are independent of each other.
 template <typename T, int D>
 __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeArgs a) {
   constexpr int PER_LANE = D / 64;
   const int64_t units = (int64_t)a.B * a.Hq * a.Nq;
   const int64_t unit = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
-  if (unit >= units) return;
+  if (unit >= units) return;   // whole waves leave together (unit is wave-uniform)
   float m = -INFINITY;
-  for (int sp = 0; sp < a.splits; ++sp) m = fmaxf(m, a.part_lse[sp * units + unit]);
+  for (int sp = lane; sp < a.splits; sp += 64) m = fmaxf(m, a.part_lse[sp * units + unit]);
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
   float acc[PER_LANE] = {};
   float wsum = 0.f;
   if (m != -INFINITY) {
-    for (int sp = 0; sp < a.splits; ++sp) {
-      const float ls = a.part_lse[sp * units + unit];
-      if (ls == -INFINITY) continue;           // this split saw no key of the row
-      const float w = expf(ls - m);
-      wsum += w;
-      const float* po = a.part_o + (sp * units + unit) * D;
+    for (int base = 0; base < a.splits; base += 64) {
+      const int sp = base + lane;
+      const float ls = sp < a.splits ? a.part_lse[sp * units + unit] : -INFINITY;
+      const float w = ls == -INFINITY ? 0.f : expf(ls - m);   // a split with no key weighs 0
+      const int cnt = min(64, a.splits - base);
+      const float* po = a.part_o + ((int64_t)base * units + unit) * D + PER_LANE * lane;
+#pragma unroll 4
+      for (int j = 0; j < cnt; ++j) {
+        const float wj = __shfl(w, j);
+        wsum += wj;
 #pragma unroll
-      for (int e = 0; e < PER_LANE; ++e) acc[e] = fmaf(w, po[PER_LANE * lane + e], acc[e]);
+        for (int e = 0; e < PER_LANE; ++e) acc[e] = fmaf(wj, po[j * units * D + e], acc[e]);
+      }
     }
   }
   const int qi = (int)(unit % a.Nq);
@@ -206,29 +229,39 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeArgs a) {
 }
 
 template <typename T, int D, bool CAUSAL>
-hipError_t launch(const DecodeArgs& a, hipStream_t s) {
+hipError_t launch(const DecodeArgs& a, int stage, hipStream_t s) {
   (void)hipGetLastError();  // drop an error left pending by earlier, unrelated HIP calls
-  const int64_t g1 = (int64_t)a.n_rb * a.splits * a.Hkv * a.B;
-  hipLaunchKernelGGL((decode_kernel<T, D, CAUSAL>), dim3((unsigned)g1), dim3(64), 0, s, a);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  const int64_t units = (int64_t)a.B * a.Hq * a.Nq;
-  hipLaunchKernelGGL((decode_combine_kernel<T, D>), dim3((unsigned)((units + 3) / 4)), dim3(256),
-                     0, s, a);
-  return hipGetLastError();
+  if (stage < 0 || stage == 0) {
+    const int64_t g1 = (int64_t)a.n_rb * a.splits * a.Hkv * a.B;
+    hipLaunchKernelGGL((decode_kernel<T, D, CAUSAL>), dim3((unsigned)g1), dim3(64), 0, s, a);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (stage < 0 || stage == 1) {
+    const int64_t units = (int64_t)a.B * a.Hq * a.Nq;
+    hipLaunchKernelGGL((decode_combine_kernel<T, D>), dim3((unsigned)((units + 3) / 4)),
+                       dim3(256), 0, s, a);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 }  // namespace
 
 int decode_tile_keys() { return kTK; }
+int decode_num_stages() { return 2; }
 
-hipError_t launch_decode(const DecodeArgs& a, bool bf16_in, int d, bool causal, hipStream_t s) {
+hipError_t launch_decode(const DecodeArgs& a, bool bf16_in, int d, bool causal, int stage,
+                         hipStream_t s) {
   if (bf16_in) {
-    if (d == 64) return causal ? launch<bf16, 64, true>(a, s) : launch<bf16, 64, false>(a, s);
-    return causal ? launch<bf16, 128, true>(a, s) : launch<bf16, 128, false>(a, s);
+    if (d == 64)
+      return causal ? launch<bf16, 64, true>(a, stage, s) : launch<bf16, 64, false>(a, stage, s);
+    return causal ? launch<bf16, 128, true>(a, stage, s) : launch<bf16, 128, false>(a, stage, s);
   }
-  if (d == 64) return causal ? launch<f16, 64, true>(a, s) : launch<f16, 64, false>(a, s);
-  return causal ? launch<f16, 128, true>(a, s) : launch<f16, 128, false>(a, s);
+  if (d == 64)
+    return causal ? launch<f16, 64, true>(a, stage, s) : launch<f16, 64, false>(a, stage, s);
+  return causal ? launch<f16, 128, true>(a, stage, s) : launch<f16, 128, false>(a, stage, s);
 }
 
 }  // namespace fa

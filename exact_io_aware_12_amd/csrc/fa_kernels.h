@@ -66,6 +66,9 @@ int bwd_num_stages();
 hipError_t launch_bwd(const BwdArgs& a, bool bf16_in, int d, bool causal, bool varlen, int stage,
                       hipStream_t s);
 int decode_tile_keys();
-hipError_t launch_decode(const DecodeArgs& a, bool bf16_in, int d, bool causal, hipStream_t s);
+// stage < 0: both stages; 0: per-range partial results; 1: merge into o, lse.
+int decode_num_stages();
+hipError_t launch_decode(const DecodeArgs& a, bool bf16_in, int d, bool causal, int stage,
+                         hipStream_t s);
 
 }  // namespace fa

@@ -147,6 +147,21 @@ int fa_fwd_kvcache(const void* q, const void* k_cache, const void* v_cache,
                    int num_splits, int dtype, void* workspace, size_t workspace_bytes,
                    hipStream_t stream);
 
+/*
+ * fa_fwd_kvcache is two stages on one stream: 0 computes the per-range
+ * partial results into the workspace, 1 merges them into o and lse.
+ * fa_fwd_kvcache_stage enqueues one of them with fa_fwd_kvcache's arguments
+ * and checks (stage 1 reads what stage 0 wrote for the same arguments), so
+ * a caller can time them separately. A stage index outside
+ * [0, fa_fwd_kvcache_num_stages()) is FA_ERR_INVALID_ARG.
+ */
+int fa_fwd_kvcache_num_stages(void);
+int fa_fwd_kvcache_stage(int stage, const void* q, const void* k_cache, const void* v_cache,
+                         const int32_t* cache_seqlens, void* o, float* lse,
+                         int B, int Hq, int Hkv, int Nq, int Nk, int d, float scale, int causal,
+                         int num_splits, int dtype, void* workspace, size_t workspace_bytes,
+                         hipStream_t stream);
+
 /* The key-range count fa_fwd_kvcache uses for num_splits = 0 (>= 1); 0 on bad sizes. */
 int fa_kvcache_num_splits(int B, int Hq, int Hkv, int Nq, int Nk, int d);
 

@@ -22,6 +22,7 @@ def declared_functions():
 def test_header_declares_the_boundary():
     assert declared_functions() == ["fa_bwd", "fa_bwd_num_stages", "fa_bwd_stage",
                                     "fa_bwd_workspace_size", "fa_fwd", "fa_fwd_kvcache",
+                                    "fa_fwd_kvcache_num_stages", "fa_fwd_kvcache_stage",
                                     "fa_fwd_kvcache_workspace_size", "fa_kvcache_num_splits",
                                     "fa_status_string"]
 
@@ -167,3 +168,13 @@ def test_kvcache_splits_and_workspace():
     assert fa.fa_fwd_kvcache_workspace_size(2, 4, 2, 3, 64, 128, 5) == (5 * 2 * 4 * 3 * 129 * 4 + 255) // 256 * 256
     assert fa.fa_fwd_kvcache_workspace_size(16, 32, 8, 1, 8192, 128, 0) == 16 * 16 * 32 * 129 * 4
     assert fa.fa_fwd_kvcache_workspace_size(1, 2, 2, 1, 64, 80, 1) == 0
+
+
+def test_kvcache_stage_index_checked():
+    assert fa.fa_fwd_kvcache_num_stages() == 2
+    for stage in (-1, 2):
+        assert fa.fa_fwd_kvcache_stage(stage, P, P, P, P, P, P, 2, 4, 2, 1, 64, 128, 0.125, 1, 2,
+                                       fa.FA_BF16, P, 1 << 20, None) == fa.FA_ERR_INVALID_ARG
+    # a valid stage still runs the host checks first
+    assert fa.fa_fwd_kvcache_stage(0, P, P, P, P, P, P, 2, 4, 2, 1, 64, 96, 0.125, 1, 2,
+                                   fa.FA_BF16, P, 1 << 20, None) == fa.FA_ERR_UNSUPPORTED
