@@ -14,14 +14,14 @@ constexpr float kLog2e = 1.4426950408889634f;
 // Checks shared by fa_fwd and fa_bwd that need no pointer. Returns FA_OK or
 // the status to report; *noop is set when there is nothing to compute.
 int check_sizes(int B, int Hq, int Hkv, int N, int d, float scale, int causal, int dtype,
-                bool* noop) {
+                bool* noop, int max_d = 128) {
   *noop = false;
   if (dtype != FA_FP16 && dtype != FA_BF16) return FA_ERR_INVALID_ARG;
   if (B < 0 || N < 0 || Hq <= 0 || Hkv <= 0 || d <= 0) return FA_ERR_INVALID_ARG;
   if (Hq % Hkv != 0) return FA_ERR_INVALID_ARG;
   if (causal != 0 && causal != 1) return FA_ERR_INVALID_ARG;
   if (!std::isfinite(scale) || !(scale > 0.f)) return FA_ERR_INVALID_ARG;
-  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+  if (d != 64 && d != 128 && !(d == 256 && max_d >= 256)) return FA_ERR_UNSUPPORTED;
   // token and grid indices are 32-bit inside the kernels
   const int64_t T = (int64_t)B * N;
   if (T >= (int64_t)1 << 31 || T * Hq >= (int64_t)1 << 31) return FA_ERR_UNSUPPORTED;
@@ -40,7 +40,7 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int
            int Hkv, int N, int d, float scale, int causal, const int32_t* cu_seqlens, int dtype,
            hipStream_t stream) {
   bool noop;
-  int st = check_sizes(B, Hq, Hkv, N, d, scale, causal, dtype, &noop);
+  int st = check_sizes(B, Hq, Hkv, N, d, scale, causal, dtype, &noop, 256);
   if (st != FA_OK || noop) return st;
   if (!q || !k || !v || !o || !lse) return FA_ERR_INVALID_ARG;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse))
@@ -148,7 +148,7 @@ int check_kvcache(int B, int Hq, int Hkv, int Nq, int Nk, int d, float scale, in
   if (Hq % Hkv != 0) return FA_ERR_INVALID_ARG;
   if (causal != 0 && causal != 1) return FA_ERR_INVALID_ARG;
   if (!std::isfinite(scale) || !(scale > 0.f)) return FA_ERR_INVALID_ARG;
-  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+  if (d != 64 && d != 128 && d != 256) return FA_ERR_UNSUPPORTED;
   // cache and row indices are formed in 64 bits, grid and query counts in 32
   if ((int64_t)B * Nq * Hq >= (int64_t)1 << 31 || (int64_t)Nk * Hkv * d >= (int64_t)1 << 31)
     return FA_ERR_UNSUPPORTED;

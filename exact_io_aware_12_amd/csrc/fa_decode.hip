@@ -219,10 +219,16 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeArgs a) {
   const int h = (int)(bh % a.Hq), b = (int)(bh / a.Hq);
   T* op = static_cast<T*>(a.o) + (((int64_t)b * a.Nq + qi) * a.Hq + h) * D;
   const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
-  if constexpr (PER_LANE == 2)
+  if constexpr (PER_LANE == 4) {
+    u32x2 w;
+    w[0] = pack2<T>(acc[0] * inv, acc[1] * inv);
+    w[1] = pack2<T>(acc[2] * inv, acc[3] * inv);
+    *reinterpret_cast<u32x2*>(op + 4 * lane) = w;
+  } else if constexpr (PER_LANE == 2) {
     *reinterpret_cast<uint32_t*>(op + 2 * lane) = pack2<T>(acc[0] * inv, acc[1] * inv);
-  else
+  } else {
     op[lane] = static_cast<T>(acc[0] * inv);
+  }
   if (lane == 0)
     a.lse[(int64_t)h * a.B * a.Nq + (int64_t)b * a.Nq + qi] =
         wsum > 0.f ? m + logf(wsum) : -INFINITY;
@@ -257,11 +263,15 @@ hipError_t launch_decode(const DecodeArgs& a, bool bf16_in, int d, bool causal, 
   if (bf16_in) {
     if (d == 64)
       return causal ? launch<bf16, 64, true>(a, stage, s) : launch<bf16, 64, false>(a, stage, s);
-    return causal ? launch<bf16, 128, true>(a, stage, s) : launch<bf16, 128, false>(a, stage, s);
+    if (d == 128)
+      return causal ? launch<bf16, 128, true>(a, stage, s) : launch<bf16, 128, false>(a, stage, s);
+    return causal ? launch<bf16, 256, true>(a, stage, s) : launch<bf16, 256, false>(a, stage, s);
   }
   if (d == 64)
     return causal ? launch<f16, 64, true>(a, stage, s) : launch<f16, 64, false>(a, stage, s);
-  return causal ? launch<f16, 128, true>(a, stage, s) : launch<f16, 128, false>(a, stage, s);
+  if (d == 128)
+    return causal ? launch<f16, 128, true>(a, stage, s) : launch<f16, 128, false>(a, stage, s);
+  return causal ? launch<f16, 256, true>(a, stage, s) : launch<f16, 256, false>(a, stage, s);
 }
 
 }  // namespace fa

@@ -176,9 +176,12 @@ __device__ __forceinline__ void tile_to_lds_t(T* lds_t, T* lds, const T* src, in
 // The permutation makes both read patterns below bank-conflict free (64
 // banks x 4 bytes): 16 lanes reading one chunk of 16 consecutive rows, and
 // 32 lanes reading 4 consecutive rows x 32 columns with the transposing read.
+// Rows of 256 and 512 bytes (d = 128, 256) start on the same bank, so the
+// bank of a chunk depends only on its index mod 16 and one 4-bit
+// permutation serves both; 128-byte rows (d = 64) need their own.
 template <int D>
 __device__ __forceinline__ constexpr int swz(int r) {
-  return D == 128 ? (((r & 3) << 2) | ((r >> 2) & 3)) : ((((r >> 1) & 1) << 2) | ((r >> 2) & 3));
+  return D >= 128 ? (((r & 3) << 2) | ((r >> 2) & 3)) : ((((r >> 1) & 1) << 2) | ((r >> 2) & 3));
 }
 
 // Stage rows r0 .. r0+R-1 (row stride `rstride` elements) of a D-column tile.

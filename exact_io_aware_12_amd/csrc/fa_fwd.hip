@@ -103,7 +103,9 @@ __device__ __forceinline__ void fwd_tile(const T* kt, const T* vt, const u32x4 (
 }
 
 template <typename T, int D, bool CAUSAL, bool VARLEN>
-__global__ __launch_bounds__(kThreads, 2) void fwd_kernel(FwdArgs a) {
+// two workgroups per CU up to d = 128; at d = 256 the O accumulators alone
+// take 128 registers and the kernel runs one workgroup per CU
+__global__ __launch_bounds__(kThreads, D <= 128 ? 2 : 1) void fwd_kernel(FwdArgs a) {
   constexpr int NKB = D / 16;    // k steps of K·Qᵀ
   constexpr int NCB = D / 32;    // 32-row blocks of Oᵀ
   constexpr int TILE = kBC * D;  // elements per K or V tile
@@ -233,11 +235,14 @@ int fwd_query_tile() { return kBR; }
 
 hipError_t launch_fwd(const FwdArgs& a, bool bf16_in, int d, bool causal, bool varlen,
                       hipStream_t s) {
-  if (bf16_in)
-    return d == 64 ? dispatch_mask<bf16, 64>(a, causal, varlen, s)
-                   : dispatch_mask<bf16, 128>(a, causal, varlen, s);
-  return d == 64 ? dispatch_mask<f16, 64>(a, causal, varlen, s)
-                 : dispatch_mask<f16, 128>(a, causal, varlen, s);
+  if (bf16_in) {
+    if (d == 64) return dispatch_mask<bf16, 64>(a, causal, varlen, s);
+    if (d == 128) return dispatch_mask<bf16, 128>(a, causal, varlen, s);
+    return dispatch_mask<bf16, 256>(a, causal, varlen, s);
+  }
+  if (d == 64) return dispatch_mask<f16, 64>(a, causal, varlen, s);
+  if (d == 128) return dispatch_mask<f16, 128>(a, causal, varlen, s);
+  return dispatch_mask<f16, 256>(a, causal, varlen, s);
 }
 
 }  // namespace fa

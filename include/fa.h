@@ -31,7 +31,11 @@
  *   Hq must be a multiple of Hkv).
  * Causal: key j is visible from query i iff j <= i, positions counted from
  *   the start of the sequence.
- * Supported: dtype FA_FP16 or FA_BF16; d = 64 or 128; scale finite and > 0.
+ * Supported: dtype FA_FP16 or FA_BF16; scale finite and > 0; head dim d = 64,
+ *   128 or 256 for fa_fwd and fa_fwd_kvcache, d = 64 or 128 for fa_bwd (the
+ *   pages' envelope reaches d = 256, Flash Attention 是什麼, adersaytech.com,
+ *   section 硬體與版本需求; the backward keeps dK, dV and dQ accumulators in
+ *   registers, which do not fit at d = 256).
  *
  * Alignment: every tensor pointer must be 16-byte aligned (FA_ERR_INVALID_ARG
  *   otherwise); rows are moved as 16-byte vectors.
@@ -66,7 +70,7 @@ typedef enum {
   FA_OK = 0,
   FA_ERR_INVALID_ARG = -1,  /* null or misaligned pointer, negative size, bad enum,
                                Hq % Hkv != 0, bad scale */
-  FA_ERR_UNSUPPORTED = -2,  /* head dim other than 64 / 128 */
+  FA_ERR_UNSUPPORTED = -2,  /* head dim outside the supported set (see above) */
   FA_ERR_HIP = -3,          /* the HIP runtime refused a launch (e.g. no device) */
   FA_ERR_WORKSPACE = -4     /* workspace missing or smaller than the size function returns */
 } fa_status;
@@ -120,8 +124,9 @@ size_t fa_bwd_workspace_size(int B, int Hq, int Hkv, int N, int d);
 
 /*
  * Decode: attention of Nq new queries per batch entry over a key/value cache
- * (the inference use of the method, Flash Attention 是什麼, adersaytech.com,
- * "適用場景": long contexts at inference time).
+ * (the inference use of the method: long-context inference and inference
+ * tools, Flash Attention 是什麼, adersaytech.com, sections 原理拆解 and
+ * 各推論工具怎麼開).
  *   q       : [B, Nq, Hq, d]   the new queries, `dtype`
  *   k_cache : [B, Nk, Hkv, d]  cache capacity Nk per entry, `dtype`
  *   v_cache : [B, Nk, Hkv, d]

@@ -6,8 +6,9 @@ Per batch entry b the cache holds L_b = cache_seqlens[b] valid positions
 (0 .. L_b−1) of keys and values; the Nq queries of entry b are the newest Nq
 positions of that sequence, so query i sits at position p_i = L_b − Nq + i
 (the decode reading: the new tokens were appended to the cache before
-attention runs; the pages only speak of fast inference with long contexts,
-adersaytech.com, "適用場景", and leave the alignment open).
+attention runs; the pages speak of long-context inference and of inference
+tools that turn the method on, Flash Attention 是什麼, adersaytech.com,
+sections 原理拆解 and 各推論工具怎麼開, and leave the alignment open).
 
 For query head h and its KV head g = ⌊h / (Hq/Hkv)⌋ the scores, softmax and
 output are those of plain attention (FlashAttention guide, cxbdf.cn, part 1):

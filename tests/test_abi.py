@@ -79,7 +79,7 @@ def bwd(**kw):
     (dict(lse=None), fa.FA_ERR_INVALID_ARG),
     (dict(k=P + 8), fa.FA_ERR_INVALID_ARG),      # not 16-byte aligned
     (dict(d=96), fa.FA_ERR_UNSUPPORTED),
-    (dict(d=256), fa.FA_ERR_UNSUPPORTED),
+    (dict(d=512), fa.FA_ERR_UNSUPPORTED),
     (dict(B=1 << 16, N=1 << 16), fa.FA_ERR_UNSUPPORTED),
     (dict(B=0), fa.FA_OK),                       # empty batch: no-op
     (dict(N=0, q=None, k=None), fa.FA_OK),       # empty sequence: no-op, pointers unused
@@ -94,6 +94,7 @@ def test_fwd_host_checks(kw, status):
     (dict(dv=None), fa.FA_ERR_INVALID_ARG),
     (dict(do=P + 2), fa.FA_ERR_INVALID_ARG),
     (dict(d=32), fa.FA_ERR_UNSUPPORTED),
+    (dict(d=256), fa.FA_ERR_UNSUPPORTED),        # the backward stops at d = 128
     (dict(ws=None), fa.FA_ERR_WORKSPACE),
     (dict(wsb=64), fa.FA_ERR_WORKSPACE),
     (dict(B=0), fa.FA_OK),
@@ -126,6 +127,8 @@ def test_no_device_reports_hip_error():
     if torch.cuda.is_available():
         pytest.skip("a GPU is present")
     assert fwd() == fa.FA_ERR_HIP
+    assert fwd(d=256) == fa.FA_ERR_HIP          # the forward accepts d = 256
+    assert kvc(d=256) == fa.FA_ERR_HIP
 
 
 def kvc(**kw):
@@ -146,6 +149,7 @@ def kvc(**kw):
     (dict(causal=2), fa.FA_ERR_INVALID_ARG),
     (dict(scale=0.0), fa.FA_ERR_INVALID_ARG),
     (dict(d=96), fa.FA_ERR_UNSUPPORTED),
+    (dict(d=512), fa.FA_ERR_UNSUPPORTED),
     (dict(lens=None), fa.FA_ERR_INVALID_ARG),
     (dict(q=P + 8), fa.FA_ERR_INVALID_ARG),
     (dict(lens=P + 2), fa.FA_ERR_INVALID_ARG),

@@ -83,6 +83,13 @@ def test_small_caches(dtype, d, causal, Nq):
                                   causal=causal, seed=300 + d + Nq, lens=lens))
 
 
+@pytest.mark.parametrize("dtype", ["fp16", "bf16"])
+@pytest.mark.parametrize("causal", [False, True])
+def test_head_dim_256(dtype, causal):
+    compare_whole(W.decode_custom(B=3, Hq=8, Hkv=2, Nq=2, Nk=400, d=256, dtype=dtype,
+                                  causal=causal, seed=47, lens=[400, 93, 0]))
+
+
 @pytest.mark.parametrize("splits", [1, 2, 3, 7, 13])
 def test_explicit_splits(splits):
     """Ranges that end inside a tile, and ranges past every valid key (13 x 32 > 300)."""

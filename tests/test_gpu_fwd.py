@@ -71,6 +71,20 @@ def test_ragged_lengths(dtype, d, causal, N):
 
 @pytest.mark.parametrize("dtype", ["fp16", "bf16"])
 @pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("N", [1, 65, 200])
+def test_head_dim_256(dtype, causal, N):
+    """d = 256, the top of the pages' envelope (forward and decode only)."""
+    compare_whole(W.custom(B=2, Hq=4, Hkv=2, N=N, d=256, dtype=dtype, causal=causal,
+                           seed=500 + N))
+
+
+def test_head_dim_256_varlen():
+    compare_whole(W.custom(B=0, Hq=4, Hkv=1, N=0, d=256, dtype="bf16", causal=True, seed=510,
+                           lens=[300, 0, 129]))
+
+
+@pytest.mark.parametrize("dtype", ["fp16", "bf16"])
+@pytest.mark.parametrize("causal", [False, True])
 def test_gqa(dtype, causal):
     compare_whole(W.custom(B=1, Hq=8, Hkv=2, N=200, d=128, dtype=dtype, causal=causal, seed=7))
 
