@@ -482,7 +482,8 @@ def run_sweep(args):
     import torch
     import workloads as W
     names = ["tiny", "causal_d64"] + [f"sweep_N{N}_{c}" for N in (512, 1024, 2048, 4096, 8192)
-                                      for c in ("full", "causal")] + ["gqa_varlen", "train_16k"]
+                                      for c in ("full", "causal")] + ["gqa_varlen", "train_16k",
+                                                                      "fwd_d256_N4096"]
     for n in names:
         w = W.WORKLOADS[n]
         b = Bound(w, with_bwd=False)

@@ -202,7 +202,7 @@ __global__ __launch_bounds__(kDkvThreads, 1) void dkdv_kernel(BwdArgs a, int n_k
   const int logical = xcd_remap(blockIdx.x, G);
   const int kt = logical % n_ktiles;           // ascending = heaviest first when causal
   const int gb = logical / n_ktiles;
-  const int g = gb % a.Hkv, b = gb / a.Hkv;
+  const int b = gb % a.B, g = gb / a.B;   // sequence fastest: XCD ranges balanced for varlen
   const SeqInfo si = seq_info<VARLEN>(a, b);
   const int k0 = kt * kDkvKeys;
   if (k0 >= si.L) return;
@@ -423,7 +423,7 @@ __global__ __launch_bounds__(kThreads, 2) void dq_kernel(BwdArgs a, int n_qtiles
   const int logical = xcd_remap(blockIdx.x, G);
   const int qt_ord = logical % n_qtiles;
   const int hb = logical / n_qtiles;
-  const int h = hb % a.Hq, b = hb / a.Hq;
+  const int b = hb % a.B, h = hb / a.B;   // sequence fastest: XCD ranges balanced for varlen
   const int qt = CAUSAL ? n_qtiles - 1 - qt_ord : qt_ord;
   const SeqInfo si = seq_info<VARLEN>(a, b);
   const int q0 = qt * kDqQ;

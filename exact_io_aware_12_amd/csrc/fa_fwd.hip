@@ -114,12 +114,15 @@ __global__ __launch_bounds__(kThreads, D <= 128 ? 2 : 1) void fwd_kernel(FwdArgs
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int col = lane & 31, half = lane >> 5;
 
-  // ---- work decomposition: (q tile, head, sequence), heavy tiles first -----
+  // ---- work decomposition: (q tile, sequence, head), heavy tiles first -----
   const int G = gridDim.x;
   const int logical = xcd_remap(blockIdx.x, G);
   const int qt_ord = logical % a.n_qtiles;
+  // sequence index fastest: each XCD's contiguous range holds the same heads
+  // of every sequence (balanced when lengths differ), and the q tiles of one
+  // (sequence, head) stay adjacent so they share K and V in that XCD's L2
   const int hb = logical / a.n_qtiles;
-  const int h = hb % a.Hq, b = hb / a.Hq;
+  const int b = hb % a.B, h = hb / a.B;
   const int qt = CAUSAL ? a.n_qtiles - 1 - qt_ord : qt_ord;
 
   int seq0, L, T_total;

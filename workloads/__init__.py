@@ -112,6 +112,9 @@ def _build() -> Dict[str, Workload]:
                                dtype="bf16", causal=True, seed=4, varlen=True, lens=lens)
     w["train_16k"] = Workload("train_16k", B=2, Hq=16, Hkv=16, N=16384, d=128, dtype="bf16",
                               causal=True, seed=5, backward=True)
+    # head dim 256 (forward only), the sweep's shape with half the heads
+    w["fwd_d256_N4096"] = Workload("fwd_d256_N4096", B=4, Hq=16, Hkv=16, N=4096, d=256,
+                                   dtype="bf16", causal=False, seed=8)
     return w
 
 
