@@ -146,13 +146,15 @@ __device__ __forceinline__ void dkdv_produce(const T* qt_, const T* dot_, const 
                                              float c, int q0, int L, int key, int lane) {
   constexpr int NKB = D / 16;
   const int col = lane & 31, half = lane >> 5;
+  constexpr uint32_t QBLK = 32 * D * sizeof(T);   // 32 rows
 #pragma unroll
   for (int qb = 0; qb < kDkvQ / 32; ++qb) {
     f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) {
-      s = mfma32<T>(lds_row16<T, D>(qt_, qb * 32 + col, 2 * kb + half), kf[kb], s);
-      dp = mfma32<T>(lds_row16<T, D>(dot_, qb * 32 + col, 2 * kb + half), vf[kb], dp);
+      const uint32_t off = row16_off<D>(col, 2 * kb + half) + qb * QBLK;
+      s = mfma32<T>(lds_at16<T>(qt_, off), kf[kb], s);
+      dp = mfma32<T>(lds_at16<T>(dot_, off), vf[kb], dp);
     }
 #pragma unroll
     for (int rr = 0; rr < 4; ++rr) {
@@ -291,10 +293,13 @@ __global__ __launch_bounds__(kDkvThreads, 1) void dkdv_kernel(BwdArgs a, int n_k
     }
   } else {
     f32x16 dkt[NCB], dvt[NCB];
+    uint32_t tro[NCB][2];   // byte offsets of the transposing reads (rows 4h.., 4h+8..)
 #pragma unroll
     for (int cb = 0; cb < NCB; ++cb) {
       dkt[cb] = f32x16{};
       dvt[cb] = f32x16{};
+      tro[cb][0] = tr8_off<D>(4 * half, cb * 32, lane) & kLdsAddrMask;
+      tro[cb][1] = tr8_off<D>(4 * half + 8, cb * 32, lane) & kLdsAddrMask;
     }
     for (int j = -1; j < ntile; ++j) {
       wait_vmem_all();
@@ -318,15 +323,26 @@ __global__ __launch_bounds__(kDkvThreads, 1) void dkdv_kernel(BwdArgs a, int n_k
       }
       __syncthreads();   // B (waits for the P, dS reads above)
       if (active) {
-        const T* qt_ = qd_lds[st][0];
-        const T* dot_ = qd_lds[st][1];
+        // the stage's Q tile; its dO tile follows TILE elements later
+        // LDS addresses stay below 2^18; masking the two terms proves the sum
+        // non-negative, which lets the k-step constants fold into the reads
+        const uint32_t qbase =
+            (lds_addr(qd_lds[0][0]) + st * (2 * TILE * (uint32_t)sizeof(T))) & kLdsAddrMask;
+        constexpr uint32_t KSTEP = 16 * D * sizeof(T);   // 16 rows
+        constexpr uint32_t DO = TILE * sizeof(T);
+        uint32_t aa[NCB], ab[NCB];
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb) {
+          aa[cb] = qbase + tro[cb][0];
+          ab[cb] = qbase + tro[cb][1];
+        }
 #pragma unroll
         for (int kk = 0; kk < kDkvKK; ++kk) {
-          const int kq = kk * 16 + 4 * half;
 #pragma unroll
           for (int cb = 0; cb < NCB; ++cb) {
-            dvt[cb] = mfma32<T>(lds_tr8<T, D>(dot_, kq, kq + 8, cb * 32, lane), pb[kk], dvt[cb]);
-            dkt[cb] = mfma32<T>(lds_tr8<T, D>(qt_, kq, kq + 8, cb * 32, lane), sb[kk], dkt[cb]);
+            const uint32_t oa = aa[cb] + kk * KSTEP, ob = ab[cb] + kk * KSTEP;
+            dvt[cb] = mfma32<T>(lds_read_tr8(oa + DO, ob + DO), pb[kk], dvt[cb]);
+            dkt[cb] = mfma32<T>(lds_read_tr8(oa, ob), sb[kk], dkt[cb]);
           }
         }
         // operand reads run one k-step (2·NCB products) ahead of the products

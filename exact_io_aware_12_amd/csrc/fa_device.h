@@ -288,6 +288,55 @@ __device__ __forceinline__ u32x4 lds_tr8(const T* lds, int k0, int k1, int n0, i
   return u32x4{ua[0], ua[1], ub[0], ub[1]};
 }
 
+// The same two reads with the per-lane byte offsets precomputed. The offsets
+// depend only on the lane and on the row and column blocks mod 16, so a loop
+// computes them once and adds a uniform tile base (and constant k steps)
+// instead of redoing the swizzle arithmetic for every read.
+template <int D>
+__device__ __forceinline__ uint32_t row16_off(int r, int c) {
+  return (uint32_t)(r * D + 8 * (c ^ swz<D>(r))) * 2u;
+}
+template <int D>
+__device__ __forceinline__ uint32_t tr8_off(int k, int n0, int lane) {
+  const int j = lane & 15;
+  const int n = n0 + 16 * ((lane >> 4) & 1) + 4 * (j & 3);
+  const int kr = k + (j >> 2);
+  return (uint32_t)(kr * D + 8 * ((n >> 3) ^ swz<D>(kr)) + (n & 7)) * 2u;
+}
+template <typename T>
+__device__ __forceinline__ u32x4 lds_at16(const T* base, uint32_t off) {
+  return *reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(base) + off);
+}
+template <typename T>
+__device__ __forceinline__ u32x4 lds_tr8_at(const T* base, uint32_t off_a, uint32_t off_b) {
+  typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+  const char* b = reinterpret_cast<const char*>(base);
+  const i16x4 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(b + off_a));
+  const i16x4 y = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(b + off_b));
+  const u32x2 ux = __builtin_bit_cast(u32x2, x), uy = __builtin_bit_cast(u32x2, y);
+  return u32x4{ux[0], ux[1], uy[0], uy[1]};
+}
+
+// LDS byte address of a __shared__ object (32 bits) and reads at such an
+// address: an address of the form (uniform base + per-lane offset) + constant
+// lets the constant go into the instruction's offset field.
+constexpr uint32_t kLdsAddrMask = (1u << 18) - 1;   // every LDS byte address is below this
+
+template <typename P>
+__device__ __forceinline__ uint32_t lds_addr(const P* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)(const char*)p;
+}
+__device__ __forceinline__ u32x4 lds_read16(uint32_t addr) {
+  return *(const __attribute__((address_space(3))) u32x4*)(uintptr_t)addr;
+}
+__device__ __forceinline__ u32x4 lds_read_tr8(uint32_t addr_a, uint32_t addr_b) {
+  typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+  const i16x4 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(uintptr_t)addr_a);
+  const i16x4 y = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(uintptr_t)addr_b);
+  const u32x2 ux = __builtin_bit_cast(u32x2, x), uy = __builtin_bit_cast(u32x2, y);
+  return u32x4{ux[0], ux[1], uy[0], uy[1]};
+}
+
 // Sum of the 8 values of a packed operand (4 dwords of 2 x T), fp32 accumulate.
 template <typename T>
 __device__ __forceinline__ float dot2_sum(u32x4 p, float acc) {
