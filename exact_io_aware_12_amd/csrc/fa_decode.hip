@@ -83,7 +83,7 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeArgs a) {
   f32x16 o[NCB];
 #pragma unroll
   for (int cb = 0; cb < NCB; ++cb) o[cb] = f32x16{};
-  float mc = -INFINITY, l = 0.f;
+  float mc = -INFINITY, l = 0.f, lr = 0.f;   // lr: row sum of P as rounded to T
 
   if (k_begin < k_end) {
     const int64_t kvs = (int64_t)a.Hkv * D;
@@ -137,6 +137,7 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeArgs a) {
         // a row that has seen no key yet keeps mc = −inf and nothing to scale
         const float alpha = mc_new == -INFINITY ? 1.f : fast_exp2(mc - mc_new);
         l *= alpha;
+        lr *= alpha;
 #pragma unroll
         for (int cb = 0; cb < NCB; ++cb) o[cb] *= alpha;
         mc = mc_new;
@@ -146,12 +147,13 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeArgs a) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         s[i] = fast_exp2(fmaf(s[i], c, -mcs));
-        ls[i & 3] += s[i];
+        if constexpr (kLseFromUnrounded<T>) ls[i & 3] += s[i];
       }
-      l += (ls[0] + ls[1]) + (ls[2] + ls[3]);
+      if constexpr (kLseFromUnrounded<T>) l += (ls[0] + ls[1]) + (ls[2] + ls[3]);
 #pragma unroll
       for (int kk = 0; kk < kTK / 16; ++kk) {
         const u32x4 pf = acc_operand<T>(s, kk * 2);
+        lr = dot2_sum<T>(pf, lr);   // the same sum over P as rounded for the MFMAs
         const int k0 = kk * 16 + 4 * half;
 #pragma unroll
         for (int cb = 0; cb < NCB; ++cb)
@@ -161,10 +163,13 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeArgs a) {
   }
 
   // partial result of this split: normalised O and its LSE (−inf, O = 0 if no key)
-  const float l_tot = wave_sum_halves(l);
+  // O is normalised by the sum of the rounded P that the MFMAs consumed;
+  // the LSE as in kLseFromUnrounded
+  const float lr_tot = wave_sum_halves(lr);
+  const float l_tot = kLseFromUnrounded<T> ? wave_sum_halves(l) : lr_tot;
   if (row_ok) {
     const bool any = l_tot > 0.f;
-    const float inv = any ? 1.f / l_tot : 0.f;
+    const float inv = any ? 1.f / lr_tot : 0.f;
 #pragma unroll
     for (int cb = 0; cb < NCB; ++cb)
 #pragma unroll

@@ -360,4 +360,12 @@ __device__ __forceinline__ float dot2_sum(u32x4 p, float acc) {
 
 __device__ __forceinline__ void wait_vmem_all() { __builtin_amdgcn_s_waitcnt(0x0f70); }
 
+// The forward kernels normalise O by the row sum of P as rounded to T for the
+// MFMAs (the rounding of a dominant P then cancels in O). The LSE takes that
+// same sum for fp16, whose rounding (2^-11 relative at most) stays inside the
+// LSE tolerance, but needs its own fp32 sum of the unrounded P for bf16, where
+// one rounding (up to 2^-8) could move a dominated row's LSE by 4e-3.
+template <typename T>
+constexpr bool kLseFromUnrounded = __is_same(T, bf16);
+
 }  // namespace fa

@@ -19,7 +19,9 @@
 //                    is read transposed from the row-major V tile
 // K and V tiles are copied global -> LDS directly and double-buffered: the
 // next tile is in flight while the current one is computed.
-// Epilogue: O = Oᵀ/l rounded to the input type, LSE = (m·c + log2 l)·ln 2.
+// Epilogue: O = Oᵀ/lr rounded to the input type, with lr the row sum of P as
+// rounded for the MFMAs; LSE = (m·c + log2 l)·ln 2, with l the fp32 row sum
+// of the unrounded P for bf16 and lr for fp16.
 #include <type_traits>
 
 #include "fa_device.h"
@@ -40,8 +42,8 @@ constexpr float kRescaleHeadroom = 8.f;  // log2 of the largest P before the max
 // the sequence end and, causally, keys after the query.
 template <typename T, int D, bool CAUSAL, bool EDGE>
 __device__ __forceinline__ void fwd_tile(const T* kt, const T* vt, const u32x4 (&qf)[D / 16],
-                                         f32x16 (&o)[D / 32], float& mc, float& l, float c,
-                                         int kv0, int L, int qrow, int lane) {
+                                         f32x16 (&o)[D / 32], float& mc, float& l, float& lr,
+                                         float c, int kv0, int L, int qrow, int lane) {
   constexpr int NKB = D / 16;
   constexpr int NCB = D / 32;
   const int col = lane & 31, half = lane >> 5;
@@ -76,30 +78,36 @@ __device__ __forceinline__ void fwd_tile(const T* kt, const T* vt, const u32x4 (
     const float mc_new = fmaxf(mc, mxc);     // finite: key 0 is seen in tile 0
     const float alpha = fast_exp2(mc - mc_new);
     l *= alpha;
+    lr *= alpha;
 #pragma unroll
     for (int cb = 0; cb < NCB; ++cb) o[cb] *= alpha;
     mc = mc_new;
   }
-  // row sum in fp32 from the unrounded P: LSE carries no rounding of P
+  // bf16 also sums the unrounded P in fp32 for the LSE (kLseFromUnrounded)
   float ls[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int jb = 0; jb < 2; ++jb)
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       s[jb][i] = fast_exp2(fmaf(s[jb][i], c, -mc));
-      ls[i & 3] += s[jb][i];
+      if constexpr (kLseFromUnrounded<T>) ls[i & 3] += s[jb][i];
     }
-  l += (ls[0] + ls[1]) + (ls[2] + ls[3]);
+  if constexpr (kLseFromUnrounded<T>) l += (ls[0] + ls[1]) + (ls[2] + ls[3]);
 
   // ---- Oᵀ += Vᵀ·Pᵀ ---------------------------------------------------------
+  // lr sums P as rounded to T for the MFMAs; O is normalised by it, so that
+  // the rounding of a dominant P cancels in O instead of scaling it
+  float r[kBC / 16];   // independent partial sums: short dependency chains
 #pragma unroll
   for (int kk = 0; kk < kBC / 16; ++kk) {
     const u32x4 pf = acc_operand<T>(s[kk >> 1], (kk & 1) * 2);
+    r[kk] = dot2_sum<T>(pf, 0.f);
     const int k0 = kk * 16 + 4 * half;
 #pragma unroll
     for (int cb = 0; cb < NCB; ++cb)
       o[cb] = mfma32<T>(lds_tr8<T, D>(vt, k0, k0 + 8, cb * 32, lane), pf, o[cb]);
   }
+  lr += (r[0] + r[1]) + (r[2] + r[3]);
 }
 
 template <typename T, int D, bool CAUSAL, bool VARLEN>
@@ -167,7 +175,8 @@ __global__ __launch_bounds__(kThreads, D <= 128 ? 2 : 1) void fwd_kernel(FwdArgs
   for (int cb = 0; cb < NCB; ++cb) o[cb] = f32x16{};
   const float c = a.scale_log2;
   float mc = -INFINITY;   // reference max of S·c for this row
-  float l = 0.f;          // Σ P over this lane half's keys (fp32)
+  float l = 0.f;          // Σ P over this lane half's keys (fp32), for the LSE (bf16)
+  float lr = 0.f;         // the same sum of P rounded to T, for normalising O
   const int wq_last = q0 + wave * 32 + 31;
 
   // Key tiles [0, j_int) need no masking: all their keys precede every row of
@@ -178,9 +187,13 @@ __global__ __launch_bounds__(kThreads, D <= 128 ? 2 : 1) void fwd_kernel(FwdArgs
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
   // BUF is the LDS buffer of tile j (j & 1), a compile-time constant so that
   // every LDS address is a fixed per-lane offset plus an immediate
-  auto step = [&](auto edge_tag, int j) {
+  // buf_tag fixes the tile's LDS buffer at compile time where it is known
+  // (the unrolled interior pairs), so that every LDS address is a per-lane
+  // register plus an immediate offset
+  auto step = [&](auto edge_tag, auto buf_tag, int j) __attribute__((always_inline)) {
     constexpr bool EDGE = decltype(edge_tag)::value;
-    const int BUF = j & 1;
+    constexpr int FIXED = decltype(buf_tag)::value;   // 0, 1, or -1 for j & 1
+    const int BUF = FIXED >= 0 ? FIXED : (j & 1);
     const int kv0 = j * kBC;
     wait_vmem_all();   // this thread's copies of tile j have landed
     __syncthreads();   // everyone's have, and tile j-1 is no longer read
@@ -195,15 +208,24 @@ __global__ __launch_bounds__(kThreads, D <= 128 ? 2 : 1) void fwd_kernel(FwdArgs
       }
     }
     if (EDGE && CAUSAL && kv0 > wq_last) return;  // every key of the tile is after this wave's rows
-    fwd_tile<T, D, CAUSAL, EDGE>(lds[BUF][0], lds[BUF][1], qf, o, mc, l, c, kv0, L, qrow, lane);
+    fwd_tile<T, D, CAUSAL, EDGE>(lds[BUF][0], lds[BUF][1], qf, o, mc, l, lr, c, kv0, L, qrow, lane);
   };
-  for (int j = 0; j < j_int; ++j) step(std::false_type{}, j);
-  for (int j = j_int; j < ntiles; ++j) step(std::true_type{}, j);
+  using B0 = std::integral_constant<int, 0>;
+  using B1 = std::integral_constant<int, 1>;
+  using BR = std::integral_constant<int, -1>;
+  int j = 0;
+  for (; j + 1 < j_int; j += 2) {   // tile j is in buffer 0, tile j+1 in buffer 1
+    step(std::false_type{}, B0{}, j);
+    step(std::false_type{}, B1{}, j + 1);
+  }
+  if (j < j_int) step(std::false_type{}, BR{}, j++);
+  for (; j < ntiles; ++j) step(std::true_type{}, BR{}, j);
 
   // ---- epilogue -------------------------------------------------------------
-  const float l_tot = wave_sum_halves(l);
+  const float lr_tot = wave_sum_halves(lr);
+  const float l_tot = kLseFromUnrounded<T> ? wave_sum_halves(l) : lr_tot;
   if (qrow < L) {
-    const float inv = 1.f / l_tot;
+    const float inv = 1.f / lr_tot;
     T* op = static_cast<T*>(a.o) + (int64_t)seq0 * qs + (int64_t)h * D + qrow * qs;
 #pragma unroll
     for (int cb = 0; cb < NCB; ++cb)

@@ -97,10 +97,10 @@ def test_varlen_with_empty_and_short(d, causal):
     compare_whole(w)
 
 
-@pytest.mark.parametrize("kind", ["peaked", "offset", "monotone_max"])
-def test_stress_inputs(kind):
-    """Large logits, shifted keys and a running max that grows every tile."""
-    w = W.custom(B=1, Hq=2, Hkv=2, N=700, d=128, dtype="fp16", causal=True, seed=9)
+STRESS = ["peaked", "offset", "monotone_max", "steep_max"]
+
+
+def stress_arrays(w, kind):
     a = W.generate(w)
     if kind == "peaked":
         a["q"] = a["q"] * 4.0
@@ -109,9 +109,52 @@ def test_stress_inputs(kind):
         a["k"] = a["k"] + 8.0 * u
         a["q"] = a["q"] + 0.5 * u     # positive correlation with u: large positive logits
     else:
-        a["k"][:, :, 0] = np.linspace(0, 30, w.T, dtype=np.float32)[:, None]
+        # the running max grows every tile; steeply enough in "steep_max" that
+        # the row max ends ~127 (in log2 units) above that of the first tile
+        top = 30.0 if kind == "monotone_max" else 1000.0
+        a["k"][:, :, 0] = np.linspace(0, top, w.T, dtype=np.float32)[:, None]
         a["q"][:, :, 0] = 1.0
-    compare_whole(w, a)
+    return a
+
+
+@pytest.mark.parametrize("kind", STRESS)
+def test_stress_inputs(kind):
+    """Large logits, shifted keys and a running max that grows every tile."""
+    w = W.custom(B=1, Hq=2, Hkv=2, N=700, d=128, dtype="fp16", causal=True, seed=9)
+    compare_whole(w, stress_arrays(w, kind))
+
+
+# ---- the 256-row kernel for long sequences (d = 128, N >= 2048) --------------
+@pytest.mark.parametrize("dtype", ["fp16", "bf16"])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("N", [2048, 2111, 2367])
+def test_long_ragged(dtype, causal, N):
+    compare_whole(W.custom(B=1, Hq=2, Hkv=1, N=N, d=128, dtype=dtype, causal=causal,
+                           seed=N + (1 if causal else 0)))
+
+
+@pytest.mark.parametrize("dtype", ["fp16", "bf16"])
+@pytest.mark.parametrize("kind", STRESS)
+@pytest.mark.parametrize("causal", [False, True])
+def test_long_stress(dtype, kind, causal):
+    """Stress inputs through the long-sequence kernel; 'steep_max' forces the
+    workgroup to redo its tiles with rescaling (in both fp16 and bf16)."""
+    w = W.custom(B=1, Hq=2, Hkv=2, N=2100, d=128, dtype=dtype, causal=causal, seed=19)
+    compare_whole(w, stress_arrays(w, kind))
+
+
+def test_long_gqa_varlen():
+    w = W.custom(B=0, Hq=8, Hkv=2, N=0, d=128, dtype="bf16", causal=True, seed=20,
+                 lens=[2100, 0, 5, 700, 2048, 1])
+    compare_whole(w)
+
+
+def test_long_deterministic():
+    w = W.custom(B=1, Hq=2, Hkv=2, N=2200, d=128, dtype="fp16", causal=False, seed=21)
+    a = W.generate(w)
+    o1, l1, _ = run_fwd(w, a)
+    o2, l2, _ = run_fwd(w, a)
+    assert bits_equal(o1, o2) and bits_equal(l1, l2)
 
 
 # ---- invariants that hold exactly for this kernel ----------------------------
