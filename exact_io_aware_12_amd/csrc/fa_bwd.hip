@@ -145,16 +145,31 @@ __device__ __forceinline__ void dkdv_produce(const T* qt_, const T* dot_, const 
                                              const u32x4 (&vf)[D / 16], u32x4* xp, u32x4* xs,
                                              float c, int q0, int L, int key, int lane) {
   constexpr int NKB = D / 16;
+  constexpr int NQB = kDkvQ / 32;
   const int col = lane & 31, half = lane >> 5;
   constexpr uint32_t QBLK = 32 * D * sizeof(T);   // 32 rows
+  // Per 32-query block: S and dP by MFMA, with the Q and dO operands read
+  // two k-steps ahead of their MFMAs across the whole tile (so the next
+  // block's first operands are in flight during this block's arithmetic).
+  constexpr int AHEAD = 2, NSTEP = NQB * NKB;
+  u32x4 qa[AHEAD + 1], da[AHEAD + 1];
+  auto fetch = [&](int step) __attribute__((always_inline)) {
+    const int qb = step / NKB, kb = step % NKB;
+    const uint32_t off = row16_off<D>(col, 2 * kb + half) + qb * QBLK;
+    qa[step % (AHEAD + 1)] = lds_at16<T>(qt_, off);
+    da[step % (AHEAD + 1)] = lds_at16<T>(dot_, off);
+  };
 #pragma unroll
-  for (int qb = 0; qb < kDkvQ / 32; ++qb) {
+  for (int st = 0; st < AHEAD; ++st) fetch(st);
+#pragma unroll
+  for (int qb = 0; qb < NQB; ++qb) {
     f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) {
-      const uint32_t off = row16_off<D>(col, 2 * kb + half) + qb * QBLK;
-      s = mfma32<T>(lds_at16<T>(qt_, off), kf[kb], s);
-      dp = mfma32<T>(lds_at16<T>(dot_, off), vf[kb], dp);
+      const int st = qb * NKB + kb;
+      if (st + AHEAD < NSTEP) fetch(st + AHEAD);
+      s = mfma32<T>(qa[st % (AHEAD + 1)], kf[kb], s);
+      dp = mfma32<T>(da[st % (AHEAD + 1)], vf[kb], dp);
     }
 #pragma unroll
     for (int rr = 0; rr < 4; ++rr) {
