@@ -400,6 +400,9 @@ __global__ __launch_bounds__(kDkvThreads, 1) void dkdv_kernel(BwdArgs a, int n_k
 // dQᵀ = Kᵀ·dSᵀ (Kᵀ read transposed from the row-major K tile).
 constexpr int kDqQ = 128;   // queries per workgroup (32 per wave)
 constexpr int kDqK = 64;    // keys per tile
+#ifndef FA_DQ_AHEAD
+#define FA_DQ_AHEAD 1
+#endif
 
 // One 64-key tile for one wave's 32 queries: Sᵀ and dPᵀ, then
 // dSᵀ = P∘(dP − D) with P = exp2(S·c − LSE·log2 e), then dQᵀ += Kᵀ·dSᵀ.
@@ -411,14 +414,26 @@ __device__ __forceinline__ void dq_tile(const T* kt, const T* vt, const u32x4 (&
                                         float lse2, float dl, int kv0, int L, int qrow, int lane) {
   constexpr int NKB = D / 16;
   constexpr int NCB = D / 32;
+  constexpr int NJB = kDqK / 32;
+  constexpr int A = FA_DQ_AHEAD;   // K/V row reads in flight ahead of their MFMAs
   const int col = lane & 31, half = lane >> 5;
+  // the K and V rows of Sᵀ and dPᵀ are read A MFMA steps ahead, and the
+  // next 32-key block's first rows during this block's dQ products
+  u32x4 ka[A + 1], va[A + 1];
+  auto fetch_s = [&](int jb, int kb) __attribute__((always_inline)) {
+    ka[kb % (A + 1)] = lds_row16<T, D>(kt, jb * 32 + col, 2 * kb + half);
+    va[kb % (A + 1)] = lds_row16<T, D>(vt, jb * 32 + col, 2 * kb + half);
+  };
 #pragma unroll
-  for (int jb = 0; jb < kDqK / 32; ++jb) {   // 32-key blocks
+  for (int kb = 0; kb < A; ++kb) fetch_s(0, kb);
+#pragma unroll
+  for (int jb = 0; jb < NJB; ++jb) {   // 32-key blocks
     f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) {
-      s = mfma32<T>(lds_row16<T, D>(kt, jb * 32 + col, 2 * kb + half), qf[kb], s);
-      dp = mfma32<T>(lds_row16<T, D>(vt, jb * 32 + col, 2 * kb + half), df[kb], dp);
+      if (kb + A < NKB) fetch_s(jb, kb + A);
+      s = mfma32<T>(ka[kb % (A + 1)], qf[kb], s);
+      dp = mfma32<T>(va[kb % (A + 1)], df[kb], dp);
     }
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
@@ -428,6 +443,10 @@ __device__ __forceinline__ void dq_tile(const T* kt, const T* vt, const u32x4 (&
         p = (kj < L && !(CAUSAL && kj > qrow)) ? p : 0.f;
       }
       dp[i] = p * (dp[i] - dl);
+    }
+    if (jb + 1 < NJB) {
+#pragma unroll
+      for (int kb = 0; kb < A; ++kb) fetch_s(jb + 1, kb);
     }
 #pragma unroll
     for (int h2 = 0; h2 < 2; ++h2) {
@@ -499,29 +518,41 @@ __global__ __launch_bounds__(kThreads, 2) void dq_kernel(BwdArgs a, int n_qtiles
   const int j_int = CAUSAL ? min((q0 + 1) / kDqK, L / kDqK) : L / kDqK;
   const DmaPlan<T, kDqK, D, kWaves> plan(kvs, wave, lane);
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
-  auto step = [&](auto edge_tag, int j) {
+  // buf_tag fixes the tile's LDS buffer at compile time in the unrolled
+  // interior pairs, so every LDS read is a per-lane register plus an immediate
+  auto step = [&](auto edge_tag, auto buf_tag, int j) __attribute__((always_inline)) {
     constexpr bool EDGE = decltype(edge_tag)::value;
+    constexpr int FIXED = decltype(buf_tag)::value;   // 0, 1, or -1 for j & 1
+    const int BUF = FIXED >= 0 ? FIXED : (j & 1);
     const int kv0 = j * kDqK;
-    const T* kt = lds[j & 1][0];
-    const T* vt = lds[j & 1][1];
+    const T* kt = lds[BUF][0];
+    const T* vt = lds[BUF][1];
     wait_vmem_all();
     __syncthreads();
     if (j + 1 < ntiles) {
       const int n0 = kv0 + kDqK;
       if (n0 + kDqK <= L) {
-        tile_dma_in<T, kDqK, D, kWaves>(lds[(j + 1) & 1][0], kp + (int64_t)n0 * kvs, plan, wave_u);
-        tile_dma_in<T, kDqK, D, kWaves>(lds[(j + 1) & 1][1], vp + (int64_t)n0 * kvs, plan, wave_u);
+        tile_dma_in<T, kDqK, D, kWaves>(lds[BUF ^ 1][0], kp + (int64_t)n0 * kvs, plan, wave_u);
+        tile_dma_in<T, kDqK, D, kWaves>(lds[BUF ^ 1][1], vp + (int64_t)n0 * kvs, plan, wave_u);
       } else {
-        tile_dma<T, kDqK, D, kWaves>(lds[(j + 1) & 1][0], kp, kvs, n0, L, wave, lane);
-        tile_dma<T, kDqK, D, kWaves>(lds[(j + 1) & 1][1], vp, kvs, n0, L, wave, lane);
+        tile_dma<T, kDqK, D, kWaves>(lds[BUF ^ 1][0], kp, kvs, n0, L, wave, lane);
+        tile_dma<T, kDqK, D, kWaves>(lds[BUF ^ 1][1], vp, kvs, n0, L, wave, lane);
       }
     }
     if (EDGE && CAUSAL && kv0 > wq_last) return;   // every key after this wave's queries
     dq_tile<T, D, CAUSAL, EDGE>(kt, vt, qf, df, dqt, c, lse2, dl, kv0, L, qrow, lane);
   };
+  using B0 = std::integral_constant<int, 0>;
+  using B1 = std::integral_constant<int, 1>;
+  using BR = std::integral_constant<int, -1>;
   const int j_mid = min(j_int, ntiles);
-  for (int j = 0; j < j_mid; ++j) step(std::false_type{}, j);
-  for (int j = j_mid; j < ntiles; ++j) step(std::true_type{}, j);
+  int j = 0;
+  for (; j + 1 < j_mid; j += 2) {   // tile j in buffer 0, tile j+1 in buffer 1
+    step(std::false_type{}, B0{}, j);
+    step(std::false_type{}, B1{}, j + 1);
+  }
+  if (j < j_mid) step(std::false_type{}, BR{}, j++);
+  for (; j < ntiles; ++j) step(std::true_type{}, BR{}, j);
 
   if (qrow < L) {
     T* dqp = static_cast<T*>(a.dq) + (int64_t)(si.seq0 + qrow) * qs + (int64_t)h * D;
