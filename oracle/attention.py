@@ -13,6 +13,10 @@ positions local to the sequence (FlashAttention guide, cxbdf.cn, part 1,
 
 Visibility: every key of the same sequence, or keys j ≤ i when causal (the
 causal flag of ``flash_attn_func``, Llama-Factory page, first code sample).
+Optionally a sliding window (wl, wr) keeps only keys i − wl ≤ j ≤ i + wr
+(a negative bound is unbounded): the band mask that the mlqm.cn page,
+section 四 (mask types), names among the masks standard attention allows;
+with causal the two conditions both apply.
 Sequences never see each other (padding-free packing; the mlqm.cn page,
 section 四, lists padding masks among what the method supports).
 The row logsumexp is the ``softmax_lse`` the forward kernel writes out
@@ -63,12 +67,19 @@ def _group(Hq: int, Hkv: int) -> int:
 
 
 def _scores(Qr: np.ndarray, rows: np.ndarray, Ks: np.ndarray, scale: float,
-            causal: bool) -> np.ndarray:
-    """S for the query rows ``rows`` (positions in the sequence) against all keys."""
+            causal: bool, window=None) -> np.ndarray:
+    """S for the query rows ``rows`` (positions in the sequence) against all keys;
+    invisible keys get −inf."""
     S = scale * (Qr @ Ks.T)
+    keys = np.arange(Ks.shape[0])[None, :]
     if causal:
-        keys = np.arange(Ks.shape[0])[None, :]
         S = np.where(keys <= rows[:, None], S, -np.inf)
+    if window is not None:
+        wl, wr = window
+        if wl >= 0:
+            S = np.where(keys >= rows[:, None] - wl, S, -np.inf)
+        if wr >= 0:
+            S = np.where(keys <= rows[:, None] + wr, S, -np.inf)
     return S
 
 
@@ -83,7 +94,7 @@ def _row_blocks(rows: np.ndarray, L: int):
         yield rows[a:a + step]
 
 
-def head_fwd(Qs, Ks, Vs, scale: float, causal: bool, rows=None):
+def head_fwd(Qs, Ks, Vs, scale: float, causal: bool, rows=None, window=None):
     """One (sequence, query head): O [R, d] and LSE [R] for ``rows`` (default all)."""
     Qs, Ks, Vs = _f64(Qs), _f64(Ks), _f64(Vs)
     L = Ks.shape[0]
@@ -92,7 +103,7 @@ def head_fwd(Qs, Ks, Vs, scale: float, causal: bool, rows=None):
     lse = np.empty(len(rows))
     pos = 0
     for blk in _row_blocks(rows, L):
-        S = _scores(Qs[blk], blk, Ks, scale, causal)
+        S = _scores(Qs[blk], blk, Ks, scale, causal, window)
         l = _lse(S)
         P = np.exp(S - l[:, None])
         O[pos:pos + len(blk)] = P @ Vs
@@ -101,7 +112,7 @@ def head_fwd(Qs, Ks, Vs, scale: float, causal: bool, rows=None):
     return O, lse
 
 
-def head_bwd(Qs, Ks, Vs, dOs, scale: float, causal: bool):
+def head_bwd(Qs, Ks, Vs, dOs, scale: float, causal: bool, window=None):
     """One (sequence, query head): dQ, dK, dV [L, d] by the chain rule above."""
     Qs, Ks, Vs, dOs = _f64(Qs), _f64(Ks), _f64(Vs), _f64(dOs)
     L = Qs.shape[0]
@@ -109,7 +120,7 @@ def head_bwd(Qs, Ks, Vs, dOs, scale: float, causal: bool):
     dK = np.zeros_like(Ks)
     dV = np.zeros_like(Vs)
     for blk in _row_blocks(np.arange(L), L):
-        S = _scores(Qs[blk], blk, Ks, scale, causal)
+        S = _scores(Qs[blk], blk, Ks, scale, causal, window)
         P = np.exp(S - _lse(S)[:, None])
         dO = dOs[blk]
         dV += P.T @ dO
@@ -121,14 +132,14 @@ def head_bwd(Qs, Ks, Vs, dOs, scale: float, causal: bool):
     return dQ, dK, dV
 
 
-def attention_probs(Qs, Ks, scale: float, causal: bool) -> np.ndarray:
+def attention_probs(Qs, Ks, scale: float, causal: bool, window=None) -> np.ndarray:
     """The full softmax matrix P [L, L] of one (sequence, head)."""
     Qs, Ks = _f64(Qs), _f64(Ks)
-    S = _scores(Qs, np.arange(Qs.shape[0]), Ks, scale, causal)
+    S = _scores(Qs, np.arange(Qs.shape[0]), Ks, scale, causal, window)
     return np.exp(S - _lse(S)[:, None])
 
 
-def attention_fwd(q, k, v, scale: float, causal: bool = False, cu_seqlens=None):
+def attention_fwd(q, k, v, scale: float, causal: bool = False, cu_seqlens=None, window=None):
     """Whole-tensor forward.
 
     q [T, Hq, d], k/v [T, Hkv, d] (any float type; upcast exactly to float64);
@@ -144,17 +155,18 @@ def attention_fwd(q, k, v, scale: float, causal: bool = False, cu_seqlens=None):
         if b <= a:
             continue
         for h in range(Hq):
-            O, l = head_fwd(q[a:b, h], k[a:b, h // g], v[a:b, h // g], scale, causal)
+            O, l = head_fwd(q[a:b, h], k[a:b, h // g], v[a:b, h // g], scale, causal,
+                            window=window)
             o[a:b, h] = O
             lse[h, a:b] = l
     return o, lse
 
 
 def attention_fwd_rows(q, k, v, scale: float, causal: bool, cu_seqlens, seq: int,
-                       head: int, rows: Sequence[int]):
+                       head: int, rows: Sequence[int], window=None):
     """O and LSE of selected query rows (positions inside sequence ``seq``) of one head."""
     q, k, v = _seq_head_views(q, k, v, cu_seqlens, seq, head)
-    return head_fwd(q, k, v, scale, causal, rows=np.asarray(rows))
+    return head_fwd(q, k, v, scale, causal, rows=np.asarray(rows), window=window)
 
 
 def _seq_head_views(q, k, v, cu_seqlens, seq, head):
@@ -164,7 +176,8 @@ def _seq_head_views(q, k, v, cu_seqlens, seq, head):
     return q[a:b, head], k[a:b, head // g], v[a:b, head // g]
 
 
-def attention_bwd(q, k, v, do, scale: float, causal: bool = False, cu_seqlens=None):
+def attention_bwd(q, k, v, do, scale: float, causal: bool = False, cu_seqlens=None,
+                  window=None):
     """Whole-tensor backward: dq [T, Hq, d], dk/dv [T, Hkv, d] in float64."""
     q, k, v, do = _f64(q), _f64(k), _f64(v), _f64(do)
     T, Hq, d = q.shape
@@ -177,7 +190,7 @@ def attention_bwd(q, k, v, do, scale: float, causal: bool = False, cu_seqlens=No
             continue
         for h in range(Hq):
             dQ, dK, dV = head_bwd(q[a:b, h], k[a:b, h // g], v[a:b, h // g], do[a:b, h],
-                                  scale, causal)
+                                  scale, causal, window)
             dq[a:b, h] = dQ
             dk[a:b, h // g] += dK
             dv[a:b, h // g] += dV
@@ -185,7 +198,8 @@ def attention_bwd(q, k, v, do, scale: float, causal: bool = False, cu_seqlens=No
 
 
 def attention_bwd_sampled(q, k, v, do, scale: float, causal: bool, cu_seqlens,
-                          units: Iterable[Tuple[int, int]]) -> Dict[Tuple[int, int], tuple]:
+                          units: Iterable[Tuple[int, int]],
+                          window=None) -> Dict[Tuple[int, int], tuple]:
     """Backward of selected (sequence, KV head) units only.
 
     Returns {(seq, kv_head): (dq [L, g, d], dk [L, d], dv [L, d])}, where the
@@ -204,7 +218,7 @@ def attention_bwd_sampled(q, k, v, do, scale: float, causal: bool, cu_seqlens,
         dv = np.zeros_like(Vs)
         for r in range(g):
             h = kvh * g + r
-            dQ, dK, dV = head_bwd(q[a:b, h], Ks, Vs, do[a:b, h], scale, causal)
+            dQ, dK, dV = head_bwd(q[a:b, h], Ks, Vs, do[a:b, h], scale, causal, window)
             dq[:, r] = dQ
             dk += dK
             dv += dV

@@ -8,6 +8,9 @@ h/g = head, c = feature); ``seqs`` lists (start, end) token ranges.
 Definition followed: the attention formula of the FlashAttention guide
 (cxbdf.cn, part 1), softmax along each query row, with the causal and
 padding-free visibility rules; the backward is the chain rule of that formula.
+``window`` = (left, right) additionally restricts query i to the keys i − left
+.. i + right (a negative bound is unbounded): the band ("sliding window") mask
+of the mlqm.cn page, section 四.
 """
 from __future__ import annotations
 
@@ -18,11 +21,19 @@ def _dot(a, b):
     return math.fsum(x * y for x, y in zip(a, b))
 
 
-def _visible(i, L, causal):
-    return range(0, i + 1) if causal else range(0, L)
+def _visible(i, L, causal, window=None):
+    lo, hi = 0, L - 1
+    if causal:
+        hi = min(hi, i)
+    if window is not None:
+        if window[0] >= 0:
+            lo = max(lo, i - window[0])
+        if window[1] >= 0:
+            hi = min(hi, i + window[1])
+    return range(lo, hi + 1)
 
 
-def forward(q, k, v, scale, causal, seqs):
+def forward(q, k, v, scale, causal, seqs, window=None):
     Hq, Hkv = len(q[0]), len(k[0])
     grp = Hq // Hkv
     o = [[None] * Hq for _ in q]
@@ -32,7 +43,7 @@ def forward(q, k, v, scale, causal, seqs):
         for h in range(Hq):
             g = h // grp
             for i in range(L):
-                js = list(_visible(i, L, causal))
+                js = list(_visible(i, L, causal, window))
                 s = [scale * _dot(q[a + i][h], k[a + j][g]) for j in js]
                 m = max(s)
                 lsum = math.log(math.fsum(math.exp(x - m) for x in s)) + m
@@ -44,7 +55,7 @@ def forward(q, k, v, scale, causal, seqs):
     return o, lse
 
 
-def backward(q, k, v, do, scale, causal, seqs):
+def backward(q, k, v, do, scale, causal, seqs, window=None):
     Hq, Hkv = len(q[0]), len(k[0])
     grp = Hq // Hkv
     d = len(q[0][0])
@@ -60,7 +71,7 @@ def backward(q, k, v, do, scale, causal, seqs):
             P = [[0.0] * L for _ in range(L)]
             dP = [[0.0] * L for _ in range(L)]
             for i in range(L):
-                js = list(_visible(i, L, causal))
+                js = list(_visible(i, L, causal, window))
                 s = [scale * _dot(q[a + i][h], k[a + j][g]) for j in js]
                 m = max(s)
                 lsum = math.log(math.fsum(math.exp(x - m) for x in s)) + m
