@@ -72,6 +72,13 @@ def _load():
     L.fa_bwd_num_stages.restype = i
     L.fa_bwd_workspace_size.argtypes = [i, i, i, i, i]
     L.fa_bwd_workspace_size.restype = sz
+    L.fa_fwd_window.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, i, i, vp, i, vp]
+    L.fa_fwd_window.restype = i
+    L.fa_bwd_window.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, i, vp, i,
+                                vp, sz, vp]
+    L.fa_bwd_window.restype = i
+    L.fa_bwd_window_stage.argtypes = [i] + L.fa_bwd_window.argtypes
+    L.fa_bwd_window_stage.restype = i
     L.fa_fwd_kvcache.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, i, i, vp, sz, vp]
     L.fa_fwd_kvcache.restype = i
     L.fa_fwd_kvcache_stage.argtypes = [i] + L.fa_fwd_kvcache.argtypes
@@ -105,6 +112,27 @@ def fa_bwd_stage(stage, q, k, v, o, dout, lse, dq, dk, dv, B, Hq, Hkv, N, d, sca
                  cu_seqlens, dtype, workspace, workspace_bytes, stream) -> int:
     return lib.fa_bwd_stage(stage, q, k, v, o, dout, lse, dq, dk, dv, B, Hq, Hkv, N, d, scale,
                             causal, cu_seqlens, dtype, workspace, workspace_bytes, stream)
+
+
+def fa_fwd_window(q, k, v, o, lse, B, Hq, Hkv, N, d, scale, window_left, window_right, cu_seqlens,
+                  dtype, stream) -> int:
+    return lib.fa_fwd_window(q, k, v, o, lse, B, Hq, Hkv, N, d, scale, window_left, window_right,
+                             cu_seqlens, dtype, stream)
+
+
+def fa_bwd_window(q, k, v, o, dout, lse, dq, dk, dv, B, Hq, Hkv, N, d, scale, window_left,
+                  window_right, cu_seqlens, dtype, workspace, workspace_bytes, stream) -> int:
+    return lib.fa_bwd_window(q, k, v, o, dout, lse, dq, dk, dv, B, Hq, Hkv, N, d, scale,
+                             window_left, window_right, cu_seqlens, dtype, workspace,
+                             workspace_bytes, stream)
+
+
+def fa_bwd_window_stage(stage, q, k, v, o, dout, lse, dq, dk, dv, B, Hq, Hkv, N, d, scale,
+                        window_left, window_right, cu_seqlens, dtype, workspace, workspace_bytes,
+                        stream) -> int:
+    return lib.fa_bwd_window_stage(stage, q, k, v, o, dout, lse, dq, dk, dv, B, Hq, Hkv, N, d,
+                                   scale, window_left, window_right, cu_seqlens, dtype, workspace,
+                                   workspace_bytes, stream)
 
 
 def fa_bwd_num_stages() -> int:
@@ -187,9 +215,24 @@ def _stream():
     return torch.cuda.current_stream().cuda_stream
 
 
+def _window(causal, window_size):
+    """(left, right) for the window entry points, or None for the plain mask."""
+    wl, wr = (int(x) for x in window_size)
+    if wl < -1 or wr < -1:
+        raise ValueError(f"window_size bounds must be >= -1, got {window_size}")
+    if (wl, wr) == (-1, -1):
+        return None
+    if causal:
+        wr = 0 if wr < 0 else min(wr, 0)
+    return wl, wr
+
+
 def flash_attn_func(q, k, v, causal=False, softmax_scale=None, cu_seqlens=None, max_seqlen=None,
-                    dropout_p=0.0):
-    """Forward. Returns (o, lse); lse is float32 [Hq, T] (natural log)."""
+                    dropout_p=0.0, window_size=(-1, -1)):
+    """Forward. Returns (o, lse); lse is float32 [Hq, T] (natural log).
+
+    window_size = (left, right): query i sees keys i − left .. i + right of its
+    sequence (−1: unbounded); with causal the right side is 0."""
     import torch
     if dropout_p != 0.0:
         raise NotImplementedError("dropout is not implemented (dropout_p must be 0.0)")
@@ -206,18 +249,24 @@ def flash_attn_func(q, k, v, causal=False, softmax_scale=None, cu_seqlens=None, 
     scale = softmax_scale if softmax_scale is not None else 1.0 / math.sqrt(d)
     o = torch.empty_like(q)
     lse = torch.empty((Hq, T), dtype=torch.float32, device=q.device)
-    st = lib.fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
-                    B, Hq, Hkv, N, d, float(scale), int(bool(causal)),
-                    cu_seqlens.data_ptr() if cu_seqlens is not None else None,
-                    _dtype_code(q), _stream())
+    cu = cu_seqlens.data_ptr() if cu_seqlens is not None else None
+    w = _window(causal, window_size)
+    if w is None:
+        st = lib.fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                        B, Hq, Hkv, N, d, float(scale), int(bool(causal)), cu, _dtype_code(q),
+                        _stream())
+    else:
+        st = lib.fa_fwd_window(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                               lse.data_ptr(), B, Hq, Hkv, N, d, float(scale), w[0], w[1], cu,
+                               _dtype_code(q), _stream())
     if st != FA_OK:
-        raise FaError(st, "fa_fwd")
+        raise FaError(st, "fa_fwd" if w is None else "fa_fwd_window")
     return o, lse
 
 
 def flash_attn_backward(dout, q, k, v, o, lse, causal=False, softmax_scale=None, cu_seqlens=None,
-                        max_seqlen=None, workspace=None):
-    """Backward. Returns (dq, dk, dv) shaped like q, k, v."""
+                        max_seqlen=None, workspace=None, window_size=(-1, -1)):
+    """Backward. Returns (dq, dk, dv) shaped like q, k, v (window_size as in the forward)."""
     import torch
     B, N, T, Hq, Hkv, d = _shape(q, k, cu_seqlens, max_seqlen)
     _check_dev(dout, q, k, v, o, lse)
@@ -228,13 +277,19 @@ def flash_attn_backward(dout, q, k, v, o, lse, causal=False, softmax_scale=None,
     need = fa_bwd_workspace_size(B, Hq, Hkv, N, d)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
-    st = lib.fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(),
-                    lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
-                    B, Hq, Hkv, N, d, float(scale), int(bool(causal)),
-                    cu_seqlens.data_ptr() if cu_seqlens is not None else None,
-                    _dtype_code(q), workspace.data_ptr(), workspace.numel(), _stream())
+    cu = cu_seqlens.data_ptr() if cu_seqlens is not None else None
+    w = _window(causal, window_size)
+    ptrs = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(),
+            lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr())
+    if w is None:
+        st = lib.fa_bwd(*ptrs, B, Hq, Hkv, N, d, float(scale), int(bool(causal)), cu,
+                        _dtype_code(q), workspace.data_ptr(), workspace.numel(), _stream())
+    else:
+        st = lib.fa_bwd_window(*ptrs, B, Hq, Hkv, N, d, float(scale), w[0], w[1], cu,
+                               _dtype_code(q), workspace.data_ptr(), workspace.numel(),
+                               _stream())
     if st != FA_OK:
-        raise FaError(st, "fa_bwd")
+        raise FaError(st, "fa_bwd" if w is None else "fa_bwd_window")
     return dq, dk, dv
 
 

@@ -32,15 +32,30 @@ int check_sizes(int B, int Hq, int Hkv, int N, int d, float scale, int causal, i
 // The kernels move 16-byte vectors; device pointers must be 16-byte aligned.
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-}  // namespace
+// A sliding window (left, right), −1 = unbounded, as a mask mode and bounds
+// clamped to N. Returns FA_OK, or the status to report for a bad pair.
+int window_mode(int left, int right, int N, int* mask, int* wl, int* wr) {
+  if (left < -1 || right < -1) return FA_ERR_INVALID_ARG;
+  *wl = *wr = 0;
+  if (left < 0 && right < 0) {
+    *mask = fa::kMaskNone;
+  } else if (left < 0 && right == 0) {
+    *mask = fa::kMaskCausal;       // the causal kernels, tuned for this band
+  } else {
+    *mask = fa::kMaskWindow;
+    // q0 + 128 + wr must stay inside int: keep N and the bounds below 2^30
+    if (N >= (1 << 30)) return FA_ERR_UNSUPPORTED;
+    *wl = left < 0 ? N : std::min(left, N);
+    *wr = right < 0 ? N : std::min(right, N);
+  }
+  return FA_OK;
+}
 
-extern "C" {
-
-int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq,
-           int Hkv, int N, int d, float scale, int causal, const int32_t* cu_seqlens, int dtype,
-           hipStream_t stream) {
+int fwd_common(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq,
+               int Hkv, int N, int d, float scale, int mask, int wl, int wr,
+               const int32_t* cu_seqlens, int dtype, hipStream_t stream) {
   bool noop;
-  int st = check_sizes(B, Hq, Hkv, N, d, scale, causal, dtype, &noop, 256);
+  int st = check_sizes(B, Hq, Hkv, N, d, scale, 0, dtype, &noop, 256);
   if (st != FA_OK || noop) return st;
   if (!q || !k || !v || !o || !lse) return FA_ERR_INVALID_ARG;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse))
@@ -60,9 +75,33 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int
   const int br = fa::fwd_query_tile();
   a.n_qtiles = (N + br - 1) / br;
   a.scale_log2 = scale * kLog2e;
+  a.wl = wl;
+  a.wr = wr;
   if ((int64_t)a.n_qtiles * Hq * B >= (int64_t)1 << 31) return FA_ERR_UNSUPPORTED;
-  hipError_t e = fa::launch_fwd(a, dtype == FA_BF16, d, causal != 0, cu_seqlens != nullptr, stream);
+  hipError_t e = fa::launch_fwd(a, dtype == FA_BF16, d, mask, cu_seqlens != nullptr, stream);
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq,
+           int Hkv, int N, int d, float scale, int causal, const int32_t* cu_seqlens, int dtype,
+           hipStream_t stream) {
+  if (causal != 0 && causal != 1) return FA_ERR_INVALID_ARG;
+  return fwd_common(q, k, v, o, lse, B, Hq, Hkv, N, d, scale,
+                    causal ? fa::kMaskCausal : fa::kMaskNone, 0, 0, cu_seqlens, dtype, stream);
+}
+
+int fa_fwd_window(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                  int Hq, int Hkv, int N, int d, float scale, int window_left, int window_right,
+                  const int32_t* cu_seqlens, int dtype, hipStream_t stream) {
+  int mask, wl, wr;
+  const int st = window_mode(window_left, window_right, N, &mask, &wl, &wr);
+  if (st != FA_OK) return st;
+  return fwd_common(q, k, v, o, lse, B, Hq, Hkv, N, d, scale, mask, wl, wr, cu_seqlens, dtype,
+                    stream);
 }
 
 size_t fa_bwd_workspace_size(int B, int Hq, int Hkv, int N, int d) {
@@ -78,10 +117,11 @@ namespace {
 
 int bwd_common(int stage, const void* q, const void* k, const void* v, const void* o,
                const void* dout, const float* lse, void* dq, void* dk, void* dv, int B, int Hq,
-               int Hkv, int N, int d, float scale, int causal, const int32_t* cu_seqlens, int dtype,
-               void* workspace, size_t workspace_bytes, hipStream_t stream) {
+               int Hkv, int N, int d, float scale, int mask, int wl, int wr,
+               const int32_t* cu_seqlens, int dtype, void* workspace, size_t workspace_bytes,
+               hipStream_t stream) {
   bool noop;
-  int st = check_sizes(B, Hq, Hkv, N, d, scale, causal, dtype, &noop);
+  int st = check_sizes(B, Hq, Hkv, N, d, scale, 0, dtype, &noop);
   if (st != FA_OK || noop) return st;
   if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv) return FA_ERR_INVALID_ARG;
   const void* ptrs[] = {q, k, v, o, dout, lse, dq, dk, dv, workspace};
@@ -110,7 +150,9 @@ int bwd_common(int stage, const void* q, const void* k, const void* v, const voi
   a.group = Hq / Hkv;
   a.scale = scale;
   a.scale_log2 = scale * kLog2e;
-  hipError_t e = fa::launch_bwd(a, dtype == FA_BF16, d, causal != 0, cu_seqlens != nullptr, stage,
+  a.wl = wl;
+  a.wr = wr;
+  hipError_t e = fa::launch_bwd(a, dtype == FA_BF16, d, mask, cu_seqlens != nullptr, stage,
                                 stream);
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
@@ -121,8 +163,33 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const voi
            const float* lse, void* dq, void* dk, void* dv, int B, int Hq, int Hkv, int N, int d,
            float scale, int causal, const int32_t* cu_seqlens, int dtype, void* workspace,
            size_t workspace_bytes, hipStream_t stream) {
-  return bwd_common(-1, q, k, v, o, dout, lse, dq, dk, dv, B, Hq, Hkv, N, d, scale, causal,
-                    cu_seqlens, dtype, workspace, workspace_bytes, stream);
+  if (causal != 0 && causal != 1) return FA_ERR_INVALID_ARG;
+  return bwd_common(-1, q, k, v, o, dout, lse, dq, dk, dv, B, Hq, Hkv, N, d, scale,
+                    causal ? fa::kMaskCausal : fa::kMaskNone, 0, 0, cu_seqlens, dtype, workspace,
+                    workspace_bytes, stream);
+}
+
+int fa_bwd_window(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                  const float* lse, void* dq, void* dk, void* dv, int B, int Hq, int Hkv, int N,
+                  int d, float scale, int window_left, int window_right,
+                  const int32_t* cu_seqlens, int dtype, void* workspace, size_t workspace_bytes,
+                  hipStream_t stream) {
+  return fa_bwd_window_stage(-1, q, k, v, o, dout, lse, dq, dk, dv, B, Hq, Hkv, N, d, scale,
+                             window_left, window_right, cu_seqlens, dtype, workspace,
+                             workspace_bytes, stream);
+}
+
+int fa_bwd_window_stage(int stage, const void* q, const void* k, const void* v, const void* o,
+                        const void* dout, const float* lse, void* dq, void* dk, void* dv, int B,
+                        int Hq, int Hkv, int N, int d, float scale, int window_left,
+                        int window_right, const int32_t* cu_seqlens, int dtype, void* workspace,
+                        size_t workspace_bytes, hipStream_t stream) {
+  if (stage < -1 || stage >= fa::bwd_num_stages()) return FA_ERR_INVALID_ARG;
+  int mask, wl, wr;
+  const int st = window_mode(window_left, window_right, N, &mask, &wl, &wr);
+  if (st != FA_OK) return st;
+  return bwd_common(stage, q, k, v, o, dout, lse, dq, dk, dv, B, Hq, Hkv, N, d, scale, mask, wl,
+                    wr, cu_seqlens, dtype, workspace, workspace_bytes, stream);
 }
 
 int fa_bwd_num_stages(void) { return fa::bwd_num_stages(); }
@@ -132,8 +199,10 @@ int fa_bwd_stage(int stage, const void* q, const void* k, const void* v, const v
                  int Hkv, int N, int d, float scale, int causal, const int32_t* cu_seqlens,
                  int dtype, void* workspace, size_t workspace_bytes, hipStream_t stream) {
   if (stage < 0 || stage >= fa::bwd_num_stages()) return FA_ERR_INVALID_ARG;
-  return bwd_common(stage, q, k, v, o, dout, lse, dq, dk, dv, B, Hq, Hkv, N, d, scale, causal,
-                    cu_seqlens, dtype, workspace, workspace_bytes, stream);
+  if (causal != 0 && causal != 1) return FA_ERR_INVALID_ARG;
+  return bwd_common(stage, q, k, v, o, dout, lse, dq, dk, dv, B, Hq, Hkv, N, d, scale,
+                    causal ? fa::kMaskCausal : fa::kMaskNone, 0, 0, cu_seqlens, dtype, workspace,
+                    workspace_bytes, stream);
 }
 
 namespace {

@@ -139,11 +139,12 @@ constexpr int kDkvKK = kDkvQ / 16;   // 16-query MFMA k-steps per tile
 // Producer: P and dS of one 64-query tile for 32 keys, written to `xp`
 // (P) and `xs` (dS) as MFMA B operands, [k-step][lane]. EDGE tiles zero P
 // and dS for queries past the end and, causally, for keys after the query.
-template <typename T, int D, bool CAUSAL, bool EDGE>
+template <typename T, int D, bool CAUSAL, bool EDGE, bool WIN>
 __device__ __forceinline__ void dkdv_produce(const T* qt_, const T* dot_, const float* ld,
                                              const u32x4 (&kf)[D / 16],
                                              const u32x4 (&vf)[D / 16], u32x4* xp, u32x4* xs,
-                                             float c, int q0, int L, int key, int lane) {
+                                             float c, int q0, int L, int key, int wl, int wr,
+                                             int lane) {
   constexpr int NKB = D / 16;
   constexpr int NQB = kDkvQ / 32;
   const int col = lane & 31, half = lane >> 5;
@@ -185,7 +186,8 @@ __device__ __forceinline__ void dkdv_produce(const T* qt_, const T* dot_, const 
         float ds = p * (dp[i4] - dlv[t]);
         if constexpr (EDGE) {
           const int q = q0 + qoff + t;
-          const bool keep = q < L && !(CAUSAL && key > q);
+          bool keep = q < L && !(CAUSAL && key > q);
+          if constexpr (WIN) keep = keep && q >= key - wr && q <= key + wl;
           p = keep ? p : 0.f;
           ds = keep ? ds : 0.f;
         }
@@ -201,7 +203,8 @@ __device__ __forceinline__ void dkdv_produce(const T* qt_, const T* dot_, const 
   }
 }
 
-template <typename T, int D, bool CAUSAL, bool VARLEN>
+// WIN: sliding window (see fwd_kernel); CAUSAL is false then
+template <typename T, int D, bool CAUSAL, bool VARLEN, bool WIN>
 __global__ __launch_bounds__(kDkvThreads, 1) void dkdv_kernel(BwdArgs a, int n_ktiles) {
   constexpr int NKB = D / 16;
   constexpr int NCB = D / 32;
@@ -229,25 +232,45 @@ __global__ __launch_bounds__(kDkvThreads, 1) void dkdv_kernel(BwdArgs a, int n_k
   const int key = k0 + pair * 32 + col;
   const int pk_first = k0 + pair * 32;   // first key of this wave pair
 
-  // Query tiles of one head: [qt_begin, qt_end). Edge tiles need masking: the
-  // causal diagonal (queries below k0 + kDkvKeys) and a ragged last tile. The
-  // edge tiles of every head of the group come first, then the interior ones.
-  const int qt_begin = CAUSAL ? k0 / kDkvQ : 0;
-  const int qt_end = (L + kDkvQ - 1) / kDkvQ;
-  const int nq = qt_end - qt_begin;
-  const int nd = CAUSAL ? min(kDkvKeys / kDkvQ, nq) : 0;
-  const int ne = nd + ((L % kDkvQ != 0 && nq > nd) ? 1 : 0);
-  const int ni = nq - ne;
-  const int n_edge = a.group * ne, ntile = a.group * nq;
+  // Query tiles of one head: [qt_lo, qt_hi) hold every query that sees a key
+  // of the block; [qi_lo, qi_hi) need no masking (each of their queries sees
+  // every key of the block). The rest are edge tiles: the causal diagonal or
+  // the window's two ends, and a ragged last tile. The edge tiles of every
+  // head of the group come first, then the interior ones.
+  int qt_lo, qi_lo, qi_hi, qt_hi;
+  const int wl = WIN ? a.wl : 0, wr = WIN ? a.wr : 0;
+  if constexpr (WIN) {
+    qt_lo = max(0, k0 - wr) / kDkvQ;
+    qt_hi = (min(L, k0 + kDkvKeys + wl) + kDkvQ - 1) / kDkvQ;
+    const int first_all = min(k0 + kDkvKeys, L) - 1 - wr;   // first query seeing every key
+    qi_lo = min(max(qt_lo, first_all <= 0 ? 0 : (first_all + kDkvQ - 1) / kDkvQ), qt_hi);
+    const int last_all = k0 + wl - (kDkvQ - 1);   // a tile starting here ends at k0 + wl
+    qi_hi = min(min(last_all < 0 ? 0 : last_all / kDkvQ + 1, L / kDkvQ), qt_hi);
+    if (qi_hi < qi_lo) qi_hi = qi_lo;
+  } else {
+    qt_lo = CAUSAL ? k0 / kDkvQ : 0;
+    qt_hi = (L + kDkvQ - 1) / kDkvQ;
+    const int nd = CAUSAL ? min(kDkvKeys / kDkvQ, qt_hi - qt_lo) : 0;
+    qi_lo = qt_lo + nd;
+    qi_hi = max(qi_lo, qt_hi - ((L % kDkvQ != 0 && qt_hi - qt_lo > nd) ? 1 : 0));
+  }
+  const int ne_lo = qi_lo - qt_lo, ne = ne_lo + (qt_hi - qi_hi), ni = qi_hi - qi_lo;
+  const int n_edge = a.group * ne, ntile = a.group * (qt_hi - qt_lo);
   auto tile_of = [&](int i, int& r) -> int {   // tile i -> (head r, query tile)
     if (i < n_edge) {
       r = i / ne;
       const int e = i - r * ne;
-      return e < nd ? qt_begin + e : qt_end - 1;
+      return e < ne_lo ? qt_lo + e : qi_hi + (e - ne_lo);
     }
     const int j = i - n_edge;
     r = j / ni;
-    return qt_begin + nd + (j - r * ni);
+    return qi_lo + (j - r * ni);
+  };
+  // whether a query tile holds no query that sees any key of this wave pair
+  auto pair_idle = [&](int q0) -> bool {
+    if (CAUSAL && q0 + kDkvQ - 1 < pk_first) return true;
+    if (WIN && (q0 + kDkvQ - 1 < pk_first - wr || q0 > pk_first + 31 + wl)) return true;
+    return false;
   };
   const DmaPlan<T, kDkvQ, D, kDkvWaves> plan(qs, wave, lane);
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
@@ -296,13 +319,13 @@ __global__ __launch_bounds__(kDkvThreads, 1) void dkdv_kernel(BwdArgs a, int n_k
         int r;
         const int q0 = tile_of(t, r) * kDkvQ;
         const int st = t % kDkvStages;
-        if (!(CAUSAL && q0 + kDkvQ - 1 < pk_first)) {   // else: before this pair's keys
+        if (!pair_idle(q0)) {
           if (t < n_edge)
-            dkdv_produce<T, D, CAUSAL, true>(qd_lds[st][0], qd_lds[st][1], ld_lds[st], kf, vf,
-                                             xp, xs, c, q0, L, key, lane);
+            dkdv_produce<T, D, CAUSAL, true, WIN>(qd_lds[st][0], qd_lds[st][1], ld_lds[st], kf,
+                                                  vf, xp, xs, c, q0, L, key, wl, wr, lane);
           else
-            dkdv_produce<T, D, CAUSAL, false>(qd_lds[st][0], qd_lds[st][1], ld_lds[st], kf, vf,
-                                              xp, xs, c, q0, L, key, lane);
+            dkdv_produce<T, D, CAUSAL, false, WIN>(qd_lds[st][0], qd_lds[st][1], ld_lds[st], kf,
+                                                   vf, xp, xs, c, q0, L, key, wl, wr, lane);
         }
       }
     }
@@ -327,7 +350,7 @@ __global__ __launch_bounds__(kDkvThreads, 1) void dkdv_kernel(BwdArgs a, int n_k
         int r;
         const int q0 = tile_of(j, r) * kDkvQ;
         st = j % kDkvStages;
-        active = !(CAUSAL && q0 + kDkvQ - 1 < pk_first);
+        active = !pair_idle(q0);
         if (active) {
 #pragma unroll
           for (int kk = 0; kk < kDkvKK; ++kk) {
@@ -408,10 +431,11 @@ constexpr int kDqK = 64;    // keys per tile
 // dSᵀ = P∘(dP − D) with P = exp2(S·c − LSE·log2 e), then dQᵀ += Kᵀ·dSᵀ.
 // EDGE tiles zero P for keys past the end and, causally, for keys after the
 // query.
-template <typename T, int D, bool CAUSAL, bool EDGE>
+template <typename T, int D, bool CAUSAL, bool EDGE, bool WIN>
 __device__ __forceinline__ void dq_tile(const T* kt, const T* vt, const u32x4 (&qf)[D / 16],
                                         const u32x4 (&df)[D / 16], f32x16 (&dqt)[D / 32], float c,
-                                        float lse2, float dl, int kv0, int L, int qrow, int lane) {
+                                        float lse2, float dl, int kv0, int L, int qrow, int wl,
+                                        int wr, int lane) {
   constexpr int NKB = D / 16;
   constexpr int NCB = D / 32;
   constexpr int NJB = kDqK / 32;
@@ -440,7 +464,9 @@ __device__ __forceinline__ void dq_tile(const T* kt, const T* vt, const u32x4 (&
       float p = fast_exp2(fmaf(s[i], c, -lse2));
       if constexpr (EDGE) {
         const int kj = kv0 + jb * 32 + 8 * (i >> 2) + 4 * half + (i & 3);
-        p = (kj < L && !(CAUSAL && kj > qrow)) ? p : 0.f;
+        bool vis = kj < L && !(CAUSAL && kj > qrow);
+        if constexpr (WIN) vis = vis && kj >= qrow - wl && kj <= qrow + wr;
+        p = vis ? p : 0.f;
       }
       dp[i] = p * (dp[i] - dl);
     }
@@ -459,7 +485,7 @@ __device__ __forceinline__ void dq_tile(const T* kt, const T* vt, const u32x4 (&
   }
 }
 
-template <typename T, int D, bool CAUSAL, bool VARLEN>
+template <typename T, int D, bool CAUSAL, bool VARLEN, bool WIN>
 __global__ __launch_bounds__(kThreads, 2) void dq_kernel(BwdArgs a, int n_qtiles) {
   constexpr int NKB = D / 16;
   constexpr int NCB = D / 32;
@@ -484,10 +510,27 @@ __global__ __launch_bounds__(kThreads, 2) void dq_kernel(BwdArgs a, int n_qtiles
   const int64_t qs = (int64_t)a.Hq * D, kvs = (int64_t)a.Hkv * D;
   const T* kp = static_cast<const T*>(a.k) + (int64_t)si.seq0 * kvs + (int64_t)g * D;
   const T* vp = static_cast<const T*>(a.v) + (int64_t)si.seq0 * kvs + (int64_t)g * D;
-  const int kv_end = CAUSAL ? min(L, q0 + kDqQ) : L;
-  const int ntiles = (kv_end + kDqK - 1) / kDqK;
-  tile_dma<T, kDqK, D, kWaves>(lds[0][0], kp, kvs, 0, L, wave, lane);
-  tile_dma<T, kDqK, D, kWaves>(lds[0][1], vp, kvs, 0, L, wave, lane);
+  // key tiles [j_lo, j_hi) visible to some query; [ja, jb) need no masking
+  // (the same split as in fwd_kernel)
+  int j_lo, ja, jb, j_hi;
+  const int wl = WIN ? a.wl : 0, wr = WIN ? a.wr : 0;
+  if constexpr (WIN) {
+    j_lo = max(0, q0 - wl) / kDqK;
+    j_hi = (min(L, q0 + kDqQ + wr) + kDqK - 1) / kDqK;
+    const int first_all = q0 + kDqQ - 1 - wl;
+    ja = max(j_lo, first_all <= 0 ? 0 : (first_all + kDqK - 1) / kDqK);
+    const int last_all = q0 + wr - (kDqK - 1);
+    jb = min(min(last_all < 0 ? 0 : last_all / kDqK + 1, L / kDqK), j_hi);
+    if (jb < ja) jb = ja;
+  } else {
+    const int kv_end = CAUSAL ? min(L, q0 + kDqQ) : L;
+    j_lo = ja = 0;
+    j_hi = (kv_end + kDqK - 1) / kDqK;
+    jb = min(CAUSAL ? min((q0 + 1) / kDqK, L / kDqK) : L / kDqK, j_hi);
+  }
+  const int ntiles = j_hi;
+  tile_dma<T, kDqK, D, kWaves>(lds[0][0], kp, kvs, j_lo * kDqK, L, wave, lane);
+  tile_dma<T, kDqK, D, kWaves>(lds[0][1], vp, kvs, j_lo * kDqK, L, wave, lane);
 
   const int qrow = q0 + wave * 32 + col;
   u32x4 qf[NKB], df[NKB];
@@ -510,20 +553,15 @@ __global__ __launch_bounds__(kThreads, 2) void dq_kernel(BwdArgs a, int n_qtiles
 #pragma unroll
   for (int cb = 0; cb < NCB; ++cb) dqt[cb] = f32x16{};
   const float c = a.scale_log2;
-  const int wq_last = q0 + wave * 32 + 31;
-
-  // Key tiles [0, j_int) need no masking: all their keys precede every query of
-  // the workgroup (causal) and lie inside the sequence. The rest (the causal
-  // diagonal, a ragged last tile) run in a second loop with masking.
-  const int j_int = CAUSAL ? min((q0 + 1) / kDqK, L / kDqK) : L / kDqK;
+  const int wq_first = q0 + wave * 32, wq_last = wq_first + 31;
   const DmaPlan<T, kDqK, D, kWaves> plan(kvs, wave, lane);
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
   // buf_tag fixes the tile's LDS buffer at compile time in the unrolled
   // interior pairs, so every LDS read is a per-lane register plus an immediate
   auto step = [&](auto edge_tag, auto buf_tag, int j) __attribute__((always_inline)) {
     constexpr bool EDGE = decltype(edge_tag)::value;
-    constexpr int FIXED = decltype(buf_tag)::value;   // 0, 1, or -1 for j & 1
-    const int BUF = FIXED >= 0 ? FIXED : (j & 1);
+    constexpr int FIXED = decltype(buf_tag)::value;   // 0, 1, or -1 for (j − j_lo) & 1
+    const int BUF = FIXED >= 0 ? FIXED : ((j - j_lo) & 1);
     const int kv0 = j * kDqK;
     const T* kt = lds[BUF][0];
     const T* vt = lds[BUF][1];
@@ -540,18 +578,27 @@ __global__ __launch_bounds__(kThreads, 2) void dq_kernel(BwdArgs a, int n_qtiles
       }
     }
     if (EDGE && CAUSAL && kv0 > wq_last) return;   // every key after this wave's queries
-    dq_tile<T, D, CAUSAL, EDGE>(kt, vt, qf, df, dqt, c, lse2, dl, kv0, L, qrow, lane);
+    if (EDGE && WIN && (kv0 > wq_last + wr || kv0 + kDqK - 1 < wq_first - wl))
+      return;   // the tile lies outside the windows of all this wave's queries
+    dq_tile<T, D, CAUSAL, EDGE, WIN>(kt, vt, qf, df, dqt, c, lse2, dl, kv0, L, qrow, wl, wr, lane);
   };
   using B0 = std::integral_constant<int, 0>;
   using B1 = std::integral_constant<int, 1>;
   using BR = std::integral_constant<int, -1>;
-  const int j_mid = min(j_int, ntiles);
-  int j = 0;
-  for (; j + 1 < j_mid; j += 2) {   // tile j in buffer 0, tile j+1 in buffer 1
-    step(std::false_type{}, B0{}, j);
-    step(std::false_type{}, B1{}, j + 1);
+  int j = j_lo;
+  if constexpr (WIN)
+    for (; j < ja; ++j) step(std::true_type{}, BR{}, j);   // the window's left edge tiles
+  // the unrolled pairs need registers that d = 256 and the window variants lack
+  if constexpr (D <= 128 && !WIN) {
+    if (j < jb && ((j - j_lo) & 1)) step(std::false_type{}, BR{}, j++);
+    for (; j + 1 < jb; j += 2) {   // tile j in buffer 0, tile j+1 in buffer 1
+      step(std::false_type{}, B0{}, j);
+      step(std::false_type{}, B1{}, j + 1);
+    }
+    if (j < jb) step(std::false_type{}, BR{}, j++);
+  } else {
+    for (; j < jb; ++j) step(std::false_type{}, BR{}, j);
   }
-  if (j < j_mid) step(std::false_type{}, BR{}, j++);
   for (; j < ntiles; ++j) step(std::true_type{}, BR{}, j);
 
   if (qrow < L) {
@@ -569,7 +616,7 @@ __global__ __launch_bounds__(kThreads, 2) void dq_kernel(BwdArgs a, int n_qtiles
   }
 }
 
-template <typename T, int D, bool CAUSAL, bool VARLEN>
+template <typename T, int D, bool CAUSAL, bool VARLEN, bool WIN>
 hipError_t launch(const BwdArgs& a, int stage, hipStream_t s) {
   (void)hipGetLastError();  // drop an error left pending by earlier, unrelated HIP calls
   if (stage < 0 || stage == 0) {
@@ -582,15 +629,15 @@ hipError_t launch(const BwdArgs& a, int stage, hipStream_t s) {
   }
   if (stage < 0 || stage == 1) {
     const int nkt = (a.N + kDkvKeys - 1) / kDkvKeys;
-    hipLaunchKernelGGL((dkdv_kernel<T, D, CAUSAL, VARLEN>), dim3(nkt * a.Hkv * a.B),
+    hipLaunchKernelGGL((dkdv_kernel<T, D, CAUSAL, VARLEN, WIN>), dim3(nkt * a.Hkv * a.B),
                        dim3(kDkvThreads), 0, s, a, nkt);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   if (stage < 0 || stage == 2) {
     const int nqt = (a.N + kDqQ - 1) / kDqQ;
-    hipLaunchKernelGGL((dq_kernel<T, D, CAUSAL, VARLEN>), dim3(nqt * a.Hq * a.B), dim3(kThreads),
-                       0, s, a, nqt);
+    hipLaunchKernelGGL((dq_kernel<T, D, CAUSAL, VARLEN, WIN>), dim3(nqt * a.Hq * a.B),
+                       dim3(kThreads), 0, s, a, nqt);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -598,23 +645,28 @@ hipError_t launch(const BwdArgs& a, int stage, hipStream_t s) {
 }
 
 template <typename T, int D>
-hipError_t dispatch_mask(const BwdArgs& a, bool causal, bool varlen, int stage, hipStream_t s) {
-  if (causal)
-    return varlen ? launch<T, D, true, true>(a, stage, s) : launch<T, D, true, false>(a, stage, s);
-  return varlen ? launch<T, D, false, true>(a, stage, s) : launch<T, D, false, false>(a, stage, s);
+hipError_t dispatch_mask(const BwdArgs& a, int mask, bool varlen, int stage, hipStream_t s) {
+  if (mask == kMaskWindow)
+    return varlen ? launch<T, D, false, true, true>(a, stage, s)
+                  : launch<T, D, false, false, true>(a, stage, s);
+  if (mask == kMaskCausal)
+    return varlen ? launch<T, D, true, true, false>(a, stage, s)
+                  : launch<T, D, true, false, false>(a, stage, s);
+  return varlen ? launch<T, D, false, true, false>(a, stage, s)
+                : launch<T, D, false, false, false>(a, stage, s);
 }
 
 }  // namespace
 
 int bwd_num_stages() { return 3; }
 
-hipError_t launch_bwd(const BwdArgs& a, bool bf16_in, int d, bool causal, bool varlen, int stage,
+hipError_t launch_bwd(const BwdArgs& a, bool bf16_in, int d, int mask, bool varlen, int stage,
                       hipStream_t s) {
   if (bf16_in)
-    return d == 64 ? dispatch_mask<bf16, 64>(a, causal, varlen, stage, s)
-                   : dispatch_mask<bf16, 128>(a, causal, varlen, stage, s);
-  return d == 64 ? dispatch_mask<f16, 64>(a, causal, varlen, stage, s)
-                 : dispatch_mask<f16, 128>(a, causal, varlen, stage, s);
+    return d == 64 ? dispatch_mask<bf16, 64>(a, mask, varlen, stage, s)
+                   : dispatch_mask<bf16, 128>(a, mask, varlen, stage, s);
+  return d == 64 ? dispatch_mask<f16, 64>(a, mask, varlen, stage, s)
+                 : dispatch_mask<f16, 128>(a, mask, varlen, stage, s);
 }
 
 }  // namespace fa

@@ -40,10 +40,11 @@ constexpr float kRescaleHeadroom = 8.f;  // log2 of the largest P before the max
 // One 64-key tile for one wave's 32 query rows: Sᵀ = K·Qᵀ, online softmax
 // with a lazily raised reference max, Oᵀ += Vᵀ·Pᵀ. EDGE tiles mask keys past
 // the sequence end and, causally, keys after the query.
-template <typename T, int D, bool CAUSAL, bool EDGE>
+template <typename T, int D, bool CAUSAL, bool EDGE, bool WIN>
 __device__ __forceinline__ void fwd_tile(const T* kt, const T* vt, const u32x4 (&qf)[D / 16],
                                          f32x16 (&o)[D / 32], float& mc, float& l, float& lr,
-                                         float c, int kv0, int L, int qrow, int lane) {
+                                         float c, int kv0, int L, int qrow, int wl, int wr,
+                                         int lane) {
   constexpr int NKB = D / 16;
   constexpr int NCB = D / 32;
   const int col = lane & 31, half = lane >> 5;
@@ -63,7 +64,9 @@ __device__ __forceinline__ void fwd_tile(const T* kt, const T* vt, const u32x4 (
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const int key = kv0 + jb * 32 + 8 * (i >> 2) + 4 * half + (i & 3);
-        s[jb][i] = (key < L && !(CAUSAL && key > qrow)) ? s[jb][i] : -INFINITY;
+        bool vis = key < L && !(CAUSAL && key > qrow);
+        if constexpr (WIN) vis = vis && key >= qrow - wl && key <= qrow + wr;
+        s[jb][i] = vis ? s[jb][i] : -INFINITY;
       }
   }
 
@@ -74,9 +77,12 @@ __device__ __forceinline__ void fwd_tile(const T* kt, const T* vt, const u32x4 (
 #pragma unroll
   for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[1][i]);
   const float mxc = wave_max_halves(mx) * c;
+  // a window's edge tile can hold no visible key for a row that has seen none
+  // yet either: such a row keeps mc = −inf, scales nothing and adds P = 0
+  constexpr bool GUARD = WIN && EDGE;
   if (__builtin_amdgcn_ballot_w64(mxc > mc + kRescaleHeadroom) != 0) {   // wave-uniform
-    const float mc_new = fmaxf(mc, mxc);     // finite: key 0 is seen in tile 0
-    const float alpha = fast_exp2(mc - mc_new);
+    const float mc_new = fmaxf(mc, mxc);     // finite without a window: key 0 is in tile 0
+    const float alpha = (GUARD && mc_new == -INFINITY) ? 1.f : fast_exp2(mc - mc_new);
     l *= alpha;
     lr *= alpha;
 #pragma unroll
@@ -89,7 +95,7 @@ __device__ __forceinline__ void fwd_tile(const T* kt, const T* vt, const u32x4 (
   for (int jb = 0; jb < 2; ++jb)
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      s[jb][i] = fast_exp2(fmaf(s[jb][i], c, -mc));
+      s[jb][i] = fast_exp2(fmaf(s[jb][i], c, GUARD && mc == -INFINITY ? 0.f : -mc));
       if constexpr (kLseFromUnrounded<T>) ls[i & 3] += s[jb][i];
     }
   if constexpr (kLseFromUnrounded<T>) l += (ls[0] + ls[1]) + (ls[2] + ls[3]);
@@ -110,7 +116,9 @@ __device__ __forceinline__ void fwd_tile(const T* kt, const T* vt, const u32x4 (
   lr += (r[0] + r[1]) + (r[2] + r[3]);
 }
 
-template <typename T, int D, bool CAUSAL, bool VARLEN>
+// WIN: sliding window, key j visible from query i iff i − a.wl ≤ j ≤ i + a.wr
+// (bounds clamped to N by the caller; CAUSAL is false then)
+template <typename T, int D, bool CAUSAL, bool VARLEN, bool WIN>
 // two workgroups per CU up to d = 128; at d = 256 the O accumulators alone
 // take 128 registers and the kernel runs one workgroup per CU
 __global__ __launch_bounds__(kThreads, D <= 128 ? 2 : 1) void fwd_kernel(FwdArgs a) {
@@ -152,12 +160,32 @@ __global__ __launch_bounds__(kThreads, D <= 128 ? 2 : 1) void fwd_kernel(FwdArgs
   const T* kp = static_cast<const T*>(a.k) + (int64_t)seq0 * kvs + (int64_t)g * D;
   const T* vp = static_cast<const T*>(a.v) + (int64_t)seq0 * kvs + (int64_t)g * D;
 
-  const int kv_end = CAUSAL ? min(L, q0 + kBR) : L;
-  const int ntiles = (kv_end + kBC - 1) / kBC;
+  // Key tiles [j_lo, j_hi) are visible to some row of the workgroup; within
+  // them [ja, jb) need no masking (every key inside the sequence and visible
+  // to every row). The rest (causal diagonal, window edges, a ragged end) run
+  // with masking.
+  int j_lo, ja, jb, j_hi;
+  if constexpr (WIN) {
+    const int k_lo = max(0, q0 - a.wl);
+    const int k_hi = min(L, q0 + kBR + a.wr);   // one past the last visible key
+    j_lo = k_lo / kBC;
+    j_hi = (k_hi + kBC - 1) / kBC;
+    const int first_all = q0 + kBR - 1 - a.wl;  // first key every row sees
+    ja = max(j_lo, first_all <= 0 ? 0 : (first_all + kBC - 1) / kBC);
+    const int last_all = q0 + a.wr - (kBC - 1);   // a tile starting here ends at q0 + wr
+    jb = min(min(last_all < 0 ? 0 : last_all / kBC + 1, L / kBC), j_hi);
+    if (jb < ja) jb = ja;
+  } else {
+    const int kv_end = CAUSAL ? min(L, q0 + kBR) : L;
+    j_lo = ja = 0;
+    j_hi = (kv_end + kBC - 1) / kBC;
+    jb = min(CAUSAL ? min((q0 + 1) / kBC, L / kBC) : L / kBC, j_hi);
+  }
+  const int ntiles = j_hi;
 
   // first tile in flight before anything else
-  tile_dma<T, kBC, D, kWaves>(lds[0][0], kp, kvs, 0, L, wave, lane);
-  tile_dma<T, kBC, D, kWaves>(lds[0][1], vp, kvs, 0, L, wave, lane);
+  tile_dma<T, kBC, D, kWaves>(lds[0][0], kp, kvs, j_lo * kBC, L, wave, lane);
+  tile_dma<T, kBC, D, kWaves>(lds[0][1], vp, kvs, j_lo * kBC, L, wave, lane);
 
   // ---- Q fragments (B operand of Sᵀ = K·Qᵀ), kept in registers -------------
   const int qrow = q0 + wave * 32 + col;
@@ -177,23 +205,18 @@ __global__ __launch_bounds__(kThreads, D <= 128 ? 2 : 1) void fwd_kernel(FwdArgs
   float mc = -INFINITY;   // reference max of S·c for this row
   float l = 0.f;          // Σ P over this lane half's keys (fp32), for the LSE (bf16)
   float lr = 0.f;         // the same sum of P rounded to T, for normalising O
-  const int wq_last = q0 + wave * 32 + 31;
+  const int wq_first = q0 + wave * 32, wq_last = wq_first + 31;
+  const int wl = WIN ? a.wl : 0, wr = WIN ? a.wr : 0;
 
-  // Key tiles [0, j_int) need no masking: all their keys precede every row of
-  // the workgroup (causal) and lie inside the sequence. The others (causal
-  // diagonal, ragged last tile) run in a second loop with masking.
-  const int j_int = min(CAUSAL ? min((q0 + 1) / kBC, L / kBC) : L / kBC, ntiles);
   const DmaPlan<T, kBC, D, kWaves> plan(kvs, wave, lane);
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
-  // BUF is the LDS buffer of tile j (j & 1), a compile-time constant so that
-  // every LDS address is a fixed per-lane offset plus an immediate
-  // buf_tag fixes the tile's LDS buffer at compile time where it is known
+  // tile j sits in LDS buffer (j − j_lo) & 1; buf_tag fixes the tile's LDS buffer at compile time where it is known
   // (the unrolled interior pairs), so that every LDS address is a per-lane
   // register plus an immediate offset
   auto step = [&](auto edge_tag, auto buf_tag, int j) __attribute__((always_inline)) {
     constexpr bool EDGE = decltype(edge_tag)::value;
-    constexpr int FIXED = decltype(buf_tag)::value;   // 0, 1, or -1 for j & 1
-    const int BUF = FIXED >= 0 ? FIXED : (j & 1);
+    constexpr int FIXED = decltype(buf_tag)::value;   // 0, 1, or -1 for (j − j_lo) & 1
+    const int BUF = FIXED >= 0 ? FIXED : ((j - j_lo) & 1);
     const int kv0 = j * kBC;
     wait_vmem_all();   // this thread's copies of tile j have landed
     __syncthreads();   // everyone's have, and tile j-1 is no longer read
@@ -208,17 +231,28 @@ __global__ __launch_bounds__(kThreads, D <= 128 ? 2 : 1) void fwd_kernel(FwdArgs
       }
     }
     if (EDGE && CAUSAL && kv0 > wq_last) return;  // every key of the tile is after this wave's rows
-    fwd_tile<T, D, CAUSAL, EDGE>(lds[BUF][0], lds[BUF][1], qf, o, mc, l, lr, c, kv0, L, qrow, lane);
+    if (EDGE && WIN && (kv0 > wq_last + wr || kv0 + kBC - 1 < wq_first - wl))
+      return;   // the tile lies outside the windows of all this wave's rows
+    fwd_tile<T, D, CAUSAL, EDGE, WIN>(lds[BUF][0], lds[BUF][1], qf, o, mc, l, lr, c, kv0, L, qrow,
+                                      wl, wr, lane);
   };
   using B0 = std::integral_constant<int, 0>;
   using B1 = std::integral_constant<int, 1>;
   using BR = std::integral_constant<int, -1>;
-  int j = 0;
-  for (; j + 1 < j_int; j += 2) {   // tile j is in buffer 0, tile j+1 in buffer 1
-    step(std::false_type{}, B0{}, j);
-    step(std::false_type{}, B1{}, j + 1);
+  int j = j_lo;
+  if constexpr (WIN)
+    for (; j < ja; ++j) step(std::true_type{}, BR{}, j);   // the window's left edge tiles
+  // the unrolled pairs need registers that d = 256 and the window variants lack
+  if constexpr (D <= 128 && !WIN) {
+    if (j < jb && ((j - j_lo) & 1)) step(std::false_type{}, BR{}, j++);
+    for (; j + 1 < jb; j += 2) {   // tile j is in buffer 0, tile j+1 in buffer 1
+      step(std::false_type{}, B0{}, j);
+      step(std::false_type{}, B1{}, j + 1);
+    }
+    if (j < jb) step(std::false_type{}, BR{}, j++);
+  } else {
+    for (; j < jb; ++j) step(std::false_type{}, BR{}, j);
   }
-  if (j < j_int) step(std::false_type{}, BR{}, j++);
   for (; j < ntiles; ++j) step(std::true_type{}, BR{}, j);
 
   // ---- epilogue -------------------------------------------------------------
@@ -240,34 +274,38 @@ __global__ __launch_bounds__(kThreads, D <= 128 ? 2 : 1) void fwd_kernel(FwdArgs
   }
 }
 
-template <typename T, int D, bool CAUSAL, bool VARLEN>
+template <typename T, int D, bool CAUSAL, bool VARLEN, bool WIN>
 hipError_t launch(const FwdArgs& a, hipStream_t stream) {
   const int grid = a.n_qtiles * a.Hq * a.B;
   (void)hipGetLastError();  // drop an error left pending by earlier, unrelated HIP calls
-  hipLaunchKernelGGL((fwd_kernel<T, D, CAUSAL, VARLEN>), dim3(grid), dim3(kThreads), 0, stream, a);
+  hipLaunchKernelGGL((fwd_kernel<T, D, CAUSAL, VARLEN, WIN>), dim3(grid), dim3(kThreads), 0,
+                     stream, a);
   return hipGetLastError();
 }
 
 template <typename T, int D>
-hipError_t dispatch_mask(const FwdArgs& a, bool causal, bool varlen, hipStream_t s) {
-  if (causal) return varlen ? launch<T, D, true, true>(a, s) : launch<T, D, true, false>(a, s);
-  return varlen ? launch<T, D, false, true>(a, s) : launch<T, D, false, false>(a, s);
+hipError_t dispatch_mask(const FwdArgs& a, int mask, bool varlen, hipStream_t s) {
+  if (mask == kMaskWindow)
+    return varlen ? launch<T, D, false, true, true>(a, s) : launch<T, D, false, false, true>(a, s);
+  if (mask == kMaskCausal)
+    return varlen ? launch<T, D, true, true, false>(a, s) : launch<T, D, true, false, false>(a, s);
+  return varlen ? launch<T, D, false, true, false>(a, s) : launch<T, D, false, false, false>(a, s);
 }
 
 }  // namespace
 
 int fwd_query_tile() { return kBR; }
 
-hipError_t launch_fwd(const FwdArgs& a, bool bf16_in, int d, bool causal, bool varlen,
+hipError_t launch_fwd(const FwdArgs& a, bool bf16_in, int d, int mask, bool varlen,
                       hipStream_t s) {
   if (bf16_in) {
-    if (d == 64) return dispatch_mask<bf16, 64>(a, causal, varlen, s);
-    if (d == 128) return dispatch_mask<bf16, 128>(a, causal, varlen, s);
-    return dispatch_mask<bf16, 256>(a, causal, varlen, s);
+    if (d == 64) return dispatch_mask<bf16, 64>(a, mask, varlen, s);
+    if (d == 128) return dispatch_mask<bf16, 128>(a, mask, varlen, s);
+    return dispatch_mask<bf16, 256>(a, mask, varlen, s);
   }
-  if (d == 64) return dispatch_mask<f16, 64>(a, causal, varlen, s);
-  if (d == 128) return dispatch_mask<f16, 128>(a, causal, varlen, s);
-  return dispatch_mask<f16, 256>(a, causal, varlen, s);
+  if (d == 64) return dispatch_mask<f16, 64>(a, mask, varlen, s);
+  if (d == 128) return dispatch_mask<f16, 128>(a, mask, varlen, s);
+  return dispatch_mask<f16, 256>(a, mask, varlen, s);
 }
 
 }  // namespace fa

@@ -6,6 +6,10 @@
 
 namespace fa {
 
+// Which keys a query sees (positions local to its sequence): all, keys j ≤ i
+// (causal), or keys i − wl ≤ j ≤ i + wr (sliding window; wl, wr ≤ N).
+constexpr int kMaskNone = 0, kMaskCausal = 1, kMaskWindow = 2;
+
 struct FwdArgs {
   const void* q;
   const void* k;
@@ -17,6 +21,7 @@ struct FwdArgs {
   int group;                  // Hq / Hkv
   int n_qtiles;               // ceil(N / query tile)
   float scale_log2;           // scale · log2(e)
+  int wl, wr;                 // window bounds (kMaskWindow only)
 };
 
 struct BwdArgs {
@@ -37,6 +42,7 @@ struct BwdArgs {
   int group;
   float scale;
   float scale_log2;
+  int wl, wr;                 // window bounds (kMaskWindow only)
 };
 
 struct DecodeArgs {
@@ -58,12 +64,12 @@ struct DecodeArgs {
 };
 
 int fwd_query_tile();
-hipError_t launch_fwd(const FwdArgs& a, bool bf16_in, int d, bool causal, bool varlen,
+hipError_t launch_fwd(const FwdArgs& a, bool bf16_in, int d, int mask, bool varlen,
                       hipStream_t s);
 // stage < 0: every stage in order; otherwise only stage 0 (D = rowsum(dO∘O)),
 // 1 (dK, dV) or 2 (dQ).
 int bwd_num_stages();
-hipError_t launch_bwd(const BwdArgs& a, bool bf16_in, int d, bool causal, bool varlen, int stage,
+hipError_t launch_bwd(const BwdArgs& a, bool bf16_in, int d, int mask, bool varlen, int stage,
                       hipStream_t s);
 int decode_tile_keys();
 // stage < 0: both stages; 0: per-range partial results; 1: merge into o, lse.

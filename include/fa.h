@@ -123,6 +123,39 @@ int fa_bwd_stage(int stage, const void* q, const void* k, const void* v, const v
 size_t fa_bwd_workspace_size(int B, int Hq, int Hkv, int N, int d);
 
 /*
+ * Sliding-window (band) attention: the forward and backward above with the
+ * causal flag replaced by a window. Query i of a sequence sees the keys
+ * j of the same sequence with i − window_left <= j <= i + window_right
+ * (positions local to the sequence); −1 leaves that side unbounded. This is
+ * the band mask the mlqm.cn evaluation page (Flash Attention 落地评估,
+ * section 四, mask types) lists among the masks of standard attention.
+ *   (−1, −1) is fa_fwd / fa_bwd without a mask, (−1, 0) is causal (both run
+ *   the same kernels as those calls); any other pair runs the window kernels.
+ * Every query sees at least its own position, so no row is empty.
+ * Arguments, layouts, ownership, workspace and errors as for fa_fwd and
+ * fa_bwd; a bound below −1 is FA_ERR_INVALID_ARG, and a window other than the
+ * two pairs above needs N < 2^30 (else FA_ERR_UNSUPPORTED). The backward needs
+ * the lse of fa_fwd_window with the same window. fa_bwd_window_stage runs one
+ * stage (or every stage with stage −1), as fa_bwd_stage does.
+ */
+int fa_fwd_window(const void* q, const void* k, const void* v, void* o, float* lse,
+                  int B, int Hq, int Hkv, int N, int d, float scale,
+                  int window_left, int window_right,
+                  const int32_t* cu_seqlens, int dtype, hipStream_t stream);
+int fa_bwd_window(const void* q, const void* k, const void* v, const void* o,
+                  const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                  int B, int Hq, int Hkv, int N, int d, float scale,
+                  int window_left, int window_right,
+                  const int32_t* cu_seqlens, int dtype,
+                  void* workspace, size_t workspace_bytes, hipStream_t stream);
+int fa_bwd_window_stage(int stage, const void* q, const void* k, const void* v, const void* o,
+                        const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                        int B, int Hq, int Hkv, int N, int d, float scale,
+                        int window_left, int window_right,
+                        const int32_t* cu_seqlens, int dtype,
+                        void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
  * Decode: attention of Nq new queries per batch entry over a key/value cache
  * (the inference use of the method: long-context inference and inference
  * tools, Flash Attention 是什麼, adersaytech.com, sections 原理拆解 and

@@ -21,10 +21,11 @@ def declared_functions():
 
 def test_header_declares_the_boundary():
     assert declared_functions() == ["fa_bwd", "fa_bwd_num_stages", "fa_bwd_stage",
+                                    "fa_bwd_window", "fa_bwd_window_stage",
                                     "fa_bwd_workspace_size", "fa_fwd", "fa_fwd_kvcache",
                                     "fa_fwd_kvcache_num_stages", "fa_fwd_kvcache_stage",
-                                    "fa_fwd_kvcache_workspace_size", "fa_kvcache_num_splits",
-                                    "fa_status_string"]
+                                    "fa_fwd_kvcache_workspace_size", "fa_fwd_window",
+                                    "fa_kvcache_num_splits", "fa_status_string"]
 
 
 def test_every_declared_symbol_is_exported():
@@ -182,3 +183,72 @@ def test_kvcache_stage_index_checked():
     # a valid stage still runs the host checks first
     assert fa.fa_fwd_kvcache_stage(0, P, P, P, P, P, P, 2, 4, 2, 1, 64, 96, 0.125, 1, 2,
                                    fa.FA_BF16, P, 1 << 20, None) == fa.FA_ERR_UNSUPPORTED
+
+
+def fwdw(**kw):
+    a = dict(q=P, k=P, v=P, o=P, lse=P, B=1, Hq=2, Hkv=2, N=16, d=64, scale=0.125, wl=3, wr=0,
+             cu=None, dtype=fa.FA_FP16, stream=None)
+    a.update(kw)
+    return fa.fa_fwd_window(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["Hq"], a["Hkv"],
+                            a["N"], a["d"], a["scale"], a["wl"], a["wr"], a["cu"], a["dtype"],
+                            a["stream"])
+
+
+def bwdw(stage=None, **kw):
+    a = dict(B=1, Hq=2, Hkv=2, N=16, d=64, scale=0.125, wl=3, wr=2, dtype=fa.FA_BF16, ws=P,
+             wsb=1 << 20)
+    a.update(kw)
+    ptrs = [kw.get(n, P) for n in ("q", "k", "v", "o", "do", "lse", "dq", "dk", "dv")]
+    args = (*ptrs, a["B"], a["Hq"], a["Hkv"], a["N"], a["d"], a["scale"], a["wl"], a["wr"], None,
+            a["dtype"], a["ws"], a["wsb"], None)
+    if stage is None:
+        return fa.fa_bwd_window(*args)
+    return fa.fa_bwd_window_stage(stage, *args)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(wl=-2), fa.FA_ERR_INVALID_ARG),
+    (dict(wr=-7), fa.FA_ERR_INVALID_ARG),
+    (dict(dtype=3), fa.FA_ERR_INVALID_ARG),
+    (dict(q=None), fa.FA_ERR_INVALID_ARG),
+    (dict(v=P + 4), fa.FA_ERR_INVALID_ARG),
+    (dict(d=96), fa.FA_ERR_UNSUPPORTED),
+    (dict(B=1, Hq=1, Hkv=1, N=1 << 30), fa.FA_ERR_UNSUPPORTED),   # window arithmetic bound
+    # the causal band runs the causal kernels, no window arithmetic: it reaches the launch
+    (dict(B=1, Hq=1, Hkv=1, N=1 << 30, wl=-1, wr=0), None),
+    (dict(B=0), fa.FA_OK),
+])
+def test_fwd_window_host_checks(kw, status):
+    if status is None:
+        torch = pytest.importorskip("torch")
+        if torch.cuda.is_available():
+            pytest.skip("a GPU is present")
+        assert fwdw(**kw) == fa.FA_ERR_HIP
+        return
+    assert fwdw(**kw) == status
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(wl=-3), fa.FA_ERR_INVALID_ARG),
+    (dict(d=256), fa.FA_ERR_UNSUPPORTED),        # the backward stops at d = 128
+    (dict(ws=None), fa.FA_ERR_WORKSPACE),
+    (dict(dk=P + 8), fa.FA_ERR_INVALID_ARG),
+    (dict(B=0), fa.FA_OK),
+])
+def test_bwd_window_host_checks(kw, status):
+    assert bwdw(**kw) == status
+
+
+def test_bwd_window_stage_index_checked():
+    for bad in (-2, 3, 9):
+        assert bwdw(stage=bad) == fa.FA_ERR_INVALID_ARG
+    assert bwdw(stage=1, ws=None) == fa.FA_ERR_WORKSPACE   # a valid stage runs the checks
+
+
+def test_window_no_device_reports_hip_error():
+    torch = pytest.importorskip("torch")
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    assert fwdw() == fa.FA_ERR_HIP
+    assert fwdw(d=256, wl=5, wr=5) == fa.FA_ERR_HIP
+    assert bwdw() == fa.FA_ERR_HIP
