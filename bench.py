@@ -122,11 +122,20 @@ class Bound:
         self.cu_ptr = self.cu.data_ptr() if self.cu is not None else None
         self.stream = torch.cuda.current_stream().cuda_stream
 
+    def _mask(self):
+        """The mask arguments: (causal,) or, for a window workload, (left, right)."""
+        w = self.w
+        if w.window is None:
+            return (int(w.causal),)
+        wl, wr = w.window
+        return (wl, (0 if wr < 0 else min(wr, 0)) if w.causal else wr)
+
     def fwd(self):
         w, t = self.w, self.t
-        st = self.fa.fa_fwd(t["q"].data_ptr(), t["k"].data_ptr(), t["v"].data_ptr(),
-                            self.o.data_ptr(), self.lse.data_ptr(), w.B, w.Hq, w.Hkv, w.N, w.d,
-                            w.scale, int(w.causal), self.cu_ptr, self.code, self.stream)
+        fn = self.fa.fa_fwd if w.window is None else self.fa.fa_fwd_window
+        st = fn(t["q"].data_ptr(), t["k"].data_ptr(), t["v"].data_ptr(), self.o.data_ptr(),
+                self.lse.data_ptr(), w.B, w.Hq, w.Hkv, w.N, w.d, w.scale, *self._mask(),
+                self.cu_ptr, self.code, self.stream)
         if st != self.fa.FA_OK:
             raise self.fa.FaError(st, "fa_fwd")
 
@@ -134,16 +143,20 @@ class Bound:
         w, t = self.w, self.t
         return (t["q"].data_ptr(), t["k"].data_ptr(), t["v"].data_ptr(), self.o.data_ptr(),
                 t["do"].data_ptr(), self.lse.data_ptr(), self.dq.data_ptr(), self.dk.data_ptr(),
-                self.dv.data_ptr(), w.B, w.Hq, w.Hkv, w.N, w.d, w.scale, int(w.causal),
+                self.dv.data_ptr(), w.B, w.Hq, w.Hkv, w.N, w.d, w.scale, *self._mask(),
                 self.cu_ptr, self.code, self.ws.data_ptr(), self.ws.numel(), self.stream)
 
     def bwd(self):
-        st = self.fa.fa_bwd(*self._bwd_args())
+        fn = self.fa.fa_bwd if self.w.window is None else self.fa.fa_bwd_window
+        st = fn(*self._bwd_args())
         if st != self.fa.FA_OK:
             raise self.fa.FaError(st, "fa_bwd")
 
     def bwd_stage(self, stage):
-        st = self.fa.fa_bwd_stage(stage, *self._bwd_args())
+        if self.w.window is None:
+            st = self.fa.fa_bwd_stage(stage, *self._bwd_args())
+        else:
+            st = self.fa.fa_bwd_window_stage(stage, *self._bwd_args())
         if st != self.fa.FA_OK:
             raise self.fa.FaError(st, "fa_bwd_stage")
 
@@ -187,9 +200,9 @@ def cpu_baseline(w, min_seconds=10.0, max_units=4):
     while done < max_units and (done == 0 or dt < min_seconds):
         q, k, v, do = (rng.standard_normal((L, w.d), dtype=np.float32) for _ in range(4))
         t0 = time.perf_counter()
-        O.head_fwd(q, k, v, w.scale, w.causal)
+        O.head_fwd(q, k, v, w.scale, w.causal, window=w.window)
         if w.backward:
-            O.head_bwd(q, k, v, do, w.scale, w.causal)
+            O.head_bwd(q, k, v, do, w.scale, w.causal, window=w.window)
         dt += time.perf_counter() - t0
         done += 1
     return {"value": round(done * flop_unit / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(cores),
@@ -463,8 +476,10 @@ def run_step_bench(args):
         "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms_entry, 4), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",
-        "config": {"workload": f"{w.name}: fa_fwd + fa_bwd", "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv,
-                   "N": w.N, "d": w.d, "causal": w.causal, "seed": w.seed},
+        "config": {"workload": f"{w.name}: fa_fwd + fa_bwd" if w.window is None else
+                   f"{w.name}: fa_fwd_window + fa_bwd_window", "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv,
+                   "N": w.N, "d": w.d, "causal": w.causal, "seed": w.seed,
+                   **({"window": list(w.window)} if w.window is not None else {})},
         "pct_of_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
         "fwd_tflops": round(w.fwd_flop() / (kern["fwd_kernel"] * 1e-3) / 1e12, 2),
         "bwd_tflops": round(w.bwd_flop() / (bwd_ms * 1e-3) / 1e12, 2),
@@ -483,7 +498,8 @@ def run_sweep(args):
     import workloads as W
     names = ["tiny", "causal_d64"] + [f"sweep_N{N}_{c}" for N in (512, 1024, 2048, 4096, 8192)
                                       for c in ("full", "causal")] + ["gqa_varlen", "train_16k",
-                                                                      "fwd_d256_N4096"]
+                                                                      "fwd_d256_N4096",
+                                                                      "window_16k"]
     for n in names:
         w = W.WORKLOADS[n]
         b = Bound(w, with_bwd=False)

@@ -43,6 +43,7 @@ class Workload:
     varlen: bool = False
     backward: bool = False
     lens: Optional[tuple] = None   # varlen sequence lengths
+    window: Optional[tuple] = None  # sliding window (left, right), -1 = unbounded
 
     @property
     def scale(self) -> float:
@@ -62,9 +63,24 @@ class Workload:
         return np.concatenate([[0], np.cumsum(self.seq_lens)]).astype(np.int32)
 
     def fwd_flop(self) -> float:
-        """4·Hq·L²·d per sequence, halved when causal (the metric's convention)."""
-        f = sum(4.0 * self.Hq * L * L * self.d for L in self.seq_lens)
-        return f / 2 if self.causal else f
+        """4·Hq·L²·d per sequence, halved when causal (the metric's convention).
+
+        With a sliding window: 4·Hq·d per visible (query, key) pair, counted
+        exactly (the dense L² has no meaning for a band)."""
+        if self.window is None:
+            f = sum(4.0 * self.Hq * L * L * self.d for L in self.seq_lens)
+            return f / 2 if self.causal else f
+        return 4.0 * self.Hq * self.d * sum(self.visible_pairs(L) for L in self.seq_lens)
+
+    def visible_pairs(self, L: int) -> int:
+        """Number of (query, key) pairs of a length-L sequence inside the window."""
+        wl, wr = self.window
+        if self.causal:
+            wr = 0 if wr < 0 else min(wr, 0)
+        i = np.arange(L, dtype=np.int64)
+        lo = np.maximum(0, i - wl) if wl >= 0 else np.zeros_like(i)
+        hi = np.minimum(L - 1, i + wr) if wr >= 0 else np.full_like(i, L - 1)
+        return int(np.maximum(hi - lo + 1, 0).sum())
 
     def bwd_flop(self) -> float:
         return 2.5 * self.fwd_flop()
@@ -115,6 +131,10 @@ def _build() -> Dict[str, Workload]:
     # head dim 256 (forward only), the sweep's shape with half the heads
     w["fwd_d256_N4096"] = Workload("fwd_d256_N4096", B=4, Hq=16, Hkv=16, N=4096, d=256,
                                    dtype="bf16", causal=False, seed=8)
+    # the training step's shape with a 4096-key sliding window (each query sees
+    # itself and the 4095 keys before it): the band mask, forward and backward
+    w["window_16k"] = Workload("window_16k", B=2, Hq=16, Hkv=16, N=16384, d=128, dtype="bf16",
+                               causal=False, seed=9, backward=True, window=(4095, 0))
     return w
 
 
