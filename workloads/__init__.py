@@ -179,6 +179,30 @@ def generate(w: Workload, with_grad: Optional[bool] = None):
     return out
 
 
+def quantize_e4m3(arrays, names=("q", "k", "v"), v_shift: float = 0.0):
+    """FP8 inputs: each named float32 array as e4m3fn codes plus one descale.
+
+    Recipe: descale = max|x| / 448 (the largest e4m3fn value), codes = x /
+    descale rounded to e4m3fn (nearest even) by torch's float8_e4m3fn cast;
+    ``v_shift`` is added to V first (a non-zero mean makes O far from zero).
+    Returns {name: uint8 codes of the same shape, "descale_<name>": float}.
+    """
+    import torch
+    out = {}
+    for name in names:
+        x = arrays[name].astype(np.float32)
+        if name == "v" and v_shift:
+            x = x + np.float32(v_shift)
+        amax = float(np.abs(x).max()) if x.size else 1.0
+        ds = amax / 448.0 if amax > 0 else 1.0
+        codes = torch.from_numpy(x / np.float32(ds)).to(torch.float8_e4m3fn)
+        out[name] = codes.view(torch.uint8).numpy()
+        out["descale_" + name] = ds
+    if "cu_seqlens" in arrays:
+        out["cu_seqlens"] = arrays["cu_seqlens"]
+    return out
+
+
 def to_torch(arrays, dtype: str, device="cpu"):
     """Round float32 arrays to fp16/bf16 (nearest even) as torch tensors."""
     import torch
