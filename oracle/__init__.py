@@ -27,8 +27,8 @@ from .attention import (attention_fwd, attention_bwd, attention_probs,
                         attention_fwd_rows, attention_bwd_sampled)
 from .decode import kvcache_fwd, kvcache_fwd_units
 from . import bruteforce
-from .fp8 import attention_fwd_fp8, e4m3fn_decode, dequantize, o_bound
+from .fp8 import attention_fwd_fp8, e4m3fn_decode, dequantize, head_o_bound, o_bound
 
 __all__ = ["attention_fwd", "attention_bwd", "attention_probs", "attention_fwd_rows",
            "attention_bwd_sampled", "kvcache_fwd", "kvcache_fwd_units", "bruteforce",
-           "attention_fwd_fp8", "e4m3fn_decode", "dequantize", "o_bound"]
+           "attention_fwd_fp8", "e4m3fn_decode", "dequantize", "head_o_bound", "o_bound"]

@@ -87,39 +87,51 @@ def o_bound(q, k, v, o, scale: float, causal: bool = False, cu_seqlens=None,
     exponent's fma and the hardware exp2 (≤ 2^-21 relative). Added to the
     bound: the fp32 sums of O and of the weights (≤ (n + 64)·2^-24 of
     Σ_j P_j |V_j| + |O| over the n visible keys) and the final rounding of
-    O to the output type (half an ulp: 2^-9 for bf16, 2^-12 for fp16).
+    O to the output type (half an ulp, at most 2^-8 relative for bf16 with
+    its 8 significant bits and 2^-11 for fp16 with 11, plus 2^-25 absolute
+    for fp16's subnormals).
     """
     q, k, v, o = _f64(q), _f64(k), _f64(v), _f64(o)
     T, Hq, d = q.shape
     g = _group(Hq, k.shape[1])
-    out_half_ulp = {"bf16": 2.0 ** -9, "fp16": 2.0 ** -12}[out_dtype]
     bound = np.zeros_like(o)
     for a, b in _segments(T, cu_seqlens):
         if b <= a:
             continue
         for h in range(Hq):
-            Qs, Ks, Vs = q[a:b, h], k[a:b, h // g], v[a:b, h // g]
-            rows = np.arange(b - a)
-            S = _scores(Qs, rows, Ks, scale, causal)
-            m = S.max(axis=1)
-            P = np.exp(S - m[:, None])
-            P /= P.sum(axis=1, keepdims=True)
-            A = scale * (np.abs(Qs) @ np.abs(Ks).T)
-            Sl = np.where(np.isfinite(S), np.abs(S), 0.0)
-            a_j = (math.log(2.0) * (d + 8) * 2.0 ** -24 * A * math.log2(math.e)
-                   + 2.0 ** -21 + 2.0 ** -23 * (Sl + np.abs(m)[:, None]) * math.log2(math.e))
-            e = np.maximum((U_E4M3 + a_j) * P * (1.0 + a_j),
-                           np.minimum(P, SUBNORMAL_HALF_GAP * P.max(axis=1, keepdims=True)))
-            e = np.where(P > 0, e, 0.0)
-            esum = e.sum(axis=1)
-            O = o[a:b, h]
-            num = np.empty_like(O)
-            step = max(1, (1 << 22) // max(1, (b - a) * d))      # rows per block of |V − O|
-            for r0 in range(0, b - a, step):
-                dev = np.abs(Vs[None, :, :] - O[r0:r0 + step, None, :])   # [rows, keys, d]
-                num[r0:r0 + step] = np.einsum("ij,ijc->ic", e[r0:r0 + step], dev)
-            denom = np.where(esum < 1.0, 1.0 - esum, np.nan)
-            nvis = (P > 0).sum(axis=1)
-            acc = (nvis + 64)[:, None] * 2.0 ** -24 * (P @ np.abs(Vs) + np.abs(O))
-            bound[a:b, h] = num / denom[:, None] + acc + out_half_ulp * (np.abs(O) + num)
+            bound[a:b, h] = head_o_bound(q[a:b, h], k[a:b, h // g], v[a:b, h // g], o[a:b, h],
+                                         scale, causal, out_dtype=out_dtype)
     return bound
+
+
+def head_o_bound(Qs, Ks, Vs, O, scale: float, causal: bool, rows=None,
+                 out_dtype: str = "bf16") -> np.ndarray:
+    """``o_bound`` for one (sequence, query head): the query rows ``rows``
+    (positions in the sequence, default all) with their exact outputs O."""
+    Qs, Ks, Vs, O = _f64(Qs), _f64(Ks), _f64(Vs), _f64(O)
+    d = Qs.shape[1]
+    rows = np.arange(Qs.shape[0]) if rows is None else np.asarray(rows, dtype=np.int64)
+    out_half_ulp = {"bf16": 2.0 ** -8, "fp16": 2.0 ** -11}[out_dtype]
+    out_abs = {"bf16": 0.0, "fp16": 2.0 ** -25}[out_dtype]
+    L = Ks.shape[0]
+    S = _scores(Qs[rows], rows, Ks, scale, causal)
+    m = S.max(axis=1)
+    P = np.exp(S - m[:, None])
+    P /= P.sum(axis=1, keepdims=True)
+    A = scale * (np.abs(Qs[rows]) @ np.abs(Ks).T)
+    Sl = np.where(np.isfinite(S), np.abs(S), 0.0)
+    a_j = (math.log(2.0) * (d + 8) * 2.0 ** -24 * A * math.log2(math.e)
+           + 2.0 ** -21 + 2.0 ** -23 * (Sl + np.abs(m)[:, None]) * math.log2(math.e))
+    e = np.maximum((U_E4M3 + a_j) * P * (1.0 + a_j),
+                   np.minimum(P, SUBNORMAL_HALF_GAP * P.max(axis=1, keepdims=True)))
+    e = np.where(P > 0, e, 0.0)
+    esum = e.sum(axis=1)
+    num = np.empty_like(O)
+    step = max(1, (1 << 22) // max(1, L * d))      # rows per block of |V − O|
+    for r0 in range(0, len(rows), step):
+        dev = np.abs(Vs[None, :, :] - O[r0:r0 + step, None, :])   # [rows, keys, d]
+        num[r0:r0 + step] = np.einsum("ij,ijc->ic", e[r0:r0 + step], dev)
+    denom = np.where(esum < 1.0, 1.0 - esum, np.nan)
+    nvis = (P > 0).sum(axis=1)
+    acc = (nvis + 64)[:, None] * 2.0 ** -24 * (P @ np.abs(Vs) + np.abs(O))
+    return num / denom[:, None] + acc + out_half_ulp * (np.abs(O) + num) + out_abs

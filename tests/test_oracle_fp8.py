@@ -178,3 +178,29 @@ def test_bound_rejects_a_wrong_value_descale():
     q, k, v = (dequantize(f8[n], s) for n, s in zip(("q", "k", "v"), ds))
     bnd = o_bound(q, k, v, o, 1 / 8, False)
     assert np.mean(np.abs(1.25 * o - o) > bnd) > 0.9
+
+
+def test_row_subset_bound_matches_the_whole_head():
+    from oracle import head_o_bound
+    rng = np.random.default_rng(17)
+    q, k, v = (rng.standard_normal((90, 1, 16)) for _ in range(3))
+    o, _ = attention_fwd(q, k, v, 0.3, True)
+    full = o_bound(q, k, v, o, 0.3, True)
+    rows = np.array([0, 5, 44, 89])
+    sub = head_o_bound(q[:, 0], k[:, 0], v[:, 0], o[rows, 0], 0.3, True, rows=rows)
+    np.testing.assert_allclose(sub, full[rows, 0], rtol=1e-12)
+
+
+@pytest.mark.parametrize("out", ["bf16", "fp16"])
+def test_bound_covers_the_output_rounding(out):
+    """One key: O = V exactly, so a correct kernel returns V rounded to the
+    output type; the bound must admit that rounding for every value."""
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(18)
+    v = np.concatenate([rng.standard_normal((1, 1, 64)) * 10.0 ** rng.integers(-6, 3),
+                        np.exp2(np.arange(-20, 4))[None, None, :64] * (1 + 2.0 ** -9)], axis=2)
+    q, k = rng.standard_normal((1, 1, v.shape[2])), rng.standard_normal((1, 1, v.shape[2]))
+    o, _ = attention_fwd(q, k, v, 0.1, False)
+    td = {"bf16": torch.bfloat16, "fp16": torch.float16}[out]
+    rounded = torch.from_numpy(o).to(td).double().numpy()
+    assert np.all(np.abs(rounded - o) <= o_bound(q, k, v, o, 0.1, False, out_dtype=out))
