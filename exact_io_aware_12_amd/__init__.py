@@ -79,6 +79,8 @@ def _load():
     L.fa_bwd_window.restype = i
     L.fa_bwd_window_stage.argtypes = [i] + L.fa_bwd_window.argtypes
     L.fa_bwd_window_stage.restype = i
+    L.fa_fwd_fp8.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp, f, f, f, i, vp]
+    L.fa_fwd_fp8.restype = i
     L.fa_fwd_kvcache.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, i, i, vp, sz, vp]
     L.fa_fwd_kvcache.restype = i
     L.fa_fwd_kvcache_stage.argtypes = [i] + L.fa_fwd_kvcache.argtypes
@@ -133,6 +135,12 @@ def fa_bwd_window_stage(stage, q, k, v, o, dout, lse, dq, dk, dv, B, Hq, Hkv, N,
     return lib.fa_bwd_window_stage(stage, q, k, v, o, dout, lse, dq, dk, dv, B, Hq, Hkv, N, d,
                                    scale, window_left, window_right, cu_seqlens, dtype, workspace,
                                    workspace_bytes, stream)
+
+
+def fa_fwd_fp8(q, k, v, o, lse, B, Hq, Hkv, N, d, scale, causal, cu_seqlens, descale_q,
+               descale_k, descale_v, out_dtype, stream) -> int:
+    return lib.fa_fwd_fp8(q, k, v, o, lse, B, Hq, Hkv, N, d, scale, causal, cu_seqlens,
+                          descale_q, descale_k, descale_v, out_dtype, stream)
 
 
 def fa_bwd_num_stages() -> int:
@@ -261,6 +269,36 @@ def flash_attn_func(q, k, v, causal=False, softmax_scale=None, cu_seqlens=None, 
                                _dtype_code(q), _stream())
     if st != FA_OK:
         raise FaError(st, "fa_fwd" if w is None else "fa_fwd_window")
+    return o, lse
+
+
+def flash_attn_func_fp8(q, k, v, descale_q=1.0, descale_k=1.0, descale_v=1.0, causal=False,
+                        softmax_scale=None, cu_seqlens=None, max_seqlen=None, out_dtype=None):
+    """FP8 forward: q, k, v are e4m3fn codes (torch.float8_e4m3fn or uint8 tensors)
+    with per-tensor descales (real value = code value × descale). Returns (o, lse):
+    o in out_dtype (bfloat16 by default, or float16), lse float32 [Hq, T]."""
+    import torch
+    out_dtype = torch.bfloat16 if out_dtype is None else out_dtype
+    B, N, T, Hq, Hkv, d = _shape(q, k, cu_seqlens, max_seqlen)
+    if v.shape != k.shape:
+        raise ValueError("k and v must have the same shape")
+    for t in (q, k, v):
+        if t.dtype not in (torch.float8_e4m3fn, torch.uint8):
+            raise TypeError(f"fp8 inputs must be float8_e4m3fn or uint8 codes, got {t.dtype}")
+    _check_dev(q, k, v)
+    if cu_seqlens is not None:
+        _check_dev(cu_seqlens)
+        if cu_seqlens.dtype != torch.int32:
+            raise TypeError("cu_seqlens must be int32")
+    scale = softmax_scale if softmax_scale is not None else 1.0 / math.sqrt(d)
+    o = torch.empty(q.shape, dtype=out_dtype, device=q.device)
+    lse = torch.empty((Hq, T), dtype=torch.float32, device=q.device)
+    cu = cu_seqlens.data_ptr() if cu_seqlens is not None else None
+    st = lib.fa_fwd_fp8(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                        B, Hq, Hkv, N, d, float(scale), int(bool(causal)), cu, float(descale_q),
+                        float(descale_k), float(descale_v), _dtype_code(o), _stream())
+    if st != FA_OK:
+        raise FaError(st, "fa_fwd_fp8")
     return o, lse
 
 

@@ -104,6 +104,45 @@ int fa_fwd_window(const void* q, const void* k, const void* v, void* o, float* l
                     stream);
 }
 
+int fa_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq,
+               int Hkv, int N, int d, float scale, int causal, const int32_t* cu_seqlens,
+               float descale_q, float descale_k, float descale_v, int out_dtype,
+               hipStream_t stream) {
+  bool noop;
+  int st = check_sizes(B, Hq, Hkv, N, d, scale, causal, out_dtype, &noop);
+  if (st != FA_OK) return st;
+  for (float x : {descale_q, descale_k, descale_v})
+    if (!std::isfinite(x) || !(x > 0.f)) return FA_ERR_INVALID_ARG;
+  const float c = scale * descale_q * descale_k * kLog2e;
+  if (!std::isfinite(c) || !(c > 0.f)) return FA_ERR_INVALID_ARG;
+  if (d != 128) return FA_ERR_UNSUPPORTED;
+  if (noop) return FA_OK;
+  if (!q || !k || !v || !o || !lse) return FA_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse))
+    return FA_ERR_INVALID_ARG;
+  fa::Fp8FwdArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.lse = lse;
+  a.cu_seqlens = cu_seqlens;
+  a.B = B;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.N = N;
+  a.group = Hq / Hkv;
+  const int br = fa::fwd_fp8_query_tile();
+  a.n_qtiles = (N + br - 1) / br;
+  a.scale_log2 = c;
+  a.wl = a.wr = 0;
+  a.o_scale = descale_v;
+  if ((int64_t)a.n_qtiles * Hq * B >= (int64_t)1 << 31) return FA_ERR_UNSUPPORTED;
+  hipError_t e = fa::launch_fwd_fp8(a, out_dtype == FA_BF16, d, causal != 0,
+                                    cu_seqlens != nullptr, stream);
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
 size_t fa_bwd_workspace_size(int B, int Hq, int Hkv, int N, int d) {
   bool noop;
   if (check_sizes(B, Hq, Hkv, N, d, 1.f, 0, FA_FP16, &noop) != FA_OK) return 0;

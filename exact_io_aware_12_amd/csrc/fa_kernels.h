@@ -24,6 +24,13 @@ struct FwdArgs {
   int wl, wr;                 // window bounds (kMaskWindow only)
 };
 
+// FP8 forward: q, k, v hold e4m3fn codes; scale_log2 already includes both
+// input descales (scale · descale_q · descale_k · log2 e) and O is multiplied
+// by o_scale (the descale of V) before it is rounded to the output type.
+struct Fp8FwdArgs : FwdArgs {
+  float o_scale;
+};
+
 struct BwdArgs {
   const void* q;
   const void* k;
@@ -66,6 +73,9 @@ struct DecodeArgs {
 int fwd_query_tile();
 hipError_t launch_fwd(const FwdArgs& a, bool bf16_in, int d, int mask, bool varlen,
                       hipStream_t s);
+int fwd_fp8_query_tile();
+hipError_t launch_fwd_fp8(const Fp8FwdArgs& a, bool bf16_out, int d, bool causal, bool varlen,
+                          hipStream_t s);
 // stage < 0: every stage in order; otherwise only stage 0 (D = rowsum(dO∘O)),
 // 1 (dK, dV) or 2 (dQ).
 int bwd_num_stages();

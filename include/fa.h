@@ -156,6 +156,29 @@ int fa_bwd_window_stage(int stage, const void* q, const void* k, const void* v, 
                         void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * FP8 forward: the forward of fa_fwd on e4m3 inputs. The pages name e4m3
+ * (torch.float8_e4m3fn) as the 8-bit attention format and credit
+ * FlashAttention-3 with an FP8 forward (cxbdf.cn deployment guide, section
+ * 4.3; Flash Attention 是什麼, adersaytech.com, FA-1 to FA-4 table and note).
+ *   q : [T, Hq, d]   e4m3fn codes (OCP E4M3, finite-only: bias 7, max 448)
+ *   k : [T, Hkv, d]  e4m3fn codes
+ *   v : [T, Hkv, d]  e4m3fn codes
+ *   descale_q, descale_k, descale_v : per-tensor factors, finite and > 0;
+ *       the real inputs are code value × descale
+ *   o   : [T, Hq, d] out_dtype (FA_FP16 or FA_BF16), nearest even
+ *   lse : [Hq, T]    float32, natural log, of scale·(real Q)·(real K)ᵀ
+ * The kernel rounds the softmax weights to e4m3 for the P·V product (the
+ * matrix instruction takes 8-bit operands) and normalises O by the sum of
+ * those rounded weights; LSE uses the unrounded weights. d = 128 only
+ * (other d: FA_ERR_UNSUPPORTED). Layout, varlen, causal, alignment,
+ * ownership, errors and determinism as for fa_fwd.
+ */
+int fa_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse,
+               int B, int Hq, int Hkv, int N, int d, float scale, int causal,
+               const int32_t* cu_seqlens, float descale_q, float descale_k, float descale_v,
+               int out_dtype, hipStream_t stream);
+
+/*
  * Decode: attention of Nq new queries per batch entry over a key/value cache
  * (the inference use of the method: long-context inference and inference
  * tools, Flash Attention 是什麼, adersaytech.com, sections 原理拆解 and

@@ -22,7 +22,8 @@ def declared_functions():
 def test_header_declares_the_boundary():
     assert declared_functions() == ["fa_bwd", "fa_bwd_num_stages", "fa_bwd_stage",
                                     "fa_bwd_window", "fa_bwd_window_stage",
-                                    "fa_bwd_workspace_size", "fa_fwd", "fa_fwd_kvcache",
+                                    "fa_bwd_workspace_size", "fa_fwd", "fa_fwd_fp8",
+                                    "fa_fwd_kvcache",
                                     "fa_fwd_kvcache_num_stages", "fa_fwd_kvcache_stage",
                                     "fa_fwd_kvcache_workspace_size", "fa_fwd_window",
                                     "fa_kvcache_num_splits", "fa_status_string"]
@@ -252,3 +253,40 @@ def test_window_no_device_reports_hip_error():
     assert fwdw() == fa.FA_ERR_HIP
     assert fwdw(d=256, wl=5, wr=5) == fa.FA_ERR_HIP
     assert bwdw() == fa.FA_ERR_HIP
+
+
+def fwd8(**kw):
+    a = dict(q=P, k=P, v=P, o=P, lse=P, B=1, Hq=2, Hkv=2, N=16, d=128, scale=0.125, causal=0,
+             cu=None, dq=0.01, dk=0.02, dv=0.5, dtype=fa.FA_BF16, stream=None)
+    a.update(kw)
+    return fa.fa_fwd_fp8(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["Hq"], a["Hkv"],
+                         a["N"], a["d"], a["scale"], a["causal"], a["cu"], a["dq"], a["dk"],
+                         a["dv"], a["dtype"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dq=0.0), fa.FA_ERR_INVALID_ARG),
+    (dict(dk=-1.0), fa.FA_ERR_INVALID_ARG),
+    (dict(dv=float("nan")), fa.FA_ERR_INVALID_ARG),
+    (dict(dv=float("inf")), fa.FA_ERR_INVALID_ARG),
+    (dict(dq=1e30, dk=1e30), fa.FA_ERR_INVALID_ARG),     # scale·dq·dk overflows
+    (dict(dtype=2), fa.FA_ERR_INVALID_ARG),
+    (dict(causal=3), fa.FA_ERR_INVALID_ARG),
+    (dict(Hq=3, Hkv=2), fa.FA_ERR_INVALID_ARG),
+    (dict(q=None), fa.FA_ERR_INVALID_ARG),
+    (dict(k=P + 8), fa.FA_ERR_INVALID_ARG),
+    (dict(d=64), fa.FA_ERR_UNSUPPORTED),
+    (dict(d=256), fa.FA_ERR_UNSUPPORTED),
+    (dict(B=0), fa.FA_OK),
+    (dict(N=0, q=None), fa.FA_OK),
+])
+def test_fwd_fp8_host_checks(kw, status):
+    assert fwd8(**kw) == status
+
+
+def test_fwd_fp8_no_device_reports_hip_error():
+    torch = pytest.importorskip("torch")
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    assert fwd8() == fa.FA_ERR_HIP
+    assert fwd8(causal=1, dtype=fa.FA_FP16) == fa.FA_ERR_HIP
