@@ -9,6 +9,7 @@ causal; backward 2.5× the forward.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
     python bench.py --sweep     # forward TFLOP/s for every forward workload, one line each
+    python bench.py --fp8-sweep # fa_fwd vs fa_fwd_fp8 on the d = 128 forward workloads
     python bench.py --workload decode_llama   # decode over a KV cache: HBM GB/s, one line
     python bench.py --pmc-step  # one calibration copy + one step, for rocprofv3 --pmc runs
     python bench.py --pmc-summary FETCH_DIR WRITE_DIR   # counters -> profiles/traffic_<workload>.json
@@ -40,6 +41,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16/fp16 MFMA: 256 CU x 4096 flop/clk x 2.4 GHz
+PEAK_FP8_TFLOPS = 5033.2    # dense fp8 (e4m3) MFMA: twice the bf16 rate
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 
 
@@ -52,6 +54,10 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--sweep", action="store_true",
                    help="time fa_fwd on every forward workload (10 warmup, 100 timed calls)")
+    p.add_argument("--fp8-sweep", action="store_true",
+                   help="time fa_fwd and fa_fwd_fp8 on the d = 128 forward workloads")
+    p.add_argument("--names", default=None,
+                   help="comma-separated workload names for --sweep / --fp8-sweep")
     p.add_argument("--pmc-step", action="store_true",
                    help="one calibration copy and one fa_fwd + fa_bwd step (for counter runs)")
     p.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
@@ -60,7 +66,7 @@ def parse():
 
 
 CALIB_BYTES = 256 << 20   # bytes read (and written) by the calibration copy
-KERNELS = ("fwd_kernel", "delta_kernel", "dkdv_kernel", "dq_kernel", "decode_combine_kernel",
+KERNELS = ("fwd_kernel", "fwd8_kernel", "delta_kernel", "dkdv_kernel", "dq_kernel", "decode_combine_kernel",
            "decode_kernel")
 
 
@@ -163,6 +169,34 @@ class Bound:
     def step(self):
         self.fwd()
         self.bwd()
+
+
+class Fp8Bound:
+    """Device buffers and the raw fa_fwd_fp8 call for one workload: the
+    workload's normal draws quantised per tensor to e4m3fn (descale = max|x| / 448)."""
+
+    def __init__(self, w):
+        import torch
+        import exact_io_aware_12_amd as fa
+        import workloads as W
+        self.fa, self.w = fa, w
+        f8 = W.quantize_e4m3(W.generate(w, with_grad=False))
+        self.t = {n: torch.from_numpy(f8[n]).to("cuda") for n in ("q", "k", "v")}
+        self.ds = tuple(float(f8["descale_" + n]) for n in ("q", "k", "v"))
+        self.cu = torch.from_numpy(f8["cu_seqlens"]).to("cuda") if w.varlen else None
+        self.cu_ptr = self.cu.data_ptr() if self.cu is not None else None
+        self.o = torch.empty(self.t["q"].shape, dtype=torch.bfloat16, device="cuda")
+        self.lse = torch.empty((w.Hq, w.T), dtype=torch.float32, device="cuda")
+        self.stream = torch.cuda.current_stream().cuda_stream
+
+    def fwd(self):
+        w, t = self.w, self.t
+        st = self.fa.fa_fwd_fp8(t["q"].data_ptr(), t["k"].data_ptr(), t["v"].data_ptr(),
+                                self.o.data_ptr(), self.lse.data_ptr(), w.B, w.Hq, w.Hkv, w.N,
+                                w.d, w.scale, int(w.causal), self.cu_ptr, *self.ds,
+                                self.fa.FA_BF16, self.stream)
+        if st != self.fa.FA_OK:
+            raise self.fa.FaError(st, "fa_fwd_fp8")
 
 
 def time_calls(torch, fn, iters, warmup):
@@ -500,6 +534,8 @@ def run_sweep(args):
                                       for c in ("full", "causal")] + ["gqa_varlen", "train_16k",
                                                                       "fwd_d256_N4096",
                                                                       "window_16k"]
+    if args.names:
+        names = args.names.split(",")
     for n in names:
         w = W.WORKLOADS[n]
         b = Bound(w, with_bwd=False)
@@ -510,6 +546,36 @@ def run_sweep(args):
                           "pct_of_peak": round(100 * tf / PEAK_BF16_TFLOPS, 2)}), flush=True)
         del b
         torch.cuda.empty_cache()
+
+
+def run_fp8_sweep(args):
+    """fa_fwd (bf16) and fa_fwd_fp8 (e4m3 in, bf16 out) on the d = 128 forward
+    workloads, one line each: TFLOP/s by the forward convention, against the
+    dense peak of each instruction's input type."""
+    import torch
+    import workloads as W
+    names = [f"sweep_N{N}_{c}" for N in (1024, 4096, 8192) for c in ("full", "causal")] + \
+        ["gqa_varlen", "train_16k"]
+    if args.names:
+        names = args.names.split(",")
+    for n in names:
+        w = W.WORKLOADS[n]
+        b16 = Bound(w, with_bwd=False)
+        ms16 = time_calls(torch, b16.fwd, 100, 10)
+        del b16
+        torch.cuda.empty_cache()
+        b8 = Fp8Bound(w)
+        ms8 = time_calls(torch, b8.fwd, 100, 10)
+        del b8
+        torch.cuda.empty_cache()
+        tf16 = w.fwd_flop() / (ms16 * 1e-3) / 1e12
+        tf8 = w.fwd_flop() / (ms8 * 1e-3) / 1e12
+        print(json.dumps({"workload": n, "N": w.N, "d": w.d, "causal": w.causal,
+                          "bf16_fwd_ms": round(ms16, 4), "bf16_tflops": round(tf16, 2),
+                          "bf16_pct_of_peak": round(100 * tf16 / PEAK_BF16_TFLOPS, 2),
+                          "fp8_fwd_ms": round(ms8, 4), "fp8_tflops": round(tf8, 2),
+                          "fp8_pct_of_peak": round(100 * tf8 / PEAK_FP8_TFLOPS, 2),
+                          "fp8_speedup": round(ms16 / ms8, 3)}), flush=True)
 
 
 def main():
@@ -527,6 +593,9 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
+    if args.fp8_sweep:
+        run_fp8_sweep(args)
+        return
     if args.sweep:
         run_sweep(args)
     elif args.pmc_step:

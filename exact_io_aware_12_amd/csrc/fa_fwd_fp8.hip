@@ -173,18 +173,40 @@ __device__ __forceinline__ i32x8 p_operand(const f32x16 (&s)[2]) {
 #pragma unroll
   for (int w = 0; w < 8; ++w) {
     const int jb = w >> 2, r = 4 * (w & 3);
-    const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(s[jb][r], s[jb][r + 1], 0, false);
+    // the first convert fills bytes 0-1 and keeps bytes 2-3 of its third
+    // operand, which the second convert overwrites: any register will do
+    const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(s[jb][r], s[jb][r + 1],
+                                                   __builtin_bit_cast(int, s[jb][r + 2]), false);
     p[w] = __builtin_amdgcn_cvt_pk_fp8_f32(s[jb][r + 2], s[jb][r + 3], lo, true);
   }
   return p;
 }
 
+// Where the next tile's copies go and come from (NONE: no next tile).
+enum class NextCopy { NONE, INSIDE, CLAMPED };
+
+// One 64-key tile. The copies of the next tile into the other LDS buffer are
+// issued first; with every LDS pointer declared __restrict__ in this one
+// inlined function the compiler knows those copies do not overlap the
+// current tile's reads and does not make the reads wait for them.
 template <int D, bool CAUSAL, bool EDGE>
-__device__ __forceinline__ void fwd8_tile(const u8* kt, const u8* vt, const i32x8 (&qf)[D / 64],
+__device__ __forceinline__ void fwd8_tile(const u8* __restrict__ kt, const u8* __restrict__ vt,
+                                          u8* __restrict__ nk, u8* __restrict__ nv, NextCopy next,
+                                          const u8* kp, const u8* vp, int64_t kvs, int n0,
+                                          const DmaPlan8<D>& plan, int wave_u, int wave,
+                                          bool skip, const i32x8 (&qf)[D / 64],
                                           f32x16 (&o)[D / 32], f32x16& lsum, float& mc, float& l,
                                           float c, int kv0, int L, int qrow, int lane) {
   constexpr int NKS = D / 64;
   constexpr int NCB = D / 32;
+  if (next == NextCopy::INSIDE) {
+    tile_dma8_in<D>(nk, kp + (int64_t)n0 * kvs, plan, wave_u);
+    tile_dma8_in<D>(nv, vp + (int64_t)n0 * kvs, plan, wave_u);
+  } else if (next == NextCopy::CLAMPED) {
+    tile_dma8<D>(nk, kp, kvs, n0, L, wave, lane);
+    tile_dma8<D>(nv, vp, kvs, n0, L, wave, lane);
+  }
+  if (skip) return;
   const int half = lane >> 5;
   // ---- Sᵀ = K·Qᵀ ----------------------------------------------------------
   f32x16 s[2] = {f32x16{}, f32x16{}};
@@ -316,19 +338,14 @@ __global__ __launch_bounds__(kThreads, 2) void fwd8_kernel(Fp8FwdArgs a) {
     const int kv0 = j * kBC;
     wait_vmem_all();   // this thread's copies of tile j have landed
     __syncthreads();   // everyone's have, and tile j-1 is no longer read
-    if (j + 1 < ntiles) {
-      const int n0 = kv0 + kBC;
-      if (n0 + kBC <= L) {
-        tile_dma8_in<D>(lds[BUF ^ 1][0], kp + (int64_t)n0 * kvs, plan, wave_u);
-        tile_dma8_in<D>(lds[BUF ^ 1][1], vp + (int64_t)n0 * kvs, plan, wave_u);
-      } else {
-        tile_dma8<D>(lds[BUF ^ 1][0], kp, kvs, n0, L, wave, lane);
-        tile_dma8<D>(lds[BUF ^ 1][1], vp, kvs, n0, L, wave, lane);
-      }
-    }
-    if (EDGE && CAUSAL && kv0 > wq_last) return;   // the whole tile is after this wave's rows
-    fwd8_tile<D, CAUSAL, EDGE>(lds[BUF][0], lds[BUF][1], qf, o, lsum, mc, l, c, kv0, L, qrow,
-                               lane);
+    const int n0 = kv0 + kBC;
+    const NextCopy next = j + 1 >= ntiles ? NextCopy::NONE
+                          : n0 + kBC <= L ? NextCopy::INSIDE : NextCopy::CLAMPED;
+    // an edge tile wholly after this wave's rows is only copied, not computed
+    const bool skip = EDGE && CAUSAL && kv0 > wq_last;
+    fwd8_tile<D, CAUSAL, EDGE>(lds[BUF][0], lds[BUF][1], lds[BUF ^ 1][0], lds[BUF ^ 1][1], next,
+                               kp, vp, kvs, n0, plan, wave_u, wave, skip, qf, o, lsum, mc, l, c,
+                               kv0, L, qrow, lane);
   };
   int j = 0;
   for (; j < jb; ++j) step(std::false_type{}, j);
