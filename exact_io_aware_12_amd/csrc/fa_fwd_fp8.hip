@@ -332,9 +332,13 @@ __global__ __launch_bounds__(kThreads, 2) void fwd8_kernel(Fp8FwdArgs a) {
 
   const DmaPlan8<D> plan(kvs, wave, lane);
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
-  auto step = [&](auto edge_tag, int j) __attribute__((always_inline)) {
+  // tile j sits in LDS buffer j & 1; buf_tag fixes it at compile time where
+  // it is known (the unrolled interior pairs), so that every LDS address is a
+  // per-lane register plus an immediate offset
+  auto step = [&](auto edge_tag, auto buf_tag, int j) __attribute__((always_inline)) {
     constexpr bool EDGE = decltype(edge_tag)::value;
-    const int BUF = j & 1;
+    constexpr int FIXED = decltype(buf_tag)::value;   // 0, 1, or -1 for j & 1
+    const int BUF = FIXED >= 0 ? FIXED : (j & 1);
     const int kv0 = j * kBC;
     wait_vmem_all();   // this thread's copies of tile j have landed
     __syncthreads();   // everyone's have, and tile j-1 is no longer read
@@ -347,9 +351,16 @@ __global__ __launch_bounds__(kThreads, 2) void fwd8_kernel(Fp8FwdArgs a) {
                                kp, vp, kvs, n0, plan, wave_u, wave, skip, qf, o, lsum, mc, l, c,
                                kv0, L, qrow, lane);
   };
+  using B0 = std::integral_constant<int, 0>;
+  using B1 = std::integral_constant<int, 1>;
+  using BR = std::integral_constant<int, -1>;
   int j = 0;
-  for (; j < jb; ++j) step(std::false_type{}, j);
-  for (; j < ntiles; ++j) step(std::true_type{}, j);
+  for (; j + 1 < jb; j += 2) {   // tile j is in buffer 0, tile j+1 in buffer 1
+    step(std::false_type{}, B0{}, j);
+    step(std::false_type{}, B1{}, j + 1);
+  }
+  if (j < jb) step(std::false_type{}, BR{}, j++);
+  for (; j < ntiles; ++j) step(std::true_type{}, BR{}, j);
 
   // ---- epilogue -------------------------------------------------------------
   const float l_tot = wave_sum_halves(l);
