@@ -17,6 +17,12 @@ Optionally a sliding window (wl, wr) keeps only keys i − wl ≤ j ≤ i + wr
 (a negative bound is unbounded): the band mask that the mlqm.cn page,
 section 四 (mask types), names among the masks standard attention allows;
 with causal the two conditions both apply.
+Optionally a soft cap c > 0 bounds the logits smoothly before the softmax:
+S_ij = c · tanh(scale · Q_i·K_j / c). The FlashAttention-2 page (blog.gitcode.com,
+section 2.3, adaptive soft cap) introduces a softcap step; the formula printed
+there neither bounds the score nor is continuous at the cap, so the bounded
+tanh form is the reading taken (the backward then carries the factor
+1 − tanh² of the chain rule).
 Sequences never see each other (padding-free packing; the mlqm.cn page,
 section 四, lists padding masks among what the method supports).
 The row logsumexp is the ``softmax_lse`` the forward kernel writes out
@@ -67,10 +73,12 @@ def _group(Hq: int, Hkv: int) -> int:
 
 
 def _scores(Qr: np.ndarray, rows: np.ndarray, Ks: np.ndarray, scale: float,
-            causal: bool, window=None) -> np.ndarray:
+            causal: bool, window=None, softcap=None) -> np.ndarray:
     """S for the query rows ``rows`` (positions in the sequence) against all keys;
     invisible keys get −inf."""
     S = scale * (Qr @ Ks.T)
+    if softcap:
+        S = softcap * np.tanh(S / softcap)
     keys = np.arange(Ks.shape[0])[None, :]
     if causal:
         S = np.where(keys <= rows[:, None], S, -np.inf)
@@ -94,7 +102,7 @@ def _row_blocks(rows: np.ndarray, L: int):
         yield rows[a:a + step]
 
 
-def head_fwd(Qs, Ks, Vs, scale: float, causal: bool, rows=None, window=None):
+def head_fwd(Qs, Ks, Vs, scale: float, causal: bool, rows=None, window=None, softcap=None):
     """One (sequence, query head): O [R, d] and LSE [R] for ``rows`` (default all)."""
     Qs, Ks, Vs = _f64(Qs), _f64(Ks), _f64(Vs)
     L = Ks.shape[0]
@@ -103,7 +111,7 @@ def head_fwd(Qs, Ks, Vs, scale: float, causal: bool, rows=None, window=None):
     lse = np.empty(len(rows))
     pos = 0
     for blk in _row_blocks(rows, L):
-        S = _scores(Qs[blk], blk, Ks, scale, causal, window)
+        S = _scores(Qs[blk], blk, Ks, scale, causal, window, softcap)
         l = _lse(S)
         P = np.exp(S - l[:, None])
         O[pos:pos + len(blk)] = P @ Vs
@@ -112,7 +120,7 @@ def head_fwd(Qs, Ks, Vs, scale: float, causal: bool, rows=None, window=None):
     return O, lse
 
 
-def head_bwd(Qs, Ks, Vs, dOs, scale: float, causal: bool, window=None):
+def head_bwd(Qs, Ks, Vs, dOs, scale: float, causal: bool, window=None, softcap=None):
     """One (sequence, query head): dQ, dK, dV [L, d] by the chain rule above."""
     Qs, Ks, Vs, dOs = _f64(Qs), _f64(Ks), _f64(Vs), _f64(dOs)
     L = Qs.shape[0]
@@ -120,26 +128,30 @@ def head_bwd(Qs, Ks, Vs, dOs, scale: float, causal: bool, window=None):
     dK = np.zeros_like(Ks)
     dV = np.zeros_like(Vs)
     for blk in _row_blocks(np.arange(L), L):
-        S = _scores(Qs[blk], blk, Ks, scale, causal, window)
+        S = _scores(Qs[blk], blk, Ks, scale, causal, window, softcap)
         P = np.exp(S - _lse(S)[:, None])
         dO = dOs[blk]
         dV += P.T @ dO
         dP = dO @ Vs.T
         D = (P * dP).sum(axis=1)
         dS = P * (dP - D[:, None])
+        if softcap:   # d/dx [c·tanh(x/c)] = 1 − tanh²(x/c)
+            dS = dS * (1.0 - np.tanh(scale * (Qs[blk] @ Ks.T) / softcap) ** 2)
         dQ[blk] = scale * (dS @ Ks)
         dK += scale * (dS.T @ Qs[blk])
     return dQ, dK, dV
 
 
-def attention_probs(Qs, Ks, scale: float, causal: bool, window=None) -> np.ndarray:
+def attention_probs(Qs, Ks, scale: float, causal: bool, window=None,
+                    softcap=None) -> np.ndarray:
     """The full softmax matrix P [L, L] of one (sequence, head)."""
     Qs, Ks = _f64(Qs), _f64(Ks)
-    S = _scores(Qs, np.arange(Qs.shape[0]), Ks, scale, causal, window)
+    S = _scores(Qs, np.arange(Qs.shape[0]), Ks, scale, causal, window, softcap)
     return np.exp(S - _lse(S)[:, None])
 
 
-def attention_fwd(q, k, v, scale: float, causal: bool = False, cu_seqlens=None, window=None):
+def attention_fwd(q, k, v, scale: float, causal: bool = False, cu_seqlens=None, window=None,
+                  softcap=None):
     """Whole-tensor forward.
 
     q [T, Hq, d], k/v [T, Hkv, d] (any float type; upcast exactly to float64);
@@ -156,17 +168,18 @@ def attention_fwd(q, k, v, scale: float, causal: bool = False, cu_seqlens=None, 
             continue
         for h in range(Hq):
             O, l = head_fwd(q[a:b, h], k[a:b, h // g], v[a:b, h // g], scale, causal,
-                            window=window)
+                            window=window, softcap=softcap)
             o[a:b, h] = O
             lse[h, a:b] = l
     return o, lse
 
 
 def attention_fwd_rows(q, k, v, scale: float, causal: bool, cu_seqlens, seq: int,
-                       head: int, rows: Sequence[int], window=None):
+                       head: int, rows: Sequence[int], window=None, softcap=None):
     """O and LSE of selected query rows (positions inside sequence ``seq``) of one head."""
     q, k, v = _seq_head_views(q, k, v, cu_seqlens, seq, head)
-    return head_fwd(q, k, v, scale, causal, rows=np.asarray(rows), window=window)
+    return head_fwd(q, k, v, scale, causal, rows=np.asarray(rows), window=window,
+                    softcap=softcap)
 
 
 def _seq_head_views(q, k, v, cu_seqlens, seq, head):
@@ -177,7 +190,7 @@ def _seq_head_views(q, k, v, cu_seqlens, seq, head):
 
 
 def attention_bwd(q, k, v, do, scale: float, causal: bool = False, cu_seqlens=None,
-                  window=None):
+                  window=None, softcap=None):
     """Whole-tensor backward: dq [T, Hq, d], dk/dv [T, Hkv, d] in float64."""
     q, k, v, do = _f64(q), _f64(k), _f64(v), _f64(do)
     T, Hq, d = q.shape
@@ -190,7 +203,7 @@ def attention_bwd(q, k, v, do, scale: float, causal: bool = False, cu_seqlens=No
             continue
         for h in range(Hq):
             dQ, dK, dV = head_bwd(q[a:b, h], k[a:b, h // g], v[a:b, h // g], do[a:b, h],
-                                  scale, causal, window)
+                                  scale, causal, window, softcap)
             dq[a:b, h] = dQ
             dk[a:b, h // g] += dK
             dv[a:b, h // g] += dV
@@ -199,7 +212,7 @@ def attention_bwd(q, k, v, do, scale: float, causal: bool = False, cu_seqlens=No
 
 def attention_bwd_sampled(q, k, v, do, scale: float, causal: bool, cu_seqlens,
                           units: Iterable[Tuple[int, int]],
-                          window=None) -> Dict[Tuple[int, int], tuple]:
+                          window=None, softcap=None) -> Dict[Tuple[int, int], tuple]:
     """Backward of selected (sequence, KV head) units only.
 
     Returns {(seq, kv_head): (dq [L, g, d], dk [L, d], dv [L, d])}, where the
@@ -218,7 +231,8 @@ def attention_bwd_sampled(q, k, v, do, scale: float, causal: bool, cu_seqlens,
         dv = np.zeros_like(Vs)
         for r in range(g):
             h = kvh * g + r
-            dQ, dK, dV = head_bwd(q[a:b, h], Ks, Vs, do[a:b, h], scale, causal, window)
+            dQ, dK, dV = head_bwd(q[a:b, h], Ks, Vs, do[a:b, h], scale, causal, window,
+                                  softcap)
             dq[:, r] = dQ
             dk += dK
             dv += dV

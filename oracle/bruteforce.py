@@ -10,7 +10,9 @@ Definition followed: the attention formula of the FlashAttention guide
 padding-free visibility rules; the backward is the chain rule of that formula.
 ``window`` = (left, right) additionally restricts query i to the keys i − left
 .. i + right (a negative bound is unbounded): the band ("sliding window") mask
-of the mlqm.cn page, section 四.
+of the mlqm.cn page, section 四. ``softcap`` = c > 0 replaces each logit x by
+c·tanh(x / c) (the bounded reading of the FlashAttention-2 page's soft cap,
+blog.gitcode.com section 2.3); its derivative 1 − tanh² enters the backward.
 """
 from __future__ import annotations
 
@@ -33,7 +35,11 @@ def _visible(i, L, causal, window=None):
     return range(lo, hi + 1)
 
 
-def forward(q, k, v, scale, causal, seqs, window=None):
+def _logit(x, softcap):
+    return softcap * math.tanh(x / softcap) if softcap else x
+
+
+def forward(q, k, v, scale, causal, seqs, window=None, softcap=None):
     Hq, Hkv = len(q[0]), len(k[0])
     grp = Hq // Hkv
     o = [[None] * Hq for _ in q]
@@ -44,7 +50,7 @@ def forward(q, k, v, scale, causal, seqs, window=None):
             g = h // grp
             for i in range(L):
                 js = list(_visible(i, L, causal, window))
-                s = [scale * _dot(q[a + i][h], k[a + j][g]) for j in js]
+                s = [_logit(scale * _dot(q[a + i][h], k[a + j][g]), softcap) for j in js]
                 m = max(s)
                 lsum = math.log(math.fsum(math.exp(x - m) for x in s)) + m
                 p = [math.exp(x - lsum) for x in s]
@@ -55,7 +61,7 @@ def forward(q, k, v, scale, causal, seqs, window=None):
     return o, lse
 
 
-def backward(q, k, v, do, scale, causal, seqs, window=None):
+def backward(q, k, v, do, scale, causal, seqs, window=None, softcap=None):
     Hq, Hkv = len(q[0]), len(k[0])
     grp = Hq // Hkv
     d = len(q[0][0])
@@ -70,16 +76,20 @@ def backward(q, k, v, do, scale, causal, seqs, window=None):
             # P and dP for the whole (sequence, head), then the sums term by term
             P = [[0.0] * L for _ in range(L)]
             dP = [[0.0] * L for _ in range(L)]
+            G = [[1.0] * L for _ in range(L)]   # derivative of the soft cap
             for i in range(L):
                 js = list(_visible(i, L, causal, window))
-                s = [scale * _dot(q[a + i][h], k[a + j][g]) for j in js]
+                raw = [scale * _dot(q[a + i][h], k[a + j][g]) for j in js]
+                s = [_logit(x, softcap) for x in raw]
                 m = max(s)
                 lsum = math.log(math.fsum(math.exp(x - m) for x in s)) + m
                 for n, j in enumerate(js):
                     P[i][j] = math.exp(s[n] - lsum)
                     dP[i][j] = _dot(do[a + i][h], v[a + j][g])
+                    if softcap:
+                        G[i][j] = 1.0 - math.tanh(raw[n] / softcap) ** 2
             D = [math.fsum(P[i][j] * dP[i][j] for j in range(L)) for i in range(L)]
-            dS = [[P[i][j] * (dP[i][j] - D[i]) for j in range(L)] for i in range(L)]
+            dS = [[P[i][j] * (dP[i][j] - D[i]) * G[i][j] for j in range(L)] for i in range(L)]
             for i in range(L):
                 for c in range(d):
                     dq[a + i][h][c] = scale * math.fsum(dS[i][j] * k[a + j][g][c]
