@@ -79,6 +79,13 @@ def _load():
     L.fa_bwd_window.restype = i
     L.fa_bwd_window_stage.argtypes = [i] + L.fa_bwd_window.argtypes
     L.fa_bwd_window_stage.restype = i
+    L.fa_fwd_softcap.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, i, f, vp, i, vp]
+    L.fa_fwd_softcap.restype = i
+    L.fa_bwd_softcap.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, f, vp, i,
+                                 vp, sz, vp]
+    L.fa_bwd_softcap.restype = i
+    L.fa_bwd_softcap_stage.argtypes = [i] + L.fa_bwd_softcap.argtypes
+    L.fa_bwd_softcap_stage.restype = i
     L.fa_fwd_fp8.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp, f, f, f, i, vp]
     L.fa_fwd_fp8.restype = i
     L.fa_fwd_kvcache.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, i, i, vp, sz, vp]
@@ -135,6 +142,26 @@ def fa_bwd_window_stage(stage, q, k, v, o, dout, lse, dq, dk, dv, B, Hq, Hkv, N,
     return lib.fa_bwd_window_stage(stage, q, k, v, o, dout, lse, dq, dk, dv, B, Hq, Hkv, N, d,
                                    scale, window_left, window_right, cu_seqlens, dtype, workspace,
                                    workspace_bytes, stream)
+
+
+def fa_fwd_softcap(q, k, v, o, lse, B, Hq, Hkv, N, d, scale, causal, softcap, cu_seqlens, dtype,
+                   stream) -> int:
+    return lib.fa_fwd_softcap(q, k, v, o, lse, B, Hq, Hkv, N, d, scale, causal, softcap,
+                              cu_seqlens, dtype, stream)
+
+
+def fa_bwd_softcap(q, k, v, o, dout, lse, dq, dk, dv, B, Hq, Hkv, N, d, scale, causal, softcap,
+                   cu_seqlens, dtype, workspace, workspace_bytes, stream) -> int:
+    return lib.fa_bwd_softcap(q, k, v, o, dout, lse, dq, dk, dv, B, Hq, Hkv, N, d, scale, causal,
+                              softcap, cu_seqlens, dtype, workspace, workspace_bytes, stream)
+
+
+def fa_bwd_softcap_stage(stage, q, k, v, o, dout, lse, dq, dk, dv, B, Hq, Hkv, N, d, scale,
+                         causal, softcap, cu_seqlens, dtype, workspace, workspace_bytes,
+                         stream) -> int:
+    return lib.fa_bwd_softcap_stage(stage, q, k, v, o, dout, lse, dq, dk, dv, B, Hq, Hkv, N, d,
+                                    scale, causal, softcap, cu_seqlens, dtype, workspace,
+                                    workspace_bytes, stream)
 
 
 def fa_fwd_fp8(q, k, v, o, lse, B, Hq, Hkv, N, d, scale, causal, cu_seqlens, descale_q,
@@ -236,11 +263,12 @@ def _window(causal, window_size):
 
 
 def flash_attn_func(q, k, v, causal=False, softmax_scale=None, cu_seqlens=None, max_seqlen=None,
-                    dropout_p=0.0, window_size=(-1, -1)):
+                    dropout_p=0.0, window_size=(-1, -1), softcap=0.0):
     """Forward. Returns (o, lse); lse is float32 [Hq, T] (natural log).
 
     window_size = (left, right): query i sees keys i − left .. i + right of its
-    sequence (−1: unbounded); with causal the right side is 0."""
+    sequence (−1: unbounded); with causal the right side is 0.
+    softcap = c > 0: logits c·tanh(scale·q·k / c) (not combined with a window)."""
     import torch
     if dropout_p != 0.0:
         raise NotImplementedError("dropout is not implemented (dropout_p must be 0.0)")
@@ -259,6 +287,15 @@ def flash_attn_func(q, k, v, causal=False, softmax_scale=None, cu_seqlens=None, 
     lse = torch.empty((Hq, T), dtype=torch.float32, device=q.device)
     cu = cu_seqlens.data_ptr() if cu_seqlens is not None else None
     w = _window(causal, window_size)
+    if softcap:
+        if w is not None:
+            raise NotImplementedError("softcap with a sliding window is not implemented")
+        st = lib.fa_fwd_softcap(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                                lse.data_ptr(), B, Hq, Hkv, N, d, float(scale),
+                                int(bool(causal)), float(softcap), cu, _dtype_code(q), _stream())
+        if st != FA_OK:
+            raise FaError(st, "fa_fwd_softcap")
+        return o, lse
     if w is None:
         st = lib.fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
                         B, Hq, Hkv, N, d, float(scale), int(bool(causal)), cu, _dtype_code(q),
@@ -303,8 +340,9 @@ def flash_attn_func_fp8(q, k, v, descale_q=1.0, descale_k=1.0, descale_v=1.0, ca
 
 
 def flash_attn_backward(dout, q, k, v, o, lse, causal=False, softmax_scale=None, cu_seqlens=None,
-                        max_seqlen=None, workspace=None, window_size=(-1, -1)):
-    """Backward. Returns (dq, dk, dv) shaped like q, k, v (window_size as in the forward)."""
+                        max_seqlen=None, workspace=None, window_size=(-1, -1), softcap=0.0):
+    """Backward. Returns (dq, dk, dv) shaped like q, k, v (window_size and softcap as in
+    the forward, which produced o and lse)."""
     import torch
     B, N, T, Hq, Hkv, d = _shape(q, k, cu_seqlens, max_seqlen)
     _check_dev(dout, q, k, v, o, lse)
@@ -319,6 +357,15 @@ def flash_attn_backward(dout, q, k, v, o, lse, causal=False, softmax_scale=None,
     w = _window(causal, window_size)
     ptrs = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(),
             lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr())
+    if softcap:
+        if w is not None:
+            raise NotImplementedError("softcap with a sliding window is not implemented")
+        st = lib.fa_bwd_softcap(*ptrs, B, Hq, Hkv, N, d, float(scale), int(bool(causal)),
+                                float(softcap), cu, _dtype_code(q), workspace.data_ptr(),
+                                workspace.numel(), _stream())
+        if st != FA_OK:
+            raise FaError(st, "fa_bwd_softcap")
+        return dq, dk, dv
     if w is None:
         st = lib.fa_bwd(*ptrs, B, Hq, Hkv, N, d, float(scale), int(bool(causal)), cu,
                         _dtype_code(q), workspace.data_ptr(), workspace.numel(), _stream())

@@ -51,11 +51,28 @@ int window_mode(int left, int right, int N, int* mask, int* wl, int* wr) {
   return FA_OK;
 }
 
+// A soft cap c: 0 = none; otherwise finite and > 0, with scale / c finite, and
+// only with the unmasked or causal mask at d <= 128. Sets the kernels' two
+// constants (scale / c and c·log2 e). Returns FA_OK or the status to report.
+int cap_constants(float softcap, float scale, int mask, int d, float* cap_in, float* cap_out) {
+  *cap_in = *cap_out = 0.f;
+  if (softcap == 0.f) return FA_OK;
+  if (!std::isfinite(softcap) || !(softcap > 0.f)) return FA_ERR_INVALID_ARG;
+  *cap_in = scale / softcap;
+  *cap_out = softcap * kLog2e;
+  if (!std::isfinite(*cap_in) || !std::isfinite(*cap_out)) return FA_ERR_INVALID_ARG;
+  if (mask == fa::kMaskWindow || d > 128) return FA_ERR_UNSUPPORTED;
+  return FA_OK;
+}
+
 int fwd_common(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq,
                int Hkv, int N, int d, float scale, int mask, int wl, int wr,
-               const int32_t* cu_seqlens, int dtype, hipStream_t stream) {
+               const int32_t* cu_seqlens, int dtype, hipStream_t stream, float softcap = 0.f) {
   bool noop;
   int st = check_sizes(B, Hq, Hkv, N, d, scale, 0, dtype, &noop, 256);
+  if (st != FA_OK) return st;
+  float cap_in, cap_out;
+  st = cap_constants(softcap, scale, mask, d, &cap_in, &cap_out);
   if (st != FA_OK || noop) return st;
   if (!q || !k || !v || !o || !lse) return FA_ERR_INVALID_ARG;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse))
@@ -77,8 +94,11 @@ int fwd_common(const void* q, const void* k, const void* v, void* o, float* lse,
   a.scale_log2 = scale * kLog2e;
   a.wl = wl;
   a.wr = wr;
+  a.cap_in = cap_in;
+  a.cap_out = cap_out;
   if ((int64_t)a.n_qtiles * Hq * B >= (int64_t)1 << 31) return FA_ERR_UNSUPPORTED;
-  hipError_t e = fa::launch_fwd(a, dtype == FA_BF16, d, mask, cu_seqlens != nullptr, stream);
+  hipError_t e = fa::launch_fwd(a, dtype == FA_BF16, d, mask, cu_seqlens != nullptr,
+                                softcap != 0.f, stream);
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
@@ -92,6 +112,15 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int
   if (causal != 0 && causal != 1) return FA_ERR_INVALID_ARG;
   return fwd_common(q, k, v, o, lse, B, Hq, Hkv, N, d, scale,
                     causal ? fa::kMaskCausal : fa::kMaskNone, 0, 0, cu_seqlens, dtype, stream);
+}
+
+int fa_fwd_softcap(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                   int Hq, int Hkv, int N, int d, float scale, int causal, float softcap,
+                   const int32_t* cu_seqlens, int dtype, hipStream_t stream) {
+  if (causal != 0 && causal != 1) return FA_ERR_INVALID_ARG;
+  return fwd_common(q, k, v, o, lse, B, Hq, Hkv, N, d, scale,
+                    causal ? fa::kMaskCausal : fa::kMaskNone, 0, 0, cu_seqlens, dtype, stream,
+                    softcap);
 }
 
 int fa_fwd_window(const void* q, const void* k, const void* v, void* o, float* lse, int B,
@@ -158,9 +187,12 @@ int bwd_common(int stage, const void* q, const void* k, const void* v, const voi
                const void* dout, const float* lse, void* dq, void* dk, void* dv, int B, int Hq,
                int Hkv, int N, int d, float scale, int mask, int wl, int wr,
                const int32_t* cu_seqlens, int dtype, void* workspace, size_t workspace_bytes,
-               hipStream_t stream) {
+               hipStream_t stream, float softcap = 0.f) {
   bool noop;
   int st = check_sizes(B, Hq, Hkv, N, d, scale, 0, dtype, &noop);
+  if (st != FA_OK) return st;
+  float cap_in, cap_out;
+  st = cap_constants(softcap, scale, mask, d, &cap_in, &cap_out);
   if (st != FA_OK || noop) return st;
   if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv) return FA_ERR_INVALID_ARG;
   const void* ptrs[] = {q, k, v, o, dout, lse, dq, dk, dv, workspace};
@@ -191,8 +223,10 @@ int bwd_common(int stage, const void* q, const void* k, const void* v, const voi
   a.scale_log2 = scale * kLog2e;
   a.wl = wl;
   a.wr = wr;
-  hipError_t e = fa::launch_bwd(a, dtype == FA_BF16, d, mask, cu_seqlens != nullptr, stage,
-                                stream);
+  a.cap_in = cap_in;
+  a.cap_out = cap_out;
+  hipError_t e = fa::launch_bwd(a, dtype == FA_BF16, d, mask, cu_seqlens != nullptr,
+                                softcap != 0.f, stage, stream);
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
@@ -229,6 +263,27 @@ int fa_bwd_window_stage(int stage, const void* q, const void* k, const void* v, 
   if (st != FA_OK) return st;
   return bwd_common(stage, q, k, v, o, dout, lse, dq, dk, dv, B, Hq, Hkv, N, d, scale, mask, wl,
                     wr, cu_seqlens, dtype, workspace, workspace_bytes, stream);
+}
+
+int fa_bwd_softcap(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                   const float* lse, void* dq, void* dk, void* dv, int B, int Hq, int Hkv, int N,
+                   int d, float scale, int causal, float softcap, const int32_t* cu_seqlens,
+                   int dtype, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  return fa_bwd_softcap_stage(-1, q, k, v, o, dout, lse, dq, dk, dv, B, Hq, Hkv, N, d, scale,
+                              causal, softcap, cu_seqlens, dtype, workspace, workspace_bytes,
+                              stream);
+}
+
+int fa_bwd_softcap_stage(int stage, const void* q, const void* k, const void* v, const void* o,
+                         const void* dout, const float* lse, void* dq, void* dk, void* dv, int B,
+                         int Hq, int Hkv, int N, int d, float scale, int causal, float softcap,
+                         const int32_t* cu_seqlens, int dtype, void* workspace,
+                         size_t workspace_bytes, hipStream_t stream) {
+  if (stage < -1 || stage >= fa::bwd_num_stages()) return FA_ERR_INVALID_ARG;
+  if (causal != 0 && causal != 1) return FA_ERR_INVALID_ARG;
+  return bwd_common(stage, q, k, v, o, dout, lse, dq, dk, dv, B, Hq, Hkv, N, d, scale,
+                    causal ? fa::kMaskCausal : fa::kMaskNone, 0, 0, cu_seqlens, dtype, workspace,
+                    workspace_bytes, stream, softcap);
 }
 
 int fa_bwd_num_stages(void) { return fa::bwd_num_stages(); }

@@ -139,12 +139,14 @@ constexpr int kDkvKK = kDkvQ / 16;   // 16-query MFMA k-steps per tile
 // Producer: P and dS of one 64-query tile for 32 keys, written to `xp`
 // (P) and `xs` (dS) as MFMA B operands, [k-step][lane]. EDGE tiles zero P
 // and dS for queries past the end and, causally, for keys after the query.
-template <typename T, int D, bool CAUSAL, bool EDGE, bool WIN>
+// CAP: soft-capped logits, s = cap_out·tanh(z·cap_in) in log2 units; dS then
+// carries the derivative factor 1 − tanh² (the scale is applied at the end).
+template <typename T, int D, bool CAUSAL, bool EDGE, bool WIN, bool CAP = false>
 __device__ __forceinline__ void dkdv_produce(const T* qt_, const T* dot_, const float* ld,
                                              const u32x4 (&kf)[D / 16],
                                              const u32x4 (&vf)[D / 16], u32x4* xp, u32x4* xs,
                                              float c, int q0, int L, int key, int wl, int wr,
-                                             int lane) {
+                                             int lane, float cap_in = 0.f, float cap_out = 0.f) {
   constexpr int NKB = D / 16;
   constexpr int NQB = kDkvQ / 32;
   const int col = lane & 31, half = lane >> 5;
@@ -182,8 +184,15 @@ __device__ __forceinline__ void dkdv_produce(const T* qt_, const T* dot_, const 
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
         const int i4 = 4 * rr + t;
-        float p = fast_exp2(fmaf(s[i4], c, -lsev[t]));
-        float ds = p * (dp[i4] - dlv[t]);
+        float p, ds;
+        if constexpr (CAP) {
+          const float th = tanh_fast(s[i4] * cap_in);
+          p = fast_exp2(fmaf(th, cap_out, -lsev[t]));
+          ds = p * (dp[i4] - dlv[t]) * fmaf(-th, th, 1.f);
+        } else {
+          p = fast_exp2(fmaf(s[i4], c, -lsev[t]));
+          ds = p * (dp[i4] - dlv[t]);
+        }
         if constexpr (EDGE) {
           const int q = q0 + qoff + t;
           bool keep = q < L && !(CAUSAL && key > q);
@@ -204,7 +213,7 @@ __device__ __forceinline__ void dkdv_produce(const T* qt_, const T* dot_, const 
 }
 
 // WIN: sliding window (see fwd_kernel); CAUSAL is false then
-template <typename T, int D, bool CAUSAL, bool VARLEN, bool WIN>
+template <typename T, int D, bool CAUSAL, bool VARLEN, bool WIN, bool CAP = false>
 __global__ __launch_bounds__(kDkvThreads, 1) void dkdv_kernel(BwdArgs a, int n_ktiles) {
   constexpr int NKB = D / 16;
   constexpr int NCB = D / 32;
@@ -321,11 +330,13 @@ __global__ __launch_bounds__(kDkvThreads, 1) void dkdv_kernel(BwdArgs a, int n_k
         const int st = t % kDkvStages;
         if (!pair_idle(q0)) {
           if (t < n_edge)
-            dkdv_produce<T, D, CAUSAL, true, WIN>(qd_lds[st][0], qd_lds[st][1], ld_lds[st], kf,
-                                                  vf, xp, xs, c, q0, L, key, wl, wr, lane);
+            dkdv_produce<T, D, CAUSAL, true, WIN, CAP>(qd_lds[st][0], qd_lds[st][1], ld_lds[st],
+                                                       kf, vf, xp, xs, c, q0, L, key, wl, wr,
+                                                       lane, a.cap_in, a.cap_out);
           else
-            dkdv_produce<T, D, CAUSAL, false, WIN>(qd_lds[st][0], qd_lds[st][1], ld_lds[st], kf,
-                                                   vf, xp, xs, c, q0, L, key, wl, wr, lane);
+            dkdv_produce<T, D, CAUSAL, false, WIN, CAP>(qd_lds[st][0], qd_lds[st][1], ld_lds[st],
+                                                        kf, vf, xp, xs, c, q0, L, key, wl, wr,
+                                                        lane, a.cap_in, a.cap_out);
         }
       }
     }
@@ -431,11 +442,13 @@ constexpr int kDqK = 64;    // keys per tile
 // dSᵀ = P∘(dP − D) with P = exp2(S·c − LSE·log2 e), then dQᵀ += Kᵀ·dSᵀ.
 // EDGE tiles zero P for keys past the end and, causally, for keys after the
 // query.
-template <typename T, int D, bool CAUSAL, bool EDGE, bool WIN>
+// CAP as in dkdv_produce
+template <typename T, int D, bool CAUSAL, bool EDGE, bool WIN, bool CAP = false>
 __device__ __forceinline__ void dq_tile(const T* kt, const T* vt, const u32x4 (&qf)[D / 16],
                                         const u32x4 (&df)[D / 16], f32x16 (&dqt)[D / 32], float c,
                                         float lse2, float dl, int kv0, int L, int qrow, int wl,
-                                        int wr, int lane) {
+                                        int wr, int lane, float cap_in = 0.f,
+                                        float cap_out = 0.f) {
   constexpr int NKB = D / 16;
   constexpr int NCB = D / 32;
   constexpr int NJB = kDqK / 32;
@@ -461,14 +474,22 @@ __device__ __forceinline__ void dq_tile(const T* kt, const T* vt, const u32x4 (&
     }
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      float p = fast_exp2(fmaf(s[i], c, -lse2));
+      float p, g = 1.f;
+      if constexpr (CAP) {
+        const float th = tanh_fast(s[i] * cap_in);
+        p = fast_exp2(fmaf(th, cap_out, -lse2));
+        g = fmaf(-th, th, 1.f);
+      } else {
+        p = fast_exp2(fmaf(s[i], c, -lse2));
+      }
       if constexpr (EDGE) {
         const int kj = kv0 + jb * 32 + 8 * (i >> 2) + 4 * half + (i & 3);
         bool vis = kj < L && !(CAUSAL && kj > qrow);
         if constexpr (WIN) vis = vis && kj >= qrow - wl && kj <= qrow + wr;
         p = vis ? p : 0.f;
       }
-      dp[i] = p * (dp[i] - dl);
+      if constexpr (CAP) dp[i] = p * (dp[i] - dl) * g;
+      else dp[i] = p * (dp[i] - dl);
     }
     if (jb + 1 < NJB) {
 #pragma unroll
@@ -485,7 +506,7 @@ __device__ __forceinline__ void dq_tile(const T* kt, const T* vt, const u32x4 (&
   }
 }
 
-template <typename T, int D, bool CAUSAL, bool VARLEN, bool WIN>
+template <typename T, int D, bool CAUSAL, bool VARLEN, bool WIN, bool CAP = false>
 __global__ __launch_bounds__(kThreads, 2) void dq_kernel(BwdArgs a, int n_qtiles) {
   constexpr int NKB = D / 16;
   constexpr int NCB = D / 32;
@@ -580,7 +601,8 @@ __global__ __launch_bounds__(kThreads, 2) void dq_kernel(BwdArgs a, int n_qtiles
     if (EDGE && CAUSAL && kv0 > wq_last) return;   // every key after this wave's queries
     if (EDGE && WIN && (kv0 > wq_last + wr || kv0 + kDqK - 1 < wq_first - wl))
       return;   // the tile lies outside the windows of all this wave's queries
-    dq_tile<T, D, CAUSAL, EDGE, WIN>(kt, vt, qf, df, dqt, c, lse2, dl, kv0, L, qrow, wl, wr, lane);
+    dq_tile<T, D, CAUSAL, EDGE, WIN, CAP>(kt, vt, qf, df, dqt, c, lse2, dl, kv0, L, qrow, wl, wr,
+                                          lane, a.cap_in, a.cap_out);
   };
   using B0 = std::integral_constant<int, 0>;
   using B1 = std::integral_constant<int, 1>;
@@ -616,7 +638,7 @@ __global__ __launch_bounds__(kThreads, 2) void dq_kernel(BwdArgs a, int n_qtiles
   }
 }
 
-template <typename T, int D, bool CAUSAL, bool VARLEN, bool WIN>
+template <typename T, int D, bool CAUSAL, bool VARLEN, bool WIN, bool CAP = false>
 hipError_t launch(const BwdArgs& a, int stage, hipStream_t s) {
   (void)hipGetLastError();  // drop an error left pending by earlier, unrelated HIP calls
   if (stage < 0 || stage == 0) {
@@ -629,14 +651,14 @@ hipError_t launch(const BwdArgs& a, int stage, hipStream_t s) {
   }
   if (stage < 0 || stage == 1) {
     const int nkt = (a.N + kDkvKeys - 1) / kDkvKeys;
-    hipLaunchKernelGGL((dkdv_kernel<T, D, CAUSAL, VARLEN, WIN>), dim3(nkt * a.Hkv * a.B),
+    hipLaunchKernelGGL((dkdv_kernel<T, D, CAUSAL, VARLEN, WIN, CAP>), dim3(nkt * a.Hkv * a.B),
                        dim3(kDkvThreads), 0, s, a, nkt);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   if (stage < 0 || stage == 2) {
     const int nqt = (a.N + kDqQ - 1) / kDqQ;
-    hipLaunchKernelGGL((dq_kernel<T, D, CAUSAL, VARLEN, WIN>), dim3(nqt * a.Hq * a.B),
+    hipLaunchKernelGGL((dq_kernel<T, D, CAUSAL, VARLEN, WIN, CAP>), dim3(nqt * a.Hq * a.B),
                        dim3(kThreads), 0, s, a, nqt);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -645,7 +667,15 @@ hipError_t launch(const BwdArgs& a, int stage, hipStream_t s) {
 }
 
 template <typename T, int D>
-hipError_t dispatch_mask(const BwdArgs& a, int mask, bool varlen, int stage, hipStream_t s) {
+hipError_t dispatch_mask(const BwdArgs& a, int mask, bool varlen, bool cap, int stage,
+                         hipStream_t s) {
+  if (cap) {   // soft cap: no window (checked by the caller)
+    if (mask == kMaskCausal)
+      return varlen ? launch<T, D, true, true, false, true>(a, stage, s)
+                    : launch<T, D, true, false, false, true>(a, stage, s);
+    return varlen ? launch<T, D, false, true, false, true>(a, stage, s)
+                  : launch<T, D, false, false, false, true>(a, stage, s);
+  }
   if (mask == kMaskWindow)
     return varlen ? launch<T, D, false, true, true>(a, stage, s)
                   : launch<T, D, false, false, true>(a, stage, s);
@@ -660,13 +690,13 @@ hipError_t dispatch_mask(const BwdArgs& a, int mask, bool varlen, int stage, hip
 
 int bwd_num_stages() { return 3; }
 
-hipError_t launch_bwd(const BwdArgs& a, bool bf16_in, int d, int mask, bool varlen, int stage,
-                      hipStream_t s) {
+hipError_t launch_bwd(const BwdArgs& a, bool bf16_in, int d, int mask, bool varlen, bool cap,
+                      int stage, hipStream_t s) {
   if (bf16_in)
-    return d == 64 ? dispatch_mask<bf16, 64>(a, mask, varlen, stage, s)
-                   : dispatch_mask<bf16, 128>(a, mask, varlen, stage, s);
-  return d == 64 ? dispatch_mask<f16, 64>(a, mask, varlen, stage, s)
-                 : dispatch_mask<f16, 128>(a, mask, varlen, stage, s);
+    return d == 64 ? dispatch_mask<bf16, 64>(a, mask, varlen, cap, stage, s)
+                   : dispatch_mask<bf16, 128>(a, mask, varlen, cap, stage, s);
+  return d == 64 ? dispatch_mask<f16, 64>(a, mask, varlen, cap, stage, s)
+                 : dispatch_mask<f16, 128>(a, mask, varlen, cap, stage, s);
 }
 
 }  // namespace fa

@@ -99,6 +99,12 @@ __device__ __forceinline__ float wave_sum_halves(float x) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// tanh(x) = 1 − 2 / (1 + e^(2x)) from the exponential and reciprocal units:
+// exactly ±1 once e^(2x) overflows or vanishes, absolute error ≈1e-7 near 0.
+__device__ __forceinline__ float tanh_fast(float x) {
+  return 1.f - 2.f * __builtin_amdgcn_rcpf(1.f + fast_exp2(x * (2.f * kLog2e)));
+}
+
 // Hardware places workgroup w on XCD w % 8 (8 XCDs, each with its own L2).
 // Return a logical id so that each XCD receives one contiguous range of
 // logical ids; consecutive logical ids then share K/V tiles within one L2.

@@ -39,12 +39,13 @@ constexpr float kRescaleHeadroom = 8.f;  // log2 of the largest P before the max
 
 // One 64-key tile for one wave's 32 query rows: Sᵀ = K·Qᵀ, online softmax
 // with a lazily raised reference max, Oᵀ += Vᵀ·Pᵀ. EDGE tiles mask keys past
-// the sequence end and, causally, keys after the query.
-template <typename T, int D, bool CAUSAL, bool EDGE, bool WIN>
+// the sequence end and, causally, keys after the query. CAP: the logits
+// are soft-capped, s = c_out·tanh(z·c_in) in log2 units (then c is 1).
+template <typename T, int D, bool CAUSAL, bool EDGE, bool WIN, bool CAP = false>
 __device__ __forceinline__ void fwd_tile(const T* kt, const T* vt, const u32x4 (&qf)[D / 16],
                                          f32x16 (&o)[D / 32], float& mc, float& l, float& lr,
                                          float c, int kv0, int L, int qrow, int wl, int wr,
-                                         int lane) {
+                                         int lane, float cap_in = 0.f, float cap_out = 0.f) {
   constexpr int NKB = D / 16;
   constexpr int NCB = D / 32;
   const int col = lane & 31, half = lane >> 5;
@@ -55,6 +56,12 @@ __device__ __forceinline__ void fwd_tile(const T* kt, const T* vt, const u32x4 (
 #pragma unroll
     for (int jb = 0; jb < 2; ++jb)
       s[jb] = mfma32<T>(lds_row16<T, D>(kt, jb * 32 + col, 2 * kb + half), qf[kb], s[jb]);
+  }
+  if constexpr (CAP) {
+#pragma unroll
+    for (int jb = 0; jb < 2; ++jb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) s[jb][i] = cap_out * tanh_fast(s[jb][i] * cap_in);
   }
 
   // ---- mask: keys past the sequence end, keys after the query (causal) ---
@@ -118,7 +125,7 @@ __device__ __forceinline__ void fwd_tile(const T* kt, const T* vt, const u32x4 (
 
 // WIN: sliding window, key j visible from query i iff i − a.wl ≤ j ≤ i + a.wr
 // (bounds clamped to N by the caller; CAUSAL is false then)
-template <typename T, int D, bool CAUSAL, bool VARLEN, bool WIN>
+template <typename T, int D, bool CAUSAL, bool VARLEN, bool WIN, bool CAP = false>
 // two workgroups per CU up to d = 128; at d = 256 the O accumulators alone
 // take 128 registers and the kernel runs one workgroup per CU
 __global__ __launch_bounds__(kThreads, D <= 128 ? 2 : 1) void fwd_kernel(FwdArgs a) {
@@ -201,7 +208,8 @@ __global__ __launch_bounds__(kThreads, D <= 128 ? 2 : 1) void fwd_kernel(FwdArgs
   f32x16 o[NCB];
 #pragma unroll
   for (int cb = 0; cb < NCB; ++cb) o[cb] = f32x16{};
-  const float c = a.scale_log2;
+  const float c = CAP ? 1.f : a.scale_log2;   // capped logits are already in log2 units
+  const float cap_in = CAP ? a.cap_in : 0.f, cap_out = CAP ? a.cap_out : 0.f;
   float mc = -INFINITY;   // reference max of S·c for this row
   float l = 0.f;          // Σ P over this lane half's keys (fp32), for the LSE (bf16)
   float lr = 0.f;         // the same sum of P rounded to T, for normalising O
@@ -233,8 +241,8 @@ __global__ __launch_bounds__(kThreads, D <= 128 ? 2 : 1) void fwd_kernel(FwdArgs
     if (EDGE && CAUSAL && kv0 > wq_last) return;  // every key of the tile is after this wave's rows
     if (EDGE && WIN && (kv0 > wq_last + wr || kv0 + kBC - 1 < wq_first - wl))
       return;   // the tile lies outside the windows of all this wave's rows
-    fwd_tile<T, D, CAUSAL, EDGE, WIN>(lds[BUF][0], lds[BUF][1], qf, o, mc, l, lr, c, kv0, L, qrow,
-                                      wl, wr, lane);
+    fwd_tile<T, D, CAUSAL, EDGE, WIN, CAP>(lds[BUF][0], lds[BUF][1], qf, o, mc, l, lr, c, kv0,
+                                           L, qrow, wl, wr, lane, cap_in, cap_out);
   };
   using B0 = std::integral_constant<int, 0>;
   using B1 = std::integral_constant<int, 1>;
@@ -274,17 +282,26 @@ __global__ __launch_bounds__(kThreads, D <= 128 ? 2 : 1) void fwd_kernel(FwdArgs
   }
 }
 
-template <typename T, int D, bool CAUSAL, bool VARLEN, bool WIN>
+template <typename T, int D, bool CAUSAL, bool VARLEN, bool WIN, bool CAP = false>
 hipError_t launch(const FwdArgs& a, hipStream_t stream) {
   const int grid = a.n_qtiles * a.Hq * a.B;
   (void)hipGetLastError();  // drop an error left pending by earlier, unrelated HIP calls
-  hipLaunchKernelGGL((fwd_kernel<T, D, CAUSAL, VARLEN, WIN>), dim3(grid), dim3(kThreads), 0,
+  hipLaunchKernelGGL((fwd_kernel<T, D, CAUSAL, VARLEN, WIN, CAP>), dim3(grid), dim3(kThreads), 0,
                      stream, a);
   return hipGetLastError();
 }
 
 template <typename T, int D>
-hipError_t dispatch_mask(const FwdArgs& a, int mask, bool varlen, hipStream_t s) {
+hipError_t dispatch_mask(const FwdArgs& a, int mask, bool varlen, bool cap, hipStream_t s) {
+  if constexpr (D <= 128) {   // soft cap: no window, d <= 128 (checked by the caller)
+    if (cap) {
+      if (mask == kMaskCausal)
+        return varlen ? launch<T, D, true, true, false, true>(a, s)
+                      : launch<T, D, true, false, false, true>(a, s);
+      return varlen ? launch<T, D, false, true, false, true>(a, s)
+                    : launch<T, D, false, false, false, true>(a, s);
+    }
+  }
   if (mask == kMaskWindow)
     return varlen ? launch<T, D, false, true, true>(a, s) : launch<T, D, false, false, true>(a, s);
   if (mask == kMaskCausal)
@@ -296,16 +313,16 @@ hipError_t dispatch_mask(const FwdArgs& a, int mask, bool varlen, hipStream_t s)
 
 int fwd_query_tile() { return kBR; }
 
-hipError_t launch_fwd(const FwdArgs& a, bool bf16_in, int d, int mask, bool varlen,
+hipError_t launch_fwd(const FwdArgs& a, bool bf16_in, int d, int mask, bool varlen, bool cap,
                       hipStream_t s) {
   if (bf16_in) {
-    if (d == 64) return dispatch_mask<bf16, 64>(a, mask, varlen, s);
-    if (d == 128) return dispatch_mask<bf16, 128>(a, mask, varlen, s);
-    return dispatch_mask<bf16, 256>(a, mask, varlen, s);
+    if (d == 64) return dispatch_mask<bf16, 64>(a, mask, varlen, cap, s);
+    if (d == 128) return dispatch_mask<bf16, 128>(a, mask, varlen, cap, s);
+    return dispatch_mask<bf16, 256>(a, mask, varlen, cap, s);
   }
-  if (d == 64) return dispatch_mask<f16, 64>(a, mask, varlen, s);
-  if (d == 128) return dispatch_mask<f16, 128>(a, mask, varlen, s);
-  return dispatch_mask<f16, 256>(a, mask, varlen, s);
+  if (d == 64) return dispatch_mask<f16, 64>(a, mask, varlen, cap, s);
+  if (d == 128) return dispatch_mask<f16, 128>(a, mask, varlen, cap, s);
+  return dispatch_mask<f16, 256>(a, mask, varlen, cap, s);
 }
 
 }  // namespace fa

@@ -22,6 +22,7 @@ struct FwdArgs {
   int n_qtiles;               // ceil(N / query tile)
   float scale_log2;           // scale · log2(e)
   int wl, wr;                 // window bounds (kMaskWindow only)
+  float cap_in, cap_out;      // soft cap c: scale / c and c · log2(e) (softcap kernels only)
 };
 
 // FP8 forward: q, k, v hold e4m3fn codes; scale_log2 already includes both
@@ -50,6 +51,7 @@ struct BwdArgs {
   float scale;
   float scale_log2;
   int wl, wr;                 // window bounds (kMaskWindow only)
+  float cap_in, cap_out;      // soft cap c: scale / c and c · log2(e) (softcap kernels only)
 };
 
 struct DecodeArgs {
@@ -71,7 +73,8 @@ struct DecodeArgs {
 };
 
 int fwd_query_tile();
-hipError_t launch_fwd(const FwdArgs& a, bool bf16_in, int d, int mask, bool varlen,
+// softcap: logits c·tanh(scale·q·k / c) (mask kMaskNone or kMaskCausal, d <= 128)
+hipError_t launch_fwd(const FwdArgs& a, bool bf16_in, int d, int mask, bool varlen, bool softcap,
                       hipStream_t s);
 int fwd_fp8_query_tile();
 hipError_t launch_fwd_fp8(const Fp8FwdArgs& a, bool bf16_out, int d, bool causal, bool varlen,
@@ -79,8 +82,8 @@ hipError_t launch_fwd_fp8(const Fp8FwdArgs& a, bool bf16_out, int d, bool causal
 // stage < 0: every stage in order; otherwise only stage 0 (D = rowsum(dO∘O)),
 // 1 (dK, dV) or 2 (dQ).
 int bwd_num_stages();
-hipError_t launch_bwd(const BwdArgs& a, bool bf16_in, int d, int mask, bool varlen, int stage,
-                      hipStream_t s);
+hipError_t launch_bwd(const BwdArgs& a, bool bf16_in, int d, int mask, bool varlen, bool softcap,
+                      int stage, hipStream_t s);
 int decode_tile_keys();
 // stage < 0: both stages; 0: per-range partial results; 1: merge into o, lse.
 int decode_num_stages();

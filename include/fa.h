@@ -156,6 +156,36 @@ int fa_bwd_window_stage(int stage, const void* q, const void* k, const void* v, 
                         void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * Soft-capped logits: the forward and backward of fa_fwd / fa_bwd with every
+ * logit replaced by softcap·tanh(scale·q·k / softcap) before the softmax. The
+ * FlashAttention-2 page (blog.gitcode.com, section 2.3, adaptive soft cap)
+ * adds a soft-cap step; the formula printed there is neither bounded nor
+ * continuous at the cap, so the bounded tanh form is the reading taken. The
+ * backward applies the chain rule through it (dS is multiplied by 1 − tanh²).
+ *   softcap : 0 = no cap (the plain kernels run, bit-identical results);
+ *             otherwise finite and > 0, with scale / softcap finite
+ *             (else FA_ERR_INVALID_ARG)
+ * Causal or not, fixed length or varlen, GQA; d = 64 or 128 (d = 256 with a
+ * cap: FA_ERR_UNSUPPORTED). lse is the log-sum-exp of the capped logits; the
+ * backward needs the lse of fa_fwd_softcap with the same cap. Everything else
+ * (layouts, ownership, workspace, errors, determinism) as for fa_fwd / fa_bwd;
+ * fa_bwd_softcap_stage runs one stage (or every stage with stage −1).
+ */
+int fa_fwd_softcap(const void* q, const void* k, const void* v, void* o, float* lse,
+                   int B, int Hq, int Hkv, int N, int d, float scale, int causal, float softcap,
+                   const int32_t* cu_seqlens, int dtype, hipStream_t stream);
+int fa_bwd_softcap(const void* q, const void* k, const void* v, const void* o,
+                   const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                   int B, int Hq, int Hkv, int N, int d, float scale, int causal, float softcap,
+                   const int32_t* cu_seqlens, int dtype,
+                   void* workspace, size_t workspace_bytes, hipStream_t stream);
+int fa_bwd_softcap_stage(int stage, const void* q, const void* k, const void* v, const void* o,
+                         const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                         int B, int Hq, int Hkv, int N, int d, float scale, int causal,
+                         float softcap, const int32_t* cu_seqlens, int dtype,
+                         void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
  * FP8 forward: the forward of fa_fwd on e4m3 inputs. The pages name e4m3
  * (torch.float8_e4m3fn) as the 8-bit attention format and credit
  * FlashAttention-3 with an FP8 forward (cxbdf.cn deployment guide, section

@@ -20,12 +20,13 @@ def declared_functions():
 
 
 def test_header_declares_the_boundary():
-    assert declared_functions() == ["fa_bwd", "fa_bwd_num_stages", "fa_bwd_stage",
+    assert declared_functions() == ["fa_bwd", "fa_bwd_num_stages", "fa_bwd_softcap",
+                                    "fa_bwd_softcap_stage", "fa_bwd_stage",
                                     "fa_bwd_window", "fa_bwd_window_stage",
                                     "fa_bwd_workspace_size", "fa_fwd", "fa_fwd_fp8",
                                     "fa_fwd_kvcache",
                                     "fa_fwd_kvcache_num_stages", "fa_fwd_kvcache_stage",
-                                    "fa_fwd_kvcache_workspace_size", "fa_fwd_window",
+                                    "fa_fwd_kvcache_workspace_size", "fa_fwd_softcap", "fa_fwd_window",
                                     "fa_kvcache_num_splits", "fa_status_string"]
 
 
@@ -290,3 +291,69 @@ def test_fwd_fp8_no_device_reports_hip_error():
         pytest.skip("a GPU is present")
     assert fwd8() == fa.FA_ERR_HIP
     assert fwd8(causal=1, dtype=fa.FA_FP16) == fa.FA_ERR_HIP
+
+
+def fwdc(**kw):
+    a = dict(q=P, k=P, v=P, o=P, lse=P, B=1, Hq=2, Hkv=2, N=16, d=64, scale=0.125, causal=1,
+             cap=30.0, cu=None, dtype=fa.FA_BF16, stream=None)
+    a.update(kw)
+    return fa.fa_fwd_softcap(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["Hq"], a["Hkv"],
+                             a["N"], a["d"], a["scale"], a["causal"], a["cap"], a["cu"],
+                             a["dtype"], a["stream"])
+
+
+def bwdc(stage=None, **kw):
+    a = dict(B=1, Hq=2, Hkv=2, N=16, d=64, scale=0.125, causal=0, cap=30.0, dtype=fa.FA_FP16,
+             ws=P, wsb=1 << 20)
+    a.update(kw)
+    ptrs = [kw.get(n, P) for n in ("q", "k", "v", "o", "do", "lse", "dq", "dk", "dv")]
+    args = (*ptrs, a["B"], a["Hq"], a["Hkv"], a["N"], a["d"], a["scale"], a["causal"], a["cap"],
+            None, a["dtype"], a["ws"], a["wsb"], None)
+    if stage is None:
+        return fa.fa_bwd_softcap(*args)
+    return fa.fa_bwd_softcap_stage(stage, *args)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(cap=-1.0), fa.FA_ERR_INVALID_ARG),
+    (dict(cap=float("nan")), fa.FA_ERR_INVALID_ARG),
+    (dict(cap=float("inf")), fa.FA_ERR_INVALID_ARG),
+    (dict(cap=1e-45, scale=1.0), fa.FA_ERR_INVALID_ARG),    # scale / cap overflows
+    (dict(causal=2), fa.FA_ERR_INVALID_ARG),
+    (dict(dtype=7), fa.FA_ERR_INVALID_ARG),
+    (dict(q=None), fa.FA_ERR_INVALID_ARG),
+    (dict(o=P + 2), fa.FA_ERR_INVALID_ARG),
+    (dict(d=256), fa.FA_ERR_UNSUPPORTED),               # the capped kernels stop at d = 128
+    (dict(d=96), fa.FA_ERR_UNSUPPORTED),
+    (dict(B=0), fa.FA_OK),
+    (dict(N=0, cap=5.0), fa.FA_OK),
+])
+def test_fwd_softcap_host_checks(kw, status):
+    assert fwdc(**kw) == status
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(cap=-2.0), fa.FA_ERR_INVALID_ARG),
+    (dict(d=256), fa.FA_ERR_UNSUPPORTED),
+    (dict(ws=None), fa.FA_ERR_WORKSPACE),
+    (dict(dq=P + 8), fa.FA_ERR_INVALID_ARG),
+    (dict(causal=5), fa.FA_ERR_INVALID_ARG),
+    (dict(B=0), fa.FA_OK),
+])
+def test_bwd_softcap_host_checks(kw, status):
+    assert bwdc(**kw) == status
+
+
+def test_bwd_softcap_stage_index_checked():
+    for bad in (-2, 3):
+        assert bwdc(stage=bad) == fa.FA_ERR_INVALID_ARG
+    assert bwdc(stage=2, ws=None) == fa.FA_ERR_WORKSPACE
+
+
+def test_softcap_no_device_reports_hip_error():
+    torch = pytest.importorskip("torch")
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    assert fwdc() == fa.FA_ERR_HIP
+    assert fwdc(cap=0.0) == fa.FA_ERR_HIP      # no cap: the plain kernels
+    assert bwdc() == fa.FA_ERR_HIP

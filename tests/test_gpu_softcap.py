@@ -1,0 +1,161 @@
+"""GPU parity of the soft-capped entry points (fa_fwd_softcap, fa_bwd_softcap
+through the binding's softcap=) against the oracle's capped logits
+c·tanh(scale·q·k / c).
+
+Small shapes spanning several tiles with ragged ends, both masks, d 64/128,
+fp16 and bf16, caps from 1.5 (most logits in the curved part of tanh) to 30,
+a large softmax scale that drives tanh into saturation, varlen with GQA and
+empty or one-token sequences; softcap = 0 must run the plain kernels bit for
+bit. Tolerances are the plain path's (parity_util).
+"""
+import numpy as np
+import pytest
+
+import workloads as W
+from oracle import attention_bwd, attention_fwd
+from parity_util import bits_equal, check_grad, check_lse, check_o, host64, say, to_device
+
+pytestmark = pytest.mark.gpu
+
+CAPS = [1.5, 5.0, 30.0]
+
+
+def _fa():
+    import exact_io_aware_12_amd as fa   # raises if libfa.so is missing: no fallback
+    return fa
+
+
+def _views(w, t):
+    if w.varlen:
+        return t["q"], t["k"], t["v"], dict(cu_seqlens=t["cu_seqlens"], max_seqlen=w.N)
+    shp = (w.B, w.N)
+    return (t["q"].view(*shp, w.Hq, w.d), t["k"].view(*shp, w.Hkv, w.d),
+            t["v"].view(*shp, w.Hkv, w.d), {})
+
+
+def compare_fwd(w, cap, scale=None):
+    import torch
+    fa = _fa()
+    scale = w.scale if scale is None else scale
+    t = to_device(W.generate(w, with_grad=False), w.dtype)
+    say(f"[fa_fwd_softcap] cap={cap} scale={scale:.4g} B={w.B} Hq={w.Hq} Hkv={w.Hkv} N={w.N} "
+        f"d={w.d} {w.dtype} causal={w.causal} varlen={w.varlen}")
+    q, k, v, kw = _views(w, t)
+    o, lse = fa.flash_attn_func(q, k, v, causal=w.causal, softmax_scale=scale, softcap=cap, **kw)
+    torch.cuda.synchronize()
+    cu = t["cu_seqlens"].cpu().numpy()
+    o_ref, lse_ref = attention_fwd(host64(t["q"]), host64(t["k"]), host64(t["v"]), scale,
+                                   w.causal, cu, softcap=cap)
+    e, _, _ = check_o(host64(o.reshape(w.T, w.Hq, w.d)), o_ref, w.dtype)
+    el = check_lse(host64(lse), lse_ref)
+    say(f"   max|dO|={e:.2e} max|dLSE|={el:.2e}")
+
+
+@pytest.mark.parametrize("dtype", ["fp16", "bf16"])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("cap", CAPS)
+def test_forward(dtype, d, causal, cap):
+    compare_fwd(W.custom(B=2, Hq=2, Hkv=1, N=333, d=d, dtype=dtype, causal=causal,
+                         seed=900 + d + CAPS.index(cap)), cap)
+
+
+@pytest.mark.parametrize("N", [1, 64, 65, 700])
+def test_forward_lengths(N):
+    compare_fwd(W.custom(B=1, Hq=4, Hkv=2, N=N, d=128, dtype="bf16", causal=True, seed=910 + N),
+                5.0)
+
+
+def test_forward_saturated():
+    """scale 0.6 at d = 64: raw logits of ±20 and more, tanh at ±1 for many keys."""
+    compare_fwd(W.custom(B=1, Hq=2, Hkv=2, N=400, d=64, dtype="fp16", causal=False, seed=915),
+                3.0, scale=0.6)
+
+
+def test_forward_varlen_gqa():
+    w = W.custom(B=0, Hq=8, Hkv=2, N=0, d=128, dtype="bf16", causal=True, seed=916,
+                 lens=[300, 0, 1, 129, 64, 513])
+    compare_fwd(w, 5.0)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_zero_cap_runs_the_plain_kernels(causal):
+    import torch
+    fa = _fa()
+    w = W.custom(B=2, Hq=4, Hkv=2, N=300, d=128, dtype="fp16", causal=causal, seed=917,
+                 backward=True)
+    t = to_device(W.generate(w, with_grad=True), w.dtype)
+    q, k, v, _ = _views(w, t)
+    do = t["do"].view(q.shape)
+    o1, l1 = fa.flash_attn_func(q, k, v, causal=causal)
+    o2, l2 = fa.flash_attn_func(q, k, v, causal=causal, softcap=0.0)
+    g1 = fa.flash_attn_backward(do, q, k, v, o1, l1, causal=causal)
+    g2 = fa.flash_attn_backward(do, q, k, v, o2, l2, causal=causal, softcap=0.0)
+    torch.cuda.synchronize()
+    assert bits_equal(o1, o2) and bits_equal(l1, l2)
+    assert all(bits_equal(a, b) for a, b in zip(g1, g2))
+
+
+# ---- backward -----------------------------------------------------------------
+def compare_bwd(w, cap, scale=None):
+    import torch
+    fa = _fa()
+    scale = w.scale if scale is None else scale
+    t = to_device(W.generate(w, with_grad=True), w.dtype)
+    say(f"[fa_bwd_softcap] cap={cap} scale={scale:.4g} B={w.B} Hq={w.Hq} Hkv={w.Hkv} N={w.N} "
+        f"d={w.d} {w.dtype} causal={w.causal} varlen={w.varlen}")
+    q, k, v, kw = _views(w, t)
+    do = t["do"].view(q.shape)
+    o, lse = fa.flash_attn_func(q, k, v, causal=w.causal, softmax_scale=scale, softcap=cap, **kw)
+    dq, dk, dv = fa.flash_attn_backward(do, q, k, v, o, lse, causal=w.causal, softmax_scale=scale,
+                                        softcap=cap, **kw)
+    torch.cuda.synchronize()
+    cu = t["cu_seqlens"].cpu().numpy()
+    ref = attention_bwd(host64(t["q"]), host64(t["k"]), host64(t["v"]), host64(t["do"]), scale,
+                        w.causal, cu, softcap=cap)
+    T = w.T
+    got = (dq.reshape(T, w.Hq, w.d), dk.reshape(T, w.Hkv, w.d), dv.reshape(T, w.Hkv, w.d))
+    res = [check_grad(host64(g), r, n) for g, r, n in zip(got, ref, ("dQ", "dK", "dV"))]
+    say("   " + " ".join(f"{n}: rel {a:.2e}" for n, (a, _) in zip(("dQ", "dK", "dV"), res)))
+
+
+@pytest.mark.parametrize("dtype", ["fp16", "bf16"])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("cap", CAPS)
+def test_backward(dtype, d, causal, cap):
+    compare_bwd(W.custom(B=2, Hq=2, Hkv=1, N=333, d=d, dtype=dtype, causal=causal,
+                         seed=920 + d + CAPS.index(cap), backward=True), cap)
+
+
+def test_backward_saturated():
+    compare_bwd(W.custom(B=1, Hq=2, Hkv=2, N=400, d=64, dtype="fp16", causal=True, seed=925,
+                         backward=True), 3.0, scale=0.6)
+
+
+def test_backward_varlen_gqa():
+    w = W.custom(B=0, Hq=8, Hkv=2, N=0, d=128, dtype="bf16", causal=True, seed=926,
+                 lens=[300, 0, 1, 129, 64, 513], backward=True)
+    compare_bwd(w, 5.0)
+
+
+def test_backward_long():
+    compare_bwd(W.custom(B=1, Hq=2, Hkv=2, N=1500, d=128, dtype="bf16", causal=True, seed=927,
+                         backward=True), 30.0)
+
+
+def test_softcap_deterministic():
+    import torch
+    fa = _fa()
+    w = W.custom(B=1, Hq=2, Hkv=2, N=600, d=128, dtype="bf16", causal=True, seed=928,
+                 backward=True)
+    t = to_device(W.generate(w, with_grad=True), w.dtype)
+    q, k, v, _ = _views(w, t)
+    do = t["do"].view(q.shape)
+    outs = []
+    for _ in range(2):
+        o, lse = fa.flash_attn_func(q, k, v, causal=True, softcap=5.0)
+        grads = fa.flash_attn_backward(do, q, k, v, o, lse, causal=True, softcap=5.0)
+        outs.append((o, lse) + tuple(grads))
+    torch.cuda.synchronize()
+    assert all(bits_equal(a, b) for a, b in zip(*outs))
