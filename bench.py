@@ -129,8 +129,11 @@ class Bound:
         self.stream = torch.cuda.current_stream().cuda_stream
 
     def _mask(self):
-        """The mask arguments: (causal,) or, for a window workload, (left, right)."""
+        """The mask arguments: (causal,), (left, right) for a window workload, or
+        (causal, softcap) for a soft-capped one."""
         w = self.w
+        if w.softcap:
+            return (int(w.causal), w.softcap)
         if w.window is None:
             return (int(w.causal),)
         wl, wr = w.window
@@ -138,6 +141,14 @@ class Bound:
 
     def fwd(self):
         w, t = self.w, self.t
+        if w.softcap:
+            st = self.fa.fa_fwd_softcap(t["q"].data_ptr(), t["k"].data_ptr(), t["v"].data_ptr(),
+                                        self.o.data_ptr(), self.lse.data_ptr(), w.B, w.Hq, w.Hkv,
+                                        w.N, w.d, w.scale, int(w.causal), w.softcap, self.cu_ptr,
+                                        self.code, self.stream)
+            if st != self.fa.FA_OK:
+                raise self.fa.FaError(st, "fa_fwd_softcap")
+            return
         fn = self.fa.fa_fwd if w.window is None else self.fa.fa_fwd_window
         st = fn(t["q"].data_ptr(), t["k"].data_ptr(), t["v"].data_ptr(), self.o.data_ptr(),
                 self.lse.data_ptr(), w.B, w.Hq, w.Hkv, w.N, w.d, w.scale, *self._mask(),
@@ -153,13 +164,16 @@ class Bound:
                 self.cu_ptr, self.code, self.ws.data_ptr(), self.ws.numel(), self.stream)
 
     def bwd(self):
-        fn = self.fa.fa_bwd if self.w.window is None else self.fa.fa_bwd_window
+        fn = (self.fa.fa_bwd_softcap if self.w.softcap else
+              self.fa.fa_bwd if self.w.window is None else self.fa.fa_bwd_window)
         st = fn(*self._bwd_args())
         if st != self.fa.FA_OK:
             raise self.fa.FaError(st, "fa_bwd")
 
     def bwd_stage(self, stage):
-        if self.w.window is None:
+        if self.w.softcap:
+            st = self.fa.fa_bwd_softcap_stage(stage, *self._bwd_args())
+        elif self.w.window is None:
             st = self.fa.fa_bwd_stage(stage, *self._bwd_args())
         else:
             st = self.fa.fa_bwd_window_stage(stage, *self._bwd_args())
@@ -234,9 +248,10 @@ def cpu_baseline(w, min_seconds=10.0, max_units=4):
     while done < max_units and (done == 0 or dt < min_seconds):
         q, k, v, do = (rng.standard_normal((L, w.d), dtype=np.float32) for _ in range(4))
         t0 = time.perf_counter()
-        O.head_fwd(q, k, v, w.scale, w.causal, window=w.window)
+        O.head_fwd(q, k, v, w.scale, w.causal, window=w.window, softcap=w.softcap or None)
         if w.backward:
-            O.head_bwd(q, k, v, do, w.scale, w.causal, window=w.window)
+            O.head_bwd(q, k, v, do, w.scale, w.causal, window=w.window,
+                       softcap=w.softcap or None)
         dt += time.perf_counter() - t0
         done += 1
     return {"value": round(done * flop_unit / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(cores),
@@ -510,10 +525,13 @@ def run_step_bench(args):
         "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms_entry, 4), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",
-        "config": {"workload": f"{w.name}: fa_fwd + fa_bwd" if w.window is None else
-                   f"{w.name}: fa_fwd_window + fa_bwd_window", "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv,
+        "config": {"workload": (f"{w.name}: fa_fwd_softcap + fa_bwd_softcap" if w.softcap else
+                                f"{w.name}: fa_fwd + fa_bwd" if w.window is None else
+                                f"{w.name}: fa_fwd_window + fa_bwd_window"),
+                   "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv,
                    "N": w.N, "d": w.d, "causal": w.causal, "seed": w.seed,
-                   **({"window": list(w.window)} if w.window is not None else {})},
+                   **({"window": list(w.window)} if w.window is not None else {}),
+                   **({"softcap": w.softcap} if w.softcap else {})},
         "pct_of_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
         "fwd_tflops": round(w.fwd_flop() / (kern["fwd_kernel"] * 1e-3) / 1e12, 2),
         "bwd_tflops": round(w.bwd_flop() / (bwd_ms * 1e-3) / 1e12, 2),
@@ -533,7 +551,8 @@ def run_sweep(args):
     names = ["tiny", "causal_d64"] + [f"sweep_N{N}_{c}" for N in (512, 1024, 2048, 4096, 8192)
                                       for c in ("full", "causal")] + ["gqa_varlen", "train_16k",
                                                                       "fwd_d256_N4096",
-                                                                      "window_16k"]
+                                                                      "window_16k",
+                                                                      "softcap_16k"]
     if args.names:
         names = args.names.split(",")
     for n in names:

@@ -44,6 +44,7 @@ class Workload:
     backward: bool = False
     lens: Optional[tuple] = None   # varlen sequence lengths
     window: Optional[tuple] = None  # sliding window (left, right), -1 = unbounded
+    softcap: float = 0.0            # soft cap c of the logits (0: none)
 
     @property
     def scale(self) -> float:
@@ -135,6 +136,10 @@ def _build() -> Dict[str, Workload]:
     # itself and the 4095 keys before it): the band mask, forward and backward
     w["window_16k"] = Workload("window_16k", B=2, Hq=16, Hkv=16, N=16384, d=128, dtype="bf16",
                                causal=False, seed=9, backward=True, window=(4095, 0))
+    # the training step's shape with soft-capped logits, c = 50 (the attention
+    # soft cap published for Gemma-2); FLOP by the same convention (tanh not counted)
+    w["softcap_16k"] = Workload("softcap_16k", B=2, Hq=16, Hkv=16, N=16384, d=128,
+                                dtype="bf16", causal=True, seed=10, backward=True, softcap=50.0)
     return w
 
 
