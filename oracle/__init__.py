@@ -16,6 +16,8 @@ Modules:
   attention   NumPy float64 forward and backward, whole tensors or sampled rows
   decode      NumPy float64 attention of new queries over a key/value cache
   bruteforce  pure-Python loops (math.exp / math.fsum) for tiny shapes
+  dropout     Philox4x32-10 keep decisions and attention with dropout on the
+              softmax weights (forward and backward)
   fp8         e4m3fn decoding, attention on decoded FP8 inputs, and the
               element-wise error bound of a forward that rounds P to e4m3
 
@@ -27,8 +29,12 @@ from .attention import (attention_fwd, attention_bwd, attention_probs,
                         attention_fwd_rows, attention_bwd_sampled)
 from .decode import kvcache_fwd, kvcache_fwd_units
 from . import bruteforce
+from .dropout import (attention_bwd_dropout, attention_fwd_dropout, keep_mask,
+                      keep_threshold, philox4x32_10)
 from .fp8 import attention_fwd_fp8, e4m3fn_decode, dequantize, head_o_bound, o_bound
 
 __all__ = ["attention_fwd", "attention_bwd", "attention_probs", "attention_fwd_rows",
            "attention_bwd_sampled", "kvcache_fwd", "kvcache_fwd_units", "bruteforce",
-           "attention_fwd_fp8", "e4m3fn_decode", "dequantize", "head_o_bound", "o_bound"]
+           "attention_fwd_fp8", "e4m3fn_decode", "dequantize", "head_o_bound", "o_bound",
+           "attention_fwd_dropout", "attention_bwd_dropout", "keep_mask", "keep_threshold",
+           "philox4x32_10"]

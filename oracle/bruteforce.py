@@ -141,3 +141,90 @@ def forward_kvcache(q, k, v, lens, scale, causal):
         o.append(ob)
         lse.append(lb)
     return o, lse
+
+
+# ---- dropout (the reading of oracle/dropout.py), written separately ------------
+_M32 = 0xFFFFFFFF
+
+
+def philox4x32_10(c0, c1, c2, c3, k0, k1):
+    """Philox4x32-10 on Python ints (Salmon et al., SC '11): ten rounds of two
+    32 x 32 -> 64-bit products, key bumped by the Weyl constants in between."""
+    for r in range(10):
+        if r:
+            k0 = (k0 + 0x9E3779B9) & _M32
+            k1 = (k1 + 0xBB67AE85) & _M32
+        p0 = 0xD2511F53 * c0
+        p1 = 0xCD9E8D57 * c2
+        c0, c1, c2, c3 = ((p1 >> 32) ^ c1 ^ k0, p1 & _M32, (p0 >> 32) ^ c3 ^ k1, p0 & _M32)
+    return c0, c1, c2, c3
+
+
+def _kept(seed, seq, head, i, j, t):
+    words = philox4x32_10(j // 4, i // 4, head, seq, seed & _M32, seed >> 32)
+    return ((words[i % 4] >> (8 * (j % 4))) & 0xFF) < t
+
+
+def forward_dropout(q, k, v, scale, causal, seqs, t, seed):
+    """O and LSE with dropout on the softmax weights (keep iff byte < t, kept
+    weights scaled by 256/t)."""
+    Hq, Hkv = len(q[0]), len(k[0])
+    grp = Hq // Hkv
+    dv = len(v[0][0])
+    o = [[None] * Hq for _ in q]
+    lse = [[None] * len(q) for _ in range(Hq)]
+    for sidx, (a, b) in enumerate(seqs):
+        L = b - a
+        for h in range(Hq):
+            g = h // grp
+            for i in range(L):
+                js = list(_visible(i, L, causal))
+                s = [scale * _dot(q[a + i][h], k[a + j][g]) for j in js]
+                m = max(s)
+                lsum = math.log(math.fsum(math.exp(x - m) for x in s)) + m
+                z = [256.0 / t if _kept(seed, sidx, h, i, j, t) else 0.0 for j in js]
+                p = [math.exp(x - lsum) * zz for x, zz in zip(s, z)]
+                o[a + i][h] = [math.fsum(p[n] * v[a + j][g][c] for n, j in enumerate(js))
+                               for c in range(dv)]
+                lse[h][a + i] = lsum
+    return o, lse
+
+
+def backward_dropout(q, k, v, do, scale, causal, seqs, t, seed):
+    Hq, Hkv = len(q[0]), len(k[0])
+    grp = Hq // Hkv
+    d = len(q[0][0])
+    dv_ = len(v[0][0])
+    dq = [[[0.0] * d for _ in range(Hq)] for _ in q]
+    dk = [[[0.0] * d for _ in range(Hkv)] for _ in k]
+    dvv = [[[0.0] * dv_ for _ in range(Hkv)] for _ in v]
+    for sidx, (a, b) in enumerate(seqs):
+        L = b - a
+        for h in range(Hq):
+            g = h // grp
+            P = [[0.0] * L for _ in range(L)]
+            Z = [[0.0] * L for _ in range(L)]
+            dP = [[0.0] * L for _ in range(L)]
+            for i in range(L):
+                js = list(_visible(i, L, causal))
+                s = [scale * _dot(q[a + i][h], k[a + j][g]) for j in js]
+                m = max(s)
+                lsum = math.log(math.fsum(math.exp(x - m) for x in s)) + m
+                for n, j in enumerate(js):
+                    P[i][j] = math.exp(s[n] - lsum)
+                    Z[i][j] = 256.0 / t if _kept(seed, sidx, h, i, j, t) else 0.0
+                    dP[i][j] = _dot(do[a + i][h], v[a + j][g])
+            D = [math.fsum(P[i][j] * Z[i][j] * dP[i][j] for j in range(L)) for i in range(L)]
+            dS = [[P[i][j] * (Z[i][j] * dP[i][j] - D[i]) for j in range(L)] for i in range(L)]
+            for i in range(L):
+                for c in range(d):
+                    dq[a + i][h][c] = scale * math.fsum(dS[i][j] * k[a + j][g][c]
+                                                        for j in range(L))
+            for j in range(L):
+                for c in range(d):
+                    dk[a + j][g][c] += scale * math.fsum(dS[i][j] * q[a + i][h][c]
+                                                         for i in range(L))
+                for c in range(dv_):
+                    dvv[a + j][g][c] += math.fsum(P[i][j] * Z[i][j] * do[a + i][h][c]
+                                                  for i in range(L))
+    return dq, dk, dvv
