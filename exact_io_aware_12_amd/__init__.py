@@ -7,14 +7,21 @@ fallback implementation.
 
 Raw entry points with the C names and arguments (pointers as ints):
     fa_fwd, fa_bwd, fa_bwd_stage, fa_bwd_num_stages, fa_bwd_workspace_size,
+    fa_fwd_window, fa_bwd_window, fa_bwd_window_stage,
+    fa_fwd_softcap, fa_bwd_softcap, fa_bwd_softcap_stage,
+    fa_fwd_dropout, fa_bwd_dropout, fa_bwd_dropout_stage, fa_fwd_fp8,
     fa_fwd_kvcache, fa_fwd_kvcache_stage, fa_fwd_kvcache_num_stages,
     fa_kvcache_num_splits, fa_fwd_kvcache_workspace_size,
     fa_status_string
 Tensor-level helpers:
     flash_attn_func(q, k, v, causal=False, softmax_scale=None,
-                    cu_seqlens=None, max_seqlen=None, dropout_p=0.0) -> (o, lse)
+                    cu_seqlens=None, max_seqlen=None, dropout_p=0.0,
+                    window_size=(-1, -1), softcap=0.0, dropout_seed=None) -> (o, lse)
     flash_attn_backward(dout, q, k, v, o, lse, causal=False, softmax_scale=None,
-                        cu_seqlens=None, max_seqlen=None) -> (dq, dk, dv)
+                        cu_seqlens=None, max_seqlen=None, workspace=None,
+                        window_size=(-1, -1), softcap=0.0, dropout_p=0.0,
+                        dropout_seed=None) -> (dq, dk, dv)
+    flash_attn_func_fp8(q, k, v, descale_q, descale_k, descale_v, ...) -> (o, lse)
     flash_attn_with_kvcache(q, k_cache, v_cache, cache_seqlens, causal=False,
                             softmax_scale=None, num_splits=0) -> (o, lse)
 The call shape follows flash_attn_func in the pages' examples (Llama-Factory
@@ -86,6 +93,14 @@ def _load():
     L.fa_bwd_softcap.restype = i
     L.fa_bwd_softcap_stage.argtypes = [i] + L.fa_bwd_softcap.argtypes
     L.fa_bwd_softcap_stage.restype = i
+    u64 = ctypes.c_uint64
+    L.fa_fwd_dropout.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, i, f, u64, vp, i, vp]
+    L.fa_fwd_dropout.restype = i
+    L.fa_bwd_dropout.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, f, u64,
+                                 vp, i, vp, sz, vp]
+    L.fa_bwd_dropout.restype = i
+    L.fa_bwd_dropout_stage.argtypes = [i] + L.fa_bwd_dropout.argtypes
+    L.fa_bwd_dropout_stage.restype = i
     L.fa_fwd_fp8.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp, f, f, f, i, vp]
     L.fa_fwd_fp8.restype = i
     L.fa_fwd_kvcache.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, i, i, vp, sz, vp]
@@ -162,6 +177,41 @@ def fa_bwd_softcap_stage(stage, q, k, v, o, dout, lse, dq, dk, dv, B, Hq, Hkv, N
     return lib.fa_bwd_softcap_stage(stage, q, k, v, o, dout, lse, dq, dk, dv, B, Hq, Hkv, N, d,
                                     scale, causal, softcap, cu_seqlens, dtype, workspace,
                                     workspace_bytes, stream)
+
+
+def fa_fwd_dropout(q, k, v, o, lse, B, Hq, Hkv, N, d, scale, causal, dropout_p, seed, cu_seqlens,
+                   dtype, stream) -> int:
+    return lib.fa_fwd_dropout(q, k, v, o, lse, B, Hq, Hkv, N, d, scale, causal, dropout_p, seed,
+                              cu_seqlens, dtype, stream)
+
+
+def fa_bwd_dropout(q, k, v, o, dout, lse, dq, dk, dv, B, Hq, Hkv, N, d, scale, causal, dropout_p,
+                   seed, cu_seqlens, dtype, workspace, workspace_bytes, stream) -> int:
+    return lib.fa_bwd_dropout(q, k, v, o, dout, lse, dq, dk, dv, B, Hq, Hkv, N, d, scale, causal,
+                              dropout_p, seed, cu_seqlens, dtype, workspace, workspace_bytes,
+                              stream)
+
+
+def fa_bwd_dropout_stage(stage, q, k, v, o, dout, lse, dq, dk, dv, B, Hq, Hkv, N, d, scale,
+                         causal, dropout_p, seed, cu_seqlens, dtype, workspace, workspace_bytes,
+                         stream) -> int:
+    return lib.fa_bwd_dropout_stage(stage, q, k, v, o, dout, lse, dq, dk, dv, B, Hq, Hkv, N, d,
+                                    scale, causal, dropout_p, seed, cu_seqlens, dtype, workspace,
+                                    workspace_bytes, stream)
+
+
+def _dropout_args(dropout_p, dropout_seed, causal_window, softcap):
+    """(p, seed) for the dropout entry points, or None when dropout_p is 0."""
+    if not dropout_p:
+        return None
+    if dropout_seed is None:
+        raise ValueError("dropout needs dropout_seed (the backward regenerates the same decisions)")
+    if causal_window is not None or softcap:
+        raise NotImplementedError("dropout with a sliding window or a soft cap is not implemented")
+    seed = int(dropout_seed)
+    if not 0 <= seed < 2 ** 64:
+        raise ValueError("dropout_seed must be a 64-bit unsigned integer")
+    return float(dropout_p), seed
 
 
 def fa_fwd_fp8(q, k, v, o, lse, B, Hq, Hkv, N, d, scale, causal, cu_seqlens, descale_q,
@@ -263,15 +313,15 @@ def _window(causal, window_size):
 
 
 def flash_attn_func(q, k, v, causal=False, softmax_scale=None, cu_seqlens=None, max_seqlen=None,
-                    dropout_p=0.0, window_size=(-1, -1), softcap=0.0):
+                    dropout_p=0.0, window_size=(-1, -1), softcap=0.0, dropout_seed=None):
     """Forward. Returns (o, lse); lse is float32 [Hq, T] (natural log).
 
     window_size = (left, right): query i sees keys i − left .. i + right of its
     sequence (−1: unbounded); with causal the right side is 0.
-    softcap = c > 0: logits c·tanh(scale·q·k / c) (not combined with a window)."""
+    softcap = c > 0: logits c·tanh(scale·q·k / c) (not combined with a window).
+    dropout_p > 0: dropout on the softmax weights, decisions from the Philox
+    stream of dropout_seed (required; pass the same pair to the backward)."""
     import torch
-    if dropout_p != 0.0:
-        raise NotImplementedError("dropout is not implemented (dropout_p must be 0.0)")
     B, N, T, Hq, Hkv, d = _shape(q, k, cu_seqlens, max_seqlen)
     if v.shape != k.shape:
         raise ValueError("k and v must have the same shape")
@@ -287,6 +337,15 @@ def flash_attn_func(q, k, v, causal=False, softmax_scale=None, cu_seqlens=None, 
     lse = torch.empty((Hq, T), dtype=torch.float32, device=q.device)
     cu = cu_seqlens.data_ptr() if cu_seqlens is not None else None
     w = _window(causal, window_size)
+    drop = _dropout_args(dropout_p, dropout_seed, w, softcap)
+    if drop is not None:
+        st = lib.fa_fwd_dropout(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                                lse.data_ptr(), B, Hq, Hkv, N, d, float(scale),
+                                int(bool(causal)), drop[0], drop[1], cu, _dtype_code(q),
+                                _stream())
+        if st != FA_OK:
+            raise FaError(st, "fa_fwd_dropout")
+        return o, lse
     if softcap:
         if w is not None:
             raise NotImplementedError("softcap with a sliding window is not implemented")
@@ -340,9 +399,10 @@ def flash_attn_func_fp8(q, k, v, descale_q=1.0, descale_k=1.0, descale_v=1.0, ca
 
 
 def flash_attn_backward(dout, q, k, v, o, lse, causal=False, softmax_scale=None, cu_seqlens=None,
-                        max_seqlen=None, workspace=None, window_size=(-1, -1), softcap=0.0):
-    """Backward. Returns (dq, dk, dv) shaped like q, k, v (window_size and softcap as in
-    the forward, which produced o and lse)."""
+                        max_seqlen=None, workspace=None, window_size=(-1, -1), softcap=0.0,
+                        dropout_p=0.0, dropout_seed=None):
+    """Backward. Returns (dq, dk, dv) shaped like q, k, v (window_size, softcap,
+    dropout_p and dropout_seed as in the forward, which produced o and lse)."""
     import torch
     B, N, T, Hq, Hkv, d = _shape(q, k, cu_seqlens, max_seqlen)
     _check_dev(dout, q, k, v, o, lse)
@@ -357,6 +417,14 @@ def flash_attn_backward(dout, q, k, v, o, lse, causal=False, softmax_scale=None,
     w = _window(causal, window_size)
     ptrs = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(),
             lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr())
+    drop = _dropout_args(dropout_p, dropout_seed, w, softcap)
+    if drop is not None:
+        st = lib.fa_bwd_dropout(*ptrs, B, Hq, Hkv, N, d, float(scale), int(bool(causal)),
+                                drop[0], drop[1], cu, _dtype_code(q), workspace.data_ptr(),
+                                workspace.numel(), _stream())
+        if st != FA_OK:
+            raise FaError(st, "fa_bwd_dropout")
+        return dq, dk, dv
     if softcap:
         if w is not None:
             raise NotImplementedError("softcap with a sliding window is not implemented")

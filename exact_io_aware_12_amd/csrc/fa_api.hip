@@ -65,14 +65,32 @@ int cap_constants(float softcap, float scale, int mask, int d, float* cap_in, fl
   return FA_OK;
 }
 
+// Dropout probability p: 0 = none; otherwise 0 < p < 1 with keep threshold
+// t = floor(256·(1 − p) + 1/2) >= 1, only with the unmasked or causal mask at
+// d <= 128. Returns FA_OK or the status to report.
+int drop_constants(float p, int mask, int d, uint32_t* t) {
+  *t = 256;
+  if (p == 0.f) return FA_OK;
+  if (!std::isfinite(p) || !(p > 0.f) || !(p < 1.f)) return FA_ERR_INVALID_ARG;
+  const double x = std::floor(256.0 * (1.0 - (double)p) + 0.5);
+  if (x < 1.0) return FA_ERR_INVALID_ARG;
+  *t = (uint32_t)std::min(x, 256.0);
+  if (mask == fa::kMaskWindow || d > 128) return FA_ERR_UNSUPPORTED;
+  return FA_OK;
+}
+
 int fwd_common(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq,
                int Hkv, int N, int d, float scale, int mask, int wl, int wr,
-               const int32_t* cu_seqlens, int dtype, hipStream_t stream, float softcap = 0.f) {
+               const int32_t* cu_seqlens, int dtype, hipStream_t stream, float softcap = 0.f,
+               float dropout_p = 0.f, uint64_t seed = 0) {
   bool noop;
   int st = check_sizes(B, Hq, Hkv, N, d, scale, 0, dtype, &noop, 256);
   if (st != FA_OK) return st;
   float cap_in, cap_out;
   st = cap_constants(softcap, scale, mask, d, &cap_in, &cap_out);
+  if (st != FA_OK) return st;
+  uint32_t keep_t;
+  st = drop_constants(dropout_p, mask, d, &keep_t);
   if (st != FA_OK || noop) return st;
   if (!q || !k || !v || !o || !lse) return FA_ERR_INVALID_ARG;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse))
@@ -96,9 +114,13 @@ int fwd_common(const void* q, const void* k, const void* v, void* o, float* lse,
   a.wr = wr;
   a.cap_in = cap_in;
   a.cap_out = cap_out;
+  a.seed_lo = (uint32_t)seed;
+  a.seed_hi = (uint32_t)(seed >> 32);
+  a.keep_t = keep_t;
+  a.drop_scale = 256.f / (float)keep_t;
   if ((int64_t)a.n_qtiles * Hq * B >= (int64_t)1 << 31) return FA_ERR_UNSUPPORTED;
   hipError_t e = fa::launch_fwd(a, dtype == FA_BF16, d, mask, cu_seqlens != nullptr,
-                                softcap != 0.f, stream);
+                                softcap != 0.f, dropout_p != 0.f, stream);
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
@@ -121,6 +143,15 @@ int fa_fwd_softcap(const void* q, const void* k, const void* v, void* o, float* 
   return fwd_common(q, k, v, o, lse, B, Hq, Hkv, N, d, scale,
                     causal ? fa::kMaskCausal : fa::kMaskNone, 0, 0, cu_seqlens, dtype, stream,
                     softcap);
+}
+
+int fa_fwd_dropout(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                   int Hq, int Hkv, int N, int d, float scale, int causal, float dropout_p,
+                   uint64_t seed, const int32_t* cu_seqlens, int dtype, hipStream_t stream) {
+  if (causal != 0 && causal != 1) return FA_ERR_INVALID_ARG;
+  return fwd_common(q, k, v, o, lse, B, Hq, Hkv, N, d, scale,
+                    causal ? fa::kMaskCausal : fa::kMaskNone, 0, 0, cu_seqlens, dtype, stream, 0.f,
+                    dropout_p, seed);
 }
 
 int fa_fwd_window(const void* q, const void* k, const void* v, void* o, float* lse, int B,
@@ -187,12 +218,16 @@ int bwd_common(int stage, const void* q, const void* k, const void* v, const voi
                const void* dout, const float* lse, void* dq, void* dk, void* dv, int B, int Hq,
                int Hkv, int N, int d, float scale, int mask, int wl, int wr,
                const int32_t* cu_seqlens, int dtype, void* workspace, size_t workspace_bytes,
-               hipStream_t stream, float softcap = 0.f) {
+               hipStream_t stream, float softcap = 0.f, float dropout_p = 0.f,
+               uint64_t seed = 0) {
   bool noop;
   int st = check_sizes(B, Hq, Hkv, N, d, scale, 0, dtype, &noop);
   if (st != FA_OK) return st;
   float cap_in, cap_out;
   st = cap_constants(softcap, scale, mask, d, &cap_in, &cap_out);
+  if (st != FA_OK) return st;
+  uint32_t keep_t;
+  st = drop_constants(dropout_p, mask, d, &keep_t);
   if (st != FA_OK || noop) return st;
   if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv) return FA_ERR_INVALID_ARG;
   const void* ptrs[] = {q, k, v, o, dout, lse, dq, dk, dv, workspace};
@@ -225,8 +260,12 @@ int bwd_common(int stage, const void* q, const void* k, const void* v, const voi
   a.wr = wr;
   a.cap_in = cap_in;
   a.cap_out = cap_out;
+  a.seed_lo = (uint32_t)seed;
+  a.seed_hi = (uint32_t)(seed >> 32);
+  a.keep_t = keep_t;
+  a.drop_scale = 256.f / (float)keep_t;
   hipError_t e = fa::launch_bwd(a, dtype == FA_BF16, d, mask, cu_seqlens != nullptr,
-                                softcap != 0.f, stage, stream);
+                                softcap != 0.f, dropout_p != 0.f, stage, stream);
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
@@ -284,6 +323,28 @@ int fa_bwd_softcap_stage(int stage, const void* q, const void* k, const void* v,
   return bwd_common(stage, q, k, v, o, dout, lse, dq, dk, dv, B, Hq, Hkv, N, d, scale,
                     causal ? fa::kMaskCausal : fa::kMaskNone, 0, 0, cu_seqlens, dtype, workspace,
                     workspace_bytes, stream, softcap);
+}
+
+int fa_bwd_dropout(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                   const float* lse, void* dq, void* dk, void* dv, int B, int Hq, int Hkv, int N,
+                   int d, float scale, int causal, float dropout_p, uint64_t seed,
+                   const int32_t* cu_seqlens, int dtype, void* workspace, size_t workspace_bytes,
+                   hipStream_t stream) {
+  return fa_bwd_dropout_stage(-1, q, k, v, o, dout, lse, dq, dk, dv, B, Hq, Hkv, N, d, scale,
+                              causal, dropout_p, seed, cu_seqlens, dtype, workspace,
+                              workspace_bytes, stream);
+}
+
+int fa_bwd_dropout_stage(int stage, const void* q, const void* k, const void* v, const void* o,
+                         const void* dout, const float* lse, void* dq, void* dk, void* dv, int B,
+                         int Hq, int Hkv, int N, int d, float scale, int causal, float dropout_p,
+                         uint64_t seed, const int32_t* cu_seqlens, int dtype, void* workspace,
+                         size_t workspace_bytes, hipStream_t stream) {
+  if (stage < -1 || stage >= fa::bwd_num_stages()) return FA_ERR_INVALID_ARG;
+  if (causal != 0 && causal != 1) return FA_ERR_INVALID_ARG;
+  return bwd_common(stage, q, k, v, o, dout, lse, dq, dk, dv, B, Hq, Hkv, N, d, scale,
+                    causal ? fa::kMaskCausal : fa::kMaskNone, 0, 0, cu_seqlens, dtype, workspace,
+                    workspace_bytes, stream, 0.f, dropout_p, seed);
 }
 
 int fa_bwd_num_stages(void) { return fa::bwd_num_stages(); }

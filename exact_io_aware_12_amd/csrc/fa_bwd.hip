@@ -141,12 +141,16 @@ constexpr int kDkvKK = kDkvQ / 16;   // 16-query MFMA k-steps per tile
 // and dS for queries past the end and, causally, for keys after the query.
 // CAP: soft-capped logits, s = cap_out·tanh(z·cap_in) in log2 units; dS then
 // carries the derivative factor 1 − tanh² (the scale is applied at the end).
-template <typename T, int D, bool CAUSAL, bool EDGE, bool WIN, bool CAP = false>
+// DROP: dropout; the P handed to dV is P∘Z and dS = P∘(Z∘dP − D), with
+// Z = 256/t where the weight is kept and 0 where it is dropped.
+template <typename T, int D, bool CAUSAL, bool EDGE, bool WIN, bool CAP = false, bool DROP = false>
 __device__ __forceinline__ void dkdv_produce(const T* qt_, const T* dot_, const float* ld,
                                              const u32x4 (&kf)[D / 16],
                                              const u32x4 (&vf)[D / 16], u32x4* xp, u32x4* xs,
                                              float c, int q0, int L, int key, int wl, int wr,
-                                             int lane, float cap_in = 0.f, float cap_out = 0.f) {
+                                             int lane, float cap_in = 0.f, float cap_out = 0.f,
+                                             const DropKey* dk = nullptr, int seq = 0,
+                                             int head = 0, float zs = 0.f) {
   constexpr int NKB = D / 16;
   constexpr int NQB = kDkvQ / 32;
   const int col = lane & 31, half = lane >> 5;
@@ -181,6 +185,8 @@ __device__ __forceinline__ void dkdv_produce(const T* qt_, const T* dot_, const 
       const float4 dv4 = *reinterpret_cast<const float4*>(ld + kDkvQ + qoff);
       const float lsev[4] = {lv.x, lv.y, lv.z, lv.w};
       const float dlv[4] = {dv4.x, dv4.y, dv4.z, dv4.w};
+      uint32_t dbytes = 0;   // queries q0 + qoff + 0..3 of this lane's key
+      if constexpr (DROP) dbytes = drop_col_bytes(*dk, seq, head, q0 + qoff, key);
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
         const int i4 = 4 * rr + t;
@@ -189,6 +195,11 @@ __device__ __forceinline__ void dkdv_produce(const T* qt_, const T* dot_, const 
           const float th = tanh_fast(s[i4] * cap_in);
           p = fast_exp2(fmaf(th, cap_out, -lsev[t]));
           ds = p * (dp[i4] - dlv[t]) * fmaf(-th, th, 1.f);
+        } else if constexpr (DROP) {
+          p = fast_exp2(fmaf(s[i4], c, -lsev[t]));
+          const float z = drop_keep(dbytes, t, dk->t) ? zs : 0.f;
+          ds = p * fmaf(dp[i4], z, -dlv[t]);
+          p *= z;
         } else {
           p = fast_exp2(fmaf(s[i4], c, -lsev[t]));
           ds = p * (dp[i4] - dlv[t]);
@@ -213,7 +224,8 @@ __device__ __forceinline__ void dkdv_produce(const T* qt_, const T* dot_, const 
 }
 
 // WIN: sliding window (see fwd_kernel); CAUSAL is false then
-template <typename T, int D, bool CAUSAL, bool VARLEN, bool WIN, bool CAP = false>
+template <typename T, int D, bool CAUSAL, bool VARLEN, bool WIN, bool CAP = false,
+          bool DROP = false>
 __global__ __launch_bounds__(kDkvThreads, 1) void dkdv_kernel(BwdArgs a, int n_ktiles) {
   constexpr int NKB = D / 16;
   constexpr int NCB = D / 32;
@@ -329,14 +341,16 @@ __global__ __launch_bounds__(kDkvThreads, 1) void dkdv_kernel(BwdArgs a, int n_k
         const int q0 = tile_of(t, r) * kDkvQ;
         const int st = t % kDkvStages;
         if (!pair_idle(q0)) {
+          const DropKey dk{a.seed_lo, a.seed_hi, a.keep_t};
+          const int h = g * a.group + r;
           if (t < n_edge)
-            dkdv_produce<T, D, CAUSAL, true, WIN, CAP>(qd_lds[st][0], qd_lds[st][1], ld_lds[st],
-                                                       kf, vf, xp, xs, c, q0, L, key, wl, wr,
-                                                       lane, a.cap_in, a.cap_out);
+            dkdv_produce<T, D, CAUSAL, true, WIN, CAP, DROP>(
+                qd_lds[st][0], qd_lds[st][1], ld_lds[st], kf, vf, xp, xs, c, q0, L, key, wl, wr,
+                lane, a.cap_in, a.cap_out, &dk, b, h, a.drop_scale);
           else
-            dkdv_produce<T, D, CAUSAL, false, WIN, CAP>(qd_lds[st][0], qd_lds[st][1], ld_lds[st],
-                                                        kf, vf, xp, xs, c, q0, L, key, wl, wr,
-                                                        lane, a.cap_in, a.cap_out);
+            dkdv_produce<T, D, CAUSAL, false, WIN, CAP, DROP>(
+                qd_lds[st][0], qd_lds[st][1], ld_lds[st], kf, vf, xp, xs, c, q0, L, key, wl, wr,
+                lane, a.cap_in, a.cap_out, &dk, b, h, a.drop_scale);
         }
       }
     }
@@ -443,12 +457,14 @@ constexpr int kDqK = 64;    // keys per tile
 // EDGE tiles zero P for keys past the end and, causally, for keys after the
 // query.
 // CAP as in dkdv_produce
-template <typename T, int D, bool CAUSAL, bool EDGE, bool WIN, bool CAP = false>
+// CAP and DROP as in dkdv_produce
+template <typename T, int D, bool CAUSAL, bool EDGE, bool WIN, bool CAP = false, bool DROP = false>
 __device__ __forceinline__ void dq_tile(const T* kt, const T* vt, const u32x4 (&qf)[D / 16],
                                         const u32x4 (&df)[D / 16], f32x16 (&dqt)[D / 32], float c,
                                         float lse2, float dl, int kv0, int L, int qrow, int wl,
                                         int wr, int lane, float cap_in = 0.f,
-                                        float cap_out = 0.f) {
+                                        float cap_out = 0.f, const DropKey* dk = nullptr,
+                                        int seq = 0, int head = 0, float zs = 0.f) {
   constexpr int NKB = D / 16;
   constexpr int NCB = D / 32;
   constexpr int NJB = kDqK / 32;
@@ -472,6 +488,12 @@ __device__ __forceinline__ void dq_tile(const T* kt, const T* vt, const u32x4 (&
       s = mfma32<T>(ka[kb % (A + 1)], qf[kb], s);
       dp = mfma32<T>(va[kb % (A + 1)], df[kb], dp);
     }
+    uint32_t dbytes[4] = {0, 0, 0, 0};   // keys kv0 + 32·jb + 8·r + 4·half + 0..3
+    if constexpr (DROP) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        dbytes[r] = drop_row_bytes(*dk, seq, head, qrow, kv0 + jb * 32 + 8 * r + 4 * half);
+    }
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       float p, g = 1.f;
@@ -489,6 +511,8 @@ __device__ __forceinline__ void dq_tile(const T* kt, const T* vt, const u32x4 (&
         p = vis ? p : 0.f;
       }
       if constexpr (CAP) dp[i] = p * (dp[i] - dl) * g;
+      else if constexpr (DROP)
+        dp[i] = p * fmaf(dp[i], drop_keep(dbytes[i >> 2], i & 3, dk->t) ? zs : 0.f, -dl);
       else dp[i] = p * (dp[i] - dl);
     }
     if (jb + 1 < NJB) {
@@ -506,7 +530,8 @@ __device__ __forceinline__ void dq_tile(const T* kt, const T* vt, const u32x4 (&
   }
 }
 
-template <typename T, int D, bool CAUSAL, bool VARLEN, bool WIN, bool CAP = false>
+template <typename T, int D, bool CAUSAL, bool VARLEN, bool WIN, bool CAP = false,
+          bool DROP = false>
 __global__ __launch_bounds__(kThreads, 2) void dq_kernel(BwdArgs a, int n_qtiles) {
   constexpr int NKB = D / 16;
   constexpr int NCB = D / 32;
@@ -573,6 +598,7 @@ __global__ __launch_bounds__(kThreads, 2) void dq_kernel(BwdArgs a, int n_qtiles
   f32x16 dqt[NCB];
 #pragma unroll
   for (int cb = 0; cb < NCB; ++cb) dqt[cb] = f32x16{};
+  const DropKey dk{a.seed_lo, a.seed_hi, a.keep_t};
   const float c = a.scale_log2;
   const int wq_first = q0 + wave * 32, wq_last = wq_first + 31;
   const DmaPlan<T, kDqK, D, kWaves> plan(kvs, wave, lane);
@@ -601,8 +627,9 @@ __global__ __launch_bounds__(kThreads, 2) void dq_kernel(BwdArgs a, int n_qtiles
     if (EDGE && CAUSAL && kv0 > wq_last) return;   // every key after this wave's queries
     if (EDGE && WIN && (kv0 > wq_last + wr || kv0 + kDqK - 1 < wq_first - wl))
       return;   // the tile lies outside the windows of all this wave's queries
-    dq_tile<T, D, CAUSAL, EDGE, WIN, CAP>(kt, vt, qf, df, dqt, c, lse2, dl, kv0, L, qrow, wl, wr,
-                                          lane, a.cap_in, a.cap_out);
+    dq_tile<T, D, CAUSAL, EDGE, WIN, CAP, DROP>(kt, vt, qf, df, dqt, c, lse2, dl, kv0, L, qrow,
+                                                wl, wr, lane, a.cap_in, a.cap_out, &dk, b, h,
+                                                a.drop_scale);
   };
   using B0 = std::integral_constant<int, 0>;
   using B1 = std::integral_constant<int, 1>;
@@ -638,7 +665,8 @@ __global__ __launch_bounds__(kThreads, 2) void dq_kernel(BwdArgs a, int n_qtiles
   }
 }
 
-template <typename T, int D, bool CAUSAL, bool VARLEN, bool WIN, bool CAP = false>
+template <typename T, int D, bool CAUSAL, bool VARLEN, bool WIN, bool CAP = false,
+          bool DROP = false>
 hipError_t launch(const BwdArgs& a, int stage, hipStream_t s) {
   (void)hipGetLastError();  // drop an error left pending by earlier, unrelated HIP calls
   if (stage < 0 || stage == 0) {
@@ -651,14 +679,14 @@ hipError_t launch(const BwdArgs& a, int stage, hipStream_t s) {
   }
   if (stage < 0 || stage == 1) {
     const int nkt = (a.N + kDkvKeys - 1) / kDkvKeys;
-    hipLaunchKernelGGL((dkdv_kernel<T, D, CAUSAL, VARLEN, WIN, CAP>), dim3(nkt * a.Hkv * a.B),
+    hipLaunchKernelGGL((dkdv_kernel<T, D, CAUSAL, VARLEN, WIN, CAP, DROP>), dim3(nkt * a.Hkv * a.B),
                        dim3(kDkvThreads), 0, s, a, nkt);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   if (stage < 0 || stage == 2) {
     const int nqt = (a.N + kDqQ - 1) / kDqQ;
-    hipLaunchKernelGGL((dq_kernel<T, D, CAUSAL, VARLEN, WIN, CAP>), dim3(nqt * a.Hq * a.B),
+    hipLaunchKernelGGL((dq_kernel<T, D, CAUSAL, VARLEN, WIN, CAP, DROP>), dim3(nqt * a.Hq * a.B),
                        dim3(kThreads), 0, s, a, nqt);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -667,8 +695,15 @@ hipError_t launch(const BwdArgs& a, int stage, hipStream_t s) {
 }
 
 template <typename T, int D>
-hipError_t dispatch_mask(const BwdArgs& a, int mask, bool varlen, bool cap, int stage,
+hipError_t dispatch_mask(const BwdArgs& a, int mask, bool varlen, bool cap, bool drop, int stage,
                          hipStream_t s) {
+  if (drop) {   // dropout: no window (checked by the caller)
+    if (mask == kMaskCausal)
+      return varlen ? launch<T, D, true, true, false, false, true>(a, stage, s)
+                    : launch<T, D, true, false, false, false, true>(a, stage, s);
+    return varlen ? launch<T, D, false, true, false, false, true>(a, stage, s)
+                  : launch<T, D, false, false, false, false, true>(a, stage, s);
+  }
   if (cap) {   // soft cap: no window (checked by the caller)
     if (mask == kMaskCausal)
       return varlen ? launch<T, D, true, true, false, true>(a, stage, s)
@@ -691,12 +726,12 @@ hipError_t dispatch_mask(const BwdArgs& a, int mask, bool varlen, bool cap, int 
 int bwd_num_stages() { return 3; }
 
 hipError_t launch_bwd(const BwdArgs& a, bool bf16_in, int d, int mask, bool varlen, bool cap,
-                      int stage, hipStream_t s) {
+                      bool drop, int stage, hipStream_t s) {
   if (bf16_in)
-    return d == 64 ? dispatch_mask<bf16, 64>(a, mask, varlen, cap, stage, s)
-                   : dispatch_mask<bf16, 128>(a, mask, varlen, cap, stage, s);
-  return d == 64 ? dispatch_mask<f16, 64>(a, mask, varlen, cap, stage, s)
-                 : dispatch_mask<f16, 128>(a, mask, varlen, cap, stage, s);
+    return d == 64 ? dispatch_mask<bf16, 64>(a, mask, varlen, cap, drop, stage, s)
+                   : dispatch_mask<bf16, 128>(a, mask, varlen, cap, drop, stage, s);
+  return d == 64 ? dispatch_mask<f16, 64>(a, mask, varlen, cap, drop, stage, s)
+                 : dispatch_mask<f16, 128>(a, mask, varlen, cap, drop, stage, s);
 }
 
 }  // namespace fa

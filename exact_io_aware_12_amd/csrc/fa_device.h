@@ -99,6 +99,62 @@ __device__ __forceinline__ float wave_sum_halves(float x) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// ---------------------------------------------------------------------------
+// Dropout keep decisions. Philox4x32-10, the counter-based generator of
+// Salmon, Moraes, Dror and Shaw ("Parallel Random Numbers: As Easy as 1, 2,
+// 3", SC '11): per round two 32 x 32 -> 64-bit products,
+// c <- (hi1 ^ c1 ^ k0, lo1, hi0 ^ c3 ^ k1, lo0), the key advanced by the Weyl
+// constants between rounds. One call covers a 4 x 4 block of (query i, key j)
+// of one query head and sequence: counter (j/4, i/4, head, seq), key = seed;
+// word i % 4, byte j % 4 is the element's byte, kept iff byte < t.
+__device__ __forceinline__ u32x4 philox4x32_10(uint32_t c0, uint32_t c1, uint32_t c2,
+                                               uint32_t c3, uint32_t k0, uint32_t k1) {
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    if (r) {
+      k0 += 0x9E3779B9u;
+      k1 += 0xBB67AE85u;
+    }
+    const uint64_t p0 = (uint64_t)0xD2511F53u * c0;
+    const uint64_t p1 = (uint64_t)0xCD9E8D57u * c2;
+    const uint32_t n0 = (uint32_t)(p1 >> 32) ^ c1 ^ k0;
+    const uint32_t n2 = (uint32_t)(p0 >> 32) ^ c3 ^ k1;
+    c1 = (uint32_t)p1;
+    c3 = (uint32_t)p0;
+    c0 = n0;
+    c2 = n2;
+  }
+  return u32x4{c0, c1, c2, c3};
+}
+
+struct DropKey {
+  uint32_t k0, k1;   // the seed
+  uint32_t t;        // keep iff byte < t (1 ≤ t ≤ 256)
+};
+
+// The bytes of query i for keys j0 .. j0+3 (j0 % 4 == 0): byte n is key j0 + n.
+__device__ __forceinline__ uint32_t drop_row_bytes(const DropKey& dk, int seq, int head, int i,
+                                                   int j0) {
+  const u32x4 w = philox4x32_10((uint32_t)j0 >> 2, (uint32_t)i >> 2, (uint32_t)head,
+                                (uint32_t)seq, dk.k0, dk.k1);
+  const int r = i & 3;
+  return r == 0 ? w[0] : r == 1 ? w[1] : r == 2 ? w[2] : w[3];
+}
+
+// The bytes of key j for queries i0 .. i0+3 (i0 % 4 == 0): byte n is query i0 + n.
+__device__ __forceinline__ uint32_t drop_col_bytes(const DropKey& dk, int seq, int head, int i0,
+                                                   int j) {
+  const u32x4 w = philox4x32_10((uint32_t)j >> 2, (uint32_t)i0 >> 2, (uint32_t)head,
+                                (uint32_t)seq, dk.k0, dk.k1);
+  const int sh = 8 * (j & 3);
+  return ((w[0] >> sh) & 0xffu) | (((w[1] >> sh) & 0xffu) << 8) |
+         (((w[2] >> sh) & 0xffu) << 16) | (((w[3] >> sh) & 0xffu) << 24);
+}
+
+__device__ __forceinline__ bool drop_keep(uint32_t bytes, int n, uint32_t t) {
+  return ((bytes >> (8 * n)) & 0xffu) < t;
+}
+
 // tanh(x) = 1 − 2 / (1 + e^(2x)) from the exponential and reciprocal units:
 // exactly ±1 once e^(2x) overflows or vanishes, absolute error ≈1e-7 near 0.
 __device__ __forceinline__ float tanh_fast(float x) {

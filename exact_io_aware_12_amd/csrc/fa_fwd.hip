@@ -41,11 +41,14 @@ constexpr float kRescaleHeadroom = 8.f;  // log2 of the largest P before the max
 // with a lazily raised reference max, Oᵀ += Vᵀ·Pᵀ. EDGE tiles mask keys past
 // the sequence end and, causally, keys after the query. CAP: the logits
 // are soft-capped, s = c_out·tanh(z·c_in) in log2 units (then c is 1).
-template <typename T, int D, bool CAUSAL, bool EDGE, bool WIN, bool CAP = false>
+// DROP: dropout on the weights; the row sum lr still takes every weight, the
+// P·V product only the kept ones (scaled by 256/t in the epilogue).
+template <typename T, int D, bool CAUSAL, bool EDGE, bool WIN, bool CAP = false, bool DROP = false>
 __device__ __forceinline__ void fwd_tile(const T* kt, const T* vt, const u32x4 (&qf)[D / 16],
                                          f32x16 (&o)[D / 32], float& mc, float& l, float& lr,
                                          float c, int kv0, int L, int qrow, int wl, int wr,
-                                         int lane, float cap_in = 0.f, float cap_out = 0.f) {
+                                         int lane, float cap_in = 0.f, float cap_out = 0.f,
+                                         const DropKey* dk = nullptr, int seq = 0, int head = 0) {
   constexpr int NKB = D / 16;
   constexpr int NCB = D / 32;
   const int col = lane & 31, half = lane >> 5;
@@ -113,9 +116,21 @@ __device__ __forceinline__ void fwd_tile(const T* kt, const T* vt, const u32x4 (
   float r[kBC / 16];   // independent partial sums: short dependency chains
 #pragma unroll
   for (int kk = 0; kk < kBC / 16; ++kk) {
-    const u32x4 pf = acc_operand<T>(s[kk >> 1], (kk & 1) * 2);
+    u32x4 pf = acc_operand<T>(s[kk >> 1], (kk & 1) * 2);
     r[kk] = dot2_sum<T>(pf, 0.f);
     const int k0 = kk * 16 + 4 * half;
+    if constexpr (DROP) {   // keys kv0 + k0 + 0..3 (dwords 0, 1) and + 8..11 (dwords 2, 3)
+      const uint32_t b0 = drop_row_bytes(*dk, seq, head, qrow, kv0 + k0);
+      const uint32_t b1 = drop_row_bytes(*dk, seq, head, qrow, kv0 + k0 + 8);
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const uint32_t by = w < 2 ? b0 : b1;
+        const int n = 2 * (w & 1);
+        const uint32_t m = (drop_keep(by, n, dk->t) ? 0x0000ffffu : 0u) |
+                           (drop_keep(by, n + 1, dk->t) ? 0xffff0000u : 0u);
+        pf[w] &= m;
+      }
+    }
 #pragma unroll
     for (int cb = 0; cb < NCB; ++cb)
       o[cb] = mfma32<T>(lds_tr8<T, D>(vt, k0, k0 + 8, cb * 32, lane), pf, o[cb]);
@@ -125,7 +140,8 @@ __device__ __forceinline__ void fwd_tile(const T* kt, const T* vt, const u32x4 (
 
 // WIN: sliding window, key j visible from query i iff i − a.wl ≤ j ≤ i + a.wr
 // (bounds clamped to N by the caller; CAUSAL is false then)
-template <typename T, int D, bool CAUSAL, bool VARLEN, bool WIN, bool CAP = false>
+template <typename T, int D, bool CAUSAL, bool VARLEN, bool WIN, bool CAP = false,
+          bool DROP = false>
 // two workgroups per CU up to d = 128; at d = 256 the O accumulators alone
 // take 128 registers and the kernel runs one workgroup per CU
 __global__ __launch_bounds__(kThreads, D <= 128 ? 2 : 1) void fwd_kernel(FwdArgs a) {
@@ -210,6 +226,7 @@ __global__ __launch_bounds__(kThreads, D <= 128 ? 2 : 1) void fwd_kernel(FwdArgs
   for (int cb = 0; cb < NCB; ++cb) o[cb] = f32x16{};
   const float c = CAP ? 1.f : a.scale_log2;   // capped logits are already in log2 units
   const float cap_in = CAP ? a.cap_in : 0.f, cap_out = CAP ? a.cap_out : 0.f;
+  const DropKey dk{a.seed_lo, a.seed_hi, a.keep_t};
   float mc = -INFINITY;   // reference max of S·c for this row
   float l = 0.f;          // Σ P over this lane half's keys (fp32), for the LSE (bf16)
   float lr = 0.f;         // the same sum of P rounded to T, for normalising O
@@ -241,8 +258,9 @@ __global__ __launch_bounds__(kThreads, D <= 128 ? 2 : 1) void fwd_kernel(FwdArgs
     if (EDGE && CAUSAL && kv0 > wq_last) return;  // every key of the tile is after this wave's rows
     if (EDGE && WIN && (kv0 > wq_last + wr || kv0 + kBC - 1 < wq_first - wl))
       return;   // the tile lies outside the windows of all this wave's rows
-    fwd_tile<T, D, CAUSAL, EDGE, WIN, CAP>(lds[BUF][0], lds[BUF][1], qf, o, mc, l, lr, c, kv0,
-                                           L, qrow, wl, wr, lane, cap_in, cap_out);
+    fwd_tile<T, D, CAUSAL, EDGE, WIN, CAP, DROP>(lds[BUF][0], lds[BUF][1], qf, o, mc, l, lr, c,
+                                                 kv0, L, qrow, wl, wr, lane, cap_in, cap_out,
+                                                 &dk, b, h);
   };
   using B0 = std::integral_constant<int, 0>;
   using B1 = std::integral_constant<int, 1>;
@@ -267,7 +285,7 @@ __global__ __launch_bounds__(kThreads, D <= 128 ? 2 : 1) void fwd_kernel(FwdArgs
   const float lr_tot = wave_sum_halves(lr);
   const float l_tot = kLseFromUnrounded<T> ? wave_sum_halves(l) : lr_tot;
   if (qrow < L) {
-    const float inv = 1.f / lr_tot;
+    const float inv = (DROP ? a.drop_scale : 1.f) / lr_tot;
     T* op = static_cast<T*>(a.o) + (int64_t)seq0 * qs + (int64_t)h * D + qrow * qs;
 #pragma unroll
     for (int cb = 0; cb < NCB; ++cb)
@@ -282,18 +300,27 @@ __global__ __launch_bounds__(kThreads, D <= 128 ? 2 : 1) void fwd_kernel(FwdArgs
   }
 }
 
-template <typename T, int D, bool CAUSAL, bool VARLEN, bool WIN, bool CAP = false>
+template <typename T, int D, bool CAUSAL, bool VARLEN, bool WIN, bool CAP = false,
+          bool DROP = false>
 hipError_t launch(const FwdArgs& a, hipStream_t stream) {
   const int grid = a.n_qtiles * a.Hq * a.B;
   (void)hipGetLastError();  // drop an error left pending by earlier, unrelated HIP calls
-  hipLaunchKernelGGL((fwd_kernel<T, D, CAUSAL, VARLEN, WIN, CAP>), dim3(grid), dim3(kThreads), 0,
-                     stream, a);
+  hipLaunchKernelGGL((fwd_kernel<T, D, CAUSAL, VARLEN, WIN, CAP, DROP>), dim3(grid),
+                     dim3(kThreads), 0, stream, a);
   return hipGetLastError();
 }
 
 template <typename T, int D>
-hipError_t dispatch_mask(const FwdArgs& a, int mask, bool varlen, bool cap, hipStream_t s) {
-  if constexpr (D <= 128) {   // soft cap: no window, d <= 128 (checked by the caller)
+hipError_t dispatch_mask(const FwdArgs& a, int mask, bool varlen, bool cap, bool drop,
+                         hipStream_t s) {
+  if constexpr (D <= 128) {   // soft cap or dropout: no window, d <= 128 (checked by the caller)
+    if (drop) {
+      if (mask == kMaskCausal)
+        return varlen ? launch<T, D, true, true, false, false, true>(a, s)
+                      : launch<T, D, true, false, false, false, true>(a, s);
+      return varlen ? launch<T, D, false, true, false, false, true>(a, s)
+                    : launch<T, D, false, false, false, false, true>(a, s);
+    }
     if (cap) {
       if (mask == kMaskCausal)
         return varlen ? launch<T, D, true, true, false, true>(a, s)
@@ -314,15 +341,15 @@ hipError_t dispatch_mask(const FwdArgs& a, int mask, bool varlen, bool cap, hipS
 int fwd_query_tile() { return kBR; }
 
 hipError_t launch_fwd(const FwdArgs& a, bool bf16_in, int d, int mask, bool varlen, bool cap,
-                      hipStream_t s) {
+                      bool drop, hipStream_t s) {
   if (bf16_in) {
-    if (d == 64) return dispatch_mask<bf16, 64>(a, mask, varlen, cap, s);
-    if (d == 128) return dispatch_mask<bf16, 128>(a, mask, varlen, cap, s);
-    return dispatch_mask<bf16, 256>(a, mask, varlen, cap, s);
+    if (d == 64) return dispatch_mask<bf16, 64>(a, mask, varlen, cap, drop, s);
+    if (d == 128) return dispatch_mask<bf16, 128>(a, mask, varlen, cap, drop, s);
+    return dispatch_mask<bf16, 256>(a, mask, varlen, cap, drop, s);
   }
-  if (d == 64) return dispatch_mask<f16, 64>(a, mask, varlen, cap, s);
-  if (d == 128) return dispatch_mask<f16, 128>(a, mask, varlen, cap, s);
-  return dispatch_mask<f16, 256>(a, mask, varlen, cap, s);
+  if (d == 64) return dispatch_mask<f16, 64>(a, mask, varlen, cap, drop, s);
+  if (d == 128) return dispatch_mask<f16, 128>(a, mask, varlen, cap, drop, s);
+  return dispatch_mask<f16, 256>(a, mask, varlen, cap, drop, s);
 }
 
 }  // namespace fa

@@ -23,6 +23,9 @@ struct FwdArgs {
   float scale_log2;           // scale · log2(e)
   int wl, wr;                 // window bounds (kMaskWindow only)
   float cap_in, cap_out;      // soft cap c: scale / c and c · log2(e) (softcap kernels only)
+  uint32_t seed_lo, seed_hi;  // dropout: Philox key
+  uint32_t keep_t;            // dropout: keep iff byte < keep_t
+  float drop_scale;           // dropout: 256 / keep_t
 };
 
 // FP8 forward: q, k, v hold e4m3fn codes; scale_log2 already includes both
@@ -52,6 +55,9 @@ struct BwdArgs {
   float scale_log2;
   int wl, wr;                 // window bounds (kMaskWindow only)
   float cap_in, cap_out;      // soft cap c: scale / c and c · log2(e) (softcap kernels only)
+  uint32_t seed_lo, seed_hi;  // dropout: Philox key
+  uint32_t keep_t;            // dropout: keep iff byte < keep_t
+  float drop_scale;           // dropout: 256 / keep_t
 };
 
 struct DecodeArgs {
@@ -73,9 +79,11 @@ struct DecodeArgs {
 };
 
 int fwd_query_tile();
-// softcap: logits c·tanh(scale·q·k / c) (mask kMaskNone or kMaskCausal, d <= 128)
+// softcap: logits c·tanh(scale·q·k / c); dropout: keep decisions from the
+// Philox stream of the seed (each: mask kMaskNone or kMaskCausal, d <= 128,
+// not both)
 hipError_t launch_fwd(const FwdArgs& a, bool bf16_in, int d, int mask, bool varlen, bool softcap,
-                      hipStream_t s);
+                      bool dropout, hipStream_t s);
 int fwd_fp8_query_tile();
 hipError_t launch_fwd_fp8(const Fp8FwdArgs& a, bool bf16_out, int d, bool causal, bool varlen,
                           hipStream_t s);
@@ -83,7 +91,7 @@ hipError_t launch_fwd_fp8(const Fp8FwdArgs& a, bool bf16_out, int d, bool causal
 // 1 (dK, dV) or 2 (dQ).
 int bwd_num_stages();
 hipError_t launch_bwd(const BwdArgs& a, bool bf16_in, int d, int mask, bool varlen, bool softcap,
-                      int stage, hipStream_t s);
+                      bool dropout, int stage, hipStream_t s);
 int decode_tile_keys();
 // stage < 0: both stages; 0: per-range partial results; 1: merge into o, lse.
 int decode_num_stages();

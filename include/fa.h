@@ -186,6 +186,40 @@ int fa_bwd_softcap_stage(int stage, const void* q, const void* k, const void* v,
                          void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * Dropout on the softmax weights: the forward and backward of fa_fwd / fa_bwd
+ * with O = (P ∘ Z) V, where Z is 256/t for a kept weight and 0 for a dropped
+ * one. The FlashAttention-2 page (blog.gitcode.com, API example) shows a
+ * dropout_p argument but no random-number semantics; the reading taken:
+ *   t = floor(256·(1 − dropout_p) + 1/2), keep probability t/256 (1 <= t <= 256);
+ *   keep decisions from Philox4x32-10 (Salmon, Moraes, Dror, Shaw, SC '11),
+ *   one generator call per 4 x 4 block of (query i, key j) of one query head
+ *   and sequence (positions local to the sequence): counter
+ *   (j/4, i/4, head, sequence), key (seed mod 2^32, seed / 2^32); word i % 4,
+ *   byte j % 4 of the output is the element's byte, kept iff byte < t.
+ * The LSE is that of the undropped logits. The backward needs the same seed
+ * and dropout_p (it regenerates the decisions; nothing is stored).
+ *   dropout_p : 0 = none (the plain kernels run, bit-identical results);
+ *               otherwise 0 < dropout_p < 1 with t >= 1 (else FA_ERR_INVALID_ARG)
+ * Causal or not, fixed length or varlen, GQA; d = 64 or 128 (d = 256:
+ * FA_ERR_UNSUPPORTED). Everything else as for fa_fwd / fa_bwd;
+ * fa_bwd_dropout_stage runs one stage (or every stage with stage −1).
+ */
+int fa_fwd_dropout(const void* q, const void* k, const void* v, void* o, float* lse,
+                   int B, int Hq, int Hkv, int N, int d, float scale, int causal,
+                   float dropout_p, uint64_t seed,
+                   const int32_t* cu_seqlens, int dtype, hipStream_t stream);
+int fa_bwd_dropout(const void* q, const void* k, const void* v, const void* o,
+                   const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                   int B, int Hq, int Hkv, int N, int d, float scale, int causal,
+                   float dropout_p, uint64_t seed, const int32_t* cu_seqlens, int dtype,
+                   void* workspace, size_t workspace_bytes, hipStream_t stream);
+int fa_bwd_dropout_stage(int stage, const void* q, const void* k, const void* v, const void* o,
+                         const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                         int B, int Hq, int Hkv, int N, int d, float scale, int causal,
+                         float dropout_p, uint64_t seed, const int32_t* cu_seqlens, int dtype,
+                         void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
  * FP8 forward: the forward of fa_fwd on e4m3 inputs. The pages name e4m3
  * (torch.float8_e4m3fn) as the 8-bit attention format and credit
  * FlashAttention-3 with an FP8 forward (cxbdf.cn deployment guide, section

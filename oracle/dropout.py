@@ -10,8 +10,9 @@ stated once here):
 * Dropout acts on the softmax weights: O = (P ∘ Z) V with Z_ij = M_ij · 256/t,
   M_ij ∈ {0, 1} the keep decision and t/256 the keep probability; LSE stays
   the log-sum-exp of the undropped logits.
-* t = round(256 · (1 − p)) for the caller's dropout_p = p (1 ≤ t ≤ 256), so the
-  keep probability is t/256 and 256/t keeps O unbiased.
+* t = ⌊256 · (1 − p) + 1/2⌋ for the caller's dropout_p = p as a 32-bit float
+  (the type the library receives; the arithmetic in double), 1 ≤ t ≤ 256, so
+  the keep probability is t/256 and 256/t keeps O unbiased.
 * Random bits: Philox4x32-10, the counter-based generator of Salmon, Moraes,
   Dror and Shaw, "Parallel Random Numbers: As Easy as 1, 2, 3" (SC '11),
   written here from its published definition: per round
@@ -60,9 +61,13 @@ def philox4x32_10(ctr, key):
 
 
 def keep_threshold(dropout_p: float) -> int:
-    """t = round(256·(1 − p)); keep probability t/256. Needs 0 ≤ p and t ≥ 1."""
-    t = int(round(256.0 * (1.0 - float(dropout_p))))
-    if not (0.0 <= dropout_p < 1.0) or t < 1:
+    """t = ⌊256·(1 − p) + 1/2⌋ with p rounded to float32 first; keep probability
+    t/256. Needs 0 ≤ p < 1 and t ≥ 1."""
+    p = float(np.float32(dropout_p))
+    if not (0.0 <= p < 1.0):
+        raise ValueError(f"dropout_p={dropout_p} must lie in [0, 1)")
+    t = int(np.floor(256.0 * (1.0 - p) + 0.5))
+    if t < 1:
         raise ValueError(f"dropout_p={dropout_p} gives no kept weights")
     return min(t, 256)
 

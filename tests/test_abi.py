@@ -20,10 +20,12 @@ def declared_functions():
 
 
 def test_header_declares_the_boundary():
-    assert declared_functions() == ["fa_bwd", "fa_bwd_num_stages", "fa_bwd_softcap",
+    assert declared_functions() == ["fa_bwd", "fa_bwd_dropout", "fa_bwd_dropout_stage",
+                                    "fa_bwd_num_stages", "fa_bwd_softcap",
                                     "fa_bwd_softcap_stage", "fa_bwd_stage",
                                     "fa_bwd_window", "fa_bwd_window_stage",
-                                    "fa_bwd_workspace_size", "fa_fwd", "fa_fwd_fp8",
+                                    "fa_bwd_workspace_size", "fa_fwd", "fa_fwd_dropout",
+                                    "fa_fwd_fp8",
                                     "fa_fwd_kvcache",
                                     "fa_fwd_kvcache_num_stages", "fa_fwd_kvcache_stage",
                                     "fa_fwd_kvcache_workspace_size", "fa_fwd_softcap", "fa_fwd_window",
@@ -357,3 +359,78 @@ def test_softcap_no_device_reports_hip_error():
     assert fwdc() == fa.FA_ERR_HIP
     assert fwdc(cap=0.0) == fa.FA_ERR_HIP      # no cap: the plain kernels
     assert bwdc() == fa.FA_ERR_HIP
+
+
+def fwdd(**kw):
+    a = dict(q=P, k=P, v=P, o=P, lse=P, B=1, Hq=2, Hkv=2, N=16, d=64, scale=0.125, causal=0,
+             p=0.1, seed=1234, cu=None, dtype=fa.FA_FP16, stream=None)
+    a.update(kw)
+    return fa.fa_fwd_dropout(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["Hq"], a["Hkv"],
+                             a["N"], a["d"], a["scale"], a["causal"], a["p"], a["seed"], a["cu"],
+                             a["dtype"], a["stream"])
+
+
+def bwdd(stage=None, **kw):
+    a = dict(B=1, Hq=2, Hkv=2, N=16, d=128, scale=0.125, causal=1, p=0.2, seed=2 ** 63 + 5,
+             dtype=fa.FA_BF16, ws=P, wsb=1 << 20)
+    a.update(kw)
+    ptrs = [kw.get(n, P) for n in ("q", "k", "v", "o", "do", "lse", "dq", "dk", "dv")]
+    args = (*ptrs, a["B"], a["Hq"], a["Hkv"], a["N"], a["d"], a["scale"], a["causal"], a["p"],
+            a["seed"], None, a["dtype"], a["ws"], a["wsb"], None)
+    if stage is None:
+        return fa.fa_bwd_dropout(*args)
+    return fa.fa_bwd_dropout_stage(stage, *args)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(p=-0.1), fa.FA_ERR_INVALID_ARG),
+    (dict(p=1.0), fa.FA_ERR_INVALID_ARG),
+    (dict(p=0.999), fa.FA_ERR_INVALID_ARG),    # no weight kept: t = 0
+    (dict(p=float("nan")), fa.FA_ERR_INVALID_ARG),
+    (dict(causal=2), fa.FA_ERR_INVALID_ARG),
+    (dict(v=None), fa.FA_ERR_INVALID_ARG),
+    (dict(lse=P + 4), fa.FA_ERR_INVALID_ARG),
+    (dict(d=256), fa.FA_ERR_UNSUPPORTED),
+    (dict(B=0), fa.FA_OK),
+    (dict(N=0, p=0.5), fa.FA_OK),
+])
+def test_fwd_dropout_host_checks(kw, status):
+    assert fwdd(**kw) == status
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(p=1.5), fa.FA_ERR_INVALID_ARG),
+    (dict(d=256), fa.FA_ERR_UNSUPPORTED),
+    (dict(ws=None), fa.FA_ERR_WORKSPACE),
+    (dict(dv=P + 8), fa.FA_ERR_INVALID_ARG),
+    (dict(B=0), fa.FA_OK),
+])
+def test_bwd_dropout_host_checks(kw, status):
+    assert bwdd(**kw) == status
+
+
+def test_bwd_dropout_stage_index_checked():
+    for bad in (-2, 3):
+        assert bwdd(stage=bad) == fa.FA_ERR_INVALID_ARG
+    assert bwdd(stage=0, ws=None) == fa.FA_ERR_WORKSPACE
+
+
+def test_dropout_no_device_reports_hip_error():
+    torch = pytest.importorskip("torch")
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    assert fwdd() == fa.FA_ERR_HIP
+    assert fwdd(p=0.0) == fa.FA_ERR_HIP       # no dropout: the plain kernels
+    assert bwdd() == fa.FA_ERR_HIP
+
+
+def test_binding_dropout_needs_a_seed():
+    torch = pytest.importorskip("torch")
+    q = torch.zeros((1, 4, 2, 64), dtype=torch.float16)
+    with pytest.raises(ValueError):
+        fa._dropout_args(0.1, None, None, 0.0)
+    with pytest.raises(NotImplementedError):
+        fa._dropout_args(0.1, 3, (5, 0), 0.0)
+    assert fa._dropout_args(0.0, None, None, 0.0) is None
+    assert fa._dropout_args(0.25, 7, None, 0.0) == (0.25, 7)
+    del q

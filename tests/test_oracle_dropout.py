@@ -52,7 +52,8 @@ def test_philox_vectorised_matches_scalar():
         assert tuple(int(w[n]) for w in vec) == ref
 
 
-@pytest.mark.parametrize("p,t", [(0.0, 256), (0.1, 230), (0.5, 128), (0.25, 192), (0.998, 1)])
+@pytest.mark.parametrize("p,t", [(0.0, 256), (0.1, 230), (0.5, 128), (0.25, 192), (0.998, 1),
+                                 (1.5 / 256, 255), (2.5 / 256, 254)])   # halves round up
 def test_keep_threshold(p, t):
     assert keep_threshold(p) == t
 
