@@ -130,8 +130,10 @@ class Bound:
 
     def _mask(self):
         """The mask arguments: (causal,), (left, right) for a window workload, or
-        (causal, softcap) for a soft-capped one."""
+        (causal, softcap) for a soft-capped one, (causal, p, seed) with dropout."""
         w = self.w
+        if w.dropout_p:
+            return (int(w.causal), w.dropout_p, w.dropout_seed)
         if w.softcap:
             return (int(w.causal), w.softcap)
         if w.window is None:
@@ -141,6 +143,14 @@ class Bound:
 
     def fwd(self):
         w, t = self.w, self.t
+        if w.dropout_p:
+            st = self.fa.fa_fwd_dropout(t["q"].data_ptr(), t["k"].data_ptr(), t["v"].data_ptr(),
+                                        self.o.data_ptr(), self.lse.data_ptr(), w.B, w.Hq, w.Hkv,
+                                        w.N, w.d, w.scale, int(w.causal), w.dropout_p,
+                                        w.dropout_seed, self.cu_ptr, self.code, self.stream)
+            if st != self.fa.FA_OK:
+                raise self.fa.FaError(st, "fa_fwd_dropout")
+            return
         if w.softcap:
             st = self.fa.fa_fwd_softcap(t["q"].data_ptr(), t["k"].data_ptr(), t["v"].data_ptr(),
                                         self.o.data_ptr(), self.lse.data_ptr(), w.B, w.Hq, w.Hkv,
@@ -164,14 +174,17 @@ class Bound:
                 self.cu_ptr, self.code, self.ws.data_ptr(), self.ws.numel(), self.stream)
 
     def bwd(self):
-        fn = (self.fa.fa_bwd_softcap if self.w.softcap else
+        fn = (self.fa.fa_bwd_dropout if self.w.dropout_p else
+              self.fa.fa_bwd_softcap if self.w.softcap else
               self.fa.fa_bwd if self.w.window is None else self.fa.fa_bwd_window)
         st = fn(*self._bwd_args())
         if st != self.fa.FA_OK:
             raise self.fa.FaError(st, "fa_bwd")
 
     def bwd_stage(self, stage):
-        if self.w.softcap:
+        if self.w.dropout_p:
+            st = self.fa.fa_bwd_dropout_stage(stage, *self._bwd_args())
+        elif self.w.softcap:
             st = self.fa.fa_bwd_softcap_stage(stage, *self._bwd_args())
         elif self.w.window is None:
             st = self.fa.fa_bwd_stage(stage, *self._bwd_args())
@@ -248,10 +261,19 @@ def cpu_baseline(w, min_seconds=10.0, max_units=4):
     while done < max_units and (done == 0 or dt < min_seconds):
         q, k, v, do = (rng.standard_normal((L, w.d), dtype=np.float32) for _ in range(4))
         t0 = time.perf_counter()
-        O.head_fwd(q, k, v, w.scale, w.causal, window=w.window, softcap=w.softcap or None)
-        if w.backward:
-            O.head_bwd(q, k, v, do, w.scale, w.causal, window=w.window,
-                       softcap=w.softcap or None)
+        if w.dropout_p:   # one (sequence, head) unit through the dropout oracle
+            import oracle.dropout as OD
+            u = [x[:, None, :] for x in (q, k, v, do)]
+            OD.attention_fwd_dropout(*u[:3], w.scale, w.causal, None, w.dropout_p,
+                                     w.dropout_seed)
+            if w.backward:
+                OD.attention_bwd_dropout(*u, w.scale, w.causal, None, w.dropout_p,
+                                         w.dropout_seed)
+        else:
+            O.head_fwd(q, k, v, w.scale, w.causal, window=w.window, softcap=w.softcap or None)
+            if w.backward:
+                O.head_bwd(q, k, v, do, w.scale, w.causal, window=w.window,
+                           softcap=w.softcap or None)
         dt += time.perf_counter() - t0
         done += 1
     return {"value": round(done * flop_unit / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(cores),
@@ -525,13 +547,16 @@ def run_step_bench(args):
         "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms_entry, 4), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",
-        "config": {"workload": (f"{w.name}: fa_fwd_softcap + fa_bwd_softcap" if w.softcap else
+        "config": {"workload": (f"{w.name}: fa_fwd_dropout + fa_bwd_dropout" if w.dropout_p else
+                                f"{w.name}: fa_fwd_softcap + fa_bwd_softcap" if w.softcap else
                                 f"{w.name}: fa_fwd + fa_bwd" if w.window is None else
                                 f"{w.name}: fa_fwd_window + fa_bwd_window"),
                    "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv,
                    "N": w.N, "d": w.d, "causal": w.causal, "seed": w.seed,
                    **({"window": list(w.window)} if w.window is not None else {}),
-                   **({"softcap": w.softcap} if w.softcap else {})},
+                   **({"softcap": w.softcap} if w.softcap else {}),
+                   **({"dropout_p": w.dropout_p, "dropout_seed": w.dropout_seed}
+                      if w.dropout_p else {})},
         "pct_of_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
         "fwd_tflops": round(w.fwd_flop() / (kern["fwd_kernel"] * 1e-3) / 1e12, 2),
         "bwd_tflops": round(w.bwd_flop() / (bwd_ms * 1e-3) / 1e12, 2),
@@ -552,7 +577,8 @@ def run_sweep(args):
                                       for c in ("full", "causal")] + ["gqa_varlen", "train_16k",
                                                                       "fwd_d256_N4096",
                                                                       "window_16k",
-                                                                      "softcap_16k"]
+                                                                      "softcap_16k",
+                                                                      "dropout_16k"]
     if args.names:
         names = args.names.split(",")
     for n in names:

@@ -45,6 +45,8 @@ class Workload:
     lens: Optional[tuple] = None   # varlen sequence lengths
     window: Optional[tuple] = None  # sliding window (left, right), -1 = unbounded
     softcap: float = 0.0            # soft cap c of the logits (0: none)
+    dropout_p: float = 0.0          # dropout on the softmax weights (0: none)
+    dropout_seed: int = 0
 
     @property
     def scale(self) -> float:
@@ -140,6 +142,10 @@ def _build() -> Dict[str, Workload]:
     # soft cap published for Gemma-2); FLOP by the same convention (tanh not counted)
     w["softcap_16k"] = Workload("softcap_16k", B=2, Hq=16, Hkv=16, N=16384, d=128,
                                 dtype="bf16", causal=True, seed=10, backward=True, softcap=50.0)
+    # the training step's shape with dropout p = 0.1 on the softmax weights
+    w["dropout_16k"] = Workload("dropout_16k", B=2, Hq=16, Hkv=16, N=16384, d=128,
+                                dtype="bf16", causal=True, seed=11, backward=True,
+                                dropout_p=0.1, dropout_seed=0x5EED)
     return w
 
 
