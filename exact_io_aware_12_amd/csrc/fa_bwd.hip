@@ -185,7 +185,9 @@ __device__ __forceinline__ void dkdv_produce(const T* qt_, const T* dot_, const 
       const float4 dv4 = *reinterpret_cast<const float4*>(ld + kDkvQ + qoff);
       const float lsev[4] = {lv.x, lv.y, lv.z, lv.w};
       const float dlv[4] = {dv4.x, dv4.y, dv4.z, dv4.w};
-      uint32_t dbytes = 0;   // queries q0 + qoff + 0..3 of this lane's key
+      // queries q0 + qoff + 0..3 of this lane's key; one generator call per run
+      // (sharing calls across the key quad, as the forward does, measured slower here)
+      uint32_t dbytes = 0;
       if constexpr (DROP) dbytes = drop_col_bytes(*dk, seq, head, q0 + qoff, key);
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
@@ -490,9 +492,9 @@ __device__ __forceinline__ void dq_tile(const T* kt, const T* vt, const u32x4 (&
     }
     uint32_t dbytes[4] = {0, 0, 0, 0};   // keys kv0 + 32·jb + 8·r + 4·half + 0..3
     if constexpr (DROP) {
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-        dbytes[r] = drop_row_bytes(*dk, seq, head, qrow, kv0 + jb * 32 + 8 * r + 4 * half);
+      const int jr[4] = {kv0 + jb * 32 + 4 * half, kv0 + jb * 32 + 8 + 4 * half,
+                         kv0 + jb * 32 + 16 + 4 * half, kv0 + jb * 32 + 24 + 4 * half};
+      drop_row_bytes_quad(*dk, seq, head, qrow, jr, dbytes);
     }
 #pragma unroll
     for (int i = 0; i < 16; ++i) {

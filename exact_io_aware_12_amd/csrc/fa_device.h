@@ -151,6 +151,34 @@ __device__ __forceinline__ uint32_t drop_col_bytes(const DropKey& dk, int seq, i
          (((w[2] >> sh) & 0xffu) << 16) | (((w[3] >> sh) & 0xffu) << 24);
 }
 
+__device__ __forceinline__ uint32_t pick4(const u32x4& w, int n) {
+  return n == 0 ? w[0] : n == 1 ? w[1] : n == 2 ? w[2] : w[3];
+}
+
+// drop_row_bytes for four key runs j[0..3] at once, shared by the four lanes of
+// a quad that hold the four queries of one 4 x 4 block row (query i, lane quad
+// index i % 4; j[] the same on all four lanes). Each lane runs the generator
+// for run j[i % 4] only; three exchanges inside the quad hand every lane its
+// word of the other three calls. out[m] is the row bytes for run j[m].
+__device__ __forceinline__ void drop_row_bytes_quad(const DropKey& dk, int seq, int head, int i,
+                                                    const int (&j)[4], uint32_t (&out)[4]) {
+  const int s = i & 3;
+  const int js = s == 0 ? j[0] : s == 1 ? j[1] : s == 2 ? j[2] : j[3];
+  const u32x4 w = philox4x32_10((uint32_t)js >> 2, (uint32_t)i >> 2, (uint32_t)head,
+                                (uint32_t)seq, dk.k0, dk.k1);
+  uint32_t got[4];   // got[r]: from lane s ^ r, i.e. run j[s ^ r]
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const uint32_t send = pick4(w, s ^ r);   // lane s ^ r wants word s ^ r
+    got[r] = r == 0 ? send : (uint32_t)__shfl_xor((int)send, r);
+  }
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    const int r = s ^ m;
+    out[m] = r == 0 ? got[0] : r == 1 ? got[1] : r == 2 ? got[2] : got[3];
+  }
+}
+
 __device__ __forceinline__ bool drop_keep(uint32_t bytes, int n, uint32_t t) {
   return ((bytes >> (8 * n)) & 0xffu) < t;
 }

@@ -114,14 +114,23 @@ __device__ __forceinline__ void fwd_tile(const T* kt, const T* vt, const u32x4 (
   // lr sums P as rounded to T for the MFMAs; O is normalised by it, so that
   // the rounding of a dominant P cancels in O instead of scaling it
   float r[kBC / 16];   // independent partial sums: short dependency chains
+  // dropout: the row bytes of key runs kv0 + 16·kk + 4·half (+ 8), kk = 0..3
+  uint32_t drb[2][4] = {{0, 0, 0, 0}, {0, 0, 0, 0}};
+  if constexpr (DROP) {
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const int jr[4] = {kv0 + 4 * half + 8 * e, kv0 + 16 + 4 * half + 8 * e,
+                         kv0 + 32 + 4 * half + 8 * e, kv0 + 48 + 4 * half + 8 * e};
+      drop_row_bytes_quad(*dk, seq, head, qrow, jr, drb[e]);
+    }
+  }
 #pragma unroll
   for (int kk = 0; kk < kBC / 16; ++kk) {
     u32x4 pf = acc_operand<T>(s[kk >> 1], (kk & 1) * 2);
     r[kk] = dot2_sum<T>(pf, 0.f);
     const int k0 = kk * 16 + 4 * half;
     if constexpr (DROP) {   // keys kv0 + k0 + 0..3 (dwords 0, 1) and + 8..11 (dwords 2, 3)
-      const uint32_t b0 = drop_row_bytes(*dk, seq, head, qrow, kv0 + k0);
-      const uint32_t b1 = drop_row_bytes(*dk, seq, head, qrow, kv0 + k0 + 8);
+      const uint32_t b0 = drb[0][kk], b1 = drb[1][kk];
 #pragma unroll
       for (int w = 0; w < 4; ++w) {
         const uint32_t by = w < 2 ? b0 : b1;
