@@ -205,7 +205,7 @@ int fa_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse,
 
 size_t fa_bwd_workspace_size(int B, int Hq, int Hkv, int N, int d) {
   bool noop;
-  if (check_sizes(B, Hq, Hkv, N, d, 1.f, 0, FA_FP16, &noop) != FA_OK) return 0;
+  if (check_sizes(B, Hq, Hkv, N, d, 1.f, 0, FA_FP16, &noop, 256) != FA_OK) return 0;
   // D = rowsum(dO∘O) and LSE·log2(e): two float32 [Hq][B·N + 64] arrays
   // (tiles may read up to 63 rows past a sequence end); 256-byte granule
   const size_t bytes = 2 * (size_t)Hq * ((size_t)B * N + 64) * sizeof(float);
@@ -221,8 +221,9 @@ int bwd_common(int stage, const void* q, const void* k, const void* v, const voi
                hipStream_t stream, float softcap = 0.f, float dropout_p = 0.f,
                uint64_t seed = 0) {
   bool noop;
-  int st = check_sizes(B, Hq, Hkv, N, d, scale, 0, dtype, &noop);
+  int st = check_sizes(B, Hq, Hkv, N, d, scale, 0, dtype, &noop, 256);
   if (st != FA_OK) return st;
+  if (d == 256 && mask == fa::kMaskWindow) return FA_ERR_UNSUPPORTED;   // plain masks at 256
   float cap_in, cap_out;
   st = cap_constants(softcap, scale, mask, d, &cap_in, &cap_out);
   if (st != FA_OK) return st;

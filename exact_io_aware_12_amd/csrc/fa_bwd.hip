@@ -445,6 +445,181 @@ __global__ __launch_bounds__(kDkvThreads, 1) void dkdv_kernel(BwdArgs a, int n_k
 }
 
 // ---------------------------------------------------------------------------
+// dK, dV at d = 256. The two-role kernel above cannot hold 32 keys' dKᵀ and
+// dVᵀ (256 accumulator registers) with two waves per SIMD, and one wave
+// holding both with K and V fragments does not fit 512 registers either. So
+// two passes over the same tiles, one wave per SIMD owning 32 keys: PASS 0
+// computes S (K fragments in registers), P and dVᵀ += dOᵀ·P; PASS 1 computes
+// S and dP (K and V fragments), dS and dKᵀ += Qᵀ·dS. S is computed twice (one
+// more GEMM on top of the four). Keys are MFMA columns, so P and dS come out
+// in the B-operand layout of the dV/dK products, whose Qᵀ, dOᵀ operands are
+// transposing LDS reads. Q/dO tiles of 64 queries are double-buffered in LDS
+// (128 KiB at d = 256). Plain masks only (none, causal), varlen, GQA.
+constexpr int kWideKeys = 128;   // keys per workgroup (32 per wave)
+constexpr int kWideQ = 64;       // queries per tile
+
+template <typename T, int D, bool CAUSAL, bool EDGE, int PASS>
+__device__ __forceinline__ void dkdv_wide_tile(const T* qt_, const T* dot_, const float* ld,
+                                               const u32x4 (&kf)[D / 16],
+                                               const u32x4 (&vf)[D / 16], f32x16 (&acc)[D / 32],
+                                               float c, int q0, int L, int key, int lane) {
+  constexpr int NKB = D / 16;
+  constexpr int NCB = D / 32;
+  const int col = lane & 31, half = lane >> 5;
+#pragma unroll
+  for (int qb = 0; qb < kWideQ / 32; ++qb) {
+    f32x16 s = f32x16{}, dp = f32x16{};
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) {
+      s = mfma32<T>(lds_row16<T, D>(qt_, qb * 32 + col, 2 * kb + half), kf[kb], s);
+      if constexpr (PASS == 1)
+        dp = mfma32<T>(lds_row16<T, D>(dot_, qb * 32 + col, 2 * kb + half), vf[kb], dp);
+    }
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) {
+      const int qoff = qb * 32 + 8 * rr + 4 * half;
+      const float4 lv = *reinterpret_cast<const float4*>(ld + qoff);
+      const float4 dv4 = *reinterpret_cast<const float4*>(ld + kWideQ + qoff);
+      const float lsev[4] = {lv.x, lv.y, lv.z, lv.w};
+      const float dlv[4] = {dv4.x, dv4.y, dv4.z, dv4.w};
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const int i4 = 4 * rr + t;
+        float p = fast_exp2(fmaf(s[i4], c, -lsev[t]));
+        float ds = p * (dp[i4] - dlv[t]);
+        if constexpr (EDGE) {
+          const int q = q0 + qoff + t;
+          const bool keep = q < L && !(CAUSAL && key > q);
+          p = keep ? p : 0.f;
+          ds = keep ? ds : 0.f;
+        }
+        s[i4] = p;
+        dp[i4] = ds;
+      }
+    }
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2) {
+      // PASS 0: dVᵀ += dOᵀ·P; PASS 1: dKᵀ += Qᵀ·dS
+      const u32x4 b = acc_operand<T>(PASS == 0 ? s : dp, h2 * 2);
+      const int kq = qb * 32 + h2 * 16 + 4 * half;
+#pragma unroll
+      for (int cb = 0; cb < NCB; ++cb)
+        acc[cb] = mfma32<T>(lds_tr8<T, D>(PASS == 0 ? dot_ : qt_, kq, kq + 8, cb * 32, lane), b,
+                            acc[cb]);
+    }
+  }
+}
+
+template <typename T, int D, bool CAUSAL, bool VARLEN, int PASS>
+__global__ __launch_bounds__(kThreads, 1) void dkdv_wide_kernel(BwdArgs a, int n_ktiles) {
+  constexpr int NKB = D / 16;
+  constexpr int NCB = D / 32;
+  constexpr int TILE = kWideQ * D;
+  __shared__ __attribute__((aligned(1024))) T q_lds[2][TILE];
+  __shared__ __attribute__((aligned(1024))) T do_lds[2][TILE];
+  __shared__ __attribute__((aligned(16))) float ld_lds[2][2 * kWideQ];   // LSE·log2 e, D
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int col = lane & 31, half = lane >> 5;
+
+  const int G = gridDim.x;
+  const int logical = xcd_remap(blockIdx.x, G);
+  const int kt = logical % n_ktiles;           // ascending = heaviest first when causal
+  const int gb = logical / n_ktiles;
+  const int b = gb % a.B, g = gb / a.B;   // sequence fastest, as in the other kernels
+  const SeqInfo si = seq_info<VARLEN>(a, b);
+  const int k0 = kt * kWideKeys;
+  if (k0 >= si.L) return;
+  const int L = si.L;
+
+  const int64_t qs = (int64_t)a.Hq * D, kvs = (int64_t)a.Hkv * D;
+  const int key = k0 + wave * 32 + col;
+  // Query tiles of one head: [qt_begin, qt_end). Edge tiles (the causal
+  // diagonal below k0 + 128, a ragged last tile) of every head of the group
+  // come first, then the interior tiles, which need no mask.
+  const int qt_begin = CAUSAL ? k0 / kWideQ : 0;
+  const int qt_end = (L + kWideQ - 1) / kWideQ;
+  const int nq = qt_end - qt_begin;
+  const int nd = CAUSAL ? min(kWideKeys / kWideQ, nq) : 0;
+  const int ne = nd + ((L % kWideQ != 0 && nq > nd) ? 1 : 0);
+  const int ni = nq - ne;
+  const int n_edge = a.group * ne, ntile = a.group * nq;
+  auto tile_of = [&](int i, int& r) -> int {   // tile i -> (head r, query tile)
+    if (i < n_edge) {
+      r = i / ne;
+      const int e = i - r * ne;
+      return e < nd ? qt_begin + e : qt_end - 1;
+    }
+    const int j = i - n_edge;
+    r = j / ni;
+    return qt_begin + nd + (j - r * ni);
+  };
+  auto issue = [&](int i, int buf) {
+    int r;
+    const int q0 = tile_of(i, r) * kWideQ;
+    const int h = g * a.group + r;
+    const T* qp = static_cast<const T*>(a.q) + (int64_t)si.seq0 * qs + (int64_t)h * D;
+    const T* dop = static_cast<const T*>(a.dout) + (int64_t)si.seq0 * qs + (int64_t)h * D;
+    tile_dma<T, kWideQ, D, kWaves>(q_lds[buf], qp, qs, q0, L, wave, lane);
+    tile_dma<T, kWideQ, D, kWaves>(do_lds[buf], dop, qs, q0, L, wave, lane);
+    if (wave == 0) {
+      const int64_t w0 = (int64_t)h * a.ws_stride + si.seq0 + q0;
+      rows_dma<kWideQ>(ld_lds[buf], a.lse2 + w0, a.delta + w0, lane);
+    }
+  };
+  if (ntile > 0) issue(0, 0);
+
+  // K and V fragments of this wave's 32 keys (B operands), kept in registers
+  u32x4 kf[NKB], vf[NKB];
+  {
+    const T* kp = static_cast<const T*>(a.k) + (int64_t)(si.seq0 + key) * kvs + (int64_t)g * D;
+    const T* vp = static_cast<const T*>(a.v) + (int64_t)(si.seq0 + key) * kvs + (int64_t)g * D;
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) {
+      kf[kb] = key < L ? ldg16(kp + kb * 16 + half * 8) : u32x4{0, 0, 0, 0};
+      vf[kb] = (PASS == 1 && key < L) ? ldg16(vp + kb * 16 + half * 8) : u32x4{0, 0, 0, 0};
+    }
+  }
+  f32x16 acc[NCB];   // dVᵀ (PASS 0) or dKᵀ (PASS 1)
+#pragma unroll
+  for (int cb = 0; cb < NCB; ++cb) acc[cb] = f32x16{};
+  const float c = a.scale_log2;
+  const int wk_first = k0 + wave * 32;
+
+  auto step = [&](auto edge_tag, int i) {
+    constexpr bool EDGE = decltype(edge_tag)::value;
+    const int buf = i & 1;
+    wait_vmem_all();   // this thread's copies of tile i have landed
+    __syncthreads();   // everyone's have; tile i-1 is no longer read
+    if (i + 1 < ntile) issue(i + 1, buf ^ 1);
+    int r;
+    const int q0 = tile_of(i, r) * kWideQ;
+    // a diagonal tile can lie entirely before this wave's keys
+    if (EDGE && CAUSAL && q0 + kWideQ - 1 < wk_first) return;
+    dkdv_wide_tile<T, D, CAUSAL, EDGE, PASS>(q_lds[buf], do_lds[buf], ld_lds[buf], kf, vf, acc,
+                                             c, q0, L, key, lane);
+  };
+  for (int i = 0; i < n_edge; ++i) step(std::true_type{}, i);
+  for (int i = n_edge; i < ntile; ++i) step(std::false_type{}, i);
+
+  if (key < L) {
+    const int64_t off = (int64_t)(si.seq0 + key) * kvs + (int64_t)g * D;
+    T* outp = static_cast<T*>(PASS == 0 ? a.dv : a.dk) + off;
+    const float sc = PASS == 0 ? 1.f : a.scale;   // dK = scale · Σ dSᵀ Q
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        const int d0 = cb * 32 + 8 * rr + 4 * half;
+        u32x2 w;
+        w[0] = pack2<T>(acc[cb][4 * rr + 0] * sc, acc[cb][4 * rr + 1] * sc);
+        w[1] = pack2<T>(acc[cb][4 * rr + 2] * sc, acc[cb][4 * rr + 3] * sc);
+        *reinterpret_cast<u32x2*>(outp + d0) = w;
+      }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // dQ. Orientation Sᵀ = K·Qᵀ as in the forward: one query per lane, so LSE and
 // D are per-lane scalars and the dSᵀ accumulator is the B operand of
 // dQᵀ = Kᵀ·dSᵀ (Kᵀ read transposed from the row-major K tile).
@@ -532,9 +707,11 @@ __device__ __forceinline__ void dq_tile(const T* kt, const T* vt, const u32x4 (&
   }
 }
 
+// two workgroups per CU up to d = 128; at d = 256 the dQ accumulators and the
+// Q and dO fragments take 256 registers and the kernel runs one per CU
 template <typename T, int D, bool CAUSAL, bool VARLEN, bool WIN, bool CAP = false,
           bool DROP = false>
-__global__ __launch_bounds__(kThreads, 2) void dq_kernel(BwdArgs a, int n_qtiles) {
+__global__ __launch_bounds__(kThreads, D <= 128 ? 2 : 1) void dq_kernel(BwdArgs a, int n_qtiles) {
   constexpr int NKB = D / 16;
   constexpr int NCB = D / 32;
   constexpr int TILE = kDqK * D;
@@ -680,9 +857,20 @@ hipError_t launch(const BwdArgs& a, int stage, hipStream_t s) {
     if (e != hipSuccess) return e;
   }
   if (stage < 0 || stage == 1) {
-    const int nkt = (a.N + kDkvKeys - 1) / kDkvKeys;
-    hipLaunchKernelGGL((dkdv_kernel<T, D, CAUSAL, VARLEN, WIN, CAP, DROP>), dim3(nkt * a.Hkv * a.B),
-                       dim3(kDkvThreads), 0, s, a, nkt);
+    if constexpr (D == 256) {
+      static_assert(!WIN && !CAP && !DROP, "d = 256: plain masks only");
+      const int nkt = (a.N + kWideKeys - 1) / kWideKeys;
+      hipLaunchKernelGGL((dkdv_wide_kernel<T, D, CAUSAL, VARLEN, 0>), dim3(nkt * a.Hkv * a.B),
+                         dim3(kThreads), 0, s, a, nkt);
+      const hipError_t e0 = hipGetLastError();
+      if (e0 != hipSuccess) return e0;
+      hipLaunchKernelGGL((dkdv_wide_kernel<T, D, CAUSAL, VARLEN, 1>), dim3(nkt * a.Hkv * a.B),
+                         dim3(kThreads), 0, s, a, nkt);
+    } else {
+      const int nkt = (a.N + kDkvKeys - 1) / kDkvKeys;
+      hipLaunchKernelGGL((dkdv_kernel<T, D, CAUSAL, VARLEN, WIN, CAP, DROP>),
+                         dim3(nkt * a.Hkv * a.B), dim3(kDkvThreads), 0, s, a, nkt);
+    }
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -727,8 +915,20 @@ hipError_t dispatch_mask(const BwdArgs& a, int mask, bool varlen, bool cap, bool
 
 int bwd_num_stages() { return 3; }
 
+// d = 256: unmasked or causal only (the caller rejects the rest)
+template <typename T>
+hipError_t dispatch_256(const BwdArgs& a, int mask, bool varlen, int stage, hipStream_t s) {
+  if (mask == kMaskCausal)
+    return varlen ? launch<T, 256, true, true, false>(a, stage, s)
+                  : launch<T, 256, true, false, false>(a, stage, s);
+  return varlen ? launch<T, 256, false, true, false>(a, stage, s)
+                : launch<T, 256, false, false, false>(a, stage, s);
+}
+
 hipError_t launch_bwd(const BwdArgs& a, bool bf16_in, int d, int mask, bool varlen, bool cap,
                       bool drop, int stage, hipStream_t s) {
+  if (d == 256) return bf16_in ? dispatch_256<bf16>(a, mask, varlen, stage, s)
+                               : dispatch_256<f16>(a, mask, varlen, stage, s);
   if (bf16_in)
     return d == 64 ? dispatch_mask<bf16, 64>(a, mask, varlen, cap, drop, stage, s)
                    : dispatch_mask<bf16, 128>(a, mask, varlen, cap, drop, stage, s);

@@ -99,7 +99,7 @@ def test_fwd_host_checks(kw, status):
     (dict(dv=None), fa.FA_ERR_INVALID_ARG),
     (dict(do=P + 2), fa.FA_ERR_INVALID_ARG),
     (dict(d=32), fa.FA_ERR_UNSUPPORTED),
-    (dict(d=256), fa.FA_ERR_UNSUPPORTED),        # the backward stops at d = 128
+    (dict(d=512), fa.FA_ERR_UNSUPPORTED),
     (dict(ws=None), fa.FA_ERR_WORKSPACE),
     (dict(wsb=64), fa.FA_ERR_WORKSPACE),
     (dict(B=0), fa.FA_OK),
@@ -234,7 +234,7 @@ def test_fwd_window_host_checks(kw, status):
 
 @pytest.mark.parametrize("kw,status", [
     (dict(wl=-3), fa.FA_ERR_INVALID_ARG),
-    (dict(d=256), fa.FA_ERR_UNSUPPORTED),        # the backward stops at d = 128
+    (dict(d=256), fa.FA_ERR_UNSUPPORTED),        # at d = 256 the backward takes plain masks only
     (dict(ws=None), fa.FA_ERR_WORKSPACE),
     (dict(dk=P + 8), fa.FA_ERR_INVALID_ARG),
     (dict(B=0), fa.FA_OK),
@@ -434,3 +434,13 @@ def test_binding_dropout_needs_a_seed():
     assert fa._dropout_args(0.0, None, None, 0.0) is None
     assert fa._dropout_args(0.25, 7, None, 0.0) == (0.25, 7)
     del q
+
+
+def test_bwd_d256_reaches_the_launch():
+    """The plain backward accepts d = 256 (window, soft cap and dropout do not)."""
+    torch = pytest.importorskip("torch")
+    assert fa.fa_bwd_workspace_size(1, 2, 2, 16, 256) == fa.fa_bwd_workspace_size(1, 2, 2, 16, 64)
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    assert bwd(d=256) == fa.FA_ERR_HIP
+    assert bwd(d=256, causal=1) == fa.FA_ERR_HIP

@@ -142,6 +142,9 @@ def _build() -> Dict[str, Workload]:
     # soft cap published for Gemma-2); FLOP by the same convention (tanh not counted)
     w["softcap_16k"] = Workload("softcap_16k", B=2, Hq=16, Hkv=16, N=16384, d=128,
                                 dtype="bf16", causal=True, seed=10, backward=True, softcap=50.0)
+    # head dim 256 forward and backward (the pages' envelope ends at 256)
+    w["train_d256"] = Workload("train_d256", B=4, Hq=16, Hkv=16, N=4096, d=256, dtype="bf16",
+                               causal=True, seed=12, backward=True)
     # the training step's shape with dropout p = 0.1 on the softmax weights
     w["dropout_16k"] = Workload("dropout_16k", B=2, Hq=16, Hkv=16, N=16384, d=128,
                                 dtype="bf16", causal=True, seed=11, backward=True,
