@@ -29,12 +29,13 @@ from .attention import (attention_fwd, attention_bwd, attention_probs,
                         attention_fwd_rows, attention_bwd_sampled)
 from .decode import kvcache_fwd, kvcache_fwd_units
 from . import bruteforce
-from .dropout import (attention_bwd_dropout, attention_fwd_dropout, keep_mask,
-                      keep_threshold, philox4x32_10)
+from .dropout import (attention_bwd_dropout, attention_fwd_dropout, head_bwd_dropout,
+                      head_fwd_dropout, keep_mask, keep_threshold, philox4x32_10)
 from .fp8 import attention_fwd_fp8, e4m3fn_decode, dequantize, head_o_bound, o_bound
 
 __all__ = ["attention_fwd", "attention_bwd", "attention_probs", "attention_fwd_rows",
            "attention_bwd_sampled", "kvcache_fwd", "kvcache_fwd_units", "bruteforce",
            "attention_fwd_fp8", "e4m3fn_decode", "dequantize", "head_o_bound", "o_bound",
-           "attention_fwd_dropout", "attention_bwd_dropout", "keep_mask", "keep_threshold",
+           "attention_fwd_dropout", "attention_bwd_dropout", "head_fwd_dropout",
+           "head_bwd_dropout", "keep_mask", "keep_threshold",
            "philox4x32_10"]

@@ -32,7 +32,7 @@ from __future__ import annotations
 
 import numpy as np
 
-from .attention import _f64, _group, _lse, _scores, _segments
+from .attention import _f64, _group, _lse, _row_blocks, _scores, _segments
 
 PHILOX_M0 = 0xD2511F53
 PHILOX_M1 = 0xCD9E8D57
@@ -74,13 +74,60 @@ def keep_threshold(dropout_p: float) -> int:
 
 def keep_mask(seed: int, seq: int, head: int, rows, cols, t: int) -> np.ndarray:
     """M[r, c] for query positions rows[r] and key positions cols[c] of one
-    (sequence, query head): True where the weight is kept."""
-    i = np.asarray(rows, dtype=np.int64)[:, None]
-    j = np.asarray(cols, dtype=np.int64)[None, :]
-    words = philox4x32_10((j >> 2, i >> 2, head, seq), (seed & 0xFFFFFFFF, seed >> 32))
-    w = np.choose(i & 3, words)
-    byte = (w >> (8 * (j & 3)).astype(np.uint32)) & np.uint32(0xFF)
+    (sequence, query head): True where the weight is kept. The generator runs
+    once per 4 x 4 block touched (the block's four words serve its 16 elements)."""
+    i = np.asarray(rows, dtype=np.int64)
+    j = np.asarray(cols, dtype=np.int64)
+    ub_i, inv_i = np.unique(i >> 2, return_inverse=True)
+    ub_j, inv_j = np.unique(j >> 2, return_inverse=True)
+    words = np.stack(philox4x32_10((ub_j[None, :], ub_i[:, None], head, seq),
+                                   (seed & 0xFFFFFFFF, seed >> 32)))   # [4, blocks_i, blocks_j]
+    w = words[(i & 3)[:, None], inv_i[:, None], inv_j[None, :]]
+    byte = (w >> (8 * (j & 3)).astype(np.uint32)[None, :]) & np.uint32(0xFF)
     return byte < t
+
+
+def head_fwd_dropout(Qs, Ks, Vs, scale: float, causal: bool, seq: int, head: int,
+                     dropout_p: float, seed: int, rows=None):
+    """One (sequence, query head): O [R, d] and LSE [R] for ``rows`` (default all)."""
+    Qs, Ks, Vs = _f64(Qs), _f64(Ks), _f64(Vs)
+    t = keep_threshold(dropout_p)
+    L = Ks.shape[0]
+    rows = np.arange(Qs.shape[0]) if rows is None else np.asarray(rows, dtype=np.int64)
+    O = np.empty((len(rows), Vs.shape[1]))
+    lse = np.empty(len(rows))
+    pos = 0
+    for blk in _row_blocks(rows, L):
+        S = _scores(Qs[blk], blk, Ks, scale, causal)
+        l = _lse(S)
+        Z = keep_mask(seed, seq, head, blk, np.arange(L), t) * (256.0 / t)
+        O[pos:pos + len(blk)] = (np.exp(S - l[:, None]) * Z) @ Vs
+        lse[pos:pos + len(blk)] = l
+        pos += len(blk)
+    return O, lse
+
+
+def head_bwd_dropout(Qs, Ks, Vs, dOs, scale: float, causal: bool, seq: int, head: int,
+                     dropout_p: float, seed: int):
+    """One (sequence, query head): dQ, dK, dV [L, d] of the dropout forward."""
+    Qs, Ks, Vs, dOs = _f64(Qs), _f64(Ks), _f64(Vs), _f64(dOs)
+    t = keep_threshold(dropout_p)
+    L = Qs.shape[0]
+    dQ = np.empty_like(Qs)
+    dK = np.zeros_like(Ks)
+    dV = np.zeros_like(Vs)
+    for blk in _row_blocks(np.arange(L), L):
+        S = _scores(Qs[blk], blk, Ks, scale, causal)
+        P = np.exp(S - _lse(S)[:, None])
+        Z = keep_mask(seed, seq, head, blk, np.arange(L), t) * (256.0 / t)
+        dO = dOs[blk]
+        dV += (P * Z).T @ dO
+        dP = dO @ Vs.T
+        D = (P * Z * dP).sum(axis=1)
+        dS = P * (Z * dP - D[:, None])
+        dQ[blk] = scale * (dS @ Ks)
+        dK += scale * (dS.T @ Qs[blk])
+    return dQ, dK, dV
 
 
 def attention_fwd_dropout(q, k, v, scale: float, causal: bool, cu_seqlens, dropout_p: float,
@@ -89,20 +136,15 @@ def attention_fwd_dropout(q, k, v, scale: float, causal: bool, cu_seqlens, dropo
     q, k, v = _f64(q), _f64(k), _f64(v)
     T, Hq, d = q.shape
     g = _group(Hq, k.shape[1])
-    t = keep_threshold(dropout_p)
     o = np.zeros((T, Hq, v.shape[2]))
     lse = np.zeros((Hq, T))
     for s, (a, b) in enumerate(_segments(T, cu_seqlens)):
         if b <= a:
             continue
-        L = b - a
         for h in range(Hq):
-            rows = np.arange(L)
-            S = _scores(q[a:b, h], rows, k[a:b, h // g], scale, causal)
-            l = _lse(S)
-            P = np.exp(S - l[:, None])
-            Z = keep_mask(seed, s, h, rows, rows, t) * (256.0 / t)
-            o[a:b, h] = (P * Z) @ v[a:b, h // g]
+            O, l = head_fwd_dropout(q[a:b, h], k[a:b, h // g], v[a:b, h // g], scale, causal, s,
+                                    h, dropout_p, seed)
+            o[a:b, h] = O
             lse[h, a:b] = l
     return o, lse
 
@@ -113,22 +155,14 @@ def attention_bwd_dropout(q, k, v, do, scale: float, causal: bool, cu_seqlens, d
     q, k, v, do = _f64(q), _f64(k), _f64(v), _f64(do)
     T, Hq, d = q.shape
     g = _group(Hq, k.shape[1])
-    t = keep_threshold(dropout_p)
     dq, dk, dv = np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)
     for s, (a, b) in enumerate(_segments(T, cu_seqlens)):
         if b <= a:
             continue
-        L = b - a
         for h in range(Hq):
-            Qs, Ks, Vs, dO = q[a:b, h], k[a:b, h // g], v[a:b, h // g], do[a:b, h]
-            rows = np.arange(L)
-            S = _scores(Qs, rows, Ks, scale, causal)
-            P = np.exp(S - _lse(S)[:, None])
-            Z = keep_mask(seed, s, h, rows, rows, t) * (256.0 / t)
-            dv[a:b, h // g] += (P * Z).T @ dO
-            dP = dO @ Vs.T
-            D = (P * Z * dP).sum(axis=1)
-            dS = P * (Z * dP - D[:, None])
-            dq[a:b, h] = scale * (dS @ Ks)
-            dk[a:b, h // g] += scale * (dS.T @ Qs)
+            dQ, dK, dV = head_bwd_dropout(q[a:b, h], k[a:b, h // g], v[a:b, h // g], do[a:b, h],
+                                          scale, causal, s, h, dropout_p, seed)
+            dq[a:b, h] = dQ
+            dk[a:b, h // g] += dK
+            dv[a:b, h // g] += dV
     return dq, dk, dv
