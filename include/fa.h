@@ -32,10 +32,11 @@
  * Causal: key j is visible from query i iff j <= i, positions counted from
  *   the start of the sequence.
  * Supported: dtype FA_FP16 or FA_BF16; scale finite and > 0; head dim d = 64,
- *   128 or 256 for fa_fwd and fa_fwd_kvcache, d = 64 or 128 for fa_bwd (the
- *   pages' envelope reaches d = 256, Flash Attention 是什麼, adersaytech.com,
- *   section 硬體與版本需求; the backward keeps dK, dV and dQ accumulators in
- *   registers, which do not fit at d = 256).
+ *   128 or 256 for fa_fwd, fa_bwd and fa_fwd_kvcache (the pages' envelope
+ *   reaches d = 256, Flash Attention 是什麼, adersaytech.com, section
+ *   硬體與版本需求). At d = 256 the backward computes dK and dV in two passes
+ *   (dV, then dK) so that each pass's accumulators fit the register file.
+ *   The window, soft-cap and dropout backward take d = 64 or 128 only.
  *
  * Alignment: every tensor pointer must be 16-byte aligned (FA_ERR_INVALID_ARG
  *   otherwise); rows are moved as 16-byte vectors.
