@@ -291,15 +291,19 @@ class DecodeBound:
         import workloads as W
         self.fa, self.w, self.torch = fa, w, torch
         td = {"fp16": torch.float16, "bf16": torch.bfloat16}[w.dtype]
-        a = W.generate_decode(w)
+        self.kv8 = w.kv_cache == "e4m3"
+        a = W.decode_fp8_inputs(w) if self.kv8 else W.generate_decode(w)
         self.q = torch.from_numpy(a["q"]).to(td).cuda()
-        self.k = torch.from_numpy(a["k"]).to(td).cuda()
-        self.v = torch.from_numpy(a["v"]).to(td).cuda()
+        ct = torch.uint8 if self.kv8 else td
+        self.k = torch.from_numpy(a["k"]).to(ct).cuda()
+        self.v = torch.from_numpy(a["v"]).to(ct).cuda()
+        self.descales = (a["descale_k"], a["descale_v"]) if self.kv8 else None
         self.lens = torch.from_numpy(a["cache_seqlens"]).cuda()
         del a
         self.o = torch.empty_like(self.q)
         self.lse = torch.empty((w.Hq, w.B * w.Nq), dtype=torch.float32, device="cuda")
-        self.splits = fa.fa_kvcache_num_splits(w.B, w.Hq, w.Hkv, w.Nq, w.Nk, w.d)
+        ns = fa.fa_kvcache_fp8_num_splits if self.kv8 else fa.fa_kvcache_num_splits
+        self.splits = ns(w.B, w.Hq, w.Hkv, w.Nq, w.Nk, w.d)
         nws = fa.fa_fwd_kvcache_workspace_size(w.B, w.Hq, w.Hkv, w.Nq, w.Nk, w.d, self.splits)
         self.ws = torch.empty(nws, dtype=torch.uint8, device="cuda")
         self.code = fa.FA_BF16 if w.dtype == "bf16" else fa.FA_FP16
@@ -307,20 +311,23 @@ class DecodeBound:
 
     def _args(self):
         w = self.w
+        desc = self.descales if self.kv8 else ()
         return (self.q.data_ptr(), self.k.data_ptr(), self.v.data_ptr(), self.lens.data_ptr(),
                 self.o.data_ptr(), self.lse.data_ptr(), w.B, w.Hq, w.Hkv, w.Nq, w.Nk, w.d, w.scale,
-                int(w.causal), self.splits, self.code, self.ws.data_ptr(), self.ws.numel(),
+                int(w.causal), *desc, self.splits, self.code, self.ws.data_ptr(), self.ws.numel(),
                 self.stream)
 
     def call(self):
-        st = self.fa.fa_fwd_kvcache(*self._args())
+        fn = "fa_fwd_kvcache_fp8" if self.kv8 else "fa_fwd_kvcache"
+        st = getattr(self.fa, fn)(*self._args())
         if st != self.fa.FA_OK:
-            raise self.fa.FaError(st, "fa_fwd_kvcache")
+            raise self.fa.FaError(st, fn)
 
     def stage(self, i):
-        st = self.fa.fa_fwd_kvcache_stage(i, *self._args())
+        fn = "fa_fwd_kvcache_fp8_stage" if self.kv8 else "fa_fwd_kvcache_stage"
+        st = getattr(self.fa, fn)(i, *self._args())
         if st != self.fa.FA_OK:
-            raise self.fa.FaError(st, "fa_fwd_kvcache_stage")
+            raise self.fa.FaError(st, fn)
 
 
 def cpu_baseline_decode(w, min_seconds=10.0, max_rounds=50):
@@ -333,11 +340,23 @@ def cpu_baseline_decode(w, min_seconds=10.0, max_rounds=50):
         cores = max((d.get("num_threads", 1) for d in threadpool_info()), default=1)
     except Exception:  # pragma: no cover
         cores = 1
-    a = W.generate_decode(w)
+    if w.kv_cache == "e4m3":   # the oracle on the decoded cache (decoding is inside the timing)
+        import oracle.fp8 as O8
+        a = W.decode_fp8_inputs(w)
+
+        def run():
+            OD.kvcache_fwd(a["q"], O8.dequantize(a["k"], a["descale_k"]),
+                           O8.dequantize(a["v"], a["descale_v"]), a["cache_seqlens"], w.scale,
+                           w.causal)
+    else:
+        a = W.generate_decode(w)
+
+        def run():
+            OD.kvcache_fwd(a["q"], a["k"], a["v"], a["cache_seqlens"], w.scale, w.causal)
     rounds, dt = 0, 0.0
     while rounds < max_rounds and (rounds == 0 or dt < min_seconds):
         t0 = time.perf_counter()
-        OD.kvcache_fwd(a["q"], a["k"], a["v"], a["cache_seqlens"], w.scale, w.causal)
+        run()
         dt += time.perf_counter() - t0
         rounds += 1
     return {"value": round(rounds * w.io_bytes() / dt / 1e9, 4), "unit": "GB/s",
@@ -387,9 +406,11 @@ def run_decode_bench(args):
         "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms_entry, 5), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",
-        "config": {"workload": f"{w.name}: fa_fwd_kvcache", "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv,
-                   "Nq": w.Nq, "Nk": w.Nk, "d": w.d, "causal": w.causal, "seed": w.seed,
-                   "splits": b.splits, "cache_lens": w.cache_lens()},
+        "config": {"workload": f"{w.name}: " + ("fa_fwd_kvcache_fp8" if b.kv8 else "fa_fwd_kvcache"),
+                   "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "Nq": w.Nq, "Nk": w.Nk, "d": w.d,
+                   "causal": w.causal, "seed": w.seed, "splits": b.splits,
+                   "kv_cache": w.dtype if not b.kv8 else "e4m3fn",
+                   "cache_lens": w.cache_lens()},
         "pct_of_hbm_peak": round(100 * value / PEAK_HBM_GBS, 2),
         "attention_tflops": round(w.flop() / (ms_entry * 1e-3) / 1e12, 3),
         "kernel_ms": {k: round(v, 5) for k, v in kern.items()},

@@ -39,7 +39,8 @@ __all__ = ["FA_OK", "FA_ERR_INVALID_ARG", "FA_ERR_UNSUPPORTED", "FA_ERR_HIP", "F
            "fa_bwd_workspace_size", "fa_status_string", "flash_attn_func",
            "flash_attn_backward", "fa_bwd_stage", "fa_bwd_num_stages", "fa_fwd_kvcache",
            "fa_kvcache_num_splits", "fa_fwd_kvcache_workspace_size", "flash_attn_with_kvcache",
-           "fa_fwd_kvcache_stage", "fa_fwd_kvcache_num_stages"]
+           "fa_fwd_kvcache_stage", "fa_fwd_kvcache_num_stages", "fa_fwd_kvcache_fp8",
+           "fa_fwd_kvcache_fp8_stage", "fa_kvcache_fp8_num_splits"]
 
 FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_HIP, FA_ERR_WORKSPACE = 0, -1, -2, -3, -4
 FA_FP16, FA_BF16 = 0, 1
@@ -107,10 +108,17 @@ def _load():
     L.fa_fwd_kvcache.restype = i
     L.fa_fwd_kvcache_stage.argtypes = [i] + L.fa_fwd_kvcache.argtypes
     L.fa_fwd_kvcache_stage.restype = i
+    L.fa_fwd_kvcache_fp8.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, f, f, i, i, vp,
+                                     sz, vp]
+    L.fa_fwd_kvcache_fp8.restype = i
+    L.fa_fwd_kvcache_fp8_stage.argtypes = [i] + L.fa_fwd_kvcache_fp8.argtypes
+    L.fa_fwd_kvcache_fp8_stage.restype = i
     L.fa_fwd_kvcache_num_stages.argtypes = []
     L.fa_fwd_kvcache_num_stages.restype = i
     L.fa_kvcache_num_splits.argtypes = [i, i, i, i, i, i]
     L.fa_kvcache_num_splits.restype = i
+    L.fa_kvcache_fp8_num_splits.argtypes = [i, i, i, i, i, i]
+    L.fa_kvcache_fp8_num_splits.restype = i
     L.fa_fwd_kvcache_workspace_size.argtypes = [i, i, i, i, i, i, i]
     L.fa_fwd_kvcache_workspace_size.restype = sz
     L.fa_status_string.argtypes = [i]
@@ -242,12 +250,32 @@ def fa_fwd_kvcache_stage(stage, q, k_cache, v_cache, cache_seqlens, o, lse, B, H
                                     workspace_bytes, stream)
 
 
+def fa_fwd_kvcache_fp8(q, k_cache, v_cache, cache_seqlens, o, lse, B, Hq, Hkv, Nq, Nk, d, scale,
+                       causal, descale_k, descale_v, num_splits, dtype, workspace,
+                       workspace_bytes, stream) -> int:
+    return lib.fa_fwd_kvcache_fp8(q, k_cache, v_cache, cache_seqlens, o, lse, B, Hq, Hkv, Nq, Nk,
+                                  d, scale, causal, descale_k, descale_v, num_splits, dtype,
+                                  workspace, workspace_bytes, stream)
+
+
+def fa_fwd_kvcache_fp8_stage(stage, q, k_cache, v_cache, cache_seqlens, o, lse, B, Hq, Hkv, Nq,
+                             Nk, d, scale, causal, descale_k, descale_v, num_splits, dtype,
+                             workspace, workspace_bytes, stream) -> int:
+    return lib.fa_fwd_kvcache_fp8_stage(stage, q, k_cache, v_cache, cache_seqlens, o, lse, B, Hq,
+                                        Hkv, Nq, Nk, d, scale, causal, descale_k, descale_v,
+                                        num_splits, dtype, workspace, workspace_bytes, stream)
+
+
 def fa_fwd_kvcache_num_stages() -> int:
     return lib.fa_fwd_kvcache_num_stages()
 
 
 def fa_kvcache_num_splits(B, Hq, Hkv, Nq, Nk, d) -> int:
     return lib.fa_kvcache_num_splits(B, Hq, Hkv, Nq, Nk, d)
+
+
+def fa_kvcache_fp8_num_splits(B, Hq, Hkv, Nq, Nk, d) -> int:
+    return lib.fa_kvcache_fp8_num_splits(B, Hq, Hkv, Nq, Nk, d)
 
 
 def fa_fwd_kvcache_workspace_size(B, Hq, Hkv, Nq, Nk, d, num_splits) -> int:
@@ -447,12 +475,14 @@ def flash_attn_backward(dout, q, k, v, o, lse, causal=False, softmax_scale=None,
 
 
 def flash_attn_with_kvcache(q, k_cache, v_cache, cache_seqlens, causal=False, softmax_scale=None,
-                            num_splits=0, workspace=None):
+                            num_splits=0, workspace=None, descale_k=1.0, descale_v=1.0):
     """Decode over a key/value cache. Returns (o, lse); lse is float32 [Hq, B·Nq].
 
     q [B, Nq, Hq, d]; k_cache, v_cache [B, Nk, Hkv, d]; cache_seqlens int32 [B]
     (valid positions per entry). The queries are the newest Nq positions of
-    each sequence (see fa_fwd_kvcache in include/fa.h).
+    each sequence (see fa_fwd_kvcache in include/fa.h). Caches of dtype
+    float8_e4m3fn (or uint8 codes) take the FP8 path, fa_fwd_kvcache_fp8, with
+    cached value = code × descale_k (K) or × descale_v (V); o has q's dtype.
     """
     import torch
     if q.dim() != 4 or k_cache.dim() != 4 or v_cache.shape != k_cache.shape:
@@ -461,7 +491,13 @@ def flash_attn_with_kvcache(q, k_cache, v_cache, cache_seqlens, causal=False, so
     if k_cache.shape[0] != B or k_cache.shape[3] != d:
         raise ValueError(f"q {tuple(q.shape)} and k_cache {tuple(k_cache.shape)} do not match")
     Nk, Hkv = k_cache.shape[1], k_cache.shape[2]
-    if not (q.dtype == k_cache.dtype == v_cache.dtype):
+    fp8 = (torch.float8_e4m3fn, torch.uint8)
+    kv8 = k_cache.dtype in fp8
+    if kv8:
+        if v_cache.dtype not in fp8:
+            raise TypeError("an fp8 k_cache needs an fp8 v_cache")
+        _dtype_code(q)
+    elif not (q.dtype == k_cache.dtype == v_cache.dtype):
         raise TypeError("q, k_cache, v_cache must share one dtype")
     _check_dev(q, k_cache, v_cache, cache_seqlens)
     if cache_seqlens.dtype != torch.int32 or cache_seqlens.numel() != B:
@@ -472,10 +508,19 @@ def flash_attn_with_kvcache(q, k_cache, v_cache, cache_seqlens, causal=False, so
     need = fa_fwd_kvcache_workspace_size(B, Hq, Hkv, Nq, Nk, d, num_splits)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
-    st = lib.fa_fwd_kvcache(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
-                            cache_seqlens.data_ptr(), o.data_ptr(), lse.data_ptr(), B, Hq, Hkv, Nq,
-                            Nk, d, float(scale), int(bool(causal)), int(num_splits), _dtype_code(q),
-                            workspace.data_ptr(), workspace.numel(), _stream())
+    ptrs = (q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), cache_seqlens.data_ptr(),
+            o.data_ptr(), lse.data_ptr())
+    if kv8:
+        st = lib.fa_fwd_kvcache_fp8(*ptrs, B, Hq, Hkv, Nq, Nk, d, float(scale), int(bool(causal)),
+                                    float(descale_k), float(descale_v), int(num_splits),
+                                    _dtype_code(q), workspace.data_ptr(), workspace.numel(),
+                                    _stream())
+        if st != FA_OK:
+            raise FaError(st, "fa_fwd_kvcache_fp8")
+        return o, lse
+    st = lib.fa_fwd_kvcache(*ptrs, B, Hq, Hkv, Nq, Nk, d, float(scale), int(bool(causal)),
+                            int(num_splits), _dtype_code(q), workspace.data_ptr(), workspace.numel(),
+                            _stream())
     if st != FA_OK:
         raise FaError(st, "fa_fwd_kvcache")
     return o, lse

@@ -381,13 +381,15 @@ int check_kvcache(int B, int Hq, int Hkv, int Nq, int Nk, int d, float scale, in
   return FA_OK;
 }
 
-int kv_splits(int B, int Hq, int Hkv, int Nq, int Nk) {
-  // about 8 one-wave workgroups per CU over the 256 CUs, each range at least
-  // two key tiles, at most one range per tile
+// Key ranges per (entry, KV head): about `waves` one-wave workgroups over the
+// 256 CUs (8 per CU for a 16-bit cache; 4 for an e4m3 cache, whose waves do
+// twice the work per byte and measured fastest at that count), each range at
+// least two key tiles.
+int kv_splits(int B, int Hq, int Hkv, int Nq, int Nk, int waves = 2048) {
   const int tk = fa::decode_tile_keys();
   const int64_t rows = (int64_t)(Hq / Hkv) * Nq;
   const int64_t base = (int64_t)B * Hkv * ((rows + 31) / 32);
-  const int64_t want = (2048 + base - 1) / (base > 0 ? base : 1);
+  const int64_t want = (waves + base - 1) / (base > 0 ? base : 1);
   const int64_t most = std::max<int64_t>(1, (Nk + 2 * tk - 1) / (2 * tk));
   return (int)std::max<int64_t>(1, std::min<int64_t>(want, std::min<int64_t>(most, 256)));
 }
@@ -398,6 +400,12 @@ int fa_kvcache_num_splits(int B, int Hq, int Hkv, int Nq, int Nk, int d) {
   bool noop;
   if (check_kvcache(B, Hq, Hkv, Nq, Nk, d, 1.f, 0, 0, FA_FP16, &noop) != FA_OK) return 0;
   return kv_splits(B, Hq, Hkv, Nq, Nk);
+}
+
+int fa_kvcache_fp8_num_splits(int B, int Hq, int Hkv, int Nq, int Nk, int d) {
+  bool noop;
+  if (check_kvcache(B, Hq, Hkv, Nq, Nk, d, 1.f, 0, 0, FA_FP16, &noop) != FA_OK) return 0;
+  return kv_splits(B, Hq, Hkv, Nq, Nk, 1024);
 }
 
 size_t fa_fwd_kvcache_workspace_size(int B, int Hq, int Hkv, int Nq, int Nk, int d,
@@ -411,19 +419,26 @@ size_t fa_fwd_kvcache_workspace_size(int B, int Hq, int Hkv, int Nq, int Nk, int
 
 namespace {
 
+// kv8: e4m3fn caches with descales descale_k, descale_v (ignored otherwise).
 int kvcache_common(int stage, const void* q, const void* k_cache, const void* v_cache,
                    const int32_t* cache_seqlens, void* o, float* lse, int B, int Hq, int Hkv,
                    int Nq, int Nk, int d, float scale, int causal, int num_splits, int dtype,
-                   void* workspace, size_t workspace_bytes, hipStream_t stream) {
+                   void* workspace, size_t workspace_bytes, hipStream_t stream, bool kv8 = false,
+                   float descale_k = 1.f, float descale_v = 1.f) {
   bool noop;
   int st = check_kvcache(B, Hq, Hkv, Nq, Nk, d, scale, causal, num_splits, dtype, &noop);
-  if (st != FA_OK || noop) return st;
+  if (st != FA_OK) return st;
+  if (kv8 && !(std::isfinite(descale_k) && descale_k > 0.f && std::isfinite(descale_v) &&
+               descale_v > 0.f))
+    return FA_ERR_INVALID_ARG;
+  if (noop) return st;
   if (!q || !k_cache || !v_cache || !cache_seqlens || !o || !lse) return FA_ERR_INVALID_ARG;
   const void* ptrs[] = {q, k_cache, v_cache, o, lse, workspace};
   for (const void* p : ptrs)
     if (p && !aligned16(p)) return FA_ERR_INVALID_ARG;
   if ((reinterpret_cast<uintptr_t>(cache_seqlens) & 3u) != 0) return FA_ERR_INVALID_ARG;
-  const int sp = num_splits > 0 ? num_splits : kv_splits(B, Hq, Hkv, Nq, Nk);
+  // the e4m3 count is never above the 16-bit one, so the automatic workspace size covers both
+  const int sp = num_splits > 0 ? num_splits : kv_splits(B, Hq, Hkv, Nq, Nk, kv8 ? 1024 : 2048);
   if (!workspace || workspace_bytes < fa_fwd_kvcache_workspace_size(B, Hq, Hkv, Nq, Nk, d, sp))
     return FA_ERR_WORKSPACE;
   fa::DecodeArgs a;
@@ -448,9 +463,11 @@ int kvcache_common(int stage, const void* q, const void* k_cache, const void* v_
   const int tk = fa::decode_tile_keys();
   const int per = (Nk + sp - 1) / sp;
   a.chunk = std::max(tk, (per + tk - 1) / tk * tk);
-  a.scale_log2 = scale * kLog2e;
+  a.scale_log2 = scale * kLog2e * (kv8 ? descale_k : 1.f);
+  a.o_scale = kv8 ? descale_v : 1.f;
+  if (!std::isfinite(a.scale_log2) || !(a.scale_log2 > 0.f)) return FA_ERR_INVALID_ARG;
   if ((int64_t)a.n_rb * sp * Hkv * B >= (int64_t)1 << 31) return FA_ERR_UNSUPPORTED;
-  hipError_t e = fa::launch_decode(a, dtype == FA_BF16, d, causal != 0, stage, stream);
+  hipError_t e = fa::launch_decode(a, dtype == FA_BF16, d, causal != 0, kv8, stage, stream);
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
@@ -473,6 +490,27 @@ int fa_fwd_kvcache_stage(int stage, const void* q, const void* k_cache, const vo
   if (stage < 0 || stage >= fa::decode_num_stages()) return FA_ERR_INVALID_ARG;
   return kvcache_common(stage, q, k_cache, v_cache, cache_seqlens, o, lse, B, Hq, Hkv, Nq, Nk, d,
                         scale, causal, num_splits, dtype, workspace, workspace_bytes, stream);
+}
+
+int fa_fwd_kvcache_fp8(const void* q, const void* k_cache, const void* v_cache,
+                       const int32_t* cache_seqlens, void* o, float* lse, int B, int Hq, int Hkv,
+                       int Nq, int Nk, int d, float scale, int causal, float descale_k,
+                       float descale_v, int num_splits, int dtype, void* workspace,
+                       size_t workspace_bytes, hipStream_t stream) {
+  return kvcache_common(-1, q, k_cache, v_cache, cache_seqlens, o, lse, B, Hq, Hkv, Nq, Nk, d,
+                        scale, causal, num_splits, dtype, workspace, workspace_bytes, stream, true,
+                        descale_k, descale_v);
+}
+
+int fa_fwd_kvcache_fp8_stage(int stage, const void* q, const void* k_cache, const void* v_cache,
+                             const int32_t* cache_seqlens, void* o, float* lse, int B, int Hq,
+                             int Hkv, int Nq, int Nk, int d, float scale, int causal,
+                             float descale_k, float descale_v, int num_splits, int dtype,
+                             void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (stage < 0 || stage >= fa::decode_num_stages()) return FA_ERR_INVALID_ARG;
+  return kvcache_common(stage, q, k_cache, v_cache, cache_seqlens, o, lse, B, Hq, Hkv, Nq, Nk, d,
+                        scale, causal, num_splits, dtype, workspace, workspace_bytes, stream, true,
+                        descale_k, descale_v);
 }
 
 const char* fa_status_string(int status) {

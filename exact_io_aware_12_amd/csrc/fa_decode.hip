@@ -17,6 +17,13 @@
 // with Vᵀ read transposed from the row-major LDS tile. The work per byte is
 // small (d FLOP per loaded K or V element per row), so the kernel is bound by
 // HBM: K/V tiles of 32 keys are copied global -> LDS three stages deep.
+//
+// An e4m3 cache (the FP8 KV cache of the deployment guide, cxbdf.cn, section
+// 4.3) takes the same path at half the cache bytes: tiles are copied as raw
+// codes and each operand is widened to the query's 16-bit type in registers
+// (every e4m3 value is exact in bf16 and in fp16), so the products are those
+// of the 16-bit kernel on the decoded cache; the per-tensor descales enter
+// the score scale (K) and the output normalisation (V).
 #include "fa_device.h"
 #include "fa_kernels.h"
 
@@ -48,14 +55,106 @@ __device__ __forceinline__ void wait_tiles(int newer) {
   }
 }
 
-template <typename T, int D, bool CAUSAL>
+// ---- e4m3 cache tiles -------------------------------------------------------
+// kTK x D-byte tiles; the 16-byte chunks of row r are stored in the order
+// chunk ^ kv8_swz(r). Rows of D bytes put 256 / D rows on one 256-byte sweep
+// of the 64 banks; the permutation makes both reads below conflict free:
+// 16 lanes reading one chunk of 16 consecutive rows (K), and 32 lanes
+// reading 8 consecutive rows x 2 adjacent chunks with the transposing read (V).
+template <int D>
+__device__ __forceinline__ constexpr int kv8_swz(int r) {
+  constexpr int s = D == 64 ? 2 : D == 128 ? 1 : 0;
+  return (((r >> s) & (D / 32 - 1)) << 1) | ((r >> 3) & 1);
+}
+
+// Copy rows r0 .. r0+kTK-1 of an e4m3 matrix (row stride `rstride` bytes)
+// into an LDS tile, 16 bytes per lane and 1 KiB per instruction; rows at or
+// past L repeat row L-1 (L >= 1), and the kernel masks those keys.
+template <int D>
+__device__ __forceinline__ void tile_dma_kv8(uint8_t* lds, const uint8_t* src, int64_t rstride,
+                                             int r0, int L, int lane) {
+  constexpr int CPR = D / 16;   // chunks per row
+  constexpr int RPI = 64 / CPR; // rows per instruction
+#pragma unroll
+  for (int u = 0; u < kTK / RPI; ++u) {
+    const int row = u * RPI + lane / CPR;
+    const int c = (lane % CPR) ^ kv8_swz<D>(row);
+    const uint8_t* g = src + (int64_t)min(r0 + row, L - 1) * rstride + c * 16;
+#if defined(__HIP_DEVICE_COMPILE__)  // the host pass cannot type-check this device builtin
+    __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)(lds + u * 1024),
+                                     16, 0, 0);
+#else
+    (void)g;
+#endif
+  }
+}
+
+// Eight e4m3 codes (bytes of w0 then w1, in order) as eight values of T,
+// two per dword, lower element first. Exact: e4m3 has 3 mantissa bits and
+// exponents 2^-9 .. 2^8, all inside both 16-bit types.
+template <typename T>
+__device__ __forceinline__ u32x4 widen8(uint32_t w0, uint32_t w1) {
+  if constexpr (__is_same(T, bf16)) {
+    return u32x4{__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.f, false)),
+                 __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.f, true)),
+                 __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.f, false)),
+                 __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.f, true))};
+  } else {
+    return u32x4{__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w0, 1.f, false)),
+                 __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w0, 1.f, true)),
+                 __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w1, 1.f, false)),
+                 __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w1, 1.f, true))};
+  }
+}
+
+// Logical chunk c (bytes 16c .. 16c+15) of row r of an e4m3 tile.
+template <int D>
+__device__ __forceinline__ u32x4 kv8_chunk(const uint8_t* t, int r, int c) {
+  return *reinterpret_cast<const u32x4*>(t + r * D + 16 * (c ^ kv8_swz<D>(r)));
+}
+
+// Vᵀ operand bytes for columns 32·cb .. +31 and keys k0 .. k0+7: in each
+// 16-lane group lanes 2m, 2m+1 address key k0 + m, bytes 0-7 and 8-15 of the
+// group's 16-column chunk, and the transposing read hands lane i column i of
+// the 8 keys, one byte per key in key order.
+template <int D>
+__device__ __forceinline__ u32x2 kv8_tr(const uint8_t* t, int k0, int cb, int lane) {
+  typedef int i32x2 __attribute__((ext_vector_type(2)));
+  typedef __attribute__((address_space(3))) i32x2 lds_i32x2;
+  const int j = lane & 15;
+  const int row = k0 + (j >> 1), c = 2 * cb + ((lane >> 4) & 1);
+  const i32x2 x = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+      (lds_i32x2*)(t + row * D + 16 * (c ^ kv8_swz<D>(row)) + 8 * (j & 1)));
+  return __builtin_bit_cast(u32x2, x);
+}
+
+// With an e4m3 cache, MFMA row ρ of Sᵀ reads key kv8_key(ρ) of the tile (bits
+// 2 and 3 swapped): the accumulator elements that form the P operand of key
+// step kk in lane half h then hold keys 16kk + 8h + 0..7 in order, the eight
+// consecutive keys one transposing byte read delivers for Vᵀ.
+__device__ __forceinline__ constexpr int kv8_key(int rho) {
+  return (rho & ~12) | ((rho & 4) << 1) | ((rho & 8) >> 1);
+}
+
+template <typename T, bool KV8>
+struct CacheElem {
+  using type = T;
+};
+template <typename T>
+struct CacheElem<T, true> {
+  using type = uint8_t;
+};
+
+template <typename T, int D, bool CAUSAL, bool KV8>
 __global__ __launch_bounds__(64) void decode_kernel(DecodeArgs a) {
+  using C = typename CacheElem<T, KV8>::type;   // cache element: T or an e4m3 code
   constexpr int NKB = D / 16;
   constexpr int NCB = D / 32;
   constexpr int TILE = kTK * D;
-  constexpr int PER = kTK / (64 / (D / 8));   // copy instructions per K or V tile
-  __shared__ __attribute__((aligned(1024))) T k_lds[kStages][TILE];
-  __shared__ __attribute__((aligned(1024))) T v_lds[kStages][TILE];
+  // copy instructions per K or V tile: 16 bytes per lane
+  constexpr int PER = kTK * D * (int)sizeof(C) / 1024;
+  __shared__ __attribute__((aligned(1024))) C k_lds[kStages][TILE];
+  __shared__ __attribute__((aligned(1024))) C v_lds[kStages][TILE];
 
   const int lane = threadIdx.x, col = lane & 31, half = lane >> 5;
   int idx = blockIdx.x;
@@ -87,12 +186,17 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeArgs a) {
 
   if (k_begin < k_end) {
     const int64_t kvs = (int64_t)a.Hkv * D;
-    const T* kp = static_cast<const T*>(a.k) + (int64_t)b * a.Nk * kvs + (int64_t)g * D;
-    const T* vp = static_cast<const T*>(a.v) + (int64_t)b * a.Nk * kvs + (int64_t)g * D;
+    const C* kp = static_cast<const C*>(a.k) + (int64_t)b * a.Nk * kvs + (int64_t)g * D;
+    const C* vp = static_cast<const C*>(a.v) + (int64_t)b * a.Nk * kvs + (int64_t)g * D;
     const int ntiles = (k_end - k_begin + kTK - 1) / kTK;
     auto issue = [&](int t) {   // rows past k_end repeat row k_end-1 (masked below)
-      tile_dma<T, kTK, D, 1>(k_lds[t % kStages], kp, kvs, k_begin + t * kTK, k_end, 0, lane);
-      tile_dma<T, kTK, D, 1>(v_lds[t % kStages], vp, kvs, k_begin + t * kTK, k_end, 0, lane);
+      if constexpr (KV8) {
+        tile_dma_kv8<D>(k_lds[t % kStages], kp, kvs, k_begin + t * kTK, k_end, lane);
+        tile_dma_kv8<D>(v_lds[t % kStages], vp, kvs, k_begin + t * kTK, k_end, lane);
+      } else {
+        tile_dma<T, kTK, D, 1>(k_lds[t % kStages], kp, kvs, k_begin + t * kTK, k_end, 0, lane);
+        tile_dma<T, kTK, D, 1>(v_lds[t % kStages], vp, kvs, k_begin + t * kTK, k_end, 0, lane);
+      }
     };
     // tiles 0 .. kStages-2 in flight; tile t+kStages-1 starts once tile t has landed
 #pragma unroll
@@ -102,30 +206,46 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeArgs a) {
     u32x4 qf[NKB];
     {
       const T* qp = static_cast<const T*>(a.q) + (((int64_t)b * a.Nq + qi) * a.Hq + h) * D;
+      // k step kb covers head columns 16kb + 8h .. +7 in lane half h; with an
+      // e4m3 cache one 16-byte K read serves two steps, so step 2m + u covers
+      // columns 32m + 16h + 8u .. +7 instead (the same columns for both operands)
 #pragma unroll
-      for (int kb = 0; kb < NKB; ++kb)
-        qf[kb] = row_ok ? ldg16(qp + kb * 16 + half * 8) : u32x4{0, 0, 0, 0};
+      for (int kb = 0; kb < NKB; ++kb) {
+        const int col0 = KV8 ? 32 * (kb >> 1) + 16 * half + 8 * (kb & 1) : kb * 16 + half * 8;
+        qf[kb] = row_ok ? ldg16(qp + col0) : u32x4{0, 0, 0, 0};
+      }
     }
     const float c = a.scale_log2;
+    const int krow = KV8 ? kv8_key(col) : col;   // the tile row MFMA row `col` reads
 
     for (int t = 0; t < ntiles; ++t) {
       // tile t has landed once only the copies of the newer tiles in flight
       // (at most kStages-2 of them) are outstanding
       wait_tiles<2 * PER, kStages - 2>(ntiles - 1 - t);
       if (t + kStages - 1 < ntiles) issue(t + kStages - 1);   // into the stage of tile t-1
-      const T* kt = k_lds[t % kStages];
-      const T* vt = v_lds[t % kStages];
+      const C* kt = k_lds[t % kStages];
+      const C* vt = v_lds[t % kStages];
       const int kbase = k_begin + t * kTK;
 
       f32x16 s = f32x16{};
+      if constexpr (KV8) {
 #pragma unroll
-      for (int kb = 0; kb < NKB; ++kb)
-        s = mfma32<T>(lds_row16<T, D>(kt, col, 2 * kb + half), qf[kb], s);
+        for (int m = 0; m < NKB / 2; ++m) {
+          const u32x4 raw = kv8_chunk<D>(kt, krow, 2 * m + half);
+          s = mfma32<T>(widen8<T>(raw[0], raw[1]), qf[2 * m], s);
+          s = mfma32<T>(widen8<T>(raw[2], raw[3]), qf[2 * m + 1], s);
+        }
+      } else {
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+          s = mfma32<T>(lds_row16<T, D>(kt, krow, 2 * kb + half), qf[kb], s);
+      }
 
       // mask keys past the range and, causally, keys after the query
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        const int kj = kbase + 8 * (i >> 2) + 4 * half + (i & 3);
+        const int rho = 8 * (i >> 2) + 4 * half + (i & 3);   // accumulator row of s[i]
+        const int kj = kbase + (KV8 ? kv8_key(rho) : rho);
         s[i] = (kj < k_end && !(CAUSAL && kj > qpos)) ? s[i] : -INFINITY;
       }
       float mx = s[0];
@@ -154,10 +274,18 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeArgs a) {
       for (int kk = 0; kk < kTK / 16; ++kk) {
         const u32x4 pf = acc_operand<T>(s, kk * 2);
         lr = dot2_sum<T>(pf, lr);   // the same sum over P as rounded for the MFMAs
-        const int k0 = kk * 16 + 4 * half;
+        if constexpr (KV8) {
 #pragma unroll
-        for (int cb = 0; cb < NCB; ++cb)
-          o[cb] = mfma32<T>(lds_tr8<T, D>(vt, k0, k0 + 8, cb * 32, lane), pf, o[cb]);
+          for (int cb = 0; cb < NCB; ++cb) {
+            const u32x2 vb = kv8_tr<D>(vt, kk * 16 + 8 * half, cb, lane);
+            o[cb] = mfma32<T>(widen8<T>(vb[0], vb[1]), pf, o[cb]);
+          }
+        } else {
+          const int k0 = kk * 16 + 4 * half;
+#pragma unroll
+          for (int cb = 0; cb < NCB; ++cb)
+            o[cb] = mfma32<T>(lds_tr8<T, D>(vt, k0, k0 + 8, cb * 32, lane), pf, o[cb]);
+        }
       }
     }
   }
@@ -169,7 +297,7 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeArgs a) {
   const float l_tot = kLseFromUnrounded<T> ? wave_sum_halves(l) : lr_tot;
   if (row_ok) {
     const bool any = l_tot > 0.f;
-    const float inv = any ? 1.f / lr_tot : 0.f;
+    const float inv = any ? a.o_scale / lr_tot : 0.f;   // o_scale: descale of V (1 for T)
 #pragma unroll
     for (int cb = 0; cb < NCB; ++cb)
 #pragma unroll
@@ -239,12 +367,12 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeArgs a) {
         wsum > 0.f ? m + logf(wsum) : -INFINITY;
 }
 
-template <typename T, int D, bool CAUSAL>
+template <typename T, int D, bool CAUSAL, bool KV8>
 hipError_t launch(const DecodeArgs& a, int stage, hipStream_t s) {
   (void)hipGetLastError();  // drop an error left pending by earlier, unrelated HIP calls
   if (stage < 0 || stage == 0) {
     const int64_t g1 = (int64_t)a.n_rb * a.splits * a.Hkv * a.B;
-    hipLaunchKernelGGL((decode_kernel<T, D, CAUSAL>), dim3((unsigned)g1), dim3(64), 0, s, a);
+    hipLaunchKernelGGL((decode_kernel<T, D, CAUSAL, KV8>), dim3((unsigned)g1), dim3(64), 0, s, a);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -258,25 +386,27 @@ hipError_t launch(const DecodeArgs& a, int stage, hipStream_t s) {
   return hipSuccess;
 }
 
+template <typename T, bool KV8>
+hipError_t dispatch(const DecodeArgs& a, int d, bool causal, int stage, hipStream_t s) {
+  if (d == 64)
+    return causal ? launch<T, 64, true, KV8>(a, stage, s) : launch<T, 64, false, KV8>(a, stage, s);
+  if (d == 128)
+    return causal ? launch<T, 128, true, KV8>(a, stage, s) : launch<T, 128, false, KV8>(a, stage, s);
+  return causal ? launch<T, 256, true, KV8>(a, stage, s) : launch<T, 256, false, KV8>(a, stage, s);
+}
+
 }  // namespace
 
 int decode_tile_keys() { return kTK; }
 int decode_num_stages() { return 2; }
 
-hipError_t launch_decode(const DecodeArgs& a, bool bf16_in, int d, bool causal, int stage,
-                         hipStream_t s) {
-  if (bf16_in) {
-    if (d == 64)
-      return causal ? launch<bf16, 64, true>(a, stage, s) : launch<bf16, 64, false>(a, stage, s);
-    if (d == 128)
-      return causal ? launch<bf16, 128, true>(a, stage, s) : launch<bf16, 128, false>(a, stage, s);
-    return causal ? launch<bf16, 256, true>(a, stage, s) : launch<bf16, 256, false>(a, stage, s);
-  }
-  if (d == 64)
-    return causal ? launch<f16, 64, true>(a, stage, s) : launch<f16, 64, false>(a, stage, s);
-  if (d == 128)
-    return causal ? launch<f16, 128, true>(a, stage, s) : launch<f16, 128, false>(a, stage, s);
-  return causal ? launch<f16, 256, true>(a, stage, s) : launch<f16, 256, false>(a, stage, s);
+hipError_t launch_decode(const DecodeArgs& a, bool bf16_in, int d, bool causal, bool kv8,
+                         int stage, hipStream_t s) {
+  if (bf16_in)
+    return kv8 ? dispatch<bf16, true>(a, d, causal, stage, s)
+               : dispatch<bf16, false>(a, d, causal, stage, s);
+  return kv8 ? dispatch<f16, true>(a, d, causal, stage, s)
+             : dispatch<f16, false>(a, d, causal, stage, s);
 }
 
 }  // namespace fa

@@ -75,7 +75,8 @@ struct DecodeArgs {
   int n_rb;                   // ceil(rows / 32)
   int splits;                 // key ranges per (entry, KV head)
   int chunk;                  // keys per range, a multiple of the key tile
-  float scale_log2;
+  float scale_log2;           // scale · log2(e) (· descale of K for an e4m3 cache)
+  float o_scale;              // O factor: 1, or the descale of V for an e4m3 cache
 };
 
 int fwd_query_tile();
@@ -94,8 +95,9 @@ hipError_t launch_bwd(const BwdArgs& a, bool bf16_in, int d, int mask, bool varl
                       bool dropout, int stage, hipStream_t s);
 int decode_tile_keys();
 // stage < 0: both stages; 0: per-range partial results; 1: merge into o, lse.
+// kv8: k and v hold e4m3fn codes (q and o stay 16-bit).
 int decode_num_stages();
-hipError_t launch_decode(const DecodeArgs& a, bool bf16_in, int d, bool causal, int stage,
-                         hipStream_t s);
+hipError_t launch_decode(const DecodeArgs& a, bool bf16_in, int d, bool causal, bool kv8,
+                         int stage, hipStream_t s);
 
 }  // namespace fa

@@ -288,8 +288,40 @@ int fa_fwd_kvcache_stage(int stage, const void* q, const void* k_cache, const vo
                          int num_splits, int dtype, void* workspace, size_t workspace_bytes,
                          hipStream_t stream);
 
+/*
+ * Decode over an FP8 key/value cache: fa_fwd_kvcache with k_cache and v_cache
+ * holding e4m3fn codes (1 byte each, same [B, Nk, Hkv, d] layout) and
+ * per-tensor descales (cached value = code value × descale). This is the FP8
+ * KV cache the deployment guide offers for long sequences that run out of
+ * memory (FlashAttention guide, cxbdf.cn, section 4.3, kv_cache_dtype =
+ * float8_e4m3fn); it halves the cache bytes each call reads.
+ *   q, o     : `dtype` (FA_FP16 or FA_BF16), as in fa_fwd_kvcache
+ *   descale_k, descale_v : finite and > 0, else FA_ERR_INVALID_ARG
+ * The result is that of fa_fwd_kvcache on the decoded cache (every e4m3 value
+ * is exact in both 16-bit types): scores scale·descale_k·q·k_code, and O
+ * multiplied by descale_v. Codes 0x7f and 0xff (NaN) make the rows that see
+ * them NaN. Workspace, num_splits, stages and every other convention as for
+ * fa_fwd_kvcache (same workspace size function). num_splits = 0 picks
+ * fa_kvcache_fp8_num_splits(...) ranges, never more than fa_kvcache_num_splits
+ * (about half as many: each wave does twice the work per cache byte), so the
+ * automatic workspace size still suffices.
+ */
+int fa_fwd_kvcache_fp8(const void* q, const void* k_cache, const void* v_cache,
+                       const int32_t* cache_seqlens, void* o, float* lse,
+                       int B, int Hq, int Hkv, int Nq, int Nk, int d, float scale, int causal,
+                       float descale_k, float descale_v, int num_splits, int dtype,
+                       void* workspace, size_t workspace_bytes, hipStream_t stream);
+int fa_fwd_kvcache_fp8_stage(int stage, const void* q, const void* k_cache, const void* v_cache,
+                             const int32_t* cache_seqlens, void* o, float* lse,
+                             int B, int Hq, int Hkv, int Nq, int Nk, int d, float scale,
+                             int causal, float descale_k, float descale_v, int num_splits,
+                             int dtype, void* workspace, size_t workspace_bytes,
+                             hipStream_t stream);
+
 /* The key-range count fa_fwd_kvcache uses for num_splits = 0 (>= 1); 0 on bad sizes. */
 int fa_kvcache_num_splits(int B, int Hq, int Hkv, int Nq, int Nk, int d);
+/* The same for fa_fwd_kvcache_fp8 (>= 1, <= fa_kvcache_num_splits); 0 on bad sizes. */
+int fa_kvcache_fp8_num_splits(int B, int Hq, int Hkv, int Nq, int Nk, int d);
 
 /* Workspace bytes for fa_fwd_kvcache: (d + 1)·4 bytes per (split, entry, query head,
  * query), rounded up to 256; num_splits = 0 means the automatic count. 0 on bad sizes. */

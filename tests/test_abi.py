@@ -26,10 +26,12 @@ def test_header_declares_the_boundary():
                                     "fa_bwd_window", "fa_bwd_window_stage",
                                     "fa_bwd_workspace_size", "fa_fwd", "fa_fwd_dropout",
                                     "fa_fwd_fp8",
-                                    "fa_fwd_kvcache",
+                                    "fa_fwd_kvcache", "fa_fwd_kvcache_fp8",
+                                    "fa_fwd_kvcache_fp8_stage",
                                     "fa_fwd_kvcache_num_stages", "fa_fwd_kvcache_stage",
                                     "fa_fwd_kvcache_workspace_size", "fa_fwd_softcap", "fa_fwd_window",
-                                    "fa_kvcache_num_splits", "fa_status_string"]
+                                    "fa_kvcache_fp8_num_splits", "fa_kvcache_num_splits",
+                                    "fa_status_string"]
 
 
 def test_every_declared_symbol_is_exported():
@@ -187,6 +189,64 @@ def test_kvcache_stage_index_checked():
     # a valid stage still runs the host checks first
     assert fa.fa_fwd_kvcache_stage(0, P, P, P, P, P, P, 2, 4, 2, 1, 64, 96, 0.125, 1, 2,
                                    fa.FA_BF16, P, 1 << 20, None) == fa.FA_ERR_UNSUPPORTED
+
+
+def kvc8(stage=None, **kw):
+    a = dict(q=P, k=P, v=P, lens=P, o=P, lse=P, B=2, Hq=4, Hkv=2, Nq=1, Nk=64, d=128,
+             scale=0.125, causal=1, dk=0.01, dv=0.02, splits=2, dtype=fa.FA_BF16, ws=P,
+             wsb=1 << 20)
+    a.update(kw)
+    args = (a["q"], a["k"], a["v"], a["lens"], a["o"], a["lse"], a["B"], a["Hq"], a["Hkv"],
+            a["Nq"], a["Nk"], a["d"], a["scale"], a["causal"], a["dk"], a["dv"], a["splits"],
+            a["dtype"], a["ws"], a["wsb"], None)
+    if stage is None:
+        return fa.fa_fwd_kvcache_fp8(*args)
+    return fa.fa_fwd_kvcache_fp8_stage(stage, *args)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dk=0.0), fa.FA_ERR_INVALID_ARG),
+    (dict(dv=-1.0), fa.FA_ERR_INVALID_ARG),
+    (dict(dk=float("nan")), fa.FA_ERR_INVALID_ARG),
+    (dict(dv=float("inf")), fa.FA_ERR_INVALID_ARG),
+    (dict(dk=1e38, scale=100.0), fa.FA_ERR_INVALID_ARG),   # scale·descale_k overflows
+    (dict(dtype=5), fa.FA_ERR_INVALID_ARG),
+    (dict(Hq=3), fa.FA_ERR_INVALID_ARG),
+    (dict(causal=2), fa.FA_ERR_INVALID_ARG),
+    (dict(d=96), fa.FA_ERR_UNSUPPORTED),
+    (dict(lens=None), fa.FA_ERR_INVALID_ARG),
+    (dict(k=P + 8), fa.FA_ERR_INVALID_ARG),
+    (dict(ws=None), fa.FA_ERR_WORKSPACE),
+    (dict(B=0), fa.FA_OK),
+    (dict(B=0, dk=0.0), fa.FA_ERR_INVALID_ARG),
+])
+def test_kvcache_fp8_host_checks(kw, status):
+    assert kvc8(**kw) == status
+
+
+def test_kvcache_fp8_splits():
+    # about 4 one-wave workgroups per CU: 16·8 blocks want 8 ranges (16 for a 16-bit cache)
+    assert fa.fa_kvcache_fp8_num_splits(16, 32, 8, 1, 8192, 128) == 8
+    for shape in [(16, 32, 8, 1, 8192, 128), (1, 2, 2, 1, 100, 64), (1, 8, 1, 1, 40000, 256),
+                  (3, 12, 4, 5, 777, 64), (64, 8, 8, 1, 1 << 20, 128)]:
+        n8, n16 = fa.fa_kvcache_fp8_num_splits(*shape), fa.fa_kvcache_num_splits(*shape)
+        assert 1 <= n8 <= n16, shape
+    assert fa.fa_kvcache_fp8_num_splits(1, 3, 2, 1, 64, 64) == 0
+
+
+def test_kvcache_fp8_stage_index_checked():
+    for stage in (-1, 2):
+        assert kvc8(stage=stage) == fa.FA_ERR_INVALID_ARG
+    assert kvc8(stage=0, d=96) == fa.FA_ERR_UNSUPPORTED
+
+
+def test_kvcache_fp8_no_device_reports_hip_error():
+    torch = pytest.importorskip("torch")
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    assert kvc8() == fa.FA_ERR_HIP
+    assert kvc8(d=64, dtype=fa.FA_FP16, causal=0) == fa.FA_ERR_HIP
+    assert kvc8(stage=1, d=256) == fa.FA_ERR_HIP
 
 
 def fwdw(**kw):

@@ -1,0 +1,188 @@
+"""GPU parity of fa_fwd_kvcache_fp8 (decode over an e4m3fn key/value cache)
+against the float64 oracle, through the C ABI.
+
+The oracle is the decode oracle on the decoded cache (codes × descale, the
+e4m3fn decoder of oracle.fp8): the kernel widens every code exactly to the
+query's 16-bit type, so the result must meet the same O and LSE tolerances as
+the 16-bit decode. Small caches compare every element across head dims,
+dtypes, causal or not, GQA groups, several new queries, ragged, short and
+empty cache lengths and explicit key-range splits; a cache holding every
+finite e4m3 code checks the widening; the benchmark's FP8 decode workload is
+checked on sampled units in the launch configuration the benchmark times.
+"""
+import numpy as np
+import pytest
+
+import workloads as W
+from oracle import dequantize, kvcache_fwd, kvcache_fwd_units
+from parity_util import bits_equal, check_lse, check_o, host64, say, torch_dtype
+
+pytestmark = pytest.mark.gpu
+
+
+def _fa():
+    import exact_io_aware_12_amd as fa   # raises if libfa.so is missing: no fallback
+    return fa
+
+
+def to_dev8(a, dtype):
+    """q rounded to dtype; k, v stay uint8 codes; lengths int32."""
+    import torch
+    return {"q": torch.from_numpy(a["q"]).to(torch_dtype(dtype)).cuda(),
+            "k": torch.from_numpy(a["k"]).cuda(), "v": torch.from_numpy(a["v"]).cuda(),
+            "cache_seqlens": torch.from_numpy(a["cache_seqlens"]).cuda(),
+            "descale_k": float(a["descale_k"]), "descale_v": float(a["descale_v"])}
+
+
+def run8(w, t, splits=0, as_float8=False):
+    import torch
+    fa = _fa()
+    say(f"[fa_fwd_kvcache_fp8] B={w.B} Hq={w.Hq} Hkv={w.Hkv} Nq={w.Nq} Nk={w.Nk} d={w.d} "
+        f"{w.dtype} causal={w.causal} lens={w.cache_lens()[:8]} splits={splits} "
+        f"descales=({t['descale_k']:.3e}, {t['descale_v']:.3e})")
+    k, v = t["k"], t["v"]
+    if as_float8:
+        k, v = k.view(torch.float8_e4m3fn), v.view(torch.float8_e4m3fn)
+    o, lse = fa.flash_attn_with_kvcache(t["q"], k, v, t["cache_seqlens"], causal=w.causal,
+                                        softmax_scale=w.scale, num_splits=splits,
+                                        descale_k=t["descale_k"], descale_v=t["descale_v"])
+    torch.cuda.synchronize()
+    assert o.dtype == t["q"].dtype
+    return o, lse
+
+
+def reference(w, t):
+    return kvcache_fwd(host64(t["q"]), dequantize(t["k"].cpu().numpy(), t["descale_k"]),
+                       dequantize(t["v"].cpu().numpy(), t["descale_v"]),
+                       t["cache_seqlens"].cpu().numpy(), w.scale, w.causal)
+
+
+def compare_whole(w, splits=0, t=None, as_float8=False):
+    if t is None:
+        t = to_dev8(W.decode_fp8_inputs(w), w.dtype)
+    o, lse = run8(w, t, splits, as_float8)
+    o_ref, lse_ref = reference(w, t)
+    o_g, lse_g = host64(o), host64(lse)
+    seen = np.isfinite(lse_ref)
+    empty = ~seen
+    if empty.any():
+        assert np.all(np.isneginf(lse_g[empty])), "empty rows must have LSE = -inf"
+        o_rows = o_g.transpose(2, 0, 1, 3).reshape(w.Hq, w.B * w.Nq, w.d)
+        assert np.all(o_rows[empty] == 0.0), "empty rows must have O = 0"
+    e, floor, exc = check_o(o_g, o_ref, w.dtype)
+    el = check_lse(lse_g[seen], lse_ref[seen]) if seen.any() else 0.0
+    say(f"   max|dO|={e:.2e} floor={floor:.2e} exceptions={exc} max|dLSE|={el:.2e} "
+        f"empty rows={int(empty.sum())}")
+    return o, lse, t
+
+
+@pytest.mark.parametrize("dtype", ["fp16", "bf16"])
+@pytest.mark.parametrize("d", [64, 128, 256])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("Nq", [1, 3])
+def test_small_caches(dtype, d, causal, Nq):
+    # lengths: full, ragged (not a multiple of the 32-key tile), 1, shorter than Nq, 0
+    lens = [200, 77, 1, 2, 0]
+    compare_whole(W.decode_custom(B=5, Hq=8, Hkv=2, Nq=Nq, Nk=200, d=d, dtype=dtype,
+                                  causal=causal, seed=500 + d + Nq, lens=lens, kv_cache="e4m3"))
+
+
+@pytest.mark.parametrize("splits", [1, 2, 3, 7, 13])
+def test_explicit_splits(splits):
+    """Ranges that end inside a tile, and ranges past every valid key (13 x 32 > 300)."""
+    compare_whole(W.decode_custom(B=3, Hq=4, Hkv=1, Nq=2, Nk=300, d=128, dtype="bf16",
+                                  causal=True, seed=51, lens=[300, 150, 31], kv_cache="e4m3"),
+                  splits=splits)
+
+
+def test_rows_beyond_one_block():
+    """(Hq/Hkv)·Nq = 40 rows per KV head: two 32-row blocks."""
+    compare_whole(W.decode_custom(B=2, Hq=8, Hkv=1, Nq=5, Nk=96, d=64, dtype="fp16",
+                                  causal=True, seed=52, lens=[96, 61], kv_cache="e4m3"))
+
+
+@pytest.mark.parametrize("dtype", ["fp16", "bf16"])
+@pytest.mark.parametrize("d", [64, 128, 256])
+def test_every_code(dtype, d):
+    """K and V hold every finite e4m3fn code (both signs, subnormals, ±0, ±448),
+    each key a different rotation, so a wrong widening of any code, a swapped
+    byte pair or a misplaced column shows up in O; small descales keep the
+    logits moderate so many keys contribute."""
+    import torch
+    w = W.decode_custom(B=2, Hq=4, Hkv=2, Nq=2, Nk=160, d=d, dtype=dtype, causal=False,
+                        seed=53, lens=[160, 97], kv_cache="e4m3")
+    codes = np.array([c for c in range(256) if c & 0x7F != 0x7F], dtype=np.uint8)   # 254 finite
+    n = w.B * w.Nk * w.Hkv
+    idx = (np.arange(n)[:, None] * 37 + np.arange(d)[None, :]) % codes.size
+    k8 = codes[idx].reshape(w.B, w.Nk, w.Hkv, d)
+    v8 = codes[(idx * 5 + 11) % codes.size].reshape(w.B, w.Nk, w.Hkv, d)
+    q = np.random.default_rng(54).standard_normal((w.B, w.Nq, w.Hq, d), dtype=np.float32)
+    t = {"q": torch.from_numpy(q).to(torch_dtype(dtype)).cuda(), "k": torch.from_numpy(k8).cuda(),
+         "v": torch.from_numpy(v8).cuda(),
+         "cache_seqlens": torch.tensor(w.cache_lens(), dtype=torch.int32).cuda(),
+         "descale_k": 2.0 ** -8, "descale_v": 2.0 ** -6}
+    compare_whole(w, t=t)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_mha_and_long_cache(causal):
+    compare_whole(W.decode_custom(B=2, Hq=4, Hkv=4, Nq=1, Nk=3000, d=128, dtype="bf16",
+                                  causal=causal, seed=55, lens=[3000, 2049], kv_cache="e4m3"))
+
+
+def test_float8_dtype_tensors():
+    """torch.float8_e4m3fn tensors take the same path as uint8 codes, bit for bit."""
+    w = W.decode_custom(B=2, Hq=8, Hkv=2, Nq=1, Nk=256, d=128, dtype="bf16", causal=True,
+                        seed=56, lens=[256, 130], kv_cache="e4m3")
+    o1, l1, t = compare_whole(w)
+    o2, l2, _ = compare_whole(w, t=t, as_float8=True)
+    assert bits_equal(o1, o2) and bits_equal(l1, l2)
+
+
+def test_matches_16bit_decode_on_decoded_cache():
+    """The same cache widened on the host to bf16 through fa_fwd_kvcache. With
+    power-of-two descales every decoded value is exact in bf16, so both paths
+    form the same products and differ only in the order the MFMAs sum them
+    (the FP8 path assigns keys and head columns to MFMA slots differently):
+    O agrees to an ulp and LSE closely."""
+    import torch
+    fa = _fa()
+    w = W.decode_custom(B=3, Hq=8, Hkv=2, Nq=2, Nk=700, d=128, dtype="bf16", causal=True,
+                        seed=57, lens=[700, 512, 33], kv_cache="e4m3")
+    t = to_dev8(W.decode_fp8_inputs(w), w.dtype)
+    t["descale_k"], t["descale_v"] = 2.0 ** -7, 2.0 ** -6
+    o8, l8 = run8(w, t)
+    kd = torch.from_numpy(dequantize(t["k"].cpu().numpy(), t["descale_k"])).to(torch.bfloat16)
+    vd = torch.from_numpy(dequantize(t["v"].cpu().numpy(), t["descale_v"])).to(torch.bfloat16)
+    o16, l16 = fa.flash_attn_with_kvcache(t["q"], kd.cuda(), vd.cuda(), t["cache_seqlens"],
+                                          causal=True, softmax_scale=w.scale)
+    torch.cuda.synchronize()
+    np.testing.assert_allclose(host64(o8), host64(o16), rtol=2.0 ** -7, atol=2e-3)
+    np.testing.assert_allclose(host64(l8), host64(l16), atol=1e-4)
+
+
+def test_deterministic():
+    w = W.decode_custom(B=2, Hq=8, Hkv=2, Nq=3, Nk=700, d=128, dtype="bf16", causal=True,
+                        seed=58, lens=[700, 512], kv_cache="e4m3")
+    t = to_dev8(W.decode_fp8_inputs(w), w.dtype)
+    o1, l1 = run8(w, t)
+    o2, l2 = run8(w, t)
+    assert bits_equal(o1, o2) and bits_equal(l1, l2)
+
+
+def test_benchmark_workload_sampled():
+    """decode_llama_fp8 at full size, automatic splits; sampled (entry, head) units."""
+    w = W.DECODE_WORKLOADS["decode_llama_fp8"]
+    t = to_dev8(W.decode_fp8_inputs(w), w.dtype)
+    o, lse = run8(w, t)
+    units = [(0, 0), (w.B - 1, w.Hq - 1), (w.B // 2, 5), (1, w.Hq // 2 + 1)]
+    q64, lens = host64(t["q"]), t["cache_seqlens"].cpu().numpy()
+    lse_h = host64(lse)
+    for b, h in units:   # decode only the batch entry a unit reads
+        kd = dequantize(t["k"][b:b + 1].cpu().numpy(), t["descale_k"])
+        vd = dequantize(t["v"][b:b + 1].cpu().numpy(), t["descale_v"])
+        (O, L), = kvcache_fwd_units(q64[b:b + 1], kd, vd, lens[b:b + 1], w.scale, w.causal,
+                                    [(0, h)]).values()
+        check_o(host64(o[b, :, h]), O, w.dtype, what=f"O[{b},:,{h}]")
+        check_lse(lse_h[h, b * w.Nq:(b + 1) * w.Nq], L, what=f"LSE[{h},{b}]")
+    say(f"   {len(units)} units ok")

@@ -241,7 +241,9 @@ def to_torch(arrays, dtype: str, device="cpu"):
 #   3. q [B, Nq, Hq, d], then k, v [B, Nk, Hkv, d], each
 #      rng.standard_normal(shape, dtype=float32); cache slots past L_b hold
 #      random values too (they must never be read into the result)
-#   4. the caller rounds to fp16 / bf16 (round to nearest even)
+#   4. the caller rounds to fp16 / bf16 (round to nearest even); with
+#      kv_cache="e4m3" the caches are instead quantised by quantize_e4m3
+#      (names k and v: one descale each, max|x| / 448), see decode_fp8_inputs
 @dataclasses.dataclass(frozen=True)
 class DecodeWorkload:
     name: str
@@ -255,6 +257,7 @@ class DecodeWorkload:
     causal: bool = True
     seed: int = 0
     lens: object = "full"        # "full", "draw:<lo>", or a tuple of B lengths
+    kv_cache: str = "same"       # cache element: "same" (dtype) or "e4m3" (FP8 codes)
 
     @property
     def scale(self) -> float:
@@ -269,9 +272,12 @@ class DecodeWorkload:
         return [int(x) for x in np.random.default_rng(self.seed).integers(
             lo, self.Nk, size=self.B, endpoint=True)]
 
+    def kv_elem_bytes(self) -> int:
+        return 1 if self.kv_cache == "e4m3" else 2
+
     def kv_bytes(self) -> int:
         """K and V bytes of the valid cache positions (what one call must read)."""
-        return 2 * sum(self.cache_lens()) * self.Hkv * self.d * 2
+        return 2 * sum(self.cache_lens()) * self.Hkv * self.d * self.kv_elem_bytes()
 
     def io_bytes(self) -> int:
         """Compulsory HBM bytes of one call: valid K/V, q and o, lse."""
@@ -293,16 +299,30 @@ DECODE_WORKLOADS: Dict[str, DecodeWorkload] = {
     "decode_llama": DecodeWorkload("decode_llama", B=16, Hq=32, Hkv=8, Nq=1, Nk=8192, d=128,
                                    dtype="bf16", causal=True, seed=6),
     # four new tokens per sequence (draft verification), ragged cache lengths
+    # decode_llama over an FP8 (e4m3fn) cache: the same inputs quantised, half the cache bytes
+    "decode_llama_fp8": DecodeWorkload("decode_llama_fp8", B=16, Hq=32, Hkv=8, Nq=1, Nk=8192,
+                                       d=128, dtype="bf16", causal=True, seed=6, kv_cache="e4m3"),
     "decode_multi": DecodeWorkload("decode_multi", B=4, Hq=32, Hkv=8, Nq=4, Nk=4096, d=128,
                                    dtype="bf16", causal=True, seed=7, lens="draw:1024"),
 }
 
 
-def decode_custom(B, Hq, Hkv, Nq, Nk, d, dtype="bf16", causal=True, seed=0, lens="full"):
+def decode_custom(B, Hq, Hkv, Nq, Nk, d, dtype="bf16", causal=True, seed=0, lens="full",
+                  kv_cache="same"):
     if isinstance(lens, list):
         lens = tuple(lens)
     return DecodeWorkload("decode_custom", B=B, Hq=Hq, Hkv=Hkv, Nq=Nq, Nk=Nk, d=d, dtype=dtype,
-                          causal=causal, seed=seed, lens=lens)
+                          causal=causal, seed=seed, lens=lens, kv_cache=kv_cache)
+
+
+def decode_fp8_inputs(w: DecodeWorkload):
+    """generate_decode's arrays with k and v replaced by e4m3fn codes (uint8) and
+    their descales "descale_k", "descale_v" (quantize_e4m3); q stays float32."""
+    a = generate_decode(w)
+    qa = quantize_e4m3(a, names=("k", "v"))
+    a["k"], a["v"] = qa["k"], qa["v"]
+    a["descale_k"], a["descale_v"] = qa["descale_k"], qa["descale_v"]
+    return a
 
 
 def generate_decode(w: DecodeWorkload):
