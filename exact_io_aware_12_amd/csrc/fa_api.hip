@@ -1,6 +1,7 @@
 // C ABI of libfa.so (declared in include/fa.h): argument checks, then the
 // kernel launches. Nothing here allocates memory or keeps state.
 #include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <cstdint>
 
@@ -381,16 +382,63 @@ int check_kvcache(int B, int Hq, int Hkv, int Nq, int Nk, int d, float scale, in
   return FA_OK;
 }
 
-// Key ranges per (entry, KV head): about `waves` one-wave workgroups over the
-// 256 CUs (8 per CU for a 16-bit cache; 4 for an e4m3 cache, whose waves do
-// twice the work per byte and measured fastest at that count), each range at
-// least two key tiles.
-int kv_splits(int B, int Hq, int Hkv, int Nq, int Nk, int waves = 2048) {
+// decode_kernel workgroups resident per CU and CUs per device: the runtime's
+// occupancy figure for the exact instantiation when a device is present
+// (cached per configuration: one GPU type per process), else the same bound
+// from LDS (160 KiB per CU) and registers (the counts this build allocates:
+// 2 waves per SIMD at d <= 128, 3 for an e4m3 cache at d = 64, 1 at d = 256).
+struct Residency {
+  int per_cu, cus;
+};
+Residency decode_residency(int d, bool kv8, int dtype, int causal) {
+  static std::atomic<int> cache[2][3][2][2][2];   // [bf16][d][causal][kv8][per_cu, cus]
+  const int di = d == 64 ? 0 : d == 128 ? 1 : 2;
+  const int bi = dtype == FA_BF16 ? 1 : 0, ci = causal ? 1 : 0, ki = kv8 ? 1 : 0;
+  std::atomic<int>* c = cache[bi][di][ci][ki];
+  int per_cu = c[0].load(std::memory_order_relaxed);
+  int cus = c[1].load(std::memory_order_relaxed);
+  if (per_cu > 0 && cus > 0) return {per_cu, cus};
+  int dev = 0;
+  per_cu = 0;
+  cus = 0;
+  if (hipGetDevice(&dev) == hipSuccess &&
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
+      cus > 0)
+    per_cu = fa::decode_resident_per_cu(dtype == FA_BF16, d, causal != 0, kv8);
+  (void)hipGetLastError();
+  if (per_cu > 0) {
+    c[0].store(per_cu, std::memory_order_relaxed);
+    c[1].store(cus, std::memory_order_relaxed);
+    return {per_cu, cus};
+  }
+  const int by_lds = (160 * 1024) / fa::decode_lds_bytes(d, kv8);
+  const int by_regs = 4 * (d == 256 ? 1 : (d == 64 && kv8) ? 3 : 2);
+  return {std::max(1, std::min(by_lds, by_regs)), 256};
+}
+
+// Key ranges per (entry, KV head): as many as keep every decode_kernel
+// workgroup resident at once (one round of waves over the GPU). Measured on
+// 8192-token caches, the call is fastest at exactly one full round and a
+// second, partly filled round costs up to 40 %. Each range holds at least
+// eight key tiles (256 keys: on 4096-token caches shorter ranges measured
+// slower, their merge and fixed costs outweighing the extra parallelism), and
+// there are at most 256 ranges.
+// The count depends on the head dimension and the cache type only: the
+// residency taken is the smallest over query dtype and mask, so the query
+// functions below, which take neither, report exactly what a call uses.
+int kv_splits(int B, int Hq, int Hkv, int Nq, int Nk, int d, bool kv8) {
   const int tk = fa::decode_tile_keys();
+  Residency r = decode_residency(d, kv8, FA_FP16, 0);
+  for (int dt : {FA_FP16, FA_BF16})
+    for (int c : {0, 1}) {
+      const Residency x = decode_residency(d, kv8, dt, c);
+      r.per_cu = std::min(r.per_cu, x.per_cu);
+      r.cus = std::min(r.cus, x.cus);
+    }
   const int64_t rows = (int64_t)(Hq / Hkv) * Nq;
   const int64_t base = (int64_t)B * Hkv * ((rows + 31) / 32);
-  const int64_t want = (waves + base - 1) / (base > 0 ? base : 1);
-  const int64_t most = std::max<int64_t>(1, (Nk + 2 * tk - 1) / (2 * tk));
+  const int64_t want = (int64_t)r.per_cu * r.cus / (base > 0 ? base : 1);
+  const int64_t most = std::max<int64_t>(1, (Nk + 8 * tk - 1) / (8 * tk));
   return (int)std::max<int64_t>(1, std::min<int64_t>(want, std::min<int64_t>(most, 256)));
 }
 
@@ -399,20 +447,24 @@ int kv_splits(int B, int Hq, int Hkv, int Nq, int Nk, int waves = 2048) {
 int fa_kvcache_num_splits(int B, int Hq, int Hkv, int Nq, int Nk, int d) {
   bool noop;
   if (check_kvcache(B, Hq, Hkv, Nq, Nk, d, 1.f, 0, 0, FA_FP16, &noop) != FA_OK) return 0;
-  return kv_splits(B, Hq, Hkv, Nq, Nk);
+  return kv_splits(B, Hq, Hkv, Nq, Nk, d, false);
 }
 
 int fa_kvcache_fp8_num_splits(int B, int Hq, int Hkv, int Nq, int Nk, int d) {
   bool noop;
   if (check_kvcache(B, Hq, Hkv, Nq, Nk, d, 1.f, 0, 0, FA_FP16, &noop) != FA_OK) return 0;
-  return kv_splits(B, Hq, Hkv, Nq, Nk, 1024);
+  return kv_splits(B, Hq, Hkv, Nq, Nk, d, true);
 }
 
 size_t fa_fwd_kvcache_workspace_size(int B, int Hq, int Hkv, int Nq, int Nk, int d,
                                      int num_splits) {
   bool noop;
   if (check_kvcache(B, Hq, Hkv, Nq, Nk, d, 1.f, 0, num_splits, FA_FP16, &noop) != FA_OK) return 0;
-  const int sp = num_splits > 0 ? num_splits : kv_splits(B, Hq, Hkv, Nq, Nk);
+  // num_splits = 0: enough for either cache type's automatic count
+  const int sp = num_splits > 0
+                     ? num_splits
+                     : std::max(kv_splits(B, Hq, Hkv, Nq, Nk, d, false),
+                                kv_splits(B, Hq, Hkv, Nq, Nk, d, true));
   const size_t bytes = (size_t)sp * B * Hq * Nq * (size_t)(d + 1) * sizeof(float);
   return (bytes + 255) / 256 * 256;
 }
@@ -437,8 +489,7 @@ int kvcache_common(int stage, const void* q, const void* k_cache, const void* v_
   for (const void* p : ptrs)
     if (p && !aligned16(p)) return FA_ERR_INVALID_ARG;
   if ((reinterpret_cast<uintptr_t>(cache_seqlens) & 3u) != 0) return FA_ERR_INVALID_ARG;
-  // the e4m3 count is never above the 16-bit one, so the automatic workspace size covers both
-  const int sp = num_splits > 0 ? num_splits : kv_splits(B, Hq, Hkv, Nq, Nk, kv8 ? 1024 : 2048);
+  const int sp = num_splits > 0 ? num_splits : kv_splits(B, Hq, Hkv, Nq, Nk, d, kv8);
   if (!workspace || workspace_bytes < fa_fwd_kvcache_workspace_size(B, Hq, Hkv, Nq, Nk, d, sp))
     return FA_ERR_WORKSPACE;
   fa::DecodeArgs a;

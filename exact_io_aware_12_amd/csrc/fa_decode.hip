@@ -386,6 +386,28 @@ hipError_t launch(const DecodeArgs& a, int stage, hipStream_t s) {
   return hipSuccess;
 }
 
+// Resident one-wave workgroups of one decode_kernel instantiation per CU, as
+// the runtime computes them from its LDS and register allocation; 0 if the
+// runtime cannot tell (no device).
+template <typename T, int D, bool CAUSAL, bool KV8>
+int occupancy() {
+  int n = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
+          &n, reinterpret_cast<const void*>(&decode_kernel<T, D, CAUSAL, KV8>), 64, 0) !=
+      hipSuccess) {
+    (void)hipGetLastError();
+    return 0;
+  }
+  return n;
+}
+
+template <typename T, bool KV8>
+int occupancy_of(int d, bool causal) {
+  if (d == 64) return causal ? occupancy<T, 64, true, KV8>() : occupancy<T, 64, false, KV8>();
+  if (d == 128) return causal ? occupancy<T, 128, true, KV8>() : occupancy<T, 128, false, KV8>();
+  return causal ? occupancy<T, 256, true, KV8>() : occupancy<T, 256, false, KV8>();
+}
+
 template <typename T, bool KV8>
 hipError_t dispatch(const DecodeArgs& a, int d, bool causal, int stage, hipStream_t s) {
   if (d == 64)
@@ -399,6 +421,14 @@ hipError_t dispatch(const DecodeArgs& a, int d, bool causal, int stage, hipStrea
 
 int decode_tile_keys() { return kTK; }
 int decode_num_stages() { return 2; }
+
+int decode_resident_per_cu(bool bf16_in, int d, bool causal, bool kv8) {
+  if (bf16_in)
+    return kv8 ? occupancy_of<bf16, true>(d, causal) : occupancy_of<bf16, false>(d, causal);
+  return kv8 ? occupancy_of<f16, true>(d, causal) : occupancy_of<f16, false>(d, causal);
+}
+
+int decode_lds_bytes(int d, bool kv8) { return kStages * 2 * kTK * d * (kv8 ? 1 : 2); }
 
 hipError_t launch_decode(const DecodeArgs& a, bool bf16_in, int d, bool causal, bool kv8,
                          int stage, hipStream_t s) {

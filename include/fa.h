@@ -302,9 +302,7 @@ int fa_fwd_kvcache_stage(int stage, const void* q, const void* k_cache, const vo
  * multiplied by descale_v. Codes 0x7f and 0xff (NaN) make the rows that see
  * them NaN. Workspace, num_splits, stages and every other convention as for
  * fa_fwd_kvcache (same workspace size function). num_splits = 0 picks
- * fa_kvcache_fp8_num_splits(...) ranges, never more than fa_kvcache_num_splits
- * (about half as many: each wave does twice the work per cache byte), so the
- * automatic workspace size still suffices.
+ * fa_kvcache_fp8_num_splits(...) ranges.
  */
 int fa_fwd_kvcache_fp8(const void* q, const void* k_cache, const void* v_cache,
                        const int32_t* cache_seqlens, void* o, float* lse,
@@ -318,13 +316,18 @@ int fa_fwd_kvcache_fp8_stage(int stage, const void* q, const void* k_cache, cons
                              int dtype, void* workspace, size_t workspace_bytes,
                              hipStream_t stream);
 
-/* The key-range count fa_fwd_kvcache uses for num_splits = 0 (>= 1); 0 on bad sizes. */
+/* The key-range count fa_fwd_kvcache uses for num_splits = 0 (>= 1); 0 on bad sizes.
+ * It is the largest count whose workgroups are all resident on the current device
+ * at once (from the runtime's occupancy figure for the decode kernel; a fixed
+ * per-CU bound for a 256-CU part when no device is present), at least 256 keys
+ * (eight 32-key tiles) per range and at most 256 ranges. */
 int fa_kvcache_num_splits(int B, int Hq, int Hkv, int Nq, int Nk, int d);
-/* The same for fa_fwd_kvcache_fp8 (>= 1, <= fa_kvcache_num_splits); 0 on bad sizes. */
+/* The same for fa_fwd_kvcache_fp8, whose workgroups need half the LDS. */
 int fa_kvcache_fp8_num_splits(int B, int Hq, int Hkv, int Nq, int Nk, int d);
 
-/* Workspace bytes for fa_fwd_kvcache: (d + 1)·4 bytes per (split, entry, query head,
- * query), rounded up to 256; num_splits = 0 means the automatic count. 0 on bad sizes. */
+/* Workspace bytes for fa_fwd_kvcache and fa_fwd_kvcache_fp8: (d + 1)·4 bytes per
+ * (split, entry, query head, query), rounded up to 256; num_splits = 0 means the
+ * larger of the two automatic counts. 0 on bad sizes. */
 size_t fa_fwd_kvcache_workspace_size(int B, int Hq, int Hkv, int Nq, int Nk, int d,
                                      int num_splits);
 

@@ -170,14 +170,18 @@ def test_kvcache_host_checks(kw, status):
 
 
 def test_kvcache_splits_and_workspace():
-    # rows per (entry, KV head) = (Hq/Hkv)·Nq = 4 -> one 32-row block; 16·8 blocks want 16 ranges
-    assert fa.fa_kvcache_num_splits(16, 32, 8, 1, 8192, 128) == 16
-    # at most one range per two 32-key tiles
-    assert fa.fa_kvcache_num_splits(1, 2, 2, 1, 100, 64) == 2
+    # rows per (entry, KV head) = (Hq/Hkv)·Nq = 4 -> one 32-row block; with no device the
+    # residency bound is 3 workgroups per CU (48 KiB of LDS each) on 256 CUs: 768 / (16·8) = 6
+    assert fa.fa_kvcache_num_splits(16, 32, 8, 1, 8192, 128) == 6
+    # at most one range per 256 keys (eight 32-key tiles)
+    assert fa.fa_kvcache_num_splits(1, 2, 2, 1, 100, 64) == 1
+    assert fa.fa_kvcache_num_splits(1, 2, 2, 1, 4096, 64) == 16
+    assert fa.fa_kvcache_num_splits(1, 2, 2, 1, 4097, 64) == 17
     assert fa.fa_kvcache_num_splits(1, 2, 2, 1, 0, 64) == 1
     assert fa.fa_kvcache_num_splits(1, 3, 2, 1, 64, 64) == 0
     assert fa.fa_fwd_kvcache_workspace_size(2, 4, 2, 3, 64, 128, 5) == (5 * 2 * 4 * 3 * 129 * 4 + 255) // 256 * 256
-    assert fa.fa_fwd_kvcache_workspace_size(16, 32, 8, 1, 8192, 128, 0) == 16 * 16 * 32 * 129 * 4
+    # num_splits = 0: the larger automatic count (12, the e4m3 cache's)
+    assert fa.fa_fwd_kvcache_workspace_size(16, 32, 8, 1, 8192, 128, 0) == 12 * 16 * 32 * 129 * 4
     assert fa.fa_fwd_kvcache_workspace_size(1, 2, 2, 1, 64, 80, 1) == 0
 
 
@@ -225,12 +229,14 @@ def test_kvcache_fp8_host_checks(kw, status):
 
 
 def test_kvcache_fp8_splits():
-    # about 4 one-wave workgroups per CU: 16·8 blocks want 8 ranges (16 for a 16-bit cache)
-    assert fa.fa_kvcache_fp8_num_splits(16, 32, 8, 1, 8192, 128) == 8
+    # half the LDS per workgroup: 6 resident per CU, 1536 / (16·8) = 12 ranges
+    assert fa.fa_kvcache_fp8_num_splits(16, 32, 8, 1, 8192, 128) == 12
     for shape in [(16, 32, 8, 1, 8192, 128), (1, 2, 2, 1, 100, 64), (1, 8, 1, 1, 40000, 256),
-                  (3, 12, 4, 5, 777, 64), (64, 8, 8, 1, 1 << 20, 128)]:
+                  (3, 12, 4, 5, 777, 64), (64, 8, 8, 1, 1 << 20, 128), (4, 32, 8, 4, 4096, 128)]:
         n8, n16 = fa.fa_kvcache_fp8_num_splits(*shape), fa.fa_kvcache_num_splits(*shape)
-        assert 1 <= n8 <= n16, shape
+        assert n8 >= n16 >= 1, shape
+        ws = fa.fa_fwd_kvcache_workspace_size(*shape, 0)
+        assert ws == fa.fa_fwd_kvcache_workspace_size(*shape, n8), shape
     assert fa.fa_kvcache_fp8_num_splits(1, 3, 2, 1, 64, 64) == 0
 
 

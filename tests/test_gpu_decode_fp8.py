@@ -186,3 +186,13 @@ def test_benchmark_workload_sampled():
         check_o(host64(o[b, :, h]), O, w.dtype, what=f"O[{b},:,{h}]")
         check_lse(lse_h[h, b * w.Nq:(b + 1) * w.Nq], L, what=f"LSE[{h},{b}]")
     say(f"   {len(units)} units ok")
+
+
+def test_automatic_splits_on_the_device():
+    """The automatic counts come from the runtime's occupancy figures on the device:
+    at d = 128 an MI355X holds 3 decode workgroups per CU with a 16-bit cache (48 KiB
+    of LDS each) and 6 with an e4m3 cache, on 256 CUs, so 16·8 (entry, KV head)
+    blocks take 6 and 12 ranges: one full round of resident waves."""
+    fa = _fa()
+    assert fa.fa_kvcache_num_splits(16, 32, 8, 1, 8192, 128) == 6
+    assert fa.fa_kvcache_fp8_num_splits(16, 32, 8, 1, 8192, 128) == 12
