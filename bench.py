@@ -52,6 +52,9 @@ def parse():
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--workload", default="train_16k")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--smi", metavar="PATH",
+                   help="with --sweep: read amd-smi (clock, power, temperature) while each "
+                        "workload of >= 1 ms per call runs, into PATH as JSON")
     p.add_argument("--sweep", action="store_true",
                    help="time fa_fwd on every forward workload (10 warmup, 100 timed calls)")
     p.add_argument("--fp8-sweep", action="store_true",
@@ -238,6 +241,53 @@ def time_calls(torch, fn, iters, warmup):
     e1.record()
     torch.cuda.synchronize()
     return e0.elapsed_time(e1) / iters
+
+
+def time_calls_dist(torch, fn, iters, warmup, scratch=None):
+    """Per-call HIP event pairs on the current stream: (median, min) ms per call.
+
+    With `scratch` (a device buffer larger than the 256 MB last-level cache), the
+    buffer is overwritten before each call, outside its event pair: every call
+    then starts with its inputs evicted from L2 and the cache (cold inputs)."""
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(iters)]
+    for a, b in ev:
+        if scratch is not None:
+            scratch.zero_()
+        a.record()
+        fn()
+        b.record()
+    torch.cuda.synchronize()
+    ts = sorted(a.elapsed_time(b) for a, b in ev)
+    n = len(ts)
+    med = ts[n // 2] if n % 2 else 0.5 * (ts[n // 2 - 1] + ts[n // 2])
+    return med, ts[0]
+
+
+def smi_sample(torch, fn, ms_per_call, seconds=8.0):
+    """Clock, power and temperature while the GPU runs `fn` back to back: calls
+    for about `seconds` are enqueued, amd-smi is read once while they run, and
+    its JSON (or its error text) is returned."""
+    import subprocess
+    n = max(1, int(seconds * 1e3 / max(ms_per_call, 1e-3)))
+    for _ in range(n):
+        fn()
+    try:
+        r = subprocess.run(["amd-smi", "metric", "-g", "0", "--power", "--clock",
+                            "--temperature", "--json"], capture_output=True, text=True,
+                           timeout=30)
+        out = r.stdout.strip() or r.stderr.strip()
+        try:
+            out = json.loads(out)
+        except ValueError:
+            pass
+    except Exception as e:  # the tool missing or hanging must not fail the sweep
+        out = f"amd-smi unavailable: {e}"
+    torch.cuda.synchronize()
+    return out
 
 
 def cpu_baseline(w, min_seconds=10.0, max_units=4):
@@ -602,16 +652,34 @@ def run_sweep(args):
                                                                       "dropout_16k"]
     if args.names:
         names = args.names.split(",")
+    # inputs and outputs smaller than twice the 256 MB last-level cache also get a
+    # cold-input timing (a 1 GiB scratch buffer overwritten between calls)
+    scratch = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    smi = {}
     for n in names:
         w = W.WORKLOADS[n]
         b = Bound(w, with_bwd=False)
         ms = time_calls(torch, b.fwd, 100, 10)
+        med, mn = time_calls_dist(torch, b.fwd, 100, 0)
         tf = w.fwd_flop() / (ms * 1e-3) / 1e12
-        print(json.dumps({"workload": n, "N": w.N, "d": w.d, "dtype": w.dtype, "causal": w.causal,
-                          "fwd_ms": round(ms, 4), "fwd_tflops": round(tf, 2),
-                          "pct_of_peak": round(100 * tf / PEAK_BF16_TFLOPS, 2)}), flush=True)
+        io = sum(x.numel() * x.element_size() for x in (b.t["q"], b.t["k"], b.t["v"], b.o, b.lse))
+        line = {"workload": n, "N": w.N, "d": w.d, "dtype": w.dtype, "causal": w.causal,
+                "fwd_ms": round(ms, 4), "fwd_tflops": round(tf, 2),
+                "pct_of_peak": round(100 * tf / PEAK_BF16_TFLOPS, 2),
+                "fwd_ms_median": round(med, 4), "fwd_ms_min": round(mn, 4),
+                "io_mb": round(io / 1e6, 2)}
+        if io < 512e6:
+            cmed, cmn = time_calls_dist(torch, b.fwd, 100, 0, scratch=scratch)
+            line.update({"cold_fwd_ms_median": round(cmed, 4), "cold_fwd_ms_min": round(cmn, 4),
+                         "cold_tflops": round(w.fwd_flop() / (cmed * 1e-3) / 1e12, 2)})
+        if args.smi and ms >= 1.0:
+            smi[n] = smi_sample(torch, b.fwd, ms)
+        print(json.dumps(line), flush=True)
         del b
         torch.cuda.empty_cache()
+    if args.smi:
+        with open(args.smi, "w") as f:
+            json.dump(smi, f, indent=1)
 
 
 def run_fp8_sweep(args):
