@@ -332,6 +332,33 @@ def cpu_baseline(w, min_seconds=10.0, max_units=4):
                       f"{dt:.1f} s wall; algorithmic FLOP of those units / wall time"}
 
 
+class KvlenBound:
+    """Device buffers and the raw fa_fwd_kvlen call of one chunked-prefill workload."""
+
+    def __init__(self, w):
+        import torch
+        import exact_io_aware_12_amd as fa
+        import workloads as W
+        self.fa, self.w = fa, w
+        td = {"fp16": torch.float16, "bf16": torch.bfloat16}[w.dtype]
+        a = W.generate_kvlen(w)
+        self.t = {n: torch.from_numpy(a[n]).to(td).cuda() for n in ("q", "k", "v")}
+        del a
+        self.o = torch.empty_like(self.t["q"])
+        self.lse = torch.empty((w.Hq, w.B * w.Nq), dtype=torch.float32, device="cuda")
+        self.code = fa.FA_BF16 if w.dtype == "bf16" else fa.FA_FP16
+        self.stream = torch.cuda.current_stream().cuda_stream
+
+    def fwd(self):
+        w, t = self.w, self.t
+        st = self.fa.fa_fwd_kvlen(t["q"].data_ptr(), t["k"].data_ptr(), t["v"].data_ptr(),
+                                  self.o.data_ptr(), self.lse.data_ptr(), w.B, w.Hq, w.Hkv, w.Nq,
+                                  w.Nk, w.d, w.scale, int(w.causal), None, None, self.code,
+                                  self.stream)
+        if st != self.fa.FA_OK:
+            raise self.fa.FaError(st, "fa_fwd_kvlen")
+
+
 class DecodeBound:
     """Device buffers and raw C-ABI calls of one decode workload."""
 
@@ -649,7 +676,8 @@ def run_sweep(args):
                                                                       "fwd_d256_N4096",
                                                                       "window_16k",
                                                                       "softcap_16k",
-                                                                      "dropout_16k"]
+                                                                      "dropout_16k",
+                                                                      "prefill_chunk"]
     if args.names:
         names = args.names.split(",")
     # inputs and outputs smaller than twice the 256 MB last-level cache also get a
@@ -657,6 +685,21 @@ def run_sweep(args):
     scratch = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
     smi = {}
     for n in names:
+        if n in W.KVLEN_WORKLOADS:   # queries and keys of different lengths
+            w = W.KVLEN_WORKLOADS[n]
+            b = KvlenBound(w)
+            ms = time_calls(torch, b.fwd, 100, 10)
+            med, mn = time_calls_dist(torch, b.fwd, 100, 0)
+            tf = w.fwd_flop() / (ms * 1e-3) / 1e12
+            print(json.dumps({"workload": n, "Nq": w.Nq, "Nk": w.Nk, "d": w.d, "dtype": w.dtype,
+                              "causal": w.causal, "fwd_ms": round(ms, 4),
+                              "fwd_tflops": round(tf, 2),
+                              "pct_of_peak": round(100 * tf / PEAK_BF16_TFLOPS, 2),
+                              "fwd_ms_median": round(med, 4), "fwd_ms_min": round(mn, 4)}),
+                  flush=True)
+            del b
+            torch.cuda.empty_cache()
+            continue
         w = W.WORKLOADS[n]
         b = Bound(w, with_bwd=False)
         ms = time_calls(torch, b.fwd, 100, 10)

@@ -40,7 +40,8 @@ __all__ = ["FA_OK", "FA_ERR_INVALID_ARG", "FA_ERR_UNSUPPORTED", "FA_ERR_HIP", "F
            "flash_attn_backward", "fa_bwd_stage", "fa_bwd_num_stages", "fa_fwd_kvcache",
            "fa_kvcache_num_splits", "fa_fwd_kvcache_workspace_size", "flash_attn_with_kvcache",
            "fa_fwd_kvcache_stage", "fa_fwd_kvcache_num_stages", "fa_fwd_kvcache_fp8",
-           "fa_fwd_kvcache_fp8_stage", "fa_kvcache_fp8_num_splits"]
+           "fa_fwd_kvcache_fp8_stage", "fa_kvcache_fp8_num_splits",
+           "fa_fwd_kvlen", "flash_attn_kvlen_func"]
 
 FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_HIP, FA_ERR_WORKSPACE = 0, -1, -2, -3, -4
 FA_FP16, FA_BF16 = 0, 1
@@ -102,6 +103,8 @@ def _load():
     L.fa_bwd_dropout.restype = i
     L.fa_bwd_dropout_stage.argtypes = [i] + L.fa_bwd_dropout.argtypes
     L.fa_bwd_dropout_stage.restype = i
+    L.fa_fwd_kvlen.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, vp, vp, i, vp]
+    L.fa_fwd_kvlen.restype = i
     L.fa_fwd_fp8.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp, f, f, f, i, vp]
     L.fa_fwd_fp8.restype = i
     L.fa_fwd_kvcache.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, i, i, vp, sz, vp]
@@ -220,6 +223,12 @@ def _dropout_args(dropout_p, dropout_seed, causal_window, softcap):
     if not 0 <= seed < 2 ** 64:
         raise ValueError("dropout_seed must be a 64-bit unsigned integer")
     return float(dropout_p), seed
+
+
+def fa_fwd_kvlen(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, scale, causal, cu_seqlens_q,
+                 cu_seqlens_k, dtype, stream) -> int:
+    return lib.fa_fwd_kvlen(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, scale, causal, cu_seqlens_q,
+                            cu_seqlens_k, dtype, stream)
 
 
 def fa_fwd_fp8(q, k, v, o, lse, B, Hq, Hkv, N, d, scale, causal, cu_seqlens, descale_q,
@@ -393,6 +402,59 @@ def flash_attn_func(q, k, v, causal=False, softmax_scale=None, cu_seqlens=None, 
                                _dtype_code(q), _stream())
     if st != FA_OK:
         raise FaError(st, "fa_fwd" if w is None else "fa_fwd_window")
+    return o, lse
+
+
+def flash_attn_kvlen_func(q, k, v, causal=False, softmax_scale=None, cu_seqlens_q=None,
+                          cu_seqlens_k=None, max_seqlen_q=None, max_seqlen_k=None):
+    """Forward with queries and keys of different lengths (chunked prefill).
+    Returns (o, lse); lse is float32 [Hq, Tq].
+
+    Fixed length: q [B, Nq, Hq, d], k, v [B, Nk, Hkv, d]. Varlen: q [Tq, Hq, d] with
+    cu_seqlens_q and max_seqlen_q, k, v [Tk, Hkv, d] with cu_seqlens_k and
+    max_seqlen_k (int32, B+1 entries each). The queries of a sequence are its last
+    positions: with causal, query i sees keys j <= i + Lk - Lq; a query that sees no
+    key gets o = 0 and lse = -inf (see fa_fwd_kvlen in include/fa.h)."""
+    import torch
+    if v.shape != k.shape:
+        raise ValueError("k and v must have the same shape")
+    if not (q.dtype == k.dtype == v.dtype):
+        raise TypeError("q, k, v must share one dtype")
+    if (cu_seqlens_q is None) != (cu_seqlens_k is None):
+        raise ValueError("give both cu_seqlens_q and cu_seqlens_k, or neither")
+    if cu_seqlens_q is None:
+        if q.dim() != 4 or k.dim() != 4:
+            raise ValueError("fixed-length inputs are (batch, seq, heads, head_dim)")
+        B, Nq, Hq, d = q.shape
+        if k.shape[0] != B or k.shape[3] != d:
+            raise ValueError(f"q {tuple(q.shape)} and k {tuple(k.shape)} do not match")
+        Nk, Hkv, Tq = k.shape[1], k.shape[2], B * Nq
+    else:
+        if q.dim() != 3 or k.dim() != 3:
+            raise ValueError("varlen inputs are packed (total_tokens, heads, head_dim)")
+        if max_seqlen_q is None or max_seqlen_k is None:
+            raise ValueError("varlen needs max_seqlen_q and max_seqlen_k")
+        if cu_seqlens_q.numel() != cu_seqlens_k.numel():
+            raise ValueError("cu_seqlens_q and cu_seqlens_k need the same number of entries")
+        Tq, Hq, d = q.shape
+        if k.shape[2] != d:
+            raise ValueError(f"q {tuple(q.shape)} and k {tuple(k.shape)} do not match")
+        B, Nq, Nk, Hkv = cu_seqlens_q.numel() - 1, int(max_seqlen_q), int(max_seqlen_k), k.shape[1]
+        for c in (cu_seqlens_q, cu_seqlens_k):
+            _check_dev(c)
+            if c.dtype != torch.int32:
+                raise TypeError("cu_seqlens must be int32")
+    _check_dev(q, k, v)
+    scale = softmax_scale if softmax_scale is not None else 1.0 / math.sqrt(d)
+    o = torch.empty_like(q)
+    lse = torch.empty((Hq, Tq), dtype=torch.float32, device=q.device)
+    cq = cu_seqlens_q.data_ptr() if cu_seqlens_q is not None else None
+    ck = cu_seqlens_k.data_ptr() if cu_seqlens_k is not None else None
+    st = lib.fa_fwd_kvlen(q.data_ptr(), k.data_ptr() or None, v.data_ptr() or None, o.data_ptr(),
+                          lse.data_ptr(), B, Hq, Hkv, Nq, Nk, d, float(scale), int(bool(causal)),
+                          cq, ck, _dtype_code(q), _stream())
+    if st != FA_OK:
+        raise FaError(st, "fa_fwd_kvlen")
     return o, lse
 
 

@@ -137,6 +137,50 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int
                     causal ? fa::kMaskCausal : fa::kMaskNone, 0, 0, cu_seqlens, dtype, stream);
 }
 
+int fa_fwd_kvlen(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq,
+                 int Hkv, int Nq, int Nk, int d, float scale, int causal,
+                 const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int dtype,
+                 hipStream_t stream) {
+  const bool varlen = cu_seqlens_q != nullptr;
+  if (varlen != (cu_seqlens_k != nullptr)) return FA_ERR_INVALID_ARG;
+  bool noop;
+  int st = check_sizes(B, Hq, Hkv, Nq, d, scale, causal, dtype, &noop, 256);
+  if (st != FA_OK) return st;
+  if (Nk < 0) return FA_ERR_INVALID_ARG;
+  if ((int64_t)B * Nk >= (int64_t)1 << 31) return FA_ERR_UNSUPPORTED;
+  if (noop) return FA_OK;   // no query
+  if (!q || !o || !lse) return FA_ERR_INVALID_ARG;
+  if (Nk > 0 && (!k || !v)) return FA_ERR_INVALID_ARG;   // with Nk = 0 no key is read
+  const void* ptrs[] = {q, k, v, o, lse};
+  for (const void* p : ptrs)
+    if (p && !aligned16(p)) return FA_ERR_INVALID_ARG;
+  fa::FwdArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.lse = lse;
+  a.cu_seqlens = cu_seqlens_q;
+  a.cu_seqlens_k = cu_seqlens_k;
+  a.B = B;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.N = Nq;
+  a.Nk = Nk;
+  a.group = Hq / Hkv;
+  const int br = fa::fwd_query_tile();
+  a.n_qtiles = (Nq + br - 1) / br;
+  a.scale_log2 = scale * kLog2e;
+  a.wl = a.wr = 0;
+  a.cap_in = a.cap_out = 0.f;
+  a.seed_lo = a.seed_hi = 0;
+  a.keep_t = 256;
+  a.drop_scale = 1.f;
+  if ((int64_t)a.n_qtiles * Hq * B >= (int64_t)1 << 31) return FA_ERR_UNSUPPORTED;
+  hipError_t e = fa::launch_fwd_kvlen(a, dtype == FA_BF16, d, causal != 0, varlen, stream);
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
 int fa_fwd_softcap(const void* q, const void* k, const void* v, void* o, float* lse, int B,
                    int Hq, int Hkv, int N, int d, float scale, int causal, float softcap,
                    const int32_t* cu_seqlens, int dtype, hipStream_t stream) {

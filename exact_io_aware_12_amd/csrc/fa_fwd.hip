@@ -48,7 +48,8 @@ __device__ __forceinline__ void fwd_tile(const T* kt, const T* vt, const u32x4 (
                                          f32x16 (&o)[D / 32], float& mc, float& l, float& lr,
                                          float c, int kv0, int L, int qrow, int wl, int wr,
                                          int lane, float cap_in = 0.f, float cap_out = 0.f,
-                                         const DropKey* dk = nullptr, int seq = 0, int head = 0) {
+                                         const DropKey* dk = nullptr, int seq = 0, int head = 0,
+                                         bool empty_rows = false) {
   constexpr int NKB = D / 16;
   constexpr int NCB = D / 32;
   const int col = lane & 31, half = lane >> 5;
@@ -89,10 +90,11 @@ __device__ __forceinline__ void fwd_tile(const T* kt, const T* vt, const u32x4 (
   const float mxc = wave_max_halves(mx) * c;
   // a window's edge tile can hold no visible key for a row that has seen none
   // yet either: such a row keeps mc = −inf, scales nothing and adds P = 0
-  constexpr bool GUARD = WIN && EDGE;
+  // (so can a row placed before every key when the key and query lengths differ)
+  const bool guard = (WIN || empty_rows) && EDGE;
   if (__builtin_amdgcn_ballot_w64(mxc > mc + kRescaleHeadroom) != 0) {   // wave-uniform
-    const float mc_new = fmaxf(mc, mxc);     // finite without a window: key 0 is in tile 0
-    const float alpha = (GUARD && mc_new == -INFINITY) ? 1.f : fast_exp2(mc - mc_new);
+    const float mc_new = fmaxf(mc, mxc);     // finite otherwise: key 0 is in tile 0
+    const float alpha = (guard && mc_new == -INFINITY) ? 1.f : fast_exp2(mc - mc_new);
     l *= alpha;
     lr *= alpha;
 #pragma unroll
@@ -105,7 +107,7 @@ __device__ __forceinline__ void fwd_tile(const T* kt, const T* vt, const u32x4 (
   for (int jb = 0; jb < 2; ++jb)
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      s[jb][i] = fast_exp2(fmaf(s[jb][i], c, GUARD && mc == -INFINITY ? 0.f : -mc));
+      s[jb][i] = fast_exp2(fmaf(s[jb][i], c, guard && mc == -INFINITY ? 0.f : -mc));
       if constexpr (kLseFromUnrounded<T>) ls[i & 3] += s[jb][i];
     }
   if constexpr (kLseFromUnrounded<T>) l += (ls[0] + ls[1]) + (ls[2] + ls[3]);
@@ -149,8 +151,12 @@ __device__ __forceinline__ void fwd_tile(const T* kt, const T* vt, const u32x4 (
 
 // WIN: sliding window, key j visible from query i iff i − a.wl ≤ j ≤ i + a.wr
 // (bounds clamped to N by the caller; CAUSAL is false then)
+// KVLEN: the keys of a sequence have their own length Lk (a.Nk, or
+// a.cu_seqlens_k) and the Lq queries are its last Lq positions: query i sits
+// at position i + Lk − Lq and, when causal, sees keys j ≤ i + Lk − Lq (no
+// window, soft cap or dropout). A query that sees no key gets O = 0, LSE = −inf.
 template <typename T, int D, bool CAUSAL, bool VARLEN, bool WIN, bool CAP = false,
-          bool DROP = false>
+          bool DROP = false, bool KVLEN = false>
 // two workgroups per CU up to d = 128; at d = 256 the O accumulators alone
 // take 128 registers and the kernel runs one workgroup per CU
 __global__ __launch_bounds__(kThreads, D <= 128 ? 2 : 1) void fwd_kernel(FwdArgs a) {
@@ -173,7 +179,7 @@ __global__ __launch_bounds__(kThreads, D <= 128 ? 2 : 1) void fwd_kernel(FwdArgs
   const int b = hb % a.B, h = hb / a.B;
   const int qt = CAUSAL ? a.n_qtiles - 1 - qt_ord : qt_ord;
 
-  int seq0, L, T_total;
+  int seq0, L, T_total;   // the sequence's queries: first token, count, tokens of the batch
   if constexpr (VARLEN) {
     seq0 = a.cu_seqlens[b];
     L = a.cu_seqlens[b + 1] - seq0;
@@ -183,14 +189,25 @@ __global__ __launch_bounds__(kThreads, D <= 128 ? 2 : 1) void fwd_kernel(FwdArgs
     L = a.N;
     T_total = a.B * a.N;
   }
+  int seq0k = seq0, Lk = L;   // its keys
+  if constexpr (KVLEN) {
+    if constexpr (VARLEN) {
+      seq0k = a.cu_seqlens_k[b];
+      Lk = a.cu_seqlens_k[b + 1] - seq0k;
+    } else {
+      seq0k = b * a.Nk;
+      Lk = a.Nk;
+    }
+  }
+  const int off = KVLEN ? Lk - L : 0;   // key position of query 0
   const int q0 = qt * kBR;
   if (q0 >= L) return;
   const int g = h / a.group;
 
   const int64_t qs = (int64_t)a.Hq * D, kvs = (int64_t)a.Hkv * D;
   const T* qp = static_cast<const T*>(a.q) + (int64_t)seq0 * qs + (int64_t)h * D;
-  const T* kp = static_cast<const T*>(a.k) + (int64_t)seq0 * kvs + (int64_t)g * D;
-  const T* vp = static_cast<const T*>(a.v) + (int64_t)seq0 * kvs + (int64_t)g * D;
+  const T* kp = static_cast<const T*>(a.k) + (int64_t)seq0k * kvs + (int64_t)g * D;
+  const T* vp = static_cast<const T*>(a.v) + (int64_t)seq0k * kvs + (int64_t)g * D;
 
   // Key tiles [j_lo, j_hi) are visible to some row of the workgroup; within
   // them [ja, jb) need no masking (every key inside the sequence and visible
@@ -199,25 +216,34 @@ __global__ __launch_bounds__(kThreads, D <= 128 ? 2 : 1) void fwd_kernel(FwdArgs
   int j_lo, ja, jb, j_hi;
   if constexpr (WIN) {
     const int k_lo = max(0, q0 - a.wl);
-    const int k_hi = min(L, q0 + kBR + a.wr);   // one past the last visible key
+    const int k_hi = min(Lk, q0 + kBR + a.wr);   // one past the last visible key
     j_lo = k_lo / kBC;
     j_hi = (k_hi + kBC - 1) / kBC;
     const int first_all = q0 + kBR - 1 - a.wl;  // first key every row sees
     ja = max(j_lo, first_all <= 0 ? 0 : (first_all + kBC - 1) / kBC);
     const int last_all = q0 + a.wr - (kBC - 1);   // a tile starting here ends at q0 + wr
-    jb = min(min(last_all < 0 ? 0 : last_all / kBC + 1, L / kBC), j_hi);
+    jb = min(min(last_all < 0 ? 0 : last_all / kBC + 1, Lk / kBC), j_hi);
     if (jb < ja) jb = ja;
   } else {
-    const int kv_end = CAUSAL ? min(L, q0 + kBR) : L;
     j_lo = ja = 0;
-    j_hi = (kv_end + kBC - 1) / kBC;
-    jb = min(CAUSAL ? min((q0 + 1) / kBC, L / kBC) : L / kBC, j_hi);
+    if constexpr (KVLEN) {
+      // the end may be <= 0 here (no key for any row of the tile, or Lk = 0)
+      const int kv_end = CAUSAL ? min(Lk, q0 + kBR + off) : Lk;
+      j_hi = kv_end > 0 ? (kv_end + kBC - 1) / kBC : 0;
+      jb = min(CAUSAL ? min(max(q0 + off + 1, 0) / kBC, Lk / kBC) : Lk / kBC, j_hi);
+    } else {
+      const int kv_end = CAUSAL ? min(L, q0 + kBR) : L;
+      j_hi = (kv_end + kBC - 1) / kBC;
+      jb = min(CAUSAL ? min((q0 + 1) / kBC, L / kBC) : L / kBC, j_hi);
+    }
   }
   const int ntiles = j_hi;
 
-  // first tile in flight before anything else
-  tile_dma<T, kBC, D, kWaves>(lds[0][0], kp, kvs, j_lo * kBC, L, wave, lane);
-  tile_dma<T, kBC, D, kWaves>(lds[0][1], vp, kvs, j_lo * kBC, L, wave, lane);
+  // first tile in flight before anything else (there is none only with KVLEN)
+  if (!KVLEN || ntiles > j_lo) {
+    tile_dma<T, kBC, D, kWaves>(lds[0][0], kp, kvs, j_lo * kBC, Lk, wave, lane);
+    tile_dma<T, kBC, D, kWaves>(lds[0][1], vp, kvs, j_lo * kBC, Lk, wave, lane);
+  }
 
   // ---- Q fragments (B operand of Sᵀ = K·Qᵀ), kept in registers -------------
   const int qrow = q0 + wave * 32 + col;
@@ -256,20 +282,21 @@ __global__ __launch_bounds__(kThreads, D <= 128 ? 2 : 1) void fwd_kernel(FwdArgs
     __syncthreads();   // everyone's have, and tile j-1 is no longer read
     if (j + 1 < ntiles) {
       const int n0 = kv0 + kBC;
-      if (n0 + kBC <= L) {
+      if (n0 + kBC <= Lk) {
         tile_dma_in<T, kBC, D, kWaves>(lds[BUF ^ 1][0], kp + (int64_t)n0 * kvs, plan, wave_u);
         tile_dma_in<T, kBC, D, kWaves>(lds[BUF ^ 1][1], vp + (int64_t)n0 * kvs, plan, wave_u);
       } else {
-        tile_dma<T, kBC, D, kWaves>(lds[BUF ^ 1][0], kp, kvs, n0, L, wave, lane);
-        tile_dma<T, kBC, D, kWaves>(lds[BUF ^ 1][1], vp, kvs, n0, L, wave, lane);
+        tile_dma<T, kBC, D, kWaves>(lds[BUF ^ 1][0], kp, kvs, n0, Lk, wave, lane);
+        tile_dma<T, kBC, D, kWaves>(lds[BUF ^ 1][1], vp, kvs, n0, Lk, wave, lane);
       }
     }
-    if (EDGE && CAUSAL && kv0 > wq_last) return;  // every key of the tile is after this wave's rows
+    // every key of the tile is after this wave's rows
+    if (EDGE && CAUSAL && kv0 > wq_last + off) return;
     if (EDGE && WIN && (kv0 > wq_last + wr || kv0 + kBC - 1 < wq_first - wl))
       return;   // the tile lies outside the windows of all this wave's rows
     fwd_tile<T, D, CAUSAL, EDGE, WIN, CAP, DROP>(lds[BUF][0], lds[BUF][1], qf, o, mc, l, lr, c,
-                                                 kv0, L, qrow, wl, wr, lane, cap_in, cap_out,
-                                                 &dk, b, h);
+                                                 kv0, Lk, qrow + off, wl, wr, lane, cap_in,
+                                                 cap_out, &dk, b, h, KVLEN);
   };
   using B0 = std::integral_constant<int, 0>;
   using B1 = std::integral_constant<int, 1>;
@@ -294,7 +321,9 @@ __global__ __launch_bounds__(kThreads, D <= 128 ? 2 : 1) void fwd_kernel(FwdArgs
   const float lr_tot = wave_sum_halves(lr);
   const float l_tot = kLseFromUnrounded<T> ? wave_sum_halves(l) : lr_tot;
   if (qrow < L) {
-    const float inv = (DROP ? a.drop_scale : 1.f) / lr_tot;
+    // a row that saw no key (KVLEN only): O = 0, LSE = −inf
+    const bool any = !KVLEN || l_tot > 0.f;
+    const float inv = any ? (DROP ? a.drop_scale : 1.f) / lr_tot : 0.f;
     T* op = static_cast<T*>(a.o) + (int64_t)seq0 * qs + (int64_t)h * D + qrow * qs;
 #pragma unroll
     for (int cb = 0; cb < NCB; ++cb)
@@ -305,18 +334,28 @@ __global__ __launch_bounds__(kThreads, D <= 128 ? 2 : 1) void fwd_kernel(FwdArgs
         w[1] = pack2<T>(o[cb][4 * r + 2] * inv, o[cb][4 * r + 3] * inv);
         *reinterpret_cast<u32x2*>(op + cb * 32 + 8 * r + 4 * half) = w;
       }
-    if (half == 0) a.lse[(int64_t)h * T_total + seq0 + qrow] = (mc + log2f(l_tot)) * kLn2;
+    if (half == 0)
+      a.lse[(int64_t)h * T_total + seq0 + qrow] = any ? (mc + log2f(l_tot)) * kLn2 : -INFINITY;
   }
 }
 
 template <typename T, int D, bool CAUSAL, bool VARLEN, bool WIN, bool CAP = false,
-          bool DROP = false>
+          bool DROP = false, bool KVLEN = false>
 hipError_t launch(const FwdArgs& a, hipStream_t stream) {
   const int grid = a.n_qtiles * a.Hq * a.B;
   (void)hipGetLastError();  // drop an error left pending by earlier, unrelated HIP calls
-  hipLaunchKernelGGL((fwd_kernel<T, D, CAUSAL, VARLEN, WIN, CAP, DROP>), dim3(grid),
+  hipLaunchKernelGGL((fwd_kernel<T, D, CAUSAL, VARLEN, WIN, CAP, DROP, KVLEN>), dim3(grid),
                      dim3(kThreads), 0, stream, a);
   return hipGetLastError();
+}
+
+template <typename T, int D>
+hipError_t dispatch_kvlen(const FwdArgs& a, bool causal, bool varlen, hipStream_t s) {
+  if (causal)
+    return varlen ? launch<T, D, true, true, false, false, false, true>(a, s)
+                  : launch<T, D, true, false, false, false, false, true>(a, s);
+  return varlen ? launch<T, D, false, true, false, false, false, true>(a, s)
+                : launch<T, D, false, false, false, false, false, true>(a, s);
 }
 
 template <typename T, int D>
@@ -359,6 +398,18 @@ hipError_t launch_fwd(const FwdArgs& a, bool bf16_in, int d, int mask, bool varl
   if (d == 64) return dispatch_mask<f16, 64>(a, mask, varlen, cap, drop, s);
   if (d == 128) return dispatch_mask<f16, 128>(a, mask, varlen, cap, drop, s);
   return dispatch_mask<f16, 256>(a, mask, varlen, cap, drop, s);
+}
+
+hipError_t launch_fwd_kvlen(const FwdArgs& a, bool bf16_in, int d, bool causal, bool varlen,
+                            hipStream_t s) {
+  if (bf16_in) {
+    if (d == 64) return dispatch_kvlen<bf16, 64>(a, causal, varlen, s);
+    if (d == 128) return dispatch_kvlen<bf16, 128>(a, causal, varlen, s);
+    return dispatch_kvlen<bf16, 256>(a, causal, varlen, s);
+  }
+  if (d == 64) return dispatch_kvlen<f16, 64>(a, causal, varlen, s);
+  if (d == 128) return dispatch_kvlen<f16, 128>(a, causal, varlen, s);
+  return dispatch_kvlen<f16, 256>(a, causal, varlen, s);
 }
 
 }  // namespace fa

@@ -26,6 +26,9 @@ struct FwdArgs {
   uint32_t seed_lo, seed_hi;  // dropout: Philox key
   uint32_t keep_t;            // dropout: keep iff byte < keep_t
   float drop_scale;           // dropout: 256 / keep_t
+  // separate key lengths (launch_fwd_kvlen only): keys [B·Nk] or cu_seqlens_k
+  const int32_t* cu_seqlens_k = nullptr;
+  int Nk = 0;
 };
 
 // FP8 forward: q, k, v hold e4m3fn codes; scale_log2 already includes both
@@ -85,6 +88,11 @@ int fwd_query_tile();
 // not both)
 hipError_t launch_fwd(const FwdArgs& a, bool bf16_in, int d, int mask, bool varlen, bool softcap,
                       bool dropout, hipStream_t s);
+// Queries and keys of different lengths per sequence (a.N / a.cu_seqlens for the
+// queries, a.Nk / a.cu_seqlens_k for the keys), the queries being the last
+// positions: mask none or causal, no window, soft cap or dropout.
+hipError_t launch_fwd_kvlen(const FwdArgs& a, bool bf16_in, int d, bool causal, bool varlen,
+                            hipStream_t s);
 int fwd_fp8_query_tile();
 hipError_t launch_fwd_fp8(const Fp8FwdArgs& a, bool bf16_out, int d, bool causal, bool varlen,
                           hipStream_t s);

@@ -221,6 +221,29 @@ int fa_bwd_dropout_stage(int stage, const void* q, const void* k, const void* v,
                          void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * Forward with queries and keys of different lengths (chunked prefill: a block
+ * of new tokens attending to the cached ones and to itself; the pages' envelope
+ * lists seqlen_q != seqlen_k, FlashAttention-2 page, blog.gitcode.com, and the
+ * FAQ's head-dimension and length notes).
+ *   fixed length (both cu_seqlens NULL): q, o [B, Nq, Hq, d]; k, v [B, Nk, Hkv, d];
+ *     lse [Hq, B·Nq]
+ *   varlen (both non-NULL, int32 device arrays of B+1 entries): q, o [Tq, Hq, d]
+ *     with cu_seqlens_q, k, v [Tk, Hkv, d] with cu_seqlens_k; lse [Hq, Tq];
+ *     Nq bounds every query length (it sizes the grid) and Nk every key length
+ *   one NULL and one non-NULL cu_seqlens: FA_ERR_INVALID_ARG
+ * The Lq queries of a sequence with Lk keys are its last Lq positions: query i
+ * sits at position i + Lk − Lq and, when causal, sees keys j <= i + Lk − Lq
+ * (the alignment fa_fwd_kvcache uses; with Lq = Lk it is fa_fwd's causal mask).
+ * A query that sees no key (causal with Lq > Lk, or Lk = 0) gets O = 0 and
+ * LSE = −inf. d in {64, 128, 256}; mask none or causal; no window, soft cap or
+ * dropout. k and v may be NULL when Nk = 0. Other conventions as fa_fwd.
+ */
+int fa_fwd_kvlen(const void* q, const void* k, const void* v, void* o, float* lse,
+                 int B, int Hq, int Hkv, int Nq, int Nk, int d, float scale, int causal,
+                 const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int dtype,
+                 hipStream_t stream);
+
+/*
  * FP8 forward: the forward of fa_fwd on e4m3 inputs. The pages name e4m3
  * (torch.float8_e4m3fn) as the 8-bit attention format and credit
  * FlashAttention-3 with an FP8 forward (cxbdf.cn deployment guide, section

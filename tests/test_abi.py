@@ -29,7 +29,8 @@ def test_header_declares_the_boundary():
                                     "fa_fwd_kvcache", "fa_fwd_kvcache_fp8",
                                     "fa_fwd_kvcache_fp8_stage",
                                     "fa_fwd_kvcache_num_stages", "fa_fwd_kvcache_stage",
-                                    "fa_fwd_kvcache_workspace_size", "fa_fwd_softcap", "fa_fwd_window",
+                                    "fa_fwd_kvcache_workspace_size", "fa_fwd_kvlen",
+                                    "fa_fwd_softcap", "fa_fwd_window",
                                     "fa_kvcache_fp8_num_splits", "fa_kvcache_num_splits",
                                     "fa_status_string"]
 
@@ -193,6 +194,45 @@ def test_kvcache_stage_index_checked():
     # a valid stage still runs the host checks first
     assert fa.fa_fwd_kvcache_stage(0, P, P, P, P, P, P, 2, 4, 2, 1, 64, 96, 0.125, 1, 2,
                                    fa.FA_BF16, P, 1 << 20, None) == fa.FA_ERR_UNSUPPORTED
+
+
+def fkv(**kw):
+    a = dict(q=P, k=P, v=P, o=P, lse=P, B=2, Hq=4, Hkv=2, Nq=100, Nk=300, d=128, scale=0.125,
+             causal=1, cq=None, ck=None, dtype=fa.FA_BF16)
+    a.update(kw)
+    return fa.fa_fwd_kvlen(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["Hq"], a["Hkv"],
+                           a["Nq"], a["Nk"], a["d"], a["scale"], a["causal"], a["cq"], a["ck"],
+                           a["dtype"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(cq=P), fa.FA_ERR_INVALID_ARG),             # one cu_seqlens without the other
+    (dict(ck=P), fa.FA_ERR_INVALID_ARG),
+    (dict(Nk=-1), fa.FA_ERR_INVALID_ARG),
+    (dict(Nq=-1), fa.FA_ERR_INVALID_ARG),
+    (dict(causal=2), fa.FA_ERR_INVALID_ARG),
+    (dict(dtype=7), fa.FA_ERR_INVALID_ARG),
+    (dict(Hq=3), fa.FA_ERR_INVALID_ARG),
+    (dict(scale=float("nan")), fa.FA_ERR_INVALID_ARG),
+    (dict(d=96), fa.FA_ERR_UNSUPPORTED),
+    (dict(q=None), fa.FA_ERR_INVALID_ARG),
+    (dict(k=None), fa.FA_ERR_INVALID_ARG),           # keys to read but no pointer
+    (dict(v=P + 8), fa.FA_ERR_INVALID_ARG),
+    (dict(B=1 << 20, Nk=1 << 12), fa.FA_ERR_UNSUPPORTED),
+    (dict(B=0), fa.FA_OK),
+    (dict(Nq=0), fa.FA_OK),
+])
+def test_fwd_kvlen_host_checks(kw, status):
+    assert fkv(**kw) == status
+
+
+def test_fwd_kvlen_no_device_reports_hip_error():
+    torch = pytest.importorskip("torch")
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    assert fkv() == fa.FA_ERR_HIP
+    assert fkv(Nk=0, k=None, v=None) == fa.FA_ERR_HIP   # no key: k, v may be NULL
+    assert fkv(d=256, causal=0, cq=P, ck=P) == fa.FA_ERR_HIP
 
 
 def kvc8(stage=None, **kw):

@@ -307,6 +307,59 @@ DECODE_WORKLOADS: Dict[str, DecodeWorkload] = {
 }
 
 
+# ---------------------------------------------------------------------------
+# Forward with queries and keys of different lengths (chunked prefill): Nq new
+# tokens per batch entry attend to Nk keys, the new tokens being the last Nq
+# positions. Recipe: rng = numpy.random.default_rng(seed); q [B, Nq, Hq, d],
+# then k, v [B, Nk, Hkv, d], each rng.standard_normal(shape, dtype=float32);
+# the caller rounds to fp16 / bf16 (nearest even).
+@dataclasses.dataclass(frozen=True)
+class KvlenWorkload:
+    name: str
+    B: int
+    Hq: int
+    Hkv: int
+    Nq: int
+    Nk: int
+    d: int
+    dtype: str = "bf16"
+    causal: bool = True
+    seed: int = 0
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / math.sqrt(self.d)
+
+    def visible_pairs(self) -> int:
+        """(query, key) pairs that enter the result, per (entry, query head)."""
+        if not self.causal:
+            return self.Nq * self.Nk
+        off = self.Nk - self.Nq
+        return sum(max(0, min(self.Nk, i + off + 1)) for i in range(self.Nq))
+
+    def fwd_flop(self) -> float:
+        """4·d FLOP per visible (query, key) pair (the forward convention)."""
+        return 4.0 * self.d * self.B * self.Hq * self.visible_pairs()
+
+
+KVLEN_WORKLOADS: Dict[str, KvlenWorkload] = {
+    # a 2048-token chunk of new tokens over an 8192-key context (6144 cached + the
+    # chunk), Llama-3-8B heads
+    "prefill_chunk": KvlenWorkload("prefill_chunk", B=4, Hq=32, Hkv=8, Nq=2048, Nk=8192, d=128,
+                                   dtype="bf16", causal=True, seed=8),
+}
+
+
+def generate_kvlen(w: KvlenWorkload):
+    """float32 q [B, Nq, Hq, d] and k, v [B, Nk, Hkv, d]."""
+    rng = np.random.default_rng(w.seed)
+    return {
+        "q": rng.standard_normal((w.B, w.Nq, w.Hq, w.d), dtype=np.float32),
+        "k": rng.standard_normal((w.B, w.Nk, w.Hkv, w.d), dtype=np.float32),
+        "v": rng.standard_normal((w.B, w.Nk, w.Hkv, w.d), dtype=np.float32),
+    }
+
+
 def decode_custom(B, Hq, Hkv, Nq, Nk, d, dtype="bf16", causal=True, seed=0, lens="full",
                   kv_cache="same"):
     if isinstance(lens, list):
