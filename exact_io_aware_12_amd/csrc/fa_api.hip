@@ -53,7 +53,7 @@ int window_mode(int left, int right, int N, int* mask, int* wl, int* wr) {
 }
 
 // A soft cap c: 0 = none; otherwise finite and > 0, with scale / c finite, and
-// only with the unmasked or causal mask at d <= 128. Sets the kernels' two
+// only with the unmasked or causal mask (any supported head dimension). Sets the kernels' two
 // constants (scale / c and c·log2 e). Returns FA_OK or the status to report.
 int cap_constants(float softcap, float scale, int mask, int d, float* cap_in, float* cap_out) {
   *cap_in = *cap_out = 0.f;
@@ -62,7 +62,8 @@ int cap_constants(float softcap, float scale, int mask, int d, float* cap_in, fl
   *cap_in = scale / softcap;
   *cap_out = softcap * kLog2e;
   if (!std::isfinite(*cap_in) || !std::isfinite(*cap_out)) return FA_ERR_INVALID_ARG;
-  if (mask == fa::kMaskWindow || d > 128) return FA_ERR_UNSUPPORTED;
+  if (mask == fa::kMaskWindow) return FA_ERR_UNSUPPORTED;
+  (void)d;   // every supported head dimension, 256 included
   return FA_OK;
 }
 

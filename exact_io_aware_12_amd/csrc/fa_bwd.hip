@@ -454,15 +454,17 @@ __global__ __launch_bounds__(kDkvThreads, 1) void dkdv_kernel(BwdArgs a, int n_k
 // more GEMM on top of the four). Keys are MFMA columns, so P and dS come out
 // in the B-operand layout of the dV/dK products, whose Qᵀ, dOᵀ operands are
 // transposing LDS reads. Q/dO tiles of 64 queries are double-buffered in LDS
-// (128 KiB at d = 256). Plain masks only (none, causal), varlen, GQA.
+// (128 KiB at d = 256). Masks none or causal, varlen, GQA; CAP as in
+// dkdv_produce (soft-capped logits, dS times 1 − tanh²).
 constexpr int kWideKeys = 128;   // keys per workgroup (32 per wave)
 constexpr int kWideQ = 64;       // queries per tile
 
-template <typename T, int D, bool CAUSAL, bool EDGE, int PASS>
+template <typename T, int D, bool CAUSAL, bool EDGE, int PASS, bool CAP>
 __device__ __forceinline__ void dkdv_wide_tile(const T* qt_, const T* dot_, const float* ld,
                                                const u32x4 (&kf)[D / 16],
                                                const u32x4 (&vf)[D / 16], f32x16 (&acc)[D / 32],
-                                               float c, int q0, int L, int key, int lane) {
+                                               float c, int q0, int L, int key, int lane,
+                                               float cap_in, float cap_out) {
   constexpr int NKB = D / 16;
   constexpr int NCB = D / 32;
   const int col = lane & 31, half = lane >> 5;
@@ -485,8 +487,15 @@ __device__ __forceinline__ void dkdv_wide_tile(const T* qt_, const T* dot_, cons
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
         const int i4 = 4 * rr + t;
-        float p = fast_exp2(fmaf(s[i4], c, -lsev[t]));
-        float ds = p * (dp[i4] - dlv[t]);
+        float p, ds;
+        if constexpr (CAP) {
+          const float th = tanh_fast(s[i4] * cap_in);
+          p = fast_exp2(fmaf(th, cap_out, -lsev[t]));
+          ds = p * (dp[i4] - dlv[t]) * fmaf(-th, th, 1.f);
+        } else {
+          p = fast_exp2(fmaf(s[i4], c, -lsev[t]));
+          ds = p * (dp[i4] - dlv[t]);
+        }
         if constexpr (EDGE) {
           const int q = q0 + qoff + t;
           const bool keep = q < L && !(CAUSAL && key > q);
@@ -510,7 +519,7 @@ __device__ __forceinline__ void dkdv_wide_tile(const T* qt_, const T* dot_, cons
   }
 }
 
-template <typename T, int D, bool CAUSAL, bool VARLEN, int PASS>
+template <typename T, int D, bool CAUSAL, bool VARLEN, int PASS, bool CAP>
 __global__ __launch_bounds__(kThreads, 1) void dkdv_wide_kernel(BwdArgs a, int n_ktiles) {
   constexpr int NKB = D / 16;
   constexpr int NCB = D / 32;
@@ -583,7 +592,8 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_wide_kernel(BwdArgs a, int n
   f32x16 acc[NCB];   // dVᵀ (PASS 0) or dKᵀ (PASS 1)
 #pragma unroll
   for (int cb = 0; cb < NCB; ++cb) acc[cb] = f32x16{};
-  const float c = a.scale_log2;
+  const float c = CAP ? 1.f : a.scale_log2;   // capped logits are already in log2 units
+  const float cap_in = CAP ? a.cap_in : 0.f, cap_out = CAP ? a.cap_out : 0.f;
   const int wk_first = k0 + wave * 32;
 
   auto step = [&](auto edge_tag, int i) {
@@ -596,8 +606,8 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_wide_kernel(BwdArgs a, int n
     const int q0 = tile_of(i, r) * kWideQ;
     // a diagonal tile can lie entirely before this wave's keys
     if (EDGE && CAUSAL && q0 + kWideQ - 1 < wk_first) return;
-    dkdv_wide_tile<T, D, CAUSAL, EDGE, PASS>(q_lds[buf], do_lds[buf], ld_lds[buf], kf, vf, acc,
-                                             c, q0, L, key, lane);
+    dkdv_wide_tile<T, D, CAUSAL, EDGE, PASS, CAP>(q_lds[buf], do_lds[buf], ld_lds[buf], kf, vf,
+                                                  acc, c, q0, L, key, lane, cap_in, cap_out);
   };
   for (int i = 0; i < n_edge; ++i) step(std::true_type{}, i);
   for (int i = n_edge; i < ntile; ++i) step(std::false_type{}, i);
@@ -858,14 +868,14 @@ hipError_t launch(const BwdArgs& a, int stage, hipStream_t s) {
   }
   if (stage < 0 || stage == 1) {
     if constexpr (D == 256) {
-      static_assert(!WIN && !CAP && !DROP, "d = 256: plain masks only");
+      static_assert(!WIN && !DROP, "d = 256: masks none or causal, soft cap, no dropout");
       const int nkt = (a.N + kWideKeys - 1) / kWideKeys;
-      hipLaunchKernelGGL((dkdv_wide_kernel<T, D, CAUSAL, VARLEN, 0>), dim3(nkt * a.Hkv * a.B),
-                         dim3(kThreads), 0, s, a, nkt);
+      hipLaunchKernelGGL((dkdv_wide_kernel<T, D, CAUSAL, VARLEN, 0, CAP>),
+                         dim3(nkt * a.Hkv * a.B), dim3(kThreads), 0, s, a, nkt);
       const hipError_t e0 = hipGetLastError();
       if (e0 != hipSuccess) return e0;
-      hipLaunchKernelGGL((dkdv_wide_kernel<T, D, CAUSAL, VARLEN, 1>), dim3(nkt * a.Hkv * a.B),
-                         dim3(kThreads), 0, s, a, nkt);
+      hipLaunchKernelGGL((dkdv_wide_kernel<T, D, CAUSAL, VARLEN, 1, CAP>),
+                         dim3(nkt * a.Hkv * a.B), dim3(kThreads), 0, s, a, nkt);
     } else {
       const int nkt = (a.N + kDkvKeys - 1) / kDkvKeys;
       hipLaunchKernelGGL((dkdv_kernel<T, D, CAUSAL, VARLEN, WIN, CAP, DROP>),
@@ -915,9 +925,17 @@ hipError_t dispatch_mask(const BwdArgs& a, int mask, bool varlen, bool cap, bool
 
 int bwd_num_stages() { return 3; }
 
-// d = 256: unmasked or causal only (the caller rejects the rest)
+// d = 256: unmasked or causal, with or without a soft cap (the caller rejects the rest)
 template <typename T>
-hipError_t dispatch_256(const BwdArgs& a, int mask, bool varlen, int stage, hipStream_t s) {
+hipError_t dispatch_256(const BwdArgs& a, int mask, bool varlen, bool cap, int stage,
+                        hipStream_t s) {
+  if (cap) {
+    if (mask == kMaskCausal)
+      return varlen ? launch<T, 256, true, true, false, true>(a, stage, s)
+                    : launch<T, 256, true, false, false, true>(a, stage, s);
+    return varlen ? launch<T, 256, false, true, false, true>(a, stage, s)
+                  : launch<T, 256, false, false, false, true>(a, stage, s);
+  }
   if (mask == kMaskCausal)
     return varlen ? launch<T, 256, true, true, false>(a, stage, s)
                   : launch<T, 256, true, false, false>(a, stage, s);
@@ -927,8 +945,8 @@ hipError_t dispatch_256(const BwdArgs& a, int mask, bool varlen, int stage, hipS
 
 hipError_t launch_bwd(const BwdArgs& a, bool bf16_in, int d, int mask, bool varlen, bool cap,
                       bool drop, int stage, hipStream_t s) {
-  if (d == 256) return bf16_in ? dispatch_256<bf16>(a, mask, varlen, stage, s)
-                               : dispatch_256<f16>(a, mask, varlen, stage, s);
+  if (d == 256) return bf16_in ? dispatch_256<bf16>(a, mask, varlen, cap, stage, s)
+                               : dispatch_256<f16>(a, mask, varlen, cap, stage, s);
   if (bf16_in)
     return d == 64 ? dispatch_mask<bf16, 64>(a, mask, varlen, cap, drop, stage, s)
                    : dispatch_mask<bf16, 128>(a, mask, varlen, cap, drop, stage, s);

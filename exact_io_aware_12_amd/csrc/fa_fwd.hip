@@ -361,7 +361,8 @@ hipError_t dispatch_kvlen(const FwdArgs& a, bool causal, bool varlen, hipStream_
 template <typename T, int D>
 hipError_t dispatch_mask(const FwdArgs& a, int mask, bool varlen, bool cap, bool drop,
                          hipStream_t s) {
-  if constexpr (D <= 128) {   // soft cap or dropout: no window, d <= 128 (checked by the caller)
+  // soft cap or dropout: no window; dropout at d <= 128 (both checked by the caller)
+  if constexpr (D <= 128) {
     if (drop) {
       if (mask == kMaskCausal)
         return varlen ? launch<T, D, true, true, false, false, true>(a, s)
@@ -369,13 +370,13 @@ hipError_t dispatch_mask(const FwdArgs& a, int mask, bool varlen, bool cap, bool
       return varlen ? launch<T, D, false, true, false, false, true>(a, s)
                     : launch<T, D, false, false, false, false, true>(a, s);
     }
-    if (cap) {
-      if (mask == kMaskCausal)
-        return varlen ? launch<T, D, true, true, false, true>(a, s)
-                      : launch<T, D, true, false, false, true>(a, s);
-      return varlen ? launch<T, D, false, true, false, true>(a, s)
-                    : launch<T, D, false, false, false, true>(a, s);
-    }
+  }
+  if (cap) {
+    if (mask == kMaskCausal)
+      return varlen ? launch<T, D, true, true, false, true>(a, s)
+                    : launch<T, D, true, false, false, true>(a, s);
+    return varlen ? launch<T, D, false, true, false, true>(a, s)
+                  : launch<T, D, false, false, false, true>(a, s);
   }
   if (mask == kMaskWindow)
     return varlen ? launch<T, D, false, true, true>(a, s) : launch<T, D, false, false, true>(a, s);

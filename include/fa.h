@@ -166,8 +166,8 @@ int fa_bwd_window_stage(int stage, const void* q, const void* k, const void* v, 
  *   softcap : 0 = no cap (the plain kernels run, bit-identical results);
  *             otherwise finite and > 0, with scale / softcap finite
  *             (else FA_ERR_INVALID_ARG)
- * Causal or not, fixed length or varlen, GQA; d = 64 or 128 (d = 256 with a
- * cap: FA_ERR_UNSUPPORTED). lse is the log-sum-exp of the capped logits; the
+ * Causal or not, fixed length or varlen, GQA; d = 64, 128 or 256 (the head
+ * dimension of the soft-capped models). lse is the log-sum-exp of the capped logits; the
  * backward needs the lse of fa_fwd_softcap with the same cap. Everything else
  * (layouts, ownership, workspace, errors, determinism) as for fa_fwd / fa_bwd;
  * fa_bwd_softcap_stage runs one stage (or every stage with stage −1).

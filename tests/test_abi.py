@@ -431,7 +431,6 @@ def bwdc(stage=None, **kw):
     (dict(dtype=7), fa.FA_ERR_INVALID_ARG),
     (dict(q=None), fa.FA_ERR_INVALID_ARG),
     (dict(o=P + 2), fa.FA_ERR_INVALID_ARG),
-    (dict(d=256), fa.FA_ERR_UNSUPPORTED),               # the capped kernels stop at d = 128
     (dict(d=96), fa.FA_ERR_UNSUPPORTED),
     (dict(B=0), fa.FA_OK),
     (dict(N=0, cap=5.0), fa.FA_OK),
@@ -442,7 +441,7 @@ def test_fwd_softcap_host_checks(kw, status):
 
 @pytest.mark.parametrize("kw,status", [
     (dict(cap=-2.0), fa.FA_ERR_INVALID_ARG),
-    (dict(d=256), fa.FA_ERR_UNSUPPORTED),
+    (dict(d=96), fa.FA_ERR_UNSUPPORTED),
     (dict(ws=None), fa.FA_ERR_WORKSPACE),
     (dict(dq=P + 8), fa.FA_ERR_INVALID_ARG),
     (dict(causal=5), fa.FA_ERR_INVALID_ARG),
@@ -465,6 +464,8 @@ def test_softcap_no_device_reports_hip_error():
     assert fwdc() == fa.FA_ERR_HIP
     assert fwdc(cap=0.0) == fa.FA_ERR_HIP      # no cap: the plain kernels
     assert bwdc() == fa.FA_ERR_HIP
+    assert fwdc(d=256) == fa.FA_ERR_HIP        # soft cap at d = 256 (fwd and bwd)
+    assert bwdc(d=256) == fa.FA_ERR_HIP
 
 
 def fwdd(**kw):
@@ -543,7 +544,7 @@ def test_binding_dropout_needs_a_seed():
 
 
 def test_bwd_d256_reaches_the_launch():
-    """The plain backward accepts d = 256 (window, soft cap and dropout do not)."""
+    """The plain and soft-capped backward accept d = 256 (window and dropout do not)."""
     torch = pytest.importorskip("torch")
     assert fa.fa_bwd_workspace_size(1, 2, 2, 16, 256) == fa.fa_bwd_workspace_size(1, 2, 2, 16, 64)
     if torch.cuda.is_available():

@@ -2,7 +2,7 @@
 through the binding's softcap=) against the oracle's capped logits
 c·tanh(scale·q·k / c).
 
-Small shapes spanning several tiles with ragged ends, both masks, d 64/128,
+Small shapes spanning several tiles with ragged ends, both masks, d 64/128/256,
 fp16 and bf16, caps from 1.5 (most logits in the curved part of tanh) to 30,
 a large softmax scale that drives tanh into saturation, varlen with GQA and
 empty or one-token sequences; softcap = 0 must run the plain kernels bit for
@@ -52,7 +52,7 @@ def compare_fwd(w, cap, scale=None):
 
 
 @pytest.mark.parametrize("dtype", ["fp16", "bf16"])
-@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("d", [64, 128, 256])
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("cap", CAPS)
 def test_forward(dtype, d, causal, cap):
@@ -120,7 +120,7 @@ def compare_bwd(w, cap, scale=None):
 
 
 @pytest.mark.parametrize("dtype", ["fp16", "bf16"])
-@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("d", [64, 128, 256])
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("cap", CAPS)
 def test_backward(dtype, d, causal, cap):
@@ -137,6 +137,15 @@ def test_backward_varlen_gqa():
     w = W.custom(B=0, Hq=8, Hkv=2, N=0, d=128, dtype="bf16", causal=True, seed=926,
                  lens=[300, 0, 1, 129, 64, 513], backward=True)
     compare_bwd(w, 5.0)
+
+
+def test_d256_varlen_gqa():
+    """d = 256 with a cap of 50 (the Gemma-2 setting): varlen, GQA, ragged and empty
+    sequences, forward and backward."""
+    w = W.custom(B=0, Hq=8, Hkv=4, N=0, d=256, dtype="bf16", causal=True, seed=929,
+                 lens=[300, 0, 1, 200, 129], backward=True)
+    compare_fwd(w, 50.0)
+    compare_bwd(w, 50.0)
 
 
 def test_backward_long():

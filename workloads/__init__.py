@@ -145,6 +145,9 @@ def _build() -> Dict[str, Workload]:
     # head dim 256 forward and backward (the pages' envelope ends at 256)
     w["train_d256"] = Workload("train_d256", B=4, Hq=16, Hkv=16, N=4096, d=256, dtype="bf16",
                                causal=True, seed=12, backward=True)
+    # head dim 256 with logits capped at 50 and GQA 16/8 (the Gemma-2 attention setting)
+    w["softcap_d256"] = Workload("softcap_d256", B=4, Hq=16, Hkv=8, N=4096, d=256,
+                                 dtype="bf16", causal=True, seed=14, backward=True, softcap=50.0)
     # the training step's shape with dropout p = 0.1 on the softmax weights
     w["dropout_16k"] = Workload("dropout_16k", B=2, Hq=16, Hkv=16, N=16384, d=128,
                                 dtype="bf16", causal=True, seed=11, backward=True,
