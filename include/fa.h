@@ -36,14 +36,17 @@
  *   reaches d = 256, Flash Attention 是什麼, adersaytech.com, section
  *   硬體與版本需求). At d = 256 the backward computes dK and dV in two passes
  *   (dV, then dK) so that each pass's accumulators fit the register file.
- *   The window, soft-cap and dropout backward take d = 64 or 128 only.
+ *   The window and dropout backward take d = 64 or 128 only (the soft cap
+ *   reaches 256 in both directions).
  *
  * Alignment: every tensor pointer must be 16-byte aligned (FA_ERR_INVALID_ARG
  *   otherwise); rows are moved as 16-byte vectors.
  * Ownership: every pointer is device memory owned by the caller. The library
- * allocates nothing, keeps no pointer after returning, and holds no mutable
- * global state; calls on different streams may run concurrently. Outputs must
- * not alias inputs.
+ * allocates nothing and keeps no pointer after returning. Its only global
+ * state is a cache of the decode kernel's occupancy figures, filled on first
+ * use by whichever thread gets there (the values are the same for every
+ * caller); calls on different streams may run concurrently. Outputs must not
+ * alias inputs.
  *
  * Errors: arguments are checked on the host before anything is enqueued; on
  * a negative status nothing was enqueued. FA_ERR_UNSUPPORTED marks a valid
