@@ -269,7 +269,6 @@ int bwd_common(int stage, const void* q, const void* k, const void* v, const voi
   bool noop;
   int st = check_sizes(B, Hq, Hkv, N, d, scale, 0, dtype, &noop, 256);
   if (st != FA_OK) return st;
-  if (d == 256 && mask == fa::kMaskWindow) return FA_ERR_UNSUPPORTED;   // plain masks at 256
   float cap_in, cap_out;
   st = cap_constants(softcap, scale, mask, d, &cap_in, &cap_out);
   if (st != FA_OK) return st;

@@ -454,17 +454,18 @@ __global__ __launch_bounds__(kDkvThreads, 1) void dkdv_kernel(BwdArgs a, int n_k
 // more GEMM on top of the four). Keys are MFMA columns, so P and dS come out
 // in the B-operand layout of the dV/dK products, whose Qᵀ, dOᵀ operands are
 // transposing LDS reads. Q/dO tiles of 64 queries are double-buffered in LDS
-// (128 KiB at d = 256). Masks none or causal, varlen, GQA; CAP as in
-// dkdv_produce (soft-capped logits, dS times 1 − tanh²).
+// (128 KiB at d = 256). Masks none, causal or a sliding window (WIN, as in
+// fwd_kernel; CAUSAL is false then), varlen, GQA; CAP as in dkdv_produce
+// (soft-capped logits, dS times 1 − tanh²).
 constexpr int kWideKeys = 128;   // keys per workgroup (32 per wave)
 constexpr int kWideQ = 64;       // queries per tile
 
-template <typename T, int D, bool CAUSAL, bool EDGE, int PASS, bool CAP>
+template <typename T, int D, bool CAUSAL, bool EDGE, int PASS, bool CAP, bool WIN>
 __device__ __forceinline__ void dkdv_wide_tile(const T* qt_, const T* dot_, const float* ld,
                                                const u32x4 (&kf)[D / 16],
                                                const u32x4 (&vf)[D / 16], f32x16 (&acc)[D / 32],
                                                float c, int q0, int L, int key, int lane,
-                                               float cap_in, float cap_out) {
+                                               float cap_in, float cap_out, int wl, int wr) {
   constexpr int NKB = D / 16;
   constexpr int NCB = D / 32;
   const int col = lane & 31, half = lane >> 5;
@@ -498,7 +499,8 @@ __device__ __forceinline__ void dkdv_wide_tile(const T* qt_, const T* dot_, cons
         }
         if constexpr (EDGE) {
           const int q = q0 + qoff + t;
-          const bool keep = q < L && !(CAUSAL && key > q);
+          bool keep = q < L && !(CAUSAL && key > q);
+          if constexpr (WIN) keep = keep && q >= key - wr && q <= key + wl;
           p = keep ? p : 0.f;
           ds = keep ? ds : 0.f;
         }
@@ -519,7 +521,7 @@ __device__ __forceinline__ void dkdv_wide_tile(const T* qt_, const T* dot_, cons
   }
 }
 
-template <typename T, int D, bool CAUSAL, bool VARLEN, int PASS, bool CAP>
+template <typename T, int D, bool CAUSAL, bool VARLEN, int PASS, bool CAP, bool WIN>
 __global__ __launch_bounds__(kThreads, 1) void dkdv_wide_kernel(BwdArgs a, int n_ktiles) {
   constexpr int NKB = D / 16;
   constexpr int NCB = D / 32;
@@ -543,25 +545,45 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_wide_kernel(BwdArgs a, int n
 
   const int64_t qs = (int64_t)a.Hq * D, kvs = (int64_t)a.Hkv * D;
   const int key = k0 + wave * 32 + col;
-  // Query tiles of one head: [qt_begin, qt_end). Edge tiles (the causal
-  // diagonal below k0 + 128, a ragged last tile) of every head of the group
-  // come first, then the interior tiles, which need no mask.
-  const int qt_begin = CAUSAL ? k0 / kWideQ : 0;
-  const int qt_end = (L + kWideQ - 1) / kWideQ;
-  const int nq = qt_end - qt_begin;
-  const int nd = CAUSAL ? min(kWideKeys / kWideQ, nq) : 0;
-  const int ne = nd + ((L % kWideQ != 0 && nq > nd) ? 1 : 0);
-  const int ni = nq - ne;
+  // Query tiles of one head: [qt_begin, qt_end), of which [ia, ib) are
+  // interior (every query sees every key of the block: no mask). The front
+  // edge tiles (the causal diagonal below k0 + 128, a window's leading edge)
+  // and back edge tiles (a window's trailing edge, a ragged last tile) of every
+  // head of the group come first, then the interior tiles.
+  const int wl = WIN ? a.wl : 0, wr = WIN ? a.wr : 0;
+  int qt_begin, qt_end, ia, ib;
+  if constexpr (WIN) {
+    // query i sees key j iff j − wr <= i <= j + wl
+    const int lo = max(0, k0 - wr), hi = min(L, k0 + kWideKeys + wl);
+    qt_begin = lo / kWideQ;
+    qt_end = hi > lo ? (hi + kWideQ - 1) / kWideQ : qt_begin;
+    const int first = k0 + kWideKeys - 1 - wr;   // interior queries: [first, k0 + wl]
+    ia = max(qt_begin, first <= 0 ? 0 : (first + kWideQ - 1) / kWideQ);
+    const int last = k0 + wl - (kWideQ - 1);      // a tile starting here ends at k0 + wl
+    ib = min(min(last < 0 ? 0 : last / kWideQ + 1, L / kWideQ), qt_end);
+    if (ib < ia) ib = ia;
+    ia = min(ia, qt_end);
+    ib = min(max(ib, ia), qt_end);
+  } else {
+    qt_begin = CAUSAL ? k0 / kWideQ : 0;
+    qt_end = (L + kWideQ - 1) / kWideQ;
+    const int nq0 = qt_end - qt_begin;
+    const int nd = CAUSAL ? min(kWideKeys / kWideQ, nq0) : 0;
+    ia = qt_begin + nd;
+    ib = qt_end - ((L % kWideQ != 0 && nq0 > nd) ? 1 : 0);
+  }
+  const int nq = qt_end - qt_begin, nf = ia - qt_begin, ni = ib - ia;
+  const int ne = nq - ni;
   const int n_edge = a.group * ne, ntile = a.group * nq;
   auto tile_of = [&](int i, int& r) -> int {   // tile i -> (head r, query tile)
     if (i < n_edge) {
       r = i / ne;
       const int e = i - r * ne;
-      return e < nd ? qt_begin + e : qt_end - 1;
+      return e < nf ? qt_begin + e : ib + (e - nf);
     }
     const int j = i - n_edge;
     r = j / ni;
-    return qt_begin + nd + (j - r * ni);
+    return ia + (j - r * ni);
   };
   auto issue = [&](int i, int buf) {
     int r;
@@ -606,8 +628,11 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_wide_kernel(BwdArgs a, int n
     const int q0 = tile_of(i, r) * kWideQ;
     // a diagonal tile can lie entirely before this wave's keys
     if (EDGE && CAUSAL && q0 + kWideQ - 1 < wk_first) return;
-    dkdv_wide_tile<T, D, CAUSAL, EDGE, PASS, CAP>(q_lds[buf], do_lds[buf], ld_lds[buf], kf, vf,
-                                                  acc, c, q0, L, key, lane, cap_in, cap_out);
+    // or an edge tile of a window outside the windows of all this wave's keys
+    if (EDGE && WIN && (q0 + kWideQ - 1 < wk_first - wr || q0 > wk_first + 31 + wl)) return;
+    dkdv_wide_tile<T, D, CAUSAL, EDGE, PASS, CAP, WIN>(q_lds[buf], do_lds[buf], ld_lds[buf], kf,
+                                                       vf, acc, c, q0, L, key, lane, cap_in,
+                                                       cap_out, wl, wr);
   };
   for (int i = 0; i < n_edge; ++i) step(std::true_type{}, i);
   for (int i = n_edge; i < ntile; ++i) step(std::false_type{}, i);
@@ -868,13 +893,13 @@ hipError_t launch(const BwdArgs& a, int stage, hipStream_t s) {
   }
   if (stage < 0 || stage == 1) {
     if constexpr (D == 256) {
-      static_assert(!WIN && !DROP, "d = 256: masks none or causal, soft cap, no dropout");
+      static_assert(!DROP, "d = 256: no dropout");
       const int nkt = (a.N + kWideKeys - 1) / kWideKeys;
-      hipLaunchKernelGGL((dkdv_wide_kernel<T, D, CAUSAL, VARLEN, 0, CAP>),
+      hipLaunchKernelGGL((dkdv_wide_kernel<T, D, CAUSAL, VARLEN, 0, CAP, WIN>),
                          dim3(nkt * a.Hkv * a.B), dim3(kThreads), 0, s, a, nkt);
       const hipError_t e0 = hipGetLastError();
       if (e0 != hipSuccess) return e0;
-      hipLaunchKernelGGL((dkdv_wide_kernel<T, D, CAUSAL, VARLEN, 1, CAP>),
+      hipLaunchKernelGGL((dkdv_wide_kernel<T, D, CAUSAL, VARLEN, 1, CAP, WIN>),
                          dim3(nkt * a.Hkv * a.B), dim3(kThreads), 0, s, a, nkt);
     } else {
       const int nkt = (a.N + kDkvKeys - 1) / kDkvKeys;
@@ -925,7 +950,8 @@ hipError_t dispatch_mask(const BwdArgs& a, int mask, bool varlen, bool cap, bool
 
 int bwd_num_stages() { return 3; }
 
-// d = 256: unmasked or causal, with or without a soft cap (the caller rejects the rest)
+// d = 256: unmasked, causal or a window; a soft cap with the first two (the
+// caller rejects the rest)
 template <typename T>
 hipError_t dispatch_256(const BwdArgs& a, int mask, bool varlen, bool cap, int stage,
                         hipStream_t s) {
@@ -936,6 +962,9 @@ hipError_t dispatch_256(const BwdArgs& a, int mask, bool varlen, bool cap, int s
     return varlen ? launch<T, 256, false, true, false, true>(a, stage, s)
                   : launch<T, 256, false, false, false, true>(a, stage, s);
   }
+  if (mask == kMaskWindow)
+    return varlen ? launch<T, 256, false, true, true>(a, stage, s)
+                  : launch<T, 256, false, false, true>(a, stage, s);
   if (mask == kMaskCausal)
     return varlen ? launch<T, 256, true, true, false>(a, stage, s)
                   : launch<T, 256, true, false, false>(a, stage, s);

@@ -36,8 +36,8 @@
  *   reaches d = 256, Flash Attention 是什麼, adersaytech.com, section
  *   硬體與版本需求). At d = 256 the backward computes dK and dV in two passes
  *   (dV, then dK) so that each pass's accumulators fit the register file.
- *   The window and dropout backward take d = 64 or 128 only (the soft cap
- *   reaches 256 in both directions).
+ *   The window and the soft cap reach d = 256 in both directions; dropout
+ *   takes d = 64 or 128 only.
  *
  * Alignment: every tensor pointer must be 16-byte aligned (FA_ERR_INVALID_ARG
  *   otherwise); rows are moved as 16-byte vectors.

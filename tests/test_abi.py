@@ -340,7 +340,7 @@ def test_fwd_window_host_checks(kw, status):
 
 @pytest.mark.parametrize("kw,status", [
     (dict(wl=-3), fa.FA_ERR_INVALID_ARG),
-    (dict(d=256), fa.FA_ERR_UNSUPPORTED),        # at d = 256 the backward takes plain masks only
+    (dict(d=96), fa.FA_ERR_UNSUPPORTED),
     (dict(ws=None), fa.FA_ERR_WORKSPACE),
     (dict(dk=P + 8), fa.FA_ERR_INVALID_ARG),
     (dict(B=0), fa.FA_OK),
@@ -544,10 +544,11 @@ def test_binding_dropout_needs_a_seed():
 
 
 def test_bwd_d256_reaches_the_launch():
-    """The plain and soft-capped backward accept d = 256 (window and dropout do not)."""
+    """The plain, windowed and soft-capped backward accept d = 256 (dropout does not)."""
     torch = pytest.importorskip("torch")
     assert fa.fa_bwd_workspace_size(1, 2, 2, 16, 256) == fa.fa_bwd_workspace_size(1, 2, 2, 16, 64)
     if torch.cuda.is_available():
         pytest.skip("a GPU is present")
     assert bwd(d=256) == fa.FA_ERR_HIP
     assert bwd(d=256, causal=1) == fa.FA_ERR_HIP
+    assert bwdw(d=256) == fa.FA_ERR_HIP

@@ -132,7 +132,7 @@ def compare_bwd(w, window):
 
 
 @pytest.mark.parametrize("dtype", ["fp16", "bf16"])
-@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("d", [64, 128, 256])
 @pytest.mark.parametrize("window", WINDOWS)
 def test_backward(dtype, d, window):
     compare_bwd(W.custom(B=2, Hq=2, Hkv=1, N=333, d=d, dtype=dtype, causal=False,
@@ -143,6 +143,15 @@ def test_backward_varlen_gqa():
     w = W.custom(B=0, Hq=8, Hkv=2, N=0, d=128, dtype="bf16", causal=False, seed=720,
                  lens=[300, 0, 1, 129, 64, 513], backward=True)
     compare_bwd(w, (70, 10))
+
+
+@pytest.mark.parametrize("window", [(70, 10), (4095, 0), (130, 200)])
+def test_backward_d256_varlen_gqa(window):
+    """d = 256 (two-pass dK/dV): varlen with GQA, empty and one-token sequences,
+    windows narrower and wider than the 128-key block and a causal-style band."""
+    w = W.custom(B=0, Hq=8, Hkv=2, N=0, d=256, dtype="bf16", causal=False, seed=722,
+                 lens=[300, 0, 1, 129, 64, 513], backward=True)
+    compare_bwd(w, window)
 
 
 def test_backward_long():
