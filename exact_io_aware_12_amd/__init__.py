@@ -88,6 +88,13 @@ def _load():
     L.fa_bwd_window.restype = i
     L.fa_bwd_window_stage.argtypes = [i] + L.fa_bwd_window.argtypes
     L.fa_bwd_window_stage.restype = i
+    L.fa_fwd_window_softcap.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, i, i, f, vp, i, vp]
+    L.fa_fwd_window_softcap.restype = i
+    L.fa_bwd_window_softcap.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, i,
+                                        f, vp, i, vp, sz, vp]
+    L.fa_bwd_window_softcap.restype = i
+    L.fa_bwd_window_softcap_stage.argtypes = [i] + L.fa_bwd_window_softcap.argtypes
+    L.fa_bwd_window_softcap_stage.restype = i
     L.fa_fwd_softcap.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, i, f, vp, i, vp]
     L.fa_fwd_softcap.restype = i
     L.fa_bwd_softcap.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, f, vp, i,
@@ -355,7 +362,7 @@ def flash_attn_func(q, k, v, causal=False, softmax_scale=None, cu_seqlens=None, 
 
     window_size = (left, right): query i sees keys i − left .. i + right of its
     sequence (−1: unbounded); with causal the right side is 0.
-    softcap = c > 0: logits c·tanh(scale·q·k / c) (not combined with a window).
+    softcap = c > 0: logits c·tanh(scale·q·k / c) (with or without a window).
     dropout_p > 0: dropout on the softmax weights, decisions from the Philox
     stream of dropout_seed (required; pass the same pair to the backward)."""
     import torch
@@ -383,9 +390,14 @@ def flash_attn_func(q, k, v, causal=False, softmax_scale=None, cu_seqlens=None, 
         if st != FA_OK:
             raise FaError(st, "fa_fwd_dropout")
         return o, lse
+    if softcap and w is not None:
+        st = lib.fa_fwd_window_softcap(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                                       lse.data_ptr(), B, Hq, Hkv, N, d, float(scale), w[0], w[1],
+                                       float(softcap), cu, _dtype_code(q), _stream())
+        if st != FA_OK:
+            raise FaError(st, "fa_fwd_window_softcap")
+        return o, lse
     if softcap:
-        if w is not None:
-            raise NotImplementedError("softcap with a sliding window is not implemented")
         st = lib.fa_fwd_softcap(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
                                 lse.data_ptr(), B, Hq, Hkv, N, d, float(scale),
                                 int(bool(causal)), float(softcap), cu, _dtype_code(q), _stream())
@@ -515,9 +527,14 @@ def flash_attn_backward(dout, q, k, v, o, lse, causal=False, softmax_scale=None,
         if st != FA_OK:
             raise FaError(st, "fa_bwd_dropout")
         return dq, dk, dv
+    if softcap and w is not None:
+        st = lib.fa_bwd_window_softcap(*ptrs, B, Hq, Hkv, N, d, float(scale), w[0], w[1],
+                                       float(softcap), cu, _dtype_code(q), workspace.data_ptr(),
+                                       workspace.numel(), _stream())
+        if st != FA_OK:
+            raise FaError(st, "fa_bwd_window_softcap")
+        return dq, dk, dv
     if softcap:
-        if w is not None:
-            raise NotImplementedError("softcap with a sliding window is not implemented")
         st = lib.fa_bwd_softcap(*ptrs, B, Hq, Hkv, N, d, float(scale), int(bool(causal)),
                                 float(softcap), cu, _dtype_code(q), workspace.data_ptr(),
                                 workspace.numel(), _stream())

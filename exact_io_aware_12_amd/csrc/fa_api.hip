@@ -52,8 +52,8 @@ int window_mode(int left, int right, int N, int* mask, int* wl, int* wr) {
   return FA_OK;
 }
 
-// A soft cap c: 0 = none; otherwise finite and > 0, with scale / c finite, and
-// only with the unmasked or causal mask (any supported head dimension). Sets the kernels' two
+// A soft cap c: 0 = none; otherwise finite and > 0, with scale / c finite
+// (any mask, any supported head dimension). Sets the kernels' two
 // constants (scale / c and c·log2 e). Returns FA_OK or the status to report.
 int cap_constants(float softcap, float scale, int mask, int d, float* cap_in, float* cap_out) {
   *cap_in = *cap_out = 0.f;
@@ -62,8 +62,8 @@ int cap_constants(float softcap, float scale, int mask, int d, float* cap_in, fl
   *cap_in = scale / softcap;
   *cap_out = softcap * kLog2e;
   if (!std::isfinite(*cap_in) || !std::isfinite(*cap_out)) return FA_ERR_INVALID_ARG;
-  if (mask == fa::kMaskWindow) return FA_ERR_UNSUPPORTED;
-  (void)d;   // every supported head dimension, 256 included
+  (void)mask;   // every mask, a window included
+  (void)d;      // every supported head dimension, 256 included
   return FA_OK;
 }
 
@@ -198,6 +198,17 @@ int fa_fwd_dropout(const void* q, const void* k, const void* v, void* o, float* 
   return fwd_common(q, k, v, o, lse, B, Hq, Hkv, N, d, scale,
                     causal ? fa::kMaskCausal : fa::kMaskNone, 0, 0, cu_seqlens, dtype, stream, 0.f,
                     dropout_p, seed);
+}
+
+int fa_fwd_window_softcap(const void* q, const void* k, const void* v, void* o, float* lse,
+                          int B, int Hq, int Hkv, int N, int d, float scale, int window_left,
+                          int window_right, float softcap, const int32_t* cu_seqlens, int dtype,
+                          hipStream_t stream) {
+  int mask, wl, wr;
+  const int st = window_mode(window_left, window_right, N, &mask, &wl, &wr);
+  if (st != FA_OK) return st;
+  return fwd_common(q, k, v, o, lse, B, Hq, Hkv, N, d, scale, mask, wl, wr, cu_seqlens, dtype,
+                    stream, softcap);
 }
 
 int fa_fwd_window(const void* q, const void* k, const void* v, void* o, float* lse, int B,
@@ -348,6 +359,30 @@ int fa_bwd_window_stage(int stage, const void* q, const void* k, const void* v, 
   if (st != FA_OK) return st;
   return bwd_common(stage, q, k, v, o, dout, lse, dq, dk, dv, B, Hq, Hkv, N, d, scale, mask, wl,
                     wr, cu_seqlens, dtype, workspace, workspace_bytes, stream);
+}
+
+int fa_bwd_window_softcap_stage(int stage, const void* q, const void* k, const void* v,
+                                const void* o, const void* dout, const float* lse, void* dq,
+                                void* dk, void* dv, int B, int Hq, int Hkv, int N, int d,
+                                float scale, int window_left, int window_right, float softcap,
+                                const int32_t* cu_seqlens, int dtype, void* workspace,
+                                size_t workspace_bytes, hipStream_t stream) {
+  if (stage < -1 || stage >= fa::bwd_num_stages()) return FA_ERR_INVALID_ARG;
+  int mask, wl, wr;
+  const int st = window_mode(window_left, window_right, N, &mask, &wl, &wr);
+  if (st != FA_OK) return st;
+  return bwd_common(stage, q, k, v, o, dout, lse, dq, dk, dv, B, Hq, Hkv, N, d, scale, mask, wl,
+                    wr, cu_seqlens, dtype, workspace, workspace_bytes, stream, softcap);
+}
+
+int fa_bwd_window_softcap(const void* q, const void* k, const void* v, const void* o,
+                          const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                          int B, int Hq, int Hkv, int N, int d, float scale, int window_left,
+                          int window_right, float softcap, const int32_t* cu_seqlens, int dtype,
+                          void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  return fa_bwd_window_softcap_stage(-1, q, k, v, o, dout, lse, dq, dk, dv, B, Hq, Hkv, N, d,
+                                     scale, window_left, window_right, softcap, cu_seqlens, dtype,
+                                     workspace, workspace_bytes, stream);
 }
 
 int fa_bwd_softcap(const void* q, const void* k, const void* v, const void* o, const void* dout,

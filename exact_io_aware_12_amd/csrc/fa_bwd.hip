@@ -929,7 +929,10 @@ hipError_t dispatch_mask(const BwdArgs& a, int mask, bool varlen, bool cap, bool
     return varlen ? launch<T, D, false, true, false, false, true>(a, stage, s)
                   : launch<T, D, false, false, false, false, true>(a, stage, s);
   }
-  if (cap) {   // soft cap: no window (checked by the caller)
+  if (cap) {
+    if (mask == kMaskWindow)
+      return varlen ? launch<T, D, false, true, true, true>(a, stage, s)
+                    : launch<T, D, false, false, true, true>(a, stage, s);
     if (mask == kMaskCausal)
       return varlen ? launch<T, D, true, true, false, true>(a, stage, s)
                     : launch<T, D, true, false, false, true>(a, stage, s);
@@ -950,12 +953,15 @@ hipError_t dispatch_mask(const BwdArgs& a, int mask, bool varlen, bool cap, bool
 
 int bwd_num_stages() { return 3; }
 
-// d = 256: unmasked, causal or a window; a soft cap with the first two (the
-// caller rejects the rest)
+// d = 256: unmasked, causal or a window, each with or without a soft cap (the
+// caller rejects dropout)
 template <typename T>
 hipError_t dispatch_256(const BwdArgs& a, int mask, bool varlen, bool cap, int stage,
                         hipStream_t s) {
   if (cap) {
+    if (mask == kMaskWindow)
+      return varlen ? launch<T, 256, false, true, true, true>(a, stage, s)
+                    : launch<T, 256, false, false, true, true>(a, stage, s);
     if (mask == kMaskCausal)
       return varlen ? launch<T, 256, true, true, false, true>(a, stage, s)
                     : launch<T, 256, true, false, false, true>(a, stage, s);

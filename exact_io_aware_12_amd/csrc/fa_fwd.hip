@@ -361,7 +361,7 @@ hipError_t dispatch_kvlen(const FwdArgs& a, bool causal, bool varlen, hipStream_
 template <typename T, int D>
 hipError_t dispatch_mask(const FwdArgs& a, int mask, bool varlen, bool cap, bool drop,
                          hipStream_t s) {
-  // soft cap or dropout: no window; dropout at d <= 128 (both checked by the caller)
+  // dropout: no window, d <= 128; soft cap: any mask (checked by the caller)
   if constexpr (D <= 128) {
     if (drop) {
       if (mask == kMaskCausal)
@@ -372,6 +372,9 @@ hipError_t dispatch_mask(const FwdArgs& a, int mask, bool varlen, bool cap, bool
     }
   }
   if (cap) {
+    if (mask == kMaskWindow)
+      return varlen ? launch<T, D, false, true, true, true>(a, s)
+                    : launch<T, D, false, false, true, true>(a, s);
     if (mask == kMaskCausal)
       return varlen ? launch<T, D, true, true, false, true>(a, s)
                     : launch<T, D, true, false, false, true>(a, s);

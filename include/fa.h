@@ -190,6 +190,31 @@ int fa_bwd_softcap_stage(int stage, const void* q, const void* k, const void* v,
                          void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * A sliding window and a soft cap together (the local-attention layers of
+ * soft-capped models): fa_fwd_window / fa_bwd_window with every visible logit
+ * replaced by softcap·tanh(scale·q·k / softcap), as fa_fwd_softcap does.
+ * Arguments as fa_fwd_window / fa_bwd_window(_stage) plus `softcap` after
+ * window_right; the checks of both apply (softcap = 0 runs the window kernels).
+ * d = 64, 128 or 256.
+ */
+int fa_fwd_window_softcap(const void* q, const void* k, const void* v, void* o, float* lse,
+                          int B, int Hq, int Hkv, int N, int d, float scale, int window_left,
+                          int window_right, float softcap, const int32_t* cu_seqlens, int dtype,
+                          hipStream_t stream);
+int fa_bwd_window_softcap(const void* q, const void* k, const void* v, const void* o,
+                          const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                          int B, int Hq, int Hkv, int N, int d, float scale, int window_left,
+                          int window_right, float softcap, const int32_t* cu_seqlens, int dtype,
+                          void* workspace, size_t workspace_bytes, hipStream_t stream);
+int fa_bwd_window_softcap_stage(int stage, const void* q, const void* k, const void* v,
+                                const void* o, const void* dout, const float* lse, void* dq,
+                                void* dk, void* dv, int B, int Hq, int Hkv, int N, int d,
+                                float scale, int window_left, int window_right, float softcap,
+                                const int32_t* cu_seqlens, int dtype, void* workspace,
+                                size_t workspace_bytes, hipStream_t stream);
+
+
+/*
  * Dropout on the softmax weights: the forward and backward of fa_fwd / fa_bwd
  * with O = (P ∘ Z) V, where Z is 256/t for a kept weight and 0 for a dropped
  * one. The FlashAttention-2 page (blog.gitcode.com, API example) shows a

@@ -23,14 +23,15 @@ def test_header_declares_the_boundary():
     assert declared_functions() == ["fa_bwd", "fa_bwd_dropout", "fa_bwd_dropout_stage",
                                     "fa_bwd_num_stages", "fa_bwd_softcap",
                                     "fa_bwd_softcap_stage", "fa_bwd_stage",
-                                    "fa_bwd_window", "fa_bwd_window_stage",
+                                    "fa_bwd_window", "fa_bwd_window_softcap",
+                                    "fa_bwd_window_softcap_stage", "fa_bwd_window_stage",
                                     "fa_bwd_workspace_size", "fa_fwd", "fa_fwd_dropout",
                                     "fa_fwd_fp8",
                                     "fa_fwd_kvcache", "fa_fwd_kvcache_fp8",
                                     "fa_fwd_kvcache_fp8_stage",
                                     "fa_fwd_kvcache_num_stages", "fa_fwd_kvcache_stage",
                                     "fa_fwd_kvcache_workspace_size", "fa_fwd_kvlen",
-                                    "fa_fwd_softcap", "fa_fwd_window",
+                                    "fa_fwd_softcap", "fa_fwd_window", "fa_fwd_window_softcap",
                                     "fa_kvcache_fp8_num_splits", "fa_kvcache_num_splits",
                                     "fa_status_string"]
 
@@ -466,6 +467,61 @@ def test_softcap_no_device_reports_hip_error():
     assert bwdc() == fa.FA_ERR_HIP
     assert fwdc(d=256) == fa.FA_ERR_HIP        # soft cap at d = 256 (fwd and bwd)
     assert bwdc(d=256) == fa.FA_ERR_HIP
+
+
+def fwdwc(**kw):
+    a = dict(q=P, k=P, v=P, o=P, lse=P, B=1, Hq=2, Hkv=2, N=16, d=64, scale=0.125, wl=3, wr=0,
+             cap=20.0, cu=None, dtype=fa.FA_BF16, stream=None)
+    a.update(kw)
+    return fa.lib.fa_fwd_window_softcap(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["Hq"],
+                                        a["Hkv"], a["N"], a["d"], a["scale"], a["wl"], a["wr"],
+                                        a["cap"], a["cu"], a["dtype"], a["stream"])
+
+
+def bwdwc(stage=None, **kw):
+    a = dict(B=1, Hq=2, Hkv=2, N=16, d=64, scale=0.125, wl=3, wr=2, cap=20.0, dtype=fa.FA_BF16,
+             ws=P, wsb=1 << 20)
+    a.update(kw)
+    ptrs = [kw.get(n, P) for n in ("q", "k", "v", "o", "do", "lse", "dq", "dk", "dv")]
+    args = (*ptrs, a["B"], a["Hq"], a["Hkv"], a["N"], a["d"], a["scale"], a["wl"], a["wr"],
+            a["cap"], None, a["dtype"], a["ws"], a["wsb"], None)
+    if stage is None:
+        return fa.lib.fa_bwd_window_softcap(*args)
+    return fa.lib.fa_bwd_window_softcap_stage(stage, *args)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(cap=-1.0), fa.FA_ERR_INVALID_ARG),
+    (dict(cap=float("nan")), fa.FA_ERR_INVALID_ARG),
+    (dict(wl=-2), fa.FA_ERR_INVALID_ARG),
+    (dict(d=96), fa.FA_ERR_UNSUPPORTED),
+    (dict(q=None), fa.FA_ERR_INVALID_ARG),
+    (dict(B=0), fa.FA_OK),
+])
+def test_fwd_window_softcap_host_checks(kw, status):
+    assert fwdwc(**kw) == status
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(cap=0.0, wr=-5), fa.FA_ERR_INVALID_ARG),
+    (dict(cap=-3.0), fa.FA_ERR_INVALID_ARG),
+    (dict(ws=None), fa.FA_ERR_WORKSPACE),
+    (dict(B=0), fa.FA_OK),
+])
+def test_bwd_window_softcap_host_checks(kw, status):
+    assert bwdwc(**kw) == status
+
+
+def test_window_softcap_stage_and_no_device():
+    for bad in (-2, 3):
+        assert bwdwc(stage=bad) == fa.FA_ERR_INVALID_ARG
+    torch = pytest.importorskip("torch")
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    assert fwdwc() == fa.FA_ERR_HIP
+    assert fwdwc(d=256) == fa.FA_ERR_HIP
+    assert bwdwc() == fa.FA_ERR_HIP
+    assert bwdwc(d=256, stage=1) == fa.FA_ERR_HIP
 
 
 def fwdd(**kw):

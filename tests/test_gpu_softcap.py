@@ -33,19 +33,21 @@ def _views(w, t):
             t["v"].view(*shp, w.Hkv, w.d), {})
 
 
-def compare_fwd(w, cap, scale=None):
+def compare_fwd(w, cap, scale=None, window=None):
     import torch
     fa = _fa()
     scale = w.scale if scale is None else scale
+    win = {} if window is None else {"window_size": window}
     t = to_device(W.generate(w, with_grad=False), w.dtype)
     say(f"[fa_fwd_softcap] cap={cap} scale={scale:.4g} B={w.B} Hq={w.Hq} Hkv={w.Hkv} N={w.N} "
         f"d={w.d} {w.dtype} causal={w.causal} varlen={w.varlen}")
     q, k, v, kw = _views(w, t)
-    o, lse = fa.flash_attn_func(q, k, v, causal=w.causal, softmax_scale=scale, softcap=cap, **kw)
+    o, lse = fa.flash_attn_func(q, k, v, causal=w.causal, softmax_scale=scale, softcap=cap,
+                                **win, **kw)
     torch.cuda.synchronize()
     cu = t["cu_seqlens"].cpu().numpy()
     o_ref, lse_ref = attention_fwd(host64(t["q"]), host64(t["k"]), host64(t["v"]), scale,
-                                   w.causal, cu, softcap=cap)
+                                   w.causal, cu, softcap=cap, window=window)
     e, _, _ = check_o(host64(o.reshape(w.T, w.Hq, w.d)), o_ref, w.dtype)
     el = check_lse(host64(lse), lse_ref)
     say(f"   max|dO|={e:.2e} max|dLSE|={el:.2e}")
@@ -97,22 +99,24 @@ def test_zero_cap_runs_the_plain_kernels(causal):
 
 
 # ---- backward -----------------------------------------------------------------
-def compare_bwd(w, cap, scale=None):
+def compare_bwd(w, cap, scale=None, window=None):
     import torch
     fa = _fa()
     scale = w.scale if scale is None else scale
+    win = {} if window is None else {"window_size": window}
     t = to_device(W.generate(w, with_grad=True), w.dtype)
     say(f"[fa_bwd_softcap] cap={cap} scale={scale:.4g} B={w.B} Hq={w.Hq} Hkv={w.Hkv} N={w.N} "
         f"d={w.d} {w.dtype} causal={w.causal} varlen={w.varlen}")
     q, k, v, kw = _views(w, t)
     do = t["do"].view(q.shape)
-    o, lse = fa.flash_attn_func(q, k, v, causal=w.causal, softmax_scale=scale, softcap=cap, **kw)
+    o, lse = fa.flash_attn_func(q, k, v, causal=w.causal, softmax_scale=scale, softcap=cap,
+                                **win, **kw)
     dq, dk, dv = fa.flash_attn_backward(do, q, k, v, o, lse, causal=w.causal, softmax_scale=scale,
-                                        softcap=cap, **kw)
+                                        softcap=cap, **win, **kw)
     torch.cuda.synchronize()
     cu = t["cu_seqlens"].cpu().numpy()
     ref = attention_bwd(host64(t["q"]), host64(t["k"]), host64(t["v"]), host64(t["do"]), scale,
-                        w.causal, cu, softcap=cap)
+                        w.causal, cu, softcap=cap, window=window)
     T = w.T
     got = (dq.reshape(T, w.Hq, w.d), dk.reshape(T, w.Hkv, w.d), dv.reshape(T, w.Hkv, w.d))
     res = [check_grad(host64(g), r, n) for g, r, n in zip(got, ref, ("dQ", "dK", "dV"))]
@@ -168,3 +172,24 @@ def test_softcap_deterministic():
         outs.append((o, lse) + tuple(grads))
     torch.cuda.synchronize()
     assert all(bits_equal(a, b) for a, b in zip(*outs))
+
+
+@pytest.mark.parametrize("dtype", ["fp16", "bf16"])
+@pytest.mark.parametrize("d", [64, 128, 256])
+@pytest.mark.parametrize("window", [(40, 0), (63, 65), (-1, 37)])
+def test_window_and_cap(dtype, d, window):
+    """A sliding window and a soft cap together (fa_fwd_window_softcap and
+    fa_bwd_window_softcap through the binding): forward and backward."""
+    w = W.custom(B=2, Hq=2, Hkv=1, N=333, d=d, dtype=dtype, causal=False, seed=940 + d,
+                 backward=True)
+    compare_fwd(w, 5.0, window=window)
+    compare_bwd(w, 5.0, window=window)
+
+
+def test_window_and_cap_varlen_gqa_d256():
+    """Gemma-2's local layers: window (4095, 0), cap 50, d = 256, varlen GQA."""
+    w = W.custom(B=0, Hq=8, Hkv=4, N=0, d=256, dtype="bf16", causal=False, seed=945,
+                 lens=[300, 0, 1, 200, 129], backward=True)
+    compare_fwd(w, 50.0, window=(100, 0))
+    compare_bwd(w, 50.0, window=(100, 0))
+
