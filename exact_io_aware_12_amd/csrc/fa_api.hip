@@ -68,8 +68,8 @@ int cap_constants(float softcap, float scale, int mask, int d, float* cap_in, fl
 }
 
 // Dropout probability p: 0 = none; otherwise 0 < p < 1 with keep threshold
-// t = floor(256·(1 − p) + 1/2) >= 1, only with the unmasked or causal mask at
-// d <= 128. Returns FA_OK or the status to report.
+// t = floor(256·(1 − p) + 1/2) >= 1, only with the unmasked or causal mask
+// (any supported head dimension). Returns FA_OK or the status to report.
 int drop_constants(float p, int mask, int d, uint32_t* t) {
   *t = 256;
   if (p == 0.f) return FA_OK;
@@ -77,7 +77,8 @@ int drop_constants(float p, int mask, int d, uint32_t* t) {
   const double x = std::floor(256.0 * (1.0 - (double)p) + 0.5);
   if (x < 1.0) return FA_ERR_INVALID_ARG;
   *t = (uint32_t)std::min(x, 256.0);
-  if (mask == fa::kMaskWindow || d > 128) return FA_ERR_UNSUPPORTED;
+  (void)d;   // every supported head dimension, 256 included
+  if (mask == fa::kMaskWindow) return FA_ERR_UNSUPPORTED;
   return FA_OK;
 }
 

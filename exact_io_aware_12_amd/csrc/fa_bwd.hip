@@ -455,17 +455,19 @@ __global__ __launch_bounds__(kDkvThreads, 1) void dkdv_kernel(BwdArgs a, int n_k
 // in the B-operand layout of the dV/dK products, whose Qᵀ, dOᵀ operands are
 // transposing LDS reads. Q/dO tiles of 64 queries are double-buffered in LDS
 // (128 KiB at d = 256). Masks none, causal or a sliding window (WIN, as in
-// fwd_kernel; CAUSAL is false then), varlen, GQA; CAP as in dkdv_produce
-// (soft-capped logits, dS times 1 − tanh²).
+// fwd_kernel; CAUSAL is false then), varlen, GQA; CAP and DROP as in
+// dkdv_produce (soft-capped logits, dS times 1 − tanh²; dropout: dV takes
+// P∘Z, dS = P∘(Z∘dP − D)).
 constexpr int kWideKeys = 128;   // keys per workgroup (32 per wave)
 constexpr int kWideQ = 64;       // queries per tile
 
-template <typename T, int D, bool CAUSAL, bool EDGE, int PASS, bool CAP, bool WIN>
+template <typename T, int D, bool CAUSAL, bool EDGE, int PASS, bool CAP, bool WIN, bool DROP>
 __device__ __forceinline__ void dkdv_wide_tile(const T* qt_, const T* dot_, const float* ld,
                                                const u32x4 (&kf)[D / 16],
                                                const u32x4 (&vf)[D / 16], f32x16 (&acc)[D / 32],
                                                float c, int q0, int L, int key, int lane,
-                                               float cap_in, float cap_out, int wl, int wr) {
+                                               float cap_in, float cap_out, int wl, int wr,
+                                               const DropKey& dk, int seq, int head, float zs) {
   constexpr int NKB = D / 16;
   constexpr int NCB = D / 32;
   const int col = lane & 31, half = lane >> 5;
@@ -485,6 +487,8 @@ __device__ __forceinline__ void dkdv_wide_tile(const T* qt_, const T* dot_, cons
       const float4 dv4 = *reinterpret_cast<const float4*>(ld + kWideQ + qoff);
       const float lsev[4] = {lv.x, lv.y, lv.z, lv.w};
       const float dlv[4] = {dv4.x, dv4.y, dv4.z, dv4.w};
+      uint32_t dbytes = 0;   // dropout: queries q0 + qoff + 0..3 of this lane's key
+      if constexpr (DROP) dbytes = drop_col_bytes(dk, seq, head, q0 + qoff, key);
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
         const int i4 = 4 * rr + t;
@@ -493,6 +497,11 @@ __device__ __forceinline__ void dkdv_wide_tile(const T* qt_, const T* dot_, cons
           const float th = tanh_fast(s[i4] * cap_in);
           p = fast_exp2(fmaf(th, cap_out, -lsev[t]));
           ds = p * (dp[i4] - dlv[t]) * fmaf(-th, th, 1.f);
+        } else if constexpr (DROP) {
+          p = fast_exp2(fmaf(s[i4], c, -lsev[t]));
+          const float z = drop_keep(dbytes, t, dk.t) ? zs : 0.f;
+          ds = p * fmaf(dp[i4], z, -dlv[t]);
+          p *= z;
         } else {
           p = fast_exp2(fmaf(s[i4], c, -lsev[t]));
           ds = p * (dp[i4] - dlv[t]);
@@ -521,7 +530,7 @@ __device__ __forceinline__ void dkdv_wide_tile(const T* qt_, const T* dot_, cons
   }
 }
 
-template <typename T, int D, bool CAUSAL, bool VARLEN, int PASS, bool CAP, bool WIN>
+template <typename T, int D, bool CAUSAL, bool VARLEN, int PASS, bool CAP, bool WIN, bool DROP>
 __global__ __launch_bounds__(kThreads, 1) void dkdv_wide_kernel(BwdArgs a, int n_ktiles) {
   constexpr int NKB = D / 16;
   constexpr int NCB = D / 32;
@@ -616,6 +625,7 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_wide_kernel(BwdArgs a, int n
   for (int cb = 0; cb < NCB; ++cb) acc[cb] = f32x16{};
   const float c = CAP ? 1.f : a.scale_log2;   // capped logits are already in log2 units
   const float cap_in = CAP ? a.cap_in : 0.f, cap_out = CAP ? a.cap_out : 0.f;
+  const DropKey dk{a.seed_lo, a.seed_hi, a.keep_t};
   const int wk_first = k0 + wave * 32;
 
   auto step = [&](auto edge_tag, int i) {
@@ -630,9 +640,9 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_wide_kernel(BwdArgs a, int n
     if (EDGE && CAUSAL && q0 + kWideQ - 1 < wk_first) return;
     // or an edge tile of a window outside the windows of all this wave's keys
     if (EDGE && WIN && (q0 + kWideQ - 1 < wk_first - wr || q0 > wk_first + 31 + wl)) return;
-    dkdv_wide_tile<T, D, CAUSAL, EDGE, PASS, CAP, WIN>(q_lds[buf], do_lds[buf], ld_lds[buf], kf,
-                                                       vf, acc, c, q0, L, key, lane, cap_in,
-                                                       cap_out, wl, wr);
+    dkdv_wide_tile<T, D, CAUSAL, EDGE, PASS, CAP, WIN, DROP>(
+        q_lds[buf], do_lds[buf], ld_lds[buf], kf, vf, acc, c, q0, L, key, lane, cap_in, cap_out,
+        wl, wr, dk, b, g * a.group + r, a.drop_scale);
   };
   for (int i = 0; i < n_edge; ++i) step(std::true_type{}, i);
   for (int i = n_edge; i < ntile; ++i) step(std::false_type{}, i);
@@ -893,13 +903,12 @@ hipError_t launch(const BwdArgs& a, int stage, hipStream_t s) {
   }
   if (stage < 0 || stage == 1) {
     if constexpr (D == 256) {
-      static_assert(!DROP, "d = 256: no dropout");
       const int nkt = (a.N + kWideKeys - 1) / kWideKeys;
-      hipLaunchKernelGGL((dkdv_wide_kernel<T, D, CAUSAL, VARLEN, 0, CAP, WIN>),
+      hipLaunchKernelGGL((dkdv_wide_kernel<T, D, CAUSAL, VARLEN, 0, CAP, WIN, DROP>),
                          dim3(nkt * a.Hkv * a.B), dim3(kThreads), 0, s, a, nkt);
       const hipError_t e0 = hipGetLastError();
       if (e0 != hipSuccess) return e0;
-      hipLaunchKernelGGL((dkdv_wide_kernel<T, D, CAUSAL, VARLEN, 1, CAP, WIN>),
+      hipLaunchKernelGGL((dkdv_wide_kernel<T, D, CAUSAL, VARLEN, 1, CAP, WIN, DROP>),
                          dim3(nkt * a.Hkv * a.B), dim3(kThreads), 0, s, a, nkt);
     } else {
       const int nkt = (a.N + kDkvKeys - 1) / kDkvKeys;
@@ -953,11 +962,18 @@ hipError_t dispatch_mask(const BwdArgs& a, int mask, bool varlen, bool cap, bool
 
 int bwd_num_stages() { return 3; }
 
-// d = 256: unmasked, causal or a window, each with or without a soft cap (the
-// caller rejects dropout)
+// d = 256: unmasked, causal or a window, each with or without a soft cap;
+// dropout with the first two (the caller rejects the rest)
 template <typename T>
-hipError_t dispatch_256(const BwdArgs& a, int mask, bool varlen, bool cap, int stage,
+hipError_t dispatch_256(const BwdArgs& a, int mask, bool varlen, bool cap, bool drop, int stage,
                         hipStream_t s) {
+  if (drop) {
+    if (mask == kMaskCausal)
+      return varlen ? launch<T, 256, true, true, false, false, true>(a, stage, s)
+                    : launch<T, 256, true, false, false, false, true>(a, stage, s);
+    return varlen ? launch<T, 256, false, true, false, false, true>(a, stage, s)
+                  : launch<T, 256, false, false, false, false, true>(a, stage, s);
+  }
   if (cap) {
     if (mask == kMaskWindow)
       return varlen ? launch<T, 256, false, true, true, true>(a, stage, s)
@@ -980,8 +996,8 @@ hipError_t dispatch_256(const BwdArgs& a, int mask, bool varlen, bool cap, int s
 
 hipError_t launch_bwd(const BwdArgs& a, bool bf16_in, int d, int mask, bool varlen, bool cap,
                       bool drop, int stage, hipStream_t s) {
-  if (d == 256) return bf16_in ? dispatch_256<bf16>(a, mask, varlen, cap, stage, s)
-                               : dispatch_256<f16>(a, mask, varlen, cap, stage, s);
+  if (d == 256) return bf16_in ? dispatch_256<bf16>(a, mask, varlen, cap, drop, stage, s)
+                               : dispatch_256<f16>(a, mask, varlen, cap, drop, stage, s);
   if (bf16_in)
     return d == 64 ? dispatch_mask<bf16, 64>(a, mask, varlen, cap, drop, stage, s)
                    : dispatch_mask<bf16, 128>(a, mask, varlen, cap, drop, stage, s);

@@ -361,15 +361,13 @@ hipError_t dispatch_kvlen(const FwdArgs& a, bool causal, bool varlen, hipStream_
 template <typename T, int D>
 hipError_t dispatch_mask(const FwdArgs& a, int mask, bool varlen, bool cap, bool drop,
                          hipStream_t s) {
-  // dropout: no window, d <= 128; soft cap: any mask (checked by the caller)
-  if constexpr (D <= 128) {
-    if (drop) {
-      if (mask == kMaskCausal)
-        return varlen ? launch<T, D, true, true, false, false, true>(a, s)
-                      : launch<T, D, true, false, false, false, true>(a, s);
-      return varlen ? launch<T, D, false, true, false, false, true>(a, s)
-                    : launch<T, D, false, false, false, false, true>(a, s);
-    }
+  // dropout: no window; soft cap: any mask (checked by the caller)
+  if (drop) {
+    if (mask == kMaskCausal)
+      return varlen ? launch<T, D, true, true, false, false, true>(a, s)
+                    : launch<T, D, true, false, false, false, true>(a, s);
+    return varlen ? launch<T, D, false, true, false, false, true>(a, s)
+                  : launch<T, D, false, false, false, false, true>(a, s);
   }
   if (cap) {
     if (mask == kMaskWindow)

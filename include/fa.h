@@ -36,8 +36,7 @@
  *   reaches d = 256, Flash Attention 是什麼, adersaytech.com, section
  *   硬體與版本需求). At d = 256 the backward computes dK and dV in two passes
  *   (dV, then dK) so that each pass's accumulators fit the register file.
- *   The window and the soft cap reach d = 256 in both directions; dropout
- *   takes d = 64 or 128 only.
+ *   The window, the soft cap and dropout reach d = 256 in both directions.
  *
  * Alignment: every tensor pointer must be 16-byte aligned (FA_ERR_INVALID_ARG
  *   otherwise); rows are moved as 16-byte vectors.
@@ -229,8 +228,8 @@ int fa_bwd_window_softcap_stage(int stage, const void* q, const void* k, const v
  * and dropout_p (it regenerates the decisions; nothing is stored).
  *   dropout_p : 0 = none (the plain kernels run, bit-identical results);
  *               otherwise 0 < dropout_p < 1 with t >= 1 (else FA_ERR_INVALID_ARG)
- * Causal or not, fixed length or varlen, GQA; d = 64 or 128 (d = 256:
- * FA_ERR_UNSUPPORTED). Everything else as for fa_fwd / fa_bwd;
+ * Causal or not, fixed length or varlen, GQA; d = 64, 128 or 256. Everything
+ * else as for fa_fwd / fa_bwd;
  * fa_bwd_dropout_stage runs one stage (or every stage with stage −1).
  */
 int fa_fwd_dropout(const void* q, const void* k, const void* v, void* o, float* lse,

@@ -553,7 +553,7 @@ def bwdd(stage=None, **kw):
     (dict(causal=2), fa.FA_ERR_INVALID_ARG),
     (dict(v=None), fa.FA_ERR_INVALID_ARG),
     (dict(lse=P + 4), fa.FA_ERR_INVALID_ARG),
-    (dict(d=256), fa.FA_ERR_UNSUPPORTED),
+    (dict(d=96), fa.FA_ERR_UNSUPPORTED),
     (dict(B=0), fa.FA_OK),
     (dict(N=0, p=0.5), fa.FA_OK),
 ])
@@ -563,7 +563,7 @@ def test_fwd_dropout_host_checks(kw, status):
 
 @pytest.mark.parametrize("kw,status", [
     (dict(p=1.5), fa.FA_ERR_INVALID_ARG),
-    (dict(d=256), fa.FA_ERR_UNSUPPORTED),
+    (dict(d=96), fa.FA_ERR_UNSUPPORTED),
     (dict(ws=None), fa.FA_ERR_WORKSPACE),
     (dict(dv=P + 8), fa.FA_ERR_INVALID_ARG),
     (dict(B=0), fa.FA_OK),
@@ -600,7 +600,7 @@ def test_binding_dropout_needs_a_seed():
 
 
 def test_bwd_d256_reaches_the_launch():
-    """The plain, windowed and soft-capped backward accept d = 256 (dropout does not)."""
+    """The plain, windowed, soft-capped and dropout backward accept d = 256."""
     torch = pytest.importorskip("torch")
     assert fa.fa_bwd_workspace_size(1, 2, 2, 16, 256) == fa.fa_bwd_workspace_size(1, 2, 2, 16, 64)
     if torch.cuda.is_available():

@@ -133,7 +133,7 @@ def compare(w, p, seed, backward=True):
 
 
 @pytest.mark.parametrize("dtype", ["fp16", "bf16"])
-@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("d", [64, 128, 256])
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("p", [0.1, 0.5])
 def test_dropout_parity(dtype, d, causal, p):
@@ -151,6 +151,13 @@ def test_dropout_varlen_gqa():
     w = W.custom(B=0, Hq=8, Hkv=2, N=0, d=128, dtype="bf16", causal=True, seed=965,
                  lens=[300, 0, 1, 129, 64, 513], backward=True)
     compare(w, 0.15, 2 ** 64 - 1)
+
+
+def test_dropout_varlen_gqa_d256():
+    """d = 256 (the two-pass dK/dV kernel draws the same decisions in both passes)."""
+    w = W.custom(B=0, Hq=8, Hkv=4, N=0, d=256, dtype="bf16", causal=True, seed=967,
+                 lens=[300, 0, 1, 200, 129], backward=True)
+    compare(w, 0.2, 0xDEADBEEF)
 
 
 def test_dropout_long():
