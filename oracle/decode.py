@@ -20,6 +20,12 @@ Visibility: every valid key j < L_b, or keys j ≤ p_i when causal. A query
 that sees no key (L_b = 0, or causal with p_i < 0) has the empty sum: O_i = 0
 and LSE_i = −∞.
 
+Options, as in the full-sequence oracle (oracle.attention): a sliding window
+of `window_left` keys behind the query (keys j ≥ p_i − window_left stay
+visible; the sliding-window reading of the FlashAttention-2 page,
+blog.gitcode.com, local attention) and a soft cap c (S_ij → c·tanh(S_ij / c),
+the same page's section 2.3 in the bounded reading).
+
 Layouts: q [B, Nq, Hq, d], k/v [B, Nk, Hkv, d] with Nk ≥ max L_b;
 returns o [B, Nq, Hq, d] and lse [Hq, B·Nq] (query (b, i) at column b·Nq + i).
 """
@@ -34,7 +40,7 @@ def _f64(x) -> np.ndarray:
     return np.asarray(x, dtype=np.float64)
 
 
-def kvcache_head(Qs, Ks, Vs, scale: float, causal: bool):
+def kvcache_head(Qs, Ks, Vs, scale: float, causal: bool, window_left=None, softcap=None):
     """One (batch entry, query head): Qs [Nq, d], Ks/Vs [L, d] (valid keys only).
 
     Returns O [Nq, dv] and LSE [Nq].
@@ -46,9 +52,13 @@ def kvcache_head(Qs, Ks, Vs, scale: float, causal: bool):
     if L == 0:
         return O, lse
     S = scale * (Qs @ Ks.T)                                  # [Nq, L]
+    if softcap:
+        S = softcap * np.tanh(S / softcap)
+    pos = L - Nq + np.arange(Nq)                              # query positions
     if causal:
-        pos = L - Nq + np.arange(Nq)                          # query positions
         S = np.where(np.arange(L)[None, :] <= pos[:, None], S, -np.inf)
+    if window_left is not None and window_left >= 0:
+        S = np.where(np.arange(L)[None, :] >= pos[:, None] - window_left, S, -np.inf)
     seen = np.isfinite(S).any(axis=1)
     if not seen.any():
         return O, lse
@@ -60,7 +70,8 @@ def kvcache_head(Qs, Ks, Vs, scale: float, causal: bool):
     return O, lse
 
 
-def kvcache_fwd(q, k_cache, v_cache, cache_seqlens, scale: float, causal: bool = False):
+def kvcache_fwd(q, k_cache, v_cache, cache_seqlens, scale: float, causal: bool = False,
+                window_left=None, softcap=None):
     """Whole-tensor decode attention; see the module docstring for layouts."""
     q, k, v = _f64(q), _f64(k_cache), _f64(v_cache)
     lens = [int(x) for x in np.asarray(_f64(cache_seqlens))]
@@ -74,7 +85,8 @@ def kvcache_fwd(q, k_cache, v_cache, cache_seqlens, scale: float, causal: bool =
     for b in range(B):
         L = lens[b]
         for h in range(Hq):
-            O, l = kvcache_head(q[b, :, h], k[b, :L, h // g], v[b, :L, h // g], scale, causal)
+            O, l = kvcache_head(q[b, :, h], k[b, :L, h // g], v[b, :L, h // g], scale, causal,
+                                window_left, softcap)
             o[b, :, h] = O
             lse[h, b * Nq:(b + 1) * Nq] = l
     return o, lse

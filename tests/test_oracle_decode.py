@@ -87,6 +87,38 @@ def test_queries_are_the_whole_sequence(causal):
     np.testing.assert_allclose(lse, lf, atol=1e-12)
 
 
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("wl,cap", [(3, None), (None, 2.0), (2, 1.5), (0, 4.0)])
+def test_window_and_cap_queries_are_the_whole_sequence(causal, wl, cap):
+    """Nq = L with a left window and/or a soft cap: the full-sequence oracle with
+    window (wl, unbounded right) and the same cap, both pinned separately."""
+    rng = np.random.default_rng(11)
+    B, L, Hq, Hkv, d = 2, 9, 4, 2, 8
+    q, k, v = _cache(rng, B, L, L, Hq, Hkv, d)
+    o, lse = kvcache_fwd(q, k, v, [L] * B, 0.5, causal, window_left=wl, softcap=cap)
+    cu = np.arange(B + 1) * L
+    win = None if wl is None else (wl, -1)
+    of, lf = attention_fwd(q.reshape(B * L, Hq, d), k.reshape(B * L, Hkv, d),
+                           v.reshape(B * L, Hkv, d), 0.5, causal, cu, window=win, softcap=cap)
+    np.testing.assert_allclose(o.reshape(B * L, Hq, d), of, atol=1e-12)
+    np.testing.assert_allclose(lse, lf, atol=1e-12)
+
+
+def test_zero_window_sees_only_itself():
+    """window_left = 0, causal: each query sees only the key at its own position, so
+    O is that key's V row and the LSE is its (capped) logit, c·tanh(s / c)."""
+    rng = np.random.default_rng(12)
+    B, Nq, L, H, d, c = 1, 3, 7, 2, 4, 1.5
+    q, k, v = _cache(rng, B, Nq, L, H, H, d)
+    o, lse = kvcache_fwd(q, k, v, [L], 0.7, True, window_left=0, softcap=c)
+    for h in range(H):
+        for i in range(Nq):
+            p = L - Nq + i
+            np.testing.assert_allclose(o[0, i, h], v[0, p, h], atol=1e-12)
+            s = 0.7 * float(q[0, i, h] @ k[0, p, h])
+            assert abs(lse[h, i] - c * math.tanh(s / c)) < 1e-12
+
+
 def test_single_query_causal_equals_full():
     """With one new query every valid key is at or before it."""
     rng = np.random.default_rng(8)
