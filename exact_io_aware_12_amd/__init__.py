@@ -41,7 +41,7 @@ __all__ = ["FA_OK", "FA_ERR_INVALID_ARG", "FA_ERR_UNSUPPORTED", "FA_ERR_HIP", "F
            "fa_kvcache_num_splits", "fa_fwd_kvcache_workspace_size", "flash_attn_with_kvcache",
            "fa_fwd_kvcache_stage", "fa_fwd_kvcache_num_stages", "fa_fwd_kvcache_fp8",
            "fa_fwd_kvcache_fp8_stage", "fa_kvcache_fp8_num_splits",
-           "fa_fwd_kvlen", "flash_attn_kvlen_func"]
+           "fa_fwd_kvlen", "flash_attn_kvlen_func", "fa_fwd_kvcache_local"]
 
 FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_HIP, FA_ERR_WORKSPACE = 0, -1, -2, -3, -4
 FA_FP16, FA_BF16 = 0, 1
@@ -118,6 +118,9 @@ def _load():
     L.fa_fwd_kvcache.restype = i
     L.fa_fwd_kvcache_stage.argtypes = [i] + L.fa_fwd_kvcache.argtypes
     L.fa_fwd_kvcache_stage.restype = i
+    L.fa_fwd_kvcache_local.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, i, f, i, i,
+                                       vp, sz, vp]
+    L.fa_fwd_kvcache_local.restype = i
     L.fa_fwd_kvcache_fp8.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, f, f, i, i, vp,
                                      sz, vp]
     L.fa_fwd_kvcache_fp8.restype = i
@@ -272,6 +275,14 @@ def fa_fwd_kvcache_fp8(q, k_cache, v_cache, cache_seqlens, o, lse, B, Hq, Hkv, N
     return lib.fa_fwd_kvcache_fp8(q, k_cache, v_cache, cache_seqlens, o, lse, B, Hq, Hkv, Nq, Nk,
                                   d, scale, causal, descale_k, descale_v, num_splits, dtype,
                                   workspace, workspace_bytes, stream)
+
+
+def fa_fwd_kvcache_local(q, k_cache, v_cache, cache_seqlens, o, lse, B, Hq, Hkv, Nq, Nk, d, scale,
+                         causal, window_left, softcap, num_splits, dtype, workspace,
+                         workspace_bytes, stream) -> int:
+    return lib.fa_fwd_kvcache_local(q, k_cache, v_cache, cache_seqlens, o, lse, B, Hq, Hkv, Nq,
+                                    Nk, d, scale, causal, window_left, softcap, num_splits, dtype,
+                                    workspace, workspace_bytes, stream)
 
 
 def fa_fwd_kvcache_fp8_stage(stage, q, k_cache, v_cache, cache_seqlens, o, lse, B, Hq, Hkv, Nq,
@@ -554,7 +565,8 @@ def flash_attn_backward(dout, q, k, v, o, lse, causal=False, softmax_scale=None,
 
 
 def flash_attn_with_kvcache(q, k_cache, v_cache, cache_seqlens, causal=False, softmax_scale=None,
-                            num_splits=0, workspace=None, descale_k=1.0, descale_v=1.0):
+                            num_splits=0, workspace=None, descale_k=1.0, descale_v=1.0,
+                            window_left=-1, softcap=0.0):
     """Decode over a key/value cache. Returns (o, lse); lse is float32 [Hq, B·Nq].
 
     q [B, Nq, Hq, d]; k_cache, v_cache [B, Nk, Hkv, d]; cache_seqlens int32 [B]
@@ -562,6 +574,8 @@ def flash_attn_with_kvcache(q, k_cache, v_cache, cache_seqlens, causal=False, so
     each sequence (see fa_fwd_kvcache in include/fa.h). Caches of dtype
     float8_e4m3fn (or uint8 codes) take the FP8 path, fa_fwd_kvcache_fp8, with
     cached value = code × descale_k (K) or × descale_v (V); o has q's dtype.
+    window_left >= 0 (keys at most that far behind each query) or softcap > 0
+    take fa_fwd_kvcache_local (16-bit caches).
     """
     import torch
     if q.dim() != 4 or k_cache.dim() != 4 or v_cache.shape != k_cache.shape:
@@ -589,6 +603,16 @@ def flash_attn_with_kvcache(q, k_cache, v_cache, cache_seqlens, causal=False, so
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
     ptrs = (q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), cache_seqlens.data_ptr(),
             o.data_ptr(), lse.data_ptr())
+    if window_left != -1 or softcap:
+        if kv8:
+            raise NotImplementedError("a window or soft cap over an fp8 cache is not implemented")
+        st = lib.fa_fwd_kvcache_local(*ptrs, B, Hq, Hkv, Nq, Nk, d, float(scale),
+                                      int(bool(causal)), int(window_left), float(softcap),
+                                      int(num_splits), _dtype_code(q), workspace.data_ptr(),
+                                      workspace.numel(), _stream())
+        if st != FA_OK:
+            raise FaError(st, "fa_fwd_kvcache_local")
+        return o, lse
     if kv8:
         st = lib.fa_fwd_kvcache_fp8(*ptrs, B, Hq, Hkv, Nq, Nk, d, float(scale), int(bool(causal)),
                                     float(descale_k), float(descale_v), int(num_splits),

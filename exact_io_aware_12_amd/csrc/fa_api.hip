@@ -623,6 +623,67 @@ int fa_fwd_kvcache_stage(int stage, const void* q, const void* k_cache, const vo
                         scale, causal, num_splits, dtype, workspace, workspace_bytes, stream);
 }
 
+int fa_fwd_kvcache_local(const void* q, const void* k_cache, const void* v_cache,
+                         const int32_t* cache_seqlens, void* o, float* lse, int B, int Hq,
+                         int Hkv, int Nq, int Nk, int d, float scale, int causal,
+                         int window_left, float softcap, int num_splits, int dtype,
+                         void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  bool noop;
+  int st = check_kvcache(B, Hq, Hkv, Nq, Nk, d, scale, causal, num_splits, dtype, &noop);
+  if (st != FA_OK) return st;
+  if (window_left < -1) return FA_ERR_INVALID_ARG;
+  float cap_in = 0.f, cap_out = 0.f;
+  if (softcap != 0.f) {
+    if (!std::isfinite(softcap) || !(softcap > 0.f)) return FA_ERR_INVALID_ARG;
+    cap_in = scale / softcap;
+    cap_out = softcap * kLog2e;
+    if (!std::isfinite(cap_in) || !std::isfinite(cap_out)) return FA_ERR_INVALID_ARG;
+  }
+  if (noop) return FA_OK;
+  if (!q || !k_cache || !v_cache || !cache_seqlens || !o || !lse) return FA_ERR_INVALID_ARG;
+  const void* ptrs[] = {q, k_cache, v_cache, o, lse, workspace};
+  for (const void* p : ptrs)
+    if (p && !aligned16(p)) return FA_ERR_INVALID_ARG;
+  if ((reinterpret_cast<uintptr_t>(cache_seqlens) & 3u) != 0) return FA_ERR_INVALID_ARG;
+  // the keys any query of an entry can see: the last Nq + window_left positions
+  const int wl = window_left < 0 ? Nk : std::min(window_left, Nk);
+  const int span = (int)std::min<int64_t>(Nk, (int64_t)Nq + wl);
+  const int sp = num_splits > 0 ? num_splits : kv_splits(B, Hq, Hkv, Nq, span, d, false);
+  if (!workspace || workspace_bytes < fa_fwd_kvcache_workspace_size(B, Hq, Hkv, Nq, Nk, d, sp))
+    return FA_ERR_WORKSPACE;
+  fa::DecodeArgs a;
+  a.q = q;
+  a.k = k_cache;
+  a.v = v_cache;
+  a.seqlens = cache_seqlens;
+  a.o = o;
+  a.lse = lse;
+  const size_t units = (size_t)B * Hq * Nq;
+  a.part_o = static_cast<float*>(workspace);
+  a.part_lse = a.part_o + (size_t)sp * units * d;
+  a.B = B;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.Nq = Nq;
+  a.Nk = Nk;
+  a.group = Hq / Hkv;
+  a.rows = a.group * Nq;
+  a.n_rb = (a.rows + 31) / 32;
+  a.splits = sp;
+  const int tk = fa::decode_tile_keys();
+  const int per = (std::max(span, 1) + sp - 1) / sp;
+  a.chunk = std::max(tk, (per + tk - 1) / tk * tk);
+  a.scale_log2 = softcap != 0.f ? 1.f : scale * kLog2e;   // capped logits are in log2 units
+  a.o_scale = 1.f;
+  a.wl = wl;
+  a.cap_on = softcap != 0.f;
+  a.cap_in = cap_in;
+  a.cap_out = cap_out;
+  if ((int64_t)a.n_rb * sp * Hkv * B >= (int64_t)1 << 31) return FA_ERR_UNSUPPORTED;
+  hipError_t e = fa::launch_decode_ext(a, dtype == FA_BF16, d, causal != 0, -1, stream);
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
 int fa_fwd_kvcache_fp8(const void* q, const void* k_cache, const void* v_cache,
                        const int32_t* cache_seqlens, void* o, float* lse, int B, int Hq, int Hkv,
                        int Nq, int Nk, int d, float scale, int causal, float descale_k,

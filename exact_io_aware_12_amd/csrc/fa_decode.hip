@@ -145,7 +145,10 @@ struct CacheElem<T, true> {
   using type = uint8_t;
 };
 
-template <typename T, int D, bool CAUSAL, bool KV8>
+// EXT: a sliding window of a.wl keys behind each query (keys j >= p − wl stay
+// visible; the key ranges then start at the entry's floor L − Nq − wl) and,
+// when a.cap_on, soft-capped logits a.cap_out·tanh(z·a.cap_in) (scale_log2 = 1).
+template <typename T, int D, bool CAUSAL, bool KV8, bool EXT = false>
 __global__ __launch_bounds__(64) void decode_kernel(DecodeArgs a) {
   using C = typename CacheElem<T, KV8>::type;   // cache element: T or an e4m3 code
   constexpr int NKB = D / 16;
@@ -165,7 +168,9 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeArgs a) {
   const int g = idx % a.Hkv, b = idx / a.Hkv;
 
   const int L = min(max(a.seqlens[b], 0), a.Nk);   // valid cache positions
-  const int k_begin = sp * a.chunk;
+  // keys before the window of the entry's first query are never visible
+  const int k_floor = EXT ? max(0, L - a.Nq - a.wl) : 0;
+  const int k_begin = k_floor + sp * a.chunk;
   const int k_end = min(L, k_begin + a.chunk);
 
   // this lane's row: query head g·group + hg, query i
@@ -241,12 +246,20 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeArgs a) {
           s = mfma32<T>(lds_row16<T, D>(kt, krow, 2 * kb + half), qf[kb], s);
       }
 
+      if constexpr (EXT) {
+        if (a.cap_on) {   // uniform
+#pragma unroll
+          for (int i = 0; i < 16; ++i) s[i] = a.cap_out * tanh_fast(s[i] * a.cap_in);
+        }
+      }
       // mask keys past the range and, causally, keys after the query
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const int rho = 8 * (i >> 2) + 4 * half + (i & 3);   // accumulator row of s[i]
         const int kj = kbase + (KV8 ? kv8_key(rho) : rho);
-        s[i] = (kj < k_end && !(CAUSAL && kj > qpos)) ? s[i] : -INFINITY;
+        bool vis = kj < k_end && !(CAUSAL && kj > qpos);
+        if constexpr (EXT) vis = vis && kj >= qpos - a.wl;
+        s[i] = vis ? s[i] : -INFINITY;
       }
       float mx = s[0];
 #pragma unroll
@@ -367,12 +380,13 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeArgs a) {
         wsum > 0.f ? m + logf(wsum) : -INFINITY;
 }
 
-template <typename T, int D, bool CAUSAL, bool KV8>
+template <typename T, int D, bool CAUSAL, bool KV8, bool EXT = false>
 hipError_t launch(const DecodeArgs& a, int stage, hipStream_t s) {
   (void)hipGetLastError();  // drop an error left pending by earlier, unrelated HIP calls
   if (stage < 0 || stage == 0) {
     const int64_t g1 = (int64_t)a.n_rb * a.splits * a.Hkv * a.B;
-    hipLaunchKernelGGL((decode_kernel<T, D, CAUSAL, KV8>), dim3((unsigned)g1), dim3(64), 0, s, a);
+    hipLaunchKernelGGL((decode_kernel<T, D, CAUSAL, KV8, EXT>), dim3((unsigned)g1), dim3(64), 0,
+                       s, a);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -429,6 +443,24 @@ int decode_resident_per_cu(bool bf16_in, int d, bool causal, bool kv8) {
 }
 
 int decode_lds_bytes(int d, bool kv8) { return kStages * 2 * kTK * d * (kv8 ? 1 : 2); }
+
+template <typename T>
+static hipError_t dispatch_ext(const DecodeArgs& a, int d, bool causal, int stage, hipStream_t s) {
+  if (d == 64)
+    return causal ? launch<T, 64, true, false, true>(a, stage, s)
+                  : launch<T, 64, false, false, true>(a, stage, s);
+  if (d == 128)
+    return causal ? launch<T, 128, true, false, true>(a, stage, s)
+                  : launch<T, 128, false, false, true>(a, stage, s);
+  return causal ? launch<T, 256, true, false, true>(a, stage, s)
+                : launch<T, 256, false, false, true>(a, stage, s);
+}
+
+hipError_t launch_decode_ext(const DecodeArgs& a, bool bf16_in, int d, bool causal, int stage,
+                             hipStream_t s) {
+  return bf16_in ? dispatch_ext<bf16>(a, d, causal, stage, s)
+                 : dispatch_ext<f16>(a, d, causal, stage, s);
+}
 
 hipError_t launch_decode(const DecodeArgs& a, bool bf16_in, int d, bool causal, bool kv8,
                          int stage, hipStream_t s) {

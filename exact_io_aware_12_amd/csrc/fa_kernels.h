@@ -80,6 +80,10 @@ struct DecodeArgs {
   int chunk;                  // keys per range, a multiple of the key tile
   float scale_log2;           // scale · log2(e) (· descale of K for an e4m3 cache)
   float o_scale;              // O factor: 1, or the descale of V for an e4m3 cache
+  // launch_decode_ext only: window of wl keys behind each query, soft cap
+  int wl = 0;
+  int cap_on = 0;
+  float cap_in = 0.f, cap_out = 0.f;   // scale / c and c·log2 e (scale_log2 = 1 then)
 };
 
 int fwd_query_tile();
@@ -109,6 +113,9 @@ int decode_num_stages();
 // from the runtime's occupancy calculation; 0 when no device is available.
 int decode_resident_per_cu(bool bf16_in, int d, bool causal, bool kv8);
 int decode_lds_bytes(int d, bool kv8);   // LDS per decode_kernel workgroup
+// 16-bit caches with a sliding window (a.wl) and/or a soft cap (a.cap_on)
+hipError_t launch_decode_ext(const DecodeArgs& a, bool bf16_in, int d, bool causal, int stage,
+                             hipStream_t s);
 hipError_t launch_decode(const DecodeArgs& a, bool bf16_in, int d, bool causal, bool kv8,
                          int stage, hipStream_t s);
 

@@ -339,6 +339,27 @@ int fa_fwd_kvcache_stage(int stage, const void* q, const void* k_cache, const vo
                          hipStream_t stream);
 
 /*
+ * Decode with a sliding window and/or a soft cap (the local layers and capped
+ * logits of models such as Gemma-2; window: the FlashAttention-2 page,
+ * blog.gitcode.com, local attention; cap: its section 2.3, bounded reading):
+ * fa_fwd_kvcache with
+ *   window_left : −1 = none; otherwise query i of entry b (at position
+ *                 p = L_b − Nq + i) sees only keys j >= p − window_left (with
+ *                 causal also j <= p); < −1 is FA_ERR_INVALID_ARG
+ *   softcap     : 0 = none; otherwise logits softcap·tanh(scale·q·k / softcap),
+ *                 finite and > 0 with scale / softcap finite (else INVALID_ARG)
+ * The key ranges split only the last Nq + window_left positions of each entry,
+ * which are all any of its queries can see. 16-bit caches only; the workspace
+ * is that of fa_fwd_kvcache (fa_fwd_kvcache_workspace_size suffices with
+ * num_splits = 0). Other conventions as fa_fwd_kvcache.
+ */
+int fa_fwd_kvcache_local(const void* q, const void* k_cache, const void* v_cache,
+                         const int32_t* cache_seqlens, void* o, float* lse,
+                         int B, int Hq, int Hkv, int Nq, int Nk, int d, float scale, int causal,
+                         int window_left, float softcap, int num_splits, int dtype,
+                         void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
  * Decode over an FP8 key/value cache: fa_fwd_kvcache with k_cache and v_cache
  * holding e4m3fn codes (1 byte each, same [B, Nk, Hkv, d] layout) and
  * per-tensor descales (cached value = code value × descale). This is the FP8

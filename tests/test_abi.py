@@ -28,7 +28,7 @@ def test_header_declares_the_boundary():
                                     "fa_bwd_workspace_size", "fa_fwd", "fa_fwd_dropout",
                                     "fa_fwd_fp8",
                                     "fa_fwd_kvcache", "fa_fwd_kvcache_fp8",
-                                    "fa_fwd_kvcache_fp8_stage",
+                                    "fa_fwd_kvcache_fp8_stage", "fa_fwd_kvcache_local",
                                     "fa_fwd_kvcache_num_stages", "fa_fwd_kvcache_stage",
                                     "fa_fwd_kvcache_workspace_size", "fa_fwd_kvlen",
                                     "fa_fwd_softcap", "fa_fwd_window", "fa_fwd_window_softcap",
@@ -234,6 +234,40 @@ def test_fwd_kvlen_no_device_reports_hip_error():
     assert fkv() == fa.FA_ERR_HIP
     assert fkv(Nk=0, k=None, v=None) == fa.FA_ERR_HIP   # no key: k, v may be NULL
     assert fkv(d=256, causal=0, cq=P, ck=P) == fa.FA_ERR_HIP
+
+
+def kvcl(**kw):
+    a = dict(q=P, k=P, v=P, lens=P, o=P, lse=P, B=2, Hq=4, Hkv=2, Nq=1, Nk=64, d=128,
+             scale=0.125, causal=1, wl=16, cap=30.0, splits=2, dtype=fa.FA_BF16, ws=P,
+             wsb=1 << 20)
+    a.update(kw)
+    return fa.fa_fwd_kvcache_local(a["q"], a["k"], a["v"], a["lens"], a["o"], a["lse"], a["B"],
+                                   a["Hq"], a["Hkv"], a["Nq"], a["Nk"], a["d"], a["scale"],
+                                   a["causal"], a["wl"], a["cap"], a["splits"], a["dtype"],
+                                   a["ws"], a["wsb"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(wl=-2), fa.FA_ERR_INVALID_ARG),
+    (dict(cap=-1.0), fa.FA_ERR_INVALID_ARG),
+    (dict(cap=float("inf")), fa.FA_ERR_INVALID_ARG),
+    (dict(cap=1e-45, scale=1.0), fa.FA_ERR_INVALID_ARG),
+    (dict(d=96), fa.FA_ERR_UNSUPPORTED),
+    (dict(dtype=4), fa.FA_ERR_INVALID_ARG),
+    (dict(lens=None), fa.FA_ERR_INVALID_ARG),
+    (dict(ws=None), fa.FA_ERR_WORKSPACE),
+    (dict(B=0), fa.FA_OK),
+])
+def test_kvcache_local_host_checks(kw, status):
+    assert kvcl(**kw) == status
+
+
+def test_kvcache_local_no_device_reports_hip_error():
+    torch = pytest.importorskip("torch")
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    assert kvcl() == fa.FA_ERR_HIP
+    assert kvcl(wl=-1, cap=0.0, d=256, causal=0) == fa.FA_ERR_HIP
 
 
 def kvc8(stage=None, **kw):
