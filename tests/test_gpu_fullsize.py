@@ -1,6 +1,7 @@
 """Parity at the full sizes the benchmark times, for the workloads beyond the
-training step: the sliding window (window_16k), the soft cap (softcap_16k),
-dropout (dropout_16k) and head dimension 256 (train_d256). Each runs forward
+training step: the sliding window (window_16k), the soft cap (softcap_16k, and
+softcap_d256 at head dimension 256), dropout (dropout_16k) and head dimension
+256 (train_d256). Each runs forward
 and backward through the same entry points bench.py times, at the same shape;
 the oracle then computes sampled query rows of the forward one by one and whole
 (sequence, head) units of the backward.
@@ -101,3 +102,8 @@ def test_dropout_16k_full_size():
 
 def test_train_d256_full_size():
     _check(W.WORKLOADS["train_d256"], [(0, 0), (3, 15), (2, 7)], [(1, 5), (3, 0)], seed=34)
+
+
+def test_softcap_d256_full_size():
+    """Soft cap 50 at d = 256 with GQA 16/8 (the Gemma-2 setting) at the benchmark's size."""
+    _check(W.WORKLOADS["softcap_d256"], [(0, 0), (3, 15), (1, 6)], [(2, 3), (0, 7)], seed=35)
