@@ -349,14 +349,25 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeArgs a) {
       const int sp = base + lane;
       const float ls = sp < a.splits ? a.part_lse[sp * units + unit] : -INFINITY;
       const float w = ls == -INFINITY ? 0.f : expf(ls - m);   // a split with no key weighs 0
-      const int cnt = min(64, a.splits - base);
+      const int cnt = min(64, a.splits - base);   // uniform
       const float* po = a.part_o + ((int64_t)base * units + unit) * D + PER_LANE * lane;
-#pragma unroll 4
-      for (int j = 0; j < cnt; ++j) {
-        const float wj = __shfl(w, j);
-        wsum += wj;
+      // 16 splits' partial rows are loaded before any is accumulated, so their
+      // reads are in flight together (one memory round trip per 16 splits)
+      constexpr int BLK = 16;
+      for (int j0 = 0; j0 < cnt; j0 += BLK) {
+        float vals[BLK][PER_LANE];
 #pragma unroll
-        for (int e = 0; e < PER_LANE; ++e) acc[e] = fmaf(wj, po[j * units * D + e], acc[e]);
+        for (int u = 0; u < BLK; ++u)
+#pragma unroll
+          for (int e = 0; e < PER_LANE; ++e)
+            vals[u][e] = j0 + u < cnt ? po[(int64_t)(j0 + u) * units * D + e] : 0.f;
+#pragma unroll
+        for (int u = 0; u < BLK; ++u) {
+          const float wj = j0 + u < cnt ? __shfl(w, j0 + u) : 0.f;
+          wsum += wj;
+#pragma unroll
+          for (int e = 0; e < PER_LANE; ++e) acc[e] = fmaf(wj, vals[u][e], acc[e]);
+        }
       }
     }
   }
