@@ -18,8 +18,8 @@
 // small (d FLOP per loaded K or V element per row), so the kernel is bound by
 // HBM: K/V tiles of 32 keys are copied global -> LDS three stages deep.
 //
-// An e4m3 cache (the FP8 KV cache of the deployment guide, cxbdf.cn, section
-// 4.3) takes the same path at half the cache bytes: tiles are copied as raw
+// An e4m3 cache (the FP8 KV cache of the FlashAttention-2 全解析 page,
+// blog.gitcode.com, section 4.3) takes the same path at half the cache bytes: tiles are copied as raw
 // codes and each operand is widened to the query's 16-bit type in registers
 // (every e4m3 value is exact in bf16 and in fp16), so the products are those
 // of the 16-bit kernel on the decoded cache; the per-tensor descales enter

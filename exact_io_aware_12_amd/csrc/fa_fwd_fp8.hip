@@ -4,8 +4,8 @@
 // value times the descale is the real input); O is written as bf16 or fp16
 // and LSE as fp32, as in the 16-bit forward. The pages name e4m3 as the
 // 8-bit attention format and credit FlashAttention-3 with an FP8 forward
-// (Flash Attention 是什麼, adersaytech.com, FA-1 to FA-4 table; cxbdf.cn
-// deployment guide, section 4.3); the scaling recipe is not given there and
+// (Flash Attention 是什麼, adersaytech.com, FA-1 to FA-4 table; FlashAttention-2
+// 全解析, blog.gitcode.com, section 4.3); the scaling recipe is not given there and
 // per-tensor descales are the plain reading.
 //
 // Same tiling as the 16-bit forward (128 query rows per workgroup, 32 per

@@ -249,9 +249,9 @@ int fa_bwd_dropout_stage(int stage, const void* q, const void* k, const void* v,
 
 /*
  * Forward with queries and keys of different lengths (chunked prefill: a block
- * of new tokens attending to the cached ones and to itself; the pages' envelope
- * lists seqlen_q != seqlen_k, FlashAttention-2 page, blog.gitcode.com, and the
- * FAQ's head-dimension and length notes).
+ * of new tokens attending to the cached ones and to itself). The tiling sketch
+ * of the FlashAttention-2 全解析 page (blog.gitcode.com, section 2.1) takes
+ * seqlen_q and seqlen_k as separate arguments.
  *   fixed length (both cu_seqlens NULL): q, o [B, Nq, Hq, d]; k, v [B, Nk, Hkv, d];
  *     lse [Hq, B·Nq]
  *   varlen (both non-NULL, int32 device arrays of B+1 entries): q, o [Tq, Hq, d]
@@ -273,8 +273,8 @@ int fa_fwd_kvlen(const void* q, const void* k, const void* v, void* o, float* ls
 /*
  * FP8 forward: the forward of fa_fwd on e4m3 inputs. The pages name e4m3
  * (torch.float8_e4m3fn) as the 8-bit attention format and credit
- * FlashAttention-3 with an FP8 forward (cxbdf.cn deployment guide, section
- * 4.3; Flash Attention 是什麼, adersaytech.com, FA-1 to FA-4 table and note).
+ * FlashAttention-3 with an FP8 forward (FlashAttention-2 全解析, blog.gitcode.com,
+ * section 4.3; Flash Attention 是什麼, adersaytech.com, FA-1 to FA-4 table and note).
  *   q : [T, Hq, d]   e4m3fn codes (OCP E4M3, finite-only: bias 7, max 448)
  *   k : [T, Hkv, d]  e4m3fn codes
  *   v : [T, Hkv, d]  e4m3fn codes
@@ -340,8 +340,9 @@ int fa_fwd_kvcache_stage(int stage, const void* q, const void* k_cache, const vo
 
 /*
  * Decode with a sliding window and/or a soft cap (the local layers and capped
- * logits of models such as Gemma-2; window: the FlashAttention-2 page,
- * blog.gitcode.com, local attention; cap: its section 2.3, bounded reading):
+ * logits of models such as Gemma-2; window: the sliding-window mask named on
+ * the mlqm.cn evaluation page, section 四; cap: the FlashAttention-2 page,
+ * blog.gitcode.com, section 2.3, bounded reading):
  * fa_fwd_kvcache with
  *   window_left : −1 = none; otherwise query i of entry b (at position
  *                 p = L_b − Nq + i) sees only keys j >= p − window_left (with
@@ -363,9 +364,9 @@ int fa_fwd_kvcache_local(const void* q, const void* k_cache, const void* v_cache
  * Decode over an FP8 key/value cache: fa_fwd_kvcache with k_cache and v_cache
  * holding e4m3fn codes (1 byte each, same [B, Nk, Hkv, d] layout) and
  * per-tensor descales (cached value = code value × descale). This is the FP8
- * KV cache the deployment guide offers for long sequences that run out of
- * memory (FlashAttention guide, cxbdf.cn, section 4.3, kv_cache_dtype =
- * float8_e4m3fn); it halves the cache bytes each call reads.
+ * KV cache the FlashAttention-2 全解析 page (blog.gitcode.com, section 4.3,
+ * kv_cache_dtype = float8_e4m3fn) offers for long sequences that run out of
+ * memory; it halves the cache bytes each call reads.
  *   q, o     : `dtype` (FA_FP16 or FA_BF16), as in fa_fwd_kvcache
  *   descale_k, descale_v : finite and > 0, else FA_ERR_INVALID_ARG
  * The result is that of fa_fwd_kvcache on the decoded cache (every e4m3 value

@@ -238,3 +238,58 @@ def attention_bwd_sampled(q, k, v, do, scale: float, causal: bool, cu_seqlens,
             dv += dV
         res[(s, kvh)] = (dq, dk, dv)
     return res
+
+
+def attention_bwd_rows(q, k, v, do, scale: float, causal: bool, cu_seqlens, seq: int,
+                       kv_head: int, q_rows: Sequence[int], k_rows: Sequence[int],
+                       window=None, softcap=None):
+    """Backward of one (sequence, KV head) at selected positions only.
+
+    Returns (dq [len(q_rows), g, d], dk [len(k_rows), d], dv [len(k_rows), d]):
+    dQ at query positions ``q_rows`` for each of the g query heads sharing the
+    KV head, and dK, dV at key positions ``k_rows``, summed over those heads.
+
+    The same chain rule as head_bwd. A selected key's dK/dV column sums over
+    every query row, and each row's P needs its whole LSE and its D, so S, P,
+    dP and D are formed for every row (in blocks of whole rows); only the
+    selected rows of dQ and the selected columns of dK/dV are then contracted.
+    With causal and no window, a block of rows sees no key past its last row,
+    so the keys after it are left out of the block's products (their weights
+    are exactly zero). Inputs may be torch tensors; only the slices of this
+    (sequence, KV head) are upcast.
+    """
+    T, Hq = q.shape[0], q.shape[1]
+    g = _group(Hq, k.shape[1])
+    a, b = _segments(T, cu_seqlens)[seq]
+    L = b - a
+    Ks, Vs = _f64(k[a:b, kv_head]), _f64(v[a:b, kv_head])
+    qr = np.asarray(q_rows, dtype=np.int64)
+    kr = np.asarray(k_rows, dtype=np.int64)
+    if L and ((qr < 0).any() or (qr >= L).any() or (kr < 0).any() or (kr >= L).any()):
+        raise ValueError("selected positions must lie inside the sequence")
+    dq = np.zeros((len(qr), g, Ks.shape[1]))
+    dk = np.zeros((len(kr), Ks.shape[1]))
+    dv = np.zeros((len(kr), Vs.shape[1]))
+    prefix = causal and window is None
+    for r in range(g):
+        h = kv_head * g + r
+        Qs, dOs = _f64(q[a:b, h]), _f64(do[a:b, h])
+        for blk in _row_blocks(np.arange(L), L):
+            hi = int(blk[-1]) + 1 if prefix else L       # keys any row of the block can see
+            Kb, Vb = Ks[:hi], Vs[:hi]
+            S = _scores(Qs[blk], blk, Kb, scale, causal, window, softcap)
+            P = np.exp(S - _lse(S)[:, None])
+            dO = dOs[blk]
+            dP = dO @ Vb.T
+            D = (P * dP).sum(axis=1)
+            dS = P * (dP - D[:, None])
+            if softcap:   # d/dx [c·tanh(x/c)] = 1 − tanh²(x/c)
+                dS = dS * (1.0 - np.tanh(scale * (Qs[blk] @ Kb.T) / softcap) ** 2)
+            sel = kr < hi                                  # selected keys inside this block's range
+            if sel.any():
+                dv[sel] += P[:, kr[sel]].T @ dO
+                dk[sel] += scale * (dS[:, kr[sel]].T @ Qs[blk])
+            mine = np.nonzero((qr >= blk[0]) & (qr <= blk[-1]))[0]
+            if len(mine):
+                dq[mine, r] = scale * (dS[qr[mine] - blk[0]] @ Kb)
+    return dq, dk, dv

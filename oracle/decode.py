@@ -22,8 +22,8 @@ and LSE_i = −∞.
 
 Options, as in the full-sequence oracle (oracle.attention): a sliding window
 of `window_left` keys behind the query (keys j ≥ p_i − window_left stay
-visible; the sliding-window reading of the FlashAttention-2 page,
-blog.gitcode.com, local attention) and a soft cap c (S_ij → c·tanh(S_ij / c),
+visible; the sliding-window mask that the mlqm.cn evaluation page, section
+四, names among the masks standard attention supports) and a soft cap c (S_ij → c·tanh(S_ij / c),
 the same page's section 2.3 in the bounded reading).
 
 Layouts: q [B, Nq, Hq, d], k/v [B, Nk, Hkv, d] with Nk ≥ max L_b;
@@ -92,17 +92,21 @@ def kvcache_fwd(q, k_cache, v_cache, cache_seqlens, scale: float, causal: bool =
     return o, lse
 
 
-def kvcache_fwd_units(q, k_cache, v_cache, cache_seqlens, scale: float, causal: bool, units):
+def kvcache_fwd_units(q, k_cache, v_cache, cache_seqlens, scale: float, causal: bool, units,
+                      window_left=None, softcap=None):
     """O and LSE of selected (batch entry, query head) units: {(b, h): (O [Nq, d], LSE [Nq])}.
 
-    Inputs may be torch tensors; only the selected slices are upcast.
+    The same per-unit computation as kvcache_fwd (window and cap included);
+    inputs may be torch tensors, and only the selected slices are upcast.
     """
     lens = [int(x) for x in np.asarray(_f64(cache_seqlens))]
     Hq, Hkv = q.shape[2], k_cache.shape[2]
+    if Hkv <= 0 or Hq % Hkv:
+        raise ValueError(f"Hq={Hq} must be a positive multiple of Hkv={Hkv}")
     g = Hq // Hkv
     res = {}
     for b, h in units:
         L = lens[b]
         res[(b, h)] = kvcache_head(q[b, :, h], k_cache[b, :L, h // g], v_cache[b, :L, h // g],
-                                   scale, causal)
+                                   scale, causal, window_left, softcap)
     return res

@@ -3,7 +3,7 @@
 Test infrastructure only (see the package docstring).
 
 The pages name e4m3 (``torch.float8_e4m3fn``) as the 8-bit format for keys
-and values (FlashAttention deployment guide, cxbdf.cn, section 4.3, the
+and values (FlashAttention-2 全解析, blog.gitcode.com, section 4.3, the
 KV-cache quantisation pitfall) and credit FlashAttention-3's FP8 forward with
 a lower error than plain FP8 attention (Flash Attention 是什麼,
 adersaytech.com, FA-1 to FA-4 table and the note after it). They give no

@@ -171,3 +171,65 @@ def test_sampled_matches_whole():
     np.testing.assert_allclose(sq, dq[11:, 2:4], atol=1e-14)
     np.testing.assert_allclose(sk, dk[11:, 1], atol=1e-14)
     np.testing.assert_allclose(sv, dv[11:, 1], atol=1e-14)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("Hq,Hkv", [(2, 2), (4, 1)])
+@pytest.mark.parametrize("opt", ["plain", "window", "softcap"])
+def test_rows_match_whole(monkeypatch, causal, Hq, Hkv, opt):
+    """attention_bwd_rows at selected query rows and key columns equals those rows
+    and columns of the whole-tensor backward (itself pinned above), across
+    several row blocks (a tiny block size) and two sequences of a packed batch."""
+    import oracle.attention as A
+    monkeypatch.setattr(A, "_BLOCK_ELEMS", 40)   # blocks of one to a few rows
+    rng = np.random.default_rng(11 + Hq)
+    lens = [9, 23]
+    cu = np.concatenate([[0], np.cumsum(lens)])
+    T, d = int(cu[-1]), 6
+    q, k, v, do = _rand(rng, T, Hq, d), _rand(rng, T, Hkv, d), _rand(rng, T, Hkv, d), \
+        _rand(rng, T, Hq, d)
+    kw = {"plain": {}, "window": {"window": (4, 2)}, "softcap": {"softcap": 1.5}}[opt]
+    dq, dk, dv = attention_bwd(q, k, v, do, 0.45, causal, cu, **kw)
+    g = Hq // Hkv
+    for s in range(2):
+        a, L = int(cu[s]), lens[s]
+        qr, kr = [0, L // 2, L - 1], [L - 1, 0, 3]
+        for kvh in range(Hkv):
+            rq, rk, rv = A.attention_bwd_rows(q, k, v, do, 0.45, causal, cu, s, kvh, qr, kr, **kw)
+            np.testing.assert_allclose(rq, dq[a + np.array(qr), kvh * g:(kvh + 1) * g],
+                                       atol=1e-13)
+            np.testing.assert_allclose(rk, dk[a + np.array(kr), kvh], atol=1e-13)
+            np.testing.assert_allclose(rv, dv[a + np.array(kr), kvh], atol=1e-13)
+
+
+def test_rows_torch_autograd():
+    """attention_bwd_rows against torch's CPU float64 autograd of plain causal GQA
+    attention (an implementation that shares nothing with the oracle)."""
+    torch = pytest.importorskip("torch")
+    from oracle import attention_bwd_rows
+    rng = np.random.default_rng(5)
+    L, Hq, Hkv, d = 37, 4, 2, 8
+    q, k, v, do = _rand(rng, L, Hq, d), _rand(rng, L, Hkv, d), _rand(rng, L, Hkv, d), \
+        _rand(rng, L, Hq, d)
+    tq, tk, tv = (torch.tensor(x, requires_grad=True) for x in (q, k, v))
+    kk = tk.repeat_interleave(Hq // Hkv, dim=1)
+    vv = tv.repeat_interleave(Hq // Hkv, dim=1)
+    s = torch.einsum("ihc,jhc->hij", tq, kk) * 0.3
+    mask = torch.ones(L, L, dtype=torch.bool).tril()
+    s = s.masked_fill(~mask, float("-inf"))
+    o = torch.einsum("hij,jhc->ihc", torch.softmax(s, dim=-1), vv)
+    o.backward(torch.tensor(do))
+    qr, kr = [0, 5, 36], [0, 17, 36]
+    for kvh in range(Hkv):
+        rq, rk, rv = attention_bwd_rows(q, k, v, do, 0.3, True, None, 0, kvh, qr, kr)
+        np.testing.assert_allclose(rq, tq.grad.numpy()[qr, 2 * kvh:2 * kvh + 2], atol=1e-12)
+        np.testing.assert_allclose(rk, tk.grad.numpy()[kr, kvh], atol=1e-12)
+        np.testing.assert_allclose(rv, tv.grad.numpy()[kr, kvh], atol=1e-12)
+
+
+def test_rows_rejects_positions_outside():
+    from oracle import attention_bwd_rows
+    rng = np.random.default_rng(1)
+    q = _rand(rng, 5, 1, 4)
+    with pytest.raises(ValueError):
+        attention_bwd_rows(q, q, q, q, 1.0, False, None, 0, 0, [5], [0])

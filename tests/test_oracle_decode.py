@@ -187,3 +187,40 @@ def test_gqa_head_map():
     o, _ = kvcache_fwd(q, k, v, [5], 1.0, False)
     o_sw, _ = kvcache_fwd(q[:, :, [2, 3, 0, 1]], k[:, :, [1, 0]], v[:, :, [1, 0]], [5], 1.0, False)
     np.testing.assert_allclose(o_sw, o[:, :, [2, 3, 0, 1]], atol=1e-14)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("opts", [{}, {"window_left": 3}, {"softcap": 2.0},
+                                  {"window_left": 0, "softcap": 1.0}])
+def test_units_match_whole(causal, opts):
+    """kvcache_fwd_units on selected (entry, head) units equals those units of the
+    whole-tensor kvcache_fwd (pinned above): ragged, empty and one-key caches,
+    GQA, several queries, with and without a window and a cap."""
+    from oracle import kvcache_fwd_units
+    rng = np.random.default_rng(31)
+    B, Nq, Nk, Hq, Hkv, d = 5, 3, 12, 4, 2, 8
+    q, k, v = _cache(rng, B, Nq, Nk, Hq, Hkv, d)
+    lens = np.array([12, 0, 1, 7, 2], dtype=np.int32)   # full, empty, one key, ragged, < Nq
+    o, lse = kvcache_fwd(q, k, v, lens, 0.35, causal, **opts)
+    units = [(b, h) for b in range(B) for h in range(Hq)]
+    res = kvcache_fwd_units(q, k, v, lens, 0.35, causal, units, **opts)
+    assert sorted(res) == units
+    for (b, h), (O, L) in res.items():
+        np.testing.assert_allclose(O, o[b, :, h], atol=1e-14)
+        np.testing.assert_array_equal(np.isneginf(L), np.isneginf(lse[h, b * Nq:(b + 1) * Nq]))
+        fin = np.isfinite(L)
+        np.testing.assert_allclose(L[fin], lse[h, b * Nq:(b + 1) * Nq][fin], atol=1e-14)
+    # a one-key cache (closed form): a query that sees the key returns its value
+    # row; causal queries placed before position 0 see nothing (O = 0, LSE = −inf)
+    O2, L2 = res[(2, 3)]
+    sees = np.array([not causal, not causal, True])
+    np.testing.assert_allclose(O2[sees], np.broadcast_to(v[2, 0, 1], O2[sees].shape), atol=1e-14)
+    assert (O2[~sees] == 0).all() and np.isneginf(L2[~sees]).all()
+
+
+def test_units_rejects_bad_group():
+    from oracle import kvcache_fwd_units
+    q = np.zeros((1, 1, 3, 4))
+    k = np.zeros((1, 2, 2, 4))
+    with pytest.raises(ValueError):
+        kvcache_fwd_units(q, k, k, np.array([2]), 1.0, False, [(0, 0)])

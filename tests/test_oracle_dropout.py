@@ -176,3 +176,26 @@ def test_delta_is_do_dot_o():
     Z = km(77, 0, 0, np.arange(20), np.arange(20), keep_threshold(0.2)) * (256 / keep_threshold(0.2))
     D = (P * Z * (do[:, 0] @ v[:, 0].T)).sum(axis=1)
     np.testing.assert_allclose(D, (do[:, 0] * o[:, 0]).sum(axis=1), atol=1e-12)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_rows_match_whole(monkeypatch, causal):
+    """head_fwd_dropout(rows=...) equals those rows of attention_fwd_dropout
+    (pinned above), across row blocks of a few rows, in the second sequence of a
+    packed batch and for the second head of a GQA group (so the generator's
+    sequence, head and row counters all differ from 0)."""
+    import oracle.attention as A
+    from oracle import head_fwd_dropout
+    monkeypatch.setattr(A, "_BLOCK_ELEMS", 50)
+    rng = np.random.default_rng(8)
+    lens = [13, 29]
+    cu = np.concatenate([[0], np.cumsum(lens)])
+    T, Hq, Hkv, d = int(cu[-1]), 4, 2, 5
+    q, k, v = (rng.standard_normal((T, H, d)) for H in (Hq, Hkv, Hkv))
+    o, lse = attention_fwd_dropout(q, k, v, 0.6, causal, cu, 0.3, 2 ** 40 + 77)
+    rows = [28, 0, 5, 17, 4]
+    a = int(cu[1])
+    O, L = head_fwd_dropout(q[a:, 3], k[a:, 1], v[a:, 1], 0.6, causal, 1, 3, 0.3, 2 ** 40 + 77,
+                            rows=rows)
+    np.testing.assert_allclose(O, o[a + np.array(rows), 3], atol=1e-14)
+    np.testing.assert_allclose(L, lse[3, a + np.array(rows)], atol=1e-14)
