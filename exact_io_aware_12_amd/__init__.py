@@ -5,14 +5,9 @@ kernels of libfa.so; torch supplies device memory and the current stream.
 If the library has not been built, importing the binding raises: there is no
 fallback implementation.
 
-Raw entry points with the C names and arguments (pointers as ints):
-    fa_fwd, fa_bwd, fa_bwd_stage, fa_bwd_num_stages, fa_bwd_workspace_size,
-    fa_fwd_window, fa_bwd_window, fa_bwd_window_stage,
-    fa_fwd_softcap, fa_bwd_softcap, fa_bwd_softcap_stage,
-    fa_fwd_dropout, fa_bwd_dropout, fa_bwd_dropout_stage, fa_fwd_fp8,
-    fa_fwd_kvcache, fa_fwd_kvcache_stage, fa_fwd_kvcache_num_stages,
-    fa_kvcache_num_splits, fa_fwd_kvcache_workspace_size,
-    fa_status_string
+Raw entry points: every function include/fa.h declares, under its C name
+with its C arguments (pointers as ints, None for NULL), returning the status
+(or size); fa_status_string returns a str.
 Tensor-level helpers:
     flash_attn_func(q, k, v, causal=False, softmax_scale=None,
                     cu_seqlens=None, max_seqlen=None, dropout_p=0.0,
@@ -34,14 +29,6 @@ import ctypes
 import math
 import os
 
-__all__ = ["FA_OK", "FA_ERR_INVALID_ARG", "FA_ERR_UNSUPPORTED", "FA_ERR_HIP", "FA_ERR_WORKSPACE",
-           "FA_FP16", "FA_BF16", "FaError", "lib", "lib_path", "fa_fwd", "fa_bwd",
-           "fa_bwd_workspace_size", "fa_status_string", "flash_attn_func",
-           "flash_attn_backward", "fa_bwd_stage", "fa_bwd_num_stages", "fa_fwd_kvcache",
-           "fa_kvcache_num_splits", "fa_fwd_kvcache_workspace_size", "flash_attn_with_kvcache",
-           "fa_fwd_kvcache_stage", "fa_fwd_kvcache_num_stages", "fa_fwd_kvcache_fp8",
-           "fa_fwd_kvcache_fp8_stage", "fa_kvcache_fp8_num_splits",
-           "fa_fwd_kvlen", "flash_attn_kvlen_func", "fa_fwd_kvcache_local"]
 
 FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_HIP, FA_ERR_WORKSPACE = 0, -1, -2, -3, -4
 FA_FP16, FA_BF16 = 0, 1
@@ -59,6 +46,45 @@ class FaError(RuntimeError):
         super().__init__(f"{where}: {fa_status_string(status)} ({status})")
 
 
+# C signatures of the exported functions (include/fa.h), for ctypes: pointer
+# arguments (device pointers, streams) are void*; fa_dtype and the status are int.
+_VP, _I, _F, _SZ, _U64 = (ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t,
+                          ctypes.c_uint64)
+_FWD_HEAD = [_VP] * 5 + [_I] * 5 + [_F]                 # q k v o lse  B Hq Hkv N d  scale
+_BWD_HEAD = [_VP] * 9 + [_I] * 5 + [_F]                 # q k v o dout lse dq dk dv  B..d  scale
+_BWD_TAIL = [_VP, _I, _VP, _SZ, _VP]                    # cu_seqlens dtype workspace bytes stream
+_KVC_HEAD = [_VP] * 6 + [_I] * 6 + [_F, _I]             # q kc vc lens o lse  B Hq Hkv Nq Nk d  scale causal
+_WS_TAIL = [_VP, _SZ, _VP]                              # workspace bytes stream
+_SIGS = {
+    "fa_fwd": (_I, _FWD_HEAD + [_I, _VP, _I, _VP]),
+    "fa_bwd": (_I, _BWD_HEAD + [_I] + _BWD_TAIL),
+    "fa_bwd_num_stages": (_I, []),
+    "fa_bwd_workspace_size": (_SZ, [_I] * 5),
+    "fa_fwd_window": (_I, _FWD_HEAD + [_I, _I, _VP, _I, _VP]),
+    "fa_bwd_window": (_I, _BWD_HEAD + [_I, _I] + _BWD_TAIL),
+    "fa_fwd_window_softcap": (_I, _FWD_HEAD + [_I, _I, _F, _VP, _I, _VP]),
+    "fa_bwd_window_softcap": (_I, _BWD_HEAD + [_I, _I, _F] + _BWD_TAIL),
+    "fa_fwd_softcap": (_I, _FWD_HEAD + [_I, _F, _VP, _I, _VP]),
+    "fa_bwd_softcap": (_I, _BWD_HEAD + [_I, _F] + _BWD_TAIL),
+    "fa_fwd_dropout": (_I, _FWD_HEAD + [_I, _F, _U64, _VP, _I, _VP]),
+    "fa_bwd_dropout": (_I, _BWD_HEAD + [_I, _F, _U64] + _BWD_TAIL),
+    "fa_fwd_kvlen": (_I, [_VP] * 5 + [_I] * 6 + [_F, _I, _VP, _VP, _I, _VP]),
+    "fa_fwd_fp8": (_I, _FWD_HEAD + [_I, _VP, _F, _F, _F, _I, _VP]),
+    "fa_fwd_kvcache": (_I, _KVC_HEAD + [_I, _I] + _WS_TAIL),
+    "fa_fwd_kvcache_local": (_I, _KVC_HEAD + [_I, _F, _I, _I] + _WS_TAIL),
+    "fa_fwd_kvcache_fp8": (_I, _KVC_HEAD + [_F, _F, _I, _I] + _WS_TAIL),
+    "fa_fwd_kvcache_num_stages": (_I, []),
+    "fa_kvcache_num_splits": (_I, [_I] * 6),
+    "fa_kvcache_fp8_num_splits": (_I, [_I] * 6),
+    "fa_fwd_kvcache_workspace_size": (_SZ, [_I] * 7),
+    "fa_status_string": (ctypes.c_char_p, [_I]),
+}
+# each staged entry point takes a leading stage index, then its parent's arguments
+for _n in ("fa_bwd", "fa_bwd_window", "fa_bwd_window_softcap", "fa_bwd_softcap",
+           "fa_bwd_dropout", "fa_fwd_kvcache", "fa_fwd_kvcache_fp8"):
+    _SIGS[_n + "_stage"] = (_I, [_I] + _SIGS[_n][1])
+
+
 def _load():
     path = lib_path()
     if not os.path.exists(path):
@@ -70,157 +96,31 @@ def _load():
     # libfa.so first would pull in a second runtime that cannot see torch's memory.
     import torch  # noqa: F401
     L = ctypes.CDLL(path)
-    vp, i, f, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
-    L.fa_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp, i, vp]
-    L.fa_fwd.restype = i
-    L.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp, i, vp, sz, vp]
-    L.fa_bwd.restype = i
-    L.fa_bwd_stage.argtypes = [i] + L.fa_bwd.argtypes
-    L.fa_bwd_stage.restype = i
-    L.fa_bwd_num_stages.argtypes = []
-    L.fa_bwd_num_stages.restype = i
-    L.fa_bwd_workspace_size.argtypes = [i, i, i, i, i]
-    L.fa_bwd_workspace_size.restype = sz
-    L.fa_fwd_window.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, i, i, vp, i, vp]
-    L.fa_fwd_window.restype = i
-    L.fa_bwd_window.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, i, vp, i,
-                                vp, sz, vp]
-    L.fa_bwd_window.restype = i
-    L.fa_bwd_window_stage.argtypes = [i] + L.fa_bwd_window.argtypes
-    L.fa_bwd_window_stage.restype = i
-    L.fa_fwd_window_softcap.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, i, i, f, vp, i, vp]
-    L.fa_fwd_window_softcap.restype = i
-    L.fa_bwd_window_softcap.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, i,
-                                        f, vp, i, vp, sz, vp]
-    L.fa_bwd_window_softcap.restype = i
-    L.fa_bwd_window_softcap_stage.argtypes = [i] + L.fa_bwd_window_softcap.argtypes
-    L.fa_bwd_window_softcap_stage.restype = i
-    L.fa_fwd_softcap.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, i, f, vp, i, vp]
-    L.fa_fwd_softcap.restype = i
-    L.fa_bwd_softcap.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, f, vp, i,
-                                 vp, sz, vp]
-    L.fa_bwd_softcap.restype = i
-    L.fa_bwd_softcap_stage.argtypes = [i] + L.fa_bwd_softcap.argtypes
-    L.fa_bwd_softcap_stage.restype = i
-    u64 = ctypes.c_uint64
-    L.fa_fwd_dropout.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, i, f, u64, vp, i, vp]
-    L.fa_fwd_dropout.restype = i
-    L.fa_bwd_dropout.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, f, u64,
-                                 vp, i, vp, sz, vp]
-    L.fa_bwd_dropout.restype = i
-    L.fa_bwd_dropout_stage.argtypes = [i] + L.fa_bwd_dropout.argtypes
-    L.fa_bwd_dropout_stage.restype = i
-    L.fa_fwd_kvlen.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, vp, vp, i, vp]
-    L.fa_fwd_kvlen.restype = i
-    L.fa_fwd_fp8.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp, f, f, f, i, vp]
-    L.fa_fwd_fp8.restype = i
-    L.fa_fwd_kvcache.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, i, i, vp, sz, vp]
-    L.fa_fwd_kvcache.restype = i
-    L.fa_fwd_kvcache_stage.argtypes = [i] + L.fa_fwd_kvcache.argtypes
-    L.fa_fwd_kvcache_stage.restype = i
-    L.fa_fwd_kvcache_local.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, i, f, i, i,
-                                       vp, sz, vp]
-    L.fa_fwd_kvcache_local.restype = i
-    L.fa_fwd_kvcache_fp8.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, f, f, i, i, vp,
-                                     sz, vp]
-    L.fa_fwd_kvcache_fp8.restype = i
-    L.fa_fwd_kvcache_fp8_stage.argtypes = [i] + L.fa_fwd_kvcache_fp8.argtypes
-    L.fa_fwd_kvcache_fp8_stage.restype = i
-    L.fa_fwd_kvcache_num_stages.argtypes = []
-    L.fa_fwd_kvcache_num_stages.restype = i
-    L.fa_kvcache_num_splits.argtypes = [i, i, i, i, i, i]
-    L.fa_kvcache_num_splits.restype = i
-    L.fa_kvcache_fp8_num_splits.argtypes = [i, i, i, i, i, i]
-    L.fa_kvcache_fp8_num_splits.restype = i
-    L.fa_fwd_kvcache_workspace_size.argtypes = [i, i, i, i, i, i, i]
-    L.fa_fwd_kvcache_workspace_size.restype = sz
-    L.fa_status_string.argtypes = [i]
-    L.fa_status_string.restype = ctypes.c_char_p
+    for name, (res, args) in _SIGS.items():
+        fn = getattr(L, name)
+        fn.restype, fn.argtypes = res, args
     return L
 
 
 lib = _load()
 
-
-# ---- raw C entry points ------------------------------------------------------
-def fa_fwd(q, k, v, o, lse, B, Hq, Hkv, N, d, scale, causal, cu_seqlens, dtype, stream) -> int:
-    return lib.fa_fwd(q, k, v, o, lse, B, Hq, Hkv, N, d, scale, causal, cu_seqlens, dtype, stream)
-
-
-def fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, B, Hq, Hkv, N, d, scale, causal, cu_seqlens, dtype,
-           workspace, workspace_bytes, stream) -> int:
-    return lib.fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, B, Hq, Hkv, N, d, scale, causal,
-                      cu_seqlens, dtype, workspace, workspace_bytes, stream)
+# ---- raw C entry points: the library's functions themselves, C names and
+# argument order (pointers as ints or None), returning the status or size
+for _n in _SIGS:
+    if _n != "fa_status_string":
+        globals()[_n] = getattr(lib, _n)
 
 
-def fa_bwd_stage(stage, q, k, v, o, dout, lse, dq, dk, dv, B, Hq, Hkv, N, d, scale, causal,
-                 cu_seqlens, dtype, workspace, workspace_bytes, stream) -> int:
-    return lib.fa_bwd_stage(stage, q, k, v, o, dout, lse, dq, dk, dv, B, Hq, Hkv, N, d, scale,
-                            causal, cu_seqlens, dtype, workspace, workspace_bytes, stream)
+def fa_status_string(status: int) -> str:
+    return lib.fa_status_string(status).decode()
 
 
-def fa_fwd_window(q, k, v, o, lse, B, Hq, Hkv, N, d, scale, window_left, window_right, cu_seqlens,
-                  dtype, stream) -> int:
-    return lib.fa_fwd_window(q, k, v, o, lse, B, Hq, Hkv, N, d, scale, window_left, window_right,
-                             cu_seqlens, dtype, stream)
+__all__ = (["FA_OK", "FA_ERR_INVALID_ARG", "FA_ERR_UNSUPPORTED", "FA_ERR_HIP", "FA_ERR_WORKSPACE",
+            "FA_FP16", "FA_BF16", "FaError", "lib", "lib_path", "flash_attn_func",
+            "flash_attn_backward", "flash_attn_func_fp8", "flash_attn_kvlen_func",
+            "flash_attn_with_kvcache"] + sorted(_SIGS))
 
-
-def fa_bwd_window(q, k, v, o, dout, lse, dq, dk, dv, B, Hq, Hkv, N, d, scale, window_left,
-                  window_right, cu_seqlens, dtype, workspace, workspace_bytes, stream) -> int:
-    return lib.fa_bwd_window(q, k, v, o, dout, lse, dq, dk, dv, B, Hq, Hkv, N, d, scale,
-                             window_left, window_right, cu_seqlens, dtype, workspace,
-                             workspace_bytes, stream)
-
-
-def fa_bwd_window_stage(stage, q, k, v, o, dout, lse, dq, dk, dv, B, Hq, Hkv, N, d, scale,
-                        window_left, window_right, cu_seqlens, dtype, workspace, workspace_bytes,
-                        stream) -> int:
-    return lib.fa_bwd_window_stage(stage, q, k, v, o, dout, lse, dq, dk, dv, B, Hq, Hkv, N, d,
-                                   scale, window_left, window_right, cu_seqlens, dtype, workspace,
-                                   workspace_bytes, stream)
-
-
-def fa_fwd_softcap(q, k, v, o, lse, B, Hq, Hkv, N, d, scale, causal, softcap, cu_seqlens, dtype,
-                   stream) -> int:
-    return lib.fa_fwd_softcap(q, k, v, o, lse, B, Hq, Hkv, N, d, scale, causal, softcap,
-                              cu_seqlens, dtype, stream)
-
-
-def fa_bwd_softcap(q, k, v, o, dout, lse, dq, dk, dv, B, Hq, Hkv, N, d, scale, causal, softcap,
-                   cu_seqlens, dtype, workspace, workspace_bytes, stream) -> int:
-    return lib.fa_bwd_softcap(q, k, v, o, dout, lse, dq, dk, dv, B, Hq, Hkv, N, d, scale, causal,
-                              softcap, cu_seqlens, dtype, workspace, workspace_bytes, stream)
-
-
-def fa_bwd_softcap_stage(stage, q, k, v, o, dout, lse, dq, dk, dv, B, Hq, Hkv, N, d, scale,
-                         causal, softcap, cu_seqlens, dtype, workspace, workspace_bytes,
-                         stream) -> int:
-    return lib.fa_bwd_softcap_stage(stage, q, k, v, o, dout, lse, dq, dk, dv, B, Hq, Hkv, N, d,
-                                    scale, causal, softcap, cu_seqlens, dtype, workspace,
-                                    workspace_bytes, stream)
-
-
-def fa_fwd_dropout(q, k, v, o, lse, B, Hq, Hkv, N, d, scale, causal, dropout_p, seed, cu_seqlens,
-                   dtype, stream) -> int:
-    return lib.fa_fwd_dropout(q, k, v, o, lse, B, Hq, Hkv, N, d, scale, causal, dropout_p, seed,
-                              cu_seqlens, dtype, stream)
-
-
-def fa_bwd_dropout(q, k, v, o, dout, lse, dq, dk, dv, B, Hq, Hkv, N, d, scale, causal, dropout_p,
-                   seed, cu_seqlens, dtype, workspace, workspace_bytes, stream) -> int:
-    return lib.fa_bwd_dropout(q, k, v, o, dout, lse, dq, dk, dv, B, Hq, Hkv, N, d, scale, causal,
-                              dropout_p, seed, cu_seqlens, dtype, workspace, workspace_bytes,
-                              stream)
-
-
-def fa_bwd_dropout_stage(stage, q, k, v, o, dout, lse, dq, dk, dv, B, Hq, Hkv, N, d, scale,
-                         causal, dropout_p, seed, cu_seqlens, dtype, workspace, workspace_bytes,
-                         stream) -> int:
-    return lib.fa_bwd_dropout_stage(stage, q, k, v, o, dout, lse, dq, dk, dv, B, Hq, Hkv, N, d,
-                                    scale, causal, dropout_p, seed, cu_seqlens, dtype, workspace,
-                                    workspace_bytes, stream)
-
-
+# ---- tensor helpers ----------------------------------------------------------
 def _dropout_args(dropout_p, dropout_seed, causal_window, softcap):
     """(p, seed) for the dropout entry points, or None when dropout_p is 0."""
     if not dropout_p:
@@ -235,85 +135,6 @@ def _dropout_args(dropout_p, dropout_seed, causal_window, softcap):
     return float(dropout_p), seed
 
 
-def fa_fwd_kvlen(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, scale, causal, cu_seqlens_q,
-                 cu_seqlens_k, dtype, stream) -> int:
-    return lib.fa_fwd_kvlen(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, scale, causal, cu_seqlens_q,
-                            cu_seqlens_k, dtype, stream)
-
-
-def fa_fwd_fp8(q, k, v, o, lse, B, Hq, Hkv, N, d, scale, causal, cu_seqlens, descale_q,
-               descale_k, descale_v, out_dtype, stream) -> int:
-    return lib.fa_fwd_fp8(q, k, v, o, lse, B, Hq, Hkv, N, d, scale, causal, cu_seqlens,
-                          descale_q, descale_k, descale_v, out_dtype, stream)
-
-
-def fa_bwd_num_stages() -> int:
-    return lib.fa_bwd_num_stages()
-
-
-def fa_bwd_workspace_size(B, Hq, Hkv, N, d) -> int:
-    return lib.fa_bwd_workspace_size(B, Hq, Hkv, N, d)
-
-
-def fa_fwd_kvcache(q, k_cache, v_cache, cache_seqlens, o, lse, B, Hq, Hkv, Nq, Nk, d, scale, causal,
-                   num_splits, dtype, workspace, workspace_bytes, stream) -> int:
-    return lib.fa_fwd_kvcache(q, k_cache, v_cache, cache_seqlens, o, lse, B, Hq, Hkv, Nq, Nk, d,
-                              scale, causal, num_splits, dtype, workspace, workspace_bytes, stream)
-
-
-def fa_fwd_kvcache_stage(stage, q, k_cache, v_cache, cache_seqlens, o, lse, B, Hq, Hkv, Nq, Nk, d,
-                         scale, causal, num_splits, dtype, workspace, workspace_bytes,
-                         stream) -> int:
-    return lib.fa_fwd_kvcache_stage(stage, q, k_cache, v_cache, cache_seqlens, o, lse, B, Hq, Hkv,
-                                    Nq, Nk, d, scale, causal, num_splits, dtype, workspace,
-                                    workspace_bytes, stream)
-
-
-def fa_fwd_kvcache_fp8(q, k_cache, v_cache, cache_seqlens, o, lse, B, Hq, Hkv, Nq, Nk, d, scale,
-                       causal, descale_k, descale_v, num_splits, dtype, workspace,
-                       workspace_bytes, stream) -> int:
-    return lib.fa_fwd_kvcache_fp8(q, k_cache, v_cache, cache_seqlens, o, lse, B, Hq, Hkv, Nq, Nk,
-                                  d, scale, causal, descale_k, descale_v, num_splits, dtype,
-                                  workspace, workspace_bytes, stream)
-
-
-def fa_fwd_kvcache_local(q, k_cache, v_cache, cache_seqlens, o, lse, B, Hq, Hkv, Nq, Nk, d, scale,
-                         causal, window_left, softcap, num_splits, dtype, workspace,
-                         workspace_bytes, stream) -> int:
-    return lib.fa_fwd_kvcache_local(q, k_cache, v_cache, cache_seqlens, o, lse, B, Hq, Hkv, Nq,
-                                    Nk, d, scale, causal, window_left, softcap, num_splits, dtype,
-                                    workspace, workspace_bytes, stream)
-
-
-def fa_fwd_kvcache_fp8_stage(stage, q, k_cache, v_cache, cache_seqlens, o, lse, B, Hq, Hkv, Nq,
-                             Nk, d, scale, causal, descale_k, descale_v, num_splits, dtype,
-                             workspace, workspace_bytes, stream) -> int:
-    return lib.fa_fwd_kvcache_fp8_stage(stage, q, k_cache, v_cache, cache_seqlens, o, lse, B, Hq,
-                                        Hkv, Nq, Nk, d, scale, causal, descale_k, descale_v,
-                                        num_splits, dtype, workspace, workspace_bytes, stream)
-
-
-def fa_fwd_kvcache_num_stages() -> int:
-    return lib.fa_fwd_kvcache_num_stages()
-
-
-def fa_kvcache_num_splits(B, Hq, Hkv, Nq, Nk, d) -> int:
-    return lib.fa_kvcache_num_splits(B, Hq, Hkv, Nq, Nk, d)
-
-
-def fa_kvcache_fp8_num_splits(B, Hq, Hkv, Nq, Nk, d) -> int:
-    return lib.fa_kvcache_fp8_num_splits(B, Hq, Hkv, Nq, Nk, d)
-
-
-def fa_fwd_kvcache_workspace_size(B, Hq, Hkv, Nq, Nk, d, num_splits) -> int:
-    return lib.fa_fwd_kvcache_workspace_size(B, Hq, Hkv, Nq, Nk, d, num_splits)
-
-
-def fa_status_string(status: int) -> str:
-    return lib.fa_status_string(status).decode()
-
-
-# ---- tensor helpers ----------------------------------------------------------
 def _dtype_code(t):
     import torch
     if t.dtype == torch.float16:
@@ -342,12 +163,41 @@ def _shape(q, k, cu_seqlens, max_seqlen):
     return cu_seqlens.numel() - 1, int(max_seqlen), T, Hq, k.shape[1], d
 
 
+def _check_cu(cu_seqlens, T, max_seqlen, validate=True, what="cu_seqlens"):
+    """A packed batch's prefix sums: int32 on the GPU, and (unless validate is
+    False, or the stream is being captured into a graph) consistent with the
+    packed tensors: cu[0] = 0, non-decreasing, cu[-1] = T and no sequence
+    longer than max_seqlen. The kernels index the LSE with stride cu[-1] and
+    size their grid by max_seqlen, so a mismatch would misplace rows or leave
+    them unwritten. The check reads the B+1 entries back (one small copy)."""
+    import torch
+    _check_dev(cu_seqlens)
+    if cu_seqlens.dtype != torch.int32:
+        raise TypeError(f"{what} must be int32")
+    if cu_seqlens.dim() != 1 or cu_seqlens.numel() < 1:
+        raise ValueError(f"{what} must be a 1-d tensor of B+1 prefix sums")
+    if not validate or torch.cuda.is_current_stream_capturing():
+        return
+    cu = cu_seqlens.cpu().tolist()
+    lens = [b - a for a, b in zip(cu[:-1], cu[1:])]
+    if cu[0] != 0 or any(n < 0 for n in lens):
+        raise ValueError(f"{what} must start at 0 and never decrease")
+    if cu[-1] != T:
+        raise ValueError(f"{what}[-1] = {cu[-1]} but the packed tensors hold {T} tokens")
+    if lens and max(lens) > int(max_seqlen):
+        raise ValueError(f"a sequence of {max(lens)} tokens exceeds max_seqlen = {max_seqlen}")
+
+
 def _check_dev(*ts):
     for t in ts:
         if not t.is_cuda:
             raise ValueError("fa tensors must be on the GPU")
         if not t.is_contiguous():
             raise ValueError("fa tensors must be contiguous")
+
+
+def _nbytes(t):
+    return t.numel() * t.element_size()
 
 
 def _stream():
@@ -368,9 +218,13 @@ def _window(causal, window_size):
 
 
 def flash_attn_func(q, k, v, causal=False, softmax_scale=None, cu_seqlens=None, max_seqlen=None,
-                    dropout_p=0.0, window_size=(-1, -1), softcap=0.0, dropout_seed=None):
+                    dropout_p=0.0, window_size=(-1, -1), softcap=0.0, dropout_seed=None,
+                    validate=True):
     """Forward. Returns (o, lse); lse is float32 [Hq, T] (natural log).
 
+    cu_seqlens (int32, B+1 prefix sums) with max_seqlen: a packed batch of
+    [T, H, d] tensors; validate=False skips reading cu_seqlens back to check it
+    against T and max_seqlen (no host synchronisation).
     window_size = (left, right): query i sees keys i − left .. i + right of its
     sequence (−1: unbounded); with causal the right side is 0.
     softcap = c > 0: logits c·tanh(scale·q·k / c) (with or without a window).
@@ -384,9 +238,7 @@ def flash_attn_func(q, k, v, causal=False, softmax_scale=None, cu_seqlens=None, 
         raise TypeError("q, k, v must share one dtype")
     _check_dev(q, k, v)
     if cu_seqlens is not None:
-        _check_dev(cu_seqlens)
-        if cu_seqlens.dtype != torch.int32:
-            raise TypeError("cu_seqlens must be int32")
+        _check_cu(cu_seqlens, T, N, validate)
     scale = softmax_scale if softmax_scale is not None else 1.0 / math.sqrt(d)
     o = torch.empty_like(q)
     lse = torch.empty((Hq, T), dtype=torch.float32, device=q.device)
@@ -429,7 +281,8 @@ def flash_attn_func(q, k, v, causal=False, softmax_scale=None, cu_seqlens=None, 
 
 
 def flash_attn_kvlen_func(q, k, v, causal=False, softmax_scale=None, cu_seqlens_q=None,
-                          cu_seqlens_k=None, max_seqlen_q=None, max_seqlen_k=None):
+                          cu_seqlens_k=None, max_seqlen_q=None, max_seqlen_k=None,
+                          validate=True):
     """Forward with queries and keys of different lengths (chunked prefill).
     Returns (o, lse); lse is float32 [Hq, Tq].
 
@@ -463,10 +316,8 @@ def flash_attn_kvlen_func(q, k, v, causal=False, softmax_scale=None, cu_seqlens_
         if k.shape[2] != d:
             raise ValueError(f"q {tuple(q.shape)} and k {tuple(k.shape)} do not match")
         B, Nq, Nk, Hkv = cu_seqlens_q.numel() - 1, int(max_seqlen_q), int(max_seqlen_k), k.shape[1]
-        for c in (cu_seqlens_q, cu_seqlens_k):
-            _check_dev(c)
-            if c.dtype != torch.int32:
-                raise TypeError("cu_seqlens must be int32")
+        _check_cu(cu_seqlens_q, Tq, Nq, validate, "cu_seqlens_q")
+        _check_cu(cu_seqlens_k, k.shape[0], Nk, validate, "cu_seqlens_k")
     _check_dev(q, k, v)
     scale = softmax_scale if softmax_scale is not None else 1.0 / math.sqrt(d)
     o = torch.empty_like(q)
@@ -482,7 +333,8 @@ def flash_attn_kvlen_func(q, k, v, causal=False, softmax_scale=None, cu_seqlens_
 
 
 def flash_attn_func_fp8(q, k, v, descale_q=1.0, descale_k=1.0, descale_v=1.0, causal=False,
-                        softmax_scale=None, cu_seqlens=None, max_seqlen=None, out_dtype=None):
+                        softmax_scale=None, cu_seqlens=None, max_seqlen=None, out_dtype=None,
+                        validate=True):
     """FP8 forward: q, k, v are e4m3fn codes (torch.float8_e4m3fn or uint8 tensors)
     with per-tensor descales (real value = code value × descale). Returns (o, lse):
     o in out_dtype (bfloat16 by default, or float16), lse float32 [Hq, T]."""
@@ -496,9 +348,7 @@ def flash_attn_func_fp8(q, k, v, descale_q=1.0, descale_k=1.0, descale_v=1.0, ca
             raise TypeError(f"fp8 inputs must be float8_e4m3fn or uint8 codes, got {t.dtype}")
     _check_dev(q, k, v)
     if cu_seqlens is not None:
-        _check_dev(cu_seqlens)
-        if cu_seqlens.dtype != torch.int32:
-            raise TypeError("cu_seqlens must be int32")
+        _check_cu(cu_seqlens, T, N, validate)
     scale = softmax_scale if softmax_scale is not None else 1.0 / math.sqrt(d)
     o = torch.empty(q.shape, dtype=out_dtype, device=q.device)
     lse = torch.empty((Hq, T), dtype=torch.float32, device=q.device)
@@ -513,14 +363,28 @@ def flash_attn_func_fp8(q, k, v, descale_q=1.0, descale_k=1.0, descale_v=1.0, ca
 
 def flash_attn_backward(dout, q, k, v, o, lse, causal=False, softmax_scale=None, cu_seqlens=None,
                         max_seqlen=None, workspace=None, window_size=(-1, -1), softcap=0.0,
-                        dropout_p=0.0, dropout_seed=None):
+                        dropout_p=0.0, dropout_seed=None, validate=True):
     """Backward. Returns (dq, dk, dv) shaped like q, k, v (window_size, softcap,
-    dropout_p and dropout_seed as in the forward, which produced o and lse)."""
+    dropout_p, dropout_seed, cu_seqlens and validate as in the forward, which
+    produced o and lse). workspace: optional device buffer of at least
+    fa_bwd_workspace_size(B, Hq, Hkv, N, d) bytes."""
     import torch
     B, N, T, Hq, Hkv, d = _shape(q, k, cu_seqlens, max_seqlen)
+    if v.shape != k.shape:
+        raise ValueError("k and v must have the same shape")
+    if not (q.dtype == k.dtype == v.dtype == o.dtype == dout.dtype):
+        raise TypeError("q, k, v, o and dout must share one dtype")
+    if o.shape != q.shape or dout.shape != q.shape:
+        raise ValueError(f"o {tuple(o.shape)} and dout {tuple(dout.shape)} must have q's shape "
+                         f"{tuple(q.shape)}")
+    if lse.dtype != torch.float32 or tuple(lse.shape) != (Hq, T):
+        raise ValueError(f"lse must be float32 of shape ({Hq}, {T}), got {lse.dtype} "
+                         f"{tuple(lse.shape)}")
     _check_dev(dout, q, k, v, o, lse)
     if cu_seqlens is not None:
-        _check_dev(cu_seqlens)
+        _check_cu(cu_seqlens, T, N, validate)
+    if workspace is not None:
+        _check_dev(workspace)
     scale = softmax_scale if softmax_scale is not None else 1.0 / math.sqrt(d)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     need = fa_bwd_workspace_size(B, Hq, Hkv, N, d)
@@ -534,30 +398,30 @@ def flash_attn_backward(dout, q, k, v, o, lse, causal=False, softmax_scale=None,
     if drop is not None:
         st = lib.fa_bwd_dropout(*ptrs, B, Hq, Hkv, N, d, float(scale), int(bool(causal)),
                                 drop[0], drop[1], cu, _dtype_code(q), workspace.data_ptr(),
-                                workspace.numel(), _stream())
+                                _nbytes(workspace), _stream())
         if st != FA_OK:
             raise FaError(st, "fa_bwd_dropout")
         return dq, dk, dv
     if softcap and w is not None:
         st = lib.fa_bwd_window_softcap(*ptrs, B, Hq, Hkv, N, d, float(scale), w[0], w[1],
                                        float(softcap), cu, _dtype_code(q), workspace.data_ptr(),
-                                       workspace.numel(), _stream())
+                                       _nbytes(workspace), _stream())
         if st != FA_OK:
             raise FaError(st, "fa_bwd_window_softcap")
         return dq, dk, dv
     if softcap:
         st = lib.fa_bwd_softcap(*ptrs, B, Hq, Hkv, N, d, float(scale), int(bool(causal)),
                                 float(softcap), cu, _dtype_code(q), workspace.data_ptr(),
-                                workspace.numel(), _stream())
+                                _nbytes(workspace), _stream())
         if st != FA_OK:
             raise FaError(st, "fa_bwd_softcap")
         return dq, dk, dv
     if w is None:
         st = lib.fa_bwd(*ptrs, B, Hq, Hkv, N, d, float(scale), int(bool(causal)), cu,
-                        _dtype_code(q), workspace.data_ptr(), workspace.numel(), _stream())
+                        _dtype_code(q), workspace.data_ptr(), _nbytes(workspace), _stream())
     else:
         st = lib.fa_bwd_window(*ptrs, B, Hq, Hkv, N, d, float(scale), w[0], w[1], cu,
-                               _dtype_code(q), workspace.data_ptr(), workspace.numel(),
+                               _dtype_code(q), workspace.data_ptr(), _nbytes(workspace),
                                _stream())
     if st != FA_OK:
         raise FaError(st, "fa_bwd" if w is None else "fa_bwd_window")
@@ -609,20 +473,20 @@ def flash_attn_with_kvcache(q, k_cache, v_cache, cache_seqlens, causal=False, so
         st = lib.fa_fwd_kvcache_local(*ptrs, B, Hq, Hkv, Nq, Nk, d, float(scale),
                                       int(bool(causal)), int(window_left), float(softcap),
                                       int(num_splits), _dtype_code(q), workspace.data_ptr(),
-                                      workspace.numel(), _stream())
+                                      _nbytes(workspace), _stream())
         if st != FA_OK:
             raise FaError(st, "fa_fwd_kvcache_local")
         return o, lse
     if kv8:
         st = lib.fa_fwd_kvcache_fp8(*ptrs, B, Hq, Hkv, Nq, Nk, d, float(scale), int(bool(causal)),
                                     float(descale_k), float(descale_v), int(num_splits),
-                                    _dtype_code(q), workspace.data_ptr(), workspace.numel(),
+                                    _dtype_code(q), workspace.data_ptr(), _nbytes(workspace),
                                     _stream())
         if st != FA_OK:
             raise FaError(st, "fa_fwd_kvcache_fp8")
         return o, lse
     st = lib.fa_fwd_kvcache(*ptrs, B, Hq, Hkv, Nq, Nk, d, float(scale), int(bool(causal)),
-                            int(num_splits), _dtype_code(q), workspace.data_ptr(), workspace.numel(),
+                            int(num_splits), _dtype_code(q), workspace.data_ptr(), _nbytes(workspace),
                             _stream())
     if st != FA_OK:
         raise FaError(st, "fa_fwd_kvcache")

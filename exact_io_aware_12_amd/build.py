@@ -33,15 +33,7 @@ def sources():
     return sorted(glob.glob(os.path.join(CSRC, "*.hip")))
 
 
-def build(resource_usage: bool = False, verbose: bool = False) -> str:
-    objs = []
-    tmp = LIB + ".tmp"
-    cmd = [hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
-           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-           "-I", os.path.join(ROOT, "include"), "-I", CSRC,
-           "-o", tmp] + sources()
-    if resource_usage:
-        cmd.insert(1, "-Rpass-analysis=kernel-resource-usage")
+def _run(cmd, verbose):
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -50,6 +42,31 @@ def build(resource_usage: bool = False, verbose: bool = False) -> str:
     msgs = "\n".join(line for line in (res.stdout + res.stderr).splitlines() if noise not in line)
     if res.returncode != 0:
         raise RuntimeError(f"hipcc failed ({res.returncode}):\n{msgs}")
+    return msgs
+
+
+def build(resource_usage: bool = False, verbose: bool = False) -> str:
+    """Compile every source to an object in parallel (each holds its kernels and
+    their launch code, so no device linking is needed), then link libfa.so."""
+    from concurrent.futures import ThreadPoolExecutor
+    tmpdir = os.path.join(HERE, "_build")
+    os.makedirs(tmpdir, exist_ok=True)
+    flags = [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
+             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+             "-I", os.path.join(ROOT, "include"), "-I", CSRC]
+    if resource_usage:
+        flags.insert(0, "-Rpass-analysis=kernel-resource-usage")
+    jobs = []
+    for src in sources():
+        obj = os.path.join(tmpdir, os.path.basename(src) + ".o")
+        jobs.append((obj, [hipcc()] + flags + ["-c", src, "-o", obj]))
+    workers = max(1, min(len(jobs), os.cpu_count() or 1, 8))
+    with ThreadPoolExecutor(workers) as ex:
+        outs = list(ex.map(lambda j: _run(j[1], verbose), jobs))
+    tmp = LIB + ".tmp"
+    outs.append(_run([hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] +
+                     [o for o, _ in jobs], verbose))
+    msgs = "\n".join(m for m in outs if m.strip())
     if msgs.strip() and (verbose or resource_usage):
         print(msgs)
     os.replace(tmp, LIB)

@@ -1,5 +1,7 @@
 // C ABI of libfa.so (declared in include/fa.h): argument checks, then the
-// kernel launches. Nothing here allocates memory or keeps state.
+// kernel launches. Nothing here allocates memory. The only global state is
+// the cache of the decode kernel's occupancy figures (decode_residency),
+// filled once per process with values that are the same for every caller.
 #include <algorithm>
 #include <atomic>
 #include <cmath>
@@ -132,7 +134,7 @@ int fwd_common(const void* q, const void* k, const void* v, void* o, float* lse,
 extern "C" {
 
 int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq,
-           int Hkv, int N, int d, float scale, int causal, const int32_t* cu_seqlens, int dtype,
+           int Hkv, int N, int d, float scale, int causal, const int32_t* cu_seqlens, fa_dtype dtype,
            hipStream_t stream) {
   if (causal != 0 && causal != 1) return FA_ERR_INVALID_ARG;
   return fwd_common(q, k, v, o, lse, B, Hq, Hkv, N, d, scale,
@@ -141,7 +143,7 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int
 
 int fa_fwd_kvlen(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq,
                  int Hkv, int Nq, int Nk, int d, float scale, int causal,
-                 const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int dtype,
+                 const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, fa_dtype dtype,
                  hipStream_t stream) {
   const bool varlen = cu_seqlens_q != nullptr;
   if (varlen != (cu_seqlens_k != nullptr)) return FA_ERR_INVALID_ARG;
@@ -185,7 +187,7 @@ int fa_fwd_kvlen(const void* q, const void* k, const void* v, void* o, float* ls
 
 int fa_fwd_softcap(const void* q, const void* k, const void* v, void* o, float* lse, int B,
                    int Hq, int Hkv, int N, int d, float scale, int causal, float softcap,
-                   const int32_t* cu_seqlens, int dtype, hipStream_t stream) {
+                   const int32_t* cu_seqlens, fa_dtype dtype, hipStream_t stream) {
   if (causal != 0 && causal != 1) return FA_ERR_INVALID_ARG;
   return fwd_common(q, k, v, o, lse, B, Hq, Hkv, N, d, scale,
                     causal ? fa::kMaskCausal : fa::kMaskNone, 0, 0, cu_seqlens, dtype, stream,
@@ -194,7 +196,7 @@ int fa_fwd_softcap(const void* q, const void* k, const void* v, void* o, float* 
 
 int fa_fwd_dropout(const void* q, const void* k, const void* v, void* o, float* lse, int B,
                    int Hq, int Hkv, int N, int d, float scale, int causal, float dropout_p,
-                   uint64_t seed, const int32_t* cu_seqlens, int dtype, hipStream_t stream) {
+                   uint64_t seed, const int32_t* cu_seqlens, fa_dtype dtype, hipStream_t stream) {
   if (causal != 0 && causal != 1) return FA_ERR_INVALID_ARG;
   return fwd_common(q, k, v, o, lse, B, Hq, Hkv, N, d, scale,
                     causal ? fa::kMaskCausal : fa::kMaskNone, 0, 0, cu_seqlens, dtype, stream, 0.f,
@@ -203,7 +205,7 @@ int fa_fwd_dropout(const void* q, const void* k, const void* v, void* o, float* 
 
 int fa_fwd_window_softcap(const void* q, const void* k, const void* v, void* o, float* lse,
                           int B, int Hq, int Hkv, int N, int d, float scale, int window_left,
-                          int window_right, float softcap, const int32_t* cu_seqlens, int dtype,
+                          int window_right, float softcap, const int32_t* cu_seqlens, fa_dtype dtype,
                           hipStream_t stream) {
   int mask, wl, wr;
   const int st = window_mode(window_left, window_right, N, &mask, &wl, &wr);
@@ -214,7 +216,7 @@ int fa_fwd_window_softcap(const void* q, const void* k, const void* v, void* o, 
 
 int fa_fwd_window(const void* q, const void* k, const void* v, void* o, float* lse, int B,
                   int Hq, int Hkv, int N, int d, float scale, int window_left, int window_right,
-                  const int32_t* cu_seqlens, int dtype, hipStream_t stream) {
+                  const int32_t* cu_seqlens, fa_dtype dtype, hipStream_t stream) {
   int mask, wl, wr;
   const int st = window_mode(window_left, window_right, N, &mask, &wl, &wr);
   if (st != FA_OK) return st;
@@ -224,7 +226,7 @@ int fa_fwd_window(const void* q, const void* k, const void* v, void* o, float* l
 
 int fa_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq,
                int Hkv, int N, int d, float scale, int causal, const int32_t* cu_seqlens,
-               float descale_q, float descale_k, float descale_v, int out_dtype,
+               float descale_q, float descale_k, float descale_v, fa_dtype out_dtype,
                hipStream_t stream) {
   bool noop;
   int st = check_sizes(B, Hq, Hkv, N, d, scale, causal, out_dtype, &noop);
@@ -331,7 +333,7 @@ int bwd_common(int stage, const void* q, const void* k, const void* v, const voi
 
 int fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
            const float* lse, void* dq, void* dk, void* dv, int B, int Hq, int Hkv, int N, int d,
-           float scale, int causal, const int32_t* cu_seqlens, int dtype, void* workspace,
+           float scale, int causal, const int32_t* cu_seqlens, fa_dtype dtype, void* workspace,
            size_t workspace_bytes, hipStream_t stream) {
   if (causal != 0 && causal != 1) return FA_ERR_INVALID_ARG;
   return bwd_common(-1, q, k, v, o, dout, lse, dq, dk, dv, B, Hq, Hkv, N, d, scale,
@@ -342,7 +344,7 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const voi
 int fa_bwd_window(const void* q, const void* k, const void* v, const void* o, const void* dout,
                   const float* lse, void* dq, void* dk, void* dv, int B, int Hq, int Hkv, int N,
                   int d, float scale, int window_left, int window_right,
-                  const int32_t* cu_seqlens, int dtype, void* workspace, size_t workspace_bytes,
+                  const int32_t* cu_seqlens, fa_dtype dtype, void* workspace, size_t workspace_bytes,
                   hipStream_t stream) {
   return fa_bwd_window_stage(-1, q, k, v, o, dout, lse, dq, dk, dv, B, Hq, Hkv, N, d, scale,
                              window_left, window_right, cu_seqlens, dtype, workspace,
@@ -352,7 +354,7 @@ int fa_bwd_window(const void* q, const void* k, const void* v, const void* o, co
 int fa_bwd_window_stage(int stage, const void* q, const void* k, const void* v, const void* o,
                         const void* dout, const float* lse, void* dq, void* dk, void* dv, int B,
                         int Hq, int Hkv, int N, int d, float scale, int window_left,
-                        int window_right, const int32_t* cu_seqlens, int dtype, void* workspace,
+                        int window_right, const int32_t* cu_seqlens, fa_dtype dtype, void* workspace,
                         size_t workspace_bytes, hipStream_t stream) {
   if (stage < -1 || stage >= fa::bwd_num_stages()) return FA_ERR_INVALID_ARG;
   int mask, wl, wr;
@@ -366,7 +368,7 @@ int fa_bwd_window_softcap_stage(int stage, const void* q, const void* k, const v
                                 const void* o, const void* dout, const float* lse, void* dq,
                                 void* dk, void* dv, int B, int Hq, int Hkv, int N, int d,
                                 float scale, int window_left, int window_right, float softcap,
-                                const int32_t* cu_seqlens, int dtype, void* workspace,
+                                const int32_t* cu_seqlens, fa_dtype dtype, void* workspace,
                                 size_t workspace_bytes, hipStream_t stream) {
   if (stage < -1 || stage >= fa::bwd_num_stages()) return FA_ERR_INVALID_ARG;
   int mask, wl, wr;
@@ -379,7 +381,7 @@ int fa_bwd_window_softcap_stage(int stage, const void* q, const void* k, const v
 int fa_bwd_window_softcap(const void* q, const void* k, const void* v, const void* o,
                           const void* dout, const float* lse, void* dq, void* dk, void* dv,
                           int B, int Hq, int Hkv, int N, int d, float scale, int window_left,
-                          int window_right, float softcap, const int32_t* cu_seqlens, int dtype,
+                          int window_right, float softcap, const int32_t* cu_seqlens, fa_dtype dtype,
                           void* workspace, size_t workspace_bytes, hipStream_t stream) {
   return fa_bwd_window_softcap_stage(-1, q, k, v, o, dout, lse, dq, dk, dv, B, Hq, Hkv, N, d,
                                      scale, window_left, window_right, softcap, cu_seqlens, dtype,
@@ -389,7 +391,7 @@ int fa_bwd_window_softcap(const void* q, const void* k, const void* v, const voi
 int fa_bwd_softcap(const void* q, const void* k, const void* v, const void* o, const void* dout,
                    const float* lse, void* dq, void* dk, void* dv, int B, int Hq, int Hkv, int N,
                    int d, float scale, int causal, float softcap, const int32_t* cu_seqlens,
-                   int dtype, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+                   fa_dtype dtype, void* workspace, size_t workspace_bytes, hipStream_t stream) {
   return fa_bwd_softcap_stage(-1, q, k, v, o, dout, lse, dq, dk, dv, B, Hq, Hkv, N, d, scale,
                               causal, softcap, cu_seqlens, dtype, workspace, workspace_bytes,
                               stream);
@@ -398,7 +400,7 @@ int fa_bwd_softcap(const void* q, const void* k, const void* v, const void* o, c
 int fa_bwd_softcap_stage(int stage, const void* q, const void* k, const void* v, const void* o,
                          const void* dout, const float* lse, void* dq, void* dk, void* dv, int B,
                          int Hq, int Hkv, int N, int d, float scale, int causal, float softcap,
-                         const int32_t* cu_seqlens, int dtype, void* workspace,
+                         const int32_t* cu_seqlens, fa_dtype dtype, void* workspace,
                          size_t workspace_bytes, hipStream_t stream) {
   if (stage < -1 || stage >= fa::bwd_num_stages()) return FA_ERR_INVALID_ARG;
   if (causal != 0 && causal != 1) return FA_ERR_INVALID_ARG;
@@ -410,7 +412,7 @@ int fa_bwd_softcap_stage(int stage, const void* q, const void* k, const void* v,
 int fa_bwd_dropout(const void* q, const void* k, const void* v, const void* o, const void* dout,
                    const float* lse, void* dq, void* dk, void* dv, int B, int Hq, int Hkv, int N,
                    int d, float scale, int causal, float dropout_p, uint64_t seed,
-                   const int32_t* cu_seqlens, int dtype, void* workspace, size_t workspace_bytes,
+                   const int32_t* cu_seqlens, fa_dtype dtype, void* workspace, size_t workspace_bytes,
                    hipStream_t stream) {
   return fa_bwd_dropout_stage(-1, q, k, v, o, dout, lse, dq, dk, dv, B, Hq, Hkv, N, d, scale,
                               causal, dropout_p, seed, cu_seqlens, dtype, workspace,
@@ -420,7 +422,7 @@ int fa_bwd_dropout(const void* q, const void* k, const void* v, const void* o, c
 int fa_bwd_dropout_stage(int stage, const void* q, const void* k, const void* v, const void* o,
                          const void* dout, const float* lse, void* dq, void* dk, void* dv, int B,
                          int Hq, int Hkv, int N, int d, float scale, int causal, float dropout_p,
-                         uint64_t seed, const int32_t* cu_seqlens, int dtype, void* workspace,
+                         uint64_t seed, const int32_t* cu_seqlens, fa_dtype dtype, void* workspace,
                          size_t workspace_bytes, hipStream_t stream) {
   if (stage < -1 || stage >= fa::bwd_num_stages()) return FA_ERR_INVALID_ARG;
   if (causal != 0 && causal != 1) return FA_ERR_INVALID_ARG;
@@ -434,7 +436,7 @@ int fa_bwd_num_stages(void) { return fa::bwd_num_stages(); }
 int fa_bwd_stage(int stage, const void* q, const void* k, const void* v, const void* o,
                  const void* dout, const float* lse, void* dq, void* dk, void* dv, int B, int Hq,
                  int Hkv, int N, int d, float scale, int causal, const int32_t* cu_seqlens,
-                 int dtype, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+                 fa_dtype dtype, void* workspace, size_t workspace_bytes, hipStream_t stream) {
   if (stage < 0 || stage >= fa::bwd_num_stages()) return FA_ERR_INVALID_ARG;
   if (causal != 0 && causal != 1) return FA_ERR_INVALID_ARG;
   return bwd_common(stage, q, k, v, o, dout, lse, dq, dk, dv, B, Hq, Hkv, N, d, scale,
@@ -606,7 +608,7 @@ int kvcache_common(int stage, const void* q, const void* k_cache, const void* v_
 
 int fa_fwd_kvcache(const void* q, const void* k_cache, const void* v_cache,
                    const int32_t* cache_seqlens, void* o, float* lse, int B, int Hq, int Hkv,
-                   int Nq, int Nk, int d, float scale, int causal, int num_splits, int dtype,
+                   int Nq, int Nk, int d, float scale, int causal, int num_splits, fa_dtype dtype,
                    void* workspace, size_t workspace_bytes, hipStream_t stream) {
   return kvcache_common(-1, q, k_cache, v_cache, cache_seqlens, o, lse, B, Hq, Hkv, Nq, Nk, d,
                         scale, causal, num_splits, dtype, workspace, workspace_bytes, stream);
@@ -617,7 +619,7 @@ int fa_fwd_kvcache_num_stages(void) { return fa::decode_num_stages(); }
 int fa_fwd_kvcache_stage(int stage, const void* q, const void* k_cache, const void* v_cache,
                          const int32_t* cache_seqlens, void* o, float* lse, int B, int Hq,
                          int Hkv, int Nq, int Nk, int d, float scale, int causal, int num_splits,
-                         int dtype, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+                         fa_dtype dtype, void* workspace, size_t workspace_bytes, hipStream_t stream) {
   if (stage < 0 || stage >= fa::decode_num_stages()) return FA_ERR_INVALID_ARG;
   return kvcache_common(stage, q, k_cache, v_cache, cache_seqlens, o, lse, B, Hq, Hkv, Nq, Nk, d,
                         scale, causal, num_splits, dtype, workspace, workspace_bytes, stream);
@@ -626,7 +628,7 @@ int fa_fwd_kvcache_stage(int stage, const void* q, const void* k_cache, const vo
 int fa_fwd_kvcache_local(const void* q, const void* k_cache, const void* v_cache,
                          const int32_t* cache_seqlens, void* o, float* lse, int B, int Hq,
                          int Hkv, int Nq, int Nk, int d, float scale, int causal,
-                         int window_left, float softcap, int num_splits, int dtype,
+                         int window_left, float softcap, int num_splits, fa_dtype dtype,
                          void* workspace, size_t workspace_bytes, hipStream_t stream) {
   bool noop;
   int st = check_kvcache(B, Hq, Hkv, Nq, Nk, d, scale, causal, num_splits, dtype, &noop);
@@ -687,7 +689,7 @@ int fa_fwd_kvcache_local(const void* q, const void* k_cache, const void* v_cache
 int fa_fwd_kvcache_fp8(const void* q, const void* k_cache, const void* v_cache,
                        const int32_t* cache_seqlens, void* o, float* lse, int B, int Hq, int Hkv,
                        int Nq, int Nk, int d, float scale, int causal, float descale_k,
-                       float descale_v, int num_splits, int dtype, void* workspace,
+                       float descale_v, int num_splits, fa_dtype dtype, void* workspace,
                        size_t workspace_bytes, hipStream_t stream) {
   return kvcache_common(-1, q, k_cache, v_cache, cache_seqlens, o, lse, B, Hq, Hkv, Nq, Nk, d,
                         scale, causal, num_splits, dtype, workspace, workspace_bytes, stream, true,
@@ -697,7 +699,7 @@ int fa_fwd_kvcache_fp8(const void* q, const void* k_cache, const void* v_cache,
 int fa_fwd_kvcache_fp8_stage(int stage, const void* q, const void* k_cache, const void* v_cache,
                              const int32_t* cache_seqlens, void* o, float* lse, int B, int Hq,
                              int Hkv, int Nq, int Nk, int d, float scale, int causal,
-                             float descale_k, float descale_v, int num_splits, int dtype,
+                             float descale_k, float descale_v, int num_splits, fa_dtype dtype,
                              void* workspace, size_t workspace_bytes, hipStream_t stream) {
   if (stage < 0 || stage >= fa::decode_num_stages()) return FA_ERR_INVALID_ARG;
   return kvcache_common(stage, q, k_cache, v_cache, cache_seqlens, o, lse, B, Hq, Hkv, Nq, Nk, d,

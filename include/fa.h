@@ -78,7 +78,13 @@ typedef enum {
   FA_ERR_WORKSPACE = -4     /* workspace missing or smaller than the size function returns */
 } fa_status;
 
-typedef enum { FA_FP16 = 0, FA_BF16 = 1 } fa_dtype;
+typedef enum {
+  FA_FP16 = 0,
+  FA_BF16 = 1,
+  FA_DTYPE_FORCE_INT = 0x7fffffff  /* not a dtype: keeps fa_dtype an int-sized type whose
+                                      range covers any int, so a bad code is rejected
+                                      (FA_ERR_INVALID_ARG) rather than undefined */
+} fa_dtype;
 
 /*
  * Forward: o = softmax(q·kᵀ·scale [causal])·v and lse = ln Σ_j exp(scale·q·k_j)
@@ -88,7 +94,7 @@ typedef enum { FA_FP16 = 0, FA_BF16 = 1 } fa_dtype;
  */
 int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
            int B, int Hq, int Hkv, int N, int d, float scale, int causal,
-           const int32_t* cu_seqlens, int dtype, hipStream_t stream);
+           const int32_t* cu_seqlens, fa_dtype dtype, hipStream_t stream);
 
 /*
  * Backward of fa_fwd for the upstream gradient `dout`, given the forward's
@@ -102,7 +108,7 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
 int fa_bwd(const void* q, const void* k, const void* v, const void* o,
            const void* dout, const float* lse, void* dq, void* dk, void* dv,
            int B, int Hq, int Hkv, int N, int d, float scale, int causal,
-           const int32_t* cu_seqlens, int dtype,
+           const int32_t* cu_seqlens, fa_dtype dtype,
            void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
@@ -119,7 +125,7 @@ int fa_bwd_num_stages(void);
 int fa_bwd_stage(int stage, const void* q, const void* k, const void* v, const void* o,
                  const void* dout, const float* lse, void* dq, void* dk, void* dv,
                  int B, int Hq, int Hkv, int N, int d, float scale, int causal,
-                 const int32_t* cu_seqlens, int dtype,
+                 const int32_t* cu_seqlens, fa_dtype dtype,
                  void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* Workspace bytes fa_bwd needs; an upper bound that uses T <= B·N. 0 on bad sizes. */
@@ -144,18 +150,18 @@ size_t fa_bwd_workspace_size(int B, int Hq, int Hkv, int N, int d);
 int fa_fwd_window(const void* q, const void* k, const void* v, void* o, float* lse,
                   int B, int Hq, int Hkv, int N, int d, float scale,
                   int window_left, int window_right,
-                  const int32_t* cu_seqlens, int dtype, hipStream_t stream);
+                  const int32_t* cu_seqlens, fa_dtype dtype, hipStream_t stream);
 int fa_bwd_window(const void* q, const void* k, const void* v, const void* o,
                   const void* dout, const float* lse, void* dq, void* dk, void* dv,
                   int B, int Hq, int Hkv, int N, int d, float scale,
                   int window_left, int window_right,
-                  const int32_t* cu_seqlens, int dtype,
+                  const int32_t* cu_seqlens, fa_dtype dtype,
                   void* workspace, size_t workspace_bytes, hipStream_t stream);
 int fa_bwd_window_stage(int stage, const void* q, const void* k, const void* v, const void* o,
                         const void* dout, const float* lse, void* dq, void* dk, void* dv,
                         int B, int Hq, int Hkv, int N, int d, float scale,
                         int window_left, int window_right,
-                        const int32_t* cu_seqlens, int dtype,
+                        const int32_t* cu_seqlens, fa_dtype dtype,
                         void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
@@ -176,16 +182,16 @@ int fa_bwd_window_stage(int stage, const void* q, const void* k, const void* v, 
  */
 int fa_fwd_softcap(const void* q, const void* k, const void* v, void* o, float* lse,
                    int B, int Hq, int Hkv, int N, int d, float scale, int causal, float softcap,
-                   const int32_t* cu_seqlens, int dtype, hipStream_t stream);
+                   const int32_t* cu_seqlens, fa_dtype dtype, hipStream_t stream);
 int fa_bwd_softcap(const void* q, const void* k, const void* v, const void* o,
                    const void* dout, const float* lse, void* dq, void* dk, void* dv,
                    int B, int Hq, int Hkv, int N, int d, float scale, int causal, float softcap,
-                   const int32_t* cu_seqlens, int dtype,
+                   const int32_t* cu_seqlens, fa_dtype dtype,
                    void* workspace, size_t workspace_bytes, hipStream_t stream);
 int fa_bwd_softcap_stage(int stage, const void* q, const void* k, const void* v, const void* o,
                          const void* dout, const float* lse, void* dq, void* dk, void* dv,
                          int B, int Hq, int Hkv, int N, int d, float scale, int causal,
-                         float softcap, const int32_t* cu_seqlens, int dtype,
+                         float softcap, const int32_t* cu_seqlens, fa_dtype dtype,
                          void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
@@ -198,18 +204,18 @@ int fa_bwd_softcap_stage(int stage, const void* q, const void* k, const void* v,
  */
 int fa_fwd_window_softcap(const void* q, const void* k, const void* v, void* o, float* lse,
                           int B, int Hq, int Hkv, int N, int d, float scale, int window_left,
-                          int window_right, float softcap, const int32_t* cu_seqlens, int dtype,
+                          int window_right, float softcap, const int32_t* cu_seqlens, fa_dtype dtype,
                           hipStream_t stream);
 int fa_bwd_window_softcap(const void* q, const void* k, const void* v, const void* o,
                           const void* dout, const float* lse, void* dq, void* dk, void* dv,
                           int B, int Hq, int Hkv, int N, int d, float scale, int window_left,
-                          int window_right, float softcap, const int32_t* cu_seqlens, int dtype,
+                          int window_right, float softcap, const int32_t* cu_seqlens, fa_dtype dtype,
                           void* workspace, size_t workspace_bytes, hipStream_t stream);
 int fa_bwd_window_softcap_stage(int stage, const void* q, const void* k, const void* v,
                                 const void* o, const void* dout, const float* lse, void* dq,
                                 void* dk, void* dv, int B, int Hq, int Hkv, int N, int d,
                                 float scale, int window_left, int window_right, float softcap,
-                                const int32_t* cu_seqlens, int dtype, void* workspace,
+                                const int32_t* cu_seqlens, fa_dtype dtype, void* workspace,
                                 size_t workspace_bytes, hipStream_t stream);
 
 
@@ -235,16 +241,16 @@ int fa_bwd_window_softcap_stage(int stage, const void* q, const void* k, const v
 int fa_fwd_dropout(const void* q, const void* k, const void* v, void* o, float* lse,
                    int B, int Hq, int Hkv, int N, int d, float scale, int causal,
                    float dropout_p, uint64_t seed,
-                   const int32_t* cu_seqlens, int dtype, hipStream_t stream);
+                   const int32_t* cu_seqlens, fa_dtype dtype, hipStream_t stream);
 int fa_bwd_dropout(const void* q, const void* k, const void* v, const void* o,
                    const void* dout, const float* lse, void* dq, void* dk, void* dv,
                    int B, int Hq, int Hkv, int N, int d, float scale, int causal,
-                   float dropout_p, uint64_t seed, const int32_t* cu_seqlens, int dtype,
+                   float dropout_p, uint64_t seed, const int32_t* cu_seqlens, fa_dtype dtype,
                    void* workspace, size_t workspace_bytes, hipStream_t stream);
 int fa_bwd_dropout_stage(int stage, const void* q, const void* k, const void* v, const void* o,
                          const void* dout, const float* lse, void* dq, void* dk, void* dv,
                          int B, int Hq, int Hkv, int N, int d, float scale, int causal,
-                         float dropout_p, uint64_t seed, const int32_t* cu_seqlens, int dtype,
+                         float dropout_p, uint64_t seed, const int32_t* cu_seqlens, fa_dtype dtype,
                          void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
@@ -267,7 +273,7 @@ int fa_bwd_dropout_stage(int stage, const void* q, const void* k, const void* v,
  */
 int fa_fwd_kvlen(const void* q, const void* k, const void* v, void* o, float* lse,
                  int B, int Hq, int Hkv, int Nq, int Nk, int d, float scale, int causal,
-                 const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int dtype,
+                 const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, fa_dtype dtype,
                  hipStream_t stream);
 
 /*
@@ -291,7 +297,7 @@ int fa_fwd_kvlen(const void* q, const void* k, const void* v, void* o, float* ls
 int fa_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse,
                int B, int Hq, int Hkv, int N, int d, float scale, int causal,
                const int32_t* cu_seqlens, float descale_q, float descale_k, float descale_v,
-               int out_dtype, hipStream_t stream);
+               fa_dtype out_dtype, hipStream_t stream);
 
 /*
  * Decode: attention of Nq new queries per batch entry over a key/value cache
@@ -320,7 +326,7 @@ int fa_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse,
 int fa_fwd_kvcache(const void* q, const void* k_cache, const void* v_cache,
                    const int32_t* cache_seqlens, void* o, float* lse,
                    int B, int Hq, int Hkv, int Nq, int Nk, int d, float scale, int causal,
-                   int num_splits, int dtype, void* workspace, size_t workspace_bytes,
+                   int num_splits, fa_dtype dtype, void* workspace, size_t workspace_bytes,
                    hipStream_t stream);
 
 /*
@@ -335,7 +341,7 @@ int fa_fwd_kvcache_num_stages(void);
 int fa_fwd_kvcache_stage(int stage, const void* q, const void* k_cache, const void* v_cache,
                          const int32_t* cache_seqlens, void* o, float* lse,
                          int B, int Hq, int Hkv, int Nq, int Nk, int d, float scale, int causal,
-                         int num_splits, int dtype, void* workspace, size_t workspace_bytes,
+                         int num_splits, fa_dtype dtype, void* workspace, size_t workspace_bytes,
                          hipStream_t stream);
 
 /*
@@ -357,7 +363,7 @@ int fa_fwd_kvcache_stage(int stage, const void* q, const void* k_cache, const vo
 int fa_fwd_kvcache_local(const void* q, const void* k_cache, const void* v_cache,
                          const int32_t* cache_seqlens, void* o, float* lse,
                          int B, int Hq, int Hkv, int Nq, int Nk, int d, float scale, int causal,
-                         int window_left, float softcap, int num_splits, int dtype,
+                         int window_left, float softcap, int num_splits, fa_dtype dtype,
                          void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
@@ -379,13 +385,13 @@ int fa_fwd_kvcache_local(const void* q, const void* k_cache, const void* v_cache
 int fa_fwd_kvcache_fp8(const void* q, const void* k_cache, const void* v_cache,
                        const int32_t* cache_seqlens, void* o, float* lse,
                        int B, int Hq, int Hkv, int Nq, int Nk, int d, float scale, int causal,
-                       float descale_k, float descale_v, int num_splits, int dtype,
+                       float descale_k, float descale_v, int num_splits, fa_dtype dtype,
                        void* workspace, size_t workspace_bytes, hipStream_t stream);
 int fa_fwd_kvcache_fp8_stage(int stage, const void* q, const void* k_cache, const void* v_cache,
                              const int32_t* cache_seqlens, void* o, float* lse,
                              int B, int Hq, int Hkv, int Nq, int Nk, int d, float scale,
                              int causal, float descale_k, float descale_v, int num_splits,
-                             int dtype, void* workspace, size_t workspace_bytes,
+                             fa_dtype dtype, void* workspace, size_t workspace_bytes,
                              hipStream_t stream);
 
 /* The key-range count fa_fwd_kvcache uses for num_splits = 0 (>= 1); 0 on bad sizes.

@@ -42,6 +42,60 @@ def test_every_declared_symbol_is_exported():
         assert hasattr(lib, name), name
 
 
+def declared_prototypes():
+    """{name: (return type, [parameter types])} from include/fa.h."""
+    text = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    protos = {}
+    for m in re.finditer(r"^\s*((?:const\s+)?\w+\s*\**)\s*(fa_\w+)\s*\(([^)]*)\)\s*;", text,
+                         flags=re.M):
+        params = [p.strip() for p in m.group(3).split(",")]
+        types = [] if params == ["void"] else [re.sub(r"\s*\b\w+$", "", p).strip() for p in params]
+        protos[m.group(2)] = (m.group(1).strip(), types)
+    return protos
+
+
+def test_binding_prototypes_match_the_header():
+    """Every ctypes signature the binding sets equals the C prototype in
+    include/fa.h, parameter by parameter; the dtype arguments are fa_dtype."""
+    C = {"int": ctypes.c_int, "fa_dtype": ctypes.c_int, "float": ctypes.c_float,
+         "size_t": ctypes.c_size_t, "uint64_t": ctypes.c_uint64, "hipStream_t": ctypes.c_void_p,
+         "const char*": ctypes.c_char_p}
+    protos = declared_prototypes()
+    assert sorted(protos) == declared_functions()
+    for name, (ret, params) in protos.items():
+        fn = getattr(fa.lib, name)
+        assert fn.restype is C[ret], (name, ret)
+        want = [ctypes.c_void_p if p.endswith("*") else C[p] for p in params]
+        assert list(fn.argtypes) == want, (name, params)
+        for p, orig in zip(params, re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+                           .split(name + "(", 1)[1].split(")", 1)[0].split(",")):
+            if re.search(r"\b(dtype|out_dtype)\s*$", orig.strip()):
+                assert p == "fa_dtype", (name, orig)
+
+
+def test_binding_loads_torch_hip_runtime_first():
+    """The binding imports torch before it loads libfa.so, so the library binds to
+    torch's HIP runtime (a second runtime could not see torch's memory). In a fresh
+    interpreter, importing the binding leaves exactly one libamdhip64 mapped, and
+    it is torch's."""
+    import subprocess
+    import sys
+    code = ("import exact_io_aware_12_amd, torch, os\n"
+            "maps = open('/proc/self/maps').read().split('\\n')\n"
+            "libs = sorted({l.split()[-1] for l in maps if 'libamdhip64' in l})\n"
+            "print(len(libs), int(os.path.dirname(torch.__file__) in libs[0]))\n")
+    out = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, cwd=ROOT,
+                         timeout=300)
+    assert out.returncode == 0, out.stderr
+    assert out.stdout.split() == ["1", "1"], out.stdout
+
+
+def test_binding_source_imports_torch_before_loading():
+    src = open(os.path.join(ROOT, "exact_io_aware_12_amd", "__init__.py")).read()
+    body = src[src.index("def _load():"):]
+    assert body.index("import torch") < body.index("ctypes.CDLL(")
+
+
 def test_status_strings():
     for code in (0, -1, -2, -3, -4):
         assert fa.fa_status_string(code).startswith(
@@ -642,3 +696,46 @@ def test_bwd_d256_reaches_the_launch():
     assert bwd(d=256) == fa.FA_ERR_HIP
     assert bwd(d=256, causal=1) == fa.FA_ERR_HIP
     assert bwdw(d=256) == fa.FA_ERR_HIP
+
+
+def _bwd_tensors(dtype="bf16", T=8, Hq=2, Hkv=1, d=64):
+    import torch
+    dt = {"bf16": torch.bfloat16, "fp16": torch.float16}[dtype]
+    q = torch.zeros(1, T, Hq, d, dtype=dt)
+    k = torch.zeros(1, T, Hkv, d, dtype=dt)
+    return dict(dout=q.clone(), q=q, k=k, v=k.clone(), o=q.clone(),
+                lse=torch.zeros(Hq, T, dtype=torch.float32))
+
+
+@pytest.mark.parametrize("bad", ["dout_dtype", "o_dtype", "dout_shape", "lse_dtype", "lse_shape",
+                                 "v_shape", "k_dtype"])
+def test_binding_backward_rejects_bad_tensors(bad):
+    """flash_attn_backward checks every tensor's dtype and shape before it looks
+    at devices or launches anything (these are CPU tensors: a launch would fail)."""
+    import torch
+    t = _bwd_tensors()
+    if bad == "dout_dtype":
+        t["dout"] = t["dout"].float()
+    elif bad == "o_dtype":
+        t["o"] = t["o"].half()
+    elif bad == "dout_shape":
+        t["dout"] = t["dout"][:, :4]
+    elif bad == "lse_dtype":
+        t["lse"] = t["lse"].double()
+    elif bad == "lse_shape":
+        t["lse"] = t["lse"][:, :4]
+    elif bad == "v_shape":
+        t["v"] = torch.zeros(1, 8, 2, 64, dtype=torch.bfloat16)
+    elif bad == "k_dtype":
+        t["k"] = t["k"].half()
+    with pytest.raises((TypeError, ValueError)):
+        fa.flash_attn_backward(t["dout"], t["q"], t["k"], t["v"], t["o"], t["lse"], causal=True)
+
+
+def test_binding_forward_rejects_mixed_dtypes_and_shapes():
+    import torch
+    q = torch.zeros(1, 8, 2, 64, dtype=torch.bfloat16)
+    with pytest.raises(TypeError):
+        fa.flash_attn_func(q, q.half(), q)
+    with pytest.raises(ValueError):
+        fa.flash_attn_func(q, q, q[:, :4])

@@ -124,7 +124,7 @@ def test_stress_inputs(kind):
     compare_whole(w, stress_arrays(w, kind))
 
 
-# ---- the 256-row kernel for long sequences (d = 128, N >= 2048) --------------
+# ---- long ragged sequences (d = 128, N >= 2048: many key tiles, ragged ends) ---
 @pytest.mark.parametrize("dtype", ["fp16", "bf16"])
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("N", [2048, 2111, 2367])
@@ -137,8 +137,9 @@ def test_long_ragged(dtype, causal, N):
 @pytest.mark.parametrize("kind", STRESS)
 @pytest.mark.parametrize("causal", [False, True])
 def test_long_stress(dtype, kind, causal):
-    """Stress inputs through the long-sequence kernel; 'steep_max' forces the
-    workgroup to redo its tiles with rescaling (in both fp16 and bf16)."""
+    """Stress inputs over many key tiles; 'steep_max' raises the row maximum in
+    every tile, so the lazily raised reference max is rescaled again and again
+    (in both fp16 and bf16)."""
     w = W.custom(B=1, Hq=2, Hkv=2, N=2100, d=128, dtype=dtype, causal=causal, seed=19)
     compare_whole(w, stress_arrays(w, kind))
 
