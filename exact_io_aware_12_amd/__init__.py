@@ -60,6 +60,7 @@ _SIGS = {
     "fa_bwd": (_I, _BWD_HEAD + [_I] + _BWD_TAIL),
     "fa_bwd_num_stages": (_I, []),
     "fa_bwd_workspace_size": (_SZ, [_I] * 5),
+    "fa_bwd_noalloc": (_I, _BWD_HEAD + [_I, _VP, _I, _VP]),
     "fa_fwd_window": (_I, _FWD_HEAD + [_I, _I, _VP, _I, _VP]),
     "fa_bwd_window": (_I, _BWD_HEAD + [_I, _I] + _BWD_TAIL),
     "fa_fwd_window_softcap": (_I, _FWD_HEAD + [_I, _I, _F, _VP, _I, _VP]),

@@ -4,6 +4,7 @@
 // filled once per process with values that are the same for every caller.
 #include <algorithm>
 #include <atomic>
+#include <mutex>
 #include <cmath>
 #include <cstdint>
 
@@ -339,6 +340,61 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const voi
   return bwd_common(-1, q, k, v, o, dout, lse, dq, dk, dv, B, Hq, Hkv, N, d, scale,
                     causal ? fa::kMaskCausal : fa::kMaskNone, 0, 0, cu_seqlens, dtype, workspace,
                     workspace_bytes, stream);
+}
+
+}  // extern "C"
+
+// Scratch of fa_bwd_noalloc: the backward's workspace (D and LSE·log2 e) in a
+// fixed device array, so that a call needs no allocation. Every GPU the library
+// runs on holds its own copy from module load until the process ends. In host
+// code `scratch` names a host-side stand-in, not the device array: the device
+// address comes from hipGetSymbolAddress, once per device.
+static __device__ __align__(256) unsigned char scratch[FA_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr size_t kScratchBytes = FA_NOALLOC_SCRATCH_BYTES;
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch_ptr[kMaxDevices];
+std::mutex g_scratch_mu;
+
+// The current device's address of `scratch`, or nullptr (no device, or the
+// runtime refused the lookup).
+void* scratch_ptr() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (p) return p;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+  if (!p) {
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess) p = nullptr;
+    if (p) g_scratch_ptr[dev].store(p, std::memory_order_release);
+  }
+  return p;
+}
+
+}  // namespace
+
+extern "C" {
+
+int fa_bwd_noalloc(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                   const float* lse, void* dq, void* dk, void* dv, int B, int Hq, int Hkv, int N,
+                   int d, float scale, int causal, const int32_t* cu_seqlens, fa_dtype dtype,
+                   hipStream_t stream) {
+  if (causal != 0 && causal != 1) return FA_ERR_INVALID_ARG;
+  bool noop;
+  int st = check_sizes(B, Hq, Hkv, N, d, scale, causal, dtype, &noop, 256);
+  if (st != FA_OK || noop) return st;
+  if (fa_bwd_workspace_size(B, Hq, Hkv, N, d) > kScratchBytes) return FA_ERR_WORKSPACE;
+  void* ws = scratch_ptr();
+  if (!ws) {
+    (void)hipGetLastError();
+    return FA_ERR_HIP;
+  }
+  return bwd_common(-1, q, k, v, o, dout, lse, dq, dk, dv, B, Hq, Hkv, N, d, scale,
+                    causal ? fa::kMaskCausal : fa::kMaskNone, 0, 0, cu_seqlens, dtype, ws,
+                    kScratchBytes, stream);
 }
 
 int fa_bwd_window(const void* q, const void* k, const void* v, const void* o, const void* dout,

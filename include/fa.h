@@ -132,6 +132,31 @@ int fa_bwd_stage(int stage, const void* q, const void* k, const void* v, const v
 size_t fa_bwd_workspace_size(int B, int Hq, int Hkv, int N, int d);
 
 /*
+ * Allocation-free backward, for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): fa_bwd with the same arguments and results, minus the
+ * workspace. The workspace lives in a fixed device array inside the library,
+ * FA_NOALLOC_SCRATCH_BYTES large, one per GPU, held from the library's first
+ * use on that GPU until the process ends; its address is looked up once per
+ * device on the first call there. The call itself allocates nothing.
+ *   Limit: fa_bwd_workspace_size(B, Hq, Hkv, N, d) <= FA_NOALLOC_SCRATCH_BYTES,
+ *          i.e. Hq·(B·N + 64) <= 4,194,304; larger sizes return
+ *          FA_ERR_WORKSPACE before anything is enqueued (use fa_bwd then).
+ *   Concurrency: every call on one GPU shares that GPU's array, so calls
+ *          that overlap on one GPU (different streams, or threads without
+ *          ordering) race and may give wrong results; calls ordered on one
+ *          stream are safe. The array keeps the last call's contents; each
+ *          call writes every byte it reads.
+ *   FA_ERR_HIP if the array's device address cannot be obtained (no device).
+ * Other checks, errors and determinism as fa_bwd (bitwise equal to it).
+ */
+#define FA_NOALLOC_SCRATCH_BYTES (32u << 20)
+int fa_bwd_noalloc(const void* q, const void* k, const void* v, const void* o,
+                   const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                   int B, int Hq, int Hkv, int N, int d, float scale, int causal,
+                   const int32_t* cu_seqlens, fa_dtype dtype, hipStream_t stream);
+
+/*
  * Sliding-window (band) attention: the forward and backward above with the
  * causal flag replaced by a window. Query i of a sequence sees the keys
  * j of the same sequence with i − window_left <= j <= i + window_right

@@ -21,7 +21,7 @@ def declared_functions():
 
 def test_header_declares_the_boundary():
     assert declared_functions() == ["fa_bwd", "fa_bwd_dropout", "fa_bwd_dropout_stage",
-                                    "fa_bwd_num_stages", "fa_bwd_softcap",
+                                    "fa_bwd_noalloc", "fa_bwd_num_stages", "fa_bwd_softcap",
                                     "fa_bwd_softcap_stage", "fa_bwd_stage",
                                     "fa_bwd_window", "fa_bwd_window_softcap",
                                     "fa_bwd_window_softcap_stage", "fa_bwd_window_stage",
@@ -739,3 +739,22 @@ def test_binding_forward_rejects_mixed_dtypes_and_shapes():
         fa.flash_attn_func(q, q.half(), q)
     with pytest.raises(ValueError):
         fa.flash_attn_func(q, q, q[:, :4])
+
+
+def test_bwd_noalloc_host_checks():
+    """fa_bwd_noalloc refuses sizes its fixed scratch cannot hold (FA_ERR_WORKSPACE)
+    and bad arguments before it touches a device; without a device a valid call
+    reports FA_ERR_HIP (the scratch address cannot be looked up)."""
+    lim = 32 << 20
+    args = lambda B, Hq, N, **kw: [P] * 9 + [B, Hq, kw.get("Hkv", 1), N, kw.get("d", 64),
+                                             kw.get("scale", 0.125), kw.get("causal", 1),
+                                             None, kw.get("dtype", fa.FA_BF16), None]
+    assert fa.fa_bwd_workspace_size(1, 1, 1, lim // 8 - 64, 64) <= lim
+    assert fa.fa_bwd_noalloc(*args(1, 1, lim // 8 - 64)) == fa.FA_ERR_HIP
+    assert fa.fa_bwd_noalloc(*args(1, 1, lim // 8)) == fa.FA_ERR_WORKSPACE
+    assert fa.fa_bwd_noalloc(*args(2, 32, 65536)) == fa.FA_ERR_WORKSPACE
+    assert fa.fa_bwd_noalloc(*args(1, 2, 16, causal=2)) == fa.FA_ERR_INVALID_ARG
+    assert fa.fa_bwd_noalloc(*args(1, 2, 16, dtype=5)) == fa.FA_ERR_INVALID_ARG
+    assert fa.fa_bwd_noalloc(*args(1, 3, 16, Hkv=2)) == fa.FA_ERR_INVALID_ARG
+    assert fa.fa_bwd_noalloc(*args(1, 2, 16, d=96)) == fa.FA_ERR_UNSUPPORTED
+    assert fa.fa_bwd_noalloc(*args(0, 2, 16)) == fa.FA_OK
