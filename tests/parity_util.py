@@ -103,3 +103,30 @@ def bits_equal(a, b) -> bool:
 
 def host64(t):
     return t.detach().float().cpu().double().numpy() if t.dtype != np.float64 else t
+
+
+def host32(t):
+    """A device tensor of 16-bit values as a float32 NumPy array (exact)."""
+    return t.detach().float().cpu().numpy()
+
+
+def tile_rows(rng, L, tile, n_random=2):
+    """Positions that cover a sequence's first, one inner and last tile of
+    `tile` rows: each tile's first two and last positions, plus random rows."""
+    if L <= 0:
+        return []
+    nt = (L + tile - 1) // tile
+    inner = int(rng.integers(0, nt))
+    rows = set()
+    for t0 in (0, inner * tile, (nt - 1) * tile):
+        rows.update(r for r in (t0, t0 + 1, min(t0 + tile, L) - 1) if 0 <= r < L)
+    rows.update(int(x) for x in rng.integers(0, L, size=n_random))
+    return sorted(rows)
+
+
+def map_units(fn, units, workers=8):
+    """fn(unit) for every unit on a thread pool (NumPy releases the GIL in its
+    large array operations); returns the results in the units' order."""
+    from concurrent.futures import ThreadPoolExecutor
+    with ThreadPoolExecutor(max(1, min(workers, len(units)))) as ex:
+        return list(ex.map(fn, units))

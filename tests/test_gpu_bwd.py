@@ -7,8 +7,9 @@ import numpy as np
 import pytest
 
 import workloads as W
-from oracle import attention_bwd, attention_bwd_sampled
-from parity_util import bits_equal, check_grad, host64, say, to_device
+from oracle import attention_bwd, attention_bwd_rows
+from parity_util import (bits_equal, check_grad, host32, host64, map_units, say,
+                         tile_rows, to_device)
 
 pytestmark = pytest.mark.gpu
 
@@ -93,16 +94,28 @@ def test_deterministic():
         assert bits_equal(x, y)
 
 
-def test_train_16k_backward_sampled():
-    """The training-step workload at full size; two (sequence, head) units by the oracle."""
+def test_train_16k_backward_every_unit():
+    """The training-step workload at full size: every (sequence, KV head) unit,
+    dQ on query rows and dK, dV on keys from each unit's first, one inner and
+    last tile, against the oracle's selected-row backward."""
     w = W.WORKLOADS["train_16k"]
     (dq, dk, dv), t = run_fwd_bwd(w)
     cu = w.cu_seqlens()
-    units = [(0, 3), (1, 12)]
-    ref = attention_bwd_sampled(t["q"], t["k"], t["v"], t["do"], w.scale, w.causal, cu, units)
-    for (s, g), (rq, rk, rv) in ref.items():
-        sl = slice(int(cu[s]), int(cu[s + 1]))
-        check_grad(host64(dq[sl, g:g + 1]), rq, f"dQ seq {s} head {g}")
-        check_grad(host64(dk[sl, g]), rk, f"dK seq {s} head {g}")
-        r = check_grad(host64(dv[sl, g]), rv, f"dV seq {s} head {g}")
-        say(f"   unit ({s},{g}) ok; dV rel {r[0]:.2e}")
+    rng = np.random.default_rng(55)
+    q, k, v, do = (host32(t[n]) for n in ("q", "k", "v", "do"))
+    g = w.Hq // w.Hkv
+    units = [(s, kvh) for s in range(w.B) for kvh in range(w.Hkv)]
+    sel = {u: (tile_rows(rng, w.N, 128), tile_rows(rng, w.N, 128)) for u in units}
+    refs = map_units(lambda u: attention_bwd_rows(q, k, v, do, w.scale, w.causal, cu, u[0], u[1],
+                                                  *sel[u]), units)
+    dq_h, dk_h, dv_h = host64(dq), host64(dk), host64(dv)
+    worst = [0.0, 0.0, 0.0]
+    for u, (rq, rk, rv) in zip(units, refs):
+        (s, kvh), (qr, kr) = u, sel[u]
+        tq, tk = cu[s] + np.array(qr), cu[s] + np.array(kr)
+        res = (check_grad(dq_h[tq, kvh * g:(kvh + 1) * g], rq, f"dQ unit {u}"),
+               check_grad(dk_h[tk, kvh], rk, f"dK unit {u}"),
+               check_grad(dv_h[tk, kvh], rv, f"dV unit {u}"))
+        worst = [max(a, r[0]) for a, r in zip(worst, res)]
+    say(f"   every unit ({len(units)}): worst rel dQ {worst[0]:.2e} dK {worst[1]:.2e} "
+        f"dV {worst[2]:.2e}")

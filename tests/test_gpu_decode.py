@@ -152,15 +152,16 @@ def test_matches_full_attention_when_queries_are_the_sequence(dtype):
 
 
 @pytest.mark.parametrize("name", ["decode_llama", "decode_multi"])
-def test_benchmark_workload_sampled(name):
-    """The benchmark's workloads at full size, automatic splits; sampled (entry, head) units."""
+def test_benchmark_workload_every_unit(name):
+    """The benchmark's workloads at full size, automatic splits: every
+    (entry, query head) unit against the oracle."""
     w = W.DECODE_WORKLOADS[name]
     o, lse, t = run_decode(w)
-    units = [(0, 0), (w.B - 1, w.Hq - 1), (w.B // 2, 5), (1, w.Hq // 2 + 1)]
+    units = [(b, h) for b in range(w.B) for h in range(w.Hq)]
     ref = kvcache_fwd_units(t["q"], t["k"], t["v"], t["cache_seqlens"].cpu(), w.scale, w.causal,
                             units)
-    lse_h = host64(lse)
+    lse_h, o_h = host64(lse), host64(o)
     for (b, h), (O, L) in ref.items():
-        check_o(host64(o[b, :, h]), O, w.dtype, what=f"O[{b},:,{h}]")
+        check_o(o_h[b, :, h], O, w.dtype, what=f"O[{b},:,{h}]")
         check_lse(lse_h[h, b * w.Nq:(b + 1) * w.Nq], L, what=f"LSE[{h},{b}]")
     say(f"   {len(units)} units ok")

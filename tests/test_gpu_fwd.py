@@ -9,7 +9,8 @@ import pytest
 
 import workloads as W
 from oracle import attention_fwd, attention_fwd_rows
-from parity_util import bits_equal, check_lse, check_o, host64, say, to_device
+from parity_util import (bits_equal, check_lse, check_o, host32, host64, map_units, say,
+                         tile_rows, to_device)
 
 pytestmark = pytest.mark.gpu
 
@@ -214,50 +215,49 @@ def test_constant_values_exact():
     check_o(host64(o), want, w.dtype, "O with constant V")
 
 
-# ---- sampled parity at the full workload sizes --------------------------------
-def _sample_rows(rng, L, n=12):
-    fixed = [0, 1, 63, 64, 127, 128, L // 2, L - 129, L - 65, L - 1]
-    rows = set(r for r in fixed if 0 <= r < L)
-    rows.update(int(x) for x in rng.integers(0, L, size=n))
-    return sorted(rows)
-
-
-def compare_sampled(w, o, lse, t, units, seed=0):
+# ---- parity at the full workload sizes: every (sequence, head) unit ----------
+# The launch configuration (tile order, XCD remapping, heavy-first causal order,
+# sequence-fastest indexing) only takes its full form at these sizes, so every
+# unit is checked, on rows from its first, one inner and its last query tile.
+def compare_every_unit(w, o, lse, t, seed=0):
     import torch
     rng = np.random.default_rng(seed)
     cu = w.cu_seqlens()
-    worst_o = worst_l = 0.0
-    for s, h in units:
-        L = int(cu[s + 1] - cu[s])
-        rows = _sample_rows(rng, L)
-        o_ref, l_ref = attention_fwd_rows(t["q"], t["k"], t["v"], w.scale, w.causal, cu, s, h,
-                                          rows)
-        gi = torch.as_tensor(cu[s] + np.array(rows), device=o.device)
-        e, _, _ = check_o(host64(o[gi, h]), o_ref, w.dtype, f"O seq {s} head {h}")
-        el = check_lse(host64(lse[h, gi]), l_ref, f"LSE seq {s} head {h}")
-        worst_o, worst_l = max(worst_o, e), max(worst_l, el)
-    say(f"   sampled {len(units)} (seq, head) units: max|dO|={worst_o:.2e} max|dLSE|={worst_l:.2e}")
+    q, k, v = host32(t["q"]), host32(t["k"]), host32(t["v"])
+    units = [(s, h) for s in range(len(cu) - 1) for h in range(w.Hq) if cu[s + 1] > cu[s]]
+    rows = {u: tile_rows(rng, int(cu[u[0] + 1] - cu[u[0]]), 128) for u in units}
+    toks = np.concatenate([cu[s] + np.array(rows[(s, h)]) for s, h in units])
+    heads = np.concatenate([np.full(len(rows[u]), u[1]) for u in units])
+    ti = torch.as_tensor(toks, device=o.device)
+    hi = torch.as_tensor(heads, device=o.device)
+    o_g, l_g = host64(o[ti, hi]), host64(lse[hi, ti])
+    refs = map_units(lambda u: attention_fwd_rows(q, k, v, w.scale, w.causal, cu, u[0], u[1],
+                                                  rows[u]), units)
+    o_ref = np.concatenate([r[0] for r in refs])
+    l_ref = np.concatenate([r[1] for r in refs])
+    e, _, _ = check_o(o_g, o_ref, w.dtype, f"O ({len(units)} units)")
+    el = check_lse(l_g, l_ref, f"LSE ({len(units)} units)")
+    say(f"   every unit ({len(units)}, {len(toks)} rows): max|dO|={e:.2e} max|dLSE|={el:.2e}")
 
 
 @pytest.mark.parametrize("N", [512, 1024, 2048, 4096, 8192])
-def test_sweep_sampled(N):
+def test_sweep_every_unit(N):
     base = W.WORKLOADS[f"sweep_N{N}_full"]
     a = W.generate(base)
     for causal in (False, True):
         w = W.WORKLOADS[f"sweep_N{N}_{'causal' if causal else 'full'}"]
         o, lse, t = run_fwd(w, a)
-        compare_sampled(w, o, lse, t, [(0, 0), (3, 31), (1, 17)], seed=N)
+        compare_every_unit(w, o, lse, t, seed=N + causal)
         del o, lse, t
 
 
-def test_gqa_varlen_sampled():
+def test_gqa_varlen_every_unit():
     w = W.WORKLOADS["gqa_varlen"]
     o, lse, t = run_fwd(w)
-    units = [(s, h) for s, h in zip(range(8), (0, 5, 9, 14, 18, 23, 27, 31))]
-    compare_sampled(w, o, lse, t, units, seed=4)
+    compare_every_unit(w, o, lse, t, seed=4)
 
 
-def test_train_16k_forward_sampled():
+def test_train_16k_forward_every_unit():
     w = W.WORKLOADS["train_16k"]
     o, lse, t = run_fwd(w)
-    compare_sampled(w, o, lse, t, [(0, 0), (1, 15), (1, 6)], seed=5)
+    compare_every_unit(w, o, lse, t, seed=5)
