@@ -236,7 +236,10 @@ __global__ __launch_bounds__(kDkvThreads, 1) void dkdv_kernel(BwdArgs a, int n_k
   __shared__ __attribute__((aligned(16))) float ld_lds[kDkvStages][2 * kDkvQ];  // LSE·log2 e, D
   __shared__ __attribute__((aligned(16))) u32x4 xch[4][2][kDkvKK * 64];   // [pair][P, dS]
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // the wave index is the same on every lane: readfirstlane lets the compiler
+  // see that, so branches on it are scalar rather than divergent
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int pair = wave & 3;
   const bool producer = wave < 4;
   const int col = lane & 31, half = lane >> 5;
@@ -539,7 +542,10 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_wide_kernel(BwdArgs a, int n
   __shared__ __attribute__((aligned(1024))) T do_lds[2][TILE];
   __shared__ __attribute__((aligned(16))) float ld_lds[2][2 * kWideQ];   // LSE·log2 e, D
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // the wave index is the same on every lane: readfirstlane lets the compiler
+  // see that, so branches on it are scalar rather than divergent
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 31, half = lane >> 5;
 
   const int G = gridDim.x;
@@ -762,7 +768,10 @@ __global__ __launch_bounds__(kThreads, D <= 128 ? 2 : 1) void dq_kernel(BwdArgs 
   constexpr int TILE = kDqK * D;
   __shared__ __attribute__((aligned(1024))) T lds[2][2][TILE];   // [buffer][K, V]
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // the wave index is the same on every lane: readfirstlane lets the compiler
+  // see that, so branches on it are scalar rather than divergent
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 31, half = lane >> 5;
 
   const int G = gridDim.x;

@@ -88,13 +88,21 @@ __device__ __forceinline__ u32x2 transpose_col(const u32x4 (&in)[4], int w) {
   return r;
 }
 
+// Lanes l and l^32 hold the two halves of one column. v_permlane32_swap
+// (gfx950) exchanges the upper half of its first operand with the lower half
+// of its second, so swapping x with itself leaves, in every lane, x of lanes
+// l and l^32 in the two results (in the same order on both halves: the sum
+// is bitwise identical across the pair). A VALU exchange, no LDS round trip.
 __device__ __forceinline__ float wave_max_halves(float x) {
-  // lanes l and l^32 hold the two halves of one column
-  return fmaxf(x, __shfl_xor(x, 32));
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
 __device__ __forceinline__ float wave_sum_halves(float x) {
-  return x + __shfl_xor(x, 32);
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }

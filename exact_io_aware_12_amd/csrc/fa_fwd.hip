@@ -165,7 +165,10 @@ __global__ __launch_bounds__(kThreads, D <= 128 ? 2 : 1) void fwd_kernel(FwdArgs
   constexpr int TILE = kBC * D;  // elements per K or V tile
   __shared__ __attribute__((aligned(1024))) T lds[2][2][TILE];   // [buffer][K, V]
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // the wave index is the same on every lane: readfirstlane lets the compiler
+  // see that, so branches on it are scalar rather than divergent
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 31, half = lane >> 5;
 
   // ---- work decomposition: (q tile, sequence, head), heavy tiles first -----

@@ -267,7 +267,10 @@ __global__ __launch_bounds__(kThreads, 2) void fwd8_kernel(Fp8FwdArgs a) {
   constexpr int TILE = kBC * D;   // bytes per K or V tile
   __shared__ __attribute__((aligned(1024))) u8 lds[2][2][TILE];   // [buffer][K, V]
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // the wave index is the same on every lane: readfirstlane lets the compiler
+  // see that, so branches on it are scalar rather than divergent
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 31, half = lane >> 5;
 
   // ---- work decomposition as in the 16-bit forward -------------------------
