@@ -15,7 +15,8 @@ approximation: Flash Attention ÊòØ‰ªÄÈ∫º, adersaytech.com, section "exact, ‰∏çÊò
 Modules:
   attention   NumPy float64 forward and backward, whole tensors or sampled rows
               (the backward also at selected query rows and key columns)
-  decode      NumPy float64 attention of new queries over a key/value cache
+  decode      NumPy float64 attention of new queries over a key/value cache,
+              and its backward for queries and keys of different lengths
   bruteforce  pure-Python loops (math.exp / math.fsum) for tiny shapes
   dropout     Philox4x32-10 keep decisions and attention with dropout on the
               softmax weights (forward and backward)
@@ -28,14 +29,14 @@ differences and torch's CPU float64 SDPA. No function is "parity unpinned".
 """
 from .attention import (attention_fwd, attention_bwd, attention_probs,
                         attention_fwd_rows, attention_bwd_sampled, attention_bwd_rows)
-from .decode import kvcache_fwd, kvcache_fwd_units
+from .decode import kvcache_fwd, kvcache_fwd_units, kvlen_bwd, kvlen_head_bwd
 from . import bruteforce
 from .dropout import (attention_bwd_dropout, attention_fwd_dropout, head_bwd_dropout,
                       head_fwd_dropout, keep_mask, keep_threshold, philox4x32_10)
 from .fp8 import attention_fwd_fp8, e4m3fn_decode, dequantize, head_o_bound, o_bound
 
 __all__ = ["attention_fwd", "attention_bwd", "attention_probs", "attention_fwd_rows",
-           "attention_bwd_sampled", "attention_bwd_rows", "kvcache_fwd", "kvcache_fwd_units", "bruteforce",
+           "attention_bwd_sampled", "attention_bwd_rows", "kvcache_fwd", "kvcache_fwd_units", "kvlen_bwd", "kvlen_head_bwd", "bruteforce",
            "attention_fwd_fp8", "e4m3fn_decode", "dequantize", "head_o_bound", "o_bound",
            "attention_fwd_dropout", "attention_bwd_dropout", "head_fwd_dropout",
            "head_bwd_dropout", "keep_mask", "keep_threshold",

@@ -28,6 +28,19 @@ the same page's section 2.3 in the bounded reading).
 
 Layouts: q [B, Nq, Hq, d], k/v [B, Nk, Hkv, d] with Nk ≥ max L_b;
 returns o [B, Nq, Hq, d] and lse [Hq, B·Nq] (query (b, i) at column b·Nq + i).
+
+The same placement serves queries and keys of different lengths in a
+training step (a chunk of new tokens over a longer context): kvlen_head_bwd
+is the backward of kvcache_head by the chain rule (the pages only say the
+backward recomputes the scores rather than storing them: FlashAttention
+guide, cxbdf.cn, part 2, item 3), with P_ij = exp(S_ij − LSE_i) over the
+visible keys:
+
+    dV_j = Σ_i P_ij dO_i,  dP_ij = dO_i·V_j,  D_i = Σ_j P_ij dP_ij,
+    dS_ij = P_ij (dP_ij − D_i),  dQ_i = scale Σ_j dS_ij K_j,  dK_j = scale Σ_i dS_ij Q_i.
+
+A query that sees no key has no weights: its dQ is 0 and it adds nothing to
+dK and dV. kvlen_bwd applies it to packed [T, H, d] tensors.
 """
 from __future__ import annotations
 
@@ -110,3 +123,59 @@ def kvcache_fwd_units(q, k_cache, v_cache, cache_seqlens, scale: float, causal: 
         res[(b, h)] = kvcache_head(q[b, :, h], k_cache[b, :L, h // g], v_cache[b, :L, h // g],
                                    scale, causal, window_left, softcap)
     return res
+
+
+def kvlen_head_bwd(Qs, Ks, Vs, dOs, scale: float, causal: bool):
+    """One (sequence, query head): Qs, dOs [Lq, d], Ks, Vs [Lk, d], the queries
+    at the last Lq key positions. Returns dQ [Lq, d], dK [Lk, d], dV [Lk, dv]."""
+    Qs, Ks, Vs, dOs = _f64(Qs), _f64(Ks), _f64(Vs), _f64(dOs)
+    Lq, Lk = Qs.shape[0], Ks.shape[0]
+    dQ = np.zeros_like(Qs)
+    dK = np.zeros_like(Ks)
+    dV = np.zeros_like(Vs)
+    if Lq == 0 or Lk == 0:
+        return dQ, dK, dV
+    S = scale * (Qs @ Ks.T)                                  # [Lq, Lk]
+    if causal:
+        pos = Lk - Lq + np.arange(Lq)
+        S = np.where(np.arange(Lk)[None, :] <= pos[:, None], S, -np.inf)
+    seen = np.isfinite(S).any(axis=1)
+    if not seen.any():
+        return dQ, dK, dV
+    Sv = S[seen]
+    m = Sv.max(axis=1)
+    lse = m + np.log(np.exp(Sv - m[:, None]).sum(axis=1))
+    P = np.exp(Sv - lse[:, None])                            # rows that see a key
+    dO = dOs[seen]
+    dV = P.T @ dO
+    dP = dO @ Vs.T
+    D = (P * dP).sum(axis=1)
+    dS = P * (dP - D[:, None])
+    dQ[seen] = scale * (dS @ Ks)
+    dK = scale * (dS.T @ Qs[seen])
+    return dQ, dK, dV
+
+
+def kvlen_bwd(q, k, v, do, scale: float, causal: bool, cu_q, cu_k):
+    """Packed backward: q, do [Tq, Hq, d] split by cu_q, k, v [Tk, Hkv, d] by cu_k
+    (B+1 prefix sums each). dK, dV of a KV head are summed over its query heads.
+    Returns dq [Tq, Hq, d], dk, dv [Tk, Hkv, d] in float64."""
+    q, k, v, do = _f64(q), _f64(k), _f64(v), _f64(do)
+    cq = [int(x) for x in np.asarray(cu_q)]
+    ck = [int(x) for x in np.asarray(cu_k)]
+    if len(cq) != len(ck):
+        raise ValueError("cu_q and cu_k need the same number of entries")
+    Hq, Hkv = q.shape[1], k.shape[1]
+    if Hkv <= 0 or Hq % Hkv:
+        raise ValueError(f"Hq={Hq} must be a positive multiple of Hkv={Hkv}")
+    g = Hq // Hkv
+    dq, dk, dv = np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)
+    for b in range(len(cq) - 1):
+        qa, qb, ka, kb = cq[b], cq[b + 1], ck[b], ck[b + 1]
+        for h in range(Hq):
+            dQ, dK, dV = kvlen_head_bwd(q[qa:qb, h], k[ka:kb, h // g], v[ka:kb, h // g],
+                                        do[qa:qb, h], scale, causal)
+            dq[qa:qb, h] = dQ
+            dk[ka:kb, h // g] += dK
+            dv[ka:kb, h // g] += dV
+    return dq, dk, dv
