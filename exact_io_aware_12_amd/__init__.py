@@ -17,6 +17,8 @@ Tensor-level helpers:
                         window_size=(-1, -1), softcap=0.0, dropout_p=0.0,
                         dropout_seed=None) -> (dq, dk, dv)
     flash_attn_func_fp8(q, k, v, descale_q, descale_k, descale_v, ...) -> (o, lse)
+    flash_attn_kvlen_func(q, k, v, ...) -> (o, lse)   (queries and keys of different lengths)
+    flash_attn_kvlen_backward(dout, q, k, v, o, lse, ...) -> (dq, dk, dv)
     flash_attn_with_kvcache(q, k_cache, v_cache, cache_seqlens, causal=False,
                             softmax_scale=None, num_splits=0) -> (o, lse)
 The call shape follows flash_attn_func in the pages' examples (Llama-Factory
@@ -70,6 +72,7 @@ _SIGS = {
     "fa_fwd_dropout": (_I, _FWD_HEAD + [_I, _F, _U64, _VP, _I, _VP]),
     "fa_bwd_dropout": (_I, _BWD_HEAD + [_I, _F, _U64] + _BWD_TAIL),
     "fa_fwd_kvlen": (_I, [_VP] * 5 + [_I] * 6 + [_F, _I, _VP, _VP, _I, _VP]),
+    "fa_bwd_kvlen": (_I, [_VP] * 9 + [_I] * 6 + [_F, _I, _VP, _VP, _I, _VP, _SZ, _VP]),
     "fa_fwd_fp8": (_I, _FWD_HEAD + [_I, _VP, _F, _F, _F, _I, _VP]),
     "fa_fwd_kvcache": (_I, _KVC_HEAD + [_I, _I] + _WS_TAIL),
     "fa_fwd_kvcache_local": (_I, _KVC_HEAD + [_I, _F, _I, _I] + _WS_TAIL),
@@ -82,7 +85,7 @@ _SIGS = {
 }
 # each staged entry point takes a leading stage index, then its parent's arguments
 for _n in ("fa_bwd", "fa_bwd_window", "fa_bwd_window_softcap", "fa_bwd_softcap",
-           "fa_bwd_dropout", "fa_fwd_kvcache", "fa_fwd_kvcache_fp8"):
+           "fa_bwd_dropout", "fa_bwd_kvlen", "fa_fwd_kvcache", "fa_fwd_kvcache_fp8"):
     _SIGS[_n + "_stage"] = (_I, [_I] + _SIGS[_n][1])
 
 
@@ -119,7 +122,7 @@ def fa_status_string(status: int) -> str:
 __all__ = (["FA_OK", "FA_ERR_INVALID_ARG", "FA_ERR_UNSUPPORTED", "FA_ERR_HIP", "FA_ERR_WORKSPACE",
             "FA_FP16", "FA_BF16", "FaError", "lib", "lib_path", "flash_attn_func",
             "flash_attn_backward", "flash_attn_func_fp8", "flash_attn_kvlen_func",
-            "flash_attn_with_kvcache"] + sorted(_SIGS))
+            "flash_attn_kvlen_backward", "flash_attn_with_kvcache"] + sorted(_SIGS))
 
 # ---- tensor helpers ----------------------------------------------------------
 def _dropout_args(dropout_p, dropout_seed, causal_window, softcap):
@@ -331,6 +334,62 @@ def flash_attn_kvlen_func(q, k, v, causal=False, softmax_scale=None, cu_seqlens_
     if st != FA_OK:
         raise FaError(st, "fa_fwd_kvlen")
     return o, lse
+
+
+def flash_attn_kvlen_backward(dout, q, k, v, o, lse, causal=False, softmax_scale=None,
+                              cu_seqlens_q=None, cu_seqlens_k=None, max_seqlen_q=None,
+                              max_seqlen_k=None, workspace=None, validate=True):
+    """Backward of flash_attn_kvlen_func (same layouts and arguments; o, lse its
+    outputs). Returns (dq, dk, dv) shaped like q, k, v (see fa_bwd_kvlen)."""
+    import torch
+    if v.shape != k.shape:
+        raise ValueError("k and v must have the same shape")
+    if not (q.dtype == k.dtype == v.dtype == o.dtype == dout.dtype):
+        raise TypeError("q, k, v, o and dout must share one dtype")
+    if o.shape != q.shape or dout.shape != q.shape:
+        raise ValueError("o and dout must have q's shape")
+    if (cu_seqlens_q is None) != (cu_seqlens_k is None):
+        raise ValueError("give both cu_seqlens_q and cu_seqlens_k, or neither")
+    if cu_seqlens_q is None:
+        if q.dim() != 4 or k.dim() != 4:
+            raise ValueError("fixed-length inputs are (batch, seq, heads, head_dim)")
+        B, Nq, Hq, d = q.shape
+        if k.shape[0] != B or k.shape[3] != d:
+            raise ValueError(f"q {tuple(q.shape)} and k {tuple(k.shape)} do not match")
+        Nk, Hkv, Tq = k.shape[1], k.shape[2], B * Nq
+    else:
+        if q.dim() != 3 or k.dim() != 3:
+            raise ValueError("varlen inputs are packed (total_tokens, heads, head_dim)")
+        if max_seqlen_q is None or max_seqlen_k is None:
+            raise ValueError("varlen needs max_seqlen_q and max_seqlen_k")
+        if cu_seqlens_q.numel() != cu_seqlens_k.numel():
+            raise ValueError("cu_seqlens_q and cu_seqlens_k need the same number of entries")
+        Tq, Hq, d = q.shape
+        if k.shape[2] != d:
+            raise ValueError(f"q {tuple(q.shape)} and k {tuple(k.shape)} do not match")
+        B, Nq, Nk, Hkv = cu_seqlens_q.numel() - 1, int(max_seqlen_q), int(max_seqlen_k), k.shape[1]
+    if lse.dtype != torch.float32 or tuple(lse.shape) != (Hq, Tq):
+        raise ValueError(f"lse must be float32 of shape ({Hq}, {Tq})")
+    _check_dev(dout, q, k, v, o, lse)
+    if cu_seqlens_q is not None:
+        _check_cu(cu_seqlens_q, Tq, Nq, validate, "cu_seqlens_q")
+        _check_cu(cu_seqlens_k, k.shape[0], Nk, validate, "cu_seqlens_k")
+    scale = softmax_scale if softmax_scale is not None else 1.0 / math.sqrt(d)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    need = fa_bwd_workspace_size(B, Hq, Hkv, Nq, d)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    else:
+        _check_dev(workspace)
+    cq = cu_seqlens_q.data_ptr() if cu_seqlens_q is not None else None
+    ck = cu_seqlens_k.data_ptr() if cu_seqlens_k is not None else None
+    ptr = lambda t: t.data_ptr() if t.numel() else None   # noqa: E731  (empty side: NULL)
+    st = lib.fa_bwd_kvlen(ptr(q), ptr(k), ptr(v), ptr(o), ptr(dout), ptr(lse), ptr(dq), ptr(dk),
+                          ptr(dv), B, Hq, Hkv, Nq, Nk, d, float(scale), int(bool(causal)), cq, ck,
+                          _dtype_code(q), workspace.data_ptr(), _nbytes(workspace), _stream())
+    if st != FA_OK:
+        raise FaError(st, "fa_bwd_kvlen")
+    return dq, dk, dv
 
 
 def flash_attn_func_fp8(q, k, v, descale_q=1.0, descale_k=1.0, descale_v=1.0, causal=False,

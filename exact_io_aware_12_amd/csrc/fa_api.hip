@@ -489,6 +489,90 @@ int fa_bwd_dropout_stage(int stage, const void* q, const void* k, const void* v,
 
 int fa_bwd_num_stages(void) { return fa::bwd_num_stages(); }
 
+}  // extern "C"
+
+namespace {
+
+// The backward of fa_fwd_kvlen; stage < 0 runs every stage.
+int bwd_kvlen_common(int stage, const void* q, const void* k, const void* v, const void* o,
+                     const void* dout, const float* lse, void* dq, void* dk, void* dv, int B,
+                     int Hq, int Hkv, int Nq, int Nk, int d, float scale, int causal,
+                     const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int dtype,
+                     void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  const bool varlen = cu_seqlens_q != nullptr;
+  if (varlen != (cu_seqlens_k != nullptr)) return FA_ERR_INVALID_ARG;
+  bool noop;
+  int st = check_sizes(B, Hq, Hkv, Nq, d, scale, causal, dtype, &noop, 128);
+  if (st != FA_OK) return st;
+  if (Nk < 0) return FA_ERR_INVALID_ARG;
+  if ((int64_t)B * Nk >= (int64_t)1 << 31 || (int64_t)B * Nk * Hkv >= (int64_t)1 << 31)
+    return FA_ERR_UNSUPPORTED;
+  // no query: dk, dv are zero (still written); no key either: nothing to do
+  if (B == 0 || (Nq == 0 && Nk == 0)) return FA_OK;
+  if (Nq > 0 && (!q || !o || !dout || !lse || !dq)) return FA_ERR_INVALID_ARG;
+  if (Nk > 0 && (!k || !v || !dk || !dv)) return FA_ERR_INVALID_ARG;
+  const void* ptrs[] = {q, k, v, o, dout, lse, dq, dk, dv, workspace};
+  for (const void* p : ptrs)
+    if (p && !aligned16(p)) return FA_ERR_INVALID_ARG;
+  if (!workspace || workspace_bytes < fa_bwd_workspace_size(B, Hq, Hkv, Nq, d))
+    return FA_ERR_WORKSPACE;
+  fa::BwdArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.dout = dout;
+  a.lse = lse;
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  a.ws_stride = B * Nq + 64;
+  a.delta = static_cast<float*>(workspace);
+  a.lse2 = a.delta + (size_t)Hq * a.ws_stride;
+  a.cu_seqlens = cu_seqlens_q;
+  a.cu_seqlens_k = cu_seqlens_k;
+  a.B = B;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.N = Nq;
+  a.Nk = Nk;
+  a.group = Hq / Hkv;
+  a.scale = scale;
+  a.scale_log2 = scale * kLog2e;
+  a.wl = a.wr = 0;
+  a.cap_in = a.cap_out = 0.f;
+  a.seed_lo = a.seed_hi = 0;
+  a.keep_t = 256;
+  a.drop_scale = 1.f;
+  hipError_t e = fa::launch_bwd_kvlen(a, dtype == FA_BF16, d, causal != 0, varlen, stage, stream);
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+int fa_bwd_kvlen(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                 const float* lse, void* dq, void* dk, void* dv, int B, int Hq, int Hkv, int Nq,
+                 int Nk, int d, float scale, int causal, const int32_t* cu_seqlens_q,
+                 const int32_t* cu_seqlens_k, fa_dtype dtype, void* workspace,
+                 size_t workspace_bytes, hipStream_t stream) {
+  return bwd_kvlen_common(-1, q, k, v, o, dout, lse, dq, dk, dv, B, Hq, Hkv, Nq, Nk, d, scale,
+                          causal, cu_seqlens_q, cu_seqlens_k, dtype, workspace, workspace_bytes,
+                          stream);
+}
+
+int fa_bwd_kvlen_stage(int stage, const void* q, const void* k, const void* v, const void* o,
+                       const void* dout, const float* lse, void* dq, void* dk, void* dv, int B,
+                       int Hq, int Hkv, int Nq, int Nk, int d, float scale, int causal,
+                       const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, fa_dtype dtype,
+                       void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (stage < 0 || stage >= fa::bwd_num_stages()) return FA_ERR_INVALID_ARG;
+  return bwd_kvlen_common(stage, q, k, v, o, dout, lse, dq, dk, dv, B, Hq, Hkv, Nq, Nk, d, scale,
+                          causal, cu_seqlens_q, cu_seqlens_k, dtype, workspace, workspace_bytes,
+                          stream);
+}
+
 int fa_bwd_stage(int stage, const void* q, const void* k, const void* v, const void* o,
                  const void* dout, const float* lse, void* dq, void* dk, void* dv, int B, int Hq,
                  int Hkv, int N, int d, float scale, int causal, const int32_t* cu_seqlens,

@@ -30,18 +30,40 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kWaves = 4;
 
+// A sequence's queries (first token, count, tokens of the batch) and keys
+// (first token, count); off = Lk − L is the key position of query 0 (0 unless
+// KVLEN: the queries are the last L of the Lk positions).
 struct SeqInfo {
   int seq0, L, T;
+  int seq0k, Lk, off;
 };
 
-template <bool VARLEN>
+template <bool VARLEN, bool KVLEN = false>
 __device__ __forceinline__ SeqInfo seq_info(const BwdArgs& a, int b) {
+  SeqInfo r;
   if constexpr (VARLEN) {
-    const int s0 = a.cu_seqlens[b];
-    return {s0, a.cu_seqlens[b + 1] - s0, a.cu_seqlens[a.B]};
+    r.seq0 = a.cu_seqlens[b];
+    r.L = a.cu_seqlens[b + 1] - r.seq0;
+    r.T = a.cu_seqlens[a.B];
   } else {
-    return {b * a.N, a.N, a.B * a.N};
+    r.seq0 = b * a.N;
+    r.L = a.N;
+    r.T = a.B * a.N;
   }
+  if constexpr (KVLEN) {
+    if constexpr (VARLEN) {
+      r.seq0k = a.cu_seqlens_k[b];
+      r.Lk = a.cu_seqlens_k[b + 1] - r.seq0k;
+    } else {
+      r.seq0k = b * a.Nk;
+      r.Lk = a.Nk;
+    }
+  } else {
+    r.seq0k = r.seq0;
+    r.Lk = r.L;
+  }
+  r.off = r.Lk - r.L;
+  return r;
 }
 
 template <typename T>
@@ -150,7 +172,7 @@ __device__ __forceinline__ void dkdv_produce(const T* qt_, const T* dot_, const 
                                              float c, int q0, int L, int key, int wl, int wr,
                                              int lane, float cap_in = 0.f, float cap_out = 0.f,
                                              const DropKey* dk = nullptr, int seq = 0,
-                                             int head = 0, float zs = 0.f) {
+                                             int head = 0, float zs = 0.f, int off = 0) {
   constexpr int NKB = D / 16;
   constexpr int NQB = kDkvQ / 32;
   const int col = lane & 31, half = lane >> 5;
@@ -208,7 +230,7 @@ __device__ __forceinline__ void dkdv_produce(const T* qt_, const T* dot_, const 
         }
         if constexpr (EDGE) {
           const int q = q0 + qoff + t;
-          bool keep = q < L && !(CAUSAL && key > q);
+          bool keep = q < L && !(CAUSAL && key > q + off);
           if constexpr (WIN) keep = keep && q >= key - wr && q <= key + wl;
           p = keep ? p : 0.f;
           ds = keep ? ds : 0.f;
@@ -226,8 +248,9 @@ __device__ __forceinline__ void dkdv_produce(const T* qt_, const T* dot_, const 
 }
 
 // WIN: sliding window (see fwd_kernel); CAUSAL is false then
+// KVLEN: keys of their own length (see seq_info); no window, cap or dropout
 template <typename T, int D, bool CAUSAL, bool VARLEN, bool WIN, bool CAP = false,
-          bool DROP = false>
+          bool DROP = false, bool KVLEN = false>
 __global__ __launch_bounds__(kDkvThreads, 1) void dkdv_kernel(BwdArgs a, int n_ktiles) {
   constexpr int NKB = D / 16;
   constexpr int NCB = D / 32;
@@ -249,10 +272,10 @@ __global__ __launch_bounds__(kDkvThreads, 1) void dkdv_kernel(BwdArgs a, int n_k
   const int kt = logical % n_ktiles;           // ascending = heaviest first when causal
   const int gb = logical / n_ktiles;
   const int b = gb % a.B, g = gb / a.B;   // sequence fastest: XCD ranges balanced for varlen
-  const SeqInfo si = seq_info<VARLEN>(a, b);
+  const SeqInfo si = seq_info<VARLEN, KVLEN>(a, b);
   const int k0 = kt * kDkvKeys;
-  if (k0 >= si.L) return;
-  const int L = si.L;
+  if (k0 >= si.Lk) return;
+  const int L = si.L, Lk = si.Lk, off = si.off;   // queries, keys, key position of query 0
 
   const int64_t qs = (int64_t)a.Hq * D, kvs = (int64_t)a.Hkv * D;
   const int key = k0 + pair * 32 + col;
@@ -273,6 +296,15 @@ __global__ __launch_bounds__(kDkvThreads, 1) void dkdv_kernel(BwdArgs a, int n_k
     const int last_all = k0 + wl - (kDkvQ - 1);   // a tile starting here ends at k0 + wl
     qi_hi = min(min(last_all < 0 ? 0 : last_all / kDkvQ + 1, L / kDkvQ), qt_hi);
     if (qi_hi < qi_lo) qi_hi = qi_lo;
+  } else if constexpr (KVLEN) {
+    // causal: query i sees key j iff j <= i + off. Tiles from the one holding
+    // the first query that sees key k0; interior from the first query that
+    // sees every key of the block (keys past Lk never reach dK, dV)
+    qt_hi = (L + kDkvQ - 1) / kDkvQ;
+    qt_lo = CAUSAL ? min(max(0, k0 - off) / kDkvQ, qt_hi) : 0;
+    const int first_all = CAUSAL ? min(k0 + kDkvKeys, Lk) - 1 - off : 0;
+    qi_lo = min(max(qt_lo, first_all <= 0 ? 0 : (first_all + kDkvQ - 1) / kDkvQ), qt_hi);
+    qi_hi = max(qi_lo, qt_hi - (L % kDkvQ != 0 ? 1 : 0));
   } else {
     qt_lo = CAUSAL ? k0 / kDkvQ : 0;
     qt_hi = (L + kDkvQ - 1) / kDkvQ;
@@ -294,7 +326,7 @@ __global__ __launch_bounds__(kDkvThreads, 1) void dkdv_kernel(BwdArgs a, int n_k
   };
   // whether a query tile holds no query that sees any key of this wave pair
   auto pair_idle = [&](int q0) -> bool {
-    if (CAUSAL && q0 + kDkvQ - 1 < pk_first) return true;
+    if (CAUSAL && q0 + kDkvQ - 1 + off < pk_first) return true;
     if (WIN && (q0 + kDkvQ - 1 < pk_first - wr || q0 > pk_first + 31 + wl)) return true;
     return false;
   };
@@ -328,12 +360,12 @@ __global__ __launch_bounds__(kDkvThreads, 1) void dkdv_kernel(BwdArgs a, int n_k
   if (producer) {
     // K and V fragments of this pair's 32 keys (B operands), kept in registers
     u32x4 kf[NKB], vf[NKB];
-    const T* kp = static_cast<const T*>(a.k) + (int64_t)(si.seq0 + key) * kvs + (int64_t)g * D;
-    const T* vp = static_cast<const T*>(a.v) + (int64_t)(si.seq0 + key) * kvs + (int64_t)g * D;
+    const T* kp = static_cast<const T*>(a.k) + (int64_t)(si.seq0k + key) * kvs + (int64_t)g * D;
+    const T* vp = static_cast<const T*>(a.v) + (int64_t)(si.seq0k + key) * kvs + (int64_t)g * D;
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) {
-      kf[kb] = key < L ? ldg16(kp + kb * 16 + half * 8) : u32x4{0, 0, 0, 0};
-      vf[kb] = key < L ? ldg16(vp + kb * 16 + half * 8) : u32x4{0, 0, 0, 0};
+      kf[kb] = key < Lk ? ldg16(kp + kb * 16 + half * 8) : u32x4{0, 0, 0, 0};
+      vf[kb] = key < Lk ? ldg16(vp + kb * 16 + half * 8) : u32x4{0, 0, 0, 0};
     }
     for (int j = -1; j < ntile; ++j) {
       wait_vmem_all();   // this wave's copies of tile j+1 (and K, V) have landed
@@ -351,11 +383,11 @@ __global__ __launch_bounds__(kDkvThreads, 1) void dkdv_kernel(BwdArgs a, int n_k
           if (t < n_edge)
             dkdv_produce<T, D, CAUSAL, true, WIN, CAP, DROP>(
                 qd_lds[st][0], qd_lds[st][1], ld_lds[st], kf, vf, xp, xs, c, q0, L, key, wl, wr,
-                lane, a.cap_in, a.cap_out, &dk, b, h, a.drop_scale);
+                lane, a.cap_in, a.cap_out, &dk, b, h, a.drop_scale, off);
           else
             dkdv_produce<T, D, CAUSAL, false, WIN, CAP, DROP>(
                 qd_lds[st][0], qd_lds[st][1], ld_lds[st], kf, vf, xp, xs, c, q0, L, key, wl, wr,
-                lane, a.cap_in, a.cap_out, &dk, b, h, a.drop_scale);
+                lane, a.cap_in, a.cap_out, &dk, b, h, a.drop_scale, off);
         }
       }
     }
@@ -425,10 +457,10 @@ __global__ __launch_bounds__(kDkvThreads, 1) void dkdv_kernel(BwdArgs a, int n_k
         __builtin_amdgcn_sched_group_barrier(kSgMFMA, kPer, 0);
       }
     }
-    if (key < L) {
-      const int64_t off = (int64_t)(si.seq0 + key) * kvs + (int64_t)g * D;
-      T* dkp = static_cast<T*>(a.dk) + off;
-      T* dvp = static_cast<T*>(a.dv) + off;
+    if (key < Lk) {
+      const int64_t ko = (int64_t)(si.seq0k + key) * kvs + (int64_t)g * D;
+      T* dkp = static_cast<T*>(a.dk) + ko;
+      T* dvp = static_cast<T*>(a.dv) + ko;
       const float sc = a.scale;
 #pragma unroll
       for (int cb = 0; cb < NCB; ++cb)
@@ -760,8 +792,9 @@ __device__ __forceinline__ void dq_tile(const T* kt, const T* vt, const u32x4 (&
 
 // two workgroups per CU up to d = 128; at d = 256 the dQ accumulators and the
 // Q and dO fragments take 256 registers and the kernel runs one per CU
+// KVLEN: keys of their own length (see seq_info); no window, cap or dropout
 template <typename T, int D, bool CAUSAL, bool VARLEN, bool WIN, bool CAP = false,
-          bool DROP = false>
+          bool DROP = false, bool KVLEN = false>
 __global__ __launch_bounds__(kThreads, D <= 128 ? 2 : 1) void dq_kernel(BwdArgs a, int n_qtiles) {
   constexpr int NKB = D / 16;
   constexpr int NCB = D / 32;
@@ -780,15 +813,15 @@ __global__ __launch_bounds__(kThreads, D <= 128 ? 2 : 1) void dq_kernel(BwdArgs 
   const int hb = logical / n_qtiles;
   const int b = hb % a.B, h = hb / a.B;   // sequence fastest: XCD ranges balanced for varlen
   const int qt = CAUSAL ? n_qtiles - 1 - qt_ord : qt_ord;
-  const SeqInfo si = seq_info<VARLEN>(a, b);
+  const SeqInfo si = seq_info<VARLEN, KVLEN>(a, b);
   const int q0 = qt * kDqQ;
   if (q0 >= si.L) return;
-  const int L = si.L;
+  const int L = si.L, Lk = si.Lk, off = si.off;   // queries, keys, key position of query 0
   const int g = h / a.group;
 
   const int64_t qs = (int64_t)a.Hq * D, kvs = (int64_t)a.Hkv * D;
-  const T* kp = static_cast<const T*>(a.k) + (int64_t)si.seq0 * kvs + (int64_t)g * D;
-  const T* vp = static_cast<const T*>(a.v) + (int64_t)si.seq0 * kvs + (int64_t)g * D;
+  const T* kp = static_cast<const T*>(a.k) + (int64_t)si.seq0k * kvs + (int64_t)g * D;
+  const T* vp = static_cast<const T*>(a.v) + (int64_t)si.seq0k * kvs + (int64_t)g * D;
   // key tiles [j_lo, j_hi) visible to some query; [ja, jb) need no masking
   // (the same split as in fwd_kernel)
   int j_lo, ja, jb, j_hi;
@@ -802,14 +835,18 @@ __global__ __launch_bounds__(kThreads, D <= 128 ? 2 : 1) void dq_kernel(BwdArgs 
     jb = min(min(last_all < 0 ? 0 : last_all / kDqK + 1, L / kDqK), j_hi);
     if (jb < ja) jb = ja;
   } else {
-    const int kv_end = CAUSAL ? min(L, q0 + kDqQ) : L;
+    // causal: query i sees keys j <= i + off; the end may be <= 0 with KVLEN
+    // (no key for any query of the tile: dQ = 0)
+    const int kv_end = CAUSAL ? min(Lk, q0 + kDqQ + off) : Lk;
     j_lo = ja = 0;
-    j_hi = (kv_end + kDqK - 1) / kDqK;
-    jb = min(CAUSAL ? min((q0 + 1) / kDqK, L / kDqK) : L / kDqK, j_hi);
+    j_hi = kv_end > 0 ? (kv_end + kDqK - 1) / kDqK : 0;
+    jb = min(CAUSAL ? min(max(q0 + off + 1, 0) / kDqK, Lk / kDqK) : Lk / kDqK, j_hi);
   }
   const int ntiles = j_hi;
-  tile_dma<T, kDqK, D, kWaves>(lds[0][0], kp, kvs, j_lo * kDqK, L, wave, lane);
-  tile_dma<T, kDqK, D, kWaves>(lds[0][1], vp, kvs, j_lo * kDqK, L, wave, lane);
+  if (ntiles > j_lo) {
+    tile_dma<T, kDqK, D, kWaves>(lds[0][0], kp, kvs, j_lo * kDqK, Lk, wave, lane);
+    tile_dma<T, kDqK, D, kWaves>(lds[0][1], vp, kvs, j_lo * kDqK, Lk, wave, lane);
+  }
 
   const int qrow = q0 + wave * 32 + col;
   u32x4 qf[NKB], df[NKB];
@@ -849,20 +886,21 @@ __global__ __launch_bounds__(kThreads, D <= 128 ? 2 : 1) void dq_kernel(BwdArgs 
     __syncthreads();
     if (j + 1 < ntiles) {
       const int n0 = kv0 + kDqK;
-      if (n0 + kDqK <= L) {
+      if (n0 + kDqK <= Lk) {
         tile_dma_in<T, kDqK, D, kWaves>(lds[BUF ^ 1][0], kp + (int64_t)n0 * kvs, plan, wave_u);
         tile_dma_in<T, kDqK, D, kWaves>(lds[BUF ^ 1][1], vp + (int64_t)n0 * kvs, plan, wave_u);
       } else {
-        tile_dma<T, kDqK, D, kWaves>(lds[BUF ^ 1][0], kp, kvs, n0, L, wave, lane);
-        tile_dma<T, kDqK, D, kWaves>(lds[BUF ^ 1][1], vp, kvs, n0, L, wave, lane);
+        tile_dma<T, kDqK, D, kWaves>(lds[BUF ^ 1][0], kp, kvs, n0, Lk, wave, lane);
+        tile_dma<T, kDqK, D, kWaves>(lds[BUF ^ 1][1], vp, kvs, n0, Lk, wave, lane);
       }
     }
-    if (EDGE && CAUSAL && kv0 > wq_last) return;   // every key after this wave's queries
+    if (EDGE && CAUSAL && kv0 > wq_last + off) return;   // every key after this wave's queries
     if (EDGE && WIN && (kv0 > wq_last + wr || kv0 + kDqK - 1 < wq_first - wl))
       return;   // the tile lies outside the windows of all this wave's queries
-    dq_tile<T, D, CAUSAL, EDGE, WIN, CAP, DROP>(kt, vt, qf, df, dqt, c, lse2, dl, kv0, L, qrow,
-                                                wl, wr, lane, a.cap_in, a.cap_out, &dk, b, h,
-                                                a.drop_scale);
+    // keys are compared with the query's position qrow + off
+    dq_tile<T, D, CAUSAL, EDGE, WIN, CAP, DROP>(kt, vt, qf, df, dqt, c, lse2, dl, kv0, Lk,
+                                                qrow + off, wl, wr, lane, a.cap_in, a.cap_out,
+                                                &dk, b, h, a.drop_scale);
   };
   using B0 = std::integral_constant<int, 0>;
   using B1 = std::integral_constant<int, 1>;
@@ -899,14 +937,16 @@ __global__ __launch_bounds__(kThreads, D <= 128 ? 2 : 1) void dq_kernel(BwdArgs 
 }
 
 template <typename T, int D, bool CAUSAL, bool VARLEN, bool WIN, bool CAP = false,
-          bool DROP = false>
+          bool DROP = false, bool KVLEN = false>
 hipError_t launch(const BwdArgs& a, int stage, hipStream_t s) {
+  static_assert(!KVLEN || D <= 128, "separate key lengths: d = 64 or 128");
   (void)hipGetLastError();  // drop an error left pending by earlier, unrelated HIP calls
   if (stage < 0 || stage == 0) {
     const int64_t rows = (int64_t)a.B * a.N * a.Hq;   // upper bound on T·Hq
     const int rows_per_block = kThreads / (D / 8);
     const int g0 = (int)((rows + rows_per_block - 1) / rows_per_block);
-    hipLaunchKernelGGL((delta_kernel<T, D, VARLEN>), dim3(g0), dim3(kThreads), 0, s, a);
+    if (g0 > 0)
+      hipLaunchKernelGGL((delta_kernel<T, D, VARLEN>), dim3(g0), dim3(kThreads), 0, s, a);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -920,17 +960,19 @@ hipError_t launch(const BwdArgs& a, int stage, hipStream_t s) {
       hipLaunchKernelGGL((dkdv_wide_kernel<T, D, CAUSAL, VARLEN, 1, CAP, WIN, DROP>),
                          dim3(nkt * a.Hkv * a.B), dim3(kThreads), 0, s, a, nkt);
     } else {
-      const int nkt = (a.N + kDkvKeys - 1) / kDkvKeys;
-      hipLaunchKernelGGL((dkdv_kernel<T, D, CAUSAL, VARLEN, WIN, CAP, DROP>),
-                         dim3(nkt * a.Hkv * a.B), dim3(kDkvThreads), 0, s, a, nkt);
+      const int nkt = ((KVLEN ? a.Nk : a.N) + kDkvKeys - 1) / kDkvKeys;
+      if (nkt > 0)
+        hipLaunchKernelGGL((dkdv_kernel<T, D, CAUSAL, VARLEN, WIN, CAP, DROP, KVLEN>),
+                           dim3(nkt * a.Hkv * a.B), dim3(kDkvThreads), 0, s, a, nkt);
     }
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   if (stage < 0 || stage == 2) {
     const int nqt = (a.N + kDqQ - 1) / kDqQ;
-    hipLaunchKernelGGL((dq_kernel<T, D, CAUSAL, VARLEN, WIN, CAP, DROP>), dim3(nqt * a.Hq * a.B),
-                       dim3(kThreads), 0, s, a, nqt);
+    if (nqt > 0)
+      hipLaunchKernelGGL((dq_kernel<T, D, CAUSAL, VARLEN, WIN, CAP, DROP, KVLEN>),
+                         dim3(nqt * a.Hq * a.B), dim3(kThreads), 0, s, a, nqt);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -1001,6 +1043,19 @@ hipError_t dispatch_256(const BwdArgs& a, int mask, bool varlen, bool cap, bool 
                   : launch<T, 256, true, false, false>(a, stage, s);
   return varlen ? launch<T, 256, false, true, false>(a, stage, s)
                 : launch<T, 256, false, false, false>(a, stage, s);
+}
+
+hipError_t launch_bwd_kvlen(const BwdArgs& a, bool bf16_in, int d, bool causal, bool varlen,
+                            int stage, hipStream_t s) {
+  // <T, D, CAUSAL, VARLEN, WIN, CAP, DROP, KVLEN>
+#define FA_KVLEN_BWD(T, D)                                                                   \
+  (causal ? (varlen ? launch<T, D, true, true, false, false, false, true>(a, stage, s)       \
+                    : launch<T, D, true, false, false, false, false, true>(a, stage, s))     \
+          : (varlen ? launch<T, D, false, true, false, false, false, true>(a, stage, s)      \
+                    : launch<T, D, false, false, false, false, false, true>(a, stage, s)))
+  if (bf16_in) return d == 64 ? FA_KVLEN_BWD(bf16, 64) : FA_KVLEN_BWD(bf16, 128);
+  return d == 64 ? FA_KVLEN_BWD(f16, 64) : FA_KVLEN_BWD(f16, 128);
+#undef FA_KVLEN_BWD
 }
 
 hipError_t launch_bwd(const BwdArgs& a, bool bf16_in, int d, int mask, bool varlen, bool cap,

@@ -61,6 +61,10 @@ struct BwdArgs {
   uint32_t seed_lo, seed_hi;  // dropout: Philox key
   uint32_t keep_t;            // dropout: keep iff byte < keep_t
   float drop_scale;           // dropout: 256 / keep_t
+  // separate key lengths (launch_bwd_kvlen only): keys [B·Nk] or cu_seqlens_k;
+  // the queries of a sequence are its last positions, as in the forward
+  const int32_t* cu_seqlens_k = nullptr;
+  int Nk = 0;
 };
 
 struct DecodeArgs {
@@ -105,6 +109,10 @@ hipError_t launch_fwd_fp8(const Fp8FwdArgs& a, bool bf16_out, int d, bool causal
 int bwd_num_stages();
 hipError_t launch_bwd(const BwdArgs& a, bool bf16_in, int d, int mask, bool varlen, bool softcap,
                       bool dropout, int stage, hipStream_t s);
+// The backward of launch_fwd_kvlen (a.N / a.cu_seqlens for the queries, a.Nk /
+// a.cu_seqlens_k for the keys): mask none or causal, d = 64 or 128.
+hipError_t launch_bwd_kvlen(const BwdArgs& a, bool bf16_in, int d, bool causal, bool varlen,
+                            int stage, hipStream_t s);
 int decode_tile_keys();
 // stage < 0: both stages; 0: per-range partial results; 1: merge into o, lse.
 // kv8: k and v hold e4m3fn codes (q and o stay 16-bit).

@@ -302,6 +302,35 @@ int fa_fwd_kvlen(const void* q, const void* k, const void* v, void* o, float* ls
                  hipStream_t stream);
 
 /*
+ * Backward of fa_fwd_kvlen: queries and keys of different lengths, for
+ * training on a chunk of new tokens over a longer context. The layouts,
+ * lengths, placement of the queries (the last Lq of a sequence's Lk positions,
+ * bottom-right causal alignment) and cu_seqlens conventions are those of
+ * fa_fwd_kvlen; o and lse are its outputs. The tiling sketch of the
+ * FlashAttention-2 全解析 page (blog.gitcode.com, section 2.1) takes seqlen_q and
+ * seqlen_k separately; the backward recomputes the probabilities from lse
+ * (cxbdf.cn guide, part 2, item 3).
+ *   dq [.., Hq, d] like q; dk, dv [.., Hkv, d] like k, v (summed over the
+ *   query heads that share a KV head)
+ * A query that sees no key (lse = −inf) gets dq = 0 and adds nothing to dk,
+ * dv; a key no query sees gets dk = dv = 0 (with Nq = 0 every dk, dv is 0).
+ * Supported: d = 64 or 128 (else FA_ERR_UNSUPPORTED); causal 0 or 1.
+ * workspace: at least fa_bwd_workspace_size(B, Hq, Hkv, Nq, d) bytes.
+ * Other checks, errors and determinism as fa_bwd; fa_bwd_kvlen_stage runs one
+ * stage (0 D, 1 dk/dv, 2 dq) as fa_bwd_stage does.
+ */
+int fa_bwd_kvlen(const void* q, const void* k, const void* v, const void* o,
+                 const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                 int B, int Hq, int Hkv, int Nq, int Nk, int d, float scale, int causal,
+                 const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, fa_dtype dtype,
+                 void* workspace, size_t workspace_bytes, hipStream_t stream);
+int fa_bwd_kvlen_stage(int stage, const void* q, const void* k, const void* v, const void* o,
+                       const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                       int B, int Hq, int Hkv, int Nq, int Nk, int d, float scale, int causal,
+                       const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, fa_dtype dtype,
+                       void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
  * FP8 forward: the forward of fa_fwd on e4m3 inputs. The pages name e4m3
  * (torch.float8_e4m3fn) as the 8-bit attention format and credit
  * FlashAttention-3 with an FP8 forward (FlashAttention-2 全解析, blog.gitcode.com,

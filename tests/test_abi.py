@@ -21,6 +21,7 @@ def declared_functions():
 
 def test_header_declares_the_boundary():
     assert declared_functions() == ["fa_bwd", "fa_bwd_dropout", "fa_bwd_dropout_stage",
+                                    "fa_bwd_kvlen", "fa_bwd_kvlen_stage",
                                     "fa_bwd_noalloc", "fa_bwd_num_stages", "fa_bwd_softcap",
                                     "fa_bwd_softcap_stage", "fa_bwd_stage",
                                     "fa_bwd_window", "fa_bwd_window_softcap",
@@ -758,3 +759,46 @@ def test_bwd_noalloc_host_checks():
     assert fa.fa_bwd_noalloc(*args(1, 3, 16, Hkv=2)) == fa.FA_ERR_INVALID_ARG
     assert fa.fa_bwd_noalloc(*args(1, 2, 16, d=96)) == fa.FA_ERR_UNSUPPORTED
     assert fa.fa_bwd_noalloc(*args(0, 2, 16)) == fa.FA_OK
+
+
+def bkv(stage=None, **kw):
+    a = dict(q=P, k=P, v=P, o=P, do=P, lse=P, dq=P, dk=P, dv=P, B=2, Hq=4, Hkv=2, Nq=16, Nk=40,
+             d=128, scale=0.088, causal=1, cq=None, ck=None, dtype=fa.FA_BF16, ws=P,
+             wsb=1 << 20, stream=None)
+    a.update(kw)
+    args = [a[n] for n in ("q", "k", "v", "o", "do", "lse", "dq", "dk", "dv", "B", "Hq", "Hkv",
+                           "Nq", "Nk", "d", "scale", "causal", "cq", "ck", "dtype", "ws", "wsb",
+                           "stream")]
+    return fa.fa_bwd_kvlen(*args) if stage is None else fa.fa_bwd_kvlen_stage(stage, *args)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(d=256), fa.FA_ERR_UNSUPPORTED),
+    (dict(d=96), fa.FA_ERR_UNSUPPORTED),
+    (dict(causal=2), fa.FA_ERR_INVALID_ARG),
+    (dict(Nk=-1), fa.FA_ERR_INVALID_ARG),
+    (dict(Hq=3), fa.FA_ERR_INVALID_ARG),
+    (dict(dtype=7), fa.FA_ERR_INVALID_ARG),
+    (dict(cq=P), fa.FA_ERR_INVALID_ARG),
+    (dict(q=None), fa.FA_ERR_INVALID_ARG),
+    (dict(dk=None), fa.FA_ERR_INVALID_ARG),
+    (dict(dv=P + 8), fa.FA_ERR_INVALID_ARG),
+    (dict(ws=None), fa.FA_ERR_WORKSPACE),
+    (dict(wsb=64), fa.FA_ERR_WORKSPACE),
+    (dict(B=0), fa.FA_OK),
+    (dict(Nq=0, Nk=0), fa.FA_OK),
+    (dict(Nq=0, q=None, o=None, do=None, lse=None, dq=None), fa.FA_ERR_HIP),
+    (dict(Nk=0, k=None, v=None, dk=None, dv=None), fa.FA_ERR_HIP),
+    (dict(), fa.FA_ERR_HIP),
+])
+def test_bwd_kvlen_host_checks(kw, status):
+    """Bad arguments are refused on the host; valid ones (here with no device)
+    reach the launch and report FA_ERR_HIP. With no query or no key the
+    pointers of the empty side may be NULL."""
+    assert bkv(**kw) == status
+
+
+def test_bwd_kvlen_stage_index_checked():
+    assert bkv(stage=3) == fa.FA_ERR_INVALID_ARG
+    assert bkv(stage=-1) == fa.FA_ERR_INVALID_ARG
+    assert bkv(stage=1) == fa.FA_ERR_HIP
