@@ -145,11 +145,11 @@ __device__ __forceinline__ void rows_dma(float* lds, const float* lse2, const fl
 //
 // Per iteration j (j = -1 .. ntile-1), between two workgroup barriers:
 //   A: tile j+1 (Q, dO, LSE, D) has landed; the copy of tile j+2 starts
-//      into the stage that tile j-1 used;
+//      into the stage that tile j-1 used (and has until the next A to land);
 //      consumer: P, dS of tile j from LDS into registers;
 //      producer: S, dP of tile j+1;
-//   B: consumer: dK/dV products of tile j; producer: P, dS of tile j+1 into
-//      LDS.
+//   B (orders LDS accesses only): consumer: dK/dV products of tile j;
+//      producer: P, dS of tile j+1 into LDS.
 // Q/dO tiles take 3 stages: j (consumer), j+1 (producer), j+2 (in flight).
 constexpr int kDkvKeys = 128;     // keys per workgroup (32 per wave pair)
 constexpr int kDkvQ = 64;         // queries per tile
@@ -332,31 +332,47 @@ __global__ __launch_bounds__(kDkvThreads, 1) void dkdv_kernel(BwdArgs a, int n_k
   };
   const DmaPlan<T, kDkvQ, D, kDkvWaves> plan(qs, wave, lane);
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
-  auto issue = [&](int i) {   // start copying tile i into stage i % 3
+  // start copying tile i into a stage: Q at qdn, dO at qdn + TILE, the rows at
+  // ldn; qg, dog, l2g, dg are a.q, a.dout, a.lse2 and a.delta
+  auto issue = [&](int i, T* qdn, float* ldn, const T* qg, const T* dog, const float* l2g,
+                   const float* dg) __attribute__((always_inline)) {
     int r;
     const int q0 = tile_of(i, r) * kDkvQ;
-    const int h = g * a.group + r, st = i % kDkvStages;
-    const T* qp = static_cast<const T*>(a.q) + (int64_t)si.seq0 * qs + (int64_t)h * D;
-    const T* dop = static_cast<const T*>(a.dout) + (int64_t)si.seq0 * qs + (int64_t)h * D;
+    const int h = g * a.group + r;
+    const T* qp = qg + (int64_t)si.seq0 * qs + (int64_t)h * D;
+    const T* dop = dog + (int64_t)si.seq0 * qs + (int64_t)h * D;
     if (q0 + kDkvQ <= L) {
-      tile_dma_in<T, kDkvQ, D, kDkvWaves>(qd_lds[st][0], qp + (int64_t)q0 * qs, plan, wave_u);
-      tile_dma_in<T, kDkvQ, D, kDkvWaves>(qd_lds[st][1], dop + (int64_t)q0 * qs, plan, wave_u);
+      tile_dma_in<T, kDkvQ, D, kDkvWaves>(qdn, qp + (int64_t)q0 * qs, plan, wave_u);
+      tile_dma_in<T, kDkvQ, D, kDkvWaves>(qdn + TILE, dop + (int64_t)q0 * qs, plan, wave_u);
     } else {
-      tile_dma<T, kDkvQ, D, kDkvWaves>(qd_lds[st][0], qp, qs, q0, L, wave, lane);
-      tile_dma<T, kDkvQ, D, kDkvWaves>(qd_lds[st][1], dop, qs, q0, L, wave, lane);
+      tile_dma<T, kDkvQ, D, kDkvWaves>(qdn, qp, qs, q0, L, wave, lane);
+      tile_dma<T, kDkvQ, D, kDkvWaves>(qdn + TILE, dop, qs, q0, L, wave, lane);
     }
     if (wave == 0) {
       const int64_t w0 = (int64_t)h * a.ws_stride + si.seq0 + q0;
-      rows_dma<kDkvQ>(ld_lds[st], a.lse2 + w0, a.delta + w0, lane);
+      rows_dma<kDkvQ>(ldn, l2g + w0, dg + w0, lane);
     }
   };
-  if (ntile > 0) issue(0);
-  if (ntile > 1) issue(1);
+  const T* q_g = static_cast<const T*>(a.q);
+  const T* do_g = static_cast<const T*>(a.dout);
+  // tile i sits in stage i % 3; iteration j copies tile j+2, so the first
+  // iteration (j = -1) copies tile 1
+  if (ntile > 0) issue(0, qd_lds[0][0], ld_lds[0], q_g, do_g, a.lse2, a.delta);
 
   u32x4* xp = xch[pair][0];
   u32x4* xs = xch[pair][1];
   const float c = a.scale_log2;
 
+  // In iteration j the copies of tile j+2 run while the producers read tile
+  // j+1 and the consumers tile j: three distinct stages. The bodies below
+  // take the stages as restrict-qualified pointers, which tells the compiler
+  // so; otherwise the reads of tiles j and j+1 would wait for the copies of
+  // tile j+2 and leave them nothing to overlap. The copies' global sources
+  // come in restrict-qualified too: with every pointer a copy uses being a
+  // restrict parameter, the compiler can tell the copies apart from the reads
+  // without proving that no pointer escaped. Barrier B is an LDS-only barrier
+  // for the same reason: the copies of tile j+2 need to have landed only at
+  // the next iteration's barrier A.
   if (producer) {
     // K and V fragments of this pair's 32 keys (B operands), kept in registers
     u32x4 kf[NKB], vf[NKB];
@@ -367,29 +383,37 @@ __global__ __launch_bounds__(kDkvThreads, 1) void dkdv_kernel(BwdArgs a, int n_k
       kf[kb] = key < Lk ? ldg16(kp + kb * 16 + half * 8) : u32x4{0, 0, 0, 0};
       vf[kb] = key < Lk ? ldg16(vp + kb * 16 + half * 8) : u32x4{0, 0, 0, 0};
     }
-    for (int j = -1; j < ntile; ++j) {
-      wait_vmem_all();   // this wave's copies of tile j+1 (and K, V) have landed
-      __syncthreads();   // A
-      if (j + 2 < ntile) issue(j + 2);
-      __syncthreads();   // B: the consumers hold tile j's P and dS in registers
+    // iteration j: copy tile j+2 into the stage (qdn, ldn); P and dS of tile
+    // t = j+1 from the stage (qdt, ldt)
+    auto body = [&](int j, const T* __restrict__ qdt, const float* __restrict__ ldt,
+                    T* __restrict__ qdn, float* __restrict__ ldn, const T* __restrict__ qg,
+                    const T* __restrict__ dog, const float* __restrict__ l2g,
+                    const float* __restrict__ dg) __attribute__((always_inline)) {
+      if (j + 2 < ntile) issue(j + 2, qdn, ldn, qg, dog, l2g, dg);
+      lds_barrier();     // B: the consumers hold tile j's P and dS in registers
       const int t = j + 1;
       if (t < ntile) {
         int r;
         const int q0 = tile_of(t, r) * kDkvQ;
-        const int st = t % kDkvStages;
         if (!pair_idle(q0)) {
           const DropKey dk{a.seed_lo, a.seed_hi, a.keep_t};
           const int h = g * a.group + r;
           if (t < n_edge)
             dkdv_produce<T, D, CAUSAL, true, WIN, CAP, DROP>(
-                qd_lds[st][0], qd_lds[st][1], ld_lds[st], kf, vf, xp, xs, c, q0, L, key, wl, wr,
-                lane, a.cap_in, a.cap_out, &dk, b, h, a.drop_scale, off);
+                qdt, qdt + TILE, ldt, kf, vf, xp, xs, c, q0, L, key, wl, wr, lane, a.cap_in,
+                a.cap_out, &dk, b, h, a.drop_scale, off);
           else
             dkdv_produce<T, D, CAUSAL, false, WIN, CAP, DROP>(
-                qd_lds[st][0], qd_lds[st][1], ld_lds[st], kf, vf, xp, xs, c, q0, L, key, wl, wr,
-                lane, a.cap_in, a.cap_out, &dk, b, h, a.drop_scale, off);
+                qdt, qdt + TILE, ldt, kf, vf, xp, xs, c, q0, L, key, wl, wr, lane, a.cap_in,
+                a.cap_out, &dk, b, h, a.drop_scale, off);
         }
       }
+    };
+    for (int j = -1; j < ntile; ++j) {
+      wait_vmem_all();   // this wave's copies of tile j+1 (and K, V) have landed
+      __syncthreads();   // A
+      const int st = (j + 1) % kDkvStages, sn = (j + 2) % kDkvStages;
+      body(j, qd_lds[st][0], ld_lds[st], qd_lds[sn][0], ld_lds[sn], q_g, do_g, a.lse2, a.delta);
     }
   } else {
     f32x16 dkt[NCB], dvt[NCB];
@@ -398,20 +422,23 @@ __global__ __launch_bounds__(kDkvThreads, 1) void dkdv_kernel(BwdArgs a, int n_k
     for (int cb = 0; cb < NCB; ++cb) {
       dkt[cb] = f32x16{};
       dvt[cb] = f32x16{};
+      // below 2^18: with a constant added the sum cannot wrap, so the k-step
+      // constants fold into the reads' offset fields
       tro[cb][0] = tr8_off<D>(4 * half, cb * 32, lane) & kLdsAddrMask;
       tro[cb][1] = tr8_off<D>(4 * half + 8, cb * 32, lane) & kLdsAddrMask;
     }
-    for (int j = -1; j < ntile; ++j) {
-      wait_vmem_all();
-      __syncthreads();   // A: tile j's P and dS are in LDS
-      if (j + 2 < ntile) issue(j + 2);
+    // iteration j: copy tile j+2 into the stage (qdn, ldn); dK, dV products of
+    // tile j from the stage qdt
+    auto body = [&](int j, const T* __restrict__ qdt, T* __restrict__ qdn,
+                    float* __restrict__ ldn, const T* __restrict__ qg, const T* __restrict__ dog,
+                    const float* __restrict__ l2g, const float* __restrict__ dg)
+                    __attribute__((always_inline)) {
+      if (j + 2 < ntile) issue(j + 2, qdn, ldn, qg, dog, l2g, dg);
       bool active = false;
       u32x4 pb[kDkvKK], sb[kDkvKK];
-      int st = 0;
       if (j >= 0) {
         int r;
         const int q0 = tile_of(j, r) * kDkvQ;
-        st = j % kDkvStages;
         active = !pair_idle(q0);
         if (active) {
 #pragma unroll
@@ -421,28 +448,17 @@ __global__ __launch_bounds__(kDkvThreads, 1) void dkdv_kernel(BwdArgs a, int n_k
           }
         }
       }
-      __syncthreads();   // B (waits for the P, dS reads above)
+      lds_barrier();     // B (waits for the P, dS reads above; not for the copies of tile j+2)
       if (active) {
-        // the stage's Q tile; its dO tile follows TILE elements later
-        // LDS addresses stay below 2^18; masking the two terms proves the sum
-        // non-negative, which lets the k-step constants fold into the reads
-        const uint32_t qbase =
-            (lds_addr(qd_lds[0][0]) + st * (2 * TILE * (uint32_t)sizeof(T))) & kLdsAddrMask;
         constexpr uint32_t KSTEP = 16 * D * sizeof(T);   // 16 rows
-        constexpr uint32_t DO = TILE * sizeof(T);
-        uint32_t aa[NCB], ab[NCB];
-#pragma unroll
-        for (int cb = 0; cb < NCB; ++cb) {
-          aa[cb] = qbase + tro[cb][0];
-          ab[cb] = qbase + tro[cb][1];
-        }
+        constexpr uint32_t DO = TILE * sizeof(T);        // the dO tile follows the Q tile
 #pragma unroll
         for (int kk = 0; kk < kDkvKK; ++kk) {
 #pragma unroll
           for (int cb = 0; cb < NCB; ++cb) {
-            const uint32_t oa = aa[cb] + kk * KSTEP, ob = ab[cb] + kk * KSTEP;
-            dvt[cb] = mfma32<T>(lds_read_tr8(oa + DO, ob + DO), pb[kk], dvt[cb]);
-            dkt[cb] = mfma32<T>(lds_read_tr8(oa, ob), sb[kk], dkt[cb]);
+            const uint32_t oa = tro[cb][0] + kk * KSTEP, ob = tro[cb][1] + kk * KSTEP;
+            dvt[cb] = mfma32<T>(lds_tr8_at<T>(qdt, oa + DO, ob + DO), pb[kk], dvt[cb]);
+            dkt[cb] = mfma32<T>(lds_tr8_at<T>(qdt, oa, ob), sb[kk], dkt[cb]);
           }
         }
         // operand reads run one k-step (2·NCB products) ahead of the products
@@ -456,6 +472,12 @@ __global__ __launch_bounds__(kDkvThreads, 1) void dkdv_kernel(BwdArgs a, int n_k
         }
         __builtin_amdgcn_sched_group_barrier(kSgMFMA, kPer, 0);
       }
+    };
+    for (int j = -1; j < ntile; ++j) {
+      wait_vmem_all();
+      __syncthreads();   // A: tile j's P and dS are in LDS
+      const int st = (j + kDkvStages) % kDkvStages, sn = (j + 2) % kDkvStages;
+      body(j, qd_lds[st][0], qd_lds[sn][0], ld_lds[sn], q_g, do_g, a.lse2, a.delta);
     }
     if (key < Lk) {
       const int64_t ko = (int64_t)(si.seq0k + key) * kvs + (int64_t)g * D;

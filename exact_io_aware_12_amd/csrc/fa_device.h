@@ -282,10 +282,15 @@ __device__ __forceinline__ constexpr int swz(int r) {
   return D >= 128 ? (((r & 3) << 2) | ((r >> 2) & 3)) : ((((r >> 1) & 1) << 2) | ((r >> 2) & 3));
 }
 
+// Cache-policy operand of a global load: 0 keeps the lines for reuse; kCpolStream
+// marks them non-temporal (the gfx940-family NT bit), for data read exactly once.
+constexpr int kCpolStream = 2;
+
 // Stage rows r0 .. r0+R-1 (row stride `rstride` elements) of a D-column tile.
 // Rows at or past L are replaced by row L-1 (L >= 1): callers mask them.
-// The tile is split evenly over the NW waves of the workgroup.
-template <typename T, int R, int D, int NW>
+// The tile is split evenly over the NW waves of the workgroup; CPOL is the
+// copies' cache policy.
+template <typename T, int R, int D, int NW, int CPOL = 0>
 __device__ __forceinline__ void tile_dma(T* lds, const T* src, int64_t rstride, int r0, int L,
                                          int wave, int lane) {
   constexpr int CPR = D / 8;                  // 16-byte chunks per row
@@ -301,7 +306,7 @@ __device__ __forceinline__ void tile_dma(T* lds, const T* src, int64_t rstride, 
     const T* g = src + (int64_t)srow * rstride + c * 8;
 #if defined(__HIP_DEVICE_COMPILE__)  // the host pass cannot type-check this device builtin
     __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)(lds + inst * 512),
-                                     16, 0, 0);
+                                     16, 0, CPOL);
 #else
     (void)g;
 #endif
@@ -457,6 +462,16 @@ __device__ __forceinline__ float dot2_sum(u32x4 p, float acc) {
 }
 
 __device__ __forceinline__ void wait_vmem_all() { __builtin_amdgcn_s_waitcnt(0x0f70); }
+
+// Workgroup barrier for LDS traffic only: this wave's LDS reads and writes
+// have completed (lgkmcnt 0) when it arrives. Unlike __syncthreads it does not
+// wait for global loads or for global -> LDS copies still in flight (a
+// workgroup release fence does, since the copies write LDS); the caller orders
+// those copies itself. The memory clobber keeps the compiler from moving
+// memory accesses across it.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
 
 // The forward kernels normalise O by the row sum of P as rounded to T for the
 // MFMAs (the rounding of a dominant P then cancels in O). The LSE takes that

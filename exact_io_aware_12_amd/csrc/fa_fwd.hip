@@ -273,33 +273,45 @@ __global__ __launch_bounds__(kThreads, D <= 128 ? 2 : 1) void fwd_kernel(FwdArgs
 
   const DmaPlan<T, kBC, D, kWaves> plan(kvs, wave, lane);
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
-  // tile j sits in LDS buffer (j − j_lo) & 1; buf_tag fixes the tile's LDS buffer at compile time where it is known
-  // (the unrolled interior pairs), so that every LDS address is a per-lane
-  // register plus an immediate offset
-  auto step = [&](auto edge_tag, auto buf_tag, int j) __attribute__((always_inline)) {
+  // One tile: the copies of tile j+1 go into one LDS buffer (kn, vn) while
+  // tile j is read from the other (kt, vt). Restrict-qualified, the two
+  // buffers are known to be distinct, so the compiler does not make the reads
+  // of tile j wait for the copies in flight (without it the transposing reads
+  // of V waited for them, and the next tile's copy overlapped only the first
+  // half of a tile). One body serves every call site: called with different
+  // buffers, its pointer arguments stay arguments until it is inlined, which
+  // is where the compiler turns the qualifiers into alias information.
+  auto body = [&](auto edge_tag, int j, const T* __restrict__ kt, const T* __restrict__ vt,
+                  T* __restrict__ kn, T* __restrict__ vn) __attribute__((always_inline)) {
     constexpr bool EDGE = decltype(edge_tag)::value;
-    constexpr int FIXED = decltype(buf_tag)::value;   // 0, 1, or -1 for (j − j_lo) & 1
-    const int BUF = FIXED >= 0 ? FIXED : ((j - j_lo) & 1);
     const int kv0 = j * kBC;
-    wait_vmem_all();   // this thread's copies of tile j have landed
-    __syncthreads();   // everyone's have, and tile j-1 is no longer read
     if (j + 1 < ntiles) {
       const int n0 = kv0 + kBC;
       if (n0 + kBC <= Lk) {
-        tile_dma_in<T, kBC, D, kWaves>(lds[BUF ^ 1][0], kp + (int64_t)n0 * kvs, plan, wave_u);
-        tile_dma_in<T, kBC, D, kWaves>(lds[BUF ^ 1][1], vp + (int64_t)n0 * kvs, plan, wave_u);
+        tile_dma_in<T, kBC, D, kWaves>(kn, kp + (int64_t)n0 * kvs, plan, wave_u);
+        tile_dma_in<T, kBC, D, kWaves>(vn, vp + (int64_t)n0 * kvs, plan, wave_u);
       } else {
-        tile_dma<T, kBC, D, kWaves>(lds[BUF ^ 1][0], kp, kvs, n0, Lk, wave, lane);
-        tile_dma<T, kBC, D, kWaves>(lds[BUF ^ 1][1], vp, kvs, n0, Lk, wave, lane);
+        tile_dma<T, kBC, D, kWaves>(kn, kp, kvs, n0, Lk, wave, lane);
+        tile_dma<T, kBC, D, kWaves>(vn, vp, kvs, n0, Lk, wave, lane);
       }
     }
     // every key of the tile is after this wave's rows
     if (EDGE && CAUSAL && kv0 > wq_last + off) return;
     if (EDGE && WIN && (kv0 > wq_last + wr || kv0 + kBC - 1 < wq_first - wl))
       return;   // the tile lies outside the windows of all this wave's rows
-    fwd_tile<T, D, CAUSAL, EDGE, WIN, CAP, DROP>(lds[BUF][0], lds[BUF][1], qf, o, mc, l, lr, c,
-                                                 kv0, Lk, qrow + off, wl, wr, lane, cap_in,
-                                                 cap_out, &dk, b, h, KVLEN);
+    fwd_tile<T, D, CAUSAL, EDGE, WIN, CAP, DROP>(kt, vt, qf, o, mc, l, lr, c, kv0, Lk,
+                                                 qrow + off, wl, wr, lane, cap_in, cap_out, &dk,
+                                                 b, h, KVLEN);
+  };
+  // tile j sits in LDS buffer (j − j_lo) & 1; buf_tag fixes the tile's LDS
+  // buffer at compile time where it is known (the unrolled interior pairs), so
+  // that every LDS address is a per-lane register plus an immediate offset
+  auto step = [&](auto edge_tag, auto buf_tag, int j) __attribute__((always_inline)) {
+    constexpr int FIXED = decltype(buf_tag)::value;   // 0, 1, or -1 for (j − j_lo) & 1
+    const int BUF = FIXED >= 0 ? FIXED : ((j - j_lo) & 1);
+    wait_vmem_all();   // this thread's copies of tile j have landed
+    __syncthreads();   // everyone's have, and tile j-1 is no longer read
+    body(edge_tag, j, lds[BUF][0], lds[BUF][1], lds[BUF ^ 1][0], lds[BUF ^ 1][1]);
   };
   using B0 = std::integral_constant<int, 0>;
   using B1 = std::integral_constant<int, 1>;
