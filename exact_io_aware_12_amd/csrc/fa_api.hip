@@ -607,8 +607,9 @@ int check_kvcache(int B, int Hq, int Hkv, int Nq, int Nk, int d, float scale, in
 // decode_kernel workgroups resident per CU and CUs per device: the runtime's
 // occupancy figure for the exact instantiation when a device is present
 // (cached per configuration: one GPU type per process), else the same bound
-// from LDS (160 KiB per CU) and registers (the counts this build allocates:
-// 2 waves per SIMD at d <= 128, 3 for an e4m3 cache at d = 64, 1 at d = 256).
+// from LDS (160 KiB per CU) and registers (two-wave workgroups; the waves per
+// SIMD the register counts of this build allow: 4 at d = 64, 2 at d = 128 (3
+// for an e4m3 cache), 1 at d = 256).
 struct Residency {
   int per_cu, cus;
 };
@@ -634,7 +635,7 @@ Residency decode_residency(int d, bool kv8, int dtype, int causal) {
     return {per_cu, cus};
   }
   const int by_lds = (160 * 1024) / fa::decode_lds_bytes(d, kv8);
-  const int by_regs = 4 * (d == 256 ? 1 : (d == 64 && kv8) ? 3 : 2);
+  const int by_regs = 2 * (d == 256 ? 1 : d == 128 ? (kv8 ? 3 : 2) : 4);
   return {std::max(1, std::min(by_lds, by_regs)), 256};
 }
 

@@ -3,7 +3,7 @@
 // Per batch entry b the cache holds L_b valid positions; the Nq new queries
 // are its newest Nq positions (query i at L_b − Nq + i) and, when causal, see
 // the keys at or before their position. The cache is split along the keys
-// into `splits` ranges; one wavefront per (32-row block, split, KV head,
+// into `splits` ranges; one workgroup per (32-row block, split, KV head,
 // entry) streams its range of K and V through LDS once and computes, for the
 // rows of that block, a partial O over its keys and the matching log-sum-exp.
 // The rows are the Hq/Hkv query heads of the KV head times the Nq queries,
@@ -12,11 +12,17 @@
 // LSE = ln Σ_s e^{LSE_s}, O = Σ_s e^{LSE_s − LSE}·O_s), the identity that also
 // merges results computed on different GPUs.
 //
-// Inside a wave the tile step is the forward's: Sᵀ = K·Qᵀ on MFMA (a lane per
-// row), masking, online softmax with a lazily raised reference max, Oᵀ += Vᵀ·Pᵀ
-// with Vᵀ read transposed from the row-major LDS tile. The work per byte is
-// small (d FLOP per loaded K or V element per row), so the kernel is bound by
-// HBM: K/V tiles of 32 keys are copied global -> LDS three stages deep. Every
+// The tile step is the forward's: Sᵀ = K·Qᵀ on MFMA (a lane per row), masking,
+// online softmax with a lazily raised reference max, Oᵀ += Vᵀ·Pᵀ with Vᵀ read
+// transposed from the row-major LDS tile. The work per byte is small (d FLOP
+// per loaded K or V element per row), so the kernel is bound by HBM: K/V tiles
+// of 32 keys are copied global -> LDS three stages deep. A workgroup has two
+// waves: one only issues the copies and waits for them, the other only
+// computes, with one LDS barrier per tile between them. In one wave doing
+// both, the copies of the next tile and the arithmetic of the current one
+// overlapped poorly (issuing a tile's copies held the wave back), and even a
+// few hundred VALU operations per tile cost a large part of the bandwidth; with
+// the roles split, the arithmetic hides under the copies. Every
 // cache byte is read exactly once, so the copies carry the non-temporal cache
 // policy: on MI355X that alone moved a copy-only pass of this access pattern
 // from 5.9 to 6.7 TB/s.
@@ -152,7 +158,7 @@ struct CacheElem<T, true> {
 // visible; the key ranges then start at the entry's floor L − Nq − wl) and,
 // when a.cap_on, soft-capped logits a.cap_out·tanh(z·a.cap_in) (scale_log2 = 1).
 template <typename T, int D, bool CAUSAL, bool KV8, bool EXT = false>
-__global__ __launch_bounds__(64) void decode_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(128, D <= 128 ? 2 : 1) void decode_kernel(DecodeArgs a) {
   using C = typename CacheElem<T, KV8>::type;   // cache element: T or an e4m3 code
   constexpr int NKB = D / 16;
   constexpr int NCB = D / 32;
@@ -162,7 +168,10 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeArgs a) {
   __shared__ __attribute__((aligned(1024))) C k_lds[kStages][TILE];
   __shared__ __attribute__((aligned(1024))) C v_lds[kStages][TILE];
 
-  const int lane = threadIdx.x, col = lane & 31, half = lane >> 5;
+  // wave 0 copies, wave 1 computes; the wave index is the same on every lane
+  // (readfirstlane lets the compiler see that, so branches on it are scalar)
+  const int lane = threadIdx.x & 63, col = lane & 31, half = lane >> 5;
+  const bool copier = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) == 0;
   int idx = blockIdx.x;
   const int rb = idx % a.n_rb;
   idx /= a.n_rb;
@@ -197,9 +206,11 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeArgs a) {
     const C* kp = static_cast<const C*>(a.k) + (int64_t)b * a.Nk * kvs + (int64_t)g * D;
     const C* vp = static_cast<const C*>(a.v) + (int64_t)b * a.Nk * kvs + (int64_t)g * D;
     const int ntiles = (k_end - k_begin + kTK - 1) / kTK;
-    // copies of tile t into the stage (kd, vd); rows past k_end repeat row
-    // k_end-1 (masked below)
-    auto issue = [&](C* kd, C* vd, int t) __attribute__((always_inline)) {
+    // copies of tile t into its stage; rows past k_end repeat row k_end-1
+    // (masked below)
+    auto issue = [&](int t) __attribute__((always_inline)) {
+      C* kd = k_lds[t % kStages];
+      C* vd = v_lds[t % kStages];
       if constexpr (KV8) {
         tile_dma_kv8<D>(kd, kp, kvs, k_begin + t * kTK, k_end, lane);
         tile_dma_kv8<D>(vd, vp, kvs, k_begin + t * kTK, k_end, lane);
@@ -208,6 +219,24 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeArgs a) {
         tile_dma<T, kTK, D, 1, kCpolStream>(vd, vp, kvs, k_begin + t * kTK, k_end, 0, lane);
       }
     };
+    if (copier) {
+      // Each role runs its own loop (one barrier per tile in each, the same
+      // count), so neither role's loop state takes registers from the other.
+      // Iteration t: start tile t+kStages-1 into the stage tile t-1 left (the
+      // computing wave is done with it, by the previous barrier), then wait
+      // until tile t+1 has landed (at most kStages-2 newer tiles outstanding).
+#pragma unroll
+      for (int p = 0; p < kStages - 1; ++p)
+        if (p < ntiles) issue(p);
+      wait_tiles<2 * PER, kStages - 2>(ntiles - 1);
+      lds_barrier();   // tile 0 is in LDS
+      for (int t = 0; t < ntiles; ++t) {
+        if (t + kStages - 1 < ntiles) issue(t + kStages - 1);
+        wait_tiles<2 * PER, kStages - 2>(ntiles - 2 - t);
+        lds_barrier();   // tile t+1 is in LDS; tile t is no longer read
+      }
+      return;
+    }
     u32x4 qf[NKB];
     {
       const T* qp = static_cast<const T*>(a.q) + (((int64_t)b * a.Nq + qi) * a.Hq + h) * D;
@@ -220,22 +249,11 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeArgs a) {
         qf[kb] = row_ok ? ldg16(qp + col0) : u32x4{0, 0, 0, 0};
       }
     }
-    // tiles 0 .. kStages-2 in flight
-#pragma unroll
-    for (int p = 0; p < kStages - 1; ++p)
-      if (p < ntiles) issue(k_lds[p], v_lds[p], p);
     const float c = a.scale_log2;
     const int krow = KV8 ? kv8_key(col) : col;   // the tile row MFMA row `col` reads
 
-    // One tile: start the copies of tile tn (if tn < ntiles) into the stage
-    // (kn, vn) and consume tile t from the stage (kt, vt). The two stages are
-    // distinct; saying so with restrict-qualified pointers lets the compiler
-    // see that the reads of tile t do not depend on the copies in flight, so
-    // it does not make them wait for those copies (the explicit wait before
-    // the step is what orders the copies of tile t before its reads).
-    auto step = [&](const C* __restrict__ kt, const C* __restrict__ vt, C* __restrict__ kn,
-                    C* __restrict__ vn, int t, int tn) __attribute__((always_inline)) {
-      if (tn < ntiles) issue(kn, vn, tn);
+    // the computing wave's step: consume tile t from the stage (kt, vt)
+    auto step = [&](const C* kt, const C* vt, int t) __attribute__((always_inline)) {
       const int kbase = k_begin + t * kTK;
 
       f32x16 s = f32x16{};
@@ -308,19 +326,17 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeArgs a) {
       }
     };
 
-    // tile t+kStages-1 starts once tile t has landed
+    lds_barrier();   // tile 0 is in LDS
     for (int t = 0; t < ntiles; ++t) {
-      // tile t has landed once only the copies of the newer tiles in flight
-      // (at most kStages-2 of them) are outstanding
-      wait_tiles<2 * PER, kStages - 2>(ntiles - 1 - t);
-      const int st = t % kStages, sn = (t + kStages - 1) % kStages;   // sn: the stage of tile t-1
-      step(k_lds[st], v_lds[st], k_lds[sn], v_lds[sn], t, t + kStages - 1);
+      step(k_lds[t % kStages], v_lds[t % kStages], t);
+      lds_barrier();   // done with tile t; tile t+1 is in LDS
     }
   }
 
   // partial result of this split: normalised O and its LSE (−inf, O = 0 if no key)
   // O is normalised by the sum of the rounded P that the MFMAs consumed;
   // the LSE as in kLseFromUnrounded
+  if (copier) return;   // (a workgroup with an empty key range)
   const float lr_tot = wave_sum_halves(lr);
   const float l_tot = kLseFromUnrounded<T> ? wave_sum_halves(l) : lr_tot;
   if (row_ok) {
@@ -421,7 +437,7 @@ hipError_t launch(const DecodeArgs& a, int stage, hipStream_t s) {
   (void)hipGetLastError();  // drop an error left pending by earlier, unrelated HIP calls
   if (stage < 0 || stage == 0) {
     const int64_t g1 = (int64_t)a.n_rb * a.splits * a.Hkv * a.B;
-    hipLaunchKernelGGL((decode_kernel<T, D, CAUSAL, KV8, EXT>), dim3((unsigned)g1), dim3(64), 0,
+    hipLaunchKernelGGL((decode_kernel<T, D, CAUSAL, KV8, EXT>), dim3((unsigned)g1), dim3(128), 0,
                        s, a);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -436,14 +452,14 @@ hipError_t launch(const DecodeArgs& a, int stage, hipStream_t s) {
   return hipSuccess;
 }
 
-// Resident one-wave workgroups of one decode_kernel instantiation per CU, as
+// Resident two-wave workgroups of one decode_kernel instantiation per CU, as
 // the runtime computes them from its LDS and register allocation; 0 if the
 // runtime cannot tell (no device).
 template <typename T, int D, bool CAUSAL, bool KV8>
 int occupancy() {
   int n = 0;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-          &n, reinterpret_cast<const void*>(&decode_kernel<T, D, CAUSAL, KV8>), 64, 0) !=
+          &n, reinterpret_cast<const void*>(&decode_kernel<T, D, CAUSAL, KV8>), 128, 0) !=
       hipSuccess) {
     (void)hipGetLastError();
     return 0;

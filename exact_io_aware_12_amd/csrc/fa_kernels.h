@@ -117,7 +117,7 @@ int decode_tile_keys();
 // stage < 0: both stages; 0: per-range partial results; 1: merge into o, lse.
 // kv8: k and v hold e4m3fn codes (q and o stay 16-bit).
 int decode_num_stages();
-// decode_kernel workgroups (one wave each) resident per CU for this instantiation,
+// decode_kernel workgroups (two waves each) resident per CU for this instantiation,
 // from the runtime's occupancy calculation; 0 when no device is available.
 int decode_resident_per_cu(bool bf16_in, int d, bool causal, bool kv8);
 int decode_lds_bytes(int d, bool kv8);   // LDS per decode_kernel workgroup
