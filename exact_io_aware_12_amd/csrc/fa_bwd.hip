@@ -113,19 +113,29 @@ __global__ __launch_bounds__(kThreads) void delta_kernel(BwdArgs a) {
 // lds[0..R-1] and lds[R..2R-1]: one instruction, lanes 0 .. R/2-1 of one wave.
 // Rows past the sequence end read neighbouring workspace entries; the callers
 // mask those rows.
+// Buffer-form copies (one per array, on that array's lanes): they issue far
+// faster than flat-address copies beside the MFMA work of other waves.
 template <int R>
 __device__ __forceinline__ void rows_dma(float* lds, const float* lse2, const float* delta,
                                          int lane) {
   constexpr int LN = R / 4;   // lanes per array
-  if (lane < 2 * LN) {
-    const float* g = lane < LN ? lse2 + 4 * lane : delta + 4 * (lane - LN);
 #if defined(__HIP_DEVICE_COMPILE__)
-    __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)lds, 16, 0, 0);
-#else
-    (void)g;
-    (void)lds;
-#endif
+  typedef __attribute__((address_space(3))) void lds_void;
+  if (lane < LN) {
+    const __amdgpu_buffer_rsrc_t r =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(lse2), 0, 0x7fffffff, kBufferDword3);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds, 16, 16 * lane, 0, 0, 0);
+  } else if (lane < 2 * LN) {
+    const __amdgpu_buffer_rsrc_t r =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(delta), 0, 0x7fffffff, kBufferDword3);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds, 16, 16 * (lane - LN), 0, 0, 0);
   }
+#else
+  (void)lds;
+  (void)lse2;
+  (void)delta;
+  (void)lane;
+#endif
 }
 
 // ---------------------------------------------------------------------------

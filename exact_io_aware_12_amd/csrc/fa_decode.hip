@@ -33,6 +33,8 @@
 // (every e4m3 value is exact in bf16 and in fp16), so the products are those
 // of the 16-bit kernel on the decoded cache; the per-tensor descales enter
 // the score scale (K) and the output normalisation (V).
+#include <type_traits>
+
 #include "fa_device.h"
 #include "fa_kernels.h"
 
@@ -96,6 +98,42 @@ __device__ __forceinline__ void tile_dma_kv8(uint8_t* lds, const uint8_t* src, i
     (void)g;
 #endif
   }
+}
+
+// Per-lane byte offsets of tile_dma_kv8's copies relative to the tile's first
+// row, and the buffer-form copy of a tile whose kTK rows all lie inside the
+// range (faster to issue than the flat-address form beside other waves' MFMAs).
+template <int D>
+struct Kv8Plan {
+  static constexpr int CPR = D / 16;
+  static constexpr int RPI = 64 / CPR;
+  static constexpr int PER = kTK / RPI;   // copy instructions per tile
+  uint32_t off[PER];
+  __device__ __forceinline__ Kv8Plan(int64_t rstride, int lane) {
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int row = u * RPI + lane / CPR;
+      const int c = (lane % CPR) ^ kv8_swz<D>(row);
+      off[u] = (uint32_t)(row * rstride + c * 16);
+    }
+  }
+};
+template <int D>
+__device__ __forceinline__ void tile_dma_kv8_in(uint8_t* lds, const uint8_t* src_r0,
+                                                const Kv8Plan<D>& p) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  const __amdgpu_buffer_rsrc_t rsrc =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(src_r0), 0, 0x7fffffff, kBufferDword3);
+#pragma unroll
+  for (int u = 0; u < Kv8Plan<D>::PER; ++u)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        rsrc, (__attribute__((address_space(3))) void*)(lds + u * 1024), 16, p.off[u], 0, 0,
+        kCpolStream);
+#else
+  (void)lds;
+  (void)src_r0;
+  (void)p;
+#endif
 }
 
 // Eight e4m3 codes (bytes of w0 then w1, in order) as eight values of T,
@@ -206,17 +244,27 @@ __global__ __launch_bounds__(128, D <= 128 ? 2 : 1) void decode_kernel(DecodeArg
     const C* kp = static_cast<const C*>(a.k) + (int64_t)b * a.Nk * kvs + (int64_t)g * D;
     const C* vp = static_cast<const C*>(a.v) + (int64_t)b * a.Nk * kvs + (int64_t)g * D;
     const int ntiles = (k_end - k_begin + kTK - 1) / kTK;
-    // copies of tile t into its stage; rows past k_end repeat row k_end-1
-    // (masked below)
-    auto issue = [&](int t) __attribute__((always_inline)) {
+    // copies of tile t into its stage: a tile inside the range from its first
+    // row's address with the buffer form; the range's ragged last tile with the
+    // flat form, whose rows past k_end repeat row k_end-1 (masked below)
+    auto issue = [&](int t, const auto& plan) __attribute__((always_inline)) {
       C* kd = k_lds[t % kStages];
       C* vd = v_lds[t % kStages];
-      if constexpr (KV8) {
-        tile_dma_kv8<D>(kd, kp, kvs, k_begin + t * kTK, k_end, lane);
-        tile_dma_kv8<D>(vd, vp, kvs, k_begin + t * kTK, k_end, lane);
+      const int r0 = k_begin + t * kTK;
+      if (r0 + kTK <= k_end) {
+        if constexpr (KV8) {
+          tile_dma_kv8_in<D>(kd, kp + (int64_t)r0 * kvs, plan);
+          tile_dma_kv8_in<D>(vd, vp + (int64_t)r0 * kvs, plan);
+        } else {
+          tile_dma_in<T, kTK, D, 1, kCpolStream>(kd, kp + (int64_t)r0 * kvs, plan, 0);
+          tile_dma_in<T, kTK, D, 1, kCpolStream>(vd, vp + (int64_t)r0 * kvs, plan, 0);
+        }
+      } else if constexpr (KV8) {
+        tile_dma_kv8<D>(kd, kp, kvs, r0, k_end, lane);
+        tile_dma_kv8<D>(vd, vp, kvs, r0, k_end, lane);
       } else {
-        tile_dma<T, kTK, D, 1, kCpolStream>(kd, kp, kvs, k_begin + t * kTK, k_end, 0, lane);
-        tile_dma<T, kTK, D, 1, kCpolStream>(vd, vp, kvs, k_begin + t * kTK, k_end, 0, lane);
+        tile_dma<T, kTK, D, 1, kCpolStream>(kd, kp, kvs, r0, k_end, 0, lane);
+        tile_dma<T, kTK, D, 1, kCpolStream>(vd, vp, kvs, r0, k_end, 0, lane);
       }
     };
     if (copier) {
@@ -225,13 +273,18 @@ __global__ __launch_bounds__(128, D <= 128 ? 2 : 1) void decode_kernel(DecodeArg
       // Iteration t: start tile t+kStages-1 into the stage tile t-1 left (the
       // computing wave is done with it, by the previous barrier), then wait
       // until tile t+1 has landed (at most kStages-2 newer tiles outstanding).
+      using Plan = std::conditional_t<KV8, Kv8Plan<D>, DmaPlan<T, kTK, D, 1>>;
+      const Plan plan = [&] {
+        if constexpr (KV8) return Kv8Plan<D>(kvs, lane);
+        else return DmaPlan<T, kTK, D, 1>(kvs, 0, lane);
+      }();
 #pragma unroll
       for (int p = 0; p < kStages - 1; ++p)
-        if (p < ntiles) issue(p);
+        if (p < ntiles) issue(p, plan);
       wait_tiles<2 * PER, kStages - 2>(ntiles - 1);
       lds_barrier();   // tile 0 is in LDS
       for (int t = 0; t < ntiles; ++t) {
-        if (t + kStages - 1 < ntiles) issue(t + kStages - 1);
+        if (t + kStages - 1 < ntiles) issue(t + kStages - 1, plan);
         wait_tiles<2 * PER, kStages - 2>(ntiles - 2 - t);
         lds_barrier();   // tile t+1 is in LDS; tile t is no longer read
       }

@@ -342,8 +342,11 @@ struct DmaPlan {
 // points at the tile's first row and `wave` is the same on all lanes. A
 // buffer load with a 32-bit per-lane offset keeps the base in scalar
 // registers; the resource covers 2 GiB from the tile's first row and the
-// offsets stay far below that.
-template <typename T, int R, int D, int NW>
+// offsets stay far below that. The buffer form also issues far faster than
+// the flat-address form (global_load_lds) while another wave on the same SIMD
+// runs MFMAs: measured on MI355X, 8 copies took 149 cycles against 1925.
+// CPOL is the copies' cache policy.
+template <typename T, int R, int D, int NW, int CPOL = 0>
 __device__ __forceinline__ void tile_dma_in(T* lds, const T* src_r0, const DmaPlan<T, R, D, NW>& p,
                                             int wave) {
 #if defined(__HIP_DEVICE_COMPILE__)  // the host pass cannot type-check these device builtins
@@ -354,7 +357,7 @@ __device__ __forceinline__ void tile_dma_in(T* lds, const T* src_r0, const DmaPl
     __builtin_amdgcn_raw_ptr_buffer_load_lds(
         rsrc,
         (__attribute__((address_space(3))) void*)(lds + (wave * DmaPlan<T, R, D, NW>::PER + u) * 512),
-        16, p.off[u], 0, 0, 0);
+        16, p.off[u], 0, 0, CPOL);
 #else
   (void)lds;
   (void)src_r0;
