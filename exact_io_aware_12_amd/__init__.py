@@ -39,7 +39,11 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 
 
 def lib_path() -> str:
-    return os.path.join(_HERE, "libfa.so")
+    """libfa.so, or with FA_DEBUG=1 in the environment libfa_debug.so: the same
+    kernels built with FA_DEBUG (cu_seqlens checked on the host before each
+    launch, a synchronisation after each launch)."""
+    return os.path.join(_HERE, "libfa_debug.so" if os.environ.get("FA_DEBUG") == "1"
+                        else "libfa.so")
 
 
 class FaError(RuntimeError):
@@ -82,6 +86,7 @@ _SIGS = {
     "fa_kvcache_fp8_num_splits": (_I, [_I] * 6),
     "fa_fwd_kvcache_workspace_size": (_SZ, [_I] * 7),
     "fa_status_string": (ctypes.c_char_p, [_I]),
+    "fa_check_cu_seqlens": (_I, [_VP, _I, _I]),
 }
 # each staged entry point takes a leading stage index, then its parent's arguments
 for _n in ("fa_bwd", "fa_bwd_window", "fa_bwd_window_softcap", "fa_bwd_softcap",
@@ -92,7 +97,7 @@ for _n in ("fa_bwd", "fa_bwd_window", "fa_bwd_window_softcap", "fa_bwd_softcap",
 def _load():
     path = lib_path()
     if not os.path.exists(path):
-        raise ImportError(f"{path} is missing: build it with `python exact_io_aware_12_amd/build.py` "
+        raise ImportError(f"{path} is missing: build it with `python exact_io_aware_12_amd/build.py --all` "
                           "(there is no non-HIP fallback)")
     # torch bundles its own HIP runtime under the same soname (libamdhip64.so.7).
     # Loading torch first makes libfa.so bind to that runtime, so the tensors torch

@@ -1,7 +1,10 @@
 // C ABI of libfa.so (declared in include/fa.h): argument checks, then the
-// kernel launches. Nothing here allocates memory. The only global state is
-// the cache of the decode kernel's occupancy figures (decode_residency),
-// filled once per process with values that are the same for every caller.
+// kernel launches. Nothing here allocates device memory. The only global
+// state is the cache of the decode kernel's occupancy figures
+// (decode_residency), filled once per process with values that are the same
+// for every caller. Built with FA_DEBUG defined, every cu_seqlens argument is
+// copied to the host and checked before the launch, and every launch is
+// followed by a synchronisation that reports a failed kernel.
 #include <algorithm>
 #include <atomic>
 #include <mutex>
@@ -11,7 +14,44 @@
 #include "fa.h"
 #include "fa_kernels.h"
 
+#ifdef FA_DEBUG
+#include <vector>
+#endif
+
 namespace {
+
+// The status of a call whose launches returned `e`. Debug builds also wait for
+// the work and report a kernel that failed.
+int launched(hipError_t e, hipStream_t stream) {
+  if (e != hipSuccess) return FA_ERR_HIP;
+#ifdef FA_DEBUG
+  if (hipStreamSynchronize(stream) != hipSuccess || hipGetLastError() != hipSuccess)
+    return FA_ERR_HIP;
+#else
+  (void)stream;
+#endif
+  return FA_OK;
+}
+
+// Debug builds: fa_check_cu_seqlens on a host copy of the device array `cu`
+// (B+1 entries, lengths at most N). Release builds: FA_OK without reading it.
+int debug_cu_seqlens(const int32_t* cu, int B, int N, hipStream_t stream) {
+#ifdef FA_DEBUG
+  if (cu == nullptr || B <= 0) return FA_OK;
+  std::vector<int32_t> h((size_t)B + 1);
+  if (hipMemcpyAsync(h.data(), cu, h.size() * sizeof(int32_t), hipMemcpyDeviceToHost, stream) !=
+          hipSuccess ||
+      hipStreamSynchronize(stream) != hipSuccess)
+    return FA_ERR_HIP;
+  return fa_check_cu_seqlens(h.data(), B, N);
+#else
+  (void)cu;
+  (void)B;
+  (void)N;
+  (void)stream;
+  return FA_OK;
+#endif
+}
 
 constexpr float kLog2e = 1.4426950408889634f;
 
@@ -125,9 +165,11 @@ int fwd_common(const void* q, const void* k, const void* v, void* o, float* lse,
   a.keep_t = keep_t;
   a.drop_scale = 256.f / (float)keep_t;
   if ((int64_t)a.n_qtiles * Hq * B >= (int64_t)1 << 31) return FA_ERR_UNSUPPORTED;
+  st = debug_cu_seqlens(cu_seqlens, B, N, stream);
+  if (st != FA_OK) return st;
   hipError_t e = fa::launch_fwd(a, dtype == FA_BF16, d, mask, cu_seqlens != nullptr,
                                 softcap != 0.f, dropout_p != 0.f, stream);
-  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+  return launched(e, stream);
 }
 
 }  // namespace
@@ -182,8 +224,13 @@ int fa_fwd_kvlen(const void* q, const void* k, const void* v, void* o, float* ls
   a.keep_t = 256;
   a.drop_scale = 1.f;
   if ((int64_t)a.n_qtiles * Hq * B >= (int64_t)1 << 31) return FA_ERR_UNSUPPORTED;
+  if (varlen) {
+    int st = debug_cu_seqlens(cu_seqlens_q, B, Nq, stream);
+    if (st == FA_OK) st = debug_cu_seqlens(cu_seqlens_k, B, Nk, stream);
+    if (st != FA_OK) return st;
+  }
   hipError_t e = fa::launch_fwd_kvlen(a, dtype == FA_BF16, d, causal != 0, varlen, stream);
-  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+  return launched(e, stream);
 }
 
 int fa_fwd_softcap(const void* q, const void* k, const void* v, void* o, float* lse, int B,
@@ -259,9 +306,11 @@ int fa_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse,
   a.wl = a.wr = 0;
   a.o_scale = descale_v;
   if ((int64_t)a.n_qtiles * Hq * B >= (int64_t)1 << 31) return FA_ERR_UNSUPPORTED;
+  st = debug_cu_seqlens(cu_seqlens, B, N, stream);
+  if (st != FA_OK) return st;
   hipError_t e = fa::launch_fwd_fp8(a, out_dtype == FA_BF16, d, causal != 0,
                                     cu_seqlens != nullptr, stream);
-  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+  return launched(e, stream);
 }
 
 size_t fa_bwd_workspace_size(int B, int Hq, int Hkv, int N, int d) {
@@ -325,9 +374,11 @@ int bwd_common(int stage, const void* q, const void* k, const void* v, const voi
   a.seed_hi = (uint32_t)(seed >> 32);
   a.keep_t = keep_t;
   a.drop_scale = 256.f / (float)keep_t;
+  st = debug_cu_seqlens(cu_seqlens, B, N, stream);
+  if (st != FA_OK) return st;
   hipError_t e = fa::launch_bwd(a, dtype == FA_BF16, d, mask, cu_seqlens != nullptr,
                                 softcap != 0.f, dropout_p != 0.f, stage, stream);
-  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+  return launched(e, stream);
 }
 
 }  // namespace
@@ -544,8 +595,13 @@ int bwd_kvlen_common(int stage, const void* q, const void* k, const void* v, con
   a.seed_lo = a.seed_hi = 0;
   a.keep_t = 256;
   a.drop_scale = 1.f;
+  if (varlen) {
+    int st = debug_cu_seqlens(cu_seqlens_q, B, Nq, stream);
+    if (st == FA_OK) st = debug_cu_seqlens(cu_seqlens_k, B, Nk, stream);
+    if (st != FA_OK) return st;
+  }
   hipError_t e = fa::launch_bwd_kvlen(a, dtype == FA_BF16, d, causal != 0, varlen, stage, stream);
-  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+  return launched(e, stream);
 }
 
 }  // namespace
@@ -742,7 +798,7 @@ int kvcache_common(int stage, const void* q, const void* k_cache, const void* v_
   if (!std::isfinite(a.scale_log2) || !(a.scale_log2 > 0.f)) return FA_ERR_INVALID_ARG;
   if ((int64_t)a.n_rb * sp * Hkv * B >= (int64_t)1 << 31) return FA_ERR_UNSUPPORTED;
   hipError_t e = fa::launch_decode(a, dtype == FA_BF16, d, causal != 0, kv8, stage, stream);
-  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+  return launched(e, stream);
 }
 
 }  // namespace
@@ -824,7 +880,7 @@ int fa_fwd_kvcache_local(const void* q, const void* k_cache, const void* v_cache
   a.cap_out = cap_out;
   if ((int64_t)a.n_rb * sp * Hkv * B >= (int64_t)1 << 31) return FA_ERR_UNSUPPORTED;
   hipError_t e = fa::launch_decode_ext(a, dtype == FA_BF16, d, causal != 0, -1, stream);
-  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+  return launched(e, stream);
 }
 
 int fa_fwd_kvcache_fp8(const void* q, const void* k_cache, const void* v_cache,
@@ -846,6 +902,16 @@ int fa_fwd_kvcache_fp8_stage(int stage, const void* q, const void* k_cache, cons
   return kvcache_common(stage, q, k_cache, v_cache, cache_seqlens, o, lse, B, Hq, Hkv, Nq, Nk, d,
                         scale, causal, num_splits, dtype, workspace, workspace_bytes, stream, true,
                         descale_k, descale_v);
+}
+
+int fa_check_cu_seqlens(const int32_t* cu_seqlens_host, int B, int N) {
+  if (cu_seqlens_host == nullptr || B < 0 || N < 0) return FA_ERR_INVALID_ARG;
+  if (cu_seqlens_host[0] != 0) return FA_ERR_INVALID_ARG;
+  for (int s = 0; s < B; ++s) {
+    const int64_t len = (int64_t)cu_seqlens_host[s + 1] - cu_seqlens_host[s];
+    if (len < 0 || len > N) return FA_ERR_INVALID_ARG;
+  }
+  return FA_OK;
 }
 
 const char* fa_status_string(int status) {

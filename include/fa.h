@@ -52,7 +52,8 @@
  * request outside the supported envelope, so the caller can fall back to
  * another attention implementation. FA_OK means the work was enqueued on
  * `stream` (NULL = the default stream); device faults surface at the caller's
- * next synchronisation. B = 0 or N = 0 is a no-op returning FA_OK.
+ * next synchronisation (with FA_DEBUG, before the call returns; see
+ * fa_check_cu_seqlens). B = 0 or N = 0 is a no-op returning FA_OK.
  * A launching call clears the calling thread's pending HIP error
  * (hipGetLastError) first, so that FA_ERR_HIP reports its own launches only.
  *
@@ -465,6 +466,25 @@ size_t fa_fwd_kvcache_workspace_size(int B, int Hq, int Hkv, int Nq, int Nk, int
 
 /* Static, NUL-terminated text for a status code. */
 const char* fa_status_string(int status);
+
+/*
+ * Host check of a cu_seqlens array: the packed variable-length batch that
+ * takes the place of a padding mask (the Variable length convention above).
+ * cu_seqlens_host is HOST memory holding a copy of the device array an entry
+ * point would take; exactly its B+1 entries are read. It holds when
+ * cu_seqlens_host[0] = 0 and every length cu_seqlens_host[s+1] −
+ * cu_seqlens_host[s] lies in [0, N] (so the entries are non-decreasing and
+ * the last is at most B·N). Returns FA_OK, or FA_ERR_INVALID_ARG for a NULL
+ * pointer, B < 0, N < 0 or a violated condition. Nothing else is touched.
+ *
+ * Builds with FA_DEBUG defined (build.py --debug: libfa_debug.so) run this
+ * check on a copy of every cu_seqlens argument (cu_seqlens_q against Nq and
+ * cu_seqlens_k against Nk for the kvlen entry points) before launching, and
+ * synchronise the stream after every launch, reporting a failed copy, launch
+ * or kernel as FA_ERR_HIP. Those synchronisations make a debug build unfit
+ * for graph capture. Release builds never read cu_seqlens on the host.
+ */
+int fa_check_cu_seqlens(const int32_t* cu_seqlens_host, int B, int N);
 
 #ifdef __cplusplus
 }

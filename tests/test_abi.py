@@ -26,7 +26,8 @@ def test_header_declares_the_boundary():
                                     "fa_bwd_softcap_stage", "fa_bwd_stage",
                                     "fa_bwd_window", "fa_bwd_window_softcap",
                                     "fa_bwd_window_softcap_stage", "fa_bwd_window_stage",
-                                    "fa_bwd_workspace_size", "fa_fwd", "fa_fwd_dropout",
+                                    "fa_bwd_workspace_size", "fa_check_cu_seqlens", "fa_fwd",
+                                    "fa_fwd_dropout",
                                     "fa_fwd_fp8",
                                     "fa_fwd_kvcache", "fa_fwd_kvcache_fp8",
                                     "fa_fwd_kvcache_fp8_stage", "fa_fwd_kvcache_local",
@@ -802,3 +803,44 @@ def test_bwd_kvlen_stage_index_checked():
     assert bkv(stage=3) == fa.FA_ERR_INVALID_ARG
     assert bkv(stage=-1) == fa.FA_ERR_INVALID_ARG
     assert bkv(stage=1) == fa.FA_ERR_HIP
+
+
+def _cu_check(values, B, N):
+    import numpy as np
+    a = np.ascontiguousarray(np.asarray(values, dtype=np.int32))
+    return fa.fa_check_cu_seqlens(a.ctypes.data if a.size else None, B, N)
+
+
+@pytest.mark.parametrize("values,B,N,ok", [
+    ([0], 0, 0, True),
+    ([0, 5], 1, 5, True),
+    ([0, 5], 1, 4, False),            # a sequence longer than N
+    ([1, 5], 1, 8, False),            # first entry not 0
+    ([0, 5, 3], 2, 8, False),         # decreasing
+    ([0, 0, 0, 7], 3, 7, True),       # empty sequences
+    ([0, 2**31 - 1], 1, 2**31 - 1, True),
+    ([0, 2**31 - 1, -2**31], 2, 2**31 - 1, False),   # no wrap-around
+])
+def test_check_cu_seqlens_cases(values, B, N, ok):
+    assert _cu_check(values, B, N) == (fa.FA_OK if ok else fa.FA_ERR_INVALID_ARG)
+
+
+def test_check_cu_seqlens_bad_arguments():
+    assert fa.fa_check_cu_seqlens(None, 1, 4) == fa.FA_ERR_INVALID_ARG
+    assert _cu_check([0, 1], -1, 4) == fa.FA_ERR_INVALID_ARG
+    assert _cu_check([0, 1], 1, -1) == fa.FA_ERR_INVALID_ARG
+
+
+def test_check_cu_seqlens_random_against_brute_force():
+    """Random arrays, half with one entry nudged: the library agrees with the
+    packing convention checked length by length in Python."""
+    import numpy as np
+    rng = np.random.default_rng(7)
+    for _ in range(500):
+        B, N = int(rng.integers(0, 30)), int(rng.integers(0, 200))
+        v = np.zeros(B + 1, dtype=np.int64)
+        v[1:] = np.cumsum(rng.integers(0, N + 1, size=B))
+        if B and rng.random() < 0.5:
+            v[rng.integers(0, B + 1)] += int(rng.integers(-3, 4))
+        ok = v[0] == 0 and all(0 <= v[s + 1] - v[s] <= N for s in range(B))
+        assert _cu_check(v, B, N) == (fa.FA_OK if ok else fa.FA_ERR_INVALID_ARG), (v, N)
