@@ -727,8 +727,9 @@ def run_sweep(args):
 
 def run_fp8_sweep(args):
     """fa_fwd (bf16) and fa_fwd_fp8 (e4m3 in, bf16 out) on the d = 128 forward
-    workloads, one line each: TFLOP/s by the forward convention, against the
-    dense peak of each instruction's input type."""
+    workloads (--names picks others, d = 64 and 256 included), one line each:
+    TFLOP/s by the forward convention, against the dense peak of each
+    instruction's input type."""
     import torch
     import workloads as W
     names = [f"sweep_N{N}_{c}" for N in (1024, 4096, 8192) for c in ("full", "causal")] + \

@@ -277,13 +277,12 @@ int fa_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse,
                float descale_q, float descale_k, float descale_v, fa_dtype out_dtype,
                hipStream_t stream) {
   bool noop;
-  int st = check_sizes(B, Hq, Hkv, N, d, scale, causal, out_dtype, &noop);
+  int st = check_sizes(B, Hq, Hkv, N, d, scale, causal, out_dtype, &noop, 256);
   if (st != FA_OK) return st;
   for (float x : {descale_q, descale_k, descale_v})
     if (!std::isfinite(x) || !(x > 0.f)) return FA_ERR_INVALID_ARG;
   const float c = scale * descale_q * descale_k * kLog2e;
   if (!std::isfinite(c) || !(c > 0.f)) return FA_ERR_INVALID_ARG;
-  if (d != 128) return FA_ERR_UNSUPPORTED;
   if (noop) return FA_OK;
   if (!q || !k || !v || !o || !lse) return FA_ERR_INVALID_ARG;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse))

@@ -17,9 +17,11 @@
 //                  tile's keys chosen so that lane half g's accumulators
 //                  hold keys 32g .. 32g+31 in order (element r of block jb
 //                  is key 32g + 16·jb + r).
-//   softmax        as in the 16-bit kernel: base-2, scale folded into c,
-//                  reference max raised lazily (P ≤ 2^8 < 448, the largest
-//                  e4m3 value).
+//   softmax        as in the 16-bit kernel: base-2, scale folded into c;
+//                  the reference sits 8 (log2 units) below the running max,
+//                  so P ≤ 2^8 < 448 (the largest e4m3 value), the row's
+//                  largest weight is exactly 2^8 and few weights are small
+//                  enough for e4m3's subnormal range.
 //   Oᵀ += Vᵀ·Pᵀ    P rounded to e4m3 (nearest even) packs straight into the
 //                  B operand (slot e of half g = key 32g + e); the Vᵀ operand
 //                  comes from 8-bit transposing LDS reads, 8 keys per read.
@@ -54,13 +56,21 @@ __device__ __forceinline__ f32x16 mfma_fp8(i32x8 a, i32x8 b, f32x16 c) {
                                                           kScaleOne);
 }
 
-// LDS tile: D-byte rows, 16-byte chunks stored in the order chunk ^ swz8(row).
-// With 128-byte rows a bank depends on the row's parity and the chunk; the
-// permutation spreads (a) the 16 rows {16jb + 0..7, 32 + 16jb + 0..7} that
-// 16 lanes read one chunk of for Sᵀ, and (b) the 8 consecutive rows x 2
-// chunks that 32 lanes read with the transposing read for Vᵀ, over all banks.
+// LDS tile: D-byte rows, 16-byte chunks stored in the order chunk ^ swz8<D>(row).
+// The permutation spreads over all banks (a) the 16 rows {16jb + 0..7,
+// 32 + 16jb + 0..7} that 16 lanes read one chunk of for Sᵀ, and (b) the 8
+// consecutive rows x 2 chunks that 32 lanes read with the transposing read
+// for Vᵀ. Where a row lands in the 256 bytes of one pass over the banks
+// depends on the row's low bits when rows are shorter than 256 bytes, so
+// the chunk permutation needs only the row bits that do not already do so:
+//   d = 64  (four rows per pass):  bits 2 and 5 of the row;
+//   d = 128 (two rows per pass):   bits 1, 2 and 5;
+//   d = 256 (one row per pass):    bits 0, 1, 2 and 5.
+template <int D>
 __device__ __forceinline__ constexpr int swz8(int r) {
-  return (((r >> 1) & 3) << 1) | ((r >> 5) & 1);
+  if constexpr (D == 64) return (((r >> 2) & 1) << 1) | ((r >> 5) & 1);
+  else if constexpr (D == 128) return (((r >> 1) & 3) << 1) | ((r >> 5) & 1);
+  else return ((r & 7) << 1) | ((r >> 5) & 1);
 }
 
 // The tile row (key) that MFMA row i of key block jb reads for Sᵀ: rows with
@@ -82,7 +92,7 @@ __device__ __forceinline__ void tile_dma8(u8* lds, const u8* src, int64_t rstrid
   for (int u = 0; u < PER; ++u) {
     const int inst = wave * PER + u;
     const int row = inst * RPI + lane / CPR;
-    const int c = (lane % CPR) ^ swz8(row);
+    const int c = (lane % CPR) ^ swz8<D>(row);
     const u8* g = src + (int64_t)min(r0 + row, L - 1) * rstride + c * 16;
 #if defined(__HIP_DEVICE_COMPILE__)
     __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)(lds + inst * 1024),
@@ -106,7 +116,7 @@ struct DmaPlan8 {
 #pragma unroll
     for (int u = 0; u < PER; ++u) {
       const int row = (wave * PER + u) * RPI + lane / CPR;
-      off[u] = (uint32_t)(row * rstride + ((lane % CPR) ^ swz8(row)) * 16);
+      off[u] = (uint32_t)(row * rstride + ((lane % CPR) ^ swz8<D>(row)) * 16);
     }
   }
 };
@@ -139,8 +149,8 @@ template <int D>
 __device__ __forceinline__ i32x8 k_operand(const u8* kt, int jb, int ks, int lane) {
   const int row = s_key(jb, lane & 31);
   const int c0 = 4 * ks + 2 * (lane >> 5);
-  const u32x4 a = lds16_at(kt, row * D + 16 * (c0 ^ swz8(row)));
-  const u32x4 b = lds16_at(kt, row * D + 16 * ((c0 + 1) ^ swz8(row)));
+  const u32x4 a = lds16_at(kt, row * D + 16 * (c0 ^ swz8<D>(row)));
+  const u32x4 b = lds16_at(kt, row * D + 16 * ((c0 + 1) ^ swz8<D>(row)));
   return i32x8{(int)a[0], (int)a[1], (int)a[2], (int)a[3], (int)b[0], (int)b[1], (int)b[2],
                (int)b[3]};
 }
@@ -159,7 +169,7 @@ __device__ __forceinline__ i32x8 v_operand(const u8* vt, int cb, int lane) {
   for (int q = 0; q < 4; ++q) {
     const int row = 32 * g + 8 * q + (j >> 1);
     const i32x2 t = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
-        (lds_i32x2*)(vt + row * D + 16 * (c ^ swz8(row)) + 8 * (j & 1)));
+        (lds_i32x2*)(vt + row * D + 16 * (c ^ swz8<D>(row)) + 8 * (j & 1)));
     r[2 * q] = t[0];
     r[2 * q + 1] = t[1];
   }
@@ -233,8 +243,14 @@ __device__ __forceinline__ void fwd8_tile(const u8* __restrict__ kt, const u8* _
 #pragma unroll
   for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[1][i]);
   const float mxc = wave_max_halves(mx) * c;
+  // The reference is kept exactly kRescaleHeadroom below the row's running max
+  // (raised when a tile's max passes the running max, decided per wave): every
+  // weight is at most 2^8 = 256 < 448, the row's largest weight is exactly 256,
+  // an e4m3 value, and small weights sit 2^8 further above e4m3's coarse
+  // subnormal range than with weights ≤ 1.
   if (__builtin_amdgcn_ballot_w64(mxc > mc + kRescaleHeadroom) != 0) {   // wave-uniform
-    const float mc_new = fmaxf(mc, mxc);   // finite: key 0 is visible to every row
+    // finite: key 0 is visible to every row
+    const float mc_new = fmaxf(mc, mxc - kRescaleHeadroom);
     const float alpha = fast_exp2(mc - mc_new);
     l *= alpha;
     lsum[0] *= alpha;
@@ -260,8 +276,10 @@ __device__ __forceinline__ void fwd8_tile(const u8* __restrict__ kt, const u8* _
   for (int cb = 0; cb < NCB; ++cb) o[cb] = mfma_fp8(v_operand<D>(vt, cb, lane), pf, o[cb]);
 }
 
+// two workgroups per CU up to d = 128; at d = 256 the O accumulators alone take
+// 128 registers and the kernel runs one per CU
 template <typename TO, int D, bool CAUSAL, bool VARLEN>
-__global__ __launch_bounds__(kThreads, 2) void fwd8_kernel(Fp8FwdArgs a) {
+__global__ __launch_bounds__(kThreads, D <= 128 ? 2 : 1) void fwd8_kernel(Fp8FwdArgs a) {
   constexpr int NKS = D / 64;
   constexpr int NCB = D / 32;
   constexpr int TILE = kBC * D;   // bytes per K or V tile
@@ -404,7 +422,13 @@ int fwd_fp8_query_tile() { return kBR; }
 
 hipError_t launch_fwd_fp8(const Fp8FwdArgs& a, bool bf16_out, int d, bool causal, bool varlen,
                           hipStream_t s) {
-  (void)d;   // d = 128 (checked by the caller)
+  // d is 64, 128 or 256 (checked by the caller)
+  if (d == 64)
+    return bf16_out ? dispatch8<bf16, 64>(a, causal, varlen, s)
+                    : dispatch8<f16, 64>(a, causal, varlen, s);
+  if (d == 256)
+    return bf16_out ? dispatch8<bf16, 256>(a, causal, varlen, s)
+                    : dispatch8<f16, 256>(a, causal, varlen, s);
   return bf16_out ? dispatch8<bf16, 128>(a, causal, varlen, s)
                   : dispatch8<f16, 128>(a, causal, varlen, s);
 }

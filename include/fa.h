@@ -345,9 +345,9 @@ int fa_bwd_kvlen_stage(int stage, const void* q, const void* k, const void* v, c
  *   lse : [Hq, T]    float32, natural log, of scale·(real Q)·(real K)ᵀ
  * The kernel rounds the softmax weights to e4m3 for the P·V product (the
  * matrix instruction takes 8-bit operands) and normalises O by the sum of
- * those rounded weights; LSE uses the unrounded weights. d = 128 only
- * (other d: FA_ERR_UNSUPPORTED). Layout, varlen, causal, alignment,
- * ownership, errors and determinism as for fa_fwd.
+ * those rounded weights; LSE uses the unrounded weights. d = 64, 128 or 256,
+ * as for fa_fwd (other d: FA_ERR_UNSUPPORTED). Layout, varlen, causal,
+ * alignment, ownership, errors and determinism as for fa_fwd.
  */
 int fa_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse,
                int B, int Hq, int Hkv, int N, int d, float scale, int causal,

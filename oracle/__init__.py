@@ -20,8 +20,9 @@ Modules:
   bruteforce  pure-Python loops (math.exp / math.fsum) for tiny shapes
   dropout     Philox4x32-10 keep decisions and attention with dropout on the
               softmax weights (forward and backward)
-  fp8         e4m3fn decoding, attention on decoded FP8 inputs, and the
-              element-wise error bound of a forward that rounds P to e4m3
+  fp8         e4m3fn decoding and rounding, attention on decoded FP8 inputs,
+              the element-wise error bound of a forward that rounds P to e4m3,
+              and plain FP8 attention (the accuracy baseline)
 
 Pins: every function here is checked in tests/test_oracle_*.py against hand-
 derived worked values (tests/golden/), closed forms, invariants, finite
@@ -33,11 +34,13 @@ from .decode import kvcache_fwd, kvcache_fwd_units, kvlen_bwd, kvlen_head_bwd
 from . import bruteforce
 from .dropout import (attention_bwd_dropout, attention_fwd_dropout, head_bwd_dropout,
                       head_fwd_dropout, keep_mask, keep_threshold, philox4x32_10)
-from .fp8 import attention_fwd_fp8, e4m3fn_decode, dequantize, head_o_bound, o_bound
+from .fp8 import (attention_fwd_fp8, attention_fwd_fp8_plain, e4m3fn_decode, e4m3fn_round,
+                  dequantize, head_o_bound, o_bound)
 
 __all__ = ["attention_fwd", "attention_bwd", "attention_probs", "attention_fwd_rows",
            "attention_bwd_sampled", "attention_bwd_rows", "kvcache_fwd", "kvcache_fwd_units", "kvlen_bwd", "kvlen_head_bwd", "bruteforce",
-           "attention_fwd_fp8", "e4m3fn_decode", "dequantize", "head_o_bound", "o_bound",
+           "attention_fwd_fp8", "attention_fwd_fp8_plain", "e4m3fn_decode", "e4m3fn_round",
+           "dequantize", "head_o_bound", "o_bound",
            "attention_fwd_dropout", "attention_bwd_dropout", "head_fwd_dropout",
            "head_bwd_dropout", "keep_mask", "keep_threshold",
            "philox4x32_10"]

@@ -60,6 +60,55 @@ def attention_fwd_fp8(q8, k8, v8, scale: float, descale_q: float, descale_k: flo
                          dequantize(v8, descale_v), scale, causal, cu_seqlens)
 
 
+# values of the non-negative finite codes 0x00 .. 0x7E, increasing with the code
+_E4M3_POS = None
+
+
+def e4m3fn_round(x) -> np.ndarray:
+    """x rounded to the nearest e4m3fn value (float64 in, float64 out).
+
+    Ties go to the code with an even last mantissa bit; magnitudes above 448
+    saturate to ±448 (the reading taken for a value past the largest code);
+    the sign is kept, zero stays zero. Written from the format: the finite
+    non-negative values are the codes 0x00 .. 0x7E, increasing with the code,
+    so the nearest one is found between two neighbours of a sorted table.
+    """
+    global _E4M3_POS
+    if _E4M3_POS is None:
+        _E4M3_POS = e4m3fn_decode(np.arange(0x7F, dtype=np.uint8))
+    x = np.asarray(x, dtype=np.float64)
+    a = np.minimum(np.abs(x), E4M3_MAX)
+    i = np.clip(np.searchsorted(_E4M3_POS, a), 1, 0x7E)   # _E4M3_POS[i-1] < a <= _E4M3_POS[i]
+    lo, hi = _E4M3_POS[i - 1], _E4M3_POS[i]
+    up = (hi - a < a - lo) | ((hi - a == a - lo) & (i % 2 == 0))
+    return np.copysign(np.where(up, hi, lo), x)
+
+
+def attention_fwd_fp8_plain(q8, k8, v8, scale: float, descale_q: float, descale_k: float,
+                            descale_v: float, causal: bool = False, cu_seqlens=None):
+    """O [T, Hq, d] (float64) of plain FP8 attention: the baseline that the
+    pages compare FlashAttention-3's FP8 forward with (Flash Attention 是什麼,
+    adersaytech.com, the note after the FA-1 to FA-4 table), which they do not
+    define. The plainest reading: the same per-tensor e4m3 inputs; per row the
+    softmax weights P_j = exp(S_j − max S) in [0, 1], each rounded to e4m3 for
+    the FP8 product with V; O = Σ_j round(P_j)·V_j / Σ_j P_j, normalised by
+    the sum of the unrounded weights. Everything else is exact (float64), so
+    the only roundings are those of the inputs and of P.
+    """
+    q, k, v = dequantize(q8, descale_q), dequantize(k8, descale_k), dequantize(v8, descale_v)
+    T, Hq, d = q.shape
+    g = _group(Hq, k.shape[1])
+    o = np.zeros((T, Hq, d))
+    for a, b in _segments(T, cu_seqlens):
+        if b <= a:
+            continue
+        for h in range(Hq):
+            S = _scores(q[a:b, h], np.arange(b - a), k[a:b, h // g], scale, causal)
+            P = np.exp(S - S.max(axis=1, keepdims=True))
+            o[a:b, h] = (e4m3fn_round(P) @ v[a:b, h // g]) / P.sum(axis=1, keepdims=True)
+    return o
+
+
 def o_bound(q, k, v, o, scale: float, causal: bool = False, cu_seqlens=None,
             out_dtype: str = "bf16") -> np.ndarray:
     """Element-wise bound on |O_kernel − O| for a forward that rounds P to e4m3.
@@ -69,6 +118,10 @@ def o_bound(q, k, v, o, scale: float, causal: bool = False, cu_seqlens=None,
     p̃_j = 2^(S_j·log2 e − m̃) for some reference m̃ not above the row's true
     maximum, each rounded to e4m3 (p̃'_j = p̃_j + ε_j), and
     O' = Σ_j p̃'_j V_j / Σ_j p̃'_j, both sums over the same rounded weights.
+    (A kernel may round key j's weight at an earlier, lower reference m̃_j ≤ m̃
+    and carry it to m̃ exactly; in units of m̃ that rounding moves it by at
+    most U_E4M3 relative, or 2^-10·2^(m̃_j − m̃) ≤ 2^-10 absolute, so the
+    terms below hold for it too.)
     Writing P_j = p̃_j / Σ p̃ (the exact softmax) and e_j ≥ |ε_j| / Σ p̃,
 
         O' − O = Σ_j ε_j (V_j − O) / Σ_j p̃'_j

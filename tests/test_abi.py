@@ -475,8 +475,8 @@ def fwd8(**kw):
     (dict(Hq=3, Hkv=2), fa.FA_ERR_INVALID_ARG),
     (dict(q=None), fa.FA_ERR_INVALID_ARG),
     (dict(k=P + 8), fa.FA_ERR_INVALID_ARG),
-    (dict(d=64), fa.FA_ERR_UNSUPPORTED),
-    (dict(d=256), fa.FA_ERR_UNSUPPORTED),
+    (dict(d=96), fa.FA_ERR_UNSUPPORTED),
+    (dict(d=512), fa.FA_ERR_UNSUPPORTED),
     (dict(B=0), fa.FA_OK),
     (dict(N=0, q=None), fa.FA_OK),
 ])
@@ -490,6 +490,7 @@ def test_fwd_fp8_no_device_reports_hip_error():
         pytest.skip("a GPU is present")
     assert fwd8() == fa.FA_ERR_HIP
     assert fwd8(causal=1, dtype=fa.FA_FP16) == fa.FA_ERR_HIP
+    assert fwd8(d=64) == fa.FA_ERR_HIP and fwd8(d=256) == fa.FA_ERR_HIP
 
 
 def fwdc(**kw):

@@ -96,6 +96,22 @@ def test_fp8_forward(N, causal, out):
             out=out)
 
 
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("N", [1, 65, 700])
+@pytest.mark.parametrize("d", [64, 256])
+def test_fp8_forward_head_dims(d, N, causal):
+    """d = 64 and 256: rows of 64 and 256 bytes, each with its own LDS swizzle;
+    d = 256 runs one workgroup per CU."""
+    compare(W.custom(B=2, Hq=2, Hkv=1, N=N, d=d, causal=causal, seed=820 + N + d), v_shift=0.5)
+
+
+@pytest.mark.parametrize("d", [64, 256])
+def test_fp8_forward_head_dims_varlen_gqa_fp16(d):
+    w = W.custom(B=0, Hq=8, Hkv=2, N=0, d=d, causal=True, seed=821 + d,
+                 lens=[300, 0, 1, 129, 64, 513])
+    compare(w, v_shift=-0.3, out="fp16")
+
+
 @pytest.mark.parametrize("scale", [0.02, 0.5])
 def test_fp8_forward_sharp_and_flat(scale):
     """A large scale makes rows peaked (the rounded-sum normalisation matters);
@@ -157,3 +173,54 @@ def test_fp8_empty_and_zero_length():
     o, lse = fa.flash_attn_func_fp8(q, q[:, :2], q[:, :2], cu_seqlens=cu, max_seqlen=0)
     torch.cuda.synchronize()
     assert o.shape == (0, 4, 128) and lse.shape == (4, 0)
+
+
+@pytest.mark.parametrize("v_shift", [0.0, 2.0])
+@pytest.mark.parametrize("mix", ["normal", "outliers"])
+@pytest.mark.parametrize("d", [64, 128, 256])
+def test_fp8_accuracy_against_plain_baseline(d, mix, v_shift):
+    """Error of the FP8 forward next to plain FP8 attention (the baseline the
+    pages compare FlashAttention-3's FP8 forward with; oracle
+    attention_fwd_fp8_plain) and the bf16 forward, all against exact float64
+    attention on the unquantised inputs. Inputs (B1 H4 N1024, not causal):
+    standard normal Q, K, V, or the same with 0.1 % of the Q and K entries ten
+    times larger (outliers that set the per-tensor descale and sharpen some
+    rows); V as drawn or shifted by 2 (values with a common offset). Both
+    FP8 results are written as fp16 (the finer of the two output types; the
+    baseline's float64 O is rounded the same way), the bf16 forward as bf16.
+    The FP8 forward's weights are rounded 8 (log2 units) above the running
+    max's reference, so the largest is exactly 256 and few fall into e4m3's
+    coarse subnormal range, and O is normalised by the sum of the rounded
+    weights it was built from. It must be at least as accurate as the
+    baseline in every case (emulated on the CPU first: 0.99x the baseline's
+    rms error for zero-mean V, down to 0.36x with shifted V and outliers)."""
+    import torch
+    from oracle import attention_fwd_fp8_plain
+    w = W.custom(B=1, Hq=4, Hkv=4, N=1024, d=d, causal=False, seed=830 + d)
+    a = W.generate(w, with_grad=False)
+    if mix == "outliers":
+        rng = np.random.default_rng(831 + d)
+        for n in ("q", "k"):
+            m = rng.random(a[n].shape) < 1e-3
+            a[n] = np.where(m, a[n] * 10.0, a[n]).astype(np.float32)
+    a["v"] = (a["v"] + np.float32(v_shift)).astype(np.float32)
+    exact, _ = attention_fwd(a["q"], a["k"], a["v"], w.scale, False)
+    f8 = W.quantize_e4m3(a)
+    dev = {n: torch.from_numpy(f8[n]).cuda().view(torch.float8_e4m3fn) for n in ("q", "k", "v")}
+    o8, _ = run_fp8(w, f8, dev, out="fp16")
+    plain = attention_fwd_fp8_plain(f8["q"], f8["k"], f8["v"], w.scale, f8["descale_q"],
+                                    f8["descale_k"], f8["descale_v"])
+    # both written as fp16 (nearest even): the output's own rounding on both sides
+    plain = torch.from_numpy(plain).to(torch.float16).double().numpy()
+    fa = _fa()
+    t = {n: torch.from_numpy(a[n]).to(torch.bfloat16).cuda().view(1, w.N, w.Hq, d)
+         for n in ("q", "k", "v")}
+    o16, _ = fa.flash_attn_func(t["q"], t["k"], t["v"], causal=False)
+    torch.cuda.synchronize()
+    rms = lambda x: float(np.sqrt((x ** 2).mean()))
+    e8 = rms(o8.double().cpu().numpy() - exact)
+    ep = rms(plain - exact)
+    e16 = rms(o16.view(w.T, w.Hq, d).double().cpu().numpy() - exact)
+    say(f"[fp8 accuracy] d={d} {mix} v_shift={v_shift}: rms error bf16 {e16:.3e}  "
+        f"fa_fwd_fp8 {e8:.3e}  plain FP8 {ep:.3e}  (fa_fwd_fp8 / plain = {e8 / ep:.2f})")
+    assert e8 <= ep, (e8, ep)

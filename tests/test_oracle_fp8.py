@@ -6,8 +6,8 @@ finite 448, smallest subnormal 2^-9, smallest normal 2^-6, NaN codes). The
 forward on decoded inputs is checked against closed forms (one key; a
 descale only scales its own tensor) and torch's CPU float64 SDPA. The bound
 is checked against its own model: weights rounded to e4m3 by torch's cast,
-with a reference max up to 8 (log2 units) below the true one, never exceed
-it; an adversarial rounding direction reaches most of it; and a forward that
+each at a reference 8 (log2 units) below the running max of its tile's
+time, never exceed it; an adversarial rounding direction reaches most of it; and a forward that
 loses one key block falls outside it.
 """
 import math
@@ -99,16 +99,23 @@ def _round_e4m3(x):
     return torch.from_numpy(x).to(torch.float8_e4m3fn).to(torch.float64).numpy()
 
 
-def _model_forward(q, k, v, scale, causal, rng, stale=8.0):
-    """The bound's model, one head: reference max up to `stale` log2 units low,
-    weights rounded to e4m3 by torch's cast, O normalised by the rounded sum."""
-    S = scale * (q @ k.T)
+def _model_forward(q, k, v, scale, causal, rng, lift=8.0):
+    """The bound's model, one head, in log2 units: key j's weight is rounded to
+    e4m3 (torch's cast) at the reference its tile had, r_j = M_j − lift with
+    M_j anywhere between its own score s_j and the row's max M (the running
+    max when the tile was processed), so 2^(s_j − r_j) ≤ 2^lift; it is then
+    carried to the final reference M − lift exactly, and O is normalised by
+    the sum of the rounded weights."""
+    S = scale * (q @ k.T) * math.log2(math.e)
     L = S.shape[0]
     if causal:
         S = np.where(np.arange(L)[None, :] <= np.arange(L)[:, None], S, -np.inf)
-    m = S.max(axis=1) * math.log2(math.e) - rng.uniform(0, stale, size=L)
-    p = np.exp2(S * math.log2(math.e) - m[:, None])
-    pr = _round_e4m3(p)
+    M = S.max(axis=1, keepdims=True)
+    Sf = np.where(np.isfinite(S), S, M)
+    Mj = Sf + rng.uniform(0, 1, size=S.shape) * (M - Sf)
+    Mj = np.where(rng.random(S.shape) < 0.5, M, Mj)   # half the keys: the final reference
+    r = Mj - lift
+    pr = _round_e4m3(np.exp2(S - r)) * np.exp2(r - (M - lift))
     return (pr @ v) / pr.sum(axis=1, keepdims=True)
 
 
@@ -204,3 +211,96 @@ def test_bound_covers_the_output_rounding(out):
     td = {"bf16": torch.bfloat16, "fp16": torch.float16}[out]
     rounded = torch.from_numpy(o).to(td).double().numpy()
     assert np.all(np.abs(rounded - o) <= o_bound(q, k, v, o, 0.1, False, out_dtype=out))
+
+
+# ---- e4m3fn rounding and the plain FP8 baseline --------------------------------
+
+def test_e4m3_round_keeps_every_code():
+    from oracle import e4m3fn_round
+    codes = np.array([c for c in range(256) if (c & 0x7F) != 0x7F], dtype=np.uint8)
+    vals = e4m3fn_decode(codes)
+    assert np.array_equal(e4m3fn_round(vals), vals)
+
+
+def test_e4m3_round_ties_to_even_and_nearest():
+    """Midpoints between neighbouring codes go to the code whose last mantissa
+    bit is 0; a hair either side goes to the nearer code."""
+    from oracle import e4m3fn_round
+    pos = e4m3fn_decode(np.arange(0x7F, dtype=np.uint8))
+    for c in range(0x7E):
+        lo, hi = pos[c], pos[c + 1]
+        mid = 0.5 * (lo + hi)
+        even = lo if c % 2 == 0 else hi
+        assert e4m3fn_round(mid) == even, (c, mid)
+        assert e4m3fn_round(-mid) == -even
+        eps = (hi - lo) * 1e-6
+        assert e4m3fn_round(mid - eps) == lo and e4m3fn_round(mid + eps) == hi
+    assert e4m3fn_round(1e6) == 448.0 and e4m3fn_round(-449.0) == -448.0
+
+
+def test_e4m3_round_matches_torch_cast():
+    """Against torch's float8_e4m3fn conversion (round to nearest even) on
+    magnitudes from below the subnormals to the largest code."""
+    import torch
+    rng = np.random.default_rng(3)
+    x = np.exp2(rng.uniform(-12, np.log2(448.0), 200_000)) * rng.choice([-1.0, 1.0], 200_000)
+    x = x.astype(np.float32).astype(np.float64)        # torch converts from float32
+    from oracle import e4m3fn_round
+    ref = torch.from_numpy(x.astype(np.float32)).to(torch.float8_e4m3fn).to(torch.float64).numpy()
+    assert np.array_equal(e4m3fn_round(x), ref)
+
+
+def test_plain_fp8_baseline_exact_cases():
+    """Where every weight is an e4m3 value the baseline is exact attention on
+    the decoded inputs: equal scores (all weights 1) and the first causal row
+    (a single key). Elsewhere it differs from the exact result by no more than
+    the weights' rounding allows."""
+    from oracle import attention_fwd_fp8_plain
+    rng = np.random.default_rng(9)
+    T, H, d = 40, 2, 16
+    f8 = {"q": np.zeros((T, H, d), np.float32), "k": rng.standard_normal((T, H, d)).astype(np.float32),
+          "v": rng.standard_normal((T, H, d)).astype(np.float32)}
+    import workloads as W
+    c = W.quantize_e4m3(f8)
+    ds = (1.0, c["descale_k"], c["descale_v"])
+    exact, _ = attention_fwd_fp8(c["q"], c["k"], c["v"], 0.3, *ds)
+    plain = attention_fwd_fp8_plain(c["q"], c["k"], c["v"], 0.3, *ds)
+    assert np.allclose(plain, exact, rtol=0, atol=1e-13)          # Q = 0: every P_j = 1
+    f8["q"] = rng.standard_normal((T, H, d)).astype(np.float32)
+    c = W.quantize_e4m3(f8)
+    ds = (c["descale_q"], c["descale_k"], c["descale_v"])
+    exact, _ = attention_fwd_fp8(c["q"], c["k"], c["v"], 0.3, *ds, causal=True)
+    plain = attention_fwd_fp8_plain(c["q"], c["k"], c["v"], 0.3, *ds, causal=True)
+    assert np.allclose(plain[0], exact[0], rtol=0, atol=1e-13)    # one visible key
+    q, k, v = (dequantize(c[n], ds[i]) for i, n in enumerate("qkv"))
+    err = np.abs(plain - exact)
+    assert err.max() > 1e-6                                       # the rounding shows
+    # each weight moves by at most max(2^-4·P, min(P, 2^-10)) (half an ulp of a
+    # normal code, or of the 2^-9 subnormal spacing, never past zero), so
+    # |O_plain − O| ≤ Σ_j max(2^-4·P_j, min(P_j, 2^-10))·|V_j| / Σ_j P_j
+    for h in range(H):
+        S = 0.3 * q[:, h] @ k[:, h].T
+        S = np.where(np.tril(np.ones((T, T), bool)), S, -np.inf)
+        P = np.exp(S - S.max(axis=1, keepdims=True))
+        e = np.maximum(2.0 ** -4 * P, np.minimum(P, 2.0 ** -10))
+        bound = (e @ np.abs(v[:, h])) / P.sum(axis=1, keepdims=True)
+        assert np.all(err[:, h] <= bound * (1 + 1e-9) + 1e-15), h
+
+
+def test_plain_fp8_baseline_worked_two_keys():
+    """One query, two keys, worked by hand: q = 1, k0 = 0, k1 = ln 0.53 (code
+    −1.0 with descale −ln 0.53), v0 = 0, v1 = 1, scale 1. Then S = (0, ln 0.53),
+    P = (1, 0.53); 0.53 lies between the codes 0.5 and 0.5625 and rounds to
+    0.5. Plain FP8 attention gives 0.5 / (1 + 0.53) (rounded weight over the
+    unrounded sum), exact attention 0.53 / 1.53; normalising by the rounded
+    sum instead would give 0.5 / 1.5."""
+    from oracle import attention_fwd_fp8_plain
+    q8 = np.full((1, 1, 1), 0x38, np.uint8)                 # 1.0
+    k8 = np.array([0x00, 0xB8], np.uint8).reshape(2, 1, 1)  # 0, −1.0
+    v8 = np.array([0x00, 0x38], np.uint8).reshape(2, 1, 1)  # 0, 1.0
+    q8 = np.concatenate([q8, q8])                           # two queries, same row
+    ds = (1.0, -np.log(0.53), 1.0)
+    plain = attention_fwd_fp8_plain(q8, k8, v8, 1.0, *ds)
+    exact, _ = attention_fwd_fp8(q8, k8, v8, 1.0, *ds)
+    assert abs(plain[0, 0, 0] - 0.5 / 1.53) < 1e-12
+    assert abs(exact[0, 0, 0] - 0.53 / 1.53) < 1e-12
