@@ -229,11 +229,19 @@ class Fp8Bound:
             raise self.fa.FaError(st, "fa_fwd_fp8")
 
 
-def time_calls(torch, fn, iters, warmup):
-    """Average ms per call with HIP events on the current stream."""
+def time_calls(torch, fn, iters, warmup, min_warm_s=0.0):
+    """Average ms per call with HIP events on the current stream, after `warmup`
+    calls and then more until at least `min_warm_s` seconds of back-to-back
+    calls have run (a short kernel's first milliseconds run below the clock the
+    part settles at under load)."""
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < min_warm_s:
+        for _ in range(20):
+            fn()
+        torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
     for _ in range(iters):
@@ -688,7 +696,7 @@ def run_sweep(args):
         if n in W.KVLEN_WORKLOADS:   # queries and keys of different lengths
             w = W.KVLEN_WORKLOADS[n]
             b = KvlenBound(w)
-            ms = time_calls(torch, b.fwd, 100, 10)
+            ms = time_calls(torch, b.fwd, 100, 10, min_warm_s=0.2)
             med, mn = time_calls_dist(torch, b.fwd, 100, 0)
             tf = w.fwd_flop() / (ms * 1e-3) / 1e12
             print(json.dumps({"workload": n, "Nq": w.Nq, "Nk": w.Nk, "d": w.d, "dtype": w.dtype,
@@ -702,7 +710,7 @@ def run_sweep(args):
             continue
         w = W.WORKLOADS[n]
         b = Bound(w, with_bwd=False)
-        ms = time_calls(torch, b.fwd, 100, 10)
+        ms = time_calls(torch, b.fwd, 100, 10, min_warm_s=0.2)
         med, mn = time_calls_dist(torch, b.fwd, 100, 0)
         tf = w.fwd_flop() / (ms * 1e-3) / 1e12
         io = sum(x.numel() * x.element_size() for x in (b.t["q"], b.t["k"], b.t["v"], b.o, b.lse))
@@ -739,11 +747,11 @@ def run_fp8_sweep(args):
     for n in names:
         w = W.WORKLOADS[n]
         b16 = Bound(w, with_bwd=False)
-        ms16 = time_calls(torch, b16.fwd, 100, 10)
+        ms16 = time_calls(torch, b16.fwd, 100, 10, min_warm_s=0.2)
         del b16
         torch.cuda.empty_cache()
         b8 = Fp8Bound(w)
-        ms8 = time_calls(torch, b8.fwd, 100, 10)
+        ms8 = time_calls(torch, b8.fwd, 100, 10, min_warm_s=0.2)
         del b8
         torch.cuda.empty_cache()
         tf16 = w.fwd_flop() / (ms16 * 1e-3) / 1e12
