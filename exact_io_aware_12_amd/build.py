@@ -52,8 +52,11 @@ def _jobs(debug: bool, resource_usage: bool):
     """(object, command) per source for one variant, the largest source first."""
     tmpdir = os.path.join(HERE, "_build", "debug" if debug else "")
     os.makedirs(tmpdir, exist_ok=True)
+    # host symbols hidden except the C ABI that include/fa.h declares (device
+    # code keeps its default visibility: the runtime finds kernels by name)
     flags = [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
              "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+             "-Xarch_host", "-fvisibility=hidden",
              "-I", os.path.join(ROOT, "include"), "-I", CSRC]
     if debug:
         flags.append("-DFA_DEBUG")

@@ -66,6 +66,9 @@
 #include <stdint.h>
 #include <hip/hip_runtime_api.h>
 
+/* The library is built with hidden symbols; what this header declares is its
+ * whole exported interface. */
+#pragma GCC visibility push(default)
 #ifdef __cplusplus
 extern "C" {
 #endif
@@ -489,5 +492,6 @@ int fa_check_cu_seqlens(const int32_t* cu_seqlens_host, int B, int N);
 #ifdef __cplusplus
 }
 #endif
+#pragma GCC visibility pop
 
 #endif /* FA_H_ */

@@ -845,3 +845,18 @@ def test_check_cu_seqlens_random_against_brute_force():
             v[rng.integers(0, B + 1)] += int(rng.integers(-3, 4))
         ok = v[0] == 0 and all(0 <= v[s + 1] - v[s] <= N for s in range(B))
         assert _cu_check(v, B, N) == (fa.FA_OK if ok else fa.FA_ERR_INVALID_ARG), (v, N)
+
+
+def test_library_exports_exactly_the_header():
+    """The library's exported functions are the header's declarations and
+    nothing else (host symbols are hidden; the C ABI is the whole interface)."""
+    import shutil
+    import subprocess
+    nm = shutil.which("nm")
+    if nm is None:
+        pytest.skip("nm (binutils) is not installed")
+    out = subprocess.run([nm, "-D", "--defined-only", fa.lib_path()], capture_output=True,
+                         text=True, check=True).stdout
+    funcs = sorted(line.split()[-1] for line in out.splitlines()
+                   if len(line.split()) == 3 and line.split()[1] == "T")
+    assert funcs == declared_functions()
