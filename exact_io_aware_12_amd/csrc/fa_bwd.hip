@@ -153,13 +153,13 @@ __device__ __forceinline__ void rows_dma(float* lds, const float* lse2, const fl
 // consumer works one tile behind the producer, so one wave's VALU work
 // overlaps the other's MFMAs on the same SIMD.
 //
-// Per iteration j (j = -1 .. ntile-1), between two workgroup barriers:
-//   A: tile j+1 (Q, dO, LSE, D) has landed; the copy of tile j+2 starts
-//      into the stage that tile j-1 used (and has until the next A to land);
-//      consumer: P, dS of tile j from LDS into registers;
-//      producer: S, dP of tile j+1;
-//   B (orders LDS accesses only): consumer: dK/dV products of tile j;
-//      producer: P, dS of tile j+1 into LDS.
+// Per iteration j (j = -1 .. ntile-1), after one workgroup barrier A (tile
+// j+1's Q, dO, LSE and D have landed; the copy of tile j+2 starts into the
+// stage that tile j-1 used and has until the next A to land):
+//   consumer: P, dS of tile j from LDS into registers, then releases its
+//      pair's exchange buffer (an LDS flag) and runs the dK/dV products;
+//   producer: waits for its own consumer's release only (not for the whole
+//      workgroup), then S, dP, P and dS of tile j+1 into the buffer.
 // Q/dO tiles take 3 stages: j (consumer), j+1 (producer), j+2 (in flight).
 constexpr int kDkvKeys = 128;     // keys per workgroup (32 per wave pair)
 constexpr int kDkvQ = 64;         // queries per tile
@@ -167,6 +167,29 @@ constexpr int kDkvWaves = 8;      // 4 producers, 4 consumers
 constexpr int kDkvThreads = 64 * kDkvWaves;
 constexpr int kDkvStages = 3;
 constexpr int kDkvKK = kDkvQ / 16;   // 16-query MFMA k-steps per tile
+
+// Hand-over of a pair's P/dS buffer. The consumer of a pair releases
+// iteration j once its reads of the buffer (tile j's P and dS) have returned;
+// the producer acquires iteration j just before it overwrites the buffer with
+// tile j+1. The consumer never waits for the producer inside an iteration, so
+// every release happens; the spin is bounded all the same.
+constexpr int kHandSpinLimit = 1 << 20;
+
+typedef volatile __attribute__((address_space(3))) int lds_flag_t;
+
+__device__ __forceinline__ void pair_release(const int* flag, int j) {
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // the buffer reads have returned
+  *(lds_flag_t*)(uintptr_t)lds_addr(flag) = j;
+}
+
+__device__ __forceinline__ void pair_acquire(const int* flag, int j) {
+  lds_flag_t* f = (lds_flag_t*)(uintptr_t)lds_addr(flag);
+  for (int spin = 0; spin < kHandSpinLimit; ++spin) {
+    if (__builtin_amdgcn_readfirstlane(*f) >= j) break;
+    __builtin_amdgcn_s_sleep(1);
+  }
+  asm volatile("" ::: "memory");   // the buffer writes stay after the wait
+}
 
 // Producer: P and dS of one 64-query tile for 32 keys, written to `xp`
 // (P) and `xs` (dS) as MFMA B operands, [k-step][lane]. EDGE tiles zero P
@@ -182,7 +205,8 @@ __device__ __forceinline__ void dkdv_produce(const T* qt_, const T* dot_, const 
                                              float c, int q0, int L, int key, int wl, int wr,
                                              int lane, float cap_in = 0.f, float cap_out = 0.f,
                                              const DropKey* dk = nullptr, int seq = 0,
-                                             int head = 0, float zs = 0.f, int off = 0) {
+                                             int head = 0, float zs = 0.f, int off = 0,
+                                             const int* hand = nullptr, int hand_j = 0) {
   constexpr int NKB = D / 16;
   constexpr int NQB = kDkvQ / 32;
   const int col = lane & 31, half = lane >> 5;
@@ -191,6 +215,14 @@ __device__ __forceinline__ void dkdv_produce(const T* qt_, const T* dot_, const 
   // two k-steps ahead of their MFMAs across the whole tile (so the next
   // block's first operands are in flight during this block's arithmetic).
   constexpr int AHEAD = 2, NSTEP = NQB * NKB;
+  // The buffer is written below, so the consumer must have read it first.
+  // The wait sits right before the first write, where the consumer has
+  // finished long since; with a soft cap or dropout, whose tiles need more
+  // registers, it sits before the tile instead, since a wait inside the tile
+  // splits its code and makes the compiler spill (measured on train_16k: the
+  // late wait made dK/dV 3.7 % faster than the early one).
+  constexpr bool kLateWait = !CAP && !DROP;
+  if constexpr (!kLateWait) pair_acquire(hand, hand_j);
   u32x4 qa[AHEAD + 1], da[AHEAD + 1];
   auto fetch = [&](int step) __attribute__((always_inline)) {
     const int qb = step / NKB, kb = step % NKB;
@@ -249,6 +281,7 @@ __device__ __forceinline__ void dkdv_produce(const T* qt_, const T* dot_, const 
         dp[i4] = ds;
       }
     }
+    if (kLateWait && qb == 0) pair_acquire(hand, hand_j);
 #pragma unroll
     for (int h2 = 0; h2 < 2; ++h2) {
       xp[(2 * qb + h2) * 64 + lane] = acc_operand<T>(s, h2 * 2);
@@ -268,6 +301,7 @@ __global__ __launch_bounds__(kDkvThreads, 1) void dkdv_kernel(BwdArgs a, int n_k
   __shared__ __attribute__((aligned(1024))) T qd_lds[kDkvStages][2][TILE];   // [stage][Q, dO]
   __shared__ __attribute__((aligned(16))) float ld_lds[kDkvStages][2 * kDkvQ];  // LSE·log2 e, D
   __shared__ __attribute__((aligned(16))) u32x4 xch[4][2][kDkvKK * 64];   // [pair][P, dS]
+  __shared__ int hand[4];   // per pair: the last iteration whose P/dS the consumer has read
 
   // the wave index is the same on every lane: readfirstlane lets the compiler
   // see that, so branches on it are scalar rather than divergent
@@ -276,6 +310,7 @@ __global__ __launch_bounds__(kDkvThreads, 1) void dkdv_kernel(BwdArgs a, int n_k
   const int pair = wave & 3;
   const bool producer = wave < 4;
   const int col = lane & 31, half = lane >> 5;
+  if (tid < 4) hand[tid] = -2;   // ordered before any use by the first barrier A
 
   const int G = gridDim.x;
   const int logical = xcd_remap(blockIdx.x, G);
@@ -380,9 +415,9 @@ __global__ __launch_bounds__(kDkvThreads, 1) void dkdv_kernel(BwdArgs a, int n_k
   // tile j+2 and leave them nothing to overlap. The copies' global sources
   // come in restrict-qualified too: with every pointer a copy uses being a
   // restrict parameter, the compiler can tell the copies apart from the reads
-  // without proving that no pointer escaped. Barrier B is an LDS-only barrier
-  // for the same reason: the copies of tile j+2 need to have landed only at
-  // the next iteration's barrier A.
+  // without proving that no pointer escaped. The pair hand-over waits only
+  // for LDS operations for the same reason: the copies of tile j+2 need to
+  // have landed only at the next iteration's barrier A.
   if (producer) {
     // K and V fragments of this pair's 32 keys (B operands), kept in registers
     u32x4 kf[NKB], vf[NKB];
@@ -400,7 +435,6 @@ __global__ __launch_bounds__(kDkvThreads, 1) void dkdv_kernel(BwdArgs a, int n_k
                     const T* __restrict__ dog, const float* __restrict__ l2g,
                     const float* __restrict__ dg) __attribute__((always_inline)) {
       if (j + 2 < ntile) issue(j + 2, qdn, ldn, qg, dog, l2g, dg);
-      lds_barrier();     // B: the consumers hold tile j's P and dS in registers
       const int t = j + 1;
       if (t < ntile) {
         int r;
@@ -411,11 +445,11 @@ __global__ __launch_bounds__(kDkvThreads, 1) void dkdv_kernel(BwdArgs a, int n_k
           if (t < n_edge)
             dkdv_produce<T, D, CAUSAL, true, WIN, CAP, DROP>(
                 qdt, qdt + TILE, ldt, kf, vf, xp, xs, c, q0, L, key, wl, wr, lane, a.cap_in,
-                a.cap_out, &dk, b, h, a.drop_scale, off);
+                a.cap_out, &dk, b, h, a.drop_scale, off, &hand[pair], j);
           else
             dkdv_produce<T, D, CAUSAL, false, WIN, CAP, DROP>(
                 qdt, qdt + TILE, ldt, kf, vf, xp, xs, c, q0, L, key, wl, wr, lane, a.cap_in,
-                a.cap_out, &dk, b, h, a.drop_scale, off);
+                a.cap_out, &dk, b, h, a.drop_scale, off, &hand[pair], j);
         }
       }
     };
@@ -458,7 +492,7 @@ __global__ __launch_bounds__(kDkvThreads, 1) void dkdv_kernel(BwdArgs a, int n_k
           }
         }
       }
-      lds_barrier();     // B (waits for the P, dS reads above; not for the copies of tile j+2)
+      pair_release(&hand[pair], j);   // tile j's P and dS are in registers
       if (active) {
         constexpr uint32_t KSTEP = 16 * D * sizeof(T);   // 16 rows
         constexpr uint32_t DO = TILE * sizeof(T);        // the dO tile follows the Q tile
