@@ -2,12 +2,12 @@
 //
 // One workgroup = 4 wavefronts = a tile of 128 query rows of one (sequence,
 // query head); each wavefront owns 32 rows. The workgroup streams the visible
-// 64-key tiles of K and V through LDS (tiling and fusion as in the
+// 64-key tiles (128 at d = 64) of K and V through LDS (tiling and fusion as in the
 // FlashAttention guide, cxbdf.cn, part 2; K/V blocks in fast on-chip memory
 // with a loop over Q blocks, Flash Attention 是什麼, adersaytech.com, section
 // 分塊計算), so S and P live only in registers.
 //
-// Per 64-key tile and wavefront:
+// Per key tile and wavefront:
 //   Sᵀ = K·Qᵀ        32 MFMA columns = the wave's 32 queries, so every lane
 //                    owns one query row and the row statistics are lane-local
 //                    (plus one exchange between the two lane halves)
@@ -32,12 +32,17 @@ namespace fa {
 namespace {
 
 constexpr int kBR = 128;  // query rows per workgroup
-constexpr int kBC = 64;   // keys per tile
+// Keys per tile: 128 at d = 64, where a wave's tile state is small enough to
+// take twice the keys per step (more independent MFMA chains per step, half
+// the steps on the longest causal tile's critical path), 64 otherwise (and
+// with dropout, whose generator calls are laid out for 64-key tiles).
+template <int D, bool DROP>
+constexpr int keys_per_tile() { return D == 64 && !DROP ? 128 : 64; }
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 constexpr float kRescaleHeadroom = 8.f;  // log2 of the largest P before the max is raised
 
-// One 64-key tile for one wave's 32 query rows: Sᵀ = K·Qᵀ, online softmax
+// One tile of BC keys for one wave's 32 query rows: Sᵀ = K·Qᵀ, online softmax
 // with a lazily raised reference max, Oᵀ += Vᵀ·Pᵀ. EDGE tiles mask keys past
 // the sequence end and, causally, keys after the query. CAP: the logits
 // are soft-capped, s = c_out·tanh(z·c_in) in log2 units (then c is 1).
@@ -52,18 +57,22 @@ __device__ __forceinline__ void fwd_tile(const T* kt, const T* vt, const u32x4 (
                                          bool empty_rows = false) {
   constexpr int NKB = D / 16;
   constexpr int NCB = D / 32;
+  constexpr int BC = keys_per_tile<D, DROP>();
+  constexpr int NJB = BC / 32;   // 32-key blocks of Sᵀ
   const int col = lane & 31, half = lane >> 5;
   // ---- Sᵀ = K·Qᵀ ----------------------------------------------------------
-  f32x16 s[2] = {f32x16{}, f32x16{}};
+  f32x16 s[NJB];
+#pragma unroll
+  for (int jb = 0; jb < NJB; ++jb) s[jb] = f32x16{};
 #pragma unroll
   for (int kb = 0; kb < NKB; ++kb) {
 #pragma unroll
-    for (int jb = 0; jb < 2; ++jb)
+    for (int jb = 0; jb < NJB; ++jb)
       s[jb] = mfma32<T>(lds_row16<T, D>(kt, jb * 32 + col, 2 * kb + half), qf[kb], s[jb]);
   }
   if constexpr (CAP) {
 #pragma unroll
-    for (int jb = 0; jb < 2; ++jb)
+    for (int jb = 0; jb < NJB; ++jb)
 #pragma unroll
       for (int i = 0; i < 16; ++i) s[jb][i] = cap_out * tanh_fast(s[jb][i] * cap_in);
   }
@@ -71,7 +80,7 @@ __device__ __forceinline__ void fwd_tile(const T* kt, const T* vt, const u32x4 (
   // ---- mask: keys past the sequence end, keys after the query (causal) ---
   if constexpr (EDGE) {
 #pragma unroll
-    for (int jb = 0; jb < 2; ++jb)
+    for (int jb = 0; jb < NJB; ++jb)
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const int key = kv0 + jb * 32 + 8 * (i >> 2) + 4 * half + (i & 3);
@@ -86,7 +95,9 @@ __device__ __forceinline__ void fwd_tile(const T* kt, const T* vt, const u32x4 (
 #pragma unroll
   for (int i = 1; i < 16; ++i) mx = fmaxf(mx, s[0][i]);
 #pragma unroll
-  for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[1][i]);
+  for (int jb = 1; jb < NJB; ++jb)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[jb][i]);
   const float mxc = wave_max_halves(mx) * c;
   // a window's edge tile can hold no visible key for a row that has seen none
   // yet either: such a row keeps mc = −inf, scales nothing and adds P = 0
@@ -104,7 +115,7 @@ __device__ __forceinline__ void fwd_tile(const T* kt, const T* vt, const u32x4 (
   // bf16 also sums the unrounded P in fp32 for the LSE (kLseFromUnrounded)
   float ls[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int jb = 0; jb < 2; ++jb)
+  for (int jb = 0; jb < NJB; ++jb)
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       s[jb][i] = fast_exp2(fmaf(s[jb][i], c, guard && mc == -INFINITY ? 0.f : -mc));
@@ -115,7 +126,7 @@ __device__ __forceinline__ void fwd_tile(const T* kt, const T* vt, const u32x4 (
   // ---- Oᵀ += Vᵀ·Pᵀ ---------------------------------------------------------
   // lr sums P as rounded to T for the MFMAs; O is normalised by it, so that
   // the rounding of a dominant P cancels in O instead of scaling it
-  float r[kBC / 16];   // independent partial sums: short dependency chains
+  float r[BC / 16];   // independent partial sums: short dependency chains
   // dropout: the row bytes of key runs kv0 + 16·kk + 4·half (+ 8), kk = 0..3
   uint32_t drb[2][4] = {{0, 0, 0, 0}, {0, 0, 0, 0}};
   if constexpr (DROP) {
@@ -127,7 +138,7 @@ __device__ __forceinline__ void fwd_tile(const T* kt, const T* vt, const u32x4 (
     }
   }
 #pragma unroll
-  for (int kk = 0; kk < kBC / 16; ++kk) {
+  for (int kk = 0; kk < BC / 16; ++kk) {
     u32x4 pf = acc_operand<T>(s[kk >> 1], (kk & 1) * 2);
     r[kk] = dot2_sum<T>(pf, 0.f);
     const int k0 = kk * 16 + 4 * half;
@@ -146,7 +157,10 @@ __device__ __forceinline__ void fwd_tile(const T* kt, const T* vt, const u32x4 (
     for (int cb = 0; cb < NCB; ++cb)
       o[cb] = mfma32<T>(lds_tr8<T, D>(vt, k0, k0 + 8, cb * 32, lane), pf, o[cb]);
   }
-  lr += (r[0] + r[1]) + (r[2] + r[3]);
+  float rs = (r[0] + r[1]) + (r[2] + r[3]);
+#pragma unroll
+  for (int kk = 4; kk < BC / 16; kk += 4) rs += (r[kk] + r[kk + 1]) + (r[kk + 2] + r[kk + 3]);
+  lr += rs;
 }
 
 // WIN: sliding window, key j visible from query i iff i − a.wl ≤ j ≤ i + a.wr
@@ -160,6 +174,7 @@ template <typename T, int D, bool CAUSAL, bool VARLEN, bool WIN, bool CAP = fals
 // two workgroups per CU up to d = 128; at d = 256 the O accumulators alone
 // take 128 registers and the kernel runs one workgroup per CU
 __global__ __launch_bounds__(kThreads, D <= 128 ? 2 : 1) void fwd_kernel(FwdArgs a) {
+  constexpr int kBC = keys_per_tile<D, DROP>();   // keys per tile
   constexpr int NKB = D / 16;    // k steps of K·Qᵀ
   constexpr int NCB = D / 32;    // 32-row blocks of Oᵀ
   constexpr int TILE = kBC * D;  // elements per K or V tile
