@@ -87,11 +87,32 @@ _SIGS = {
     "fa_fwd_kvcache_workspace_size": (_SZ, [_I] * 7),
     "fa_status_string": (ctypes.c_char_p, [_I]),
     "fa_check_cu_seqlens": (_I, [_VP, _I, _I]),
+    "fa_fwd_ex": (_I, _FWD_HEAD + [_VP, _VP, _I, _VP]),      # ... scale  opts cu_seqlens dtype stream
+    "fa_bwd_ex": (_I, _BWD_HEAD + [_VP] + _BWD_TAIL),       # ... scale  opts cu_seqlens dtype ws bytes stream
 }
 # each staged entry point takes a leading stage index, then its parent's arguments
 for _n in ("fa_bwd", "fa_bwd_window", "fa_bwd_window_softcap", "fa_bwd_softcap",
            "fa_bwd_dropout", "fa_bwd_kvlen", "fa_fwd_kvcache", "fa_fwd_kvcache_fp8"):
     _SIGS[_n + "_stage"] = (_I, [_I] + _SIGS[_n][1])
+
+
+FA_MASK_NONE, FA_MASK_CAUSAL, FA_MASK_WINDOW = 0, 1, 2
+
+
+class FaAttnOptions(ctypes.Structure):
+    """fa_attn_options of include/fa.h (the argument of fa_fwd_ex / fa_bwd_ex)."""
+    _fields_ = [("struct_size", ctypes.c_size_t), ("mask", ctypes.c_int),
+                ("window_left", ctypes.c_int), ("window_right", ctypes.c_int),
+                ("softcap", ctypes.c_float), ("dropout_p", ctypes.c_float),
+                ("dropout_seed", ctypes.c_uint64)]
+
+
+def attn_options(mask=FA_MASK_NONE, window=(-1, -1), softcap=0.0, dropout_p=0.0,
+                 dropout_seed=0) -> FaAttnOptions:
+    """An fa_attn_options with struct_size filled in; pass ctypes.addressof(...)
+    (keep the object alive across the call)."""
+    return FaAttnOptions(ctypes.sizeof(FaAttnOptions), int(mask), int(window[0]),
+                         int(window[1]), float(softcap), float(dropout_p), int(dropout_seed))
 
 
 def _load():
@@ -125,7 +146,8 @@ def fa_status_string(status: int) -> str:
 
 
 __all__ = (["FA_OK", "FA_ERR_INVALID_ARG", "FA_ERR_UNSUPPORTED", "FA_ERR_HIP", "FA_ERR_WORKSPACE",
-            "FA_FP16", "FA_BF16", "FaError", "lib", "lib_path", "flash_attn_func",
+            "FA_FP16", "FA_BF16", "FA_MASK_NONE", "FA_MASK_CAUSAL", "FA_MASK_WINDOW",
+            "FaAttnOptions", "attn_options", "FaError", "lib", "lib_path", "flash_attn_func",
             "flash_attn_backward", "flash_attn_func_fp8", "flash_attn_kvlen_func",
             "flash_attn_kvlen_backward", "flash_attn_with_kvcache"] + sorted(_SIGS))
 

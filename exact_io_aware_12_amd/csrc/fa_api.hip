@@ -1,14 +1,16 @@
 // C ABI of libfa.so (declared in include/fa.h): argument checks, then the
-// kernel launches. Nothing here allocates device memory. The only global
-// state is the cache of the decode kernel's occupancy figures
-// (decode_residency), filled once per process with values that are the same
-// for every caller. Built with FA_DEBUG defined, every cu_seqlens argument is
+// kernel launches. Nothing here allocates device memory. The global state is
+// the cache of the decode kernel's occupancy figures (decode_residency),
+// filled once per process with values that are the same for every caller,
+// and fa_bwd_noalloc's fixed device array `scratch` with its per-device
+// addresses. Built with FA_DEBUG defined, every cu_seqlens argument is
 // copied to the host and checked before the launch, and every launch is
 // followed by a synchronisation that reports a failed kernel.
 #include <algorithm>
 #include <atomic>
 #include <mutex>
 #include <cmath>
+#include <cstddef>
 #include <cstdint>
 
 #include "fa.h"
@@ -538,6 +540,84 @@ int fa_bwd_dropout_stage(int stage, const void* q, const void* k, const void* v,
 }
 
 int fa_bwd_num_stages(void) { return fa::bwd_num_stages(); }
+
+// fa_attn_options as the binding mirrors it (ctypes lays it out by the same C rules)
+static_assert(sizeof(fa_attn_options) == 40 && offsetof(fa_attn_options, mask) == 8 &&
+                  offsetof(fa_attn_options, softcap) == 20 &&
+                  offsetof(fa_attn_options, dropout_seed) == 32,
+              "fa_attn_options layout");
+
+// The options of fa_fwd_ex / fa_bwd_ex, checked; which entry point they select.
+enum class ExRoute { kPlain, kWindow, kSoftcap, kWindowSoftcap, kDropout };
+
+static int ex_route(const fa_attn_options* opts, ExRoute* route) {
+  if (opts == nullptr || opts->struct_size < sizeof(fa_attn_options)) return FA_ERR_INVALID_ARG;
+  const int mask = static_cast<int>(opts->mask);
+  if (mask != FA_MASK_NONE && mask != FA_MASK_CAUSAL && mask != FA_MASK_WINDOW)
+    return FA_ERR_INVALID_ARG;
+  const bool window = mask == FA_MASK_WINDOW;
+  const bool cap = opts->softcap != 0.f, drop = opts->dropout_p != 0.f;
+  if (drop && (window || cap)) return FA_ERR_UNSUPPORTED;
+  *route = drop ? ExRoute::kDropout
+         : window ? (cap ? ExRoute::kWindowSoftcap : ExRoute::kWindow)
+         : cap ? ExRoute::kSoftcap : ExRoute::kPlain;
+  return FA_OK;
+}
+
+int fa_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq,
+              int Hkv, int N, int d, float scale, const fa_attn_options* opts,
+              const int32_t* cu_seqlens, fa_dtype dtype, hipStream_t stream) {
+  ExRoute r;
+  const int st = ex_route(opts, &r);
+  if (st != FA_OK) return st;
+  const int causal = opts->mask == FA_MASK_CAUSAL;
+  switch (r) {
+    case ExRoute::kWindow:
+      return fa_fwd_window(q, k, v, o, lse, B, Hq, Hkv, N, d, scale, opts->window_left,
+                           opts->window_right, cu_seqlens, dtype, stream);
+    case ExRoute::kSoftcap:
+      return fa_fwd_softcap(q, k, v, o, lse, B, Hq, Hkv, N, d, scale, causal, opts->softcap,
+                            cu_seqlens, dtype, stream);
+    case ExRoute::kWindowSoftcap:
+      return fa_fwd_window_softcap(q, k, v, o, lse, B, Hq, Hkv, N, d, scale, opts->window_left,
+                                   opts->window_right, opts->softcap, cu_seqlens, dtype, stream);
+    case ExRoute::kDropout:
+      return fa_fwd_dropout(q, k, v, o, lse, B, Hq, Hkv, N, d, scale, causal, opts->dropout_p,
+                            opts->dropout_seed, cu_seqlens, dtype, stream);
+    default:
+      return fa_fwd(q, k, v, o, lse, B, Hq, Hkv, N, d, scale, causal, cu_seqlens, dtype, stream);
+  }
+}
+
+int fa_bwd_ex(const void* q, const void* k, const void* v, const void* o, const void* dout,
+              const float* lse, void* dq, void* dk, void* dv, int B, int Hq, int Hkv, int N,
+              int d, float scale, const fa_attn_options* opts, const int32_t* cu_seqlens,
+              fa_dtype dtype, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  ExRoute r;
+  const int st = ex_route(opts, &r);
+  if (st != FA_OK) return st;
+  const int causal = opts->mask == FA_MASK_CAUSAL;
+  switch (r) {
+    case ExRoute::kWindow:
+      return fa_bwd_window(q, k, v, o, dout, lse, dq, dk, dv, B, Hq, Hkv, N, d, scale,
+                           opts->window_left, opts->window_right, cu_seqlens, dtype, workspace,
+                           workspace_bytes, stream);
+    case ExRoute::kSoftcap:
+      return fa_bwd_softcap(q, k, v, o, dout, lse, dq, dk, dv, B, Hq, Hkv, N, d, scale, causal,
+                            opts->softcap, cu_seqlens, dtype, workspace, workspace_bytes, stream);
+    case ExRoute::kWindowSoftcap:
+      return fa_bwd_window_softcap(q, k, v, o, dout, lse, dq, dk, dv, B, Hq, Hkv, N, d, scale,
+                                   opts->window_left, opts->window_right, opts->softcap,
+                                   cu_seqlens, dtype, workspace, workspace_bytes, stream);
+    case ExRoute::kDropout:
+      return fa_bwd_dropout(q, k, v, o, dout, lse, dq, dk, dv, B, Hq, Hkv, N, d, scale, causal,
+                            opts->dropout_p, opts->dropout_seed, cu_seqlens, dtype, workspace,
+                            workspace_bytes, stream);
+    default:
+      return fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, B, Hq, Hkv, N, d, scale, causal,
+                    cu_seqlens, dtype, workspace, workspace_bytes, stream);
+  }
+}
 
 }  // extern "C"
 

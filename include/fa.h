@@ -41,11 +41,11 @@
  * Alignment: every tensor pointer must be 16-byte aligned (FA_ERR_INVALID_ARG
  *   otherwise); rows are moved as 16-byte vectors.
  * Ownership: every pointer is device memory owned by the caller. The library
- * allocates nothing and keeps no pointer after returning. Its only global
- * state is a cache of the decode kernel's occupancy figures, filled on first
- * use by whichever thread gets there (the values are the same for every
- * caller); calls on different streams may run concurrently. Outputs must not
- * alias inputs.
+ * allocates nothing and keeps no pointer after returning. Its global state
+ * is a cache of the decode kernel's occupancy figures, filled on first use by
+ * whichever thread gets there (the values are the same for every caller), and
+ * the fixed device array that only fa_bwd_noalloc uses (see there); calls on
+ * different streams may run concurrently. Outputs must not alias inputs.
  *
  * Errors: arguments are checked on the host before anything is enqueued; on
  * a negative status nothing was enqueued. FA_ERR_UNSUPPORTED marks a valid
@@ -281,6 +281,52 @@ int fa_bwd_dropout_stage(int stage, const void* q, const void* k, const void* v,
                          int B, int Hq, int Hkv, int N, int d, float scale, int causal,
                          float dropout_p, uint64_t seed, const int32_t* cu_seqlens, fa_dtype dtype,
                          void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * One forward and one backward for every mask and extra above, chosen by an
+ * options struct instead of by entry point, so that a caller (or a new
+ * combination) needs no further pair of symbols. Each call checks the options
+ * and then runs exactly the entry point named below, with the same arguments,
+ * checks, results (bit for bit), workspace and errors:
+ *   mask FA_MASK_NONE / FA_MASK_CAUSAL, no extras ........ fa_fwd / fa_bwd
+ *   FA_MASK_WINDOW (window_left, window_right as for
+ *     fa_fwd_window) ...................................... fa_fwd_window / fa_bwd_window
+ *   softcap > 0, mask NONE or CAUSAL ..................... fa_fwd_softcap / fa_bwd_softcap
+ *   softcap > 0 with FA_MASK_WINDOW ...................... fa_fwd_window_softcap / ...
+ *   dropout_p > 0, mask NONE or CAUSAL, no soft cap ...... fa_fwd_dropout / fa_bwd_dropout
+ *   dropout with a window or a soft cap: FA_ERR_UNSUPPORTED (no kernel has both)
+ * opts must point to host memory holding an fa_attn_options whose struct_size
+ * is at least sizeof(fa_attn_options) (the struct may grow at its end); a NULL
+ * opts, a smaller struct_size or another mask is FA_ERR_INVALID_ARG. The
+ * window fields are read only with FA_MASK_WINDOW, dropout_seed only with
+ * dropout_p > 0. Nothing in *opts is kept after the call.
+ */
+typedef enum {
+  FA_MASK_NONE = 0,
+  FA_MASK_CAUSAL = 1,
+  FA_MASK_WINDOW = 2,
+  FA_MASK_FORCE_INT = 0x7fffffff   /* not a mask: keeps fa_mask int-sized */
+} fa_mask;
+
+typedef struct {
+  size_t struct_size;      /* sizeof(fa_attn_options) */
+  fa_mask mask;
+  int window_left;         /* FA_MASK_WINDOW: as fa_fwd_window's (-1 = unbounded) */
+  int window_right;
+  float softcap;           /* 0 = none; else as fa_fwd_softcap's */
+  float dropout_p;         /* 0 = none; else as fa_fwd_dropout's */
+  uint64_t dropout_seed;
+} fa_attn_options;
+
+int fa_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse,
+              int B, int Hq, int Hkv, int N, int d, float scale,
+              const fa_attn_options* opts, const int32_t* cu_seqlens, fa_dtype dtype,
+              hipStream_t stream);
+int fa_bwd_ex(const void* q, const void* k, const void* v, const void* o,
+              const void* dout, const float* lse, void* dq, void* dk, void* dv,
+              int B, int Hq, int Hkv, int N, int d, float scale,
+              const fa_attn_options* opts, const int32_t* cu_seqlens, fa_dtype dtype,
+              void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
  * Forward with queries and keys of different lengths (chunked prefill: a block

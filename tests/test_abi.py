@@ -21,13 +21,14 @@ def declared_functions():
 
 def test_header_declares_the_boundary():
     assert declared_functions() == ["fa_bwd", "fa_bwd_dropout", "fa_bwd_dropout_stage",
+                                    "fa_bwd_ex",
                                     "fa_bwd_kvlen", "fa_bwd_kvlen_stage",
                                     "fa_bwd_noalloc", "fa_bwd_num_stages", "fa_bwd_softcap",
                                     "fa_bwd_softcap_stage", "fa_bwd_stage",
                                     "fa_bwd_window", "fa_bwd_window_softcap",
                                     "fa_bwd_window_softcap_stage", "fa_bwd_window_stage",
                                     "fa_bwd_workspace_size", "fa_check_cu_seqlens", "fa_fwd",
-                                    "fa_fwd_dropout",
+                                    "fa_fwd_dropout", "fa_fwd_ex",
                                     "fa_fwd_fp8",
                                     "fa_fwd_kvcache", "fa_fwd_kvcache_fp8",
                                     "fa_fwd_kvcache_fp8_stage", "fa_fwd_kvcache_local",
@@ -860,3 +861,81 @@ def test_library_exports_exactly_the_header():
     funcs = sorted(line.split()[-1] for line in out.splitlines()
                    if len(line.split()) == 3 and line.split()[1] == "T")
     assert funcs == declared_functions()
+
+
+# ---- fa_fwd_ex / fa_bwd_ex: the options struct ----------------------------------
+
+def test_attn_options_layout():
+    """The ctypes mirror has the C layout the library asserts at compile time."""
+    import ctypes
+    O = fa.FaAttnOptions
+    assert ctypes.sizeof(O) == 40
+    assert (O.mask.offset, O.window_left.offset, O.softcap.offset, O.dropout_p.offset,
+            O.dropout_seed.offset) == (8, 12, 20, 24, 32)
+
+
+def fwd_ex(opts, **kw):
+    import ctypes
+    a = dict(q=P, k=P, v=P, o=P, lse=P, B=1, Hq=2, Hkv=2, N=16, d=64, scale=0.125,
+             dtype=fa.FA_FP16)
+    a.update(kw)
+    ptr = None if opts is None else ctypes.addressof(opts)
+    return fa.fa_fwd_ex(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["Hq"], a["Hkv"],
+                        a["N"], a["d"], a["scale"], ptr, None, a["dtype"], None)
+
+
+def bwd_ex(opts, **kw):
+    import ctypes
+    a = dict(B=1, Hq=2, Hkv=2, N=16, d=64, scale=0.125, dtype=fa.FA_BF16, ws=P, wsb=1 << 20)
+    a.update(kw)
+    ptrs = [kw.get(n, P) for n in ("q", "k", "v", "o", "do", "lse", "dq", "dk", "dv")]
+    ptr = None if opts is None else ctypes.addressof(opts)
+    return fa.fa_bwd_ex(*ptrs, a["B"], a["Hq"], a["Hkv"], a["N"], a["d"], a["scale"], ptr, None,
+                        a["dtype"], a["ws"], a["wsb"], None)
+
+
+def _short_struct():
+    o = fa.attn_options()
+    o.struct_size = 32
+    return o
+
+
+@pytest.mark.parametrize("opts,kw,status", [
+    (None, {}, fa.FA_ERR_INVALID_ARG),                                            # NULL options
+    ("short", {}, fa.FA_ERR_INVALID_ARG),                                         # struct too small
+    (dict(mask=3), {}, fa.FA_ERR_INVALID_ARG),                                    # no such mask
+    (dict(mask=-1), {}, fa.FA_ERR_INVALID_ARG),
+    (dict(mask=fa.FA_MASK_WINDOW, dropout_p=0.1), {}, fa.FA_ERR_UNSUPPORTED),    # no kernel has both
+    (dict(softcap=5.0, dropout_p=0.1), {}, fa.FA_ERR_UNSUPPORTED),
+    (dict(mask=fa.FA_MASK_WINDOW, window=(-2, 0)), {}, fa.FA_ERR_INVALID_ARG),   # fa_fwd_window's check
+    (dict(softcap=-1.0), {}, fa.FA_ERR_INVALID_ARG),                              # fa_fwd_softcap's check
+    (dict(softcap=float("nan")), {}, fa.FA_ERR_INVALID_ARG),
+    (dict(dropout_p=1.5), {}, fa.FA_ERR_INVALID_ARG),                             # fa_fwd_dropout's check
+    (dict(mask=fa.FA_MASK_CAUSAL), dict(dtype=7), fa.FA_ERR_INVALID_ARG),         # fa_fwd's check
+    (dict(mask=fa.FA_MASK_CAUSAL), dict(d=96), fa.FA_ERR_UNSUPPORTED),
+    (dict(mask=fa.FA_MASK_CAUSAL, softcap=5.0), dict(B=0), fa.FA_OK),             # empty batch
+])
+def test_ex_host_checks(opts, kw, status):
+    o = None if opts is None else _short_struct() if opts == "short" else fa.attn_options(**opts)
+    assert fwd_ex(o, **kw) == status
+    bkw = {k: v for k, v in kw.items() if k != "dtype"}
+    if "dtype" in kw:
+        bkw["dtype"] = kw["dtype"]
+    assert bwd_ex(o, **bkw) == status
+
+
+def test_ex_backward_workspace_checked():
+    assert bwd_ex(fa.attn_options(mask=fa.FA_MASK_CAUSAL), ws=None) == fa.FA_ERR_WORKSPACE
+    assert bwd_ex(fa.attn_options(dropout_p=0.2, dropout_seed=3), wsb=64) == fa.FA_ERR_WORKSPACE
+
+
+def test_ex_no_device_reports_hip_error():
+    """Each route passes its checks and fails only at the launch without a GPU."""
+    torch = pytest.importorskip("torch")
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    for opts in (dict(), dict(mask=fa.FA_MASK_CAUSAL), dict(mask=fa.FA_MASK_WINDOW, window=(8, 0)),
+                 dict(softcap=5.0), dict(mask=fa.FA_MASK_WINDOW, window=(8, 8), softcap=5.0),
+                 dict(mask=fa.FA_MASK_CAUSAL, dropout_p=0.2, dropout_seed=9)):
+        assert fwd_ex(fa.attn_options(**opts)) == fa.FA_ERR_HIP, opts
+        assert bwd_ex(fa.attn_options(**opts)) == fa.FA_ERR_HIP, opts
