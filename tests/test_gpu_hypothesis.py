@@ -82,3 +82,70 @@ def test_random_shapes_match_oracle(w):
     for g, r, n in zip((dq, dk, dv), g_ref, ("dQ", "dK", "dV")):
         if np.abs(r).max(initial=0.0) > 0:
             check_grad(host64(g.body), r, n)
+
+
+@st.composite
+def masked(draw):
+    """A shape plus options for fa_fwd_ex / fa_bwd_ex: a mask (none, causal, or a
+    window with each bound unbounded or 0-300 positions) and a soft cap (none or
+    1-60)."""
+    w = draw(shapes())
+    kind = draw(st.sampled_from(["none", "causal", "window"]))
+    cap = draw(st.one_of(st.just(0.0), st.floats(1.0, 60.0)))
+    bound = st.one_of(st.just(-1), st.integers(0, 300))
+    window = (draw(bound), draw(bound)) if kind == "window" else (-1, -1)
+    return w, kind, window, cap
+
+
+@settings(max_examples=30, deadline=None, derandomize=True, database=None,
+          suppress_health_check=list(HealthCheck))
+@given(case=masked())
+def test_random_masks_and_caps_match_oracle(case):
+    """The options-struct entry points on drawn shapes, masks and soft caps, against
+    the oracle's window and soft-cap arguments, inside guard bands."""
+    import ctypes
+    import torch
+    import exact_io_aware_12_amd as fa
+    w, kind, window, cap = case
+    mask = {"none": fa.FA_MASK_NONE, "causal": fa.FA_MASK_CAUSAL, "window": fa.FA_MASK_WINDOW}[kind]
+    say(f"[hypothesis-ex] B={w.B} Hq={w.Hq} Hkv={w.Hkv} N={w.N} d={w.d} {w.dtype} lens={w.lens} "
+        f"seed={w.seed} mask={kind} window={window} softcap={cap}")
+    opts = fa.attn_options(mask=mask, window=window, softcap=cap)
+    a = W.generate(w, with_grad=True)
+    t = to_device(a, w.dtype)
+    td = t["q"].dtype
+    code = fa.FA_BF16 if w.dtype == "bf16" else fa.FA_FP16
+    cu = t["cu_seqlens"].data_ptr() if w.varlen else None
+    o = Guarded((w.T, w.Hq, w.d), td)
+    lse = Guarded((w.Hq, w.T), torch.float32)
+    st_ = fa.fa_fwd_ex(t["q"].data_ptr(), t["k"].data_ptr(), t["v"].data_ptr(), o.ptr(), lse.ptr(),
+                       w.B, w.Hq, w.Hkv, w.N, w.d, float(w.scale), ctypes.addressof(opts), cu, code,
+                       _stream())
+    assert st_ == fa.FA_OK, fa.fa_status_string(st_)
+    dq = Guarded((w.T, w.Hq, w.d), td)
+    dk = Guarded((w.T, w.Hkv, w.d), td)
+    dv = Guarded((w.T, w.Hkv, w.d), td)
+    nws = fa.fa_bwd_workspace_size(w.B, w.Hq, w.Hkv, w.N, w.d)
+    ws = Guarded((max(nws, 1),), torch.uint8)
+    st_ = fa.fa_bwd_ex(t["q"].data_ptr(), t["k"].data_ptr(), t["v"].data_ptr(), o.ptr(),
+                       t["do"].data_ptr(), lse.ptr(), dq.ptr(), dk.ptr(), dv.ptr(), w.B, w.Hq,
+                       w.Hkv, w.N, w.d, float(w.scale), ctypes.addressof(opts), cu, code,
+                       ws.ptr(), nws, _stream())
+    assert st_ == fa.FA_OK, fa.fa_status_string(st_)
+    torch.cuda.synchronize()
+    for g, n in ((o, "O"), (lse, "LSE"), (dq, "dQ"), (dk, "dK"), (dv, "dV"), (ws, "workspace")):
+        g.check(n)
+    h = {n: host64(t[n]) for n in ("q", "k", "v", "do")}
+    cus = a["cu_seqlens"]
+    causal = kind == "causal"
+    win = window if kind == "window" else None
+    sc = cap if cap else None
+    o_ref, lse_ref = attention_fwd(h["q"], h["k"], h["v"], w.scale, causal, cus, window=win,
+                                   softcap=sc)
+    check_o(host64(o.body), o_ref, w.dtype)
+    check_lse(host64(lse.body), lse_ref)
+    g_ref = attention_bwd(h["q"], h["k"], h["v"], h["do"], w.scale, causal, cus, window=win,
+                          softcap=sc)
+    for g, r, n in zip((dq, dk, dv), g_ref, ("dQ", "dK", "dV")):
+        if np.abs(r).max(initial=0.0) > 0:
+            check_grad(host64(g.body), r, n)
