@@ -156,6 +156,62 @@ void forward_cases(Buffers& m) {
                        nullptr), FA_ERR_INVALID_ARG);
 }
 
+// fa_fwd_ex / fa_bwd_ex: the options struct sits in a heap block of exactly its size, so
+// a read past it is reported
+void options_cases(Buffers& m) {
+  const int B = 2, H = 4, N = 64, d = 128;
+  const size_t t = (size_t)B * N * H * d * 2;
+  void *q = m.get(t), *k = m.get(t), *v = m.get(t), *o = m.get(t), *dout = m.get(t);
+  void *dq = m.get(t), *dk = m.get(t), *dv = m.get(t);
+  float* lse = static_cast<float*>(m.get((size_t)H * B * N * 4));
+  const size_t wsb = fa_bwd_workspace_size(B, H, H, N, d);
+  void* ws = m.get(wsb);
+  const float sc = 0.125f;
+  fa_attn_options* op = static_cast<fa_attn_options*>(m.get(sizeof(fa_attn_options)));
+  auto set = [&](int mask, int wl, int wr, float cap, float p) {
+    op->struct_size = sizeof(fa_attn_options);
+    op->mask = (fa_mask)mask;
+    op->window_left = wl;
+    op->window_right = wr;
+    op->softcap = cap;
+    op->dropout_p = p;
+    op->dropout_seed = 11;
+  };
+  auto fwd = [&](const fa_attn_options* x) {
+    return fa_fwd_ex(q, k, v, o, lse, B, H, H, N, d, sc, x, nullptr, FA_BF16, nullptr);
+  };
+  auto bwd = [&](const fa_attn_options* x) {
+    return fa_bwd_ex(q, k, v, o, dout, lse, dq, dk, dv, B, H, H, N, d, sc, x, nullptr, FA_BF16,
+                     ws, wsb, nullptr);
+  };
+  EXPECT_ST(fwd(nullptr), FA_ERR_INVALID_ARG);
+  EXPECT_ST(bwd(nullptr), FA_ERR_INVALID_ARG);
+  set(FA_MASK_CAUSAL, -1, -1, 0.f, 0.f);
+  op->struct_size = sizeof(fa_attn_options) - 8;
+  EXPECT_ST(fwd(op), FA_ERR_INVALID_ARG);                        // struct too small
+  set(3, -1, -1, 0.f, 0.f);
+  EXPECT_ST(fwd(op), FA_ERR_INVALID_ARG);                        // no such mask
+  EXPECT_ST(bwd(op), FA_ERR_INVALID_ARG);
+  set(FA_MASK_WINDOW, 8, 0, 0.f, 0.2f);
+  EXPECT_ST(fwd(op), FA_ERR_UNSUPPORTED);                        // dropout with a window
+  set(FA_MASK_CAUSAL, -1, -1, 5.f, 0.2f);
+  EXPECT_ST(bwd(op), FA_ERR_UNSUPPORTED);                        // dropout with a soft cap
+  set(FA_MASK_WINDOW, -2, 0, 0.f, 0.f);
+  EXPECT_ST(fwd(op), FA_ERR_INVALID_ARG);                        // the window entry's check
+  set(FA_MASK_NONE, -1, -1, -1.f, 0.f);
+  EXPECT_ST(fwd(op), FA_ERR_INVALID_ARG);                        // the soft-cap entry's check
+  set(FA_MASK_CAUSAL, -1, -1, 0.f, 0.f);
+  EXPECT_ST(bwd(op), FA_ERR_HIP);                                 // past the checks
+  const int routes[5][5] = {{FA_MASK_NONE, -1, -1, 0, 0}, {FA_MASK_WINDOW, 16, 0, 0, 0},
+                            {FA_MASK_CAUSAL, -1, -1, 1, 0}, {FA_MASK_WINDOW, 8, 8, 1, 0},
+                            {FA_MASK_CAUSAL, -1, -1, 0, 1}};
+  for (const auto& r : routes) {
+    set(r[0], r[1], r[2], r[3] ? 30.f : 0.f, r[4] ? 0.1f : 0.f);
+    EXPECT_ST(fwd(op), FA_ERR_HIP);
+    EXPECT_ST(bwd(op), FA_ERR_HIP);
+  }
+}
+
 void backward_cases(Buffers& m) {
   const int B = 2, H = 4, N = 64, d = 128;
   const size_t t = (size_t)B * N * H * d * 2;
@@ -253,6 +309,7 @@ int main() {
   Buffers m;
   cu_seqlens_cases();
   forward_cases(m);
+  options_cases(m);
   backward_cases(m);
   size_cases();
   decode_cases(m);
