@@ -119,3 +119,35 @@ def test_train_16k_backward_every_unit():
         worst = [max(a, r[0]) for a, r in zip(worst, res)]
     say(f"   every unit ({len(units)}): worst rel dQ {worst[0]:.2e} dK {worst[1]:.2e} "
         f"dV {worst[2]:.2e}")
+
+
+def test_gqa_varlen_backward_every_unit():
+    """The GQA packed-batch workload (Hq 32, Hkv 8, 8 sequences of 1024-8192
+    tokens, causal) through the backward at full size: for every (sequence, KV
+    head) unit, dQ of the unit's 4 query heads on query rows and dK, dV on keys
+    from the first, one inner and the last tile of the sequence, against the
+    oracle's selected-row backward. The dK/dV kernel's loop over the query heads
+    of a group and its ragged last tiles run here at their full-size form."""
+    w = W.WORKLOADS["gqa_varlen"]
+    (dq, dk, dv), t = run_fwd_bwd(w)
+    cu = w.cu_seqlens()
+    rng = np.random.default_rng(56)
+    q, k, v, do = (host32(t[n]) for n in ("q", "k", "v", "do"))
+    g = w.Hq // w.Hkv
+    units = [(s, kvh) for s in range(w.B) for kvh in range(w.Hkv)]
+    lens = np.diff(cu)
+    sel = {u: (tile_rows(rng, int(lens[u[0]]), 128), tile_rows(rng, int(lens[u[0]]), 128))
+           for u in units}
+    refs = map_units(lambda u: attention_bwd_rows(q, k, v, do, w.scale, w.causal, cu, u[0], u[1],
+                                                  *sel[u]), units)
+    dq_h, dk_h, dv_h = host64(dq), host64(dk), host64(dv)
+    worst = [0.0, 0.0, 0.0]
+    for u, (rq, rk, rv) in zip(units, refs):
+        (s, kvh), (qr, kr) = u, sel[u]
+        tq, tk = cu[s] + np.array(qr), cu[s] + np.array(kr)
+        res = (check_grad(dq_h[tq, kvh * g:(kvh + 1) * g], rq, f"dQ unit {u}"),
+               check_grad(dk_h[tk, kvh], rk, f"dK unit {u}"),
+               check_grad(dv_h[tk, kvh], rv, f"dV unit {u}"))
+        worst = [max(a, r[0]) for a, r in zip(worst, res)]
+    say(f"   every unit ({len(units)}): worst rel dQ {worst[0]:.2e} dK {worst[1]:.2e} "
+        f"dV {worst[2]:.2e}")
