@@ -239,8 +239,8 @@ def test_kvcache_splits_and_workspace():
     assert fa.fa_kvcache_num_splits(1, 2, 2, 1, 0, 64) == 1
     assert fa.fa_kvcache_num_splits(1, 3, 2, 1, 64, 64) == 0
     assert fa.fa_fwd_kvcache_workspace_size(2, 4, 2, 3, 64, 128, 5) == (5 * 2 * 4 * 3 * 129 * 4 + 255) // 256 * 256
-    # num_splits = 0: the larger automatic count (12, the e4m3 cache's)
-    assert fa.fa_fwd_kvcache_workspace_size(16, 32, 8, 1, 8192, 128, 0) == 12 * 16 * 32 * 129 * 4
+    # num_splits = 0: the larger automatic count (6 for both caches here)
+    assert fa.fa_fwd_kvcache_workspace_size(16, 32, 8, 1, 8192, 128, 0) == 6 * 16 * 32 * 129 * 4
     assert fa.fa_fwd_kvcache_workspace_size(1, 2, 2, 1, 64, 80, 1) == 0
 
 
@@ -361,8 +361,10 @@ def test_kvcache_fp8_host_checks(kw, status):
 
 
 def test_kvcache_fp8_splits():
-    # half the LDS per workgroup: 6 resident per CU, 1536 / (16·8) = 12 ranges
-    assert fa.fa_kvcache_fp8_num_splits(16, 32, 8, 1, 8192, 128) == 12
+    # half the LDS per workgroup: 6 resident per CU; the e4m3 count takes half of
+    # them, rounded up: 768 / (16·8) = 6 ranges (and ceil(768 / 512) = 2 for 64 entries)
+    assert fa.fa_kvcache_fp8_num_splits(16, 32, 8, 1, 8192, 128) == 6
+    assert fa.fa_kvcache_fp8_num_splits(64, 32, 8, 1, 2048, 128) == 2
     for shape in [(16, 32, 8, 1, 8192, 128), (1, 2, 2, 1, 100, 64), (1, 8, 1, 1, 40000, 256),
                   (3, 12, 4, 5, 777, 64), (64, 8, 8, 1, 1 << 20, 128), (4, 32, 8, 4, 4096, 128)]:
         n8, n16 = fa.fa_kvcache_fp8_num_splits(*shape), fa.fa_kvcache_num_splits(*shape)
