@@ -781,11 +781,13 @@ Residency decode_residency(int d, bool kv8, int dtype, int causal) {
 // eight key tiles (256 keys: on 4096-token caches shorter ranges measured
 // slower, their merge and fixed costs outweighing the extra parallelism), and
 // there are at most 256 ranges.
-// An e4m3 cache takes half that many workgroups, rounded up (so up to a full
-// round when the half is not whole): measured on six shapes (2048- to
-// 32768-token caches, 1 and 4 queries, 8 and 64 query heads, d = 128), half
-// the resident count was fastest in every one, by 9-18 % over a full round
-// (decode_llama's shape over an e4m3 cache: 47.5 against 54.7 µs).
+// An e4m3 cache at d <= 128 takes half that many workgroups, rounded up (so up
+// to a full round when the half is not whole): measured on six shapes at
+// d = 128 (2048- to 32768-token caches, 1 and 4 queries, 8 and 64 query heads)
+// and one at d = 64, half the resident count was fastest in every one, by
+// 9-18 % over a full round (decode_llama's shape over an e4m3 cache: 47.5
+// against 54.7 µs). At d = 256, where only two workgroups fit per CU, half
+// measured 30 % slower than the full round, which is kept there.
 // The count depends on the head dimension and the cache type only: the
 // residency taken is the smallest over query dtype and mask, so the query
 // functions below, which take neither, report exactly what a call uses.
@@ -801,7 +803,7 @@ int kv_splits(int B, int Hq, int Hkv, int Nq, int Nk, int d, bool kv8) {
   const int64_t rows = (int64_t)(Hq / Hkv) * Nq;
   const int64_t base = (int64_t)B * Hkv * ((rows + 31) / 32);
   const int64_t slots = (int64_t)r.per_cu * r.cus, b = base > 0 ? base : 1;
-  const int64_t want = kv8 ? (slots + 2 * b - 1) / (2 * b) : slots / b;
+  const int64_t want = kv8 && d <= 128 ? (slots + 2 * b - 1) / (2 * b) : slots / b;
   const int64_t most = std::max<int64_t>(1, (Nk + 8 * tk - 1) / (8 * tk));
   return (int)std::max<int64_t>(1, std::min<int64_t>(want, std::min<int64_t>(most, 256)));
 }

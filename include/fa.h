@@ -505,9 +505,9 @@ int fa_fwd_kvcache_fp8_stage(int stage, const void* q, const void* k_cache, cons
  * (eight 32-key tiles) per range and at most 256 ranges. */
 int fa_kvcache_num_splits(int B, int Hq, int Hkv, int Nq, int Nk, int d);
 /* The count fa_fwd_kvcache_fp8 uses for num_splits = 0: its workgroups need half
- * the LDS, so twice as many are resident, and the count is the one that fills half
- * of them, rounded up (measured fastest on every shape tried); the same range
- * bounds apply. */
+ * the LDS, so more are resident, and at d <= 128 the count is the one that fills
+ * half of them, rounded up (measured fastest on every shape tried; at d = 256 the
+ * full round measured fastest); the same range bounds apply. */
 int fa_kvcache_fp8_num_splits(int B, int Hq, int Hkv, int Nq, int Nk, int d);
 
 /* Workspace bytes for fa_fwd_kvcache and fa_fwd_kvcache_fp8: (d + 1)·4 bytes per

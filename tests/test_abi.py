@@ -365,6 +365,8 @@ def test_kvcache_fp8_splits():
     # them, rounded up: 768 / (16·8) = 6 ranges (and ceil(768 / 512) = 2 for 64 entries)
     assert fa.fa_kvcache_fp8_num_splits(16, 32, 8, 1, 8192, 128) == 6
     assert fa.fa_kvcache_fp8_num_splits(64, 32, 8, 1, 2048, 128) == 2
+    # d = 256 keeps the full round: 2 resident per CU (registers), 512 / (16·8) = 4 ranges
+    assert fa.fa_kvcache_fp8_num_splits(16, 32, 8, 1, 8192, 256) == 4
     for shape in [(16, 32, 8, 1, 8192, 128), (1, 2, 2, 1, 100, 64), (1, 8, 1, 1, 40000, 256),
                   (3, 12, 4, 5, 777, 64), (64, 8, 8, 1, 1 << 20, 128), (4, 32, 8, 4, 4096, 128)]:
         n8, n16 = fa.fa_kvcache_fp8_num_splits(*shape), fa.fa_kvcache_num_splits(*shape)
