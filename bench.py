@@ -13,6 +13,7 @@ causal; backward 2.5× the forward.
     python bench.py --workload decode_llama   # decode over a KV cache: HBM GB/s, one line
     python bench.py --pmc-step  # one calibration copy + one step, for rocprofv3 --pmc runs
     python bench.py --pmc-summary FETCH_DIR WRITE_DIR   # counters -> profiles/traffic_<workload>.json
+    python bench.py --split-sweep decode_llama_fp8,16-32-8-4-8192-e4m3-128   # decode: every split count
 
 HBM traffic (roofline.traffic) comes from two rocprofv3 --pmc runs of
 --pmc-step, one collecting FETCH_SIZE and one WRITE_SIZE. Both counters are
@@ -63,6 +64,10 @@ def parse():
                    help="comma-separated workload names for --sweep / --fp8-sweep")
     p.add_argument("--pmc-step", action="store_true",
                    help="one calibration copy and one fa_fwd + fa_bwd step (for counter runs)")
+    p.add_argument("--split-sweep", metavar="SHAPES", default=None,
+                   help="decode: time every key-range count on each shape, one JSON line per shape; "
+                        "SHAPES is a comma-separated list of decode workload names or "
+                        "B-Hq-Hkv-Nq-Nk-cache-d specs (cache: same or e4m3; bf16 queries, causal)")
     p.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                    help="turn FETCH_SIZE / WRITE_SIZE counter runs into profiles/traffic_<workload>.json")
     return p.parse_args()
@@ -510,6 +515,56 @@ def run_decode_bench(args):
     print(json.dumps(out), flush=True)
 
 
+def run_split_sweep(args):
+    """Decode: per shape, the median µs per call (8 rounds of 50 calls, rounds
+    interleaved over the counts) at every key-range count from 1 to 64 that the
+    shape allows, beside the automatic count the library picks."""
+    import statistics
+    import torch
+    import workloads as W
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    for spec in args.split_sweep.split(","):
+        if spec in W.DECODE_WORKLOADS:
+            w = W.DECODE_WORKLOADS[spec]
+        else:
+            B, Hq, Hkv, Nq, Nk, cache, d = spec.split("-")
+            w = W.decode_custom(int(B), int(Hq), int(Hkv), int(Nq), int(Nk), int(d), dtype="bf16",
+                                causal=True, seed=3, kv_cache=cache)
+        b = DecodeBound(w)
+        fa, auto = b.fa, b.splits
+        most = max(1, (w.Nk + 255) // 256)
+        counts = sorted({n for n in (1, 2, 3, 4, 6, 8, 12, 16, 24, 32, 48, 64, auto, 2 * auto)
+                         if n <= min(most, 256)} | {auto})
+        ws = {}
+        for n in counts:
+            nb = fa.fa_fwd_kvcache_workspace_size(w.B, w.Hq, w.Hkv, w.Nq, w.Nk, w.d, n)
+            ws[n] = torch.empty(max(nb, 1), dtype=torch.uint8, device="cuda")
+
+        def run(n):
+            b.splits, b.ws = n, ws[n]
+            b.call()
+
+        for n in counts:
+            for _ in range(20):
+                run(n)
+        torch.cuda.synchronize()
+        res = {n: [] for n in counts}
+        for _ in range(8):
+            for n in counts:
+                ev[0].record()
+                for _ in range(50):
+                    run(n)
+                ev[1].record()
+                torch.cuda.synchronize()
+                res[n].append(ev[0].elapsed_time(ev[1]) / 50 * 1000)
+        med = {n: round(statistics.median(v), 2) for n, v in res.items()}
+        best = min(med, key=med.get)
+        print(json.dumps({"shape": spec, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "Nq": w.Nq, "Nk": w.Nk,
+                          "d": w.d, "cache": "e4m3fn" if b.kv8 else w.dtype, "auto_splits": auto,
+                          "us_auto": med[auto], "best_splits": best, "us_best": med[best],
+                          "us_by_splits": {str(n): med[n] for n in counts}}), flush=True)
+
+
 def run_pmc_step(args):
     """Calibration copy of known size, then one fa_fwd + fa_bwd step (no timing)."""
     import torch
@@ -781,6 +836,9 @@ def main():
         sys.exit(1)
     if args.fp8_sweep:
         run_fp8_sweep(args)
+        return
+    if args.split_sweep:
+        run_split_sweep(args)
         return
     if args.sweep:
         run_sweep(args)
